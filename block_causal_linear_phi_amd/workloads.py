@@ -1,0 +1,125 @@
+"""Seeded synthetic inputs for block-causal linear attention.
+
+This module only draws and rounds numbers; it holds none of the method's
+arithmetic.  The same bits feed the HIP library (uploaded by torch) and the
+fp64 oracle (upcast), so parity compares the two on identical inputs.
+
+Every (workload, tensor, batch, head, step) slice has its own seed, drawn with
+numpy's PCG64 as float32 N(0, 1), scaled where the workload says so, then
+rounded to bf16 (round-to-nearest-even) for bf16 workloads.  Any slice can be
+regenerated alone, which keeps the oracle's memory bounded at large sizes.
+
+The latent grids are video-shaped: a 480p clip of 81 frames becomes a
+21 x 30 x 52 latent grid and a 720p clip a 21 x 45 x 80 grid (75,600 tokens,
+the ">75000 tokens" the cstia.com SANA-Video article quotes for a 5-second
+720p video); blocks are 3 latent frames.
+"""
+from __future__ import annotations
+
+import zlib
+from dataclasses import dataclass, field
+from typing import Optional, Tuple
+
+import numpy as np
+
+
+@dataclass(frozen=True)
+class Workload:
+    name: str
+    B: int
+    H: int
+    d: int
+    T: int
+    Hs: int
+    Ws: int
+    F: int
+    dtype: str                      # "f32" or "bf16"
+    rope: bool
+    split: Tuple[int, int, int] = (0, 0, 0)
+    base: float = 10000.0
+    eps: float = 1e-6
+    k_scale: float = 1.0
+    t0: int = 0
+    steps: int = 1                  # denoising steps (cached-step workload)
+    prior_blocks: int = 0           # committed blocks before the current one
+
+    @property
+    def N(self) -> int:
+        return self.T * self.Hs * self.Ws
+
+    @property
+    def nb(self) -> int:
+        return self.T // self.F
+
+    @property
+    def block_tokens(self) -> int:
+        return self.F * self.Hs * self.Ws
+
+
+WORKLOADS = {
+    # 4 blocks x 64 tokens, fp32, no RoPE; grid 4 x 8 x 8 with 1 frame a block
+    "tiny": Workload("tiny", B=1, H=2, d=32, T=4, Hs=8, Ws=8, F=1, dtype="f32", rope=False),
+    "480p": Workload("480p", B=1, H=16, d=64, T=21, Hs=30, Ws=52, F=3, dtype="bf16",
+                     rope=True, split=(16, 24, 24)),
+    # one 3-frame block at t0 = 18 against a cache of 6 prior blocks, 4 steps
+    "cached_step": Workload("cached_step", B=1, H=16, d=64, T=3, Hs=30, Ws=52, F=3,
+                            dtype="bf16", rope=True, split=(16, 24, 24), t0=18, steps=4,
+                            prior_blocks=6),
+    "720p": Workload("720p", B=1, H=16, d=64, T=21, Hs=45, Ws=80, F=3, dtype="bf16",
+                     rope=True, split=(16, 24, 24), k_scale=0.5),
+    "minute": Workload("minute", B=2, H=16, d=64, T=240, Hs=30, Ws=52, F=3, dtype="bf16",
+                       rope=True, split=(16, 24, 24)),
+}
+
+
+def seed_for(workload: str, tensor: str, b: int, h: int, step: int = 0) -> int:
+    return zlib.crc32(f"{workload}/{tensor}/{b}/{h}/{step}".encode()) & 0x7FFFFFFF
+
+
+def round_to_bf16_bits(x: np.ndarray) -> np.ndarray:
+    """float32 -> bf16 bit patterns (uint16), round-to-nearest-even."""
+    u = np.ascontiguousarray(x, dtype=np.float32).view(np.uint32)
+    lsb = (u >> 16) & 1
+    return ((u + 0x7FFF + lsb) >> 16).astype(np.uint16)
+
+
+def bf16_bits_to_f32(b: np.ndarray) -> np.ndarray:
+    return (b.astype(np.uint32) << 16).view(np.float32)
+
+
+def draw(shape, seed: int, scale: float = 1.0, dtype: str = "bf16"):
+    """N(0,1) * scale as float32 values exactly representable in `dtype`.
+    Returns (values_f32, raw) where raw is uint16 bf16 bits or float32."""
+    x = np.random.default_rng(np.random.PCG64(seed)).standard_normal(shape, dtype=np.float32)
+    if scale != 1.0:
+        x = (x * np.float32(scale)).astype(np.float32)
+    if dtype == "bf16":
+        bits = round_to_bf16_bits(x)
+        return bf16_bits_to_f32(bits), bits
+    return x, x
+
+
+def slice_qkv(w: Workload, tensor: str, b: int, h: int, step: int = 0, n_tokens: Optional[int] = None):
+    """One [N, d] slice of Q, K or V for (b, h, step)."""
+    n = w.N if n_tokens is None else n_tokens
+    scale = w.k_scale if tensor == "k" else 1.0
+    return draw((n, w.d), seed_for(w.name, tensor, b, h, step), scale, w.dtype)
+
+
+def full_qkv(w: Workload, step: int = 0, n_tokens: Optional[int] = None, heads=None):
+    """Stacked [B, H, N, d] host arrays for q, k, v: returns dict of
+    (values_f32, raw) per tensor.  `heads` restricts to a list of (b, h)."""
+    n = w.N if n_tokens is None else n_tokens
+    out = {}
+    for tensor in ("q", "k", "v"):
+        vals = np.empty((w.B, w.H, n, w.d), dtype=np.float32)
+        raw = np.empty((w.B, w.H, n, w.d), dtype=np.uint16 if w.dtype == "bf16" else np.float32)
+        for b in range(w.B):
+            for h in range(w.H):
+                if heads is not None and (b, h) not in heads:
+                    vals[b, h] = 0
+                    raw[b, h] = 0
+                    continue
+                vals[b, h], raw[b, h] = slice_qkv(w, tensor, b, h, step, n)
+        out[tensor] = (vals, raw)
+    return out
