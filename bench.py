@@ -1,0 +1,192 @@
+"""Benchmark: block-causal ReLU linear attention forward (one step = one
+sva_lin_attn_fwd call: per-block reduction, prefix scan, output pass) on the
+720p-shaped workload, B=1, H=16, d=64, bf16, 21 x 45 x 80 latent grid
+(75,600 tokens), blocks of 3 frames, numerator-only 3D RoPE split 16/24/24,
+K scaled by 0.5.  Inputs are seeded synthetic draws, resident in HBM before
+timing; two buffer sets alternate so the 256 MB Infinity Cache cannot hold a
+step's working set.
+
+Prints one JSON line.  `value` = tokens/s over all heads (B*N tokens per
+step / step time).  The `roofline` object rates the dominant kernel by its
+algorithmic bytes (its inputs read once + its outputs written once) over its
+average duration, timed live with HIP events recorded by the library on the
+stream it launches on.
+"""
+from __future__ import annotations
+
+import argparse
+import ctypes
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0  # MI355X HBM3E, GB/s
+
+
+class HipEvents:
+    """hipEvent_t handles from the HIP runtime (the library records them on
+    the stream its kernels run on)."""
+
+    def __init__(self):
+        self.rt = ctypes.CDLL("libamdhip64.so")
+        self.rt.hipEventCreate.argtypes = [ctypes.POINTER(ctypes.c_void_p)]
+        self.rt.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float), ctypes.c_void_p, ctypes.c_void_p]
+        self.rt.hipEventDestroy.argtypes = [ctypes.c_void_p]
+
+    def create(self):
+        ev = ctypes.c_void_p()
+        if self.rt.hipEventCreate(ctypes.byref(ev)) != 0:
+            raise RuntimeError("hipEventCreate failed")
+        return ev.value
+
+    def elapsed_ms(self, a, b) -> float:
+        ms = ctypes.c_float()
+        if self.rt.hipEventElapsedTime(ctypes.byref(ms), a, b) != 0:
+            raise RuntimeError("hipEventElapsedTime failed")
+        return ms.value
+
+    def destroy(self, ev):
+        self.rt.hipEventDestroy(ev)
+
+
+def gpu_leg(w, steps: int, warmup: int, sets: int):
+    import torch
+    from block_causal_linear_phi_amd import sva
+    from block_causal_linear_phi_amd import workloads as wl
+
+    dev = torch.device("cuda:0")
+    tdt = torch.bfloat16 if w.dtype == "bf16" else torch.float32
+    shape = (w.B, w.H, w.N, w.d)
+    base = {}
+    for t in ("q", "k", "v"):
+        x = torch.empty(shape, dtype=tdt, device=dev)
+        for b in range(w.B):
+            for h in range(w.H):
+                _, raw = wl.slice_qkv(w, t, b, h)
+                src = torch.from_numpy(raw.view("int16") if w.dtype == "bf16" else raw)
+                x[b, h].copy_(src.view(tdt) if w.dtype == "bf16" else src)
+        base[t] = x
+    bufs = [base] + [{t: base[t].clone() for t in base} for _ in range(sets - 1)]
+    outs = [torch.empty(shape, dtype=tdt, device=dev) for _ in range(sets)]
+    desc = sva.make_desc(w.B, w.H, w.d, (w.T, w.Hs, w.Ws), w.F, t0=w.t0, rope=w.rope, split=w.split,
+                         base=w.base, eps=w.eps, dtype=sva.SVA_BF16 if w.dtype == "bf16" else sva.SVA_F32)
+    ws = torch.empty(sva.sva_lin_attn_fwd_workspace(desc), dtype=torch.uint8, device=dev)
+    stream = torch.cuda.current_stream()
+    hip = HipEvents()
+    evs = [[hip.create() for _ in range(4)] for _ in range(steps)]
+
+    def step(i, events=None):
+        s = i % sets
+        x = bufs[s]
+        sva.sva_lin_attn_fwd(x["q"], x["k"], x["v"], (w.T, w.Hs, w.Ws), w.F, t0=w.t0, rope=w.rope,
+                             split=w.split, base=w.base, eps=w.eps, out=outs[s], ws=ws, stream=stream,
+                             events=events)
+
+    for i in range(warmup):
+        step(i)
+    torch.cuda.synchronize()
+    t_start = torch.cuda.Event(enable_timing=True)
+    t_end = torch.cuda.Event(enable_timing=True)
+    t_start.record(stream)
+    for i in range(steps):
+        step(warmup + i, evs[i])
+    t_end.record(stream)
+    torch.cuda.synchronize()
+    total_ms = t_start.elapsed_time(t_end)
+    per = {"reduce": [], "scan": [], "apply": []}
+    for e in evs:
+        per["reduce"].append(hip.elapsed_ms(e[0], e[1]))
+        per["scan"].append(hip.elapsed_ms(e[1], e[2]))
+        per["apply"].append(hip.elapsed_ms(e[2], e[3]))
+    for e in evs:
+        for x in e:
+            hip.destroy(x)
+    return total_ms, per
+
+
+def cpu_leg(w, reps: int):
+    """The fp64 oracle on the host: all heads of the workload, `reps` times."""
+    import numpy as np
+    from threadpoolctl import threadpool_info, threadpool_limits
+    from block_causal_linear_phi_amd import workloads as wl
+    from oracle import sva_oracle
+
+    cores = len(os.sched_getaffinity(0))
+    heads = [(b, h) for b in range(w.B) for h in range(w.H)]
+    data = {bh: tuple(wl.slice_qkv(w, t, *bh)[0][None, None] for t in "qkv") for bh in heads}
+    with threadpool_limits(limits=cores):
+        blas_threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+        t0 = time.perf_counter()
+        for _ in range(reps):
+            for bh in heads:
+                q, k, v = data[bh]
+                sva_oracle.lin_attn_fwd(q, k, v, (w.T, w.Hs, w.Ws), w.F, t0=w.t0, rope=w.rope, split=w.split,
+                                        base=w.base, eps=w.eps)
+        secs = time.perf_counter() - t0
+    tok_s = w.B * w.N * reps / secs
+    return {"value": tok_s, "unit": "tokens/s", "cores": int(min(cores, blas_threads)), "kind": "oracle",
+            "sample": f"{w.name}: all {len(heads)} heads, {reps} passes, {secs:.1f} s, numpy fp64 "
+                      f"(BLAS threads {blas_threads} of {cores} host cores; elementwise steps single-threaded)"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--workload", default="720p")
+    ap.add_argument("--sets", type=int, default=2, help="input buffer sets that alternate between steps")
+    ap.add_argument("--cpu-reps", type=int, default=2)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print("bench.py measures one GPU: this build has no multi-GPU path (heads and samples shard "
+              "with no communication; see the design notes). Run with --gpus 1.", file=sys.stderr)
+        sys.exit(2)
+
+    from block_causal_linear_phi_amd import workloads as wl
+    w = wl.WORKLOADS[args.workload]
+    total_ms, per = gpu_leg(w, args.steps, args.warmup, args.sets)
+    ms_per_step = total_ms / args.steps
+    esz = 2 if w.dtype == "bf16" else 4
+    elems = w.B * w.H * w.N * w.d
+    alg_bytes = {"reduce": 2 * elems * esz, "apply": 2 * elems * esz, "scan": 0}
+    avg = {k: sum(v) / len(v) for k, v in per.items()}
+    dom = "reduce" if avg["reduce"] >= avg["apply"] else "apply"
+    achieved = alg_bytes[dom] / (avg[dom] * 1e-3) / 1e9
+    step_bytes = 4 * elems * esz
+    line = {
+        "metric": "tokens/s (all heads) block-causal linear attn fwd; % of HBM peak",
+        "value": w.B * w.N / (ms_per_step * 1e-3),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_per_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16" if w.dtype == "bf16" else "f32",
+        "data": "synthetic (seeded N(0,1) draws, K x0.5; resident in HBM)",
+        "config": {"workload": f"{w.name}: B={w.B} H={w.H} d={w.d} grid {w.T}x{w.Hs}x{w.Ws} "
+                               f"({w.N} tokens) blocks of {w.F} frames ({w.nb} blocks), {w.dtype}, "
+                               f"numerator-only 3D RoPE {w.split[0]}/{w.split[1]}/{w.split[2]}",
+                   "B": w.B, "H": w.H, "d": w.d, "tokens": w.N, "blocks": w.nb},
+        "hbm_frac_step": step_bytes / (ms_per_step * 1e-3) / (HBM_PEAK_GBS * 1e9),
+        "roofline": {"bound": "hbm", "kernel": dom, "achieved": achieved, "peak": HBM_PEAK_GBS,
+                     "unit": "GB/s", "frac": achieved / HBM_PEAK_GBS, "traffic": None},
+        "kernels_us": {k: round(v * 1e3, 2) for k, v in avg.items()},
+        "kernels_gbs": {k: round(alg_bytes[k] / (avg[k] * 1e-3) / 1e9, 1) for k in ("reduce", "apply")},
+    }
+    if not args.no_cpu_baseline:
+        line["cpu_baseline"] = cpu_leg(w, args.cpu_reps)
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,10 @@
+"""Block-causal ReLU linear attention with numerator-only 3D RoPE and a
+constant-size block KV cache (SANA-Video) on AMD MI355X (gfx950).
+
+The computation lives in libsva.so (hand-written HIP kernels behind the C ABI
+in include/sva.h); `sva` is its thin ctypes binding.
+"""
+from .sva import (  # noqa: F401
+    SVA_BF16, SVA_F32, SvaDesc, SvaError, make_desc, sva_block_cache_apply, sva_block_cache_commit,
+    sva_block_cache_workspace, sva_lin_attn_fwd, sva_lin_attn_fwd_workspace, sva_phi_rope_prep,
+)

@@ -1,0 +1,197 @@
+"""Thin ctypes binding of libsva (include/sva.h).
+
+Argument marshalling only: every step of the computation runs in the HIP
+kernels of libsva.so.  torch supplies device memory and the current stream.
+If the library is not built, every call raises: there is no fallback.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional, Sequence, Tuple
+
+SVA_F32 = 0
+SVA_BF16 = 1
+
+SVA_OK = 0
+SVA_ERR_INVALID_ARG = -1
+SVA_ERR_UNSUPPORTED = -2
+SVA_ERR_WORKSPACE = -3
+SVA_ERR_HIP = -4
+
+LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libsva.so")
+
+
+class SvaDesc(ctypes.Structure):
+    _fields_ = [
+        ("B", ctypes.c_int), ("H", ctypes.c_int), ("d", ctypes.c_int),
+        ("T", ctypes.c_int), ("Hs", ctypes.c_int), ("Ws", ctypes.c_int),
+        ("frames_per_block", ctypes.c_int), ("t0", ctypes.c_int), ("rope", ctypes.c_int),
+        ("rope_dt", ctypes.c_int), ("rope_dh", ctypes.c_int), ("rope_dw", ctypes.c_int),
+        ("rope_base", ctypes.c_float), ("eps", ctypes.c_float), ("dtype", ctypes.c_int),
+    ]
+
+
+class SvaError(RuntimeError):
+    def __init__(self, status: int, where: str):
+        self.status = status
+        super().__init__(f"{where}: {status_string(status)} (status {status})")
+
+
+_lib = None
+
+_VP = ctypes.c_void_p
+_SIG = {
+    "sva_status_string": (ctypes.c_char_p, [ctypes.c_int]),
+    "sva_version": (ctypes.c_int, []),
+    "sva_lin_attn_fwd_workspace": (ctypes.c_int, [ctypes.POINTER(SvaDesc), ctypes.POINTER(ctypes.c_size_t)]),
+    "sva_lin_attn_fwd": (ctypes.c_int, [ctypes.POINTER(SvaDesc), _VP, _VP, _VP, _VP, _VP, _VP, _VP, _VP,
+                                        _VP, ctypes.c_size_t, _VP]),
+    "sva_lin_attn_fwd_traced": (ctypes.c_int, [ctypes.POINTER(SvaDesc), _VP, _VP, _VP, _VP, _VP, _VP, _VP,
+                                               _VP, _VP, ctypes.c_size_t, _VP, ctypes.POINTER(_VP)]),
+    "sva_block_cache_workspace": (ctypes.c_int, [ctypes.POINTER(SvaDesc), ctypes.POINTER(ctypes.c_size_t)]),
+    "sva_block_cache_apply": (ctypes.c_int, [ctypes.POINTER(SvaDesc), _VP, _VP, _VP, _VP, _VP, _VP, _VP,
+                                             ctypes.c_size_t, _VP]),
+    "sva_block_cache_commit": (ctypes.c_int, [ctypes.POINTER(SvaDesc), _VP, _VP, _VP, _VP, _VP,
+                                              ctypes.c_size_t, _VP]),
+    "sva_phi_rope_prep": (ctypes.c_int, [ctypes.POINTER(SvaDesc), _VP, _VP, _VP, _VP]),
+}
+
+
+def lib():
+    """The loaded libsva.so; raises if it has not been built."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(f"libsva.so is not built ({LIB_PATH}); run __graft_entry__.build()")
+        handle = ctypes.CDLL(LIB_PATH)
+        for name, (res, args) in _SIG.items():
+            fn = getattr(handle, name)
+            fn.restype = res
+            fn.argtypes = args
+        _lib = handle
+    return _lib
+
+
+def status_string(status: int) -> str:
+    return lib().sva_status_string(status).decode()
+
+
+def make_desc(B: int, H: int, d: int, grid: Sequence[int], frames_per_block: int, *, t0: int = 0,
+              rope: bool = False, split: Optional[Sequence[int]] = None, base: float = 10000.0,
+              eps: float = 1e-6, dtype: int = SVA_BF16) -> SvaDesc:
+    T, Hs, Ws = grid
+    dt, dh, dw = split if (rope and split is not None) else (0, 0, 0)
+    return SvaDesc(B, H, d, T, Hs, Ws, frames_per_block, t0, 1 if rope else 0, dt, dh, dw,
+                   float(base), float(eps), dtype)
+
+
+def _ptr(t) -> Optional[int]:
+    return None if t is None else t.data_ptr()
+
+
+def _stream(stream) -> Optional[int]:
+    import torch
+    s = torch.cuda.current_stream() if stream is None else stream
+    return s.cuda_stream
+
+
+def _dtype_code(t) -> int:
+    import torch
+    if t.dtype == torch.bfloat16:
+        return SVA_BF16
+    if t.dtype == torch.float32:
+        return SVA_F32
+    raise TypeError(f"unsupported dtype {t.dtype}; use torch.bfloat16 or torch.float32")
+
+
+def _check(status: int, where: str):
+    if status != SVA_OK:
+        raise SvaError(status, where)
+
+
+def _desc_from(q, grid, F, t0, rope, split, base, eps) -> SvaDesc:
+    if q.dim() != 4:
+        raise ValueError("q, k, v must be [B, H, N, d]")
+    B, H, N, d = q.shape
+    return make_desc(B, H, d, grid, F, t0=t0, rope=rope, split=split, base=base, eps=eps,
+                     dtype=_dtype_code(q))
+
+
+def sva_lin_attn_fwd_workspace(desc: SvaDesc) -> int:
+    n = ctypes.c_size_t(0)
+    _check(lib().sva_lin_attn_fwd_workspace(ctypes.byref(desc), ctypes.byref(n)), "sva_lin_attn_fwd_workspace")
+    return n.value
+
+
+def sva_block_cache_workspace(desc: SvaDesc) -> int:
+    n = ctypes.c_size_t(0)
+    _check(lib().sva_block_cache_workspace(ctypes.byref(desc), ctypes.byref(n)), "sva_block_cache_workspace")
+    return n.value
+
+
+def _workspace(nbytes: int, like, ws):
+    import torch
+    if ws is not None:
+        return ws
+    return torch.empty(max(nbytes, 1), dtype=torch.uint8, device=like.device)
+
+
+def sva_lin_attn_fwd(q, k, v, grid: Tuple[int, int, int], frames_per_block: int, *, t0: int = 0,
+                     rope: bool = False, split=None, base: float = 10000.0, eps: float = 1e-6,
+                     S0=None, z0=None, out=None, S_out=None, z_out=None, ws=None, stream=None,
+                     events=None):
+    """One-shot block-causal forward (sva_lin_attn_fwd).  Returns `out`."""
+    import torch
+    desc = _desc_from(q, grid, frames_per_block, t0, rope, split, base, eps)
+    if out is None:
+        out = torch.empty_like(q)
+    nbytes = sva_lin_attn_fwd_workspace(desc)
+    ws = _workspace(nbytes, q, ws)
+    args = (ctypes.byref(desc), _ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(S0), _ptr(z0), _ptr(S_out),
+            _ptr(z_out), _ptr(ws), ws.numel() * ws.element_size(), _stream(stream))
+    if events is None:
+        st = lib().sva_lin_attn_fwd(*args)
+    else:
+        arr = (_VP * 4)(*[ctypes.c_void_p(e) for e in events])
+        st = lib().sva_lin_attn_fwd_traced(*args, arr)
+    _check(st, "sva_lin_attn_fwd")
+    return out
+
+
+def sva_block_cache_apply(S, z, q, k, v, frame_grid: Tuple[int, int, int], *, t0: int, rope: bool = False,
+                          split=None, base: float = 10000.0, eps: float = 1e-6, out=None, ws=None,
+                          stream=None):
+    """Output of one block against the committed cache (S, z); the cache is
+    not modified.  frame_grid = (F, Hs, Ws).  Returns `out`."""
+    import torch
+    desc = _desc_from(q, frame_grid, frame_grid[0], t0, rope, split, base, eps)
+    if out is None:
+        out = torch.empty_like(q)
+    ws = _workspace(sva_block_cache_workspace(desc), q, ws)
+    st = lib().sva_block_cache_apply(ctypes.byref(desc), _ptr(S), _ptr(z), _ptr(q), _ptr(k), _ptr(v),
+                                     _ptr(out), _ptr(ws), ws.numel() * ws.element_size(), _stream(stream))
+    _check(st, "sva_block_cache_apply")
+    return out
+
+
+def sva_block_cache_commit(S, z, k, v, frame_grid: Tuple[int, int, int], *, t0: int, rope: bool = False,
+                           split=None, base: float = 10000.0, ws=None, stream=None):
+    """Adds one block's K, V to the cache (S, z) in place."""
+    desc = _desc_from(k, frame_grid, frame_grid[0], t0, rope, split, base, 0.0)
+    ws = _workspace(sva_block_cache_workspace(desc), k, ws)
+    st = lib().sva_block_cache_commit(ctypes.byref(desc), _ptr(S), _ptr(z), _ptr(k), _ptr(v), _ptr(ws),
+                                      ws.numel() * ws.element_size(), _stream(stream))
+    _check(st, "sva_block_cache_commit")
+
+
+def sva_phi_rope_prep(x, grid: Tuple[int, int, int], *, t0: int = 0, rope: bool = False, split=None,
+                      base: float = 10000.0, want_phi: bool = True, stream=None):
+    """The phi + RoPE stage alone: returns (RoPE(phi x), phi x) as fp32."""
+    import torch
+    desc = _desc_from(x, grid, grid[0], t0, rope, split, base, 0.0)
+    xr = torch.empty(x.shape, dtype=torch.float32, device=x.device)
+    xp = torch.empty_like(xr) if want_phi else None
+    st = lib().sva_phi_rope_prep(ctypes.byref(desc), _ptr(x), _ptr(xr), _ptr(xp), _stream(stream))
+    _check(st, "sva_phi_rope_prep")
+    return xr, xp

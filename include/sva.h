@@ -1,0 +1,153 @@
+/*
+ * sva.h -- C ABI of libsva: block-causal ReLU linear attention with a
+ * numerator-only 3D RoPE and a constant-size block KV cache, as used by
+ * SANA-Video, for AMD MI355X (gfx950).
+ *
+ * Pages this interface follows:
+ *   [talk] "SANA-Video: Efficient Video Generation with Block Linear Diffusion
+ *          Transformer, [ICLR 2026, Oral]" talk transcript (shadowingenglish.com):
+ *          - linear-attention segment: the state is d x d whatever the length;
+ *          - block KV cache segment: the state of a block is cached and each
+ *            later block adds only its own KV contribution to the cache;
+ *          - block causal segment: block 1 cannot see block 2, block 2 sees
+ *            block 1; constant memory with global history;
+ *          - opening: generate block by block causally, diffuse within a block;
+ *          - 3D RoPE segment: RoPE over (t, h, w) for the linear attention.
+ *   [news] cstia.com SANA-Video article, positional-encoding paragraph: RoPE is
+ *          kept in the numerator and removed from the denominator.
+ *
+ * What is computed, per batch b and head h (tokens n in row-major (t, h, w)
+ * order on a T x Hs x Ws latent grid, blocks of F whole frames):
+ *   phi(x)   = max(x, 0)                     (reading taken: ReLU)
+ *   qr, kr   = RoPE(phi q), RoPE(phi k)      (numerator copies only)
+ *   A_c      = sum_{n in block c} kr_n v_n^T      (d x d)
+ *   zeta_c   = sum_{n in block c} phi(k)_n        (d)
+ *   S_c      = S0 + sum_{c' <= c} A_c',  Z_c = z0 + sum_{c' <= c} zeta_c'
+ *   out_n    = (qr_n^T S_c) / (phi(q)_n . Z_c + eps),  c = block of n.
+ * RoPE: head dims [0, dt) follow the global latent frame t = t0 + local frame,
+ * [dt, dt+dh) follow h, [dt+dh, d) follow w.  In an axis slice of width d_a
+ * the adjacent pair (2i, 2i+1) turns by pos * rope_base^(-2i/d_a) radians:
+ * (x, y) -> (x cos - y sin, x sin + y cos).
+ *
+ * Layouts: q, k, v, out are contiguous [B, H, N, d], N = T*Hs*Ws, in the
+ * descriptor's dtype (fp32 or bf16).  S is fp32 [B, H, d, d] row-major with
+ * S[i][j] = sum kr_i v_j; z is fp32 [B, H, d].  Every pointer is a device
+ * pointer and must be 16-byte aligned.
+ *
+ * Ownership: the caller allocates and frees every buffer, including the
+ * workspace.  The library allocates nothing, keeps no pointer after a call
+ * returns and holds no global state: calls on disjoint buffers may run
+ * concurrently.  `out` must not overlap q, k or v.
+ *
+ * Errors: validation is synchronous, happens before anything is launched,
+ * and on error nothing is written.  Work is queued on `stream` (a
+ * hipStream_t; NULL = the default stream) and runs asynchronously; a kernel
+ * fault surfaces at the caller's next synchronisation.  A failed launch
+ * returns SVA_ERR_HIP.  NaN/Inf inputs are not checked (ReLU maps NaN to 0).
+ * Sums are taken in a fixed order: two calls on equal inputs give equal bits.
+ */
+#ifndef SVA_H
+#define SVA_H
+
+#include <stddef.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum sva_dtype { SVA_F32 = 0, SVA_BF16 = 1 } sva_dtype;
+
+typedef enum sva_status {
+  SVA_OK = 0,
+  SVA_ERR_INVALID_ARG = -1,  /* null/misaligned pointer, bad shape, overlap */
+  SVA_ERR_UNSUPPORTED = -2,  /* d not 32/64, bad RoPE split, grid too large */
+  SVA_ERR_WORKSPACE = -3,    /* workspace missing or smaller than required */
+  SVA_ERR_HIP = -4           /* a HIP launch failed */
+} sva_status;
+
+/* Problem descriptor.  All fields are read; none is kept after the call. */
+typedef struct sva_desc {
+  int B, H, d;               /* batch, heads, head dim (32 or 64) */
+  int T, Hs, Ws;             /* latent grid of this call: frames x height x width */
+  int frames_per_block;      /* F; T % F == 0.  apply/commit need T == F */
+  int t0;                    /* global latent frame index of this call's frame 0 */
+  int rope;                  /* 0: no RoPE, 1: 3D RoPE on the numerator */
+  int rope_dt, rope_dh, rope_dw; /* even widths with dt + dh + dw == d */
+  float rope_base;           /* frequency base, > 0 (10000 is customary) */
+  float eps;                 /* added to the denominator, >= 0 */
+  int dtype;                 /* sva_dtype of q, k, v and out */
+} sva_desc;
+
+/* Human-readable text for a status code (static storage). */
+const char* sva_status_string(int status);
+
+/* ABI version of this header: 1. */
+int sva_version(void);
+
+/* Workspace bytes sva_lin_attn_fwd needs for this descriptor (per-block
+ * partial states and the prefix states; about nb*B*H*d*d*8 bytes). */
+sva_status sva_lin_attn_fwd_workspace(const sva_desc* desc, size_t* bytes);
+
+/* One-shot block-causal forward over all T/F blocks ([talk], block causal
+ * segment: the whole sequence in one pass, as in block-causal training).
+ *   q, k, v  in:  [B, H, N, d] dtype
+ *   out      out: [B, H, N, d] dtype (round-to-nearest-even for bf16)
+ *   S0, z0   in:  initial cache [B,H,d,d], [B,H,d] fp32, or both NULL (zeros)
+ *   S_out, z_out out: final cache (S_{nb-1}, Z_{nb-1}) fp32, or both NULL;
+ *            may be the same buffers as S0, z0 (updated in place)
+ *   ws, ws_bytes: caller-owned scratch of at least sva_lin_attn_fwd_workspace
+ */
+sva_status sva_lin_attn_fwd(const sva_desc* desc, const void* q, const void* k,
+                            const void* v, void* out, const float* S0,
+                            const float* z0, float* S_out, float* z_out,
+                            void* ws, size_t ws_bytes, void* stream);
+
+/* Same as sva_lin_attn_fwd, and records the four hipEvent_t in `events` on
+ * `stream`: before the per-block reduction, after it, after the prefix scan
+ * and after the output pass, so a caller can time each kernel. */
+sva_status sva_lin_attn_fwd_traced(const sva_desc* desc, const void* q,
+                                   const void* k, const void* v, void* out,
+                                   const float* S0, const float* z0,
+                                   float* S_out, float* z_out, void* ws,
+                                   size_t ws_bytes, void* stream,
+                                   void* const events[4]);
+
+/* Workspace bytes sva_block_cache_apply / sva_block_cache_commit need for a
+ * one-block descriptor; independent of how many blocks were committed. */
+sva_status sva_block_cache_workspace(const sva_desc* desc, size_t* bytes);
+
+/* Output of ONE block (desc->T == desc->frames_per_block, first frame at
+ * global index desc->t0) against a committed cache (S, z): the block sees
+ * the cache and itself ([talk] opening: diffuse within the current block;
+ * block KV cache segment: cached state plus the current block's KV).
+ * The cache is read only and left unchanged, so this may be called for
+ * every denoising step of the block.
+ *   S, z     in:  cache [B,H,d,d], [B,H,d] fp32
+ *   q, k, v  in:  [B, H, F*Hs*Ws, d];  out: same shape and dtype */
+sva_status sva_block_cache_apply(const sva_desc* desc, const float* S,
+                                 const float* z, const void* q, const void* k,
+                                 const void* v, void* out, void* ws,
+                                 size_t ws_bytes, void* stream);
+
+/* Adds ONE block to the cache in place ([talk], block KV cache segment: the
+ * state is updated additively): S += sum RoPE(phi k) v^T, z += sum phi k over
+ * the block's tokens at global frames t0 .. t0+F-1.  The caller chooses which
+ * step's k, v to commit and zero-fills a fresh cache.  The cache size,
+ * B*H*(d*d+d)*4 bytes, does not depend on the number of committed blocks. */
+sva_status sva_block_cache_commit(const sva_desc* desc, float* S, float* z,
+                                  const void* k, const void* v, void* ws,
+                                  size_t ws_bytes, void* stream);
+
+/* The phi + 3D-RoPE stage on its own, for testing it in isolation:
+ *   x      in:  [B, H, N, d] dtype
+ *   x_rot  out: [B, H, N, d] fp32 = RoPE(phi x)   (phi x when desc->rope == 0)
+ *   x_phi  out: [B, H, N, d] fp32 = phi x  (may be NULL)
+ * The fused kernels run exactly this stage in registers. */
+sva_status sva_phi_rope_prep(const sva_desc* desc, const void* x, float* x_rot,
+                             float* x_phi, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* SVA_H */

@@ -1,0 +1,128 @@
+"""The C-ABI library on the CPU: it loads, exports every function that
+include/sva.h declares, sizes its workspaces as documented, and rejects bad
+descriptors before launching anything (no GPU is touched by these calls)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+from block_causal_linear_phi_amd import sva
+
+# The checks below hand the library fake device addresses that validation must
+# reject before any launch.  They run only where no GPU is reachable, so a
+# validation bug can never turn into a launch on those addresses.
+try:
+    import torch
+    _GPU_VISIBLE = torch.cuda.device_count() > 0
+except Exception:  # pragma: no cover
+    _GPU_VISIBLE = False
+fake_pointers = pytest.mark.skipif(_GPU_VISIBLE, reason="fake device pointers; host-only check")
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "sva.h")
+
+
+def _declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(sva_[a-z0-9_]+)\s*\(", text)))
+
+
+def test_library_exports_every_declared_function():
+    names = _declared_functions()
+    assert len(names) >= 9
+    lib = ctypes.CDLL(sva.LIB_PATH)
+    for n in names:
+        assert hasattr(lib, n), n
+    assert set(names) == set(sva._SIG), "binding and header disagree"
+
+
+def test_version_and_status_strings():
+    assert sva.lib().sva_version() == 1
+    for code in (0, -1, -2, -3, -4):
+        assert sva.status_string(code)
+    assert sva.status_string(-99) == "unknown status"
+
+
+def _desc(**kw):
+    base = dict(B=1, H=16, d=64, grid=(21, 45, 80), frames_per_block=3, rope=True,
+                split=(16, 24, 24), dtype=sva.SVA_BF16)
+    base.update(kw)
+    grid = base.pop("grid")
+    F = base.pop("frames_per_block")
+    return sva.make_desc(base.pop("B"), base.pop("H"), base.pop("d"), grid, F, **base)
+
+
+def test_cache_workspace_is_independent_of_stream_length():
+    """[talk] constant memory: the one-block apply/commit workspace and the
+    cache never depend on how many blocks came before (t0)."""
+    sizes = {sva.sva_block_cache_workspace(_desc(grid=(3, 30, 52), t0=t0)) for t0 in (0, 3, 90, 237)}
+    assert len(sizes) == 1
+
+
+def test_fwd_workspace_is_small_relative_to_inputs():
+    n = sva.sva_lin_attn_fwd_workspace(_desc())
+    traffic = 4 * 16 * 75600 * 64 * 2          # q, k, v read + out written, bf16
+    assert 0 < n < 0.05 * traffic
+
+
+BAD = [
+    (dict(d=48), sva.SVA_ERR_UNSUPPORTED),
+    (dict(dtype=7), sva.SVA_ERR_UNSUPPORTED),
+    (dict(split=(16, 24, 22)), sva.SVA_ERR_UNSUPPORTED),
+    (dict(split=(15, 25, 24)), sva.SVA_ERR_UNSUPPORTED),
+    (dict(base=-1.0), sva.SVA_ERR_UNSUPPORTED),
+    (dict(frames_per_block=4), sva.SVA_ERR_INVALID_ARG),   # 21 % 4 != 0
+    (dict(B=0), sva.SVA_ERR_INVALID_ARG),
+    (dict(eps=-1.0), sva.SVA_ERR_INVALID_ARG),
+    (dict(t0=-3), sva.SVA_ERR_INVALID_ARG),
+    (dict(grid=(240, 400, 400)), sva.SVA_ERR_UNSUPPORTED),  # RoPE table too large
+]
+
+
+@fake_pointers
+@pytest.mark.parametrize("kw,code", BAD)
+def test_bad_descriptors_are_rejected(kw, code):
+    d = _desc(**kw)
+    n = ctypes.c_size_t(123)
+    assert sva.lib().sva_lin_attn_fwd_workspace(ctypes.byref(d), ctypes.byref(n)) == code
+    assert n.value == 123  # nothing written on error
+    # the compute entry points validate before touching any pointer or the GPU
+    st = sva.lib().sva_lin_attn_fwd(ctypes.byref(d), 16, 16, 16, 4096, None, None, None, None, 16, 1 << 40, None)
+    assert st == code
+
+
+@fake_pointers
+def test_pointer_checks_happen_before_launch():
+    d = _desc()
+    lib = sva.lib()
+    big = 1 << 40
+    # null q
+    assert lib.sva_lin_attn_fwd(ctypes.byref(d), None, 16, 32, 1 << 36, None, None, None, None, 16, big, None) \
+        == sva.SVA_ERR_INVALID_ARG
+    # misaligned k
+    assert lib.sva_lin_attn_fwd(ctypes.byref(d), 16, 24, 1 << 33, 1 << 36, None, None, None, None, 16, big, None) \
+        == sva.SVA_ERR_INVALID_ARG
+    # out overlapping q
+    assert lib.sva_lin_attn_fwd(ctypes.byref(d), 1 << 30, 1 << 33, 1 << 34, (1 << 30) + 4096, None, None, None,
+                                None, 16, big, None) == sva.SVA_ERR_INVALID_ARG
+    # only one of S0/z0
+    assert lib.sva_lin_attn_fwd(ctypes.byref(d), 1 << 30, 1 << 33, 1 << 34, 1 << 36, 1 << 20, None, None,
+                                None, 16, big, None) == sva.SVA_ERR_INVALID_ARG
+    # workspace too small
+    assert lib.sva_lin_attn_fwd(ctypes.byref(d), 1 << 30, 1 << 33, 1 << 34, 1 << 36, None, None, None, None,
+                                16, 64, None) == sva.SVA_ERR_WORKSPACE
+    # apply/commit need exactly one block
+    assert lib.sva_block_cache_apply(ctypes.byref(d), 16, 32, 1 << 30, 1 << 33, 1 << 34, 1 << 36, 16, big,
+                                     None) == sva.SVA_ERR_INVALID_ARG
+    assert lib.sva_block_cache_commit(ctypes.byref(d), 16, 32, 1 << 30, 1 << 33, 16, big, None) \
+        == sva.SVA_ERR_INVALID_ARG
+
+
+@fake_pointers
+def test_traced_needs_events():
+    d = _desc()
+    st = sva.lib().sva_lin_attn_fwd_traced(ctypes.byref(d), 1 << 30, 1 << 33, 1 << 34, 1 << 36, None, None,
+                                           None, None, 16, 1 << 40, None, None)
+    assert st == sva.SVA_ERR_INVALID_ARG
