@@ -109,6 +109,31 @@ def gpu_leg(w, steps: int, warmup: int, sets: int):
     return total_ms, per
 
 
+def copy_calibration(mib: int, reps: int = 5):
+    """A plain streaming kernel of known size (torch.mul(x, 1.0, out=y) on
+    fp32: reads and writes mib MiB each).  Its FETCH_SIZE / WRITE_SIZE
+    counters scale the library kernels' counters to bytes, and its bandwidth
+    is the practical HBM ceiling on this machine.  Reported on stderr."""
+    import torch
+    n = mib * (1 << 20) // 4
+    x = torch.ones(n, dtype=torch.float32, device="cuda:0")
+    y = torch.empty_like(x)
+    torch.mul(x, 1.0, out=y)
+    torch.cuda.synchronize()
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    a.record()
+    for _ in range(reps):
+        torch.mul(x, 1.0, out=y)
+    b.record()
+    torch.cuda.synchronize()
+    ms = a.elapsed_time(b) / reps
+    gbs = 2 * n * 4 / (ms * 1e-3) / 1e9
+    print(json.dumps({"copy_calibration": {"kernel": "torch.mul fp32 out-of-place", "read_bytes": n * 4,
+                                           "write_bytes": n * 4, "us": ms * 1e3, "GB/s": gbs}}),
+          file=sys.stderr, flush=True)
+    del x, y
+
+
 def cpu_leg(w, reps: int):
     """The fp64 oracle on the host: all heads of the workload, `reps` times."""
     import numpy as np
@@ -143,6 +168,8 @@ def main():
     ap.add_argument("--sets", type=int, default=2, help="input buffer sets that alternate between steps")
     ap.add_argument("--cpu-reps", type=int, default=2)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-calib", type=int, default=0, metavar="MIB",
+                    help="also run a plain fp32 streaming kernel over MIB MiB (counter calibration)")
     args = ap.parse_args()
     if args.gpus != 1:
         print("bench.py measures one GPU: this build has no multi-GPU path (heads and samples shard "
@@ -151,6 +178,8 @@ def main():
 
     from block_causal_linear_phi_amd import workloads as wl
     w = wl.WORKLOADS[args.workload]
+    if args.copy_calib:
+        copy_calibration(args.copy_calib)
     total_ms, per = gpu_leg(w, args.steps, args.warmup, args.sets)
     ms_per_step = total_ms / args.steps
     esz = 2 if w.dtype == "bf16" else 4

@@ -32,6 +32,11 @@
 #include <stdint.h>
 #include <string.h>
 
+#include <map>
+#include <type_traits>
+#include <mutex>
+#include <tuple>
+
 #include "sva.h"
 
 namespace {
@@ -40,6 +45,7 @@ typedef __bf16 bf16x8_t __attribute__((__vector_size__(8 * sizeof(__bf16))));
 typedef __bf16 bf16x2_t __attribute__((__vector_size__(2 * sizeof(__bf16))));
 typedef float floatx4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 
 constexpr int kThreads = 256;          // 4 wavefronts of 64
 constexpr int kMaxTableEntries = 5632; // RoPE cos/sin table, 44 KiB of LDS
@@ -121,32 +127,47 @@ __device__ void build_rope_table(float2* tab, const RopeArgs& ra) {
   }
 }
 
-// Where the table row of global pair p starts, its row stride, and which
-// coordinate (0: frame, 1: h, 2: w) selects the row.
+// A token's RoPE coordinates packed in one word: frame (call-local, the
+// t-table row) in bits 21..31, h in bits 10..20, w in bits 0..9.  The host
+// rejects RoPE grids that do not fit (T, Hs <= 2048, Ws <= 1024).
+__device__ __forceinline__ uint32_t decode_packed(uint32_t n, const FastDiv& fHW, const FastDiv& fWs) {
+  const uint32_t frame = fdiv(n, fHW);
+  const uint32_t rem = n - frame * fHW.div;
+  const uint32_t h = fdiv(rem, fWs);
+  const uint32_t w = rem - h * fWs.div;
+  return (frame << 21) | (h << 10) | w;
+}
+
+// Table entry of one RoPE pair: row base + stride * coordinate, where the
+// coordinate is a bit field of the packed word.
 struct PairLoc {
-  int base, stride, axis;
+  int base, stride, shift, width;
 };
 
 __device__ __forceinline__ PairLoc pair_loc(int p, const RopeArgs& ra) {
   const int ht = ra.dt >> 1, hh = ra.dh >> 1;
   PairLoc r;
   if (p < ht) {
-    r.base = p; r.stride = ht; r.axis = 0;
+    r.base = p; r.stride = ht; r.shift = 21; r.width = 11;
   } else if (p < ht + hh) {
-    r.base = ra.off_h + (p - ht); r.stride = hh; r.axis = 1;
+    r.base = ra.off_h + (p - ht); r.stride = hh; r.shift = 10; r.width = 11;
   } else {
-    r.base = ra.off_w + (p - ht - hh); r.stride = ra.dw >> 1; r.axis = 2;
+    r.base = ra.off_w + (p - ht - hh); r.stride = ra.dw >> 1; r.shift = 0; r.width = 10;
   }
   return r;
 }
 
-__device__ __forceinline__ int pair_entry(const PairLoc& pl, int frame, int h, int w) {
-  const int pos = pl.axis == 0 ? frame : (pl.axis == 1 ? h : w);
-  return pl.base + pos * pl.stride;
+__device__ __forceinline__ int pair_entry(const PairLoc& pl, uint32_t packed) {
+  const uint32_t pos = __builtin_amdgcn_ubfe(packed, (uint32_t)pl.shift, (uint32_t)pl.width);
+  return __mul24((int)pos, pl.stride) + pl.base;  // 24-bit multiply: operands are small
 }
 
-// phi = ReLU
-__device__ __forceinline__ float relu(float x) { return x > 0.f ? x : 0.f; }
+// phi = ReLU on the bit pattern: a float with its sign bit set is a negative
+// int32, so max_i32(bits, 0) is 0 for every negative float (and -0) and the
+// float itself otherwise -- one v_max_i32.
+__device__ __forceinline__ float relu_bits(uint32_t bits) {
+  return __int_as_float(max((int)bits, 0));
+}
 
 // Turn the pair (x, y) by the angle whose (cos, sin) is cs.
 __device__ __forceinline__ void rotate(float& x, float& y, float2 cs) {
@@ -154,19 +175,6 @@ __device__ __forceinline__ void rotate(float& x, float& y, float2 cs) {
   const float yr = x * cs.y + y * cs.x;
   x = xr;
   y = yr;
-}
-
-struct Coord {
-  int frame, h, w;
-};
-
-__device__ __forceinline__ Coord decode(uint32_t n, const FastDiv& fHW, const FastDiv& fWs) {
-  Coord c;
-  c.frame = (int)fdiv(n, fHW);
-  const uint32_t rem = n - (uint32_t)c.frame * fHW.div;
-  c.h = (int)fdiv(rem, fWs);
-  c.w = (int)(rem - (uint32_t)c.h * fWs.div);
-  return c;
 }
 
 // ---------------------------------------------------------------------------
@@ -213,6 +221,59 @@ __device__ __forceinline__ void store_words(void* p, const uint32_t* src) {
   }
 }
 
+// Raw buffer access.  A resource covers [base, base + bytes); loads past the
+// end return zeros and stores past it are dropped by the hardware, which is
+// how the kernels handle a segment's ragged end without branches.
+// 0x00020000 is the gfx9 raw-buffer descriptor word 3 (32-bit data format).
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, 0x00020000);
+}
+
+// Cache policy of the streaming traffic.  Loads of q, k, v (each read
+// once) carry the non-temporal bit, which keeps them from churning the
+// Infinity Cache; measured on MI355X for this two-pass pattern, this stops
+// the output pass's dirty lines from draining into the next reduction
+// (memory-only floor of the two passes: 133 -> 112 us at 720p).  Output
+// stores keep the default policy: non-temporal stores complete later, and
+// since gfx9 counts stores and loads in one in-order counter, the output
+// pass's prefetch waits would inherit that latency (77 -> 98 us measured).
+constexpr int kLoadPolicy = 2;   // nt
+constexpr int kStorePolicy = 0;  // default
+
+template <int NW>
+__device__ __forceinline__ void buf_load(uint32_t* dst, __amdgpu_buffer_rsrc_t r, uint32_t off) {
+  if constexpr (NW == 1) {
+    dst[0] = (uint32_t)__builtin_amdgcn_raw_buffer_load_b32(r, off, 0, kLoadPolicy);
+  } else if constexpr (NW == 2) {
+    const uint2 t = __builtin_bit_cast(uint2, __builtin_amdgcn_raw_buffer_load_b64(r, off, 0, kLoadPolicy));
+    dst[0] = t.x; dst[1] = t.y;
+  } else {
+    static_assert(NW % 4 == 0, "word count");
+#pragma unroll
+    for (int i = 0; i < NW / 4; ++i) {
+      const uint4 t =
+          __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(r, off + 16 * i, 0, kLoadPolicy));
+      dst[4 * i] = t.x; dst[4 * i + 1] = t.y; dst[4 * i + 2] = t.z; dst[4 * i + 3] = t.w;
+    }
+  }
+}
+
+template <int NW>
+__device__ __forceinline__ void buf_store(__amdgpu_buffer_rsrc_t r, uint32_t off, const uint32_t* src) {
+  if constexpr (NW == 1) {
+    __builtin_amdgcn_raw_buffer_store_b32(src[0], r, off, 0, kStorePolicy);
+  } else if constexpr (NW == 2) {
+    __builtin_amdgcn_raw_buffer_store_b64(__builtin_bit_cast(u32x2, make_uint2(src[0], src[1])), r, off, 0,
+                                          kStorePolicy);
+  } else {
+    static_assert(NW % 4 == 0, "word count");
+#pragma unroll
+    for (int i = 0; i < NW / 4; ++i)
+      __builtin_amdgcn_raw_buffer_store_b128(
+          u32x4{src[4 * i], src[4 * i + 1], src[4 * i + 2], src[4 * i + 3]}, r, off + 16 * i, 0, kStorePolicy);
+  }
+}
+
 // Unpack `CNT` elements (bf16 pairs or fp32 words) into floats.
 template <bool BF16, int CNT>
 __device__ __forceinline__ void unpack(float* f, const uint32_t* w) {
@@ -220,6 +281,16 @@ __device__ __forceinline__ void unpack(float* f, const uint32_t* w) {
   for (int i = 0; i < CNT; ++i) {
     if (BF16) f[i] = (i & 1) ? bf16_hi(w[i >> 1]) : bf16_lo(w[i >> 1]);
     else f[i] = __uint_as_float(w[i]);
+  }
+}
+
+// Unpack with phi = ReLU applied on the bits.
+template <bool BF16, int CNT>
+__device__ __forceinline__ void unpack_relu(float* f, const uint32_t* w) {
+#pragma unroll
+  for (int i = 0; i < CNT; ++i) {
+    if (BF16) f[i] = relu_bits((i & 1) ? (w[i >> 1] & 0xffff0000u) : (w[i >> 1] << 16));
+    else f[i] = relu_bits(w[i]);
   }
 }
 
@@ -241,14 +312,13 @@ struct Geo {
   int Nb;       // tokens per block
   int nb;       // blocks
   int BH;
+  int T, Hs, Ws;
   FastDiv fHW, fWs;
 };
 
 struct SplitArgs {
   long long total;  // BH * N flattened tokens
   long long L;      // flattened tokens per workgroup
-  int maxsub;       // most (b, h, block) pieces one workgroup range can touch
-  int pad_;
 };
 
 // ---------------------------------------------------------------------------
@@ -264,7 +334,7 @@ struct SplitArgs {
 // ---------------------------------------------------------------------------
 
 template <bool BF16, int D, bool ROPE>
-__global__ __launch_bounds__(kThreads) void sva_reduce_kernel(
+__global__ __launch_bounds__(kThreads, BF16 ? 2 : 1) void sva_reduce_kernel(
     const void* __restrict__ kp, const void* __restrict__ vp, float* __restrict__ partials,
     Geo geo, SplitArgs sp, RopeArgs ra) {
   constexpr int FPL = D / 16;
@@ -272,13 +342,16 @@ __global__ __launch_bounds__(kThreads) void sva_reduce_kernel(
   constexpr int E = D * D + D;
   constexpr int ESZ = BF16 ? 2 : 4;
   constexpr int NW = FPL * ESZ / 4;  // 32-bit words per lane per token row piece
+  constexpr int ROWB = D * ESZ;      // bytes per token row
+  constexpr int STEP = 32;           // tokens per wave per step
+  constexpr int WSTRIDE = STEP * (kThreads / 64);
 
   extern __shared__ float2 tab[];
   __shared__ float red[D * D];
   __shared__ float zred[D];
 
   const int tid = threadIdx.x;
-  const int wave = tid >> 6;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform
   const int lane = tid & 63;
   const int cg = lane & 15;
   const int tg = lane >> 4;
@@ -293,7 +366,6 @@ __global__ __launch_bounds__(kThreads) void sva_reduce_kernel(
 
   const long long g0 = (long long)blockIdx.x * sp.L;
   const long long g1 = min(g0 + sp.L, sp.total);
-  const long long first_bhc = g0 / geo.Nb;
   const char* kb = (const char*)kp;
   const char* vb = (const char*)vp;
 
@@ -304,7 +376,13 @@ __global__ __launch_bounds__(kThreads) void sva_reduce_kernel(
     const int c = (int)(bhc - (long long)bh * geo.nb);
     const int js = (int)(pos - bhc * geo.Nb);        // block-local token range
     const int je = (int)(seg_end - bhc * geo.Nb);
-    const long long row0 = (long long)bh * geo.N + (long long)c * geo.Nb;  // token row of j = 0
+    // Buffer resources over the block's rows [0, je): rows past the segment
+    // end read as zeros, so a ragged last step needs no masking (zero k
+    // contributes nothing to S or z).
+    const long long blk_off = ((long long)bh * geo.N + (long long)c * geo.Nb) * ROWB;
+    const __amdgpu_buffer_rsrc_t krs = make_rsrc(kb + blk_off, (uint32_t)je * ROWB);
+    const __amdgpu_buffer_rsrc_t vrs = make_rsrc(vb + blk_off, (uint32_t)je * ROWB);
+    const uint32_t lane_col = FPL * cg * ESZ;
 
     floatx4 acc[FPL][FPL];
 #pragma unroll
@@ -315,48 +393,39 @@ __global__ __launch_bounds__(kThreads) void sva_reduce_kernel(
 #pragma unroll
     for (int r = 0; r < FPL; ++r) zacc[r] = 0.f;
 
-    for (int s0 = js + wave * 32; s0 < je; s0 += 4 * 32) {
-      uint32_t kw[8][NW], vw[8][NW];
+    // A step is 32 consecutive tokens; lane (cg, tg) takes tokens 4e + tg,
+    // each load reading 4 consecutive token rows (offsets are immediates).
+    auto load_step = [&](uint32_t (&kw)[8][NW], uint32_t (&vw)[8][NW], int s0) {
+      const uint32_t off = (uint32_t)(s0 + tg) * ROWB + lane_col;
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
-        const int j = s0 + 4 * e + tg;
-        if (j < je) {
-          const long long off = ((row0 + j) * D + FPL * cg) * ESZ;
-          load_words<NW>(kw[e], kb + off);
-          load_words<NW>(vw[e], vb + off);
-        } else {
-#pragma unroll
-          for (int w = 0; w < NW; ++w) { kw[e][w] = 0u; vw[e][w] = 0u; }
-        }
+        buf_load<NW>(kw[e], krs, off + 4 * e * ROWB);
+        buf_load<NW>(vw[e], vrs, off + 4 * e * ROWB);
       }
-      float kf[8][FPL];
+    };
+    auto compute_step = [&](const uint32_t (&kw)[8][NW], const uint32_t (&vw)[8][NW], int s0) {
+      // Coordinates: lanes 0..31 decode the step's 32 tokens (clamped to the
+      // segment so table indices stay in range), every lane fetches those of
+      // its own 8 tokens.
+      uint32_t mine = 0;
+      if (ROPE)
+        mine = decode_packed((uint32_t)(c * geo.Nb + min(s0 + (lane & 31), je - 1)), geo.fHW, geo.fWs);
+      // phi, z and RoPE for token e of this lane, in registers.
+      auto prep_token = [&](int e, float (&kf)[FPL]) {
+        unpack_relu<BF16, FPL>(kf, kw[e]);
 #pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        unpack<BF16, FPL>(kf[e], kw[e]);
+        for (int r = 0; r < FPL; ++r) zacc[r] += kf[r];
+        if (ROPE) {
+          const uint32_t co = (uint32_t)__builtin_amdgcn_ds_bpermute((4 * e + tg) * 4, (int)mine);
 #pragma unroll
-        for (int r = 0; r < FPL; ++r) {
-          kf[e][r] = relu(kf[e][r]);
-          zacc[r] += kf[e][r];
+          for (int pp = 0; pp < NPAIR; ++pp) rotate(kf[2 * pp], kf[2 * pp + 1], tab[pair_entry(pl[pp], co)]);
         }
-      }
-      if (ROPE) {
-#pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          const int j = min(s0 + 4 * e + tg, geo.Nb - 1);
-          const Coord co = decode((uint32_t)(c * geo.Nb + j), geo.fHW, geo.fWs);
-#pragma unroll
-          for (int pp = 0; pp < NPAIR; ++pp) {
-            const float2 cs = tab[pair_entry(pl[pp], co.frame, co.h, co.w)];
-            rotate(kf[e][2 * pp], kf[e][2 * pp + 1], cs);
-          }
-        }
-      }
+      };
       if (BF16) {
+        // V needs no arithmetic: regroup its bf16 halves so slot e of
+        // operand s holds feature FPL*cg + s of token e.  Then k-tilde is
+        // rounded to bf16 two tokens at a time into the A operands.
         u32x4 A[FPL], Bv[FPL];
-#pragma unroll
-        for (int r = 0; r < FPL; ++r)
-#pragma unroll
-          for (int m = 0; m < 4; ++m) A[r][m] = pack_bf16x2(kf[2 * m][r], kf[2 * m + 1][r]);
 #pragma unroll
         for (int s = 0; s < FPL; ++s) {
           const uint32_t sel = (s & 1) ? 0x07060302u : 0x05040100u;
@@ -365,21 +434,58 @@ __global__ __launch_bounds__(kThreads) void sva_reduce_kernel(
             Bv[s][m] = __builtin_amdgcn_perm(vw[2 * m + 1][s >> 1], vw[2 * m][s >> 1], sel);
         }
 #pragma unroll
+        for (int m = 0; m < 4; ++m) {
+          float k0[FPL], k1[FPL];
+          prep_token(2 * m, k0);
+          prep_token(2 * m + 1, k1);
+#pragma unroll
+          for (int r = 0; r < FPL; ++r) A[r][m] = pack_bf16x2(k0[r], k1[r]);
+        }
+#pragma unroll
         for (int r = 0; r < FPL; ++r)
 #pragma unroll
           for (int s = 0; s < FPL; ++s) acc[r][s] = mfma_bf16(A[r], Bv[s], acc[r][s]);
       } else {
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
-          float vf[FPL];
+          float kf[FPL], vf[FPL];
+          prep_token(e, kf);
           unpack<false, FPL>(vf, vw[e]);
 #pragma unroll
           for (int r = 0; r < FPL; ++r)
 #pragma unroll
-            for (int s = 0; s < FPL; ++s) acc[r][s] = mfma_f32(kf[e][r], vf[s], acc[r][s]);
+            for (int s = 0; s < FPL; ++s) acc[r][s] = mfma_f32(kf[r], vf[s], acc[r][s]);
         }
       }
+    };
+
+    // Software pipeline over the wave's steps, three register sets in a
+    // ring: while step k computes, steps k+1 and k+2 are in flight (16 KiB
+    // per wave at bf16, d = 64).  sched_barrier keeps the compiler from
+    // sinking a prefetch below the compute it should overlap.
+    const int s_first = js + wave * STEP;
+    const int nsteps = s_first < je ? (je - s_first + WSTRIDE - 1) / WSTRIDE : 0;
+    uint32_t kA[8][NW], vA[8][NW], kB[8][NW], vB[8][NW], kC[8][NW], vC[8][NW];
+    load_step(kA, vA, s_first);
+    load_step(kB, vB, s_first + WSTRIDE);
+    int k = 0;
+    for (; k + 3 <= nsteps; k += 3) {
+      const int s0 = s_first + k * WSTRIDE;
+      load_step(kC, vC, s0 + 2 * WSTRIDE);
+      __builtin_amdgcn_sched_barrier(0);
+      compute_step(kA, vA, s0);
+      __builtin_amdgcn_sched_barrier(0);
+      load_step(kA, vA, s0 + 3 * WSTRIDE);
+      __builtin_amdgcn_sched_barrier(0);
+      compute_step(kB, vB, s0 + WSTRIDE);
+      __builtin_amdgcn_sched_barrier(0);
+      load_step(kB, vB, s0 + 4 * WSTRIDE);
+      __builtin_amdgcn_sched_barrier(0);
+      compute_step(kC, vC, s0 + 2 * WSTRIDE);
+      __builtin_amdgcn_sched_barrier(0);
     }
+    if (k < nsteps) compute_step(kA, vA, s_first + k * WSTRIDE);
+    if (k + 1 < nsteps) compute_step(kB, vB, s_first + (k + 1) * WSTRIDE);
 
     // Fixed-order reduction over the four lane groups and the four waves.
 #pragma unroll
@@ -407,7 +513,10 @@ __global__ __launch_bounds__(kThreads) void sva_reduce_kernel(
       }
       __syncthreads();
     }
-    float* dst = partials + ((long long)blockIdx.x * sp.maxsub + (bhc - first_bhc)) * E;
+    // Piece (workgroup g, block bhc) goes to slot g + bhc: pieces are ordered
+    // along the flattened token axis, so g + bhc strictly increases from one
+    // piece to the next and the slots of one block's pieces are contiguous.
+    float* dst = partials + ((long long)blockIdx.x + bhc) * E;
     for (int e = tid; e < D * D; e += kThreads) dst[e] = red[e];
     for (int e = tid; e < D; e += kThreads) dst[D * D + e] = zred[e];
     __syncthreads();
@@ -429,13 +538,40 @@ __global__ __launch_bounds__(kThreads) void sva_reduce_kernel(
 
 struct ScanArgs {
   int nb, Nb;
-  long long L;
-  int maxsub;
+  long long L;      // flattened tokens per reduce workgroup
+  int cpl;          // blocks per block-lane
   int has_init;     // S0/z0 given
   int write_frags;  // emit the output-kernel operands
   int write_final;  // emit S_out/z_out
 };
 
+constexpr int kScanLanes = 8;                      // block-lanes per element
+constexpr int kScanElems = kThreads / kScanLanes;  // elements per workgroup
+
+// Sum, in slot order, of the partials of flattened block bhc at element e.
+template <int E>
+__device__ __forceinline__ float block_sum(const float* __restrict__ partials, long long bhc,
+                                           long long L, int Nb, int e) {
+  const long long start = bhc * Nb;
+  const long long gf = start / L, gl = (start + Nb - 1) / L;
+  const float* p = partials + (gf + bhc) * E + e;
+  const int n = (int)(gl - gf + 1);
+  float s = 0.f;
+  int i = 0;
+  for (; i + 4 <= n; i += 4) {
+    const float x0 = p[(long long)i * E], x1 = p[(long long)(i + 1) * E];
+    const float x2 = p[(long long)(i + 2) * E], x3 = p[(long long)(i + 3) * E];
+    s += x0; s += x1; s += x2; s += x3;
+  }
+  for (; i < n; ++i) s += p[(long long)i * E];
+  return s;
+}
+
+// kScanElems elements x kScanLanes block-lanes per workgroup.  Lane ty owns
+// blocks [ty*cpl, ty*cpl + cpl): pass 1 sums them, the lane totals are
+// scanned through LDS in lane order, pass 2 re-sums each block (the
+// partials are L2-resident) and emits the running prefix.  The order of
+// every sum is fixed by (nb, reduce grid), so results are reproducible.
 template <bool BF16, int D>
 __global__ __launch_bounds__(kThreads) void sva_scan_kernel(
     const float* __restrict__ partials, const float* S0, const float* z0, float* S_out,
@@ -443,10 +579,28 @@ __global__ __launch_bounds__(kThreads) void sva_scan_kernel(
   constexpr int E = D * D + D;
   constexpr int FPLa = D / 4;
   constexpr int NKS = BF16 ? D / 32 : D / 4;
-  const int e = blockIdx.x * kThreads + threadIdx.x;
+  __shared__ float lane_tot[kScanLanes][kScanElems];
+  const int tx = threadIdx.x % kScanElems;
+  const int ty = threadIdx.x / kScanElems;
+  const int e = blockIdx.x * kScanElems + tx;
   const int bh = blockIdx.y;
-  if (e >= E) return;
+  const bool active = e < E;
   const bool in_S = e < D * D;
+  const int c_begin = min(ty * a.cpl, a.nb);
+  const int c_end = min(c_begin + a.cpl, a.nb);
+
+  // The initial cache is read before the barrier: S_out may alias S0 and is
+  // written after it.
+  float run = 0.f;
+  if (active && a.has_init)
+    run = in_S ? S0[(long long)bh * D * D + e] : z0[(long long)bh * D + (e - D * D)];
+  float tot = 0.f;
+  if (active)
+    for (int c = c_begin; c < c_end; ++c) tot += block_sum<E>(partials, (long long)bh * a.nb + c, a.L, a.Nb, e);
+  lane_tot[ty][tx] = tot;
+  __syncthreads();
+  if (!active) return;
+  for (int l = 0; l < ty; ++l) run += lane_tot[l][tx];
 
   int frag_off = 0;
   if (in_S) {
@@ -458,29 +612,21 @@ __global__ __launch_bounds__(kThreads) void sva_scan_kernel(
     if (BF16) frag_off = ((rt * NKS + (wi >> 3)) * 64 + lane) * 8 + (wi & 7);
     else frag_off = (rt * NKS + wi) * 64 + lane;
   }
-
-  float acc = 0.f;
-  if (a.has_init) acc = in_S ? S0[(long long)bh * D * D + e] : z0[(long long)bh * D + (e - D * D)];
-  for (int c = 0; c < a.nb; ++c) {
+  for (int c = c_begin; c < c_end; ++c) {
     const long long bhc = (long long)bh * a.nb + c;
-    const long long start = bhc * a.Nb;
-    const long long gf = start / a.L, gl = (start + a.Nb - 1) / a.L;
-    for (long long g = gf; g <= gl; ++g) {
-      const long long slot = g * a.maxsub + (bhc - (g * a.L) / a.Nb);
-      acc += partials[slot * E + e];
-    }
+    run += block_sum<E>(partials, bhc, a.L, a.Nb, e);
     if (a.write_frags) {
       if (in_S) {
-        if (BF16) ((__bf16*)frags)[bhc * D * D + frag_off] = (__bf16)acc;
-        else ((float*)frags)[bhc * D * D + frag_off] = acc;
+        if (BF16) ((__bf16*)frags)[bhc * D * D + frag_off] = (__bf16)run;
+        else ((float*)frags)[bhc * D * D + frag_off] = run;
       } else {
-        zc[bhc * D + (e - D * D)] = acc;
+        zc[bhc * D + (e - D * D)] = run;
       }
     }
   }
-  if (a.write_final) {
-    if (in_S) S_out[(long long)bh * D * D + e] = acc;
-    else z_out[(long long)bh * D + (e - D * D)] = acc;
+  if (a.write_final && c_begin < c_end && c_end == a.nb) {
+    if (in_S) S_out[(long long)bh * D * D + e] = run;
+    else z_out[(long long)bh * D + (e - D * D)] = run;
   }
 }
 
@@ -511,7 +657,7 @@ __global__ __launch_bounds__(kThreads) void sva_apply_kernel(
   __shared__ uint4 fstage[FRAG_U4];
 
   const int tid = threadIdx.x;
-  const int wave = tid >> 6;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform
   const int lane = tid & 63;
   const int g = lane >> 4;
   const int row = lane & 15;
@@ -571,31 +717,27 @@ __global__ __launch_bounds__(kThreads) void sva_apply_kernel(
         for (int ks = 0; ks < NKS; ++ks) A32[rt][ks] = fs[(rt * NKS + ks) * 64 + lane];
     }
 
-    for (int t0 = js + wave * 16; t0 < je; t0 += 4 * 16) {
-      const int j = t0 + row;
-      const bool valid = j < je;
-      const long long off = ((row0 + j) * D + FPLa * g) * ESZ;
-      uint32_t qw[NW];
-      if (valid) load_words<NW>(qw, qb + off);
-      else {
-#pragma unroll
-        for (int w = 0; w < NW; ++w) qw[w] = 0u;
-      }
+    // Buffer resources over the block's rows [0, je): loads past the segment
+    // end read zeros and stores past it are dropped, so ragged tiles need no
+    // branches.
+    const long long blk_off = row0 * (D * ESZ);
+    const __amdgpu_buffer_rsrc_t qrs = make_rsrc(qb + blk_off, (uint32_t)je * (D * ESZ));
+    const __amdgpu_buffer_rsrc_t ors = make_rsrc(ob + blk_off, (uint32_t)je * (D * ESZ));
+    const uint32_t lane_col = FPLa * g * ESZ;
+    auto load_tile = [&](uint32_t (&qw)[NW], int t) {
+      buf_load<NW>(qw, qrs, (uint32_t)(t + row) * (D * ESZ) + lane_col);
+    };
+    auto compute_tile = [&](const uint32_t (&qw)[NW], int t) {
+      const int j = t + row;
       float qf[FPLa];
-      unpack<BF16, FPLa>(qf, qw);
+      unpack_relu<BF16, FPLa>(qf, qw);
       float den = 0.f;
 #pragma unroll
-      for (int m = 0; m < FPLa; ++m) {
-        qf[m] = relu(qf[m]);
-        den += qf[m] * z[m];
-      }
+      for (int m = 0; m < FPLa; ++m) den += qf[m] * z[m];
       if (ROPE) {
-        const Coord co = decode((uint32_t)(c * geo.Nb + min(j, geo.Nb - 1)), geo.fHW, geo.fWs);
+        const uint32_t co = decode_packed((uint32_t)(c * geo.Nb + min(j, je - 1)), geo.fHW, geo.fWs);
 #pragma unroll
-        for (int pp = 0; pp < NPAIR; ++pp) {
-          const float2 cs = tab[pair_entry(pl[pp], co.frame, co.h, co.w)];
-          rotate(qf[2 * pp], qf[2 * pp + 1], cs);
-        }
+        for (int pp = 0; pp < NPAIR; ++pp) rotate(qf[2 * pp], qf[2 * pp + 1], tab[pair_entry(pl[pp], co)]);
       }
       floatx4 acc[NRT];
 #pragma unroll
@@ -617,24 +759,54 @@ __global__ __launch_bounds__(kThreads) void sva_apply_kernel(
       }
       den += __shfl_xor(den, 16);
       den += __shfl_xor(den, 32);
-      const float inv = 1.0f / (den + eps);
-      if (valid) {
-        uint32_t ow[NW];
-        if (BF16) {
+      // v_rcp_f32 (1 ulp) for bf16 outputs; a correctly rounded divide for fp32.
+      const float inv = BF16 ? __builtin_amdgcn_rcpf(den + eps) : 1.0f / (den + eps);
+      uint32_t ow[NW];
+      if (BF16) {
 #pragma unroll
-          for (int rt = 0; rt < NRT; ++rt) {
-            ow[2 * rt] = pack_bf16x2(acc[rt][0] * inv, acc[rt][1] * inv);
-            ow[2 * rt + 1] = pack_bf16x2(acc[rt][2] * inv, acc[rt][3] * inv);
-          }
-        } else {
-#pragma unroll
-          for (int rt = 0; rt < NRT; ++rt)
-#pragma unroll
-            for (int i = 0; i < 4; ++i) ow[4 * rt + i] = __float_as_uint(acc[rt][i] * inv);
+        for (int rt = 0; rt < NRT; ++rt) {
+          ow[2 * rt] = pack_bf16x2(acc[rt][0] * inv, acc[rt][1] * inv);
+          ow[2 * rt + 1] = pack_bf16x2(acc[rt][2] * inv, acc[rt][3] * inv);
         }
-        store_words<NW>(ob + off, ow);
+      } else {
+#pragma unroll
+        for (int rt = 0; rt < NRT; ++rt)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) ow[4 * rt + i] = __float_as_uint(acc[rt][i] * inv);
       }
+      buf_store<NW>(ors, (uint32_t)j * (D * ESZ) + lane_col, ow);
+    };
+
+    // Four 16-token tiles per wave step (8 KiB of q at bf16, d = 64),
+    // software-pipelined as in the reduction with two register sets: step
+    // k+1's loads are issued before step k computes.
+    constexpr int TPS = 4;
+    constexpr int WSTRIDE = 16 * TPS * (kThreads / 64);
+    const int t_first = js + wave * 16 * TPS;
+    const int nsteps = t_first < je ? (je - t_first + WSTRIDE - 1) / WSTRIDE : 0;
+    uint32_t qa[TPS][NW], qb[TPS][NW];
+    auto load_stepq = [&](uint32_t (&x)[TPS][NW], int t) {
+#pragma unroll
+      for (int i = 0; i < TPS; ++i) load_tile(x[i], t + 16 * i);
+    };
+    auto compute_stepq = [&](const uint32_t (&x)[TPS][NW], int t) {
+#pragma unroll
+      for (int i = 0; i < TPS; ++i) compute_tile(x[i], t + 16 * i);
+    };
+    load_stepq(qa, t_first);
+    int k = 0;
+    for (; k + 2 <= nsteps; k += 2) {
+      const int t0 = t_first + k * WSTRIDE;
+      load_stepq(qb, t0 + WSTRIDE);
+      __builtin_amdgcn_sched_barrier(0);
+      compute_stepq(qa, t0);
+      __builtin_amdgcn_sched_barrier(0);
+      load_stepq(qa, t0 + 2 * WSTRIDE);
+      __builtin_amdgcn_sched_barrier(0);
+      compute_stepq(qb, t0 + WSTRIDE);
+      __builtin_amdgcn_sched_barrier(0);
     }
+    if (k < nsteps) compute_stepq(qa, t_first + k * WSTRIDE);
     pos = seg_end;
   }
 }
@@ -657,20 +829,15 @@ __global__ __launch_bounds__(kThreads) void sva_prep_kernel(
   uint32_t w[D * ESZ / 4];
   load_words<D * ESZ / 4>(w, (const char*)xp + t * D * ESZ);
   float f[D];
-  unpack<BF16, D>(f, w);
-#pragma unroll
-  for (int i = 0; i < D; ++i) f[i] = relu(f[i]);
+  unpack_relu<BF16, D>(f, w);
   if (xphi) {
 #pragma unroll
     for (int i = 0; i < D; i += 4) *(float4*)(xphi + t * D + i) = make_float4(f[i], f[i + 1], f[i + 2], f[i + 3]);
   }
   if (ROPE) {
-    const Coord co = decode((uint32_t)n, geo.fHW, geo.fWs);
+    const uint32_t co = decode_packed((uint32_t)n, geo.fHW, geo.fWs);
 #pragma unroll
-    for (int p = 0; p < D / 2; ++p) {
-      const PairLoc pl = pair_loc(p, ra);
-      rotate(f[2 * p], f[2 * p + 1], tab[pair_entry(pl, co.frame, co.h, co.w)]);
-    }
+    for (int p = 0; p < D / 2; ++p) rotate(f[2 * p], f[2 * p + 1], tab[pair_entry(pair_loc(p, ra), co)]);
   }
 #pragma unroll
   for (int i = 0; i < D; i += 4) *(float4*)(xr + t * D + i) = make_float4(f[i], f[i + 1], f[i + 2], f[i + 3]);
@@ -691,8 +858,8 @@ struct Plan {
   size_t off_partials, off_frags, off_zc, ws_bytes;
 };
 
-constexpr long long kRedWorkgroups = 512;   // 2 per CU on 256 CUs
-constexpr long long kAppWorkgroups = 1024;  // 4 per CU on 256 CUs
+constexpr long long kRedWorkgroupsMax = 1024;  // bounds the partials workspace
+constexpr long long kAppWorkgroupsMax = 4096;
 constexpr long long kMinTokensPerWG = 256;
 
 size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
@@ -704,7 +871,7 @@ bool overlaps(const void* a, size_t an, const void* b, size_t bn) {
   return x < y + bn && y < x + an;
 }
 
-SplitArgs make_split(long long total, long long target_wg, int Nb, int* G_out) {
+SplitArgs make_split(long long total, long long target_wg, int* G_out) {
   long long G = target_wg;
   const long long g_min_tokens = (total + kMinTokensPerWG - 1) / kMinTokensPerWG;
   if (G > g_min_tokens) G = g_min_tokens;
@@ -713,10 +880,30 @@ SplitArgs make_split(long long total, long long target_wg, int Nb, int* G_out) {
   s.total = total;
   s.L = (total + G - 1) / G;
   G = (total + s.L - 1) / s.L;
-  s.maxsub = (int)((s.L - 1) / Nb + 2);
-  s.pad_ = 0;
   *G_out = (int)G;
   return s;
+}
+
+// How many workgroups of `fn` the current device holds at once (CUs times
+// workgroups per CU for its registers and LDS).  Launching exactly that many,
+// each with an equal token range, keeps every CU streaming until the end.
+int resident_workgroups(const void* fn, size_t lds) {
+  static std::mutex mu;
+  static std::map<std::tuple<int, const void*, size_t>, int> cache;
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return 512;
+  const auto key = std::make_tuple(dev, fn, lds);
+  std::lock_guard<std::mutex> lock(mu);
+  auto it = cache.find(key);
+  if (it != cache.end()) return it->second;
+  int cus = 0, per = 0;
+  if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus < 1)
+    cus = 256;
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per, fn, kThreads, lds) != hipSuccess || per < 1)
+    per = 1;
+  const int n = cus * per;
+  cache[key] = n;
+  return n;
 }
 
 sva_status validate_desc(const sva_desc* d, bool one_block) {
@@ -733,6 +920,9 @@ sva_status validate_desc(const sva_desc* d, bool one_block) {
   const long long HW = (long long)d->Hs * d->Ws;
   const long long N = HW * d->T;
   if (N * d->d >= (1ll << 31)) return SVA_ERR_UNSUPPORTED;  // per-sequence 32-bit indexing
+  // buffer offsets within a block are 32-bit byte offsets
+  if ((long long)d->frames_per_block * HW * d->d * (d->dtype == SVA_BF16 ? 2 : 4) >= (1ll << 31))
+    return SVA_ERR_UNSUPPORTED;
   if ((long long)d->B * d->H * N >= (1ll << 40)) return SVA_ERR_UNSUPPORTED;
   if (d->t0 > (1 << 24)) return SVA_ERR_UNSUPPORTED;
   if (d->rope) {
@@ -743,6 +933,8 @@ sva_status validate_desc(const sva_desc* d, bool one_block) {
     const long long entries = (long long)d->T * (d->rope_dt / 2) +
                               (long long)d->Hs * (d->rope_dh / 2) + (long long)d->Ws * (d->rope_dw / 2);
     if (entries > kMaxTableEntries) return SVA_ERR_UNSUPPORTED;
+    // packed token coordinates: frame and h in 11 bits, w in 10
+    if (d->T > 2048 || d->Hs > 2048 || d->Ws > 1024) return SVA_ERR_UNSUPPORTED;
   }
   return SVA_OK;
 }
@@ -762,6 +954,9 @@ Plan make_plan(const sva_desc* d) {
   p.geo.Nb = p.Nb;
   p.geo.nb = p.nb;
   p.geo.BH = p.BH;
+  p.geo.T = d->T;
+  p.geo.Hs = d->Hs;
+  p.geo.Ws = d->Ws;
   p.geo.fHW = make_fastdiv((uint32_t)HW);
   p.geo.fWs = make_fastdiv((uint32_t)d->Ws);
   if (p.rope) {
@@ -782,13 +977,16 @@ Plan make_plan(const sva_desc* d) {
     p.tab_bytes = (size_t)ra.n_entries * sizeof(float2);
   }
   const long long total = (long long)p.BH * p.N;
-  p.red = make_split(total, kRedWorkgroups, p.Nb, &p.G_red);
-  p.app = make_split(total, kAppWorkgroups, p.Nb, &p.G_app);
+  // Grids are fixed at launch from the device's occupancy (plan_grids); the
+  // workspace is sized for the largest reduce grid.  Piece (g, block) of the
+  // reduce lives in slot g + block, so G + B*H*nb slots always suffice.
+  p.red = make_split(total, kRedWorkgroupsMax, &p.G_red);
+  p.app = make_split(total, kAppWorkgroupsMax, &p.G_app);
   const size_t E = (size_t)p.D * p.D + p.D;
   const size_t esz = p.bf16 ? 2 : 4;
   size_t off = 0;
   p.off_partials = off;
-  off = align256(off + (size_t)p.G_red * p.red.maxsub * E * sizeof(float));
+  off = align256(off + (size_t)(kRedWorkgroupsMax + (long long)p.BH * p.nb) * E * sizeof(float));
   p.off_frags = off;
   off = align256(off + (size_t)p.BH * p.nb * p.D * p.D * esz);
   p.off_zc = off;
@@ -815,7 +1013,7 @@ hipError_t launch_scan(const Plan& p, const float* partials, const float* S0, co
   a.nb = p.nb;
   a.Nb = p.Nb;
   a.L = p.red.L;
-  a.maxsub = p.red.maxsub;
+  a.cpl = (p.nb + kScanLanes - 1) / kScanLanes;
   a.has_init = S0 != nullptr;
   a.write_frags = write_frags;
   a.write_final = S_out != nullptr;
@@ -823,7 +1021,7 @@ hipError_t launch_scan(const Plan& p, const float* partials, const float* S0, co
                   (void*)&frags, (void*)&zc, &a};
   const int E = D * D + D;
   return hipLaunchKernel((const void*)&sva_scan_kernel<BF16, D>,
-                         dim3((E + kThreads - 1) / kThreads, p.BH), dim3(kThreads), args, 0, st);
+                         dim3((E + kScanElems - 1) / kScanElems, p.BH), dim3(kThreads), args, 0, st);
 }
 
 template <bool BF16, int D, bool ROPE>
@@ -864,6 +1062,19 @@ hipError_t launch_prep(const Plan& p, const void* x, float* xr, float* xphi, hip
   ((P).bf16 ? ((P).D == 64 ? FN<true, 64>(__VA_ARGS__) : FN<true, 32>(__VA_ARGS__))      \
             : ((P).D == 64 ? FN<false, 64>(__VA_ARGS__) : FN<false, 32>(__VA_ARGS__)))
 
+template <bool BF16, int D, bool ROPE>
+int plan_grids_t(Plan* p) {
+  const long long total = (long long)p->BH * p->N;
+  const size_t lds = ROPE ? p->tab_bytes : 0;
+  const long long r = resident_workgroups((const void*)&sva_reduce_kernel<BF16, D, ROPE>, lds);
+  const long long a = resident_workgroups((const void*)&sva_apply_kernel<BF16, D, ROPE>, lds);
+  p->red = make_split(total, r < kRedWorkgroupsMax ? r : kRedWorkgroupsMax, &p->G_red);
+  p->app = make_split(total, a < kAppWorkgroupsMax ? a : kAppWorkgroupsMax, &p->G_app);
+  return 0;
+}
+
+void plan_grids(Plan* p) { (void)SVA_DISPATCH(*p, plan_grids_t, p); }
+
 size_t qkv_bytes(const Plan& p) { return (size_t)p.BH * p.N * p.D * (p.bf16 ? 2 : 4); }
 
 sva_status check_common(const sva_desc* d, bool one_block, Plan* p) {
@@ -897,6 +1108,7 @@ sva_status run_fwd(const sva_desc* desc, const void* q, const void* k, const voi
       if (!events[i]) return SVA_ERR_INVALID_ARG;
   }
 
+  plan_grids(&p);
   hipStream_t st = (hipStream_t)stream;
   char* wsb = (char*)ws;
   float* partials = (float*)(wsb + p.off_partials);
@@ -988,6 +1200,7 @@ sva_status sva_block_cache_commit(const sva_desc* desc, float* S, float* z, cons
   if (!is_aligned16(S) || !is_aligned16(z) || !is_aligned16(k) || !is_aligned16(v))
     return SVA_ERR_INVALID_ARG;
   if (!ws || ws_bytes < p.ws_bytes || !is_aligned16(ws)) return SVA_ERR_WORKSPACE;
+  plan_grids(&p);
   hipStream_t st = (hipStream_t)stream;
   char* wsb = (char*)ws;
   float* partials = (float*)(wsb + p.off_partials);
