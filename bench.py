@@ -7,10 +7,10 @@ timing; two buffer sets alternate so the 256 MB Infinity Cache cannot hold a
 step's working set.
 
 Prints one JSON line.  `value` = tokens/s over all heads (B*N tokens per
-step / step time).  The `roofline` object rates the dominant kernel by its
-algorithmic bytes (its inputs read once + its outputs written once) over its
-average duration, timed live with HIP events recorded by the library on the
-stream it launches on.
+step / step time) over K uninstrumented steps.  The `roofline` object rates
+the dominant kernel by its algorithmic bytes (its inputs read once + its
+outputs written once) over its average duration, timed live with HIP events
+that the library records on its launch stream during K further steps.
 """
 from __future__ import annotations
 
@@ -26,6 +26,19 @@ if ROOT not in sys.path:
     sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0  # MI355X HBM3E, GB/s
+KERNEL_SRC = os.path.join(ROOT, "block_causal_linear_phi_amd", "csrc", "sva.hip")
+PROFILES = os.path.join(ROOT, "profiles")
+CALIB_KERNEL = "MulFunctor"  # the plain streaming kernel of copy_calibration()
+
+
+def source_sha256() -> str:
+    import hashlib
+    with open(KERNEL_SRC, "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()
+
+
+def traffic_file(workload: str) -> str:
+    return os.path.join(PROFILES, f"sva_traffic_{workload}.json")
 
 
 class HipEvents:
@@ -75,7 +88,7 @@ def gpu_leg(w, steps: int, warmup: int, sets: int):
     outs = [torch.empty(shape, dtype=tdt, device=dev) for _ in range(sets)]
     desc = sva.make_desc(w.B, w.H, w.d, (w.T, w.Hs, w.Ws), w.F, t0=w.t0, rope=w.rope, split=w.split,
                          base=w.base, eps=w.eps, dtype=sva.SVA_BF16 if w.dtype == "bf16" else sva.SVA_F32)
-    ws = torch.empty(sva.sva_lin_attn_fwd_workspace(desc), dtype=torch.uint8, device=dev)
+    ws = torch.zeros(sva.sva_lin_attn_fwd_workspace(desc), dtype=torch.uint8, device=dev)
     stream = torch.cuda.current_stream()
     hip = HipEvents()
     evs = [[hip.create() for _ in range(4)] for _ in range(steps)]
@@ -90,14 +103,22 @@ def gpu_leg(w, steps: int, warmup: int, sets: int):
     for i in range(warmup):
         step(i)
     torch.cuda.synchronize()
+    # Timed region: K uninstrumented steps between two synchronisations.
     t_start = torch.cuda.Event(enable_timing=True)
     t_end = torch.cuda.Event(enable_timing=True)
     t_start.record(stream)
     for i in range(steps):
-        step(warmup + i, evs[i])
+        step(warmup + i)
     t_end.record(stream)
     torch.cuda.synchronize()
     total_ms = t_start.elapsed_time(t_end)
+    # Kernel timing: the same K steps again, with the library recording HIP
+    # events on its launch stream around each kernel.  A recorded event costs
+    # a few microseconds of GPU time, so these steps are kept out of the
+    # throughput figure above.
+    for i in range(steps):
+        step(warmup + steps + i, evs[i])
+    torch.cuda.synchronize()
     per = {"reduce": [], "scan": [], "apply": []}
     for e in evs:
         per["reduce"].append(hip.elapsed_ms(e[0], e[1]))
@@ -159,6 +180,76 @@ def cpu_leg(w, reps: int):
                       f"(BLAS threads {blas_threads} of {cores} host cores; elementwise steps single-threaded)"}
 
 
+def _short_kernel(name: str) -> str:
+    for k in ("sva_reduce_kernel", "sva_scan_kernel", "sva_apply_kernel", "sva_prep_kernel"):
+        if k in name:
+            return k.replace("sva_", "").replace("_kernel", "")
+    return name.split("(")[0][-60:]
+
+
+def summarize_profile(args):
+    """Turn rocprofv3 CSV output into the committed summaries: a kernel-time
+    table and per-launch HBM traffic (FETCH_SIZE / WRITE_SIZE scaled by what
+    the same counters read for the plain streaming kernel of known size)."""
+    import csv
+    import glob
+    from collections import defaultdict
+
+    def one(pattern):
+        hits = glob.glob(os.path.join(pattern, "**", "*.csv"), recursive=True)
+        return hits
+
+    stats = [f for f in one(args.trace_dir) if f.endswith("kernel_stats.csv")][0]
+    rows = list(csv.DictReader(open(stats)))
+    counters = defaultdict(list)
+    for d, cname in ((args.fetch_dir, "FETCH_SIZE"), (args.write_dir, "WRITE_SIZE")):
+        f = [x for x in one(d) if x.endswith("counter_collection.csv")][0]
+        for r in csv.DictReader(open(f)):
+            if r["Counter_Name"] == cname:
+                counters[(r["Kernel_Name"], cname)].append(float(r["Counter_Value"]))
+    calib_bytes = args.calib_mib * (1 << 20)
+
+    def mean_for(substr, cname):
+        vals = [v for (k, c), vs in counters.items() if substr in k and c == cname for v in vs]
+        return sum(vals) / len(vals) if vals else None
+
+    f_scale = calib_bytes / (mean_for(CALIB_KERNEL, "FETCH_SIZE") * 1024)
+    w_scale = calib_bytes / (mean_for(CALIB_KERNEL, "WRITE_SIZE") * 1024)
+    traffic = {}
+    for k in ("reduce", "scan", "apply"):
+        fk, wk = mean_for(f"sva_{k}_kernel", "FETCH_SIZE"), mean_for(f"sva_{k}_kernel", "WRITE_SIZE")
+        if fk is None or wk is None:
+            continue
+        traffic[k] = {"fetch_kib": fk, "write_kib": wk, "read_bytes": fk * 1024 * f_scale,
+                      "write_bytes": wk * 1024 * w_scale, "bytes": fk * 1024 * f_scale + wk * 1024 * w_scale}
+    doc = {"workload": args.workload, "source_sha256": source_sha256(), "fetch_scale": f_scale,
+           "write_scale": w_scale, "calibration": f"{CALIB_KERNEL} kernel reading and writing "
+                                                  f"{calib_bytes} bytes", "per_launch": traffic,
+           "commands": args.commands}
+    os.makedirs(PROFILES, exist_ok=True)
+    with open(traffic_file(args.workload), "w") as f:
+        json.dump(doc, f, indent=1)
+    lines = [f"# Kernel times and HBM traffic, {args.workload} workload", "",
+             "Commands (run from the repository root on one MI355X):", ""]
+    lines += [f"    {c}" for c in args.commands]
+    lines += ["", "## rocprofv3 --kernel-trace --stats", "",
+              "| kernel | calls | average us | min us | max us | % |", "|---|---|---|---|---|---|"]
+    for r in rows:
+        lines.append(f"| {_short_kernel(r['Name'])} | {r['Calls']} | {float(r['AverageNs']) / 1e3:.2f} | "
+                     f"{float(r['MinNs']) / 1e3:.2f} | {float(r['MaxNs']) / 1e3:.2f} | {float(r['Percentage']):.1f} |")
+    lines += ["", "## HBM traffic per launch (FETCH_SIZE, WRITE_SIZE)", "",
+              f"Scale factors from the {CALIB_KERNEL} streaming kernel over {calib_bytes} bytes: "
+              f"FETCH_SIZE x {f_scale:.4f}, WRITE_SIZE x {w_scale:.4f}.", "",
+              "| kernel | FETCH_SIZE KiB | WRITE_SIZE KiB | read MB | write MB | total MB |", "|---|---|---|---|---|---|"]
+    for k, t in traffic.items():
+        lines.append(f"| {k} | {t['fetch_kib']:.0f} | {t['write_kib']:.0f} | {t['read_bytes'] / 1e6:.1f} | "
+                     f"{t['write_bytes'] / 1e6:.1f} | {t['bytes'] / 1e6:.1f} |")
+    lines += ["", f"Kernel source sha256: `{doc['source_sha256']}`", ""]
+    with open(os.path.join(PROFILES, f"sva_kernels_{args.workload}.md"), "w") as f:
+        f.write("\n".join(lines))
+    print(json.dumps({"summarized": args.workload, "traffic": traffic}))
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -170,7 +261,17 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-calib", type=int, default=0, metavar="MIB",
                     help="also run a plain fp32 streaming kernel over MIB MiB (counter calibration)")
+    ap.add_argument("--summarize-profile", action="store_true",
+                    help="write profiles/ summaries from rocprofv3 output directories, then exit")
+    ap.add_argument("--trace-dir")
+    ap.add_argument("--fetch-dir")
+    ap.add_argument("--write-dir")
+    ap.add_argument("--calib-mib", type=int, default=256)
+    ap.add_argument("--commands", nargs="*", default=[])
     args = ap.parse_args()
+    if args.summarize_profile:
+        summarize_profile(args)
+        return
     if args.gpus != 1:
         print("bench.py measures one GPU: this build has no multi-GPU path (heads and samples shard "
               "with no communication; see the design notes). Run with --gpus 1.", file=sys.stderr)
@@ -188,6 +289,14 @@ def main():
     avg = {k: sum(v) / len(v) for k, v in per.items()}
     dom = "reduce" if avg["reduce"] >= avg["apply"] else "apply"
     achieved = alg_bytes[dom] / (avg[dom] * 1e-3) / 1e9
+    traffic = None
+    try:
+        with open(traffic_file(w.name)) as f:
+            prof = json.load(f)
+        if prof.get("source_sha256") == source_sha256() and dom in prof.get("per_launch", {}):
+            traffic = prof["per_launch"][dom]["bytes"] / 1e9  # GB per launch, from the counters
+    except (OSError, ValueError):
+        traffic = None
     step_bytes = 4 * elems * esz
     line = {
         "metric": "tokens/s (all heads) block-causal linear attn fwd; % of HBM peak",
@@ -208,7 +317,8 @@ def main():
                    "B": w.B, "H": w.H, "d": w.d, "tokens": w.N, "blocks": w.nb},
         "hbm_frac_step": step_bytes / (ms_per_step * 1e-3) / (HBM_PEAK_GBS * 1e9),
         "roofline": {"bound": "hbm", "kernel": dom, "achieved": achieved, "peak": HBM_PEAK_GBS,
-                     "unit": "GB/s", "frac": achieved / HBM_PEAK_GBS, "traffic": None},
+                     "unit": "GB/s", "frac": achieved / HBM_PEAK_GBS, "traffic": traffic,
+                     "traffic_unit": "GB per launch", "alg_bytes": alg_bytes[dom] / 1e9},
         "kernels_us": {k: round(v * 1e3, 2) for k, v in avg.items()},
         "kernels_gbs": {k: round(alg_bytes[k] / (avg[k] * 1e-3) / 1e9, 1) for k in ("reduce", "apply")},
     }

@@ -294,6 +294,26 @@ __device__ __forceinline__ void unpack_relu(float* f, const uint32_t* w) {
   }
 }
 
+// Workgroup barrier for LDS data only.  __syncthreads() also orders global
+// memory, which on gfx9 means waiting for every outstanding vector load; this
+// waits for the wave's LDS operations (lgkmcnt(0), gfx9 s_waitcnt encoding
+// 0xC07F leaves vmcnt and expcnt at their maxima) so that prefetched global
+// loads stay in flight across the barrier.
+__device__ __forceinline__ void lds_barrier() {
+  __builtin_amdgcn_s_waitcnt(0xC07F);
+  __builtin_amdgcn_s_barrier();
+}
+
+// Sum of x over the four 16-lane rows of a wavefront, in every lane, with the
+// gfx950 lane-swap instructions (no LDS round trip): rows (0+1, 2+3), then
+// halves.  Every lane adds the same operands in the same order.
+__device__ __forceinline__ float sum_over_rows(float x) {
+  auto r16 = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  const float y = __uint_as_float(r16[0]) + __uint_as_float(r16[1]);
+  auto r32 = __builtin_amdgcn_permlane32_swap(__float_as_uint(y), __float_as_uint(y), false, false);
+  return __uint_as_float(r32[0]) + __uint_as_float(r32[1]);
+}
+
 __device__ __forceinline__ floatx4 mfma_bf16(const u32x4& a, const u32x4& b, floatx4 c) {
   return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, a),
                                                  __builtin_bit_cast(bf16x8_t, b), c, 0, 0, 0);
@@ -358,11 +378,9 @@ __global__ __launch_bounds__(kThreads, BF16 ? 2 : 1) void sva_reduce_kernel(
 
   PairLoc pl[NPAIR > 0 ? NPAIR : 1];
   if (ROPE) {
-    build_rope_table<!BF16>(tab, ra);
 #pragma unroll
     for (int pp = 0; pp < NPAIR; ++pp) pl[pp] = pair_loc(NPAIR * cg + pp, ra);
   }
-  __syncthreads();
 
   const long long g0 = (long long)blockIdx.x * sp.L;
   const long long g1 = min(g0 + sp.L, sp.total);
@@ -468,6 +486,10 @@ __global__ __launch_bounds__(kThreads, BF16 ? 2 : 1) void sva_reduce_kernel(
     uint32_t kA[8][NW], vA[8][NW], kB[8][NW], vB[8][NW], kC[8][NW], vC[8][NW];
     load_step(kA, vA, s_first);
     load_step(kB, vB, s_first + WSTRIDE);
+    __builtin_amdgcn_sched_barrier(0);
+    // The RoPE table is built while the first loads are in flight.
+    if (ROPE && pos == g0) build_rope_table<!BF16>(tab, ra);
+    lds_barrier();
     int k = 0;
     for (; k + 3 <= nsteps; k += 3) {
       const int s0 = s_first + k * WSTRIDE;
@@ -489,12 +511,7 @@ __global__ __launch_bounds__(kThreads, BF16 ? 2 : 1) void sva_reduce_kernel(
 
     // Fixed-order reduction over the four lane groups and the four waves.
 #pragma unroll
-    for (int r = 0; r < FPL; ++r) {
-      float z = zacc[r];
-      z += __shfl_xor(z, 16);
-      z += __shfl_xor(z, 32);
-      zacc[r] = z;
-    }
+    for (int r = 0; r < FPL; ++r) zacc[r] = sum_over_rows(zacc[r]);
     for (int w = 0; w < kThreads / 64; ++w) {
       if (wave == w) {
 #pragma unroll
@@ -511,7 +528,7 @@ __global__ __launch_bounds__(kThreads, BF16 ? 2 : 1) void sva_reduce_kernel(
             zred[FPL * cg + r] = (w == 0) ? zacc[r] : zred[FPL * cg + r] + zacc[r];
         }
       }
-      __syncthreads();
+      lds_barrier();
     }
     // Piece (workgroup g, block bhc) goes to slot g + bhc: pieces are ordered
     // along the flattened token axis, so g + bhc strictly increases from one
@@ -519,7 +536,7 @@ __global__ __launch_bounds__(kThreads, BF16 ? 2 : 1) void sva_reduce_kernel(
     float* dst = partials + ((long long)blockIdx.x + bhc) * E;
     for (int e = tid; e < D * D; e += kThreads) dst[e] = red[e];
     for (int e = tid; e < D; e += kThreads) dst[D * D + e] = zred[e];
-    __syncthreads();
+    // `red` is next written after the next segment's barrier.
     pos = seg_end;
   }
 }
@@ -528,12 +545,13 @@ __global__ __launch_bounds__(kThreads, BF16 ? 2 : 1) void sva_reduce_kernel(
 // Kernel 2: inclusive prefix over blocks, fixed order
 //
 // One thread per state element (d*d entries of S, then d of z) per (b, h).
-// Output-kernel A operand layout (the MFMA computes out^T = S^T qr^T):
-//   bf16: fragment (rt, ks), lane l, slot e holds
-//         S[FPLa*(l/16) + 8*ks + e][fo(rt, l%16)],   FPLa = d/4
-//   fp32: fragment (rt, ks), lane l holds S[FPLa*(l/16) + ks][fo(rt, l%16)]
-//   with fo(rt, r) = FPLa*(r/4) + 4*rt + r%4, so that accumulator rt of lane
-//   l holds output features FPLa*(l/16) + 4*rt + (0..3).
+// Output-kernel A operand layout (the MFMA computes out^T = S^T qr^T): for
+// k-step ks, accumulator rt and lane l = 16*g + r, the operand holds
+// S[fi][fo] with fi = feat(g, k-slot) of the output kernel and
+//   bf16: fo = 32*(rt/2) + 8*(r/4) + 4*(rt%2) + r%4
+//   fp32: fo = 16*rt + r
+// so that accumulator rt of lane l holds the output features the lane stores
+// in one contiguous 16-byte piece.
 // ---------------------------------------------------------------------------
 
 struct ScanArgs {
@@ -604,13 +622,20 @@ __global__ __launch_bounds__(kThreads) void sva_scan_kernel(
 
   int frag_off = 0;
   if (in_S) {
+    // Inverse of the output kernel's maps: input feature fi is local element
+    // m of lane group g (k-slot of k-step ks); output feature fo is row r of
+    // accumulator rt.
     const int fi = e / D, fo = e % D;
-    const int g = fi / FPLa, wi = fi % FPLa;
-    const int rem = fo % FPLa;
-    const int rt = rem >> 2;
-    const int lane = 16 * g + 4 * (fo / FPLa) + (rem & 3);
-    if (BF16) frag_off = ((rt * NKS + (wi >> 3)) * 64 + lane) * 8 + (wi & 7);
-    else frag_off = (rt * NKS + wi) * 64 + lane;
+    if (BF16) {
+      const int g = (fi & 31) >> 3, ks = fi >> 5, el = fi & 7;
+      const int rt = 2 * (fo >> 5) + ((fo & 7) >> 2);
+      const int r = 4 * ((fo & 31) >> 3) + (fo & 3);
+      frag_off = ((rt * NKS + ks) * 64 + 16 * g + r) * 8 + el;
+    } else {
+      const int g = (fi & 15) >> 2, ks = 4 * (fi >> 4) + (fi & 3);
+      const int rt = fo >> 4, r = fo & 15;
+      frag_off = (rt * NKS + ks) * 64 + 16 * g + r;
+    }
   }
   for (int c = c_begin; c < c_end; ++c) {
     const long long bhc = (long long)bh * a.nb + c;
@@ -634,12 +659,22 @@ __global__ __launch_bounds__(kThreads) void sva_scan_kernel(
 // Kernel 3: output pass
 //
 // A wavefront handles 16-token tiles.  Lane l takes token l%16 of the tile
-// and features FPLa*(l/16) .. +FPLa-1 of it (one contiguous 2*FPLa- or
-// 4*FPLa-byte piece of the row), which is exactly its B-operand share of
-// out^T = S^T qr^T.  The denominator phi q . Z is an fp32 dot over the
-// lane's features plus two cross-lane adds; the lane then scales its
-// accumulators and stores its contiguous piece of the output row.
+// and FPLa = d/4 of its features, chosen so that each 16-byte load or store
+// of the four lanes of one token covers 64 contiguous bytes of the row:
+//   lane (g = l/16) local element m  <->  feature feat(g, m)
+//     bf16: 32*(m/8) + 8*g + m%8        fp32: 16*(m/4) + 4*g + m%4
+// Those elements are exactly its B-operand share of out^T = S^T qr^T (k-slot
+// e of k-step ks is local element 8*ks + e for bf16, ks for fp32).  The A
+// operand rows are permuted (see the prefix scan) so that accumulator rt of
+// lane l holds the output features stored by the same contiguous pieces.
+// The denominator phi q . Z is an fp32 dot over the lane's features plus two
+// lane-swap adds; the lane then scales its accumulators and stores.
 // ---------------------------------------------------------------------------
+
+template <bool BF16>
+__device__ __forceinline__ int apply_feat(int g, int m) {
+  return BF16 ? 32 * (m >> 3) + 8 * g + (m & 7) : 16 * (m >> 2) + 4 * g + (m & 3);
+}
 
 template <bool BF16, int D, bool ROPE>
 __global__ __launch_bounds__(kThreads) void sva_apply_kernel(
@@ -653,8 +688,20 @@ __global__ __launch_bounds__(kThreads) void sva_apply_kernel(
   constexpr int NW = FPLa * ESZ / 4;
   constexpr int FRAG_U4 = D * D * ESZ / 16;
 
+  // Tile I/O goes through LDS so that every global load and store
+  // instruction covers whole 128-byte lines: PPR lanes per row, RPI rows per
+  // instruction.  Each wave has its own padded tile (no barrier needed:
+  // a wave's LDS operations execute in order).
+  constexpr int ROWB = D * ESZ;
+  constexpr int PPR = ROWB / 16;  // 16-byte pieces per token row
+  constexpr int RPI = 64 / PPR;   // rows per instruction
+  constexpr int NLD = 16 / RPI;   // instructions per 16-row tile
+  constexpr int SROW = ROWB / 16 + 1;  // padded LDS row stride, in 16-byte units
+  static_assert(NLD * 4 == NW, "tile pieces");
+
   extern __shared__ float2 tab[];
   __shared__ uint4 fstage[FRAG_U4];
+  __shared__ uint4 tstage[kThreads / 64][16 * SROW];
 
   const int tid = threadIdx.x;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform
@@ -664,9 +711,8 @@ __global__ __launch_bounds__(kThreads) void sva_apply_kernel(
 
   PairLoc pl[NPAIR];
   if (ROPE) {
-    build_rope_table<!BF16>(tab, ra);
 #pragma unroll
-    for (int pp = 0; pp < NPAIR; ++pp) pl[pp] = pair_loc(NPAIR * g + pp, ra);
+    for (int pp = 0; pp < NPAIR; ++pp) pl[pp] = pair_loc(apply_feat<BF16>(g, 2 * pp) >> 1, ra);
   }
 
   const long long g0 = (long long)blockIdx.x * sp.L;
@@ -683,21 +729,63 @@ __global__ __launch_bounds__(kThreads) void sva_apply_kernel(
     const int je = (int)(seg_end - bhc * geo.Nb);
     const long long row0 = (long long)bh * geo.N + (long long)c * geo.Nb;
 
-    __syncthreads();  // previous segment done with fstage (and table built)
+    // Buffer resources over the block's rows [0, je): loads past the segment
+    // end read zeros and stores past it are dropped, so ragged tiles need no
+    // branches.
+    const long long blk_off = row0 * (D * ESZ);
+    const __amdgpu_buffer_rsrc_t qrs = make_rsrc(qb + blk_off, (uint32_t)je * (D * ESZ));
+    const __amdgpu_buffer_rsrc_t ors = make_rsrc(ob + blk_off, (uint32_t)je * (D * ESZ));
+    // Global side: lane takes piece ld_piece of row ld_row (+ RPI per
+    // instruction).  MFMA side: 16-byte piece i of lane (g, row) is bytes
+    // 64*i + 16*g of the row.
+    const int ld_row = lane / PPR, ld_piece = lane % PPR;
+    uint4* wst = tstage[wave];
+    auto load_tile = [&](uint32_t (&qw)[NW], int t) {
+      const uint32_t off = (uint32_t)(t + ld_row) * ROWB + 16 * ld_piece;
+#pragma unroll
+      for (int i = 0; i < NLD; ++i) buf_load<4>(qw + 4 * i, qrs, off + i * RPI * ROWB);
+    };
+
+    // Segment prologue.  The prefix operands of this block are loaded first,
+    // then the segment's first two steps of q: vector memory results return
+    // in issue order, so staging the operands waits for them only and the q
+    // loads stay in flight while the operands (and, in the first segment,
+    // the RoPE table) go to LDS.
+    lds_barrier();  // every wave has read the previous segment's fstage
+    constexpr int FR = (FRAG_U4 + kThreads - 1) / kThreads;
+    uint4 fr[FR];
     {
       const uint4* src = (const uint4*)frags + bhc * FRAG_U4;
-      for (int i = tid; i < FRAG_U4; i += kThreads) fstage[i] = src[i];
+#pragma unroll
+      for (int i = 0; i < FR; ++i)
+        if (FRAG_U4 % kThreads == 0 || tid + i * kThreads < FRAG_U4) fr[i] = src[tid + i * kThreads];
     }
     float z[FPLa];
     {
-      const float* zsrc = zc + bhc * D + FPLa * g;
+      const float* zsrc = zc + bhc * D;
 #pragma unroll
-      for (int m = 0; m < FPLa; m += 4) {
-        const float4 t = *(const float4*)(zsrc + m);
+      for (int m = 0; m < FPLa; m += 4) {  // runs of 4 consecutive features
+        const float4 t = *(const float4*)(zsrc + apply_feat<BF16>(g, m));
         z[m] = t.x; z[m + 1] = t.y; z[m + 2] = t.z; z[m + 3] = t.w;
       }
     }
-    __syncthreads();
+    constexpr int TPS = 2;
+    constexpr int WSTRIDE = 16 * TPS * (kThreads / 64);
+    const int t_first = js + wave * 16 * TPS;
+    const int nsteps = t_first < je ? (je - t_first + WSTRIDE - 1) / WSTRIDE : 0;
+    uint32_t qa[TPS][NW], qb[TPS][NW], qc[TPS][NW];
+    auto load_stepq = [&](uint32_t (&x)[TPS][NW], int t) {
+#pragma unroll
+      for (int i = 0; i < TPS; ++i) load_tile(x[i], t + 16 * i);
+    };
+    load_stepq(qa, t_first);
+    load_stepq(qb, t_first + WSTRIDE);
+    __builtin_amdgcn_sched_barrier(0);
+    if (ROPE && pos == g0) build_rope_table<!BF16>(tab, ra);
+#pragma unroll
+    for (int i = 0; i < FR; ++i)
+      if (FRAG_U4 % kThreads == 0 || tid + i * kThreads < FRAG_U4) fstage[tid + i * kThreads] = fr[i];
+    lds_barrier();
 
     u32x4 A16[BF16 ? NRT : 1][BF16 ? NKS : 1];
     float A32[BF16 ? 1 : NRT][BF16 ? 1 : NKS];
@@ -717,18 +805,19 @@ __global__ __launch_bounds__(kThreads) void sva_apply_kernel(
         for (int ks = 0; ks < NKS; ++ks) A32[rt][ks] = fs[(rt * NKS + ks) * 64 + lane];
     }
 
-    // Buffer resources over the block's rows [0, je): loads past the segment
-    // end read zeros and stores past it are dropped, so ragged tiles need no
-    // branches.
-    const long long blk_off = row0 * (D * ESZ);
-    const __amdgpu_buffer_rsrc_t qrs = make_rsrc(qb + blk_off, (uint32_t)je * (D * ESZ));
-    const __amdgpu_buffer_rsrc_t ors = make_rsrc(ob + blk_off, (uint32_t)je * (D * ESZ));
-    const uint32_t lane_col = FPLa * g * ESZ;
-    auto load_tile = [&](uint32_t (&qw)[NW], int t) {
-      buf_load<NW>(qw, qrs, (uint32_t)(t + row) * (D * ESZ) + lane_col);
-    };
-    auto compute_tile = [&](const uint32_t (&qw)[NW], int t) {
+    auto compute_tile = [&](const uint32_t (&qg)[NW], int t) {
       const int j = t + row;
+      // global row layout -> MFMA layout through the wave's LDS tile
+#pragma unroll
+      for (int i = 0; i < NLD; ++i)
+        wst[(i * RPI + ld_row) * SROW + ld_piece] = make_uint4(qg[4 * i], qg[4 * i + 1], qg[4 * i + 2], qg[4 * i + 3]);
+      __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
+      uint32_t qw[NW];
+#pragma unroll
+      for (int i = 0; i < NW / 4; ++i) {
+        const uint4 v = wst[row * SROW + 4 * i + g];
+        qw[4 * i] = v.x; qw[4 * i + 1] = v.y; qw[4 * i + 2] = v.z; qw[4 * i + 3] = v.w;
+      }
       float qf[FPLa];
       unpack_relu<BF16, FPLa>(qf, qw);
       float den = 0.f;
@@ -757,8 +846,7 @@ __global__ __launch_bounds__(kThreads) void sva_apply_kernel(
 #pragma unroll
           for (int rt = 0; rt < NRT; ++rt) acc[rt] = mfma_f32(A32[rt][ks], qf[ks], acc[rt]);
       }
-      den += __shfl_xor(den, 16);
-      den += __shfl_xor(den, 32);
+      den = sum_over_rows(den);
       // v_rcp_f32 (1 ulp) for bf16 outputs; a correctly rounded divide for fp32.
       const float inv = BF16 ? __builtin_amdgcn_rcpf(den + eps) : 1.0f / (den + eps);
       uint32_t ow[NW];
@@ -774,39 +862,48 @@ __global__ __launch_bounds__(kThreads) void sva_apply_kernel(
 #pragma unroll
           for (int i = 0; i < 4; ++i) ow[4 * rt + i] = __float_as_uint(acc[rt][i] * inv);
       }
-      buf_store<NW>(ors, (uint32_t)j * (D * ESZ) + lane_col, ow);
+      // MFMA layout -> global row layout through the same LDS tile
+      __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
+#pragma unroll
+      for (int i = 0; i < NW / 4; ++i) wst[row * SROW + 4 * i + g] = make_uint4(ow[4 * i], ow[4 * i + 1], ow[4 * i + 2], ow[4 * i + 3]);
+      __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
+      const uint32_t off = (uint32_t)(t + ld_row) * ROWB + 16 * ld_piece;
+#pragma unroll
+      for (int i = 0; i < NLD; ++i) {
+        const uint4 v = wst[(i * RPI + ld_row) * SROW + ld_piece];
+        const uint32_t w4[4] = {v.x, v.y, v.z, v.w};
+        buf_store<4>(ors, off + i * RPI * ROWB, w4);
+      }
+      __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
     };
 
-    // Four 16-token tiles per wave step (8 KiB of q at bf16, d = 64),
-    // software-pipelined as in the reduction with two register sets: step
-    // k+1's loads are issued before step k computes.
-    constexpr int TPS = 4;
-    constexpr int WSTRIDE = 16 * TPS * (kThreads / 64);
-    const int t_first = js + wave * 16 * TPS;
-    const int nsteps = t_first < je ? (je - t_first + WSTRIDE - 1) / WSTRIDE : 0;
-    uint32_t qa[TPS][NW], qb[TPS][NW];
-    auto load_stepq = [&](uint32_t (&x)[TPS][NW], int t) {
-#pragma unroll
-      for (int i = 0; i < TPS; ++i) load_tile(x[i], t + 16 * i);
-    };
+    // TPS 16-token tiles per wave step (the first two steps were issued
+    // above), software-pipelined over a ring of three register sets: while step k computes (and issues its stores),
+    // the loads of steps k+1 and k+2 are in flight.  gfx9 counts loads and
+    // stores in one in-order counter, so the wait for step k+1's loads never
+    // has to cover step k's stores, which were issued after them.
     auto compute_stepq = [&](const uint32_t (&x)[TPS][NW], int t) {
 #pragma unroll
       for (int i = 0; i < TPS; ++i) compute_tile(x[i], t + 16 * i);
     };
-    load_stepq(qa, t_first);
     int k = 0;
-    for (; k + 2 <= nsteps; k += 2) {
+    for (; k + 3 <= nsteps; k += 3) {
       const int t0 = t_first + k * WSTRIDE;
-      load_stepq(qb, t0 + WSTRIDE);
+      load_stepq(qc, t0 + 2 * WSTRIDE);
       __builtin_amdgcn_sched_barrier(0);
       compute_stepq(qa, t0);
       __builtin_amdgcn_sched_barrier(0);
-      load_stepq(qa, t0 + 2 * WSTRIDE);
+      load_stepq(qa, t0 + 3 * WSTRIDE);
       __builtin_amdgcn_sched_barrier(0);
       compute_stepq(qb, t0 + WSTRIDE);
       __builtin_amdgcn_sched_barrier(0);
+      load_stepq(qb, t0 + 4 * WSTRIDE);
+      __builtin_amdgcn_sched_barrier(0);
+      compute_stepq(qc, t0 + 2 * WSTRIDE);
+      __builtin_amdgcn_sched_barrier(0);
     }
     if (k < nsteps) compute_stepq(qa, t_first + k * WSTRIDE);
+    if (k + 1 < nsteps) compute_stepq(qb, t_first + (k + 1) * WSTRIDE);
     pos = seg_end;
   }
 }
