@@ -48,7 +48,7 @@ typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 
 constexpr int kThreads = 256;          // 4 wavefronts of 64
-constexpr int kMaxTableEntries = 5632; // RoPE cos/sin table, 44 KiB of LDS
+constexpr int kMaxTableEntries = 4096; // RoPE cos/sin table, 32 KiB of LDS
 
 // ---------------------------------------------------------------------------
 // Small integer helpers
@@ -80,56 +80,69 @@ __device__ __forceinline__ uint32_t fdiv(uint32_t n, const FastDiv& f) {
 // ---------------------------------------------------------------------------
 
 // RoPE layout for one call.  The cos/sin table lives in LDS as float2
-// entries: [T rows x dt/2] for t (global frame t0 + row), then
-// [Hs rows x dh/2] for h, then [Ws rows x dw/2] for w.
+// entries: [F rows x dt/2] for t (the frames of the block being processed,
+// rebuilt per block), then [Hs rows x dh/2] for h, then [Ws rows x dw/2] for
+// w.  When every width is a multiple of 4 ("paired"), the two RoPE pairs a
+// lane reads next to each other sit in one 16-byte-aligned float4.
 struct RopeArgs {
   int dt, dh, dw;
   int off_h, off_w, n_entries;
-  int t0;
-  int pad_;
-  double inv_rev[32];  // base^(-2i/d_a) / (2 pi), indexed by global pair p
+  int t0;               // global frame of the call's first frame
+  int F;                // frames per block (rows of the t part)
+  double inv_rev[32];   // base^(-2i/d_a) / (2 pi), indexed by global pair p
 };
 
-// Fill the table.  PRECISE (fp32 inputs): fp64 angle reduced to one turn,
+// One table entry.  PRECISE (fp32 inputs): fp64 angle reduced to one turn,
 // then an accurate single-precision sincos.  Otherwise (bf16 inputs): the
 // same reduced angle through the hardware sine/cosine, far below bf16's
 // rounding.
 template <bool PRECISE>
-__device__ void build_rope_table(float2* tab, const RopeArgs& ra) {
+__device__ __forceinline__ float2 rope_entry(int pos, double inv_rev) {
+  double rv = (double)pos * inv_rev;
+  rv -= rint(rv);  // angle in turns, within [-1/2, 1/2]
+  float c, s;
+  if (PRECISE) {
+    sincosf((float)(rv * 6.283185307179586), &s, &c);
+  } else {
+    s = __builtin_amdgcn_sinf((float)rv);  // sin(2 pi x)
+    c = __builtin_amdgcn_cosf((float)rv);
+  }
+  return make_float2(c, s);
+}
+
+// h and w parts of the table (the same for every block).
+template <bool PRECISE>
+__device__ void build_rope_hw(float2* tab, const RopeArgs& ra) {
   const int ht = ra.dt >> 1, hh = ra.dh >> 1, hw = ra.dw >> 1;
-  for (int e = threadIdx.x; e < ra.n_entries; e += blockDim.x) {
+  for (int e = ra.off_h + threadIdx.x; e < ra.n_entries; e += blockDim.x) {
     int pos, p;
-    if (e < ra.off_h) {
-      int row = e / ht;
-      p = e - row * ht;
-      pos = ra.t0 + row;
-    } else if (e < ra.off_w) {
-      int x = e - ra.off_h;
-      int row = x / hh;
-      p = ht + (x - row * hh);
-      pos = row;
+    if (e < ra.off_w) {
+      const int x = e - ra.off_h;
+      pos = x / hh;
+      p = ht + (x - pos * hh);
     } else {
-      int x = e - ra.off_w;
-      int row = x / hw;
-      p = ht + hh + (x - row * hw);
-      pos = row;
+      const int x = e - ra.off_w;
+      pos = x / hw;
+      p = ht + hh + (x - pos * hw);
     }
-    double rv = (double)pos * ra.inv_rev[p];
-    rv -= rint(rv);  // angle in turns, within [-1/2, 1/2]
-    float c, s;
-    if (PRECISE) {
-      sincosf((float)(rv * 6.283185307179586), &s, &c);
-    } else {
-      s = __builtin_amdgcn_sinf((float)rv);  // sin(2 pi x)
-      c = __builtin_amdgcn_cosf((float)rv);
-    }
-    tab[e] = make_float2(c, s);
+    tab[e] = rope_entry<PRECISE>(pos, ra.inv_rev[p]);
   }
 }
 
-// A token's RoPE coordinates packed in one word: frame (call-local, the
-// t-table row) in bits 21..31, h in bits 10..20, w in bits 0..9.  The host
-// rejects RoPE grids that do not fit (T, Hs <= 2048, Ws <= 1024).
+// t part of the table for block c: rows are global frames t0 + c*F + row.
+template <bool PRECISE>
+__device__ void build_rope_t(float2* tab, const RopeArgs& ra, int c) {
+  const int ht = ra.dt >> 1;
+  for (int e = threadIdx.x; e < ra.off_h; e += blockDim.x) {
+    const int row = e / ht;
+    tab[e] = rope_entry<PRECISE>(ra.t0 + c * ra.F + row, ra.inv_rev[e - row * ht]);
+  }
+}
+
+// A token's RoPE coordinates packed in one word: frame within its block (the
+// t-table row) in bits 21..31, h in bits 10..20, w in bits 0..9, decoded from
+// the block-local token index.  The host rejects RoPE grids that do not fit
+// (F, Hs <= 2048, Ws <= 1024).
 __device__ __forceinline__ uint32_t decode_packed(uint32_t n, const FastDiv& fHW, const FastDiv& fWs) {
   const uint32_t frame = fdiv(n, fHW);
   const uint32_t rem = n - frame * fHW.div;
@@ -162,19 +175,39 @@ __device__ __forceinline__ int pair_entry(const PairLoc& pl, uint32_t packed) {
   return __mul24((int)pos, pl.stride) + pl.base;  // 24-bit multiply: operands are small
 }
 
-// phi = ReLU on the bit pattern: a float with its sign bit set is a negative
-// int32, so max_i32(bits, 0) is 0 for every negative float (and -0) and the
-// float itself otherwise -- one v_max_i32.
-__device__ __forceinline__ float relu_bits(uint32_t bits) {
-  return __int_as_float(max((int)bits, 0));
-}
-
 // Turn the pair (x, y) by the angle whose (cos, sin) is cs.
 __device__ __forceinline__ void rotate(float& x, float& y, float2 cs) {
   const float xr = x * cs.x - y * cs.y;
   const float yr = x * cs.y + y * cs.x;
   x = xr;
   y = yr;
+}
+
+// Rotate a lane's NPAIR consecutive pairs (local elements 2pp, 2pp+1).  In
+// paired mode (ROPE == 2: every axis width a multiple of 4) local pairs
+// (2k, 2k+1) are adjacent entries of the same axis at an even index, so one
+// 16-byte LDS read serves both.
+template <int ROPE, int NPAIR>
+__device__ __forceinline__ void rope_lane(float* x, const float2* tab, const PairLoc* pl, uint32_t co) {
+  if constexpr (ROPE == 2 && NPAIR % 2 == 0) {
+    const float4* tab4 = reinterpret_cast<const float4*>(tab);
+#pragma unroll
+    for (int pp = 0; pp < NPAIR; pp += 2) {
+      const float4 cs = tab4[pair_entry(pl[pp], co) >> 1];
+      rotate(x[2 * pp], x[2 * pp + 1], make_float2(cs.x, cs.y));
+      rotate(x[2 * pp + 2], x[2 * pp + 3], make_float2(cs.z, cs.w));
+    }
+  } else {
+#pragma unroll
+    for (int pp = 0; pp < NPAIR; ++pp) rotate(x[2 * pp], x[2 * pp + 1], tab[pair_entry(pl[pp], co)]);
+  }
+}
+
+// phi = ReLU on the bit pattern: a float with its sign bit set is a negative
+// int32, so max_i32(bits, 0) is 0 for every negative float (and -0) and the
+// float itself otherwise -- one v_max_i32.
+__device__ __forceinline__ float relu_bits(uint32_t bits) {
+  return __int_as_float(max((int)bits, 0));
 }
 
 // ---------------------------------------------------------------------------
@@ -353,7 +386,7 @@ struct SplitArgs {
 // Accumulator (r, s)[i] of lane l holds S[FPL*(4*(l/16)+i)+r][FPL*(l%16)+s].
 // ---------------------------------------------------------------------------
 
-template <bool BF16, int D, bool ROPE>
+template <bool BF16, int D, int ROPE>
 __global__ __launch_bounds__(kThreads, BF16 ? 2 : 1) void sva_reduce_kernel(
     const void* __restrict__ kp, const void* __restrict__ vp, float* __restrict__ partials,
     Geo geo, SplitArgs sp, RopeArgs ra) {
@@ -366,9 +399,10 @@ __global__ __launch_bounds__(kThreads, BF16 ? 2 : 1) void sva_reduce_kernel(
   constexpr int STEP = 32;           // tokens per wave per step
   constexpr int WSTRIDE = STEP * (kThreads / 64);
 
-  extern __shared__ float2 tab[];
-  __shared__ float red[D * D];
-  __shared__ float zred[D];
+  extern __shared__ float4 tab_raw[];  // 16-byte aligned
+  float2* tab = reinterpret_cast<float2*>(tab_raw);
+  __shared__ float red[kThreads / 64][D * D];  // one accumulator tile per wave
+  __shared__ float zred[kThreads / 64][D];
 
   const int tid = threadIdx.x;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform
@@ -427,7 +461,7 @@ __global__ __launch_bounds__(kThreads, BF16 ? 2 : 1) void sva_reduce_kernel(
       // its own 8 tokens.
       uint32_t mine = 0;
       if (ROPE)
-        mine = decode_packed((uint32_t)(c * geo.Nb + min(s0 + (lane & 31), je - 1)), geo.fHW, geo.fWs);
+        mine = decode_packed((uint32_t)min(s0 + (lane & 31), je - 1), geo.fHW, geo.fWs);
       // phi, z and RoPE for token e of this lane, in registers.
       auto prep_token = [&](int e, float (&kf)[FPL]) {
         unpack_relu<BF16, FPL>(kf, kw[e]);
@@ -435,8 +469,7 @@ __global__ __launch_bounds__(kThreads, BF16 ? 2 : 1) void sva_reduce_kernel(
         for (int r = 0; r < FPL; ++r) zacc[r] += kf[r];
         if (ROPE) {
           const uint32_t co = (uint32_t)__builtin_amdgcn_ds_bpermute((4 * e + tg) * 4, (int)mine);
-#pragma unroll
-          for (int pp = 0; pp < NPAIR; ++pp) rotate(kf[2 * pp], kf[2 * pp + 1], tab[pair_entry(pl[pp], co)]);
+          rope_lane<ROPE, NPAIR>(kf, tab, pl, co);
         }
       };
       if (BF16) {
@@ -487,8 +520,13 @@ __global__ __launch_bounds__(kThreads, BF16 ? 2 : 1) void sva_reduce_kernel(
     load_step(kA, vA, s_first);
     load_step(kB, vB, s_first + WSTRIDE);
     __builtin_amdgcn_sched_barrier(0);
-    // The RoPE table is built while the first loads are in flight.
-    if (ROPE && pos == g0) build_rope_table<!BF16>(tab, ra);
+    // The RoPE table (h, w rows once; t rows for this block) is built while
+    // the first loads are in flight.  Every wave has passed the previous
+    // segment's epilogue barrier, so no wave still reads the old t rows.
+    if (ROPE) {
+      if (pos == g0) build_rope_hw<!BF16>(tab, ra);
+      build_rope_t<!BF16>(tab, ra, c);
+    }
     lds_barrier();
     int k = 0;
     for (; k + 3 <= nsteps; k += 3) {
@@ -509,33 +547,43 @@ __global__ __launch_bounds__(kThreads, BF16 ? 2 : 1) void sva_reduce_kernel(
     if (k < nsteps) compute_step(kA, vA, s_first + k * WSTRIDE);
     if (k + 1 < nsteps) compute_step(kB, vB, s_first + (k + 1) * WSTRIDE);
 
-    // Fixed-order reduction over the four lane groups and the four waves.
+    // Fixed-order reduction over the four lane groups (lane swaps), then over
+    // the four waves: every wave stores its tile, one barrier, and each
+    // thread sums the four tiles for 16 contiguous elements in wave order.
 #pragma unroll
     for (int r = 0; r < FPL; ++r) zacc[r] = sum_over_rows(zacc[r]);
-    for (int w = 0; w < kThreads / 64; ++w) {
-      if (wave == w) {
 #pragma unroll
-        for (int r = 0; r < FPL; ++r)
+    for (int r = 0; r < FPL; ++r)
 #pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            float* dst = red + (FPL * (4 * tg + i) + r) * D + FPL * cg;
+      for (int i = 0; i < 4; ++i) {
+        float* dst = red[wave] + (FPL * (4 * tg + i) + r) * D + FPL * cg;
 #pragma unroll
-            for (int s = 0; s < FPL; ++s) dst[s] = (w == 0) ? acc[r][s][i] : dst[s] + acc[r][s][i];
-          }
-        if (tg == 0) {
-#pragma unroll
-          for (int r = 0; r < FPL; ++r)
-            zred[FPL * cg + r] = (w == 0) ? zacc[r] : zred[FPL * cg + r] + zacc[r];
-        }
+        for (int s = 0; s < FPL; ++s) dst[s] = acc[r][s][i];
       }
-      lds_barrier();
+    if (tg == 0) {
+#pragma unroll
+      for (int r = 0; r < FPL; ++r) zred[wave][FPL * cg + r] = zacc[r];
     }
+    lds_barrier();
     // Piece (workgroup g, block bhc) goes to slot g + bhc: pieces are ordered
     // along the flattened token axis, so g + bhc strictly increases from one
     // piece to the next and the slots of one block's pieces are contiguous.
     float* dst = partials + ((long long)blockIdx.x + bhc) * E;
-    for (int e = tid; e < D * D; e += kThreads) dst[e] = red[e];
-    for (int e = tid; e < D; e += kThreads) dst[D * D + e] = zred[e];
+    for (int e = 4 * tid; e < D * D; e += 4 * kThreads) {
+      float4 t = *(const float4*)(red[0] + e);
+#pragma unroll
+      for (int w = 1; w < kThreads / 64; ++w) {
+        const float4 u = *(const float4*)(red[w] + e);
+        t.x += u.x; t.y += u.y; t.z += u.z; t.w += u.w;
+      }
+      *(float4*)(dst + e) = t;
+    }
+    for (int e = tid; e < D; e += kThreads) {
+      float t = zred[0][e];
+#pragma unroll
+      for (int w = 1; w < kThreads / 64; ++w) t += zred[w][e];
+      dst[D * D + e] = t;
+    }
     // `red` is next written after the next segment's barrier.
     pos = seg_end;
   }
@@ -676,7 +724,7 @@ __device__ __forceinline__ int apply_feat(int g, int m) {
   return BF16 ? 32 * (m >> 3) + 8 * g + (m & 7) : 16 * (m >> 2) + 4 * g + (m & 3);
 }
 
-template <bool BF16, int D, bool ROPE>
+template <bool BF16, int D, int ROPE>
 __global__ __launch_bounds__(kThreads) void sva_apply_kernel(
     const void* __restrict__ qp, void* __restrict__ outp, const void* __restrict__ frags,
     const float* __restrict__ zc, Geo geo, SplitArgs sp, RopeArgs ra, float eps) {
@@ -699,7 +747,8 @@ __global__ __launch_bounds__(kThreads) void sva_apply_kernel(
   constexpr int SROW = ROWB / 16 + 1;  // padded LDS row stride, in 16-byte units
   static_assert(NLD * 4 == NW, "tile pieces");
 
-  extern __shared__ float2 tab[];
+  extern __shared__ float4 tab_raw[];  // 16-byte aligned
+  float2* tab = reinterpret_cast<float2*>(tab_raw);
   __shared__ uint4 fstage[FRAG_U4];
   __shared__ uint4 tstage[kThreads / 64][16 * SROW];
 
@@ -781,7 +830,10 @@ __global__ __launch_bounds__(kThreads) void sva_apply_kernel(
     load_stepq(qa, t_first);
     load_stepq(qb, t_first + WSTRIDE);
     __builtin_amdgcn_sched_barrier(0);
-    if (ROPE && pos == g0) build_rope_table<!BF16>(tab, ra);
+    if (ROPE) {
+      if (pos == g0) build_rope_hw<!BF16>(tab, ra);
+      build_rope_t<!BF16>(tab, ra, c);
+    }
 #pragma unroll
     for (int i = 0; i < FR; ++i)
       if (FRAG_U4 % kThreads == 0 || tid + i * kThreads < FRAG_U4) fstage[tid + i * kThreads] = fr[i];
@@ -824,9 +876,8 @@ __global__ __launch_bounds__(kThreads) void sva_apply_kernel(
 #pragma unroll
       for (int m = 0; m < FPLa; ++m) den += qf[m] * z[m];
       if (ROPE) {
-        const uint32_t co = decode_packed((uint32_t)(c * geo.Nb + min(j, je - 1)), geo.fHW, geo.fWs);
-#pragma unroll
-        for (int pp = 0; pp < NPAIR; ++pp) rotate(qf[2 * pp], qf[2 * pp + 1], tab[pair_entry(pl[pp], co)]);
+        const uint32_t co = decode_packed((uint32_t)min(j, je - 1), geo.fHW, geo.fWs);
+        rope_lane<ROPE, NPAIR>(qf, tab, pl, co);
       }
       floatx4 acc[NRT];
 #pragma unroll
@@ -912,17 +963,22 @@ __global__ __launch_bounds__(kThreads) void sva_apply_kernel(
 // Standalone phi + RoPE stage (test entry point): one thread per token.
 // ---------------------------------------------------------------------------
 
-template <bool BF16, int D, bool ROPE>
+template <bool BF16, int D, int ROPE>
 __global__ __launch_bounds__(kThreads) void sva_prep_kernel(
-    const void* __restrict__ xp, float* __restrict__ xr, float* __restrict__ xphi,
-    long long total, int N, Geo geo, RopeArgs ra) {
+    const void* __restrict__ xp, float* __restrict__ xr, float* __restrict__ xphi, Geo geo, RopeArgs ra) {
+  // grid: (token chunks of one block, blocks, b*h); one thread per token
   constexpr int ESZ = BF16 ? 2 : 4;
-  extern __shared__ float2 tab[];
-  if (ROPE) build_rope_table<!BF16>(tab, ra);
+  extern __shared__ float4 tab_raw[];  // 16-byte aligned
+  float2* tab = reinterpret_cast<float2*>(tab_raw);
+  const int c = blockIdx.y;
+  if (ROPE) {
+    build_rope_hw<!BF16>(tab, ra);
+    build_rope_t<!BF16>(tab, ra, c);
+  }
   __syncthreads();
-  const long long t = (long long)blockIdx.x * kThreads + threadIdx.x;
-  if (t >= total) return;
-  const int n = (int)(t % N);
+  const int j = blockIdx.x * kThreads + threadIdx.x;  // block-local token
+  if (j >= geo.Nb) return;
+  const long long t = (long long)blockIdx.z * geo.N + (long long)c * geo.Nb + j;
   uint32_t w[D * ESZ / 4];
   load_words<D * ESZ / 4>(w, (const char*)xp + t * D * ESZ);
   float f[D];
@@ -932,7 +988,7 @@ __global__ __launch_bounds__(kThreads) void sva_prep_kernel(
     for (int i = 0; i < D; i += 4) *(float4*)(xphi + t * D + i) = make_float4(f[i], f[i + 1], f[i + 2], f[i + 3]);
   }
   if (ROPE) {
-    const uint32_t co = decode_packed((uint32_t)n, geo.fHW, geo.fWs);
+    const uint32_t co = decode_packed((uint32_t)j, geo.fHW, geo.fWs);
 #pragma unroll
     for (int p = 0; p < D / 2; ++p) rotate(f[2 * p], f[2 * p + 1], tab[pair_entry(pair_loc(p, ra), co)]);
   }
@@ -947,6 +1003,7 @@ __global__ __launch_bounds__(kThreads) void sva_prep_kernel(
 struct Plan {
   int BH, D, N, Nb, nb;
   bool bf16, rope;
+  int rope_mode;  // 0 none, 1 general, 2 paired (every axis width a multiple of 4)
   Geo geo;
   RopeArgs ra;
   SplitArgs red, app;
@@ -1027,11 +1084,11 @@ sva_status validate_desc(const sva_desc* d, bool one_block) {
     if ((d->rope_dt | d->rope_dh | d->rope_dw) & 1) return SVA_ERR_UNSUPPORTED;
     if (d->rope_dt + d->rope_dh + d->rope_dw != d->d) return SVA_ERR_UNSUPPORTED;
     if (!(d->rope_base > 0.f) || d->rope_base > 3.0e38f) return SVA_ERR_UNSUPPORTED;
-    const long long entries = (long long)d->T * (d->rope_dt / 2) +
+    const long long entries = (long long)d->frames_per_block * (d->rope_dt / 2) +
                               (long long)d->Hs * (d->rope_dh / 2) + (long long)d->Ws * (d->rope_dw / 2);
     if (entries > kMaxTableEntries) return SVA_ERR_UNSUPPORTED;
-    // packed token coordinates: frame and h in 11 bits, w in 10
-    if (d->T > 2048 || d->Hs > 2048 || d->Ws > 1024) return SVA_ERR_UNSUPPORTED;
+    // packed token coordinates: frame-in-block and h in 11 bits, w in 10
+    if (d->frames_per_block > 2048 || d->Hs > 2048 || d->Ws > 1024) return SVA_ERR_UNSUPPORTED;
   }
   return SVA_OK;
 }
@@ -1047,6 +1104,7 @@ Plan make_plan(const sva_desc* d) {
   p.nb = d->T / d->frames_per_block;
   p.bf16 = d->dtype == SVA_BF16;
   p.rope = d->rope != 0;
+  p.rope_mode = !p.rope ? 0 : (d->rope_dt % 4 == 0 && d->rope_dh % 4 == 0 && d->rope_dw % 4 == 0) ? 2 : 1;
   p.geo.N = p.N;
   p.geo.Nb = p.Nb;
   p.geo.nb = p.nb;
@@ -1061,10 +1119,11 @@ Plan make_plan(const sva_desc* d) {
     ra.dt = d->rope_dt;
     ra.dh = d->rope_dh;
     ra.dw = d->rope_dw;
-    ra.off_h = d->T * (ra.dt / 2);
+    ra.off_h = d->frames_per_block * (ra.dt / 2);
     ra.off_w = ra.off_h + d->Hs * (ra.dh / 2);
     ra.n_entries = ra.off_w + d->Ws * (ra.dw / 2);
     ra.t0 = d->t0;
+    ra.F = d->frames_per_block;
     const double two_pi = 6.283185307179586476925286766559;
     int p_idx = 0;
     const int widths[3] = {ra.dt, ra.dh, ra.dw};
@@ -1092,7 +1151,7 @@ Plan make_plan(const sva_desc* d) {
   return p;
 }
 
-template <bool BF16, int D, bool ROPE>
+template <bool BF16, int D, int ROPE>
 hipError_t launch_reduce(const Plan& p, const void* k, const void* v, float* partials, hipStream_t st) {
   Geo geo = p.geo;
   SplitArgs sp = p.red;
@@ -1121,7 +1180,7 @@ hipError_t launch_scan(const Plan& p, const float* partials, const float* S0, co
                          dim3((E + kScanElems - 1) / kScanElems, p.BH), dim3(kThreads), args, 0, st);
 }
 
-template <bool BF16, int D, bool ROPE>
+template <bool BF16, int D, int ROPE>
 hipError_t launch_apply(const Plan& p, const void* q, void* out, const void* frags, const float* zc,
                         float eps, hipStream_t st) {
   Geo geo = p.geo;
@@ -1132,34 +1191,31 @@ hipError_t launch_apply(const Plan& p, const void* q, void* out, const void* fra
                          args, ROPE ? p.tab_bytes : 0, st);
 }
 
-template <bool BF16, int D, bool ROPE>
+template <bool BF16, int D, int ROPE>
 hipError_t launch_prep(const Plan& p, const void* x, float* xr, float* xphi, hipStream_t st) {
   Geo geo = p.geo;
   RopeArgs ra = p.ra;
-  long long total = (long long)p.BH * p.N;
-  int N = p.N;
-  void* args[] = {(void*)&x, (void*)&xr, (void*)&xphi, &total, &N, &geo, &ra};
+  void* args[] = {(void*)&x, (void*)&xr, (void*)&xphi, &geo, &ra};
   return hipLaunchKernel((const void*)&sva_prep_kernel<BF16, D, ROPE>,
-                         dim3((unsigned)((total + kThreads - 1) / kThreads)), dim3(kThreads), args,
+                         dim3((p.Nb + kThreads - 1) / kThreads, p.nb, p.BH), dim3(kThreads), args,
                          ROPE ? p.tab_bytes : 0, st);
 }
 
-// Template dispatch over (dtype, d, rope).
+// Template dispatch over (dtype, d, RoPE mode 0 none / 1 general / 2 paired).
+#define SVA_DISPATCH_R(P, FN, B, DD, ...)                                              \
+  ((P).rope_mode == 2 ? FN<B, DD, 2>(__VA_ARGS__)                                      \
+                      : (P).rope_mode == 1 ? FN<B, DD, 1>(__VA_ARGS__) : FN<B, DD, 0>(__VA_ARGS__))
 #define SVA_DISPATCH(P, FN, ...)                                                         \
-  ((P).bf16 ? ((P).D == 64 ? ((P).rope ? FN<true, 64, true>(__VA_ARGS__)                 \
-                                       : FN<true, 64, false>(__VA_ARGS__))               \
-                           : ((P).rope ? FN<true, 32, true>(__VA_ARGS__)                 \
-                                       : FN<true, 32, false>(__VA_ARGS__)))              \
-            : ((P).D == 64 ? ((P).rope ? FN<false, 64, true>(__VA_ARGS__)                \
-                                       : FN<false, 64, false>(__VA_ARGS__))              \
-                           : ((P).rope ? FN<false, 32, true>(__VA_ARGS__)                \
-                                       : FN<false, 32, false>(__VA_ARGS__))))
+  ((P).bf16 ? ((P).D == 64 ? SVA_DISPATCH_R(P, FN, true, 64, __VA_ARGS__)                \
+                           : SVA_DISPATCH_R(P, FN, true, 32, __VA_ARGS__))               \
+            : ((P).D == 64 ? SVA_DISPATCH_R(P, FN, false, 64, __VA_ARGS__)               \
+                           : SVA_DISPATCH_R(P, FN, false, 32, __VA_ARGS__)))
 
 #define SVA_DISPATCH2(P, FN, ...)                                                        \
   ((P).bf16 ? ((P).D == 64 ? FN<true, 64>(__VA_ARGS__) : FN<true, 32>(__VA_ARGS__))      \
             : ((P).D == 64 ? FN<false, 64>(__VA_ARGS__) : FN<false, 32>(__VA_ARGS__)))
 
-template <bool BF16, int D, bool ROPE>
+template <bool BF16, int D, int ROPE>
 int plan_grids_t(Plan* p) {
   const long long total = (long long)p->BH * p->N;
   const size_t lds = ROPE ? p->tab_bytes : 0;

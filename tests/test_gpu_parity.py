@@ -35,6 +35,9 @@ SMALL = [
     ("one_block_norope", 1, 2, 64, (2, 9, 9), 2, None, 0),
     ("h_only_axis", 1, 2, 64, (2, 6, 4), 1, (0, 64, 0), 0),
     ("w_frame_axes", 2, 1, 32, (6, 2, 17), 3, (16, 0, 16), 11),
+    # axis widths that are not multiples of 4: the unpaired table-lookup path
+    ("odd_split_d64", 1, 2, 64, (4, 5, 6), 2, (6, 26, 32), 3),
+    ("odd_split_d32", 2, 1, 32, (3, 4, 9), 3, (10, 10, 12), 0),
 ]
 
 
