@@ -46,6 +46,7 @@ typedef __bf16 bf16x2_t __attribute__((__vector_size__(2 * sizeof(__bf16))));
 typedef float floatx4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+typedef short i16x2_t __attribute__((ext_vector_type(2)));
 
 constexpr int kThreads = 256;          // 4 wavefronts of 64
 constexpr int kMaxTableEntries = 4096; // RoPE cos/sin table, 32 KiB of LDS
@@ -184,12 +185,12 @@ __device__ __forceinline__ void rotate(float& x, float& y, float2 cs) {
 }
 
 // Rotate a lane's NPAIR consecutive pairs (local elements 2pp, 2pp+1).  In
-// paired mode (ROPE == 2: every axis width a multiple of 4) local pairs
+// paired mode (ROPE >= 2: every axis width a multiple of 4) local pairs
 // (2k, 2k+1) are adjacent entries of the same axis at an even index, so one
 // 16-byte LDS read serves both.
 template <int ROPE, int NPAIR>
 __device__ __forceinline__ void rope_lane(float* x, const float2* tab, const PairLoc* pl, uint32_t co) {
-  if constexpr (ROPE == 2 && NPAIR % 2 == 0) {
+  if constexpr (ROPE >= 2 && NPAIR % 2 == 0) {
     const float4* tab4 = reinterpret_cast<const float4*>(tab);
 #pragma unroll
     for (int pp = 0; pp < NPAIR; pp += 2) {
@@ -200,6 +201,26 @@ __device__ __forceinline__ void rope_lane(float* x, const float2* tab, const Pai
   } else {
 #pragma unroll
     for (int pp = 0; pp < NPAIR; ++pp) rotate(x[2 * pp], x[2 * pp + 1], tab[pair_entry(pl[pp], co)]);
+  }
+}
+
+// Grouped mode (ROPE == 3: every axis width a multiple of 8) for lanes whose
+// elements come in runs of 8 consecutive features starting at a multiple of
+// 8: such a run lies in one axis, its four pairs are consecutive entries of
+// one table row starting at a multiple of 4, and two 16-byte reads at a
+// fixed distance serve them from one computed address.
+template <int NRUN>
+__device__ __forceinline__ void rope_lane_runs(float* x, const float2* tab, const PairLoc* pl, uint32_t co) {
+  const float4* tab4 = reinterpret_cast<const float4*>(tab);
+#pragma unroll
+  for (int r = 0; r < NRUN; ++r) {
+    const float4* t = tab4 + (pair_entry(pl[r], co) >> 1);
+    const float4 c0 = t[0], c1 = t[1];
+    float* y = x + 8 * r;
+    rotate(y[0], y[1], make_float2(c0.x, c0.y));
+    rotate(y[2], y[3], make_float2(c0.z, c0.w));
+    rotate(y[4], y[5], make_float2(c1.x, c1.y));
+    rotate(y[6], y[7], make_float2(c1.z, c1.w));
   }
 }
 
@@ -317,13 +338,28 @@ __device__ __forceinline__ void unpack(float* f, const uint32_t* w) {
   }
 }
 
+// phi on a pair of bf16 values in one word: each half is a bf16 bit pattern,
+// negative exactly when it is a negative int16, so a packed int16 max with 0
+// (v_pk_max_i16) zeroes the negative halves and keeps the rest.
+__device__ __forceinline__ uint32_t relu_bf16x2(uint32_t w) {
+  const i16x2_t r = __builtin_elementwise_max(__builtin_bit_cast(i16x2_t, w), i16x2_t{0, 0});
+  return __builtin_bit_cast(uint32_t, r);
+}
+
 // Unpack with phi = ReLU applied on the bits.
 template <bool BF16, int CNT>
 __device__ __forceinline__ void unpack_relu(float* f, const uint32_t* w) {
+  if constexpr (BF16) {
+    static_assert(CNT % 2 == 0, "bf16 pairs");
 #pragma unroll
-  for (int i = 0; i < CNT; ++i) {
-    if (BF16) f[i] = relu_bits((i & 1) ? (w[i >> 1] & 0xffff0000u) : (w[i >> 1] << 16));
-    else f[i] = relu_bits(w[i]);
+    for (int i = 0; i < CNT / 2; ++i) {
+      const uint32_t r = relu_bf16x2(w[i]);
+      f[2 * i] = bf16_lo(r);
+      f[2 * i + 1] = bf16_hi(r);
+    }
+  } else {
+#pragma unroll
+    for (int i = 0; i < CNT; ++i) f[i] = relu_bits(w[i]);
   }
 }
 
@@ -660,9 +696,20 @@ __global__ __launch_bounds__(kThreads) void sva_scan_kernel(
   float run = 0.f;
   if (active && a.has_init)
     run = in_S ? S0[(long long)bh * D * D + e] : z0[(long long)bh * D + (e - D * D)];
+  // Pass 1: block sums of this lane's blocks.  Up to kKeep of them stay in
+  // registers for pass 2; lanes with more blocks re-read theirs (L2 hits).
+  constexpr int kKeep = 4;
+  float keep[kKeep];
   float tot = 0.f;
-  if (active)
-    for (int c = c_begin; c < c_end; ++c) tot += block_sum<E>(partials, (long long)bh * a.nb + c, a.L, a.Nb, e);
+  if (active) {
+    for (int c = c_begin; c < c_end; ++c) {
+      const float bs = block_sum<E>(partials, (long long)bh * a.nb + c, a.L, a.Nb, e);
+#pragma unroll
+      for (int i = 0; i < kKeep; ++i)
+        if (c - c_begin == i) keep[i] = bs;
+      tot += bs;
+    }
+  }
   lane_tot[ty][tx] = tot;
   __syncthreads();
   if (!active) return;
@@ -687,7 +734,15 @@ __global__ __launch_bounds__(kThreads) void sva_scan_kernel(
   }
   for (int c = c_begin; c < c_end; ++c) {
     const long long bhc = (long long)bh * a.nb + c;
-    run += block_sum<E>(partials, bhc, a.L, a.Nb, e);
+    float bs = 0.f;
+    if (c - c_begin < kKeep) {
+#pragma unroll
+      for (int i = 0; i < kKeep; ++i)
+        if (c - c_begin == i) bs = keep[i];
+    } else {
+      bs = block_sum<E>(partials, bhc, a.L, a.Nb, e);
+    }
+    run += bs;
     if (a.write_frags) {
       if (in_S) {
         if (BF16) ((__bf16*)frags)[bhc * D * D + frag_off] = (__bf16)run;
@@ -715,8 +770,10 @@ __global__ __launch_bounds__(kThreads) void sva_scan_kernel(
 // e of k-step ks is local element 8*ks + e for bf16, ks for fp32).  The A
 // operand rows are permuted (see the prefix scan) so that accumulator rt of
 // lane l holds the output features stored by the same contiguous pieces.
-// The denominator phi q . Z is an fp32 dot over the lane's features plus two
-// lane-swap adds; the lane then scales its accumulators and stores.
+// The denominator phi q . Z is, for fp32, an fp32 dot over the lane's
+// features plus two lane-swap adds; for bf16, one more MFMA per k-step with
+// Z split into two bf16 rows, summed across the lane rows the same way.  The
+// lane then scales its accumulators and stores.
 // ---------------------------------------------------------------------------
 
 template <bool BF16>
@@ -725,7 +782,7 @@ __device__ __forceinline__ int apply_feat(int g, int m) {
 }
 
 template <bool BF16, int D, int ROPE>
-__global__ __launch_bounds__(kThreads) void sva_apply_kernel(
+__global__ __launch_bounds__(kThreads, BF16 ? 3 : 1) void sva_apply_kernel(
     const void* __restrict__ qp, void* __restrict__ outp, const void* __restrict__ frags,
     const float* __restrict__ zc, Geo geo, SplitArgs sp, RopeArgs ra, float eps) {
   constexpr int FPLa = D / 4;
@@ -758,10 +815,14 @@ __global__ __launch_bounds__(kThreads) void sva_apply_kernel(
   const int g = lane >> 4;
   const int row = lane & 15;
 
-  PairLoc pl[NPAIR];
+  // RoPE lookups: one per pair, or (grouped mode, bf16 runs of 8 features)
+  // one per run.
+  constexpr bool RUNS = BF16 && ROPE == 3;
+  constexpr int NLOC = RUNS ? NKS : NPAIR;
+  PairLoc pl[NLOC];
   if (ROPE) {
 #pragma unroll
-    for (int pp = 0; pp < NPAIR; ++pp) pl[pp] = pair_loc(apply_feat<BF16>(g, 2 * pp) >> 1, ra);
+    for (int i = 0; i < NLOC; ++i) pl[i] = pair_loc(apply_feat<BF16>(g, RUNS ? 8 * i : 2 * i) >> 1, ra);
   }
 
   const long long g0 = (long long)blockIdx.x * sp.L;
@@ -809,13 +870,34 @@ __global__ __launch_bounds__(kThreads) void sva_apply_kernel(
       for (int i = 0; i < FR; ++i)
         if (FRAG_U4 % kThreads == 0 || tid + i * kThreads < FRAG_U4) fr[i] = src[tid + i * kThreads];
     }
-    float z[FPLa];
+    // Denominator operand.  fp32: the lane's FPLa entries of Z.  bf16: the
+    // A operand of a 16x16x32 MFMA against the unrotated phi(q) tile, row 0
+    // holding Z rounded to bf16 and row 4 the rounding remainder (also in
+    // bf16), other rows zero; Z_hi + Z_lo carries Z to about 2^-17 relative,
+    // and the MFMA forms the bf16 x bf16 products exactly and sums in fp32.
+    float z[BF16 ? 1 : FPLa];
+    u32x4 az[BF16 ? NKS : 1];
     {
       const float* zsrc = zc + bhc * D;
+      if constexpr (BF16) {
 #pragma unroll
-      for (int m = 0; m < FPLa; m += 4) {  // runs of 4 consecutive features
-        const float4 t = *(const float4*)(zsrc + apply_feat<BF16>(g, m));
-        z[m] = t.x; z[m + 1] = t.y; z[m + 2] = t.z; z[m + 3] = t.w;
+        for (int ks = 0; ks < NKS; ++ks) {
+          const float4 t0 = *(const float4*)(zsrc + apply_feat<BF16>(g, 8 * ks));
+          const float4 t1 = *(const float4*)(zsrc + apply_feat<BF16>(g, 8 * ks + 4));
+          const float zz[8] = {t0.x, t0.y, t0.z, t0.w, t1.x, t1.y, t1.z, t1.w};
+#pragma unroll
+          for (int m = 0; m < 4; ++m) {
+            const bf16x2_t hi = {(__bf16)zz[2 * m], (__bf16)zz[2 * m + 1]};
+            const bf16x2_t lo = {(__bf16)(zz[2 * m] - (float)hi[0]), (__bf16)(zz[2 * m + 1] - (float)hi[1])};
+            az[ks][m] = row == 0 ? __builtin_bit_cast(uint32_t, hi) : row == 4 ? __builtin_bit_cast(uint32_t, lo) : 0u;
+          }
+        }
+      } else {
+#pragma unroll
+        for (int m = 0; m < FPLa; m += 4) {  // runs of 4 consecutive features
+          const float4 t = *(const float4*)(zsrc + apply_feat<BF16>(g, m));
+          z[m] = t.x; z[m + 1] = t.y; z[m + 2] = t.z; z[m + 3] = t.w;
+        }
       }
     }
     constexpr int TPS = 2;
@@ -870,34 +952,54 @@ __global__ __launch_bounds__(kThreads) void sva_apply_kernel(
         const uint4 v = wst[row * SROW + 4 * i + g];
         qw[4 * i] = v.x; qw[4 * i + 1] = v.y; qw[4 * i + 2] = v.z; qw[4 * i + 3] = v.w;
       }
-      float qf[FPLa];
-      unpack_relu<BF16, FPLa>(qf, qw);
-      float den = 0.f;
-#pragma unroll
-      for (int m = 0; m < FPLa; ++m) den += qf[m] * z[m];
-      if (ROPE) {
-        const uint32_t co = decode_packed((uint32_t)min(j, je - 1), geo.fHW, geo.fWs);
-        rope_lane<ROPE, NPAIR>(qf, tab, pl, co);
-      }
       floatx4 acc[NRT];
 #pragma unroll
       for (int rt = 0; rt < NRT; ++rt) acc[rt] = floatx4{0.f, 0.f, 0.f, 0.f};
-      if (BF16) {
+      float den;
+      if constexpr (BF16) {
+        // phi(q) as bf16 pairs is the B operand of the denominator MFMA, and
+        // of the numerator too when there is no rotation.
+        u32x4 rq[NKS];
 #pragma unroll
-        for (int ks = 0; ks < NKS; ++ks) {
-          u32x4 b;
+        for (int i = 0; i < NW; ++i) rq[i >> 2][i & 3] = relu_bf16x2(qw[i]);
+        floatx4 dacc = floatx4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-          for (int m = 0; m < 4; ++m) b[m] = pack_bf16x2(qf[8 * ks + 2 * m], qf[8 * ks + 2 * m + 1]);
+        for (int ks = 0; ks < NKS; ++ks) dacc = mfma_bf16(az[ks], rq[ks], dacc);
+        if constexpr (ROPE != 0) {
+          float qf[FPLa];
 #pragma unroll
-          for (int rt = 0; rt < NRT; ++rt) acc[rt] = mfma_bf16(A16[rt][ks], b, acc[rt]);
+          for (int i = 0; i < NW; ++i) {
+            qf[2 * i] = bf16_lo(rq[i >> 2][i & 3]);
+            qf[2 * i + 1] = bf16_hi(rq[i >> 2][i & 3]);
+          }
+          const uint32_t co = decode_packed((uint32_t)min(j, je - 1), geo.fHW, geo.fWs);
+          if constexpr (RUNS) rope_lane_runs<NKS>(qf, tab, pl, co);
+          else rope_lane<ROPE, NPAIR>(qf, tab, pl, co);
+#pragma unroll
+          for (int i = 0; i < NW; ++i) rq[i >> 2][i & 3] = pack_bf16x2(qf[2 * i], qf[2 * i + 1]);
         }
+#pragma unroll
+        for (int ks = 0; ks < NKS; ++ks)
+#pragma unroll
+          for (int rt = 0; rt < NRT; ++rt) acc[rt] = mfma_bf16(A16[rt][ks], rq[ks], acc[rt]);
+        // rows 0 and 4 of the denominator product sit in lane rows 0 and 1
+        den = sum_over_rows(dacc[0]);
       } else {
+        float qf[FPLa];
+        unpack_relu<BF16, FPLa>(qf, qw);
+        den = 0.f;
+#pragma unroll
+        for (int m = 0; m < FPLa; ++m) den += qf[m] * z[m];
+        if (ROPE) {
+          const uint32_t co = decode_packed((uint32_t)min(j, je - 1), geo.fHW, geo.fWs);
+          rope_lane<ROPE, NPAIR>(qf, tab, pl, co);
+        }
 #pragma unroll
         for (int ks = 0; ks < NKS; ++ks)
 #pragma unroll
           for (int rt = 0; rt < NRT; ++rt) acc[rt] = mfma_f32(A32[rt][ks], qf[ks], acc[rt]);
+        den = sum_over_rows(den);
       }
-      den = sum_over_rows(den);
       // v_rcp_f32 (1 ulp) for bf16 outputs; a correctly rounded divide for fp32.
       const float inv = BF16 ? __builtin_amdgcn_rcpf(den + eps) : 1.0f / (den + eps);
       uint32_t ow[NW];
@@ -1003,7 +1105,10 @@ __global__ __launch_bounds__(kThreads) void sva_prep_kernel(
 struct Plan {
   int BH, D, N, Nb, nb;
   bool bf16, rope;
-  int rope_mode;  // 0 none, 1 general, 2 paired (every axis width a multiple of 4)
+  // 0 none, 1 general, 2 paired (every axis width a multiple of 4),
+  // 3 grouped (every axis width a multiple of 8; paired where grouping does
+  // not apply)
+  int rope_mode;
   Geo geo;
   RopeArgs ra;
   SplitArgs red, app;
@@ -1104,7 +1209,12 @@ Plan make_plan(const sva_desc* d) {
   p.nb = d->T / d->frames_per_block;
   p.bf16 = d->dtype == SVA_BF16;
   p.rope = d->rope != 0;
-  p.rope_mode = !p.rope ? 0 : (d->rope_dt % 4 == 0 && d->rope_dh % 4 == 0 && d->rope_dw % 4 == 0) ? 2 : 1;
+  if (!p.rope) {
+    p.rope_mode = 0;
+  } else {
+    const int all = d->rope_dt | d->rope_dh | d->rope_dw;
+    p.rope_mode = (all & 7) == 0 ? 3 : (all & 3) == 0 ? 2 : 1;
+  }
   p.geo.N = p.N;
   p.geo.Nb = p.Nb;
   p.geo.nb = p.nb;
@@ -1157,7 +1267,7 @@ hipError_t launch_reduce(const Plan& p, const void* k, const void* v, float* par
   SplitArgs sp = p.red;
   RopeArgs ra = p.ra;
   void* args[] = {(void*)&k, (void*)&v, (void*)&partials, &geo, &sp, &ra};
-  return hipLaunchKernel((const void*)&sva_reduce_kernel<BF16, D, ROPE>, dim3(p.G_red), dim3(kThreads),
+  return hipLaunchKernel((const void*)&sva_reduce_kernel<BF16, D, (ROPE == 3 ? 2 : ROPE)>, dim3(p.G_red), dim3(kThreads),
                          args, ROPE ? p.tab_bytes : 0, st);
 }
 
@@ -1187,7 +1297,7 @@ hipError_t launch_apply(const Plan& p, const void* q, void* out, const void* fra
   SplitArgs sp = p.app;
   RopeArgs ra = p.ra;
   void* args[] = {(void*)&q, (void*)&out, (void*)&frags, (void*)&zc, &geo, &sp, &ra, &eps};
-  return hipLaunchKernel((const void*)&sva_apply_kernel<BF16, D, ROPE>, dim3(p.G_app), dim3(kThreads),
+  return hipLaunchKernel((const void*)&sva_apply_kernel<BF16, D, (!BF16 && ROPE == 3 ? 2 : ROPE)>, dim3(p.G_app), dim3(kThreads),
                          args, ROPE ? p.tab_bytes : 0, st);
 }
 
@@ -1196,15 +1306,18 @@ hipError_t launch_prep(const Plan& p, const void* x, float* xr, float* xphi, hip
   Geo geo = p.geo;
   RopeArgs ra = p.ra;
   void* args[] = {(void*)&x, (void*)&xr, (void*)&xphi, &geo, &ra};
-  return hipLaunchKernel((const void*)&sva_prep_kernel<BF16, D, ROPE>,
+  return hipLaunchKernel((const void*)&sva_prep_kernel<BF16, D, (ROPE == 3 ? 2 : ROPE)>,
                          dim3((p.Nb + kThreads - 1) / kThreads, p.nb, p.BH), dim3(kThreads), args,
                          ROPE ? p.tab_bytes : 0, st);
 }
 
-// Template dispatch over (dtype, d, RoPE mode 0 none / 1 general / 2 paired).
+// Template dispatch over (dtype, d, RoPE mode 0 none / 1 general / 2 paired
+// / 3 grouped).
 #define SVA_DISPATCH_R(P, FN, B, DD, ...)                                              \
-  ((P).rope_mode == 2 ? FN<B, DD, 2>(__VA_ARGS__)                                      \
-                      : (P).rope_mode == 1 ? FN<B, DD, 1>(__VA_ARGS__) : FN<B, DD, 0>(__VA_ARGS__))
+  ((P).rope_mode == 3   ? FN<B, DD, 3>(__VA_ARGS__)                                    \
+   : (P).rope_mode == 2 ? FN<B, DD, 2>(__VA_ARGS__)                                    \
+   : (P).rope_mode == 1 ? FN<B, DD, 1>(__VA_ARGS__)                                    \
+                        : FN<B, DD, 0>(__VA_ARGS__))
 #define SVA_DISPATCH(P, FN, ...)                                                         \
   ((P).bf16 ? ((P).D == 64 ? SVA_DISPATCH_R(P, FN, true, 64, __VA_ARGS__)                \
                            : SVA_DISPATCH_R(P, FN, true, 32, __VA_ARGS__))               \
@@ -1219,8 +1332,8 @@ template <bool BF16, int D, int ROPE>
 int plan_grids_t(Plan* p) {
   const long long total = (long long)p->BH * p->N;
   const size_t lds = ROPE ? p->tab_bytes : 0;
-  const long long r = resident_workgroups((const void*)&sva_reduce_kernel<BF16, D, ROPE>, lds);
-  const long long a = resident_workgroups((const void*)&sva_apply_kernel<BF16, D, ROPE>, lds);
+  const long long r = resident_workgroups((const void*)&sva_reduce_kernel<BF16, D, (ROPE == 3 ? 2 : ROPE)>, lds);
+  const long long a = resident_workgroups((const void*)&sva_apply_kernel<BF16, D, (!BF16 && ROPE == 3 ? 2 : ROPE)>, lds);
   p->red = make_split(total, r < kRedWorkgroupsMax ? r : kRedWorkgroupsMax, &p->G_red);
   p->app = make_split(total, a < kAppWorkgroupsMax ? a : kAppWorkgroupsMax, &p->G_app);
   return 0;
