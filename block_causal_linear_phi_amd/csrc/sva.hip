@@ -48,7 +48,15 @@ typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 typedef short i16x2_t __attribute__((ext_vector_type(2)));
 
-constexpr int kThreads = 256;          // 4 wavefronts of 64
+constexpr int kThreads = 256;          // 4 wavefronts of 64 (scan, prep)
+
+// Workgroup sizes of the reduction and output kernels, and how many of their
+// workgroups a CU should hold (bf16: 2 waves per SIMD for the reduction, 3
+// for the output pass; fp32 needs more registers and runs 1).
+template <bool BF16> constexpr int red_threads() { return BF16 ? 512 : 256; }
+template <bool BF16> constexpr int app_threads() { return 256; }
+template <bool BF16> constexpr int red_min_blocks() { return BF16 ? (512 / red_threads<BF16>() > 0 ? 512 / red_threads<BF16>() : 1) : 1; }
+template <bool BF16> constexpr int app_min_blocks() { return BF16 ? (768 / app_threads<BF16>() > 0 ? 768 / app_threads<BF16>() : 1) : 1; }
 constexpr int kMaxTableEntries = 4096; // RoPE cos/sin table, 32 KiB of LDS
 
 // ---------------------------------------------------------------------------
@@ -383,6 +391,19 @@ __device__ __forceinline__ float sum_over_rows(float x) {
   return __uint_as_float(r32[0]) + __uint_as_float(r32[1]);
 }
 
+// Wave priority from the share of its steps still to run (done: k of n).
+// The instruction arbiter otherwise prefers the oldest waves, so the
+// workgroups that share a CU drift apart and the last one runs alone at the
+// end; raising the priority of the waves with more work left keeps the
+// workgroups of a CU closer together.
+__device__ __forceinline__ void prio_by_remaining(int k, int n) {
+  const int r4 = 4 * (n - k);
+  if (r4 > 3 * n) __builtin_amdgcn_s_setprio(3);
+  else if (r4 > 2 * n) __builtin_amdgcn_s_setprio(2);
+  else if (r4 > n) __builtin_amdgcn_s_setprio(1);
+  else __builtin_amdgcn_s_setprio(0);
+}
+
 __device__ __forceinline__ floatx4 mfma_bf16(const u32x4& a, const u32x4& b, floatx4 c) {
   return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, a),
                                                  __builtin_bit_cast(bf16x8_t, b), c, 0, 0, 0);
@@ -423,9 +444,10 @@ struct SplitArgs {
 // ---------------------------------------------------------------------------
 
 template <bool BF16, int D, int ROPE>
-__global__ __launch_bounds__(kThreads, BF16 ? 2 : 1) void sva_reduce_kernel(
+__global__ __launch_bounds__(red_threads<BF16>(), red_min_blocks<BF16>()) void sva_reduce_kernel(
     const void* __restrict__ kp, const void* __restrict__ vp, float* __restrict__ partials,
     Geo geo, SplitArgs sp, RopeArgs ra) {
+  constexpr int RT = red_threads<BF16>();
   constexpr int FPL = D / 16;
   constexpr int NPAIR = FPL / 2;
   constexpr int E = D * D + D;
@@ -433,12 +455,17 @@ __global__ __launch_bounds__(kThreads, BF16 ? 2 : 1) void sva_reduce_kernel(
   constexpr int NW = FPL * ESZ / 4;  // 32-bit words per lane per token row piece
   constexpr int ROWB = D * ESZ;      // bytes per token row
   constexpr int STEP = 32;           // tokens per wave per step
-  constexpr int WSTRIDE = STEP * (kThreads / 64);
+  constexpr int WSTRIDE = STEP * (RT / 64);
 
   extern __shared__ float4 tab_raw[];  // 16-byte aligned
   float2* tab = reinterpret_cast<float2*>(tab_raw);
-  __shared__ float red[kThreads / 64][D * D];  // one accumulator tile per wave
-  __shared__ float zred[kThreads / 64][D];
+  // Accumulator tiles for the cross-wave sum: one per wave up to four; with
+  // eight waves, waves 4..7 hand theirs to waves 0..3 first.
+  constexpr int NWV = RT / 64;
+  constexpr int NT = NWV > 4 ? 4 : NWV;
+  static_assert(NWV == NT || NWV == 2 * NT, "waves per workgroup");
+  __shared__ float red[NT][D * D];
+  __shared__ float zred[NWV][D];
 
   const int tid = threadIdx.x;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform
@@ -566,6 +593,7 @@ __global__ __launch_bounds__(kThreads, BF16 ? 2 : 1) void sva_reduce_kernel(
     lds_barrier();
     int k = 0;
     for (; k + 3 <= nsteps; k += 3) {
+      prio_by_remaining(k, nsteps);
       const int s0 = s_first + k * WSTRIDE;
       load_step(kC, vC, s0 + 2 * WSTRIDE);
       __builtin_amdgcn_sched_barrier(0);
@@ -584,18 +612,40 @@ __global__ __launch_bounds__(kThreads, BF16 ? 2 : 1) void sva_reduce_kernel(
     if (k + 1 < nsteps) compute_step(kB, vB, s_first + (k + 1) * WSTRIDE);
 
     // Fixed-order reduction over the four lane groups (lane swaps), then over
-    // the four waves: every wave stores its tile, one barrier, and each
-    // thread sums the four tiles for 16 contiguous elements in wave order.
+    // the waves: with eight waves, waves 4..7 store their tiles and waves
+    // 0..3 add them to their own; the (up to) four tiles are stored, one
+    // barrier, and each thread sums them for 4 contiguous elements in wave
+    // order.
 #pragma unroll
     for (int r = 0; r < FPL; ++r) zacc[r] = sum_over_rows(zacc[r]);
+    auto tile_elem = [&](int slot, int r, int i) { return red[slot] + (FPL * (4 * tg + i) + r) * D + FPL * cg; };
+    auto store_tile = [&](int slot) {
 #pragma unroll
-    for (int r = 0; r < FPL; ++r)
+      for (int r = 0; r < FPL; ++r)
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        float* dst = red[wave] + (FPL * (4 * tg + i) + r) * D + FPL * cg;
+        for (int i = 0; i < 4; ++i) {
+          float* dst = tile_elem(slot, r, i);
 #pragma unroll
-        for (int s = 0; s < FPL; ++s) dst[s] = acc[r][s][i];
+          for (int s = 0; s < FPL; ++s) dst[s] = acc[r][s][i];
+        }
+    };
+    if constexpr (NWV > NT) {
+      if (wave >= NT) store_tile(wave - NT);
+      lds_barrier();
+      if (wave < NT) {
+#pragma unroll
+        for (int r = 0; r < FPL; ++r)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            const float* src = tile_elem(wave, r, i);
+#pragma unroll
+            for (int s = 0; s < FPL; ++s) acc[r][s][i] += src[s];
+          }
+        store_tile(wave);  // each lane rewrites only the elements it read
       }
+    } else {
+      store_tile(wave);
+    }
     if (tg == 0) {
 #pragma unroll
       for (int r = 0; r < FPL; ++r) zred[wave][FPL * cg + r] = zacc[r];
@@ -605,19 +655,19 @@ __global__ __launch_bounds__(kThreads, BF16 ? 2 : 1) void sva_reduce_kernel(
     // along the flattened token axis, so g + bhc strictly increases from one
     // piece to the next and the slots of one block's pieces are contiguous.
     float* dst = partials + ((long long)blockIdx.x + bhc) * E;
-    for (int e = 4 * tid; e < D * D; e += 4 * kThreads) {
+    for (int e = 4 * tid; e < D * D; e += 4 * RT) {
       float4 t = *(const float4*)(red[0] + e);
 #pragma unroll
-      for (int w = 1; w < kThreads / 64; ++w) {
+      for (int w = 1; w < NT; ++w) {
         const float4 u = *(const float4*)(red[w] + e);
         t.x += u.x; t.y += u.y; t.z += u.z; t.w += u.w;
       }
       *(float4*)(dst + e) = t;
     }
-    for (int e = tid; e < D; e += kThreads) {
+    for (int e = tid; e < D; e += RT) {
       float t = zred[0][e];
 #pragma unroll
-      for (int w = 1; w < kThreads / 64; ++w) t += zred[w][e];
+      for (int w = 1; w < NWV; ++w) t += zred[w][e];
       dst[D * D + e] = t;
     }
     // `red` is next written after the next segment's barrier.
@@ -782,9 +832,10 @@ __device__ __forceinline__ int apply_feat(int g, int m) {
 }
 
 template <bool BF16, int D, int ROPE>
-__global__ __launch_bounds__(kThreads, BF16 ? 3 : 1) void sva_apply_kernel(
+__global__ __launch_bounds__(app_threads<BF16>(), app_min_blocks<BF16>()) void sva_apply_kernel(
     const void* __restrict__ qp, void* __restrict__ outp, const void* __restrict__ frags,
     const float* __restrict__ zc, Geo geo, SplitArgs sp, RopeArgs ra, float eps) {
+  constexpr int AT = app_threads<BF16>();
   constexpr int FPLa = D / 4;
   constexpr int NRT = D / 16;
   constexpr int NKS = BF16 ? D / 32 : D / 4;
@@ -807,7 +858,7 @@ __global__ __launch_bounds__(kThreads, BF16 ? 3 : 1) void sva_apply_kernel(
   extern __shared__ float4 tab_raw[];  // 16-byte aligned
   float2* tab = reinterpret_cast<float2*>(tab_raw);
   __shared__ uint4 fstage[FRAG_U4];
-  __shared__ uint4 tstage[kThreads / 64][16 * SROW];
+  __shared__ uint4 tstage[AT / 64][16 * SROW];
 
   const int tid = threadIdx.x;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform
@@ -862,13 +913,13 @@ __global__ __launch_bounds__(kThreads, BF16 ? 3 : 1) void sva_apply_kernel(
     // loads stay in flight while the operands (and, in the first segment,
     // the RoPE table) go to LDS.
     lds_barrier();  // every wave has read the previous segment's fstage
-    constexpr int FR = (FRAG_U4 + kThreads - 1) / kThreads;
+    constexpr int FR = (FRAG_U4 + AT - 1) / AT;
     uint4 fr[FR];
     {
       const uint4* src = (const uint4*)frags + bhc * FRAG_U4;
 #pragma unroll
       for (int i = 0; i < FR; ++i)
-        if (FRAG_U4 % kThreads == 0 || tid + i * kThreads < FRAG_U4) fr[i] = src[tid + i * kThreads];
+        if (FRAG_U4 % AT == 0 || tid + i * AT < FRAG_U4) fr[i] = src[tid + i * AT];
     }
     // Denominator operand.  fp32: the lane's FPLa entries of Z.  bf16: the
     // A operand of a 16x16x32 MFMA against the unrotated phi(q) tile, row 0
@@ -901,7 +952,7 @@ __global__ __launch_bounds__(kThreads, BF16 ? 3 : 1) void sva_apply_kernel(
       }
     }
     constexpr int TPS = 2;
-    constexpr int WSTRIDE = 16 * TPS * (kThreads / 64);
+    constexpr int WSTRIDE = 16 * TPS * (AT / 64);
     const int t_first = js + wave * 16 * TPS;
     const int nsteps = t_first < je ? (je - t_first + WSTRIDE - 1) / WSTRIDE : 0;
     uint32_t qa[TPS][NW], qb[TPS][NW], qc[TPS][NW];
@@ -918,7 +969,7 @@ __global__ __launch_bounds__(kThreads, BF16 ? 3 : 1) void sva_apply_kernel(
     }
 #pragma unroll
     for (int i = 0; i < FR; ++i)
-      if (FRAG_U4 % kThreads == 0 || tid + i * kThreads < FRAG_U4) fstage[tid + i * kThreads] = fr[i];
+      if (FRAG_U4 % AT == 0 || tid + i * AT < FRAG_U4) fstage[tid + i * AT] = fr[i];
     lds_barrier();
 
     u32x4 A16[BF16 ? NRT : 1][BF16 ? NKS : 1];
@@ -1146,7 +1197,7 @@ SplitArgs make_split(long long total, long long target_wg, int* G_out) {
 // How many workgroups of `fn` the current device holds at once (CUs times
 // workgroups per CU for its registers and LDS).  Launching exactly that many,
 // each with an equal token range, keeps every CU streaming until the end.
-int resident_workgroups(const void* fn, size_t lds) {
+int resident_workgroups(const void* fn, int threads, size_t lds) {
   static std::mutex mu;
   static std::map<std::tuple<int, const void*, size_t>, int> cache;
   int dev = 0;
@@ -1158,7 +1209,7 @@ int resident_workgroups(const void* fn, size_t lds) {
   int cus = 0, per = 0;
   if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus < 1)
     cus = 256;
-  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per, fn, kThreads, lds) != hipSuccess || per < 1)
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per, fn, threads, lds) != hipSuccess || per < 1)
     per = 1;
   const int n = cus * per;
   cache[key] = n;
@@ -1267,7 +1318,7 @@ hipError_t launch_reduce(const Plan& p, const void* k, const void* v, float* par
   SplitArgs sp = p.red;
   RopeArgs ra = p.ra;
   void* args[] = {(void*)&k, (void*)&v, (void*)&partials, &geo, &sp, &ra};
-  return hipLaunchKernel((const void*)&sva_reduce_kernel<BF16, D, (ROPE == 3 ? 2 : ROPE)>, dim3(p.G_red), dim3(kThreads),
+  return hipLaunchKernel((const void*)&sva_reduce_kernel<BF16, D, (ROPE == 3 ? 2 : ROPE)>, dim3(p.G_red), dim3(red_threads<BF16>()),
                          args, ROPE ? p.tab_bytes : 0, st);
 }
 
@@ -1297,7 +1348,7 @@ hipError_t launch_apply(const Plan& p, const void* q, void* out, const void* fra
   SplitArgs sp = p.app;
   RopeArgs ra = p.ra;
   void* args[] = {(void*)&q, (void*)&out, (void*)&frags, (void*)&zc, &geo, &sp, &ra, &eps};
-  return hipLaunchKernel((const void*)&sva_apply_kernel<BF16, D, (!BF16 && ROPE == 3 ? 2 : ROPE)>, dim3(p.G_app), dim3(kThreads),
+  return hipLaunchKernel((const void*)&sva_apply_kernel<BF16, D, (!BF16 && ROPE == 3 ? 2 : ROPE)>, dim3(p.G_app), dim3(app_threads<BF16>()),
                          args, ROPE ? p.tab_bytes : 0, st);
 }
 
@@ -1332,8 +1383,8 @@ template <bool BF16, int D, int ROPE>
 int plan_grids_t(Plan* p) {
   const long long total = (long long)p->BH * p->N;
   const size_t lds = ROPE ? p->tab_bytes : 0;
-  const long long r = resident_workgroups((const void*)&sva_reduce_kernel<BF16, D, (ROPE == 3 ? 2 : ROPE)>, lds);
-  const long long a = resident_workgroups((const void*)&sva_apply_kernel<BF16, D, (!BF16 && ROPE == 3 ? 2 : ROPE)>, lds);
+  const long long r = resident_workgroups((const void*)&sva_reduce_kernel<BF16, D, (ROPE == 3 ? 2 : ROPE)>, red_threads<BF16>(), lds);
+  const long long a = resident_workgroups((const void*)&sva_apply_kernel<BF16, D, (!BF16 && ROPE == 3 ? 2 : ROPE)>, app_threads<BF16>(), lds);
   p->red = make_split(total, r < kRedWorkgroupsMax ? r : kRedWorkgroupsMax, &p->G_red);
   p->app = make_split(total, a < kAppWorkgroupsMax ? a : kAppWorkgroupsMax, &p->G_app);
   return 0;
