@@ -858,7 +858,9 @@ __global__ __launch_bounds__(app_threads<BF16>(), app_min_blocks<BF16>()) void s
   extern __shared__ float4 tab_raw[];  // 16-byte aligned
   float2* tab = reinterpret_cast<float2*>(tab_raw);
   __shared__ uint4 fstage[FRAG_U4];
-  __shared__ uint4 tstage[AT / 64][16 * SROW];
+  constexpr int TPS = 2;          // 16-token tiles per wave step
+  constexpr int TSZ = 16 * SROW;  // one tile, in 16-byte units
+  __shared__ uint4 tstage[AT / 64][TPS * TSZ];
 
   const int tid = threadIdx.x;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform
@@ -951,7 +953,6 @@ __global__ __launch_bounds__(app_threads<BF16>(), app_min_blocks<BF16>()) void s
         }
       }
     }
-    constexpr int TPS = 2;
     constexpr int WSTRIDE = 16 * TPS * (AT / 64);
     const int t_first = js + wave * 16 * TPS;
     const int nsteps = t_first < je ? (je - t_first + WSTRIDE - 1) / WSTRIDE : 0;
@@ -990,106 +991,133 @@ __global__ __launch_bounds__(app_threads<BF16>(), app_min_blocks<BF16>()) void s
         for (int ks = 0; ks < NKS; ++ks) A32[rt][ks] = fs[(rt * NKS + ks) * 64 + lane];
     }
 
-    auto compute_tile = [&](const uint32_t (&qg)[NW], int t) {
-      const int j = t + row;
-      // global row layout -> MFMA layout through the wave's LDS tile
+    // The TPS tiles of a step go through each phase together, so that their
+    // LDS round trips and MFMA chains overlap.
+    auto compute_stepq = [&](const uint32_t (&x)[TPS][NW], int t) {
+      // global row layout -> MFMA layout through the wave's LDS tiles
 #pragma unroll
-      for (int i = 0; i < NLD; ++i)
-        wst[(i * RPI + ld_row) * SROW + ld_piece] = make_uint4(qg[4 * i], qg[4 * i + 1], qg[4 * i + 2], qg[4 * i + 3]);
+      for (int u = 0; u < TPS; ++u)
+#pragma unroll
+        for (int i = 0; i < NLD; ++i)
+          wst[u * TSZ + (i * RPI + ld_row) * SROW + ld_piece] =
+              make_uint4(x[u][4 * i], x[u][4 * i + 1], x[u][4 * i + 2], x[u][4 * i + 3]);
       __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
-      uint32_t qw[NW];
+      uint32_t qw[TPS][NW];
 #pragma unroll
-      for (int i = 0; i < NW / 4; ++i) {
-        const uint4 v = wst[row * SROW + 4 * i + g];
-        qw[4 * i] = v.x; qw[4 * i + 1] = v.y; qw[4 * i + 2] = v.z; qw[4 * i + 3] = v.w;
-      }
-      floatx4 acc[NRT];
+      for (int u = 0; u < TPS; ++u)
 #pragma unroll
-      for (int rt = 0; rt < NRT; ++rt) acc[rt] = floatx4{0.f, 0.f, 0.f, 0.f};
-      float den;
+        for (int i = 0; i < NW / 4; ++i) {
+          const uint4 v = wst[u * TSZ + row * SROW + 4 * i + g];
+          qw[u][4 * i] = v.x; qw[u][4 * i + 1] = v.y; qw[u][4 * i + 2] = v.z; qw[u][4 * i + 3] = v.w;
+        }
+      floatx4 acc[TPS][NRT];
+#pragma unroll
+      for (int u = 0; u < TPS; ++u)
+#pragma unroll
+        for (int rt = 0; rt < NRT; ++rt) acc[u][rt] = floatx4{0.f, 0.f, 0.f, 0.f};
+      float den[TPS];
       if constexpr (BF16) {
         // phi(q) as bf16 pairs is the B operand of the denominator MFMA, and
         // of the numerator too when there is no rotation.
-        u32x4 rq[NKS];
+        u32x4 rq[TPS][NKS];
+        floatx4 dacc[TPS];
 #pragma unroll
-        for (int i = 0; i < NW; ++i) rq[i >> 2][i & 3] = relu_bf16x2(qw[i]);
-        floatx4 dacc = floatx4{0.f, 0.f, 0.f, 0.f};
+        for (int u = 0; u < TPS; ++u) {
 #pragma unroll
-        for (int ks = 0; ks < NKS; ++ks) dacc = mfma_bf16(az[ks], rq[ks], dacc);
+          for (int i = 0; i < NW; ++i) rq[u][i >> 2][i & 3] = relu_bf16x2(qw[u][i]);
+          dacc[u] = floatx4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+          for (int ks = 0; ks < NKS; ++ks) dacc[u] = mfma_bf16(az[ks], rq[u][ks], dacc[u]);
+        }
         if constexpr (ROPE != 0) {
-          float qf[FPLa];
 #pragma unroll
-          for (int i = 0; i < NW; ++i) {
-            qf[2 * i] = bf16_lo(rq[i >> 2][i & 3]);
-            qf[2 * i + 1] = bf16_hi(rq[i >> 2][i & 3]);
+          for (int u = 0; u < TPS; ++u) {
+            float qf[FPLa];
+#pragma unroll
+            for (int i = 0; i < NW; ++i) {
+              qf[2 * i] = bf16_lo(rq[u][i >> 2][i & 3]);
+              qf[2 * i + 1] = bf16_hi(rq[u][i >> 2][i & 3]);
+            }
+            const uint32_t co = decode_packed((uint32_t)min(t + 16 * u + row, je - 1), geo.fHW, geo.fWs);
+            if constexpr (RUNS) rope_lane_runs<NKS>(qf, tab, pl, co);
+            else rope_lane<ROPE, NPAIR>(qf, tab, pl, co);
+#pragma unroll
+            for (int i = 0; i < NW; ++i) rq[u][i >> 2][i & 3] = pack_bf16x2(qf[2 * i], qf[2 * i + 1]);
           }
-          const uint32_t co = decode_packed((uint32_t)min(j, je - 1), geo.fHW, geo.fWs);
-          if constexpr (RUNS) rope_lane_runs<NKS>(qf, tab, pl, co);
-          else rope_lane<ROPE, NPAIR>(qf, tab, pl, co);
-#pragma unroll
-          for (int i = 0; i < NW; ++i) rq[i >> 2][i & 3] = pack_bf16x2(qf[2 * i], qf[2 * i + 1]);
         }
 #pragma unroll
         for (int ks = 0; ks < NKS; ++ks)
 #pragma unroll
-          for (int rt = 0; rt < NRT; ++rt) acc[rt] = mfma_bf16(A16[rt][ks], rq[ks], acc[rt]);
+          for (int u = 0; u < TPS; ++u)
+#pragma unroll
+            for (int rt = 0; rt < NRT; ++rt) acc[u][rt] = mfma_bf16(A16[rt][ks], rq[u][ks], acc[u][rt]);
         // rows 0 and 4 of the denominator product sit in lane rows 0 and 1
-        den = sum_over_rows(dacc[0]);
-      } else {
-        float qf[FPLa];
-        unpack_relu<BF16, FPLa>(qf, qw);
-        den = 0.f;
 #pragma unroll
-        for (int m = 0; m < FPLa; ++m) den += qf[m] * z[m];
-        if (ROPE) {
-          const uint32_t co = decode_packed((uint32_t)min(j, je - 1), geo.fHW, geo.fWs);
-          rope_lane<ROPE, NPAIR>(qf, tab, pl, co);
-        }
-#pragma unroll
-        for (int ks = 0; ks < NKS; ++ks)
-#pragma unroll
-          for (int rt = 0; rt < NRT; ++rt) acc[rt] = mfma_f32(A32[rt][ks], qf[ks], acc[rt]);
-        den = sum_over_rows(den);
-      }
-      // v_rcp_f32 (1 ulp) for bf16 outputs; a correctly rounded divide for fp32.
-      const float inv = BF16 ? __builtin_amdgcn_rcpf(den + eps) : 1.0f / (den + eps);
-      uint32_t ow[NW];
-      if (BF16) {
-#pragma unroll
-        for (int rt = 0; rt < NRT; ++rt) {
-          ow[2 * rt] = pack_bf16x2(acc[rt][0] * inv, acc[rt][1] * inv);
-          ow[2 * rt + 1] = pack_bf16x2(acc[rt][2] * inv, acc[rt][3] * inv);
-        }
+        for (int u = 0; u < TPS; ++u) den[u] = sum_over_rows(dacc[u][0]);
       } else {
 #pragma unroll
-        for (int rt = 0; rt < NRT; ++rt)
+        for (int u = 0; u < TPS; ++u) {
+          float qf[FPLa];
+          unpack_relu<BF16, FPLa>(qf, qw[u]);
+          float dn = 0.f;
 #pragma unroll
-          for (int i = 0; i < 4; ++i) ow[4 * rt + i] = __float_as_uint(acc[rt][i] * inv);
+          for (int m = 0; m < FPLa; ++m) dn += qf[m] * z[m];
+          if (ROPE) {
+            const uint32_t co = decode_packed((uint32_t)min(t + 16 * u + row, je - 1), geo.fHW, geo.fWs);
+            rope_lane<ROPE, NPAIR>(qf, tab, pl, co);
+          }
+#pragma unroll
+          for (int ks = 0; ks < NKS; ++ks)
+#pragma unroll
+            for (int rt = 0; rt < NRT; ++rt) acc[u][rt] = mfma_f32(A32[rt][ks], qf[ks], acc[u][rt]);
+          den[u] = sum_over_rows(dn);
+        }
       }
-      // MFMA layout -> global row layout through the same LDS tile
+      uint32_t ow[TPS][NW];
+#pragma unroll
+      for (int u = 0; u < TPS; ++u) {
+        // v_rcp_f32 (1 ulp) for bf16 outputs; a correctly rounded divide for fp32.
+        const float inv = BF16 ? __builtin_amdgcn_rcpf(den[u] + eps) : 1.0f / (den[u] + eps);
+        if (BF16) {
+#pragma unroll
+          for (int rt = 0; rt < NRT; ++rt) {
+            ow[u][2 * rt] = pack_bf16x2(acc[u][rt][0] * inv, acc[u][rt][1] * inv);
+            ow[u][2 * rt + 1] = pack_bf16x2(acc[u][rt][2] * inv, acc[u][rt][3] * inv);
+          }
+        } else {
+#pragma unroll
+          for (int rt = 0; rt < NRT; ++rt)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) ow[u][4 * rt + i] = __float_as_uint(acc[u][rt][i] * inv);
+        }
+      }
+      // MFMA layout -> global row layout through the same LDS tiles
       __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
 #pragma unroll
-      for (int i = 0; i < NW / 4; ++i) wst[row * SROW + 4 * i + g] = make_uint4(ow[4 * i], ow[4 * i + 1], ow[4 * i + 2], ow[4 * i + 3]);
-      __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
-      const uint32_t off = (uint32_t)(t + ld_row) * ROWB + 16 * ld_piece;
+      for (int u = 0; u < TPS; ++u)
 #pragma unroll
-      for (int i = 0; i < NLD; ++i) {
-        const uint4 v = wst[(i * RPI + ld_row) * SROW + ld_piece];
-        const uint32_t w4[4] = {v.x, v.y, v.z, v.w};
-        buf_store<4>(ors, off + i * RPI * ROWB, w4);
+        for (int i = 0; i < NW / 4; ++i)
+          wst[u * TSZ + row * SROW + 4 * i + g] = make_uint4(ow[u][4 * i], ow[u][4 * i + 1], ow[u][4 * i + 2], ow[u][4 * i + 3]);
+      __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
+#pragma unroll
+      for (int u = 0; u < TPS; ++u) {
+        const uint32_t off = (uint32_t)(t + 16 * u + ld_row) * ROWB + 16 * ld_piece;
+#pragma unroll
+        for (int i = 0; i < NLD; ++i) {
+          const uint4 v = wst[u * TSZ + (i * RPI + ld_row) * SROW + ld_piece];
+          const uint32_t w4[4] = {v.x, v.y, v.z, v.w};
+          buf_store<4>(ors, off + i * RPI * ROWB, w4);
+        }
       }
       __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
     };
 
     // TPS 16-token tiles per wave step (the first two steps were issued
-    // above), software-pipelined over a ring of three register sets: while step k computes (and issues its stores),
-    // the loads of steps k+1 and k+2 are in flight.  gfx9 counts loads and
-    // stores in one in-order counter, so the wait for step k+1's loads never
-    // has to cover step k's stores, which were issued after them.
-    auto compute_stepq = [&](const uint32_t (&x)[TPS][NW], int t) {
-#pragma unroll
-      for (int i = 0; i < TPS; ++i) compute_tile(x[i], t + 16 * i);
-    };
+    // above), software-pipelined over a ring of three register sets: while
+    // step k computes (and issues its stores), the loads of steps k+1 and k+2
+    // are in flight.  gfx9 counts loads and stores in one in-order counter,
+    // so the wait for step k+1's loads never has to cover step k's stores,
+    // which were issued after them.
     int k = 0;
     for (; k + 3 <= nsteps; k += 3) {
       const int t0 = t_first + k * WSTRIDE;
