@@ -846,20 +846,24 @@ __global__ __launch_bounds__(app_threads<BF16>(), app_min_blocks<BF16>()) void s
 
   // Tile I/O goes through LDS so that every global load and store
   // instruction covers whole 128-byte lines: PPR lanes per row, RPI rows per
-  // instruction.  Each wave has its own padded tile (no barrier needed:
-  // a wave's LDS operations execute in order).
+  // instruction.  Each wave has its own tiles (no barrier needed: a wave's
+  // LDS operations execute in order).  Piece p of row r sits at unit
+  // r*PPR + (p ^ (r & SWM)): the XOR swizzle spreads both the row-order and
+  // the MFMA-order 16-byte accesses over all banks (measured on gfx950:
+  // about 5 clocks per 64-lane read instead of 8.5 with a padded row).
   constexpr int ROWB = D * ESZ;
   constexpr int PPR = ROWB / 16;  // 16-byte pieces per token row
   constexpr int RPI = 64 / PPR;   // rows per instruction
   constexpr int NLD = 16 / RPI;   // instructions per 16-row tile
-  constexpr int SROW = ROWB / 16 + 1;  // padded LDS row stride, in 16-byte units
+  constexpr int SWM = (PPR < 8 ? PPR : 8) - 1;
   static_assert(NLD * 4 == NW, "tile pieces");
+  auto tile_at = [](int r, int p) { return r * PPR + (p ^ (r & SWM)); };
 
   extern __shared__ float4 tab_raw[];  // 16-byte aligned
   float2* tab = reinterpret_cast<float2*>(tab_raw);
   __shared__ uint4 fstage[FRAG_U4];
   constexpr int TPS = 2;          // 16-token tiles per wave step
-  constexpr int TSZ = 16 * SROW;  // one tile, in 16-byte units
+  constexpr int TSZ = 16 * PPR;   // one tile, in 16-byte units
   __shared__ uint4 tstage[AT / 64][TPS * TSZ];
 
   const int tid = threadIdx.x;
@@ -999,7 +1003,7 @@ __global__ __launch_bounds__(app_threads<BF16>(), app_min_blocks<BF16>()) void s
       for (int u = 0; u < TPS; ++u)
 #pragma unroll
         for (int i = 0; i < NLD; ++i)
-          wst[u * TSZ + (i * RPI + ld_row) * SROW + ld_piece] =
+          wst[u * TSZ + tile_at(i * RPI + ld_row, ld_piece)] =
               make_uint4(x[u][4 * i], x[u][4 * i + 1], x[u][4 * i + 2], x[u][4 * i + 3]);
       __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
       uint32_t qw[TPS][NW];
@@ -1007,7 +1011,7 @@ __global__ __launch_bounds__(app_threads<BF16>(), app_min_blocks<BF16>()) void s
       for (int u = 0; u < TPS; ++u)
 #pragma unroll
         for (int i = 0; i < NW / 4; ++i) {
-          const uint4 v = wst[u * TSZ + row * SROW + 4 * i + g];
+          const uint4 v = wst[u * TSZ + tile_at(row, 4 * i + g)];
           qw[u][4 * i] = v.x; qw[u][4 * i + 1] = v.y; qw[u][4 * i + 2] = v.z; qw[u][4 * i + 3] = v.w;
         }
       floatx4 acc[TPS][NRT];
@@ -1097,14 +1101,14 @@ __global__ __launch_bounds__(app_threads<BF16>(), app_min_blocks<BF16>()) void s
       for (int u = 0; u < TPS; ++u)
 #pragma unroll
         for (int i = 0; i < NW / 4; ++i)
-          wst[u * TSZ + row * SROW + 4 * i + g] = make_uint4(ow[u][4 * i], ow[u][4 * i + 1], ow[u][4 * i + 2], ow[u][4 * i + 3]);
+          wst[u * TSZ + tile_at(row, 4 * i + g)] = make_uint4(ow[u][4 * i], ow[u][4 * i + 1], ow[u][4 * i + 2], ow[u][4 * i + 3]);
       __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
 #pragma unroll
       for (int u = 0; u < TPS; ++u) {
         const uint32_t off = (uint32_t)(t + 16 * u + ld_row) * ROWB + 16 * ld_piece;
 #pragma unroll
         for (int i = 0; i < NLD; ++i) {
-          const uint4 v = wst[u * TSZ + (i * RPI + ld_row) * SROW + ld_piece];
+          const uint4 v = wst[u * TSZ + tile_at(i * RPI + ld_row, ld_piece)];
           const uint32_t w4[4] = {v.x, v.y, v.z, v.w};
           buf_store<4>(ors, off + i * RPI * ROWB, w4);
         }
