@@ -148,39 +148,39 @@ __device__ void build_rope_t(float2* tab, const RopeArgs& ra, int c) {
   }
 }
 
-// A token's RoPE coordinates packed in one word: frame within its block (the
-// t-table row) in bits 21..31, h in bits 10..20, w in bits 0..9, decoded from
-// the block-local token index.  The host rejects RoPE grids that do not fit
-// (F, Hs <= 2048, Ws <= 1024).
+// A token's RoPE coordinates packed in one word, ten bits each: frame within
+// its block (the t-table row) in bits 20..29, h in bits 10..19, w in bits
+// 0..9, decoded from the block-local token index.  The host rejects RoPE
+// grids that do not fit (F, Hs, Ws <= 1024).
 __device__ __forceinline__ uint32_t decode_packed(uint32_t n, const FastDiv& fHW, const FastDiv& fWs) {
   const uint32_t frame = fdiv(n, fHW);
   const uint32_t rem = n - frame * fHW.div;
   const uint32_t h = fdiv(rem, fWs);
   const uint32_t w = rem - h * fWs.div;
-  return (frame << 21) | (h << 10) | w;
+  return (frame << 20) | (h << 10) | w;
 }
 
 // Table entry of one RoPE pair: row base + stride * coordinate, where the
-// coordinate is a bit field of the packed word.
+// coordinate is the ten-bit field of the packed word at `shift`.
 struct PairLoc {
-  int base, stride, shift, width;
+  int base, stride, shift;
 };
 
 __device__ __forceinline__ PairLoc pair_loc(int p, const RopeArgs& ra) {
   const int ht = ra.dt >> 1, hh = ra.dh >> 1;
   PairLoc r;
   if (p < ht) {
-    r.base = p; r.stride = ht; r.shift = 21; r.width = 11;
+    r.base = p; r.stride = ht; r.shift = 20;
   } else if (p < ht + hh) {
-    r.base = ra.off_h + (p - ht); r.stride = hh; r.shift = 10; r.width = 11;
+    r.base = ra.off_h + (p - ht); r.stride = hh; r.shift = 10;
   } else {
-    r.base = ra.off_w + (p - ht - hh); r.stride = ra.dw >> 1; r.shift = 0; r.width = 10;
+    r.base = ra.off_w + (p - ht - hh); r.stride = ra.dw >> 1; r.shift = 0;
   }
   return r;
 }
 
 __device__ __forceinline__ int pair_entry(const PairLoc& pl, uint32_t packed) {
-  const uint32_t pos = __builtin_amdgcn_ubfe(packed, (uint32_t)pl.shift, (uint32_t)pl.width);
+  const uint32_t pos = __builtin_amdgcn_ubfe(packed, (uint32_t)pl.shift, 10u);
   return __mul24((int)pos, pl.stride) + pl.base;  // 24-bit multiply: operands are small
 }
 
@@ -654,15 +654,18 @@ __global__ __launch_bounds__(red_threads<BF16>(), red_min_blocks<BF16>()) void s
     // Piece (workgroup g, block bhc) goes to slot g + bhc: pieces are ordered
     // along the flattened token axis, so g + bhc strictly increases from one
     // piece to the next and the slots of one block's pieces are contiguous.
+    // A partial holds S transposed (row fo, column fi), then z.
     float* dst = partials + ((long long)blockIdx.x + bhc) * E;
-    for (int e = 4 * tid; e < D * D; e += 4 * RT) {
-      float4 t = *(const float4*)(red[0] + e);
+    for (int e = tid; e < D * D / 4; e += RT) {
+      const int fo = e % D, fi0 = 4 * (e / D);  // consecutive lanes: consecutive fo
+      float t[4];
 #pragma unroll
-      for (int w = 1; w < NT; ++w) {
-        const float4 u = *(const float4*)(red[w] + e);
-        t.x += u.x; t.y += u.y; t.z += u.z; t.w += u.w;
+      for (int j = 0; j < 4; ++j) {
+        t[j] = red[0][(fi0 + j) * D + fo];
+#pragma unroll
+        for (int w = 1; w < NT; ++w) t[j] += red[w][(fi0 + j) * D + fo];
       }
-      *(float4*)(dst + e) = t;
+      *(float4*)(dst + fo * D + fi0) = make_float4(t[0], t[1], t[2], t[3]);
     }
     for (int e = tid; e < D; e += RT) {
       float t = zred[0][e];
@@ -678,14 +681,11 @@ __global__ __launch_bounds__(red_threads<BF16>(), red_min_blocks<BF16>()) void s
 // ---------------------------------------------------------------------------
 // Kernel 2: inclusive prefix over blocks, fixed order
 //
-// One thread per state element (d*d entries of S, then d of z) per (b, h).
-// Output-kernel A operand layout (the MFMA computes out^T = S^T qr^T): for
-// k-step ks, accumulator rt and lane l = 16*g + r, the operand holds
-// S[fi][fo] with fi = feat(g, k-slot) of the output kernel and
-//   bf16: fo = 32*(rt/2) + 8*(r/4) + 4*(rt%2) + r%4
-//   fp32: fo = 16*rt + r
-// so that accumulator rt of lane l holds the output features the lane stores
-// in one contiguous 16-byte piece.
+// One thread per state element per (b, h).  Partials and the emitted prefix
+// operands hold S transposed (row fo = value feature, column fi = key
+// feature), then z, so consecutive threads read and write consecutive
+// addresses; the output kernel reads its MFMA operands straight from that
+// layout.  S0 and S_out use the caller's [fi][fo] layout.
 // ---------------------------------------------------------------------------
 
 struct ScanArgs {
@@ -729,8 +729,6 @@ __global__ __launch_bounds__(kThreads) void sva_scan_kernel(
     const float* __restrict__ partials, const float* S0, const float* z0, float* S_out,
     float* z_out, void* __restrict__ frags, float* __restrict__ zc, ScanArgs a) {
   constexpr int E = D * D + D;
-  constexpr int FPLa = D / 4;
-  constexpr int NKS = BF16 ? D / 32 : D / 4;
   __shared__ float lane_tot[kScanLanes][kScanElems];
   const int tx = threadIdx.x % kScanElems;
   const int ty = threadIdx.x / kScanElems;
@@ -745,7 +743,7 @@ __global__ __launch_bounds__(kThreads) void sva_scan_kernel(
   // written after it.
   float run = 0.f;
   if (active && a.has_init)
-    run = in_S ? S0[(long long)bh * D * D + e] : z0[(long long)bh * D + (e - D * D)];
+    run = in_S ? S0[(long long)bh * D * D + (e % D) * D + e / D] : z0[(long long)bh * D + (e - D * D)];
   // Pass 1: block sums of this lane's blocks.  Up to kKeep of them stay in
   // registers for pass 2; lanes with more blocks re-read theirs (L2 hits).
   constexpr int kKeep = 4;
@@ -765,23 +763,6 @@ __global__ __launch_bounds__(kThreads) void sva_scan_kernel(
   if (!active) return;
   for (int l = 0; l < ty; ++l) run += lane_tot[l][tx];
 
-  int frag_off = 0;
-  if (in_S) {
-    // Inverse of the output kernel's maps: input feature fi is local element
-    // m of lane group g (k-slot of k-step ks); output feature fo is row r of
-    // accumulator rt.
-    const int fi = e / D, fo = e % D;
-    if (BF16) {
-      const int g = (fi & 31) >> 3, ks = fi >> 5, el = fi & 7;
-      const int rt = 2 * (fo >> 5) + ((fo & 7) >> 2);
-      const int r = 4 * ((fo & 31) >> 3) + (fo & 3);
-      frag_off = ((rt * NKS + ks) * 64 + 16 * g + r) * 8 + el;
-    } else {
-      const int g = (fi & 15) >> 2, ks = 4 * (fi >> 4) + (fi & 3);
-      const int rt = fo >> 4, r = fo & 15;
-      frag_off = (rt * NKS + ks) * 64 + 16 * g + r;
-    }
-  }
   for (int c = c_begin; c < c_end; ++c) {
     const long long bhc = (long long)bh * a.nb + c;
     float bs = 0.f;
@@ -795,15 +776,15 @@ __global__ __launch_bounds__(kThreads) void sva_scan_kernel(
     run += bs;
     if (a.write_frags) {
       if (in_S) {
-        if (BF16) ((__bf16*)frags)[bhc * D * D + frag_off] = (__bf16)run;
-        else ((float*)frags)[bhc * D * D + frag_off] = run;
+        if (BF16) ((__bf16*)frags)[bhc * D * D + e] = (__bf16)run;
+        else ((float*)frags)[bhc * D * D + e] = run;
       } else {
         zc[bhc * D + (e - D * D)] = run;
       }
     }
   }
   if (a.write_final && c_begin < c_end && c_end == a.nb) {
-    if (in_S) S_out[(long long)bh * D * D + e] = run;
+    if (in_S) S_out[(long long)bh * D * D + (e % D) * D + e / D] = run;
     else z_out[(long long)bh * D + (e - D * D)] = run;
   }
 }
@@ -842,7 +823,6 @@ __global__ __launch_bounds__(app_threads<BF16>(), app_min_blocks<BF16>()) void s
   constexpr int NPAIR = FPLa / 2;
   constexpr int ESZ = BF16 ? 2 : 4;
   constexpr int NW = FPLa * ESZ / 4;
-  constexpr int FRAG_U4 = D * D * ESZ / 16;
 
   // Tile I/O goes through LDS so that every global load and store
   // instruction covers whole 128-byte lines: PPR lanes per row, RPI rows per
@@ -861,7 +841,13 @@ __global__ __launch_bounds__(app_threads<BF16>(), app_min_blocks<BF16>()) void s
 
   extern __shared__ float4 tab_raw[];  // 16-byte aligned
   float2* tab = reinterpret_cast<float2*>(tab_raw);
+  // The block's prefix operand S^T (D rows of CPR 16-byte chunks) is staged
+  // in LDS with chunk c of row f at f*CPR + (c ^ (f & (CPR-1))), so that the
+  // sixteen rows a k-step's lanes read spread over the banks.
+  constexpr int CPR = D * ESZ / 16;
+  constexpr int FRAG_U4 = D * CPR;
   __shared__ uint4 fstage[FRAG_U4];
+  auto frag_at = [](int f, int c) { return f * CPR + (c ^ (f & (CPR - 1))); };
   constexpr int TPS = 2;          // 16-token tiles per wave step
   constexpr int TSZ = 16 * PPR;   // one tile, in 16-byte units
   __shared__ uint4 tstage[AT / 64][TPS * TSZ];
@@ -913,12 +899,12 @@ __global__ __launch_bounds__(app_threads<BF16>(), app_min_blocks<BF16>()) void s
       for (int i = 0; i < NLD; ++i) buf_load<4>(qw + 4 * i, qrs, off + i * RPI * ROWB);
     };
 
-    // Segment prologue.  The prefix operands of this block are loaded first,
+    // Segment prologue.  The prefix operand of this block is loaded first,
     // then the segment's first two steps of q: vector memory results return
-    // in issue order, so staging the operands waits for them only and the q
-    // loads stay in flight while the operands (and, in the first segment,
-    // the RoPE table) go to LDS.
-    lds_barrier();  // every wave has read the previous segment's fstage
+    // in issue order, so staging the operand waits for it only and the q
+    // loads stay in flight while the operand (and the RoPE table rows) go to
+    // LDS.
+    lds_barrier();  // every wave has read the previous segment's fstage and t rows
     constexpr int FR = (FRAG_U4 + AT - 1) / AT;
     uint4 fr[FR];
     {
@@ -973,26 +959,41 @@ __global__ __launch_bounds__(app_threads<BF16>(), app_min_blocks<BF16>()) void s
       build_rope_t<!BF16>(tab, ra, c);
     }
 #pragma unroll
-    for (int i = 0; i < FR; ++i)
-      if (FRAG_U4 % AT == 0 || tid + i * AT < FRAG_U4) fstage[tid + i * AT] = fr[i];
+    for (int i = 0; i < FR; ++i) {
+      const int u = tid + i * AT;
+      if (FRAG_U4 % AT == 0 || u < FRAG_U4) fstage[frag_at(u / CPR, u % CPR)] = fr[i];
+    }
     lds_barrier();
 
+    // MFMA A operands.  bf16: accumulator rt, lane row r holds output feature
+    //   fo = 32*(rt/2) + 8*(r/4) + 4*(rt%2) + r%4,
+    // so that accumulator rt holds the features the lane stores in one
+    // contiguous 16-byte piece; k-step ks, lane group g: input features
+    // 32*ks + 8*g .. +7 (chunk 4*ks + g of row fo).  fp32: fo = 16*rt + r,
+    // k-step ks: input feature feat(g, ks), four consecutive ks in chunk
+    // 4*(ks/4) + g.
     u32x4 A16[BF16 ? NRT : 1][BF16 ? NKS : 1];
     float A32[BF16 ? 1 : NRT][BF16 ? 1 : NKS];
-    if (BF16) {
+    if constexpr (BF16) {
 #pragma unroll
-      for (int rt = 0; rt < NRT; ++rt)
+      for (int rt = 0; rt < NRT; ++rt) {
+        const int fo = 32 * (rt >> 1) + 8 * (row >> 2) + 4 * (rt & 1) + (row & 3);
 #pragma unroll
         for (int ks = 0; ks < NKS; ++ks) {
-          const uint4 t = fstage[(rt * NKS + ks) * 64 + lane];
+          const uint4 t = fstage[frag_at(fo, 4 * ks + g)];
           A16[rt][ks] = u32x4{t.x, t.y, t.z, t.w};
         }
+      }
     } else {
-      const float* fs = (const float*)fstage;
 #pragma unroll
-      for (int rt = 0; rt < NRT; ++rt)
+      for (int rt = 0; rt < NRT; ++rt) {
+        const int fo = 16 * rt + row;
 #pragma unroll
-        for (int ks = 0; ks < NKS; ++ks) A32[rt][ks] = fs[(rt * NKS + ks) * 64 + lane];
+        for (int ks = 0; ks < NKS; ks += 4) {
+          const float4 t = __builtin_bit_cast(float4, fstage[frag_at(fo, ks + g)]);
+          A32[rt][ks] = t.x; A32[rt][ks + 1] = t.y; A32[rt][ks + 2] = t.z; A32[rt][ks + 3] = t.w;
+        }
+      }
     }
 
     // The TPS tiles of a step go through each phase together, so that their
@@ -1275,8 +1276,8 @@ sva_status validate_desc(const sva_desc* d, bool one_block) {
     const long long entries = (long long)d->frames_per_block * (d->rope_dt / 2) +
                               (long long)d->Hs * (d->rope_dh / 2) + (long long)d->Ws * (d->rope_dw / 2);
     if (entries > kMaxTableEntries) return SVA_ERR_UNSUPPORTED;
-    // packed token coordinates: frame-in-block and h in 11 bits, w in 10
-    if (d->frames_per_block > 2048 || d->Hs > 2048 || d->Ws > 1024) return SVA_ERR_UNSUPPORTED;
+    // packed token coordinates: frame-in-block, h and w in 10 bits each
+    if (d->frames_per_block > 1024 || d->Hs > 1024 || d->Ws > 1024) return SVA_ERR_UNSUPPORTED;
   }
   return SVA_OK;
 }

@@ -60,7 +60,10 @@ typedef enum sva_dtype { SVA_F32 = 0, SVA_BF16 = 1 } sva_dtype;
 typedef enum sva_status {
   SVA_OK = 0,
   SVA_ERR_INVALID_ARG = -1,  /* null/misaligned pointer, bad shape, overlap */
-  SVA_ERR_UNSUPPORTED = -2,  /* d not 32/64, bad RoPE split, grid too large */
+  SVA_ERR_UNSUPPORTED = -2,  /* d not 32/64, bad RoPE split, grid too large
+                                (with RoPE: F, Hs, Ws <= 1024 and at most 4096
+                                cos/sin table entries, F*dt/2 + Hs*dh/2 +
+                                Ws*dw/2) */
   SVA_ERR_WORKSPACE = -3,    /* workspace missing or smaller than required */
   SVA_ERR_HIP = -4           /* a HIP launch failed */
 } sva_status;

@@ -78,6 +78,8 @@ BAD = [
     (dict(eps=-1.0), sva.SVA_ERR_INVALID_ARG),
     (dict(t0=-3), sva.SVA_ERR_INVALID_ARG),
     (dict(grid=(240, 400, 400)), sva.SVA_ERR_UNSUPPORTED),  # RoPE table too large
+    # small table, but h does not fit the 10-bit packed coordinate
+    (dict(grid=(21, 1025, 4), split=(2, 2, 60)), sva.SVA_ERR_UNSUPPORTED),
 ]
 
 
