@@ -698,74 +698,88 @@ struct ScanArgs {
 };
 
 constexpr int kScanLanes = 8;                      // block-lanes per element
-constexpr int kScanElems = kThreads / kScanLanes;  // elements per workgroup
+constexpr int kScanElems = kThreads / kScanLanes;  // 4-element groups per workgroup
 
 // Sum, in slot order, of the partials of flattened block bhc at element e.
+__device__ __forceinline__ void add4(float4& a, const float4& b) {
+  a.x += b.x; a.y += b.y; a.z += b.z; a.w += b.w;
+}
+
+// Sum, in slot order, of the partials of flattened block bhc at elements
+// e .. e+3.
 template <int E>
-__device__ __forceinline__ float block_sum(const float* __restrict__ partials, long long bhc,
-                                           long long L, int Nb, int e) {
+__device__ __forceinline__ float4 block_sum(const float* __restrict__ partials, long long bhc,
+                                            long long L, int Nb, int e) {
   const long long start = bhc * Nb;
   const long long gf = start / L, gl = (start + Nb - 1) / L;
   const float* p = partials + (gf + bhc) * E + e;
   const int n = (int)(gl - gf + 1);
-  float s = 0.f;
+  float4 s = make_float4(0.f, 0.f, 0.f, 0.f);
   int i = 0;
   for (; i + 4 <= n; i += 4) {
-    const float x0 = p[(long long)i * E], x1 = p[(long long)(i + 1) * E];
-    const float x2 = p[(long long)(i + 2) * E], x3 = p[(long long)(i + 3) * E];
-    s += x0; s += x1; s += x2; s += x3;
+    const float4 x0 = *(const float4*)(p + (long long)i * E), x1 = *(const float4*)(p + (long long)(i + 1) * E);
+    const float4 x2 = *(const float4*)(p + (long long)(i + 2) * E), x3 = *(const float4*)(p + (long long)(i + 3) * E);
+    add4(s, x0); add4(s, x1); add4(s, x2); add4(s, x3);
   }
-  for (; i < n; ++i) s += p[(long long)i * E];
+  for (; i < n; ++i) add4(s, *(const float4*)(p + (long long)i * E));
   return s;
 }
 
-// kScanElems elements x kScanLanes block-lanes per workgroup.  Lane ty owns
-// blocks [ty*cpl, ty*cpl + cpl): pass 1 sums them, the lane totals are
-// scanned through LDS in lane order, pass 2 re-sums each block (the
-// partials are L2-resident) and emits the running prefix.  The order of
-// every sum is fixed by (nb, reduce grid), so results are reproducible.
+// kScanElems groups of 4 elements x kScanLanes block-lanes per workgroup.
+// Lane ty owns blocks [ty*cpl, ty*cpl + cpl): pass 1 sums them, the lane
+// totals are scanned through LDS in lane order, pass 2 adds each block in
+// turn (kept in registers, or re-read: the partials are L2-resident) and
+// emits the running prefix.  The order of every sum is fixed by (nb, reduce
+// grid), so results are reproducible.
 template <bool BF16, int D>
 __global__ __launch_bounds__(kThreads) void sva_scan_kernel(
     const float* __restrict__ partials, const float* S0, const float* z0, float* S_out,
     float* z_out, void* __restrict__ frags, float* __restrict__ zc, ScanArgs a) {
   constexpr int E = D * D + D;
-  __shared__ float lane_tot[kScanLanes][kScanElems];
+  static_assert(E % 4 == 0 && (D * D) % 4 == 0, "element groups");
+  __shared__ float4 lane_tot[kScanLanes][kScanElems];
   const int tx = threadIdx.x % kScanElems;
   const int ty = threadIdx.x / kScanElems;
-  const int e = blockIdx.x * kScanElems + tx;
+  const int e = 4 * (blockIdx.x * kScanElems + tx);  // first of 4 consecutive elements
   const int bh = blockIdx.y;
   const bool active = e < E;
-  const bool in_S = e < D * D;
+  const bool in_S = e < D * D;  // a group never straddles S and z
   const int c_begin = min(ty * a.cpl, a.nb);
   const int c_end = min(c_begin + a.cpl, a.nb);
 
   // The initial cache is read before the barrier: S_out may alias S0 and is
-  // written after it.
-  float run = 0.f;
-  if (active && a.has_init)
-    run = in_S ? S0[(long long)bh * D * D + (e % D) * D + e / D] : z0[(long long)bh * D + (e - D * D)];
+  // written after it.  Element e of S^T is S[e % D][e / D].
+  float4 run = make_float4(0.f, 0.f, 0.f, 0.f);
+  if (active && a.has_init) {
+    if (in_S) {
+      const float* s0 = S0 + (long long)bh * D * D + (e % D) * D + e / D;
+      run = make_float4(s0[0], s0[D], s0[2 * D], s0[3 * D]);
+    } else {
+      run = *(const float4*)(z0 + (long long)bh * D + (e - D * D));
+    }
+  }
   // Pass 1: block sums of this lane's blocks.  Up to kKeep of them stay in
   // registers for pass 2; lanes with more blocks re-read theirs (L2 hits).
   constexpr int kKeep = 4;
-  float keep[kKeep];
-  float tot = 0.f;
+  float4 keep[kKeep];
+  float4 tot = make_float4(0.f, 0.f, 0.f, 0.f);
   if (active) {
     for (int c = c_begin; c < c_end; ++c) {
-      const float bs = block_sum<E>(partials, (long long)bh * a.nb + c, a.L, a.Nb, e);
+      const float4 bs = block_sum<E>(partials, (long long)bh * a.nb + c, a.L, a.Nb, e);
 #pragma unroll
       for (int i = 0; i < kKeep; ++i)
         if (c - c_begin == i) keep[i] = bs;
-      tot += bs;
+      add4(tot, bs);
     }
   }
   lane_tot[ty][tx] = tot;
   __syncthreads();
   if (!active) return;
-  for (int l = 0; l < ty; ++l) run += lane_tot[l][tx];
+  for (int l = 0; l < ty; ++l) add4(run, lane_tot[l][tx]);
 
   for (int c = c_begin; c < c_end; ++c) {
     const long long bhc = (long long)bh * a.nb + c;
-    float bs = 0.f;
+    float4 bs;
     if (c - c_begin < kKeep) {
 #pragma unroll
       for (int i = 0; i < kKeep; ++i)
@@ -773,19 +787,26 @@ __global__ __launch_bounds__(kThreads) void sva_scan_kernel(
     } else {
       bs = block_sum<E>(partials, bhc, a.L, a.Nb, e);
     }
-    run += bs;
+    add4(run, bs);
     if (a.write_frags) {
       if (in_S) {
-        if (BF16) ((__bf16*)frags)[bhc * D * D + e] = (__bf16)run;
-        else ((float*)frags)[bhc * D * D + e] = run;
+        if (BF16) {
+          *(uint2*)((__bf16*)frags + bhc * D * D + e) = make_uint2(pack_bf16x2(run.x, run.y), pack_bf16x2(run.z, run.w));
+        } else {
+          *(float4*)((float*)frags + bhc * D * D + e) = run;
+        }
       } else {
-        zc[bhc * D + (e - D * D)] = run;
+        *(float4*)(zc + bhc * D + (e - D * D)) = run;
       }
     }
   }
   if (a.write_final && c_begin < c_end && c_end == a.nb) {
-    if (in_S) S_out[(long long)bh * D * D + (e % D) * D + e / D] = run;
-    else z_out[(long long)bh * D + (e - D * D)] = run;
+    if (in_S) {
+      float* so = S_out + (long long)bh * D * D + (e % D) * D + e / D;
+      so[0] = run.x; so[D] = run.y; so[2 * D] = run.z; so[3 * D] = run.w;
+    } else {
+      *(float4*)(z_out + (long long)bh * D + (e - D * D)) = run;
+    }
   }
 }
 
@@ -1369,9 +1390,9 @@ hipError_t launch_scan(const Plan& p, const float* partials, const float* S0, co
   a.write_final = S_out != nullptr;
   void* args[] = {(void*)&partials, (void*)&S0, (void*)&z0, (void*)&S_out, (void*)&z_out,
                   (void*)&frags, (void*)&zc, &a};
-  const int E = D * D + D;
+  constexpr int groups = (D * D + D) / 4;
   return hipLaunchKernel((const void*)&sva_scan_kernel<BF16, D>,
-                         dim3((E + kScanElems - 1) / kScanElems, p.BH), dim3(kThreads), args, 0, st);
+                         dim3((groups + kScanElems - 1) / kScanElems, p.BH), dim3(kThreads), args, 0, st);
 }
 
 template <bool BF16, int D, int ROPE>
