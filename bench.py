@@ -258,7 +258,7 @@ def main():
     ap.add_argument("--warmup", type=int, default=100)
     ap.add_argument("--workload", default="720p")
     ap.add_argument("--sets", type=int, default=2, help="input buffer sets that alternate between steps")
-    ap.add_argument("--cpu-reps", type=int, default=2)
+    ap.add_argument("--cpu-reps", type=int, default=4)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-calib", type=int, default=0, metavar="MIB",
                     help="also run a plain fp32 streaming kernel over MIB MiB (counter calibration)")
