@@ -35,6 +35,10 @@ Readings taken where the pages are silent (each is a choice, not a quote):
     frames; a token sees its own block (bidirectionally) and every earlier
     block; the initial cache is zero unless one is given.
 
+The backward (lin_attn_bwd) is reverse-mode differentiation of the same
+steps, for the training the pages run block-causally ([talk], block causal
+segment); it is pinned by finite differences of lin_attn_fwd.
+
 Parity unpinned: the RoPE pair convention (interleaved adjacent pairs) and
 frequency schedule cannot be checked against the authors' code, which the
 pages do not hold.  Everything else here is pinned by the CPU tests against
@@ -53,6 +57,7 @@ __all__ = [
     "lin_attn_fwd",
     "block_cache_apply",
     "block_cache_commit",
+    "lin_attn_bwd",
 ]
 
 
@@ -224,3 +229,113 @@ def block_cache_commit(S, z, k, v, frame_grid, *, t0, rope=False, split=None,
             S_new[b, h] += A[0]
             z_new[b, h] += Zb[0]
     return S_new, z_new
+
+
+def _rope_transpose(x, t, h, w, split, base):
+    """Transpose of rope_rotate at (t, h, w): every pair turns by the opposite
+    angle, i.e. the same rotation at negated positions."""
+    return rope_rotate(x, -np.asarray(t), -np.asarray(h), -np.asarray(w), split, base)
+
+
+def _relu_grad(x):
+    """d/dx ReLU(x): 1 where x > 0, 0 elsewhere (0 taken at the kink)."""
+    return (np.asarray(x) > 0).astype(np.float64)
+
+
+def _suffix_sum(x):
+    """Inclusive suffix sums along axis 0: the transpose of the block prefix."""
+    return np.cumsum(x[::-1], axis=0)[::-1]
+
+
+def _out_grads(qt_c, pq_c, S_c, Z_c, dout_c, eps):
+    """Gradients through one block's outputs o = (qt S_c) / (pq . Z_c + eps):
+    returns (dqt, dpq from the denominator, dS_c, dZ_c)."""
+    num = qt_c @ S_c
+    den = pq_c @ Z_c + eps
+    dnum = dout_c / den[:, None]
+    dden = -(dout_c * num).sum(axis=1) / den ** 2
+    return dnum @ S_c.T, dden[:, None] * Z_c[None, :], qt_c.T @ dnum, pq_c.T @ dden
+
+
+def _state_grads(kt_c, v_c, G_c, g_c):
+    """Gradients through one block's state A_c = kt^T v, zeta_c = sum pk when
+    G_c, g_c reach A_c, zeta_c: returns (dkt, dv, dpk)."""
+    return v_c @ G_c.T, kt_c @ G_c, np.broadcast_to(g_c[None, :], kt_c.shape)
+
+
+def _bwd_slice(q, k, v, dout, grid, F, t0, rope, split, base, eps, S0, z0, dS_fin, dz_fin):
+    """Reverse mode through _fwd_slice, step by step in the opposite order.
+
+    Forward (per block c):  num = qt S_c,  den = pq . Z_c + eps,  o = num/den,
+    with S_c = S0 + sum_{c'<=c} A_c', Z_c = z0 + sum_{c'<=c} zeta_c',
+    A_c = sum kt v^T, zeta_c = sum pk.  Given dout (and optionally the
+    gradient of the final state S_{nb-1}, Z_{nb-1}):
+      dnum = dout / den,  dden = -(dout . num) / den^2
+      dqt = dnum S_c^T,   dS_c = qt^T dnum,   dZ_c = pq^T dden,  dpq += dden Z_c
+    The prefix turns into a suffix: the gradient reaching A_c (and S0) is
+    G_c = sum_{c'>=c} dS_c' (+ dS_final), likewise g_c for zeta_c, so
+      dkt = v G_c^T,  dv = kt G_c,  dpk = g_c.
+    RoPE is a rotation per token, so its transpose is the rotation by the
+    opposite angle, and d/dx ReLU(x) = 1 for x > 0, else 0."""
+    T, Hs, Ws = grid
+    N, d = q.shape
+    block_len = F * Hs * Ws
+    nb = T // F
+    q = np.asarray(q, dtype=np.float64)
+    k = np.asarray(k, dtype=np.float64)
+    v = np.asarray(v, dtype=np.float64)
+    dout = np.asarray(dout, dtype=np.float64)
+    pq, pk, qt, kt = _prep(q, k, grid, t0, rope, split, base)
+    A, Z = block_states(kt, pk, v, block_len)
+    S = np.asarray(S0, dtype=np.float64)[None] + np.cumsum(A, axis=0)
+    Zc = np.asarray(z0, dtype=np.float64)[None] + np.cumsum(Z, axis=0)
+    dqt = np.empty_like(qt)
+    dpq = np.empty_like(pq)
+    dS = np.empty_like(S)
+    dZ = np.empty_like(Zc)
+    for c in range(nb):
+        sl = slice(c * block_len, (c + 1) * block_len)
+        dqt[sl], dpq[sl], dS[c], dZ[c] = _out_grads(qt[sl], pq[sl], S[c], Zc[c], dout[sl], eps)
+    # everything from block c on sees A_c: the prefix becomes a suffix
+    G = _suffix_sum(dS) + np.asarray(dS_fin, dtype=np.float64)[None]
+    g = _suffix_sum(dZ) + np.asarray(dz_fin, dtype=np.float64)[None]
+    dkt = np.empty_like(kt)
+    dv = np.empty_like(v)
+    dpk = np.empty_like(pk)
+    for c in range(nb):
+        sl = slice(c * block_len, (c + 1) * block_len)
+        dkt[sl], dv[sl], dpk[sl] = _state_grads(kt[sl], v[sl], G[c], g[c])
+    if rope:
+        t, h, w = token_coords(T, Hs, Ws, t0)
+        dpq = dpq + _rope_transpose(dqt, t, h, w, split, base)
+        dpk = dpk + _rope_transpose(dkt, t, h, w, split, base)
+    else:
+        dpq = dpq + dqt
+        dpk = dpk + dkt
+    return dpq * _relu_grad(q), dpk * _relu_grad(k), dv, G[0], g[0]
+
+
+def lin_attn_bwd(q, k, v, dout, grid, F, *, t0=0, rope=False, split=None,
+                 base=10000.0, eps=1e-6, S0=None, z0=None, dS_final=None, dz_final=None):
+    """Gradients of lin_attn_fwd: for the scalar
+        L = sum(out * dout) + sum(S_final * dS_final) + sum(z_final * dz_final)
+    returns (dq, dk, dv, dS0, dz0), fp64, shaped like q, k, v, S0, z0.
+    dS_final / dz_final default to zero (the final cache unused)."""
+    _check(q, k, v, grid, F)
+    B, H, N, d = q.shape
+    dvv = v.shape[3]
+    dq = np.empty((B, H, N, d))
+    dk = np.empty((B, H, N, d))
+    dv = np.empty((B, H, N, dvv))
+    dS0 = np.empty((B, H, d, dvv))
+    dz0 = np.empty((B, H, d))
+    for b in range(B):
+        for h in range(H):
+            s0 = np.zeros((d, dvv)) if S0 is None else S0[b, h]
+            zz = np.zeros(d) if z0 is None else z0[b, h]
+            dsf = np.zeros((d, dvv)) if dS_final is None else dS_final[b, h]
+            dzf = np.zeros(d) if dz_final is None else dz_final[b, h]
+            dq[b, h], dk[b, h], dv[b, h], dS0[b, h], dz0[b, h] = _bwd_slice(
+                q[b, h], k[b, h], v[b, h], dout[b, h], grid, F, t0, rope, split,
+                base, eps, s0, zz, dsf, dzf)
+    return dq, dk, dv, dS0, dz0
