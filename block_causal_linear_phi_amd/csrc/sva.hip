@@ -184,8 +184,17 @@ __device__ __forceinline__ int pair_entry(const PairLoc& pl, uint32_t packed) {
   return __mul24((int)pos, pl.stride) + pl.base;  // 24-bit multiply: operands are small
 }
 
-// Turn the pair (x, y) by the angle whose (cos, sin) is cs.
+// Turn the pair (x, y) by the angle whose (cos, sin) is cs, or by its
+// opposite (INV: the transpose of the rotation, for gradients).
+template <bool INV = false>
 __device__ __forceinline__ void rotate(float& x, float& y, float2 cs) {
+  if constexpr (INV) {
+    const float xr = x * cs.x + y * cs.y;
+    const float yr = y * cs.x - x * cs.y;
+    x = xr;
+    y = yr;
+    return;
+  }
   const float xr = x * cs.x - y * cs.y;
   const float yr = x * cs.y + y * cs.x;
   x = xr;
@@ -196,19 +205,19 @@ __device__ __forceinline__ void rotate(float& x, float& y, float2 cs) {
 // paired mode (ROPE >= 2: every axis width a multiple of 4) local pairs
 // (2k, 2k+1) are adjacent entries of the same axis at an even index, so one
 // 16-byte LDS read serves both.
-template <int ROPE, int NPAIR>
+template <int ROPE, int NPAIR, bool INV = false>
 __device__ __forceinline__ void rope_lane(float* x, const float2* tab, const PairLoc* pl, uint32_t co) {
   if constexpr (ROPE >= 2 && NPAIR % 2 == 0) {
     const float4* tab4 = reinterpret_cast<const float4*>(tab);
 #pragma unroll
     for (int pp = 0; pp < NPAIR; pp += 2) {
       const float4 cs = tab4[pair_entry(pl[pp], co) >> 1];
-      rotate(x[2 * pp], x[2 * pp + 1], make_float2(cs.x, cs.y));
-      rotate(x[2 * pp + 2], x[2 * pp + 3], make_float2(cs.z, cs.w));
+      rotate<INV>(x[2 * pp], x[2 * pp + 1], make_float2(cs.x, cs.y));
+      rotate<INV>(x[2 * pp + 2], x[2 * pp + 3], make_float2(cs.z, cs.w));
     }
   } else {
 #pragma unroll
-    for (int pp = 0; pp < NPAIR; ++pp) rotate(x[2 * pp], x[2 * pp + 1], tab[pair_entry(pl[pp], co)]);
+    for (int pp = 0; pp < NPAIR; ++pp) rotate<INV>(x[2 * pp], x[2 * pp + 1], tab[pair_entry(pl[pp], co)]);
   }
 }
 
@@ -217,7 +226,7 @@ __device__ __forceinline__ void rope_lane(float* x, const float2* tab, const Pai
 // 8: such a run lies in one axis, its four pairs are consecutive entries of
 // one table row starting at a multiple of 4, and two 16-byte reads at a
 // fixed distance serve them from one computed address.
-template <int NRUN>
+template <int NRUN, bool INV = false>
 __device__ __forceinline__ void rope_lane_runs(float* x, const float2* tab, const PairLoc* pl, uint32_t co) {
   const float4* tab4 = reinterpret_cast<const float4*>(tab);
 #pragma unroll
@@ -225,10 +234,10 @@ __device__ __forceinline__ void rope_lane_runs(float* x, const float2* tab, cons
     const float4* t = tab4 + (pair_entry(pl[r], co) >> 1);
     const float4 c0 = t[0], c1 = t[1];
     float* y = x + 8 * r;
-    rotate(y[0], y[1], make_float2(c0.x, c0.y));
-    rotate(y[2], y[3], make_float2(c0.z, c0.w));
-    rotate(y[4], y[5], make_float2(c1.x, c1.y));
-    rotate(y[6], y[7], make_float2(c1.z, c1.w));
+    rotate<INV>(y[0], y[1], make_float2(c0.x, c0.y));
+    rotate<INV>(y[2], y[3], make_float2(c0.z, c0.w));
+    rotate<INV>(y[4], y[5], make_float2(c1.x, c1.y));
+    rotate<INV>(y[6], y[7], make_float2(c1.z, c1.w));
   }
 }
 
@@ -443,10 +452,13 @@ struct SplitArgs {
 // Accumulator (r, s)[i] of lane l holds S[FPL*(4*(l/16)+i)+r][FPL*(l%16)+s].
 // ---------------------------------------------------------------------------
 
-template <bool BF16, int D, int ROPE>
+// WZ (used by the backward): two fp32 values per token, w_n = wz[n] and
+// s_n = wz[B*H*N + n] (wz is [2, B*H, N]): the z part sums w_n * phi(k_n)
+// instead of phi(k_n), and the state part uses s_n * RoPE(phi k_n).
+template <bool BF16, int D, int ROPE, bool WZ = false>
 __global__ __launch_bounds__(red_threads<BF16>(), red_min_blocks<BF16>()) void sva_reduce_kernel(
     const void* __restrict__ kp, const void* __restrict__ vp, float* __restrict__ partials,
-    Geo geo, SplitArgs sp, RopeArgs ra) {
+    Geo geo, SplitArgs sp, RopeArgs ra, const float* __restrict__ wz) {
   constexpr int RT = red_threads<BF16>();
   constexpr int FPL = D / 16;
   constexpr int NPAIR = FPL / 2;
@@ -494,7 +506,8 @@ __global__ __launch_bounds__(red_threads<BF16>(), red_min_blocks<BF16>()) void s
     // Buffer resources over the block's rows [0, je): rows past the segment
     // end read as zeros, so a ragged last step needs no masking (zero k
     // contributes nothing to S or z).
-    const long long blk_off = ((long long)bh * geo.N + (long long)c * geo.Nb) * ROWB;
+    const long long row0 = (long long)bh * geo.N + (long long)c * geo.Nb;  // block's first token row
+    const long long blk_off = row0 * ROWB;
     const __amdgpu_buffer_rsrc_t krs = make_rsrc(kb + blk_off, (uint32_t)je * ROWB);
     const __amdgpu_buffer_rsrc_t vrs = make_rsrc(vb + blk_off, (uint32_t)je * ROWB);
     const uint32_t lane_col = FPL * cg * ESZ;
@@ -525,14 +538,31 @@ __global__ __launch_bounds__(red_threads<BF16>(), red_min_blocks<BF16>()) void s
       uint32_t mine = 0;
       if (ROPE)
         mine = decode_packed((uint32_t)min(s0 + (lane & 31), je - 1), geo.fHW, geo.fWs);
+      float wmine = 0.f, smine = 0.f;  // per-token weights, fetched the same way
+      if (WZ) {
+        const long long n = row0 + min(s0 + (lane & 31), je - 1);
+        wmine = wz[n];
+        smine = wz[(long long)geo.BH * geo.N + n];
+      }
       // phi, z and RoPE for token e of this lane, in registers.
       auto prep_token = [&](int e, float (&kf)[FPL]) {
         unpack_relu<BF16, FPL>(kf, kw[e]);
+        if constexpr (WZ) {
+          const float w = __int_as_float(__builtin_amdgcn_ds_bpermute((4 * e + tg) * 4, __float_as_int(wmine)));
 #pragma unroll
-        for (int r = 0; r < FPL; ++r) zacc[r] += kf[r];
+          for (int r = 0; r < FPL; ++r) zacc[r] += w * kf[r];
+        } else {
+#pragma unroll
+          for (int r = 0; r < FPL; ++r) zacc[r] += kf[r];
+        }
         if (ROPE) {
           const uint32_t co = (uint32_t)__builtin_amdgcn_ds_bpermute((4 * e + tg) * 4, (int)mine);
           rope_lane<ROPE, NPAIR>(kf, tab, pl, co);
+        }
+        if constexpr (WZ) {
+          const float sc = __int_as_float(__builtin_amdgcn_ds_bpermute((4 * e + tg) * 4, __float_as_int(smine)));
+#pragma unroll
+          for (int r = 0; r < FPL; ++r) kf[r] *= sc;
         }
       };
       if (BF16) {
@@ -695,6 +725,7 @@ struct ScanArgs {
   int has_init;     // S0/z0 given
   int write_frags;  // emit the output-kernel operands
   int write_final;  // emit S_out/z_out
+  int reverse;      // suffix over blocks (last block first), for the backward
 };
 
 constexpr int kScanLanes = 8;                      // block-lanes per element
@@ -726,6 +757,9 @@ __device__ __forceinline__ float4 block_sum(const float* __restrict__ partials, 
 }
 
 // kScanElems groups of 4 elements x kScanLanes block-lanes per workgroup.
+// Blocks are taken in scan order: 0, 1, ... (prefix), or nb-1, nb-2, ...
+// (suffix, `reverse`, for the backward; the initial value is then the
+// gradient of the final state and the last value that of the initial one).
 // Lane ty owns blocks [ty*cpl, ty*cpl + cpl): pass 1 sums them, the lane
 // totals are scanned through LDS in lane order, pass 2 adds each block in
 // turn (kept in registers, or re-read: the partials are L2-resident) and
@@ -765,7 +799,8 @@ __global__ __launch_bounds__(kThreads) void sva_scan_kernel(
   float4 tot = make_float4(0.f, 0.f, 0.f, 0.f);
   if (active) {
     for (int c = c_begin; c < c_end; ++c) {
-      const float4 bs = block_sum<E>(partials, (long long)bh * a.nb + c, a.L, a.Nb, e);
+      const int cb = a.reverse ? a.nb - 1 - c : c;  // the block, in scan order
+      const float4 bs = block_sum<E>(partials, (long long)bh * a.nb + cb, a.L, a.Nb, e);
 #pragma unroll
       for (int i = 0; i < kKeep; ++i)
         if (c - c_begin == i) keep[i] = bs;
@@ -778,7 +813,7 @@ __global__ __launch_bounds__(kThreads) void sva_scan_kernel(
   for (int l = 0; l < ty; ++l) add4(run, lane_tot[l][tx]);
 
   for (int c = c_begin; c < c_end; ++c) {
-    const long long bhc = (long long)bh * a.nb + c;
+    const long long bhc = (long long)bh * a.nb + (a.reverse ? a.nb - 1 - c : c);
     float4 bs;
     if (c - c_begin < kKeep) {
 #pragma unroll
@@ -1167,6 +1202,455 @@ __global__ __launch_bounds__(app_threads<BF16>(), app_min_blocks<BF16>()) void s
 }
 
 // ---------------------------------------------------------------------------
+// Backward kernels (bf16)
+//
+// Gradients of L = <out, dout> (+ <S_final, dS_final> + <z_final, dz_final>)
+// by the chain rule through the forward's steps.  With num = qt S_c and
+// den = phi(q) . Z_c + eps (so out = num / den):
+//   dnum = dout / den,  dden = -(dout . num) / den^2 = -(dout . out) / den,
+//   dqt = S_c dnum,     dS_c = sum qt dnum^T,  dZ_c = sum dden phi(q),
+//   dq  = [q > 0] (RoPE^T dqt + dden Z_c),
+// the prefix over blocks becomes a suffix: G_c = sum_{c' >= c} dS_c'
+// (+ dS_final), g_c likewise, and for the tokens of block c
+//   dkt = G_c v,  dv = G_c^T kt,  dk = [k > 0] (RoPE^T dkt + g_c).
+// RoPE^T turns every pair by the opposite angle.  dnum is never rounded or
+// stored: the output side forms S_c dout from the exact bf16 dout and scales
+// by 1/den in fp32, and the state-gradient pass (the reduction kernel) sums
+// (qt / den) dout^T, scaling qt before its bf16 rounding.  The output side
+// reads q, dout and out and writes dq, dden and 1/den; the state side reads
+// k and v and writes dk and dv.  Both work on 16-token tiles in the layout of the
+// forward output pass: lane (g = l/16, row = l%16) holds features
+// feat(g, m) = 32(m/8) + 8g + m%8 of token row, which is its share of an
+// MFMA B operand whose k index is the feature, and accumulator rt of an
+// MFMA whose A operand has rows fo(rt, r) = 32(rt/2) + 8(r/4) + 4(rt%2) +
+// r%4 holds the same features of the same token (local element 4rt + i).
+// ---------------------------------------------------------------------------
+
+template <int D>
+struct BTile {
+  static constexpr int ROWB = 2 * D;           // bytes per bf16 token row
+  static constexpr int PPR = ROWB / 16;        // 16-byte pieces per row
+  static constexpr int RPI = 64 / PPR;         // rows per load instruction
+  static constexpr int NLD = 16 / RPI;         // load instructions per tile
+  static constexpr int NW = D / 8;             // words per lane in MFMA layout
+  static constexpr int SWM = (PPR < 8 ? PPR : 8) - 1;
+  static constexpr int TSZ = 16 * PPR;         // one tile, in 16-byte units
+  static constexpr int CPR = D / 8;            // 16-byte chunks per operand row
+  static constexpr int NRT = D / 16;           // accumulators (16 rows each)
+  static constexpr int NKS = D / 32;           // MFMA k-steps
+  static_assert(NLD * 4 == NW, "tile pieces");
+  __device__ static int at(int r, int p) { return r * PPR + (p ^ (r & SWM)); }
+  __device__ static int frag_at(int f, int c) { return f * CPR + (c ^ (f & (CPR - 1))); }
+  __device__ static int fo(int rt, int r) { return 32 * (rt >> 1) + 8 * (r >> 2) + 4 * (rt & 1) + (r & 3); }
+};
+
+// Global rows t .. t+15 of a bf16 [rows, D] segment into registers, in row
+// order (PPR lanes per row).
+template <int D>
+__device__ __forceinline__ void btile_load(uint32_t* w, __amdgpu_buffer_rsrc_t r, int t, int lane) {
+  using T = BTile<D>;
+  const uint32_t off = (uint32_t)(t + lane / T::PPR) * T::ROWB + 16 * (lane % T::PPR);
+#pragma unroll
+  for (int i = 0; i < T::NLD; ++i) buf_load<4>(w + 4 * i, r, off + i * T::RPI * T::ROWB);
+}
+
+// Row-order registers -> MFMA-layout words through the wave's LDS tile.
+template <int D>
+__device__ __forceinline__ void btile_to_mfma(uint4* wst, const uint32_t* w, uint32_t* out, int lane) {
+  using T = BTile<D>;
+  const int g = lane >> 4, row = lane & 15;
+#pragma unroll
+  for (int i = 0; i < T::NLD; ++i)
+    wst[T::at(i * T::RPI + lane / T::PPR, lane % T::PPR)] = make_uint4(w[4 * i], w[4 * i + 1], w[4 * i + 2], w[4 * i + 3]);
+  __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
+#pragma unroll
+  for (int i = 0; i < T::NW / 4; ++i) {
+    const uint4 v = wst[T::at(row, 4 * i + g)];
+    out[4 * i] = v.x; out[4 * i + 1] = v.y; out[4 * i + 2] = v.z; out[4 * i + 3] = v.w;
+  }
+  __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
+}
+
+// MFMA-layout words -> global rows t .. t+15 through the wave's LDS tile.
+template <int D>
+__device__ __forceinline__ void btile_store(uint4* wst, const uint32_t* ow, __amdgpu_buffer_rsrc_t r, int t,
+                                            int lane) {
+  using T = BTile<D>;
+  const int g = lane >> 4, row = lane & 15;
+#pragma unroll
+  for (int i = 0; i < T::NW / 4; ++i)
+    wst[T::at(row, 4 * i + g)] = make_uint4(ow[4 * i], ow[4 * i + 1], ow[4 * i + 2], ow[4 * i + 3]);
+  __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
+  const uint32_t off = (uint32_t)(t + lane / T::PPR) * T::ROWB + 16 * (lane % T::PPR);
+#pragma unroll
+  for (int i = 0; i < T::NLD; ++i) {
+    const uint4 v = wst[T::at(i * T::RPI + lane / T::PPR, lane % T::PPR)];
+    const uint32_t w4[4] = {v.x, v.y, v.z, v.w};
+    buf_store<4>(r, off + i * T::RPI * T::ROWB, w4);
+  }
+  __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
+}
+
+// acc[rt] += A[rt] * b over the k-steps, A's rows fo(rt, row) read from an
+// operand matrix staged in LDS (row f, chunk c at frag_at(f, c)).
+template <int D>
+__device__ __forceinline__ void mfma_staged(floatx4* acc, const uint4* fst, const u32x4* b, int lane) {
+  using T = BTile<D>;
+  const int g = lane >> 4, row = lane & 15;
+#pragma unroll
+  for (int ks = 0; ks < T::NKS; ++ks)
+#pragma unroll
+    for (int rt = 0; rt < T::NRT; ++rt) {
+      const uint4 a = fst[T::frag_at(T::fo(rt, row), 4 * ks + g)];
+      acc[rt] = mfma_bf16(u32x4{a.x, a.y, a.z, a.w}, b[ks], acc[rt]);
+    }
+}
+
+// Stage a [D, D] bf16 matrix stored row-major in global memory (M^T of the
+// prefix operands, rows = output features) into LDS: as it is (rows a), or
+// transposed (rows = its columns) for products with the other side.
+template <int D, bool TRANSPOSE>
+__device__ __forceinline__ void stage_operand(uint4* fst, const uint4 (&fr)[(D * D / 8 + kThreads - 1) / kThreads],
+                                              int tid) {
+  using T = BTile<D>;
+  constexpr int N = D * T::CPR;
+#pragma unroll
+  for (int i = 0; i < (N + kThreads - 1) / kThreads; ++i) {
+    const int u = tid + i * kThreads;
+    if (N % kThreads != 0 && u >= N) continue;
+    const int a = u / T::CPR, c = u % T::CPR;
+    if constexpr (!TRANSPOSE) {
+      fst[T::frag_at(a, c)] = fr[i];
+    } else {
+      const uint32_t w[4] = {fr[i].x, fr[i].y, fr[i].z, fr[i].w};
+      unsigned short* h = reinterpret_cast<unsigned short*>(fst);
+#pragma unroll
+      for (int j = 0; j < 8; ++j)
+        h[T::frag_at(8 * c + j, a >> 3) * 8 + (a & 7)] = (unsigned short)(w[j >> 1] >> (16 * (j & 1)));
+    }
+  }
+}
+
+template <int D>
+__device__ __forceinline__ void load_operand(uint4 (&fr)[(D * D / 8 + kThreads - 1) / kThreads], const void* frags,
+                                             long long bhc, int tid) {
+  constexpr int N = D * D / 8;
+  const uint4* src = (const uint4*)frags + bhc * N;
+#pragma unroll
+  for (int i = 0; i < (N + kThreads - 1) / kThreads; ++i)
+    if (N % kThreads == 0 || tid + i * kThreads < N) fr[i] = src[tid + i * kThreads];
+}
+
+__device__ __forceinline__ float bf16_elem(const uint32_t* w, int m) {
+  return (m & 1) ? bf16_hi(w[m >> 1]) : bf16_lo(w[m >> 1]);
+}
+
+// Output side: q, dout, out -> dq, and per token dden and 1/den (tw, [2,
+// B*H, N] fp32).  sfrag holds S_c^T (bf16) and zc holds Z_c per (b, h, block).
+template <int D, int ROPE>
+__global__ __launch_bounds__(kThreads, 2) void sva_bwd_out_kernel(
+    const void* __restrict__ qp, const void* __restrict__ dop, const void* __restrict__ op,
+    void* __restrict__ dqp, float* __restrict__ tw, const void* __restrict__ sfrag,
+    const float* __restrict__ zc, Geo geo, SplitArgs sp, RopeArgs ra, float eps) {
+  using T = BTile<D>;
+  constexpr int FPLa = D / 4;
+  constexpr int NW = T::NW, NKS = T::NKS, NRT = T::NRT;
+  constexpr int NPAIR = FPLa / 2;
+  constexpr bool RUNS = ROPE == 3;
+  constexpr int NLOC = RUNS ? NKS : NPAIR;
+  constexpr int FR = (D * D / 8 + kThreads - 1) / kThreads;
+
+  extern __shared__ float4 tab_raw[];
+  float2* tab = reinterpret_cast<float2*>(tab_raw);
+  __shared__ uint4 fst[D * T::CPR];  // S_c, rows = key features
+  __shared__ float zst[D];
+  __shared__ uint4 tiles[kThreads / 64][3][T::TSZ];
+
+  const int tid = threadIdx.x;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int lane = tid & 63;
+  const int g = lane >> 4;
+  const int row = lane & 15;
+  uint4* tq = tiles[wave][0];
+  uint4* td = tiles[wave][1];
+  uint4* to = tiles[wave][2];
+
+  PairLoc pl[NLOC];
+  if (ROPE) {
+#pragma unroll
+    for (int i = 0; i < NLOC; ++i) pl[i] = pair_loc(apply_feat<true>(g, RUNS ? 8 * i : 2 * i) >> 1, ra);
+  }
+
+  const long long g0 = (long long)blockIdx.x * sp.L;
+  const long long g1 = min(g0 + sp.L, sp.total);
+  for (long long pos = g0; pos < g1;) {
+    const long long bhc = pos / geo.Nb;
+    const long long seg_end = min(g1, (bhc + 1) * (long long)geo.Nb);
+    const int bh = (int)(bhc / geo.nb);
+    const int c = (int)(bhc - (long long)bh * geo.nb);
+    const int js = (int)(pos - bhc * geo.Nb);
+    const int je = (int)(seg_end - bhc * geo.Nb);
+    const long long row0 = (long long)bh * geo.N + (long long)c * geo.Nb;
+    const long long blk_off = row0 * T::ROWB;
+    const uint32_t nbytes = (uint32_t)je * T::ROWB;
+    const __amdgpu_buffer_rsrc_t qrs = make_rsrc((const char*)qp + blk_off, nbytes);
+    const __amdgpu_buffer_rsrc_t drs = make_rsrc((const char*)dop + blk_off, nbytes);
+    const __amdgpu_buffer_rsrc_t ors = make_rsrc((const char*)op + blk_off, nbytes);
+    const __amdgpu_buffer_rsrc_t dqrs = make_rsrc((char*)dqp + blk_off, nbytes);
+
+    lds_barrier();  // every wave is done with the previous block's operand and t rows
+    uint4 fr[FR];
+    load_operand<D>(fr, sfrag, bhc, tid);
+    const float zmine = tid < D ? zc[bhc * D + tid] : 0.f;
+    constexpr int WSTRIDE = 16 * (kThreads / 64);
+    const int t_first = js + wave * 16;
+    const int nsteps = t_first < je ? (je - t_first + WSTRIDE - 1) / WSTRIDE : 0;
+    uint32_t xa[3][NW], xb[3][NW];
+    auto load3 = [&](uint32_t (&x)[3][NW], int t) {
+      btile_load<D>(x[0], qrs, t, lane);
+      btile_load<D>(x[1], drs, t, lane);
+      btile_load<D>(x[2], ors, t, lane);
+    };
+    load3(xa, t_first);
+    __builtin_amdgcn_sched_barrier(0);
+    if (ROPE) {
+      if (pos == g0) build_rope_hw<false>(tab, ra);
+      build_rope_t<false>(tab, ra, c);
+    }
+    stage_operand<D, true>(fst, fr, tid);
+    if (tid < D) zst[tid] = zmine;
+    lds_barrier();
+
+    // Z_c for the lane's features, and the denominator operand (rows 0 and
+    // 4: Z rounded to bf16 and the remainder), as in the output pass.
+    float z[FPLa];
+#pragma unroll
+    for (int m = 0; m < FPLa; ++m) z[m] = zst[apply_feat<true>(g, m)];
+    u32x4 az[NKS];
+#pragma unroll
+    for (int ks = 0; ks < NKS; ++ks)
+#pragma unroll
+      for (int m = 0; m < 4; ++m) {
+        const float z0 = z[8 * ks + 2 * m], z1 = z[8 * ks + 2 * m + 1];
+        const bf16x2_t hi = {(__bf16)z0, (__bf16)z1};
+        const bf16x2_t lo = {(__bf16)(z0 - (float)hi[0]), (__bf16)(z1 - (float)hi[1])};
+        az[ks][m] = row == 0 ? __builtin_bit_cast(uint32_t, hi) : row == 4 ? __builtin_bit_cast(uint32_t, lo) : 0u;
+      }
+
+    auto compute = [&](const uint32_t (&x)[3][NW], int t) {
+      uint32_t qw[NW], dw[NW], ow[NW];
+      btile_to_mfma<D>(tq, x[0], qw, lane);
+      btile_to_mfma<D>(td, x[1], dw, lane);
+      btile_to_mfma<D>(to, x[2], ow, lane);
+      u32x4 rq[NKS];
+#pragma unroll
+      for (int i = 0; i < NW; ++i) rq[i >> 2][i & 3] = relu_bf16x2(qw[i]);
+      floatx4 dacc = floatx4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int ks = 0; ks < NKS; ++ks) dacc = mfma_bf16(az[ks], rq[ks], dacc);
+      float dot = 0.f;
+#pragma unroll
+      for (int m = 0; m < FPLa; ++m) dot += bf16_elem(dw, m) * bf16_elem(ow, m);
+      const float den = sum_over_rows(dacc[0]) + eps;
+      dot = sum_over_rows(dot);
+      const float inv = 1.0f / den;
+      const float dd = -dot * inv;  // dden: -(dout . out) / den
+      u32x4 bd[NKS];
+#pragma unroll
+      for (int i = 0; i < NW; ++i) bd[i >> 2][i & 3] = dw[i];
+      floatx4 acc[NRT];
+#pragma unroll
+      for (int rt = 0; rt < NRT; ++rt) acc[rt] = floatx4{0.f, 0.f, 0.f, 0.f};
+      mfma_staged<D>(acc, fst, bd, lane);  // S_c dout, then / den: S_c dnum
+      float gq[FPLa];
+#pragma unroll
+      for (int m = 0; m < FPLa; ++m) gq[m] = acc[m >> 2][m & 3] * inv;
+      if constexpr (ROPE != 0) {
+        const uint32_t co = decode_packed((uint32_t)min(t + row, je - 1), geo.fHW, geo.fWs);
+        if constexpr (RUNS) rope_lane_runs<NKS, true>(gq, tab, pl, co);
+        else rope_lane<ROPE, NPAIR, true>(gq, tab, pl, co);
+      }
+      uint32_t dqw[NW];
+#pragma unroll
+      for (int i = 0; i < NW; ++i) {
+        const uint32_t r = rq[i >> 2][i & 3];
+        const float a = (r & 0xffffu) ? gq[2 * i] + dd * z[2 * i] : 0.f;
+        const float b = (r >> 16) ? gq[2 * i + 1] + dd * z[2 * i + 1] : 0.f;
+        dqw[i] = pack_bf16x2(a, b);
+      }
+      btile_store<D>(tq, dqw, dqrs, t, lane);
+      if (t + row < je) {
+        if (g == 0) tw[row0 + t + row] = dd;
+        if (g == 1) tw[(long long)geo.BH * geo.N + row0 + t + row] = inv;
+      }
+    };
+
+    int k = 0;
+    for (; k + 2 <= nsteps; k += 2) {
+      const int t0 = t_first + k * WSTRIDE;
+      load3(xb, t0 + WSTRIDE);
+      __builtin_amdgcn_sched_barrier(0);
+      compute(xa, t0);
+      __builtin_amdgcn_sched_barrier(0);
+      load3(xa, t0 + 2 * WSTRIDE);
+      __builtin_amdgcn_sched_barrier(0);
+      compute(xb, t0 + WSTRIDE);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    if (k < nsteps) compute(xa, t_first + k * WSTRIDE);
+    pos = seg_end;
+  }
+}
+
+// State side: k, v -> dk, dv.  gfrag holds G_c^T (bf16) and gc holds g_c per
+// (b, h, block).
+template <int D, int ROPE>
+__global__ __launch_bounds__(kThreads, 2) void sva_bwd_kv_kernel(
+    const void* __restrict__ kp, const void* __restrict__ vp, void* __restrict__ dkp, void* __restrict__ dvp,
+    const void* __restrict__ gfrag, const float* __restrict__ gc, Geo geo, SplitArgs sp, RopeArgs ra) {
+  using T = BTile<D>;
+  constexpr int FPLa = D / 4;
+  constexpr int NW = T::NW, NKS = T::NKS, NRT = T::NRT;
+  constexpr int NPAIR = FPLa / 2;
+  constexpr bool RUNS = ROPE == 3;
+  constexpr int NLOC = RUNS ? NKS : NPAIR;
+  constexpr int FR = (D * D / 8 + kThreads - 1) / kThreads;
+
+  extern __shared__ float4 tab_raw[];
+  float2* tab = reinterpret_cast<float2*>(tab_raw);
+  __shared__ uint4 fsT[D * T::CPR];  // G_c^T, rows = value features (for dv)
+  __shared__ uint4 fsN[D * T::CPR];  // G_c, rows = key features (for dkt)
+  __shared__ float gst[D];
+  __shared__ uint4 tiles[kThreads / 64][2][T::TSZ];
+
+  const int tid = threadIdx.x;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int lane = tid & 63;
+  const int g = lane >> 4;
+  const int row = lane & 15;
+  uint4* tk = tiles[wave][0];
+  uint4* tv = tiles[wave][1];
+
+  PairLoc pl[NLOC];
+  if (ROPE) {
+#pragma unroll
+    for (int i = 0; i < NLOC; ++i) pl[i] = pair_loc(apply_feat<true>(g, RUNS ? 8 * i : 2 * i) >> 1, ra);
+  }
+
+  const long long g0 = (long long)blockIdx.x * sp.L;
+  const long long g1 = min(g0 + sp.L, sp.total);
+  for (long long pos = g0; pos < g1;) {
+    const long long bhc = pos / geo.Nb;
+    const long long seg_end = min(g1, (bhc + 1) * (long long)geo.Nb);
+    const int bh = (int)(bhc / geo.nb);
+    const int c = (int)(bhc - (long long)bh * geo.nb);
+    const int js = (int)(pos - bhc * geo.Nb);
+    const int je = (int)(seg_end - bhc * geo.Nb);
+    const long long row0 = (long long)bh * geo.N + (long long)c * geo.Nb;
+    const long long blk_off = row0 * T::ROWB;
+    const uint32_t nbytes = (uint32_t)je * T::ROWB;
+    const __amdgpu_buffer_rsrc_t krs = make_rsrc((const char*)kp + blk_off, nbytes);
+    const __amdgpu_buffer_rsrc_t vrs = make_rsrc((const char*)vp + blk_off, nbytes);
+    const __amdgpu_buffer_rsrc_t dkrs = make_rsrc((char*)dkp + blk_off, nbytes);
+    const __amdgpu_buffer_rsrc_t dvrs = make_rsrc((char*)dvp + blk_off, nbytes);
+
+    lds_barrier();
+    uint4 fr[FR];
+    load_operand<D>(fr, gfrag, bhc, tid);
+    const float gmine = tid < D ? gc[bhc * D + tid] : 0.f;
+    constexpr int WSTRIDE = 16 * (kThreads / 64);
+    const int t_first = js + wave * 16;
+    const int nsteps = t_first < je ? (je - t_first + WSTRIDE - 1) / WSTRIDE : 0;
+    uint32_t xa[2][NW], xb[2][NW];
+    auto load2 = [&](uint32_t (&x)[2][NW], int t) {
+      btile_load<D>(x[0], krs, t, lane);
+      btile_load<D>(x[1], vrs, t, lane);
+    };
+    load2(xa, t_first);
+    __builtin_amdgcn_sched_barrier(0);
+    if (ROPE) {
+      if (pos == g0) build_rope_hw<false>(tab, ra);
+      build_rope_t<false>(tab, ra, c);
+    }
+    stage_operand<D, false>(fsT, fr, tid);
+    stage_operand<D, true>(fsN, fr, tid);
+    if (tid < D) gst[tid] = gmine;
+    lds_barrier();
+    float gz[FPLa];
+#pragma unroll
+    for (int m = 0; m < FPLa; ++m) gz[m] = gst[apply_feat<true>(g, m)];
+
+    auto compute = [&](const uint32_t (&x)[2][NW], int t) {
+      uint32_t kw[NW], vw[NW];
+      btile_to_mfma<D>(tk, x[0], kw, lane);
+      btile_to_mfma<D>(tv, x[1], vw, lane);
+      u32x4 rk[NKS], bv[NKS];
+#pragma unroll
+      for (int i = 0; i < NW; ++i) {
+        rk[i >> 2][i & 3] = relu_bf16x2(kw[i]);
+        bv[i >> 2][i & 3] = vw[i];
+      }
+      u32x4 kt[NKS];
+      uint32_t co = 0;
+      if constexpr (ROPE != 0) {
+        co = decode_packed((uint32_t)min(t + row, je - 1), geo.fHW, geo.fWs);
+        float kf[FPLa];
+#pragma unroll
+        for (int m = 0; m < FPLa; ++m) kf[m] = (m & 1) ? bf16_hi(rk[m >> 3][(m >> 1) & 3]) : bf16_lo(rk[m >> 3][(m >> 1) & 3]);
+        if constexpr (RUNS) rope_lane_runs<NKS>(kf, tab, pl, co);
+        else rope_lane<ROPE, NPAIR>(kf, tab, pl, co);
+#pragma unroll
+        for (int i = 0; i < NW; ++i) kt[i >> 2][i & 3] = pack_bf16x2(kf[2 * i], kf[2 * i + 1]);
+      } else {
+#pragma unroll
+        for (int ks = 0; ks < NKS; ++ks) kt[ks] = rk[ks];
+      }
+      floatx4 av[NRT], ak[NRT];
+#pragma unroll
+      for (int rt = 0; rt < NRT; ++rt) {
+        av[rt] = floatx4{0.f, 0.f, 0.f, 0.f};
+        ak[rt] = floatx4{0.f, 0.f, 0.f, 0.f};
+      }
+      mfma_staged<D>(av, fsT, kt, lane);  // dv = G_c^T kt
+      mfma_staged<D>(ak, fsN, bv, lane);  // dkt = G_c v
+      float gk[FPLa];
+#pragma unroll
+      for (int m = 0; m < FPLa; ++m) gk[m] = ak[m >> 2][m & 3];
+      if constexpr (ROPE != 0) {
+        if constexpr (RUNS) rope_lane_runs<NKS, true>(gk, tab, pl, co);
+        else rope_lane<ROPE, NPAIR, true>(gk, tab, pl, co);
+      }
+      uint32_t dkw[NW], dvw[NW];
+#pragma unroll
+      for (int i = 0; i < NW; ++i) {
+        const uint32_t r = rk[i >> 2][i & 3];
+        const float a = (r & 0xffffu) ? gk[2 * i] + gz[2 * i] : 0.f;
+        const float b = (r >> 16) ? gk[2 * i + 1] + gz[2 * i + 1] : 0.f;
+        dkw[i] = pack_bf16x2(a, b);
+        dvw[i] = pack_bf16x2(av[(2 * i) >> 2][(2 * i) & 3], av[(2 * i + 1) >> 2][(2 * i + 1) & 3]);
+      }
+      btile_store<D>(tk, dkw, dkrs, t, lane);
+      btile_store<D>(tv, dvw, dvrs, t, lane);
+    };
+
+    int k = 0;
+    for (; k + 2 <= nsteps; k += 2) {
+      const int t0 = t_first + k * WSTRIDE;
+      load2(xb, t0 + WSTRIDE);
+      __builtin_amdgcn_sched_barrier(0);
+      compute(xa, t0);
+      __builtin_amdgcn_sched_barrier(0);
+      load2(xa, t0 + 2 * WSTRIDE);
+      __builtin_amdgcn_sched_barrier(0);
+      compute(xb, t0 + WSTRIDE);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    if (k < nsteps) compute(xa, t_first + k * WSTRIDE);
+    pos = seg_end;
+  }
+}
+
+// ---------------------------------------------------------------------------
 // Standalone phi + RoPE stage (test entry point): one thread per token.
 // ---------------------------------------------------------------------------
 
@@ -1218,6 +1702,8 @@ struct Plan {
   RopeArgs ra;
   SplitArgs red, app;
   int G_red, G_app;
+  SplitArgs bwd, bwd_kv;  // backward output side and state side
+  int G_bwd_out, G_bwd_kv;
   size_t tab_bytes;
   size_t off_partials, off_frags, off_zc, ws_bytes;
 };
@@ -1366,20 +1852,21 @@ Plan make_plan(const sva_desc* d) {
   return p;
 }
 
-template <bool BF16, int D, int ROPE>
-hipError_t launch_reduce(const Plan& p, const void* k, const void* v, float* partials, hipStream_t st) {
+template <bool BF16, int D, int ROPE, bool WZ = false>
+hipError_t launch_reduce(const Plan& p, const void* k, const void* v, float* partials, hipStream_t st,
+                         const float* wz = nullptr) {
   Geo geo = p.geo;
   SplitArgs sp = p.red;
   RopeArgs ra = p.ra;
-  void* args[] = {(void*)&k, (void*)&v, (void*)&partials, &geo, &sp, &ra};
-  return hipLaunchKernel((const void*)&sva_reduce_kernel<BF16, D, (ROPE == 3 ? 2 : ROPE)>, dim3(p.G_red), dim3(red_threads<BF16>()),
-                         args, ROPE ? p.tab_bytes : 0, st);
+  void* args[] = {(void*)&k, (void*)&v, (void*)&partials, &geo, &sp, &ra, (void*)&wz};
+  return hipLaunchKernel((const void*)&sva_reduce_kernel<BF16, D, (ROPE == 3 ? 2 : ROPE), WZ>, dim3(p.G_red),
+                         dim3(red_threads<BF16>()), args, ROPE ? p.tab_bytes : 0, st);
 }
 
 template <bool BF16, int D>
 hipError_t launch_scan(const Plan& p, const float* partials, const float* S0, const float* z0,
                        float* S_out, float* z_out, void* frags, float* zc, bool write_frags,
-                       hipStream_t st) {
+                       hipStream_t st, bool reverse = false) {
   ScanArgs a;
   a.nb = p.nb;
   a.Nb = p.Nb;
@@ -1388,6 +1875,7 @@ hipError_t launch_scan(const Plan& p, const float* partials, const float* S0, co
   a.has_init = S0 != nullptr;
   a.write_frags = write_frags;
   a.write_final = S_out != nullptr;
+  a.reverse = reverse;
   void* args[] = {(void*)&partials, (void*)&S0, (void*)&z0, (void*)&S_out, (void*)&z_out,
                   (void*)&frags, (void*)&zc, &a};
   constexpr int groups = (D * D + D) / 4;
@@ -1413,6 +1901,38 @@ hipError_t launch_prep(const Plan& p, const void* x, float* xr, float* xphi, hip
   void* args[] = {(void*)&x, (void*)&xr, (void*)&xphi, &geo, &ra};
   return hipLaunchKernel((const void*)&sva_prep_kernel<BF16, D, (ROPE == 3 ? 2 : ROPE)>,
                          dim3((p.Nb + kThreads - 1) / kThreads, p.nb, p.BH), dim3(kThreads), args,
+                         ROPE ? p.tab_bytes : 0, st);
+}
+
+// Backward launchers (bf16 only; BF16 is always true where they are used).
+template <bool BF16, int D, int ROPE>
+hipError_t launch_reduce_wz(const Plan& p, const void* k, const void* v, float* partials, hipStream_t st,
+                            const float* wz) {
+  return launch_reduce<BF16, D, ROPE, true>(p, k, v, partials, st, wz);
+}
+
+template <bool BF16, int D, int ROPE>
+hipError_t launch_bwd_out(const Plan& p, const void* q, const void* dout, const void* out, void* dq,
+                          float* tw, const void* frags, const float* zc, float eps, hipStream_t st) {
+  static_assert(BF16, "the backward runs on bf16 inputs");
+  Geo geo = p.geo;
+  SplitArgs sp = p.bwd;
+  RopeArgs ra = p.ra;
+  void* args[] = {(void*)&q, (void*)&dout, (void*)&out, (void*)&dq, (void*)&tw,
+                  (void*)&frags, (void*)&zc, &geo, &sp, &ra, &eps};
+  return hipLaunchKernel((const void*)&sva_bwd_out_kernel<D, ROPE>, dim3(p.G_bwd_out),
+                         dim3(kThreads), args, ROPE ? p.tab_bytes : 0, st);
+}
+
+template <bool BF16, int D, int ROPE>
+hipError_t launch_bwd_kv(const Plan& p, const void* k, const void* v, void* dk, void* dv, const void* gfrags,
+                         const float* gc, hipStream_t st) {
+  static_assert(BF16, "the backward runs on bf16 inputs");
+  Geo geo = p.geo;
+  SplitArgs sp = p.bwd_kv;
+  RopeArgs ra = p.ra;
+  void* args[] = {(void*)&k, (void*)&v, (void*)&dk, (void*)&dv, (void*)&gfrags, (void*)&gc, &geo, &sp, &ra};
+  return hipLaunchKernel((const void*)&sva_bwd_kv_kernel<D, ROPE>, dim3(p.G_bwd_kv), dim3(kThreads), args,
                          ROPE ? p.tab_bytes : 0, st);
 }
 
@@ -1445,6 +1965,22 @@ int plan_grids_t(Plan* p) {
 }
 
 void plan_grids(Plan* p) { (void)SVA_DISPATCH(*p, plan_grids_t, p); }
+
+template <bool BF16, int D, int ROPE>
+int plan_bwd_grids_t(Plan* p) {
+  const long long total = (long long)p->BH * p->N;
+  const size_t lds = ROPE ? p->tab_bytes : 0;
+  const long long a = resident_workgroups((const void*)&sva_bwd_out_kernel<D, ROPE>, kThreads, lds);
+  const long long b = resident_workgroups((const void*)&sva_bwd_kv_kernel<D, ROPE>, kThreads, lds);
+  p->bwd = make_split(total, a < kAppWorkgroupsMax ? a : kAppWorkgroupsMax, &p->G_bwd_out);
+  p->bwd_kv = make_split(total, b < kAppWorkgroupsMax ? b : kAppWorkgroupsMax, &p->G_bwd_kv);
+  return 0;
+}
+
+void plan_bwd_grids(Plan* p) {
+  (void)(p->D == 64 ? SVA_DISPATCH_R(*p, plan_bwd_grids_t, true, 64, p)
+                    : SVA_DISPATCH_R(*p, plan_bwd_grids_t, true, 32, p));
+}
 
 size_t qkv_bytes(const Plan& p) { return (size_t)p.BH * p.N * p.D * (p.bf16 ? 2 : 4); }
 
@@ -1499,6 +2035,62 @@ sva_status run_fwd(const sva_desc* desc, const void* q, const void* k, const voi
   return SVA_OK;
 }
 
+sva_status run_bwd(const sva_desc* desc, const void* q, const void* k, const void* v, const void* out,
+                   const void* dout, const float* S0, const float* z0, const float* dS_out,
+                   const float* dz_out, void* dq, void* dk, void* dv, float* dS0, float* dz0, void* ws,
+                   size_t ws_bytes, void* stream) {
+  Plan p;
+  sva_status s = check_common(desc, false, &p);
+  if (s != SVA_OK) return s;
+  if (!p.bf16) return SVA_ERR_UNSUPPORTED;
+  const void* in[] = {q, k, v, out, dout};
+  void* grads[] = {dq, dk, dv};
+  for (const void* x : in)
+    if (!x || !is_aligned16(x)) return SVA_ERR_INVALID_ARG;
+  for (void* x : grads)
+    if (!x || !is_aligned16(x)) return SVA_ERR_INVALID_ARG;
+  if ((S0 == nullptr) != (z0 == nullptr) || (dS_out == nullptr) != (dz_out == nullptr) ||
+      (dS0 == nullptr) != (dz0 == nullptr))
+    return SVA_ERR_INVALID_ARG;
+  const float* st_ptr[] = {S0, z0, dS_out, dz_out, dS0, dz0};
+  for (const float* x : st_ptr)
+    if (x && !is_aligned16(x)) return SVA_ERR_INVALID_ARG;
+  const size_t nbytes = qkv_bytes(p);
+  for (int i = 0; i < 3; ++i) {
+    for (const void* x : in)
+      if (overlaps(grads[i], nbytes, x, nbytes)) return SVA_ERR_INVALID_ARG;
+    for (int j = 0; j < i; ++j)
+      if (overlaps(grads[i], nbytes, grads[j], nbytes)) return SVA_ERR_INVALID_ARG;
+  }
+  if (!ws || ws_bytes < p.ws_bytes || !is_aligned16(ws)) return SVA_ERR_WORKSPACE;
+
+  plan_grids(&p);
+  plan_bwd_grids(&p);
+  hipStream_t st = (hipStream_t)stream;
+  char* wsb = (char*)ws;
+  float* partials = (float*)(wsb + p.off_partials);
+  void* frags = wsb + p.off_frags;
+  float* zc = (float*)(wsb + p.off_zc);
+  // dk doubles as scratch until the last kernel writes it: dden and 1/den,
+  // fp32 per token (2*B*H*N*4 bytes <= B*H*N*d*2).
+  float* tw = (float*)dk;
+#define SVA_BWD(FN, ...) (p.D == 64 ? SVA_DISPATCH_R(p, FN, true, 64, __VA_ARGS__) : SVA_DISPATCH_R(p, FN, true, 32, __VA_ARGS__))
+  if (SVA_BWD(launch_reduce, p, k, v, partials, st) != hipSuccess) return SVA_ERR_HIP;
+  if ((p.D == 64 ? launch_scan<true, 64>(p, partials, S0, z0, nullptr, nullptr, frags, zc, true, st)
+                 : launch_scan<true, 32>(p, partials, S0, z0, nullptr, nullptr, frags, zc, true, st)) != hipSuccess)
+    return SVA_ERR_HIP;
+  if (SVA_BWD(launch_bwd_out, p, q, dout, out, dq, tw, frags, zc, desc->eps, st) != hipSuccess)
+    return SVA_ERR_HIP;
+  if (SVA_BWD(launch_reduce_wz, p, q, dout, partials, st, tw) != hipSuccess) return SVA_ERR_HIP;
+  if ((p.D == 64 ? launch_scan<true, 64>(p, partials, dS_out, dz_out, dS0, dz0, frags, zc, true, st, true)
+                 : launch_scan<true, 32>(p, partials, dS_out, dz_out, dS0, dz0, frags, zc, true, st, true)) !=
+      hipSuccess)
+    return SVA_ERR_HIP;
+  if (SVA_BWD(launch_bwd_kv, p, k, v, dk, dv, frags, zc, st) != hipSuccess) return SVA_ERR_HIP;
+#undef SVA_BWD
+  return SVA_OK;
+}
+
 }  // namespace
 
 // ---------------------------------------------------------------------------
@@ -1541,6 +2133,24 @@ sva_status sva_lin_attn_fwd_traced(const sva_desc* desc, const void* q, const vo
                                    void* stream, void* const events[4]) {
   if (!events) return SVA_ERR_INVALID_ARG;
   return run_fwd(desc, q, k, v, out, S0, z0, S_out, z_out, ws, ws_bytes, stream, events);
+}
+
+sva_status sva_lin_attn_bwd_workspace(const sva_desc* desc, size_t* bytes) {
+  if (!bytes) return SVA_ERR_INVALID_ARG;
+  Plan p;
+  sva_status s = check_common(desc, false, &p);
+  if (s != SVA_OK) return s;
+  if (!p.bf16) return SVA_ERR_UNSUPPORTED;
+  *bytes = p.ws_bytes;
+  return SVA_OK;
+}
+
+sva_status sva_lin_attn_bwd(const sva_desc* desc, const void* q, const void* k, const void* v,
+                            const void* out, const void* dout, const float* S0, const float* z0,
+                            const float* dS_out, const float* dz_out, void* dq, void* dk, void* dv,
+                            float* dS0, float* dz0, void* ws, size_t ws_bytes, void* stream) {
+  return run_bwd(desc, q, k, v, out, dout, S0, z0, dS_out, dz_out, dq, dk, dv, dS0, dz0, ws, ws_bytes,
+                 stream);
 }
 
 sva_status sva_block_cache_workspace(const sva_desc* desc, size_t* bytes) {

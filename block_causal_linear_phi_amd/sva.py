@@ -49,6 +49,8 @@ _SIG = {
                                         _VP, ctypes.c_size_t, _VP]),
     "sva_lin_attn_fwd_traced": (ctypes.c_int, [ctypes.POINTER(SvaDesc), _VP, _VP, _VP, _VP, _VP, _VP, _VP,
                                                _VP, _VP, ctypes.c_size_t, _VP, ctypes.POINTER(_VP)]),
+    "sva_lin_attn_bwd_workspace": (ctypes.c_int, [ctypes.POINTER(SvaDesc), ctypes.POINTER(ctypes.c_size_t)]),
+    "sva_lin_attn_bwd": (ctypes.c_int, [ctypes.POINTER(SvaDesc)] + [_VP] * 15 + [ctypes.c_size_t, _VP]),
     "sva_block_cache_workspace": (ctypes.c_int, [ctypes.POINTER(SvaDesc), ctypes.POINTER(ctypes.c_size_t)]),
     "sva_block_cache_apply": (ctypes.c_int, [ctypes.POINTER(SvaDesc), _VP, _VP, _VP, _VP, _VP, _VP, _VP,
                                              ctypes.c_size_t, _VP]),
@@ -124,6 +126,12 @@ def sva_lin_attn_fwd_workspace(desc: SvaDesc) -> int:
     return n.value
 
 
+def sva_lin_attn_bwd_workspace(desc: SvaDesc) -> int:
+    n = ctypes.c_size_t()
+    _check(lib().sva_lin_attn_bwd_workspace(ctypes.byref(desc), ctypes.byref(n)), "sva_lin_attn_bwd_workspace")
+    return n.value
+
+
 def sva_block_cache_workspace(desc: SvaDesc) -> int:
     n = ctypes.c_size_t(0)
     _check(lib().sva_block_cache_workspace(ctypes.byref(desc), ctypes.byref(n)), "sva_block_cache_workspace")
@@ -157,6 +165,25 @@ def sva_lin_attn_fwd(q, k, v, grid: Tuple[int, int, int], frames_per_block: int,
         st = lib().sva_lin_attn_fwd_traced(*args, arr)
     _check(st, "sva_lin_attn_fwd")
     return out
+
+
+def sva_lin_attn_bwd(q, k, v, out, dout, grid: Tuple[int, int, int], frames_per_block: int, *, t0: int = 0,
+                     rope: bool = False, split=None, base: float = 10000.0, eps: float = 1e-6,
+                     S0=None, z0=None, dS_out=None, dz_out=None, dq=None, dk=None, dv=None,
+                     dS0=None, dz0=None, ws=None, stream=None):
+    """Gradients of the forward (sva_lin_attn_bwd), bf16.  Returns (dq, dk, dv);
+    dS0/dz0 are filled when given."""
+    import torch
+    desc = _desc_from(q, grid, frames_per_block, t0, rope, split, base, eps)
+    dq = torch.empty_like(q) if dq is None else dq
+    dk = torch.empty_like(k) if dk is None else dk
+    dv = torch.empty_like(v) if dv is None else dv
+    ws = _workspace(sva_lin_attn_bwd_workspace(desc), q, ws)
+    st = lib().sva_lin_attn_bwd(ctypes.byref(desc), _ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(dout),
+                                _ptr(S0), _ptr(z0), _ptr(dS_out), _ptr(dz_out), _ptr(dq), _ptr(dk), _ptr(dv),
+                                _ptr(dS0), _ptr(dz0), _ptr(ws), ws.numel() * ws.element_size(), _stream(stream))
+    _check(st, "sva_lin_attn_bwd")
+    return dq, dk, dv
 
 
 def sva_block_cache_apply(S, z, q, k, v, frame_grid: Tuple[int, int, int], *, t0: int, rope: bool = False,

@@ -115,6 +115,35 @@ sva_status sva_lin_attn_fwd_traced(const sva_desc* desc, const void* q,
                                    size_t ws_bytes, void* stream,
                                    void* const events[4]);
 
+/* Workspace bytes sva_lin_attn_bwd needs (the same as the forward's).
+ * SVA_ERR_UNSUPPORTED unless desc->dtype == SVA_BF16. */
+sva_status sva_lin_attn_bwd_workspace(const sva_desc* desc, size_t* bytes);
+
+/* Gradients of sva_lin_attn_fwd, for the block-causal training the pages
+ * run ([talk], block causal segment), by the chain rule through the same
+ * steps.  For L = <out, dout> + <S_final, dS_out> + <z_final, dz_out>:
+ *   q, k, v   in:  the forward's inputs [B, H, N, d] bf16
+ *   out       in:  the forward's output for them [B, H, N, d] bf16 (its
+ *                  denominator term uses dout . out)
+ *   dout      in:  dL/dout [B, H, N, d] bf16
+ *   S0, z0    in:  the forward's initial cache fp32, or both NULL (zeros)
+ *   dS_out, dz_out in: dL/d(final cache) [B,H,d,d], [B,H,d] fp32, or both
+ *                  NULL (zero)
+ *   dq, dk, dv out: [B, H, N, d] bf16 (round-to-nearest-even).  dk also
+ *                  serves as scratch between the kernels; none of them may
+ *                  overlap another or any input.
+ *   dS0, dz0  out: dL/d(initial cache) fp32, or both NULL
+ *   ws, ws_bytes: caller-owned scratch of at least
+ *                  sva_lin_attn_bwd_workspace bytes
+ * The derivative of ReLU is taken as 0 at 0.  bf16 only: other dtypes return
+ * SVA_ERR_UNSUPPORTED before any work. */
+sva_status sva_lin_attn_bwd(const sva_desc* desc, const void* q, const void* k,
+                            const void* v, const void* out, const void* dout,
+                            const float* S0, const float* z0,
+                            const float* dS_out, const float* dz_out, void* dq,
+                            void* dk, void* dv, float* dS0, float* dz0,
+                            void* ws, size_t ws_bytes, void* stream);
+
 /* Workspace bytes sva_block_cache_apply / sva_block_cache_commit need for a
  * one-block descriptor; independent of how many blocks were committed. */
 sva_status sva_block_cache_workspace(const sva_desc* desc, size_t* bytes);

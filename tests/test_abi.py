@@ -128,3 +128,65 @@ def test_traced_needs_events():
     st = sva.lib().sva_lin_attn_fwd_traced(ctypes.byref(d), 1 << 30, 1 << 33, 1 << 34, 1 << 36, None, None,
                                            None, None, 16, 1 << 40, None, None)
     assert st == sva.SVA_ERR_INVALID_ARG
+
+
+def test_bwd_workspace_and_dtype():
+    assert sva.sva_lin_attn_bwd_workspace(_desc()) == sva.sva_lin_attn_fwd_workspace(_desc())
+    n = ctypes.c_size_t(5)
+    d = _desc(dtype=sva.SVA_F32)
+    assert sva.lib().sva_lin_attn_bwd_workspace(ctypes.byref(d), ctypes.byref(n)) == sva.SVA_ERR_UNSUPPORTED
+    assert n.value == 5
+
+
+@fake_pointers
+@pytest.mark.parametrize("kw,code", BAD + [(dict(dtype=sva.SVA_F32), sva.SVA_ERR_UNSUPPORTED)])
+def test_bwd_bad_descriptors_are_rejected(kw, code):
+    d = _desc(**kw)
+    big = 1 << 36  # fake, widely spaced device addresses; nothing is touched
+    ptrs = [big * (i + 1) for i in range(8)]
+    st = sva.lib().sva_lin_attn_bwd(ctypes.byref(d), ptrs[0], ptrs[1], ptrs[2], ptrs[3], ptrs[4], None, None,
+                                    None, None, ptrs[5], ptrs[6], ptrs[7], None, None, 16, 1 << 40, None)
+    assert st == code
+
+
+@fake_pointers
+def test_bwd_pointer_checks_happen_before_launch():
+    d = _desc()
+    big = 1 << 36
+    p = [big * (i + 1) for i in range(8)]
+    lib = sva.lib()
+    call = lambda *a: lib.sva_lin_attn_bwd(ctypes.byref(d), *a)
+    # a gradient buffer overlapping an input
+    assert call(p[0], p[1], p[2], p[3], p[4], None, None, None, None, p[0], p[6], p[7], None, None, 16,
+                1 << 40, None) == sva.SVA_ERR_INVALID_ARG
+    # two gradient buffers overlapping each other
+    assert call(p[0], p[1], p[2], p[3], p[4], None, None, None, None, p[5], p[5] + 64, p[7], None, None, 16,
+                1 << 40, None) == sva.SVA_ERR_INVALID_ARG
+    # dS0 without dz0
+    assert call(p[0], p[1], p[2], p[3], p[4], None, None, None, None, p[5], p[6], p[7], 4096, None, 16,
+                1 << 40, None) == sva.SVA_ERR_INVALID_ARG
+    # missing dout
+    assert call(p[0], p[1], p[2], p[3], None, None, None, None, None, p[5], p[6], p[7], None, None, 16,
+                1 << 40, None) == sva.SVA_ERR_INVALID_ARG
+    # workspace too small
+    assert call(p[0], p[1], p[2], p[3], p[4], None, None, None, None, p[5], p[6], p[7], None, None, 16,
+                16, None) == sva.SVA_ERR_WORKSPACE
+
+
+def _declared_arg_counts():
+    """Parameter count of every function declared in the header."""
+    text = re.sub(r"/\*.*?\*/", "", open(HEADER).read(), flags=re.S)
+    out = {}
+    for name, params in re.findall(r"\b(sva_[a-z0-9_]+)\s*\(([^)]*)\)\s*;", text):
+        params = params.strip()
+        out[name] = 0 if params in ("", "void") else params.count(",") + 1
+    return out
+
+
+def test_binding_signatures_match_the_header():
+    """Every ctypes signature in the binding has the header's argument count,
+    so no argument is dropped or converted by ctypes' defaults."""
+    counts = _declared_arg_counts()
+    assert set(counts) == set(sva._SIG)
+    for name, (_, argtypes) in sva._SIG.items():
+        assert len(argtypes) == counts[name], name
