@@ -18,6 +18,7 @@ import argparse
 import ctypes
 import json
 import os
+import re
 import sys
 import time
 
@@ -136,6 +137,47 @@ def gpu_leg(w, steps: int, warmup: int, sets: int):
     return total_ms, per
 
 
+def bwd_leg(w, steps: int, warmup: int, sets: int):
+    """The backward (sva_lin_attn_bwd) of the workload: dout is one more
+    seeded N(0,1) tensor, `out` the library's forward output (from
+    sva_lin_attn_fwd_save, which also keeps the prefix states).  Returns ms
+    per backward call over `steps` uninstrumented calls, with the saved
+    states and with the states recomputed."""
+    import torch
+    from block_causal_linear_phi_amd import sva
+
+    base = {t: upload(w, t) for t in ("q", "k", "v", "dout")}
+    bufs = [base] + [{t: base[t].clone() for t in base} for _ in range(sets - 1)]
+    kw = dict(t0=w.t0, rope=w.rope, split=w.split, base=w.base, eps=w.eps)
+    for x in bufs:
+        x["out"], x["states"] = sva.sva_lin_attn_fwd_save(x["q"], x["k"], x["v"], (w.T, w.Hs, w.Ws), w.F, **kw)
+        x["dq"], x["dk"], x["dv"] = (torch.empty_like(x[t]) for t in ("q", "k", "v"))
+    desc = sva.make_desc(w.B, w.H, w.d, (w.T, w.Hs, w.Ws), w.F, eps=w.eps, **{k: kw[k] for k in ("t0", "rope",
+                                                                                                    "split", "base")})
+    ws = torch.zeros(sva.sva_lin_attn_bwd_workspace(desc), dtype=torch.uint8, device=torch.device("cuda:0"))
+    stream = torch.cuda.current_stream()
+
+    def step(i, saved):
+        x = bufs[i % sets]
+        sva.sva_lin_attn_bwd(x["q"], x["k"], x["v"], x["out"], x["dout"], (w.T, w.Hs, w.Ws), w.F, dq=x["dq"],
+                             dk=x["dk"], dv=x["dv"], states=x["states"] if saved else None, ws=ws,
+                             stream=stream, **kw)
+
+    res = []
+    for saved in (True, False):
+        for i in range(warmup):
+            step(i, saved)
+        torch.cuda.synchronize()
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record(stream)
+        for i in range(steps):
+            step(i, saved)
+        b.record(stream)
+        torch.cuda.synchronize()
+        res.append(a.elapsed_time(b) / steps)
+    return res[0], res[1]
+
+
 def cached_leg(w, steps: int, warmup: int):
     """Streaming generation: a cache committed from the workload's prior
     blocks, then `steps` denoising steps of one block against it
@@ -235,9 +277,14 @@ def cpu_leg(w, reps: int):
 
 
 def _short_kernel(name: str) -> str:
-    for k in ("sva_reduce_kernel", "sva_scan_kernel", "sva_apply_kernel", "sva_prep_kernel"):
+    for k in ("sva_reduce_kernel", "sva_scan_kernel", "sva_apply_kernel", "sva_prep_kernel",
+              "sva_bwd_out_kernel", "sva_bwd_kv_kernel"):
         if k in name:
-            return k.replace("sva_", "").replace("_kernel", "")
+            short = k.replace("sva_", "").replace("_kernel", "")
+            m = re.search(r"sva_reduce_kernel<([^>]*)>", name)
+            if m and m.group(1).replace(" ", "").split(",")[-1] == "true":
+                short += " (weighted, backward)"
+            return short
     return name.split("(")[0][-60:]
 
 
@@ -269,11 +316,16 @@ def summarize_profile(args):
 
     f_scale = calib_bytes / (mean_for(CALIB_KERNEL, "FETCH_SIZE") * 1024)
     w_scale = calib_bytes / (mean_for(CALIB_KERNEL, "WRITE_SIZE") * 1024)
+    by_short = defaultdict(lambda: defaultdict(list))
+    for (kname, cname), vs in counters.items():
+        if "sva_" in kname:
+            by_short[_short_kernel(kname)][cname] += vs
     traffic = {}
-    for k in ("reduce", "scan", "apply"):
-        fk, wk = mean_for(f"sva_{k}_kernel", "FETCH_SIZE"), mean_for(f"sva_{k}_kernel", "WRITE_SIZE")
-        if fk is None or wk is None:
+    for k, cs in by_short.items():
+        if not cs["FETCH_SIZE"] or not cs["WRITE_SIZE"]:
             continue
+        fk = sum(cs["FETCH_SIZE"]) / len(cs["FETCH_SIZE"])
+        wk = sum(cs["WRITE_SIZE"]) / len(cs["WRITE_SIZE"])
         traffic[k] = {"fetch_kib": fk, "write_kib": wk, "read_bytes": fk * 1024 * f_scale,
                       "write_bytes": wk * 1024 * w_scale, "bytes": fk * 1024 * f_scale + wk * 1024 * w_scale}
     doc = {"workload": args.workload, "source_sha256": source_sha256(), "fetch_scale": f_scale,
@@ -281,9 +333,10 @@ def summarize_profile(args):
                                                   f"{calib_bytes} bytes", "per_launch": traffic,
            "commands": args.commands}
     os.makedirs(PROFILES, exist_ok=True)
-    with open(traffic_file(args.workload), "w") as f:
+    with open(traffic_file(args.workload + args.label), "w") as f:
         json.dump(doc, f, indent=1)
-    lines = [f"# Kernel times and HBM traffic, {args.workload} workload", "",
+    what = "backward" if args.label == "_bwd" else "forward"
+    lines = [f"# Kernel times and HBM traffic, {args.workload} workload, {what}", "",
              "Commands (run from the repository root on one MI355X):", ""]
     lines += [f"    {c}" for c in args.commands]
     lines += ["", "## rocprofv3 --kernel-trace --stats", "",
@@ -299,7 +352,7 @@ def summarize_profile(args):
         lines.append(f"| {k} | {t['fetch_kib']:.0f} | {t['write_kib']:.0f} | {t['read_bytes'] / 1e6:.1f} | "
                      f"{t['write_bytes'] / 1e6:.1f} | {t['bytes'] / 1e6:.1f} |")
     lines += ["", f"Kernel source sha256: `{doc['source_sha256']}`", ""]
-    with open(os.path.join(PROFILES, f"sva_kernels_{args.workload}.md"), "w") as f:
+    with open(os.path.join(PROFILES, f"sva_kernels_{args.workload}{args.label}.md"), "w") as f:
         f.write("\n".join(lines))
     print(json.dumps({"summarized": args.workload, "traffic": traffic}))
 
@@ -314,6 +367,8 @@ def main():
     ap.add_argument("--sets", type=int, default=2, help="input buffer sets that alternate between steps")
     ap.add_argument("--cpu-reps", type=int, default=4)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--backward", action="store_true",
+                    help="time the backward (sva_lin_attn_bwd) instead of the forward")
     ap.add_argument("--copy-calib", type=int, default=0, metavar="MIB",
                     help="also run a plain fp32 streaming kernel over MIB MiB (counter calibration)")
     ap.add_argument("--summarize-profile", action="store_true",
@@ -323,6 +378,7 @@ def main():
     ap.add_argument("--write-dir")
     ap.add_argument("--calib-mib", type=int, default=256)
     ap.add_argument("--commands", nargs="*", default=[])
+    ap.add_argument("--label", default="", help="summary name suffix, e.g. _bwd")
     args = ap.parse_args()
     if args.summarize_profile:
         summarize_profile(args)
@@ -338,6 +394,25 @@ def main():
         copy_calibration(args.copy_calib)
     data_note = "synthetic (seeded N(0,1) draws" + (f", K x{w.k_scale:g}" if w.k_scale != 1.0 else "") + \
         "; resident in HBM)"
+    if args.backward:
+        ms, ms_recompute = bwd_leg(w, args.steps, args.warmup, args.sets)
+        esz = 2 if w.dtype == "bf16" else 4
+        tensor = w.B * w.H * w.N * w.d * esz
+        print(json.dumps({
+            "metric": "tokens/s (all heads) block-causal linear attn backward (dq, dk, dv); % of HBM peak",
+            "value": w.B * w.N / (ms * 1e-3), "unit": "tokens/s", "n_gpus": 1, "steps": args.steps,
+            "warmup": args.warmup, "ms_per_step": ms, "higher_is_better": True, "scaling": "weak",
+            "vs_baseline": None, "dtype": "bf16" if w.dtype == "bf16" else "f32", "data": data_note,
+            "config": {"workload": f"{w.name} backward: B={w.B} H={w.H} d={w.d} grid {w.T}x{w.Hs}x{w.Ws} "
+                                   f"({w.N} tokens), blocks of {w.F} frames",
+                       "B": w.B, "H": w.H, "d": w.d, "tokens": w.N, "blocks": w.nb},
+            # q, k, v, out, dout read once and dq, dk, dv written once
+            "alg_bytes": 8 * tensor,
+            "hbm_frac_step": 8 * tensor / (ms * 1e-3) / (HBM_PEAK_GBS * 1e9),
+            "states": "saved by the forward (sva_lin_attn_fwd_save)",
+            "ms_per_step_recomputing_states": ms_recompute,
+        }), flush=True)
+        return
     if w.prior_blocks:
         apply_ms, commit_ms = cached_leg(w, args.steps, args.warmup)
         tok = w.B * w.block_tokens

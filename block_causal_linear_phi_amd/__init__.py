@@ -7,5 +7,5 @@ in include/sva.h); `sva` is its thin ctypes binding.
 from .sva import (  # noqa: F401
     SVA_BF16, SVA_F32, SvaDesc, SvaError, make_desc, sva_block_cache_apply, sva_block_cache_commit,
     sva_block_cache_workspace, sva_lin_attn_bwd, sva_lin_attn_bwd_workspace, sva_lin_attn_fwd,
-    sva_lin_attn_fwd_workspace, sva_phi_rope_prep,
+    sva_lin_attn_fwd_save, sva_lin_attn_fwd_workspace, sva_lin_attn_states_bytes, sva_phi_rope_prep,
 )

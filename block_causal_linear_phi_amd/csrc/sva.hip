@@ -1706,6 +1706,7 @@ struct Plan {
   int G_bwd_out, G_bwd_kv;
   size_t tab_bytes;
   size_t off_partials, off_frags, off_zc, ws_bytes;
+  size_t states_zc, states_bytes;  // saved prefix states: operands at 0, Z_c at states_zc
 };
 
 constexpr long long kRedWorkgroupsMax = 1024;  // bounds the partials workspace
@@ -1849,6 +1850,8 @@ Plan make_plan(const sva_desc* d) {
   p.off_zc = off;
   off = align256(off + (size_t)p.BH * p.nb * p.D * sizeof(float));
   p.ws_bytes = off;
+  p.states_zc = align256((size_t)p.BH * p.nb * p.D * p.D * esz);
+  p.states_bytes = p.states_zc + align256((size_t)p.BH * p.nb * p.D * sizeof(float));
   return p;
 }
 
@@ -1993,7 +1996,7 @@ sva_status check_common(const sva_desc* d, bool one_block, Plan* p) {
 
 sva_status run_fwd(const sva_desc* desc, const void* q, const void* k, const void* v, void* out,
                    const float* S0, const float* z0, float* S_out, float* z_out, void* ws,
-                   size_t ws_bytes, void* stream, void* const* events) {
+                   size_t ws_bytes, void* stream, void* const* events, void* states = nullptr) {
   Plan p;
   sva_status s = check_common(desc, false, &p);
   if (s != SVA_OK) return s;
@@ -2010,6 +2013,7 @@ sva_status run_fwd(const sva_desc* desc, const void* q, const void* k, const voi
       overlaps(out, nbytes, v, nbytes))
     return SVA_ERR_INVALID_ARG;
   if (!ws || ws_bytes < p.ws_bytes || !is_aligned16(ws)) return SVA_ERR_WORKSPACE;
+  if (states && !is_aligned16(states)) return SVA_ERR_INVALID_ARG;
   if (events) {
     for (int i = 0; i < 4; ++i)
       if (!events[i]) return SVA_ERR_INVALID_ARG;
@@ -2019,8 +2023,9 @@ sva_status run_fwd(const sva_desc* desc, const void* q, const void* k, const voi
   hipStream_t st = (hipStream_t)stream;
   char* wsb = (char*)ws;
   float* partials = (float*)(wsb + p.off_partials);
-  void* frags = wsb + p.off_frags;
-  float* zc = (float*)(wsb + p.off_zc);
+  // the prefix states go to the caller's buffer when it keeps them
+  void* frags = states ? states : (void*)(wsb + p.off_frags);
+  float* zc = states ? (float*)((char*)states + p.states_zc) : (float*)(wsb + p.off_zc);
   hipError_t e = hipSuccess;
   if (events && (e = hipEventRecord((hipEvent_t)events[0], st)) != hipSuccess) return SVA_ERR_HIP;
   if ((e = SVA_DISPATCH(p, launch_reduce, p, k, v, partials, st)) != hipSuccess) return SVA_ERR_HIP;
@@ -2037,8 +2042,8 @@ sva_status run_fwd(const sva_desc* desc, const void* q, const void* k, const voi
 
 sva_status run_bwd(const sva_desc* desc, const void* q, const void* k, const void* v, const void* out,
                    const void* dout, const float* S0, const float* z0, const float* dS_out,
-                   const float* dz_out, void* dq, void* dk, void* dv, float* dS0, float* dz0, void* ws,
-                   size_t ws_bytes, void* stream) {
+                   const float* dz_out, void* dq, void* dk, void* dv, float* dS0, float* dz0,
+                   const void* states, void* ws, size_t ws_bytes, void* stream) {
   Plan p;
   sva_status s = check_common(desc, false, &p);
   if (s != SVA_OK) return s;
@@ -2063,6 +2068,7 @@ sva_status run_bwd(const sva_desc* desc, const void* q, const void* k, const voi
       if (overlaps(grads[i], nbytes, grads[j], nbytes)) return SVA_ERR_INVALID_ARG;
   }
   if (!ws || ws_bytes < p.ws_bytes || !is_aligned16(ws)) return SVA_ERR_WORKSPACE;
+  if (states && !is_aligned16(states)) return SVA_ERR_INVALID_ARG;
 
   plan_grids(&p);
   plan_bwd_grids(&p);
@@ -2075,11 +2081,21 @@ sva_status run_bwd(const sva_desc* desc, const void* q, const void* k, const voi
   // fp32 per token (2*B*H*N*4 bytes <= B*H*N*d*2).
   float* tw = (float*)dk;
 #define SVA_BWD(FN, ...) (p.D == 64 ? SVA_DISPATCH_R(p, FN, true, 64, __VA_ARGS__) : SVA_DISPATCH_R(p, FN, true, 32, __VA_ARGS__))
-  if (SVA_BWD(launch_reduce, p, k, v, partials, st) != hipSuccess) return SVA_ERR_HIP;
-  if ((p.D == 64 ? launch_scan<true, 64>(p, partials, S0, z0, nullptr, nullptr, frags, zc, true, st)
-                 : launch_scan<true, 32>(p, partials, S0, z0, nullptr, nullptr, frags, zc, true, st)) != hipSuccess)
-    return SVA_ERR_HIP;
-  if (SVA_BWD(launch_bwd_out, p, q, dout, out, dq, tw, frags, zc, desc->eps, st) != hipSuccess)
+  // The forward's prefix states: saved by sva_lin_attn_fwd_save, or
+  // recomputed here (reduction and scan of the forward) into the workspace.
+  const void* sfrags = frags;
+  const float* szc = zc;
+  if (states) {
+    sfrags = states;
+    szc = (const float*)((const char*)states + p.states_zc);
+  } else {
+    if (SVA_BWD(launch_reduce, p, k, v, partials, st) != hipSuccess) return SVA_ERR_HIP;
+    if ((p.D == 64 ? launch_scan<true, 64>(p, partials, S0, z0, nullptr, nullptr, frags, zc, true, st)
+                   : launch_scan<true, 32>(p, partials, S0, z0, nullptr, nullptr, frags, zc, true, st)) !=
+        hipSuccess)
+      return SVA_ERR_HIP;
+  }
+  if (SVA_BWD(launch_bwd_out, p, q, dout, out, dq, tw, sfrags, szc, desc->eps, st) != hipSuccess)
     return SVA_ERR_HIP;
   if (SVA_BWD(launch_reduce_wz, p, q, dout, partials, st, tw) != hipSuccess) return SVA_ERR_HIP;
   if ((p.D == 64 ? launch_scan<true, 64>(p, partials, dS_out, dz_out, dS0, dz0, frags, zc, true, st, true)
@@ -2147,10 +2163,28 @@ sva_status sva_lin_attn_bwd_workspace(const sva_desc* desc, size_t* bytes) {
 
 sva_status sva_lin_attn_bwd(const sva_desc* desc, const void* q, const void* k, const void* v,
                             const void* out, const void* dout, const float* S0, const float* z0,
-                            const float* dS_out, const float* dz_out, void* dq, void* dk, void* dv,
-                            float* dS0, float* dz0, void* ws, size_t ws_bytes, void* stream) {
-  return run_bwd(desc, q, k, v, out, dout, S0, z0, dS_out, dz_out, dq, dk, dv, dS0, dz0, ws, ws_bytes,
-                 stream);
+                            const float* dS_out, const float* dz_out, const void* states, void* dq,
+                            void* dk, void* dv, float* dS0, float* dz0, void* ws, size_t ws_bytes,
+                            void* stream) {
+  return run_bwd(desc, q, k, v, out, dout, S0, z0, dS_out, dz_out, dq, dk, dv, dS0, dz0, states, ws,
+                 ws_bytes, stream);
+}
+
+sva_status sva_lin_attn_states_bytes(const sva_desc* desc, size_t* bytes) {
+  if (!bytes) return SVA_ERR_INVALID_ARG;
+  Plan p;
+  sva_status s = check_common(desc, false, &p);
+  if (s != SVA_OK) return s;
+  *bytes = p.states_bytes;
+  return SVA_OK;
+}
+
+sva_status sva_lin_attn_fwd_save(const sva_desc* desc, const void* q, const void* k, const void* v,
+                                 void* out, const float* S0, const float* z0, float* S_out,
+                                 float* z_out, void* states, void* ws, size_t ws_bytes,
+                                 void* stream) {
+  if (!states) return SVA_ERR_INVALID_ARG;
+  return run_fwd(desc, q, k, v, out, S0, z0, S_out, z_out, ws, ws_bytes, stream, nullptr, states);
 }
 
 sva_status sva_block_cache_workspace(const sva_desc* desc, size_t* bytes) {

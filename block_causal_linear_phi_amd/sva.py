@@ -50,7 +50,9 @@ _SIG = {
     "sva_lin_attn_fwd_traced": (ctypes.c_int, [ctypes.POINTER(SvaDesc), _VP, _VP, _VP, _VP, _VP, _VP, _VP,
                                                _VP, _VP, ctypes.c_size_t, _VP, ctypes.POINTER(_VP)]),
     "sva_lin_attn_bwd_workspace": (ctypes.c_int, [ctypes.POINTER(SvaDesc), ctypes.POINTER(ctypes.c_size_t)]),
-    "sva_lin_attn_bwd": (ctypes.c_int, [ctypes.POINTER(SvaDesc)] + [_VP] * 15 + [ctypes.c_size_t, _VP]),
+    "sva_lin_attn_bwd": (ctypes.c_int, [ctypes.POINTER(SvaDesc)] + [_VP] * 16 + [ctypes.c_size_t, _VP]),
+    "sva_lin_attn_states_bytes": (ctypes.c_int, [ctypes.POINTER(SvaDesc), ctypes.POINTER(ctypes.c_size_t)]),
+    "sva_lin_attn_fwd_save": (ctypes.c_int, [ctypes.POINTER(SvaDesc)] + [_VP] * 10 + [ctypes.c_size_t, _VP]),
     "sva_block_cache_workspace": (ctypes.c_int, [ctypes.POINTER(SvaDesc), ctypes.POINTER(ctypes.c_size_t)]),
     "sva_block_cache_apply": (ctypes.c_int, [ctypes.POINTER(SvaDesc), _VP, _VP, _VP, _VP, _VP, _VP, _VP,
                                              ctypes.c_size_t, _VP]),
@@ -167,12 +169,39 @@ def sva_lin_attn_fwd(q, k, v, grid: Tuple[int, int, int], frames_per_block: int,
     return out
 
 
+def sva_lin_attn_states_bytes(desc: SvaDesc) -> int:
+    n = ctypes.c_size_t()
+    _check(lib().sva_lin_attn_states_bytes(ctypes.byref(desc), ctypes.byref(n)), "sva_lin_attn_states_bytes")
+    return n.value
+
+
+def sva_lin_attn_fwd_save(q, k, v, grid: Tuple[int, int, int], frames_per_block: int, *, t0: int = 0,
+                          rope: bool = False, split=None, base: float = 10000.0, eps: float = 1e-6,
+                          S0=None, z0=None, out=None, S_out=None, z_out=None, states=None, ws=None,
+                          stream=None):
+    """Forward that keeps its prefix states for the backward
+    (sva_lin_attn_fwd_save).  Returns (out, states)."""
+    import torch
+    desc = _desc_from(q, grid, frames_per_block, t0, rope, split, base, eps)
+    if out is None:
+        out = torch.empty_like(q)
+    if states is None:
+        states = torch.empty(sva_lin_attn_states_bytes(desc), dtype=torch.uint8, device=q.device)
+    ws = _workspace(sva_lin_attn_fwd_workspace(desc), q, ws)
+    st = lib().sva_lin_attn_fwd_save(ctypes.byref(desc), _ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(S0),
+                                     _ptr(z0), _ptr(S_out), _ptr(z_out), _ptr(states), _ptr(ws),
+                                     ws.numel() * ws.element_size(), _stream(stream))
+    _check(st, "sva_lin_attn_fwd_save")
+    return out, states
+
+
 def sva_lin_attn_bwd(q, k, v, out, dout, grid: Tuple[int, int, int], frames_per_block: int, *, t0: int = 0,
                      rope: bool = False, split=None, base: float = 10000.0, eps: float = 1e-6,
-                     S0=None, z0=None, dS_out=None, dz_out=None, dq=None, dk=None, dv=None,
+                     S0=None, z0=None, dS_out=None, dz_out=None, states=None, dq=None, dk=None, dv=None,
                      dS0=None, dz0=None, ws=None, stream=None):
     """Gradients of the forward (sva_lin_attn_bwd), bf16.  Returns (dq, dk, dv);
-    dS0/dz0 are filled when given."""
+    dS0/dz0 are filled when given.  `states` from sva_lin_attn_fwd_save
+    skips recomputing the forward's prefix states."""
     import torch
     desc = _desc_from(q, grid, frames_per_block, t0, rope, split, base, eps)
     dq = torch.empty_like(q) if dq is None else dq
@@ -180,7 +209,8 @@ def sva_lin_attn_bwd(q, k, v, out, dout, grid: Tuple[int, int, int], frames_per_
     dv = torch.empty_like(v) if dv is None else dv
     ws = _workspace(sva_lin_attn_bwd_workspace(desc), q, ws)
     st = lib().sva_lin_attn_bwd(ctypes.byref(desc), _ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(dout),
-                                _ptr(S0), _ptr(z0), _ptr(dS_out), _ptr(dz_out), _ptr(dq), _ptr(dk), _ptr(dv),
+                                _ptr(S0), _ptr(z0), _ptr(dS_out), _ptr(dz_out), _ptr(states), _ptr(dq),
+                                _ptr(dk), _ptr(dv),
                                 _ptr(dS0), _ptr(dz0), _ptr(ws), ws.numel() * ws.element_size(), _stream(stream))
     _check(st, "sva_lin_attn_bwd")
     return dq, dk, dv

@@ -132,6 +132,10 @@ sva_status sva_lin_attn_bwd_workspace(const sva_desc* desc, size_t* bytes);
  *   dq, dk, dv out: [B, H, N, d] bf16 (round-to-nearest-even).  dk also
  *                  serves as scratch between the kernels; none of them may
  *                  overlap another or any input.
+ *   states    in:  the prefix states the forward saved
+ *                  (sva_lin_attn_fwd_save with the same descriptor, inputs
+ *                  and initial cache), or NULL to recompute them (one more
+ *                  pass over k and v)
  *   dS0, dz0  out: dL/d(initial cache) fp32, or both NULL
  *   ws, ws_bytes: caller-owned scratch of at least
  *                  sva_lin_attn_bwd_workspace bytes
@@ -140,9 +144,25 @@ sva_status sva_lin_attn_bwd_workspace(const sva_desc* desc, size_t* bytes);
 sva_status sva_lin_attn_bwd(const sva_desc* desc, const void* q, const void* k,
                             const void* v, const void* out, const void* dout,
                             const float* S0, const float* z0,
-                            const float* dS_out, const float* dz_out, void* dq,
-                            void* dk, void* dv, float* dS0, float* dz0,
-                            void* ws, size_t ws_bytes, void* stream);
+                            const float* dS_out, const float* dz_out,
+                            const void* states, void* dq, void* dk, void* dv,
+                            float* dS0, float* dz0, void* ws, size_t ws_bytes,
+                            void* stream);
+
+/* Bytes of the prefix states one forward call can keep for the backward:
+ * every block's S_c (in the input dtype) and Z_c (fp32), B*H*nb*(d*d*esize +
+ * d*4) plus alignment; about 1.9 MB for 16 heads of d = 64 in 7 blocks. */
+sva_status sva_lin_attn_states_bytes(const sva_desc* desc, size_t* bytes);
+
+/* sva_lin_attn_fwd that also keeps its prefix states in `states`
+ * (caller-owned, sva_lin_attn_states_bytes long, 16-byte aligned) for
+ * sva_lin_attn_bwd.  The states are written instead of a workspace copy, so
+ * keeping them costs nothing extra. */
+sva_status sva_lin_attn_fwd_save(const sva_desc* desc, const void* q,
+                                 const void* k, const void* v, void* out,
+                                 const float* S0, const float* z0,
+                                 float* S_out, float* z_out, void* states,
+                                 void* ws, size_t ws_bytes, void* stream);
 
 /* Workspace bytes sva_block_cache_apply / sva_block_cache_commit need for a
  * one-block descriptor; independent of how many blocks were committed. */

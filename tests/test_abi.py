@@ -145,7 +145,7 @@ def test_bwd_bad_descriptors_are_rejected(kw, code):
     big = 1 << 36  # fake, widely spaced device addresses; nothing is touched
     ptrs = [big * (i + 1) for i in range(8)]
     st = sva.lib().sva_lin_attn_bwd(ctypes.byref(d), ptrs[0], ptrs[1], ptrs[2], ptrs[3], ptrs[4], None, None,
-                                    None, None, ptrs[5], ptrs[6], ptrs[7], None, None, 16, 1 << 40, None)
+                                    None, None, None, ptrs[5], ptrs[6], ptrs[7], None, None, 16, 1 << 40, None)
     assert st == code
 
 
@@ -155,7 +155,8 @@ def test_bwd_pointer_checks_happen_before_launch():
     big = 1 << 36
     p = [big * (i + 1) for i in range(8)]
     lib = sva.lib()
-    call = lambda *a: lib.sva_lin_attn_bwd(ctypes.byref(d), *a)
+    # arguments after `d`, with states (NULL) inserted after dz_out
+    call = lambda *a: lib.sva_lin_attn_bwd(ctypes.byref(d), *a[:9], None, *a[9:])
     # a gradient buffer overlapping an input
     assert call(p[0], p[1], p[2], p[3], p[4], None, None, None, None, p[0], p[6], p[7], None, None, 16,
                 1 << 40, None) == sva.SVA_ERR_INVALID_ARG
@@ -190,3 +191,17 @@ def test_binding_signatures_match_the_header():
     assert set(counts) == set(sva._SIG)
     for name, (_, argtypes) in sva._SIG.items():
         assert len(argtypes) == counts[name], name
+
+
+def test_states_bytes():
+    n = sva.sva_lin_attn_states_bytes(_desc())
+    d, nb, BH = 64, 7, 16
+    assert BH * nb * (d * d * 2 + d * 4) <= n <= BH * nb * (d * d * 2 + d * 4) + 512
+
+
+@fake_pointers
+def test_fwd_save_needs_states():
+    d = _desc()
+    st = sva.lib().sva_lin_attn_fwd_save(ctypes.byref(d), 1 << 36, 2 << 36, 3 << 36, 4 << 36, None, None, None,
+                                         None, None, 16, 1 << 40, None)
+    assert st == sva.SVA_ERR_INVALID_ARG

@@ -76,7 +76,7 @@ def test_bwd_small(case):
 
 
 def test_bwd_gradients_land_only_in_outputs():
-    """The scratch use of dk/dv leaves nothing behind: a second call with the
+    """The scratch use of dk leaves nothing behind: a second call with the
     gradient buffers pre-filled with garbage gives identical bits."""
     B, H, d, grid, F, split = 1, 2, 64, (6, 4, 8), 2, (16, 24, 24)
     N = grid[0] * grid[1] * grid[2]
@@ -123,3 +123,28 @@ def test_bwd_720p_sampled_heads():
         errs = (relerr(dq[b, h], rq[0, 0]), relerr(dk[b, h], rk[0, 0]), relerr(dv[b, h], rv[0, 0]))
         _say(f"  head {h}: {errs}")
         assert max(errs) <= TOL
+
+
+def test_saved_states_match_recompute():
+    """sva_lin_attn_fwd_save gives the forward's output bit for bit, and the
+    backward from its saved states equals the recomputing backward bit for
+    bit (the same fixed-order sums), with an initial cache."""
+    B, H, d, grid, F, split = 1, 3, 64, (6, 5, 9), 2, (16, 24, 24)
+    N = grid[0] * grid[1] * grid[2]
+    _say("bwd saved states")
+    _, qd = rand((B, H, N, d), 51, "bf16")
+    _, kd = rand((B, H, N, d), 52, "bf16")
+    _, vd = rand((B, H, N, d), 53, "bf16")
+    _, dod = rand((B, H, N, d), 54, "bf16")
+    S0 = torch.from_numpy(wl.draw((B, H, d, d), 55, 5.0, "f32")[0]).to(DEV)
+    z0 = torch.from_numpy(np.abs(wl.draw((B, H, d), 56, 9.0, "f32")[0])).to(DEV)
+    kw = dict(t0=2, rope=True, split=split)
+    out = sva.sva_lin_attn_fwd(qd, kd, vd, grid, F, S0=S0, z0=z0, **kw)
+    out2, states = sva.sva_lin_attn_fwd_save(qd, kd, vd, grid, F, S0=S0, z0=z0, **kw)
+    a = sva.sva_lin_attn_bwd(qd, kd, vd, out, dod, grid, F, S0=S0, z0=z0, **kw)
+    a = [x.clone() for x in a]
+    b = sva.sva_lin_attn_bwd(qd, kd, vd, out2, dod, grid, F, S0=S0, z0=z0, states=states, **kw)
+    torch.cuda.synchronize()
+    assert torch.equal(out, out2)
+    for x, y in zip(a, b):
+        assert torch.equal(x, y)
