@@ -452,13 +452,10 @@ struct SplitArgs {
 // Accumulator (r, s)[i] of lane l holds S[FPL*(4*(l/16)+i)+r][FPL*(l%16)+s].
 // ---------------------------------------------------------------------------
 
-// WZ (used by the backward): two fp32 values per token, w_n = wz[n] and
-// s_n = wz[B*H*N + n] (wz is [2, B*H, N]): the z part sums w_n * phi(k_n)
-// instead of phi(k_n), and the state part uses s_n * RoPE(phi k_n).
-template <bool BF16, int D, int ROPE, bool WZ = false>
+template <bool BF16, int D, int ROPE>
 __global__ __launch_bounds__(red_threads<BF16>(), red_min_blocks<BF16>()) void sva_reduce_kernel(
     const void* __restrict__ kp, const void* __restrict__ vp, float* __restrict__ partials,
-    Geo geo, SplitArgs sp, RopeArgs ra, const float* __restrict__ wz) {
+    Geo geo, SplitArgs sp, RopeArgs ra) {
   constexpr int RT = red_threads<BF16>();
   constexpr int FPL = D / 16;
   constexpr int NPAIR = FPL / 2;
@@ -506,8 +503,7 @@ __global__ __launch_bounds__(red_threads<BF16>(), red_min_blocks<BF16>()) void s
     // Buffer resources over the block's rows [0, je): rows past the segment
     // end read as zeros, so a ragged last step needs no masking (zero k
     // contributes nothing to S or z).
-    const long long row0 = (long long)bh * geo.N + (long long)c * geo.Nb;  // block's first token row
-    const long long blk_off = row0 * ROWB;
+    const long long blk_off = ((long long)bh * geo.N + (long long)c * geo.Nb) * ROWB;
     const __amdgpu_buffer_rsrc_t krs = make_rsrc(kb + blk_off, (uint32_t)je * ROWB);
     const __amdgpu_buffer_rsrc_t vrs = make_rsrc(vb + blk_off, (uint32_t)je * ROWB);
     const uint32_t lane_col = FPL * cg * ESZ;
@@ -538,31 +534,14 @@ __global__ __launch_bounds__(red_threads<BF16>(), red_min_blocks<BF16>()) void s
       uint32_t mine = 0;
       if (ROPE)
         mine = decode_packed((uint32_t)min(s0 + (lane & 31), je - 1), geo.fHW, geo.fWs);
-      float wmine = 0.f, smine = 0.f;  // per-token weights, fetched the same way
-      if (WZ) {
-        const long long n = row0 + min(s0 + (lane & 31), je - 1);
-        wmine = wz[n];
-        smine = wz[(long long)geo.BH * geo.N + n];
-      }
       // phi, z and RoPE for token e of this lane, in registers.
       auto prep_token = [&](int e, float (&kf)[FPL]) {
         unpack_relu<BF16, FPL>(kf, kw[e]);
-        if constexpr (WZ) {
-          const float w = __int_as_float(__builtin_amdgcn_ds_bpermute((4 * e + tg) * 4, __float_as_int(wmine)));
 #pragma unroll
-          for (int r = 0; r < FPL; ++r) zacc[r] += w * kf[r];
-        } else {
-#pragma unroll
-          for (int r = 0; r < FPL; ++r) zacc[r] += kf[r];
-        }
+        for (int r = 0; r < FPL; ++r) zacc[r] += kf[r];
         if (ROPE) {
           const uint32_t co = (uint32_t)__builtin_amdgcn_ds_bpermute((4 * e + tg) * 4, (int)mine);
           rope_lane<ROPE, NPAIR>(kf, tab, pl, co);
-        }
-        if constexpr (WZ) {
-          const float sc = __int_as_float(__builtin_amdgcn_ds_bpermute((4 * e + tg) * 4, __float_as_int(smine)));
-#pragma unroll
-          for (int r = 0; r < FPL; ++r) kf[r] *= sc;
         }
       };
       if (BF16) {
@@ -1345,12 +1324,55 @@ __device__ __forceinline__ float bf16_elem(const uint32_t* w, int m) {
   return (m & 1) ? bf16_hi(w[m >> 1]) : bf16_lo(w[m >> 1]);
 }
 
-// Output side: q, dout, out -> dq, and per token dden and 1/den (tw, [2,
-// B*H, N] fp32).  sfrag holds S_c^T (bf16) and zc holds Z_c per (b, h, block).
+// Sum over the 16 lanes of each row of the wavefront (lanes 16r .. 16r+15),
+// in every lane, with DPP: mirror, half mirror, then neighbour and pair
+// swaps inside quads.  Each lane applies the same sequence, so any one lane's
+// result is reproducible.
+__device__ __forceinline__ float sum_within_rows(float x) {
+  x += __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), 0x140, 0xF, 0xF, false));  // row_mirror
+  x += __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), 0x141, 0xF, 0xF, false));  // row_half_mirror
+  x += __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), 0xB1, 0xF, 0xF, false));   // quad_perm 1,0,3,2
+  x += __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), 0x4E, 0xF, 0xF, false));   // quad_perm 2,3,0,1
+  return x;
+}
+
+// MFMA operand with tokens along k from two 16-token tiles in LDS (row order,
+// swizzled as BTile::at): lane (g = l/16, i = l%16) gets features f0 + i of
+// tokens 8g .. 8g+7 (tile g/2, rows 8(g%2) ..), through two transposing
+// reads.  ds_read_b64_tr_b16 hands lane i of a 16-lane group element i%4 of
+// the 8-byte chunks addressed by lanes 4j + i/4 (j = 0..3), so lane x
+// addresses row T0 + x/4, features f0 + 4(x%4) .. +3 (measured on gfx950).
+template <int D>
+__device__ __forceinline__ u32x4 tr_operand(const uint4* t0, const uint4* t1, int f0, int lane) {
+  using T = BTile<D>;
+  typedef short v4i16 __attribute__((ext_vector_type(4)));
+  const int g = lane >> 4, x = lane & 15;
+  const uint4* tile = (g >> 1) ? t1 : t0;
+  const int f = f0 + 4 * (x & 3);
+  const int piece = f >> 3, half = (f >> 2) & 1;
+  u32x4 r;
+#pragma unroll
+  for (int h = 0; h < 2; ++h) {
+    const int rowi = 8 * (g & 1) + 4 * h + (x >> 2);
+    const char* a = reinterpret_cast<const char*>(tile + T::at(rowi, piece)) + 8 * half;
+    const v4i16 v = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) v4i16*)a);
+    const u32x2 w = __builtin_bit_cast(u32x2, v);
+    r[2 * h] = w[0];
+    r[2 * h + 1] = w[1];
+  }
+  return r;
+}
+
+// Output side: q, dout, out -> dq, with the gradients of the block states
+// fused in: per (workgroup, block) piece it writes dS_c^T = (sum qt dnum^T)^T
+// and dZ_c = sum dden phi(q) into `partials` (the reduction's slot layout).
+// sfrag holds S_c^T (bf16) and zc holds Z_c per (b, h, block).  dS takes
+// qt / den (rounded to bf16 once) and the exact dout as MFMA operands with
+// tokens along k, read back transposed from the wave's LDS tiles.
 template <int D, int ROPE>
 __global__ __launch_bounds__(kThreads, 2) void sva_bwd_out_kernel(
     const void* __restrict__ qp, const void* __restrict__ dop, const void* __restrict__ op,
-    void* __restrict__ dqp, float* __restrict__ tw, const void* __restrict__ sfrag,
+    void* __restrict__ dqp, float* __restrict__ partials, const void* __restrict__ sfrag,
     const float* __restrict__ zc, Geo geo, SplitArgs sp, RopeArgs ra, float eps) {
   using T = BTile<D>;
   constexpr int FPLa = D / 4;
@@ -1359,12 +1381,18 @@ __global__ __launch_bounds__(kThreads, 2) void sva_bwd_out_kernel(
   constexpr bool RUNS = ROPE == 3;
   constexpr int NLOC = RUNS ? NKS : NPAIR;
   constexpr int FR = (D * D / 8 + kThreads - 1) / kThreads;
+  constexpr int E = D * D + D;
+  constexpr int NWAVE = kThreads / 64;
 
   extern __shared__ float4 tab_raw[];
   float2* tab = reinterpret_cast<float2*>(tab_raw);
   __shared__ uint4 fst[D * T::CPR];  // S_c, rows = key features
   __shared__ float zst[D];
-  __shared__ uint4 tiles[kThreads / 64][3][T::TSZ];
+  // Per wave: q in / dq out, out, and for the two steps of a pair the dout
+  // tiles and the qt/den tiles.  After the loop the region is the scratch of
+  // the cross-wave sum (2 d*d tiles and 4 z rows).
+  __shared__ uint4 tiles[NWAVE][6][T::TSZ];
+  static_assert(sizeof(tiles) >= (2 * D * D + NWAVE * D) * sizeof(float), "epilogue scratch");
 
   const int tid = threadIdx.x;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -1372,8 +1400,7 @@ __global__ __launch_bounds__(kThreads, 2) void sva_bwd_out_kernel(
   const int g = lane >> 4;
   const int row = lane & 15;
   uint4* tq = tiles[wave][0];
-  uint4* td = tiles[wave][1];
-  uint4* to = tiles[wave][2];
+  uint4* to = tiles[wave][1];
 
   PairLoc pl[NLOC];
   if (ROPE) {
@@ -1398,11 +1425,11 @@ __global__ __launch_bounds__(kThreads, 2) void sva_bwd_out_kernel(
     const __amdgpu_buffer_rsrc_t ors = make_rsrc((const char*)op + blk_off, nbytes);
     const __amdgpu_buffer_rsrc_t dqrs = make_rsrc((char*)dqp + blk_off, nbytes);
 
-    lds_barrier();  // every wave is done with the previous block's operand and t rows
+    lds_barrier();  // every wave is done with the previous block's operand, t rows and scratch
     uint4 fr[FR];
     load_operand<D>(fr, sfrag, bhc, tid);
     const float zmine = tid < D ? zc[bhc * D + tid] : 0.f;
-    constexpr int WSTRIDE = 16 * (kThreads / 64);
+    constexpr int WSTRIDE = 16 * NWAVE;
     const int t_first = js + wave * 16;
     const int nsteps = t_first < je ? (je - t_first + WSTRIDE - 1) / WSTRIDE : 0;
     uint32_t xa[3][NW], xb[3][NW];
@@ -1421,30 +1448,45 @@ __global__ __launch_bounds__(kThreads, 2) void sva_bwd_out_kernel(
     if (tid < D) zst[tid] = zmine;
     lds_barrier();
 
-    // Z_c for the lane's features, and the denominator operand (rows 0 and
-    // 4: Z rounded to bf16 and the remainder), as in the output pass.
-    float z[FPLa];
-#pragma unroll
-    for (int m = 0; m < FPLa; ++m) z[m] = zst[apply_feat<true>(g, m)];
+    // The denominator operand (rows 0 and 4: Z rounded to bf16 and the
+    // remainder), as in the output pass.  Z_c itself is read from LDS where
+    // it is needed (registers are scarce here).
     u32x4 az[NKS];
 #pragma unroll
     for (int ks = 0; ks < NKS; ++ks)
 #pragma unroll
       for (int m = 0; m < 4; ++m) {
-        const float z0 = z[8 * ks + 2 * m], z1 = z[8 * ks + 2 * m + 1];
+        const float z0 = zst[apply_feat<true>(g, 8 * ks + 2 * m)], z1 = zst[apply_feat<true>(g, 8 * ks + 2 * m + 1)];
         const bf16x2_t hi = {(__bf16)z0, (__bf16)z1};
         const bf16x2_t lo = {(__bf16)(z0 - (float)hi[0]), (__bf16)(z1 - (float)hi[1])};
         az[ks][m] = row == 0 ? __builtin_bit_cast(uint32_t, hi) : row == 4 ? __builtin_bit_cast(uint32_t, lo) : 0u;
       }
 
-    auto compute = [&](const uint32_t (&x)[3][NW], int t) {
+    floatx4 sacc[NRT][NRT];  // dS block (rt over key features, st over value features)
+#pragma unroll
+    for (int rt = 0; rt < NRT; ++rt)
+#pragma unroll
+      for (int st = 0; st < NRT; ++st) sacc[rt][st] = floatx4{0.f, 0.f, 0.f, 0.f};
+    float zacc[FPLa];  // this lane's tokens' dden * phi(q)
+#pragma unroll
+    for (int m = 0; m < FPLa; ++m) zacc[m] = 0.f;
+
+    // One 16-token tile; `slot` picks the dout and qt/den tiles kept for the
+    // pair's dS product.
+    auto compute = [&](const uint32_t (&x)[3][NW], int t, int slot) {
+      uint4* td = tiles[wave][2 + slot];
+      uint4* ts = tiles[wave][4 + slot];
       uint32_t qw[NW], dw[NW], ow[NW];
       btile_to_mfma<D>(tq, x[0], qw, lane);
-      btile_to_mfma<D>(td, x[1], dw, lane);
+      btile_to_mfma<D>(td, x[1], dw, lane);  // the dout tile stays for the dS operand
       btile_to_mfma<D>(to, x[2], ow, lane);
+      uint32_t rqw[NW];
       u32x4 rq[NKS];
 #pragma unroll
-      for (int i = 0; i < NW; ++i) rq[i >> 2][i & 3] = relu_bf16x2(qw[i]);
+      for (int i = 0; i < NW; ++i) {
+        rqw[i] = relu_bf16x2(qw[i]);
+        rq[i >> 2][i & 3] = rqw[i];
+      }
       floatx4 dacc = floatx4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int ks = 0; ks < NKS; ++ks) dacc = mfma_bf16(az[ks], rq[ks], dacc);
@@ -1453,8 +1495,32 @@ __global__ __launch_bounds__(kThreads, 2) void sva_bwd_out_kernel(
       for (int m = 0; m < FPLa; ++m) dot += bf16_elem(dw, m) * bf16_elem(ow, m);
       const float den = sum_over_rows(dacc[0]) + eps;
       dot = sum_over_rows(dot);
-      const float inv = 1.0f / den;
+      // rows past the segment hold zeros; their 1/den is taken as 0 so that
+      // they add nothing (also when eps is 0)
+      const float inv = t + row < je ? 1.0f / den : 0.f;
       const float dd = -dot * inv;  // dden: -(dout . out) / den
+      uint32_t co = 0;
+      if constexpr (ROPE != 0) co = decode_packed((uint32_t)min(t + row, je - 1), geo.fHW, geo.fWs);
+      {
+        // qt / den, rounded to bf16, into the tile of the dS product (the
+        // unrotated phi(q) first feeds this lane's dZ share)
+        float qf[FPLa];
+#pragma unroll
+        for (int m = 0; m < FPLa; ++m) {
+          qf[m] = bf16_elem(rqw, m);
+          zacc[m] += dd * qf[m];
+        }
+        if constexpr (ROPE != 0) {
+          if constexpr (RUNS) rope_lane_runs<NKS>(qf, tab, pl, co);
+          else rope_lane<ROPE, NPAIR>(qf, tab, pl, co);
+        }
+        uint32_t sw[NW];
+#pragma unroll
+        for (int i = 0; i < NW; ++i) sw[i] = pack_bf16x2(qf[2 * i] * inv, qf[2 * i + 1] * inv);
+#pragma unroll
+        for (int i = 0; i < NW / 4; ++i)
+          ts[T::at(row, 4 * i + g)] = make_uint4(sw[4 * i], sw[4 * i + 1], sw[4 * i + 2], sw[4 * i + 3]);
+      }
       u32x4 bd[NKS];
 #pragma unroll
       for (int i = 0; i < NW; ++i) bd[i >> 2][i & 3] = dw[i];
@@ -1466,23 +1532,37 @@ __global__ __launch_bounds__(kThreads, 2) void sva_bwd_out_kernel(
 #pragma unroll
       for (int m = 0; m < FPLa; ++m) gq[m] = acc[m >> 2][m & 3] * inv;
       if constexpr (ROPE != 0) {
-        const uint32_t co = decode_packed((uint32_t)min(t + row, je - 1), geo.fHW, geo.fWs);
         if constexpr (RUNS) rope_lane_runs<NKS, true>(gq, tab, pl, co);
         else rope_lane<ROPE, NPAIR, true>(gq, tab, pl, co);
       }
       uint32_t dqw[NW];
 #pragma unroll
       for (int i = 0; i < NW; ++i) {
-        const uint32_t r = rq[i >> 2][i & 3];
-        const float a = (r & 0xffffu) ? gq[2 * i] + dd * z[2 * i] : 0.f;
-        const float b = (r >> 16) ? gq[2 * i + 1] + dd * z[2 * i + 1] : 0.f;
+        const uint32_t r = rqw[i];
+        const float2 zz = *(const float2*)(zst + apply_feat<true>(g, 2 * i));  // runs of 8: pairs stay together
+        const float a = (r & 0xffffu) ? gq[2 * i] + dd * zz.x : 0.f;
+        const float b = (r >> 16) ? gq[2 * i + 1] + dd * zz.y : 0.f;
         dqw[i] = pack_bf16x2(a, b);
       }
       btile_store<D>(tq, dqw, dqrs, t, lane);
-      if (t + row < je) {
-        if (g == 0) tw[row0 + t + row] = dd;
-        if (g == 1) tw[(long long)geo.BH * geo.N + row0 + t + row] = inv;
+    };
+    // dS += (qt/den)^T dout over the 32 tokens of a pair of steps.  The
+    // transposing reads always run on the whole wavefront: under a partial
+    // exec mask ds_read_b64_tr_b16 still writes the destination registers of
+    // the masked-off lanes (measured on gfx950), so an odd last step zeroes
+    // the second pair of tiles instead of masking lanes.
+    auto ds_pair = [&]() {
+      __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
+      u32x4 bo[NRT];
+#pragma unroll
+      for (int st = 0; st < NRT; ++st) bo[st] = tr_operand<D>(tiles[wave][2], tiles[wave][3], 16 * st, lane);
+#pragma unroll
+      for (int rt = 0; rt < NRT; ++rt) {
+        const u32x4 ao = tr_operand<D>(tiles[wave][4], tiles[wave][5], 16 * rt, lane);
+#pragma unroll
+        for (int st = 0; st < NRT; ++st) sacc[rt][st] = mfma_bf16(ao, bo[st], sacc[rt][st]);
       }
+      __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
     };
 
     int k = 0;
@@ -1490,14 +1570,75 @@ __global__ __launch_bounds__(kThreads, 2) void sva_bwd_out_kernel(
       const int t0 = t_first + k * WSTRIDE;
       load3(xb, t0 + WSTRIDE);
       __builtin_amdgcn_sched_barrier(0);
-      compute(xa, t0);
+      compute(xa, t0, 0);
       __builtin_amdgcn_sched_barrier(0);
       load3(xa, t0 + 2 * WSTRIDE);
       __builtin_amdgcn_sched_barrier(0);
-      compute(xb, t0 + WSTRIDE);
+      compute(xb, t0 + WSTRIDE, 1);
+      ds_pair();
       __builtin_amdgcn_sched_barrier(0);
     }
-    if (k < nsteps) compute(xa, t_first + k * WSTRIDE);
+    if (k < nsteps) {
+      compute(xa, t_first + k * WSTRIDE, 0);
+#pragma unroll
+      for (int u = lane; u < T::TSZ; u += 64) {
+        tiles[wave][3][u] = make_uint4(0u, 0u, 0u, 0u);
+        tiles[wave][5][u] = make_uint4(0u, 0u, 0u, 0u);
+      }
+      ds_pair();
+    }
+
+    // Fixed-order sum over the waves: waves 2, 3 store their tiles, waves 0,
+    // 1 add theirs and store, then each thread sums the two tiles for one
+    // 4-element column of dS^T; z: rows summed within each lane row, then
+    // the waves in order.
+    float* scr = reinterpret_cast<float*>(&tiles[0][0][0]);  // [2][D*D] then [NWAVE][D]
+    float* zscr = scr + 2 * D * D;
+#pragma unroll
+    for (int m = 0; m < FPLa; ++m) zacc[m] = sum_within_rows(zacc[m]);
+    lds_barrier();  // every wave is done with its tiles
+    auto tile_elem = [&](int slot, int rt, int st, int i) {
+      return scr + slot * D * D + (16 * rt + 4 * g + i) * D + 16 * st + row;
+    };
+    if (wave >= 2) {
+#pragma unroll
+      for (int rt = 0; rt < NRT; ++rt)
+#pragma unroll
+        for (int st = 0; st < NRT; ++st)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) *tile_elem(wave - 2, rt, st, i) = sacc[rt][st][i];
+    }
+    if (row == 0) {
+#pragma unroll
+      for (int m = 0; m < FPLa; ++m) zscr[wave * D + apply_feat<true>(g, m)] = zacc[m];
+    }
+    lds_barrier();
+    if (wave < 2) {
+#pragma unroll
+      for (int rt = 0; rt < NRT; ++rt)
+#pragma unroll
+        for (int st = 0; st < NRT; ++st)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            float* p = tile_elem(wave, rt, st, i);
+            *p = sacc[rt][st][i] + *p;
+          }
+    }
+    lds_barrier();
+    float* dst = partials + ((long long)blockIdx.x + bhc) * E;
+    for (int e = tid; e < D * D / 4; e += kThreads) {
+      const int fo = e % D, fi0 = 4 * (e / D);
+      float t4[4];
+#pragma unroll
+      for (int j = 0; j < 4; ++j) t4[j] = scr[(fi0 + j) * D + fo] + scr[D * D + (fi0 + j) * D + fo];
+      *(float4*)(dst + fo * D + fi0) = make_float4(t4[0], t4[1], t4[2], t4[3]);
+    }
+    for (int e = tid; e < D; e += kThreads) {
+      float t1 = zscr[e];
+#pragma unroll
+      for (int w = 1; w < NWAVE; ++w) t1 += zscr[w * D + e];
+      dst[D * D + e] = t1;
+    }
     pos = seg_end;
   }
 }
@@ -1855,25 +1996,24 @@ Plan make_plan(const sva_desc* d) {
   return p;
 }
 
-template <bool BF16, int D, int ROPE, bool WZ = false>
-hipError_t launch_reduce(const Plan& p, const void* k, const void* v, float* partials, hipStream_t st,
-                         const float* wz = nullptr) {
+template <bool BF16, int D, int ROPE>
+hipError_t launch_reduce(const Plan& p, const void* k, const void* v, float* partials, hipStream_t st) {
   Geo geo = p.geo;
   SplitArgs sp = p.red;
   RopeArgs ra = p.ra;
-  void* args[] = {(void*)&k, (void*)&v, (void*)&partials, &geo, &sp, &ra, (void*)&wz};
-  return hipLaunchKernel((const void*)&sva_reduce_kernel<BF16, D, (ROPE == 3 ? 2 : ROPE), WZ>, dim3(p.G_red),
+  void* args[] = {(void*)&k, (void*)&v, (void*)&partials, &geo, &sp, &ra};
+  return hipLaunchKernel((const void*)&sva_reduce_kernel<BF16, D, (ROPE == 3 ? 2 : ROPE)>, dim3(p.G_red),
                          dim3(red_threads<BF16>()), args, ROPE ? p.tab_bytes : 0, st);
 }
 
 template <bool BF16, int D>
 hipError_t launch_scan(const Plan& p, const float* partials, const float* S0, const float* z0,
                        float* S_out, float* z_out, void* frags, float* zc, bool write_frags,
-                       hipStream_t st, bool reverse = false) {
+                       hipStream_t st, bool reverse = false, long long L = 0) {
   ScanArgs a;
   a.nb = p.nb;
   a.Nb = p.Nb;
-  a.L = p.red.L;
+  a.L = L ? L : p.red.L;  // tokens per workgroup of the kernel that wrote the partials
   a.cpl = (p.nb + kScanLanes - 1) / kScanLanes;
   a.has_init = S0 != nullptr;
   a.write_frags = write_frags;
@@ -1909,19 +2049,13 @@ hipError_t launch_prep(const Plan& p, const void* x, float* xr, float* xphi, hip
 
 // Backward launchers (bf16 only; BF16 is always true where they are used).
 template <bool BF16, int D, int ROPE>
-hipError_t launch_reduce_wz(const Plan& p, const void* k, const void* v, float* partials, hipStream_t st,
-                            const float* wz) {
-  return launch_reduce<BF16, D, ROPE, true>(p, k, v, partials, st, wz);
-}
-
-template <bool BF16, int D, int ROPE>
 hipError_t launch_bwd_out(const Plan& p, const void* q, const void* dout, const void* out, void* dq,
-                          float* tw, const void* frags, const float* zc, float eps, hipStream_t st) {
+                          float* partials, const void* frags, const float* zc, float eps, hipStream_t st) {
   static_assert(BF16, "the backward runs on bf16 inputs");
   Geo geo = p.geo;
   SplitArgs sp = p.bwd;
   RopeArgs ra = p.ra;
-  void* args[] = {(void*)&q, (void*)&dout, (void*)&out, (void*)&dq, (void*)&tw,
+  void* args[] = {(void*)&q, (void*)&dout, (void*)&out, (void*)&dq, (void*)&partials,
                   (void*)&frags, (void*)&zc, &geo, &sp, &ra, &eps};
   return hipLaunchKernel((const void*)&sva_bwd_out_kernel<D, ROPE>, dim3(p.G_bwd_out),
                          dim3(kThreads), args, ROPE ? p.tab_bytes : 0, st);
@@ -1975,7 +2109,8 @@ int plan_bwd_grids_t(Plan* p) {
   const size_t lds = ROPE ? p->tab_bytes : 0;
   const long long a = resident_workgroups((const void*)&sva_bwd_out_kernel<D, ROPE>, kThreads, lds);
   const long long b = resident_workgroups((const void*)&sva_bwd_kv_kernel<D, ROPE>, kThreads, lds);
-  p->bwd = make_split(total, a < kAppWorkgroupsMax ? a : kAppWorkgroupsMax, &p->G_bwd_out);
+  // its partials use the reduction's slots: at most kRedWorkgroupsMax pieces
+  p->bwd = make_split(total, a < kRedWorkgroupsMax ? a : kRedWorkgroupsMax, &p->G_bwd_out);
   p->bwd_kv = make_split(total, b < kAppWorkgroupsMax ? b : kAppWorkgroupsMax, &p->G_bwd_kv);
   return 0;
 }
@@ -2077,9 +2212,6 @@ sva_status run_bwd(const sva_desc* desc, const void* q, const void* k, const voi
   float* partials = (float*)(wsb + p.off_partials);
   void* frags = wsb + p.off_frags;
   float* zc = (float*)(wsb + p.off_zc);
-  // dk doubles as scratch until the last kernel writes it: dden and 1/den,
-  // fp32 per token (2*B*H*N*4 bytes <= B*H*N*d*2).
-  float* tw = (float*)dk;
 #define SVA_BWD(FN, ...) (p.D == 64 ? SVA_DISPATCH_R(p, FN, true, 64, __VA_ARGS__) : SVA_DISPATCH_R(p, FN, true, 32, __VA_ARGS__))
   // The forward's prefix states: saved by sva_lin_attn_fwd_save, or
   // recomputed here (reduction and scan of the forward) into the workspace.
@@ -2095,12 +2227,12 @@ sva_status run_bwd(const sva_desc* desc, const void* q, const void* k, const voi
         hipSuccess)
       return SVA_ERR_HIP;
   }
-  if (SVA_BWD(launch_bwd_out, p, q, dout, out, dq, tw, sfrags, szc, desc->eps, st) != hipSuccess)
+  if (SVA_BWD(launch_bwd_out, p, q, dout, out, dq, partials, sfrags, szc, desc->eps, st) != hipSuccess)
     return SVA_ERR_HIP;
-  if (SVA_BWD(launch_reduce_wz, p, q, dout, partials, st, tw) != hipSuccess) return SVA_ERR_HIP;
-  if ((p.D == 64 ? launch_scan<true, 64>(p, partials, dS_out, dz_out, dS0, dz0, frags, zc, true, st, true)
-                 : launch_scan<true, 32>(p, partials, dS_out, dz_out, dS0, dz0, frags, zc, true, st, true)) !=
-      hipSuccess)
+  if ((p.D == 64 ? launch_scan<true, 64>(p, partials, dS_out, dz_out, dS0, dz0, frags, zc, true, st, true,
+                                         p.bwd.L)
+                 : launch_scan<true, 32>(p, partials, dS_out, dz_out, dS0, dz0, frags, zc, true, st, true,
+                                         p.bwd.L)) != hipSuccess)
     return SVA_ERR_HIP;
   if (SVA_BWD(launch_bwd_kv, p, k, v, dk, dv, frags, zc, st) != hipSuccess) return SVA_ERR_HIP;
 #undef SVA_BWD
