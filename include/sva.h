@@ -129,9 +129,8 @@ sva_status sva_lin_attn_bwd_workspace(const sva_desc* desc, size_t* bytes);
  *   S0, z0    in:  the forward's initial cache fp32, or both NULL (zeros)
  *   dS_out, dz_out in: dL/d(final cache) [B,H,d,d], [B,H,d] fp32, or both
  *                  NULL (zero)
- *   dq, dk, dv out: [B, H, N, d] bf16 (round-to-nearest-even).  dk also
- *                  serves as scratch between the kernels; none of them may
- *                  overlap another or any input.
+ *   dq, dk, dv out: [B, H, N, d] bf16 (round-to-nearest-even); none of
+ *                  them may overlap another or any input
  *   states    in:  the prefix states the forward saved
  *                  (sva_lin_attn_fwd_save with the same descriptor, inputs
  *                  and initial cache), or NULL to recompute them (one more

@@ -76,7 +76,7 @@ def test_bwd_small(case):
 
 
 def test_bwd_gradients_land_only_in_outputs():
-    """The scratch use of dk leaves nothing behind: a second call with the
+    """Every element of dq, dk, dv is written: a second call with the
     gradient buffers pre-filled with garbage gives identical bits."""
     B, H, d, grid, F, split = 1, 2, 64, (6, 4, 8), 2, (16, 24, 24)
     N = grid[0] * grid[1] * grid[2]
