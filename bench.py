@@ -28,13 +28,14 @@ if ROOT not in sys.path:
 
 HBM_PEAK_GBS = 8000.0  # MI355X HBM3E, GB/s
 KERNEL_SRC = os.path.join(ROOT, "block_causal_linear_phi_amd", "csrc", "sva.hip")
+TCONV_SRC = os.path.join(ROOT, "block_causal_linear_phi_amd", "csrc", "tconv.hip")
 PROFILES = os.path.join(ROOT, "profiles")
 CALIB_KERNEL = "MulFunctor"  # the plain streaming kernel of copy_calibration()
 
 
-def source_sha256() -> str:
+def source_sha256(path: str = KERNEL_SRC) -> str:
     import hashlib
-    with open(KERNEL_SRC, "rb") as f:
+    with open(path, "rb") as f:
         return hashlib.sha256(f.read()).hexdigest()
 
 
@@ -226,6 +227,74 @@ def cached_leg(w, steps: int, warmup: int):
     return apply_ms, a.elapsed_time(b) / steps
 
 
+def tconv_leg(w, steps: int, warmup: int, sets: int, streaming: bool = True):
+    """The causal temporal convolution (sva_tconv_fwd) over all blocks of the
+    workload's activations, `sets` input/output buffer sets alternating;
+    then, if `streaming`, apply of one block against a cache and the commit.
+    Returns (ms per one-shot call, ms per block apply, ms per commit); the
+    last two are None without `streaming`."""
+    import torch
+    from block_causal_linear_phi_amd import sva
+    from block_causal_linear_phi_amd import workloads as wl
+
+    dev = torch.device("cuda:0")
+    x0 = torch.empty((w.B, w.T, w.Hs, w.Ws, w.C), dtype=torch.bfloat16, device=dev)
+    for b in range(w.B):
+        for t in range(w.T):
+            _, raw = wl.tconv_frame(w, b, t)
+            x0[b, t].copy_(torch.from_numpy(raw.view("int16")).view(torch.bfloat16))
+    taps, bias = (torch.from_numpy(a).to(dev) for a in wl.tconv_params(w))
+    xs = [x0] + [x0.clone() for _ in range(sets - 1)]
+    ys = [torch.empty_like(x0) for _ in range(sets)]
+    stream = torch.cuda.current_stream()
+
+    def timed(fn):
+        for i in range(warmup):
+            fn(i)
+        torch.cuda.synchronize()
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record(stream)
+        for i in range(steps):
+            fn(i)
+        b.record(stream)
+        torch.cuda.synchronize()
+        return a.elapsed_time(b) / steps
+
+    fwd_ms = timed(lambda i: sva.sva_tconv_fwd(xs[i % sets], taps, bias, w.F, y=ys[i % sets], stream=stream))
+    if not streaming:
+        return fwd_ms, None, None
+    blk = x0[:, :w.F].contiguous()
+    yb = torch.empty_like(blk)
+    cache = x0[:, w.F - 1].clone()
+    apply_ms = timed(lambda i: sva.sva_tconv_apply(cache, blk, taps, bias, y=yb, stream=stream))
+    commit_ms = timed(lambda i: sva.sva_tconv_commit(cache, blk, stream=stream))
+    return fwd_ms, apply_ms, commit_ms
+
+
+def tconv_cpu_leg(w, min_secs: float = 10.0, max_frames: int = 24):
+    """The fp64 temporal-conv oracle on the host: sample 0's first
+    min(T, max_frames) frames (whole blocks), all positions and channels,
+    repeated until `min_secs` have passed; throughput in tokens per second."""
+    import numpy as np
+    from block_causal_linear_phi_amd import workloads as wl
+    from oracle import tconv_oracle
+
+    frames = min(w.T, max_frames) // w.F * w.F
+    x = np.stack([wl.tconv_frame(w, 0, t)[0] for t in range(frames)])[None]
+    taps, bias = wl.tconv_params(w)
+    reps, t0 = 0, time.perf_counter()
+    while True:
+        tconv_oracle.tconv_fwd(x, taps, bias, w.F)
+        reps += 1
+        secs = time.perf_counter() - t0
+        if secs >= min_secs:
+            break
+    tok = reps * frames * w.Hs * w.Ws
+    return {"value": tok / secs, "unit": "tokens/s", "cores": 1, "kind": "oracle",
+            "sample": f"{w.name}: sample 0, first {frames} frames, all {w.Hs * w.Ws} positions and {w.C} "
+                      f"channels, {reps} passes, {secs:.1f} s, numpy fp64 (single-threaded elementwise)"}
+
+
 def copy_calibration(mib: int, reps: int = 5):
     """A plain streaming kernel of known size (torch.mul(x, 1.0, out=y) on
     fp32: reads and writes mib MiB each).  Its FETCH_SIZE / WRITE_SIZE
@@ -278,9 +347,11 @@ def cpu_leg(w, reps: int):
 
 def _short_kernel(name: str) -> str:
     for k in ("sva_reduce_kernel", "sva_scan_kernel", "sva_apply_kernel", "sva_prep_kernel",
-              "sva_bwd_out_kernel", "sva_bwd_kv_kernel"):
+              "sva_bwd_out_kernel", "sva_bwd_kv_kernel", "sva_tconv_kernel", "sva_tconv_commit_kernel"):
         if k in name:
             short = k.replace("sva_", "").replace("_kernel", "")
+            if k == "sva_tconv_kernel" and "sva_tconv_commit_kernel" in name:
+                continue
             m = re.search(r"sva_reduce_kernel<([^>]*)>", name)
             if m and m.group(1).replace(" ", "").split(",")[-1] == "true":
                 short += " (weighted, backward)"
@@ -328,14 +399,16 @@ def summarize_profile(args):
         wk = sum(cs["WRITE_SIZE"]) / len(cs["WRITE_SIZE"])
         traffic[k] = {"fetch_kib": fk, "write_kib": wk, "read_bytes": fk * 1024 * f_scale,
                       "write_bytes": wk * 1024 * w_scale, "bytes": fk * 1024 * f_scale + wk * 1024 * w_scale}
-    doc = {"workload": args.workload, "source_sha256": source_sha256(), "fetch_scale": f_scale,
+    name = ("tconv_" if args.tconv else "") + args.workload
+    doc = {"workload": name, "source_sha256": source_sha256(TCONV_SRC if args.tconv else KERNEL_SRC),
+           "fetch_scale": f_scale,
            "write_scale": w_scale, "calibration": f"{CALIB_KERNEL} kernel reading and writing "
                                                   f"{calib_bytes} bytes", "per_launch": traffic,
            "commands": args.commands}
     os.makedirs(PROFILES, exist_ok=True)
-    with open(traffic_file(args.workload + args.label), "w") as f:
+    with open(traffic_file(name + args.label), "w") as f:
         json.dump(doc, f, indent=1)
-    what = "backward" if args.label == "_bwd" else "forward"
+    what = "causal temporal convolution" if args.tconv else "backward" if args.label == "_bwd" else "forward"
     lines = [f"# Kernel times and HBM traffic, {args.workload} workload, {what}", "",
              "Commands (run from the repository root on one MI355X):", ""]
     lines += [f"    {c}" for c in args.commands]
@@ -352,9 +425,9 @@ def summarize_profile(args):
         lines.append(f"| {k} | {t['fetch_kib']:.0f} | {t['write_kib']:.0f} | {t['read_bytes'] / 1e6:.1f} | "
                      f"{t['write_bytes'] / 1e6:.1f} | {t['bytes'] / 1e6:.1f} |")
     lines += ["", f"Kernel source sha256: `{doc['source_sha256']}`", ""]
-    with open(os.path.join(PROFILES, f"sva_kernels_{args.workload}{args.label}.md"), "w") as f:
+    with open(os.path.join(PROFILES, f"sva_kernels_{name}{args.label}.md"), "w") as f:
         f.write("\n".join(lines))
-    print(json.dumps({"summarized": args.workload, "traffic": traffic}))
+    print(json.dumps({"summarized": name, "traffic": traffic}))
 
 
 def main():
@@ -369,6 +442,10 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--backward", action="store_true",
                     help="time the backward (sva_lin_attn_bwd) instead of the forward")
+    ap.add_argument("--tconv", action="store_true",
+                    help="time the causal temporal convolution of the Mix-FFN on the workload's grid instead")
+    ap.add_argument("--no-streaming", action="store_true",
+                    help="with --tconv: time the one-shot call only (profiling runs)")
     ap.add_argument("--copy-calib", type=int, default=0, metavar="MIB",
                     help="also run a plain fp32 streaming kernel over MIB MiB (counter calibration)")
     ap.add_argument("--summarize-profile", action="store_true",
@@ -389,9 +466,41 @@ def main():
         sys.exit(2)
 
     from block_causal_linear_phi_amd import workloads as wl
-    w = wl.WORKLOADS[args.workload]
     if args.copy_calib:
         copy_calibration(args.copy_calib)
+    if args.tconv:
+        tw = wl.TCONV_WORKLOADS["tconv_" + args.workload]
+        fwd_ms, apply_ms, commit_ms = tconv_leg(tw, args.steps, args.warmup, args.sets, not args.no_streaming)
+        act = tw.elems * 2
+        gbs = 2 * act / (fwd_ms * 1e-3) / 1e9
+        line = {
+            "metric": "tokens/s of the causal temporal convolution (all channels); % of HBM peak",
+            "value": tw.B * tw.T * tw.Hs * tw.Ws / (fwd_ms * 1e-3), "unit": "tokens/s", "n_gpus": 1,
+            "steps": args.steps, "warmup": args.warmup, "ms_per_step": fwd_ms, "higher_is_better": True,
+            "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+            "data": "synthetic (seeded N(0,1) activations, N(0,1/3) taps, N(0,0.01) bias; resident in HBM)",
+            "config": {"workload": f"{tw.name}: B={tw.B} grid {tw.T}x{tw.Hs}x{tw.Ws}, C={tw.C} channels, "
+                                   f"blocks of {tw.F} frames, bf16, 3-tap depthwise, one-frame cache",
+                       "B": tw.B, "tokens": tw.T * tw.Hs * tw.Ws, "C": tw.C, "blocks": tw.nb},
+            "hbm_frac_step": gbs / HBM_PEAK_GBS,
+            # one kernel per step: x read once, y written once
+            "roofline": {"bound": "hbm", "kernel": "tconv", "achieved": gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                         "frac": gbs / HBM_PEAK_GBS, "traffic": None, "alg_bytes": 2 * act / 1e9},
+        }
+        if apply_ms is not None:
+            line["block_apply_us"], line["block_commit_us"] = apply_ms * 1e3, commit_ms * 1e3
+        try:
+            with open(traffic_file(tw.name)) as f:
+                prof = json.load(f)
+            if prof.get("source_sha256") == source_sha256() and "tconv" in prof.get("per_launch", {}):
+                line["roofline"]["traffic"] = prof["per_launch"]["tconv"]["bytes"] / 1e9
+        except (OSError, ValueError):
+            pass
+        if not args.no_cpu_baseline:
+            line["cpu_baseline"] = tconv_cpu_leg(tw)
+        print(json.dumps(line), flush=True)
+        return
+    w = wl.WORKLOADS[args.workload]
     data_note = "synthetic (seeded N(0,1) draws" + (f", K x{w.k_scale:g}" if w.k_scale != 1.0 else "") + \
         "; resident in HBM)"
     if args.backward:

@@ -1,4 +1,4 @@
-"""Builds libsva.so in-tree from csrc/sva.hip for gfx950 with hipcc."""
+"""Builds libsva.so in-tree from csrc/*.hip for gfx950 with hipcc."""
 from __future__ import annotations
 
 import os
@@ -6,7 +6,7 @@ import subprocess
 
 PKG = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(PKG)
-SRC = os.path.join(PKG, "csrc", "sva.hip")
+SRCS = [os.path.join(PKG, "csrc", n) for n in ("sva.hip", "tconv.hip")]
 OUT = os.path.join(PKG, "libsva.so")
 
 HIPCC_FLAGS = [
@@ -19,7 +19,7 @@ HIPCC_FLAGS = [
 def build(verbose: bool = False) -> str:
     hipcc = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
     tmp = OUT + ".tmp"
-    cmd = [hipcc, *HIPCC_FLAGS, "-I", os.path.join(ROOT, "include"), SRC, "-o", tmp]
+    cmd = [hipcc, *HIPCC_FLAGS, "-I", os.path.join(ROOT, "include"), *SRCS, "-o", tmp]
     r = subprocess.run(cmd, capture_output=True, text=True)
     noise = "is not a recognized feature for this target"
     msgs = "\n".join(l for l in (r.stdout + r.stderr).splitlines() if noise not in l)

@@ -32,6 +32,13 @@ class SvaDesc(ctypes.Structure):
     ]
 
 
+class SvaTconvDesc(ctypes.Structure):
+    _fields_ = [
+        ("B", ctypes.c_int), ("T", ctypes.c_int), ("Hs", ctypes.c_int), ("Ws", ctypes.c_int),
+        ("C", ctypes.c_int), ("frames_per_block", ctypes.c_int), ("dtype", ctypes.c_int),
+    ]
+
+
 class SvaError(RuntimeError):
     def __init__(self, status: int, where: str):
         self.status = status
@@ -59,6 +66,9 @@ _SIG = {
     "sva_block_cache_commit": (ctypes.c_int, [ctypes.POINTER(SvaDesc), _VP, _VP, _VP, _VP, _VP,
                                               ctypes.c_size_t, _VP]),
     "sva_phi_rope_prep": (ctypes.c_int, [ctypes.POINTER(SvaDesc), _VP, _VP, _VP, _VP]),
+    "sva_tconv_fwd": (ctypes.c_int, [ctypes.POINTER(SvaTconvDesc)] + [_VP] * 7),
+    "sva_tconv_apply": (ctypes.c_int, [ctypes.POINTER(SvaTconvDesc)] + [_VP] * 6),
+    "sva_tconv_commit": (ctypes.c_int, [ctypes.POINTER(SvaTconvDesc)] + [_VP] * 3),
 }
 
 
@@ -252,3 +262,53 @@ def sva_phi_rope_prep(x, grid: Tuple[int, int, int], *, t0: int = 0, rope: bool 
     st = lib().sva_phi_rope_prep(ctypes.byref(desc), _ptr(x), _ptr(xr), _ptr(xp), _stream(stream))
     _check(st, "sva_phi_rope_prep")
     return xr, xp
+
+
+# Causal temporal convolution with a one-token block cache (include/sva_tconv.h).
+
+def make_tconv_desc(B: int, T: int, Hs: int, Ws: int, C: int, frames_per_block: int,
+                    dtype: int = SVA_BF16) -> SvaTconvDesc:
+    return SvaTconvDesc(B, T, Hs, Ws, C, frames_per_block, dtype)
+
+
+def _tconv_desc_from(x, F) -> SvaTconvDesc:
+    if x.dim() != 5:
+        raise ValueError("x must be [B, T, Hs, Ws, C]")
+    B, T, Hs, Ws, C = x.shape
+    return make_tconv_desc(B, T, Hs, Ws, C, F, _dtype_code(x))
+
+
+def sva_tconv_fwd(x, w, bias, frames_per_block: int, *, cache_in=None, y=None, cache_out=None,
+                  stream=None):
+    """Block-causal temporal convolution over all blocks of x [B, T, Hs, Ws, C]
+    with taps w [C, 3] and bias [C] (fp32; bias may be None).  cache_in is the
+    frame carried into block 0 (None: zero); cache_out, if given, receives the
+    last frame.  Returns y."""
+    import torch
+    desc = _tconv_desc_from(x, frames_per_block)
+    if y is None:
+        y = torch.empty_like(x)
+    st = lib().sva_tconv_fwd(ctypes.byref(desc), _ptr(x), _ptr(w), _ptr(bias), _ptr(cache_in), _ptr(y),
+                             _ptr(cache_out), _stream(stream))
+    _check(st, "sva_tconv_fwd")
+    return y
+
+
+def sva_tconv_apply(cache, x, w, bias, *, y=None, stream=None):
+    """Output of one block x [B, F, Hs, Ws, C] against the cache [B, Hs, Ws, C];
+    the cache is not modified.  Returns y."""
+    import torch
+    desc = _tconv_desc_from(x, x.shape[1])
+    if y is None:
+        y = torch.empty_like(x)
+    st = lib().sva_tconv_apply(ctypes.byref(desc), _ptr(cache), _ptr(x), _ptr(w), _ptr(bias), _ptr(y),
+                               _stream(stream))
+    _check(st, "sva_tconv_apply")
+    return y
+
+
+def sva_tconv_commit(cache, x, *, stream=None):
+    """cache <- the last frame of one block x [B, F, Hs, Ws, C], in place."""
+    desc = _tconv_desc_from(x, x.shape[1])
+    st = lib().sva_tconv_commit(ctypes.byref(desc), _ptr(cache), _ptr(x), _stream(stream))
+    _check(st, "sva_tconv_commit")

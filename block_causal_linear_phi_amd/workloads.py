@@ -123,3 +123,50 @@ def full_qkv(w: Workload, step: int = 0, n_tokens: Optional[int] = None, heads=N
                 vals[b, h], raw[b, h] = slice_qkv(w, tensor, b, h, step, n)
         out[tensor] = (vals, raw)
     return out
+
+
+# Causal temporal convolution of the Mix-FFN.  The pages give no FFN width;
+# the channel count here is the attention workloads' model width, H * d =
+# 16 * 64 = 1024, on the same latent grids.  Activations are drawn per
+# (workload, b, frame) slice [Hs * Ws, C]; taps N(0, 1/3) and bias N(0, 0.01)
+# in fp32; the cache (a carried frame) like one activation frame.
+
+@dataclass(frozen=True)
+class TconvWorkload:
+    name: str
+    B: int
+    T: int
+    Hs: int
+    Ws: int
+    C: int
+    F: int
+    dtype: str                      # "f32" or "bf16"
+
+    @property
+    def nb(self) -> int:
+        return self.T // self.F
+
+    @property
+    def elems(self) -> int:
+        return self.B * self.T * self.Hs * self.Ws * self.C
+
+
+TCONV_WORKLOADS = {
+    "tconv_tiny": TconvWorkload("tconv_tiny", B=1, T=4, Hs=8, Ws=8, C=32, F=1, dtype="f32"),
+    "tconv_720p": TconvWorkload("tconv_720p", B=1, T=21, Hs=45, Ws=80, C=1024, F=3, dtype="bf16"),
+    "tconv_minute": TconvWorkload("tconv_minute", B=2, T=240, Hs=30, Ws=52, C=1024, F=3, dtype="bf16"),
+}
+
+
+def tconv_frame(w: TconvWorkload, b: int, t: int, tensor: str = "x"):
+    """One activation frame [Hs, Ws, C] of (b, t): (values_f32, raw)."""
+    vals, raw = draw((w.Hs * w.Ws * w.C,), seed_for(w.name, tensor, b, t), 1.0, w.dtype)
+    shape = (w.Hs, w.Ws, w.C)
+    return vals.reshape(shape), raw.reshape(shape)
+
+
+def tconv_params(w: TconvWorkload):
+    """(taps [C, 3], bias [C]) as float32."""
+    taps, _ = draw((w.C, 3), seed_for(w.name, "w", 0, 0), float(np.sqrt(1.0 / 3.0)), "f32")
+    bias, _ = draw((w.C,), seed_for(w.name, "bias", 0, 0), 0.1, "f32")
+    return taps, bias

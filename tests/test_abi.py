@@ -1,5 +1,5 @@
 """The C-ABI library on the CPU: it loads, exports every function that
-include/sva.h declares, sizes its workspaces as documented, and rejects bad
+include/*.h declares, sizes its workspaces as documented, and rejects bad
 descriptors before launching anything (no GPU is touched by these calls)."""
 import ctypes
 import os
@@ -20,11 +20,16 @@ except Exception:  # pragma: no cover
 fake_pointers = pytest.mark.skipif(_GPU_VISIBLE, reason="fake device pointers; host-only check")
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
-HEADER = os.path.join(ROOT, "include", "sva.h")
+HEADERS = sorted(os.path.join(ROOT, "include", n) for n in os.listdir(os.path.join(ROOT, "include"))
+                 if n.endswith(".h"))
+
+
+def _header_text():
+    return "\n".join(open(h).read() for h in HEADERS)
 
 
 def _declared_functions():
-    text = open(HEADER).read()
+    text = _header_text()
     text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
     return sorted(set(re.findall(r"\b(sva_[a-z0-9_]+)\s*\(", text)))
 
@@ -176,7 +181,7 @@ def test_bwd_pointer_checks_happen_before_launch():
 
 def _declared_arg_counts():
     """Parameter count of every function declared in the header."""
-    text = re.sub(r"/\*.*?\*/", "", open(HEADER).read(), flags=re.S)
+    text = re.sub(r"/\*.*?\*/", "", _header_text(), flags=re.S)
     out = {}
     for name, params in re.findall(r"\b(sva_[a-z0-9_]+)\s*\(([^)]*)\)\s*;", text):
         params = params.strip()
@@ -205,3 +210,57 @@ def test_fwd_save_needs_states():
     st = sva.lib().sva_lin_attn_fwd_save(ctypes.byref(d), 1 << 36, 2 << 36, 3 << 36, 4 << 36, None, None, None,
                                          None, None, 16, 1 << 40, None)
     assert st == sva.SVA_ERR_INVALID_ARG
+
+
+# Causal temporal convolution (include/sva_tconv.h)
+
+def _tdesc(**kw):
+    base = dict(B=1, T=21, Hs=45, Ws=80, C=1024, frames_per_block=3, dtype=sva.SVA_BF16)
+    base.update(kw)
+    return sva.make_tconv_desc(**base)
+
+
+TCONV_BAD = [
+    (dict(dtype=7), sva.SVA_ERR_UNSUPPORTED),
+    (dict(C=12), sva.SVA_ERR_UNSUPPORTED),          # bf16 needs whole 8-channel vectors
+    (dict(C=6, dtype=sva.SVA_F32), sva.SVA_ERR_UNSUPPORTED),
+    (dict(T=20), sva.SVA_ERR_INVALID_ARG),          # not a whole number of blocks
+    (dict(frames_per_block=0), sva.SVA_ERR_INVALID_ARG),
+    (dict(B=0), sva.SVA_ERR_INVALID_ARG),
+    (dict(Hs=0), sva.SVA_ERR_INVALID_ARG),
+    (dict(C=0), sva.SVA_ERR_INVALID_ARG),
+]
+
+
+@fake_pointers
+@pytest.mark.parametrize("kw,code", TCONV_BAD)
+def test_tconv_bad_descriptors_are_rejected(kw, code):
+    d = _tdesc(**kw)
+    lib = sva.lib()
+    assert lib.sva_tconv_fwd(ctypes.byref(d), 1 << 30, 16, None, None, 1 << 36, None, None) == code
+    assert lib.sva_tconv_commit(ctypes.byref(d), 16, 1 << 30, None) in (code, sva.SVA_ERR_INVALID_ARG)
+
+
+@fake_pointers
+def test_tconv_pointer_checks_happen_before_launch():
+    d = _tdesc()
+    lib = sva.lib()
+    X, Y, W, CI, CO = 1 << 30, 1 << 36, 16, 1 << 20, 1 << 24
+    inv = sva.SVA_ERR_INVALID_ARG
+    assert lib.sva_tconv_fwd(ctypes.byref(d), None, W, None, None, Y, None, None) == inv   # null x
+    assert lib.sva_tconv_fwd(ctypes.byref(d), X, None, None, None, Y, None, None) == inv   # null w
+    assert lib.sva_tconv_fwd(ctypes.byref(d), X, W, None, None, None, None, None) == inv   # null y
+    assert lib.sva_tconv_fwd(ctypes.byref(d), X + 8, W, None, None, Y, None, None) == inv  # misaligned x
+    assert lib.sva_tconv_fwd(ctypes.byref(d), X, W + 4, None, None, Y, None, None) == inv  # misaligned w
+    assert lib.sva_tconv_fwd(ctypes.byref(d), X, W, W + 8, None, Y, None, None) == inv     # misaligned bias
+    assert lib.sva_tconv_fwd(ctypes.byref(d), X, W, None, None, X + 4096, None, None) == inv  # y over x
+    assert lib.sva_tconv_fwd(ctypes.byref(d), X, W, None, X + 4096, Y, None, None) == inv     # cache_in in x
+    assert lib.sva_tconv_fwd(ctypes.byref(d), X, W, None, None, Y, Y + 4096, None) == inv     # cache_out in y
+    assert lib.sva_tconv_fwd(ctypes.byref(d), X, W, None, CI, Y, CI + 4096, None) == inv      # partial alias
+    # apply and commit take exactly one block, and apply needs its cache
+    assert lib.sva_tconv_apply(ctypes.byref(d), CI, X, W, None, Y, None) == inv
+    one = _tdesc(T=3)
+    assert lib.sva_tconv_apply(ctypes.byref(one), None, X, W, None, Y, None) == inv
+    assert lib.sva_tconv_commit(ctypes.byref(d), CO, X, None) == inv
+    assert lib.sva_tconv_commit(ctypes.byref(one), X + 4096, X, None) == inv  # cache inside x
+    assert lib.sva_tconv_commit(ctypes.byref(one), None, X, None) == inv
