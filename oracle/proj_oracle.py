@@ -1,0 +1,80 @@
+"""Plain fp64 CPU oracle for the QKV projection with 4-bit block-scaled
+weights that feeds the attention.
+
+TEST INFRASTRUCTURE ONLY.  This module is the slow, obviously-correct
+statement of what the HIP library computes.  Only the test suite, the smoke
+check and the CPU-baseline leg of the benchmark may import it; the product
+path never does, and this module imports nothing from the product.
+
+Sources:
+  [news]  cstia.com SANA-Video article: the 4-bit quantization paragraph
+          (SVDQuant puts the self-attention QKV and output projections, the
+          cross-attention query and output projections and the FFN 1x1
+          convolutions in 4 bits; norms, the temporal convolution and the
+          cross-attention KV projections stay in higher precision) and the
+          performance paragraph (NVFP4 deployment on an RTX 5090).
+  OCP Microscaling Formats (MX) Specification v1.0: the MXFP4 format used
+          here -- blocks of 32 elements share one E8M0 scale (2^(e-127),
+          e = 255 is NaN); each element is FP4 E2M1 (1 sign, 2 exponent bits
+          with bias 1, 1 mantissa bit; exponent 0 is subnormal: 0 or 0.5).
+
+Readings taken (each is a choice, not a quote):
+  * the 4-bit format is MXFP4 (the block-scaled FP4 that gfx950 implements),
+    not NVFP4; the blocks run along the input channels;
+  * activations stay bf16 (4-bit weights, 16-bit activations); weights are
+    decoded exactly and the products accumulate in fp32 on the GPU;
+  * the fused weight's output columns are [q | k | v], each H heads of d
+    features: column n = which * H * d + h * d + f;
+  * the outputs are q, k, v in the attention's [B, H, N, d] layout, rounded
+    to bf16; the bias, if any, is fp32.
+"""
+
+from __future__ import annotations
+
+import numpy as np
+
+__all__ = ["e2m1_value", "e8m0_value", "mxfp4_decode", "qkv_project"]
+
+
+def e2m1_value(code):
+    """Value of a 4-bit E2M1 code (0..15): bit 3 sign, bits 2..1 exponent
+    (bias 1), bit 0 mantissa; exponent 0 holds the subnormals 0 and 0.5."""
+    code = np.asarray(code, dtype=np.int64)
+    sign = np.where(code & 8, -1.0, 1.0)
+    e = (code >> 1) & 3
+    m = code & 1
+    mag = np.where(e == 0, 0.5 * m, np.ldexp(1.0 + 0.5 * m, e - 1))
+    return sign * mag
+
+
+def e8m0_value(s):
+    """Value of an E8M0 scale byte: 2^(s - 127); 255 is NaN."""
+    s = np.asarray(s, dtype=np.int64)
+    return np.where(s == 255, np.nan, np.ldexp(1.0, s - 127))
+
+
+def mxfp4_decode(codes, scales):
+    """codes [N_out, K] (4-bit values), scales [N_out, K / 32] (bytes) ->
+    W^T [N_out, K] fp64: element (n, k) is e2m1(code) * 2^(scale[n, k//32] - 127)."""
+    codes = np.asarray(codes)
+    scales = np.asarray(scales)
+    n_out, k = codes.shape
+    if k % 32 != 0 or scales.shape != (n_out, k // 32):
+        raise ValueError("scales must be [N_out, K / 32]")
+    return e2m1_value(codes) * np.repeat(e8m0_value(scales), 32, axis=1)
+
+
+def qkv_project(x, codes, scales, bias, H, d):
+    """x [B, N, C] -> (q, k, v), each [B, H, N, d] fp64:
+    y = x W + bias with W = mxfp4_decode(codes, scales)^T, columns split as
+    [q | k | v] x H heads x d features."""
+    x = np.asarray(x, dtype=np.float64)
+    B, N, C = x.shape
+    wt = mxfp4_decode(codes, scales)  # [3 H d, C]
+    if wt.shape != (3 * H * d, C):
+        raise ValueError("weights must be [3 * H * d, C]")
+    y = x @ wt.T
+    if bias is not None:
+        y = y + np.asarray(bias, dtype=np.float64)[None, None, :]
+    y = y.reshape(B, N, 3, H, d).transpose(2, 0, 3, 1, 4)  # [3, B, H, N, d]
+    return y[0].copy(), y[1].copy(), y[2].copy()
