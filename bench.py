@@ -27,8 +27,10 @@ if ROOT not in sys.path:
     sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0  # MI355X HBM3E, GB/s
+MFMA_BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 matrix peak
 KERNEL_SRC = os.path.join(ROOT, "block_causal_linear_phi_amd", "csrc", "sva.hip")
 TCONV_SRC = os.path.join(ROOT, "block_causal_linear_phi_amd", "csrc", "tconv.hip")
+PROJ_SRC = os.path.join(ROOT, "block_causal_linear_phi_amd", "csrc", "proj.hip")
 PROFILES = os.path.join(ROOT, "profiles")
 CALIB_KERNEL = "MulFunctor"  # the plain streaming kernel of copy_calibration()
 
@@ -295,6 +297,70 @@ def tconv_cpu_leg(w, min_secs: float = 10.0, max_frames: int = 24):
                       f"channels, {reps} passes, {secs:.1f} s, numpy fp64 (single-threaded elementwise)"}
 
 
+def proj_leg(w, steps: int, warmup: int, sets: int):
+    """The QKV projection with MXFP4 weights (sva_qkv_proj_mxfp4) on the
+    workload's tokens, `sets` input/output buffer sets alternating.
+    Returns ms per call."""
+    import torch
+    from block_causal_linear_phi_amd import sva
+    from block_causal_linear_phi_amd import workloads as wl
+
+    dev = torch.device("cuda:0")
+    x0 = torch.empty((w.B, w.N, w.C), dtype=torch.bfloat16, device=dev)
+    for j, s0 in enumerate(range(0, w.N, 4096)):
+        n = min(4096, w.N - s0)
+        _, raw = wl.draw((n, w.C), wl.seed_for(w.name, "x", 0, j), 1.0, "bf16")
+        x0[0, s0:s0 + n].copy_(torch.from_numpy(raw.view("int16")).view(torch.bfloat16))
+    codes, scales = wl.mxfp4_weights(w.n_out, w.C, wl.seed_for(w.name, "w", 0, 0))
+    cd = torch.from_numpy(wl.pack_nibbles(codes)).to(dev)
+    sd = torch.from_numpy(scales).to(dev)
+    bias = torch.from_numpy(wl.draw((w.n_out,), wl.seed_for(w.name, "bias", 0, 0), 0.1, "f32")[0]).to(dev)
+    xs = [x0] + [x0.clone() for _ in range(sets - 1)]
+    outs = [[torch.empty((w.B, w.H, w.N, w.d), dtype=torch.bfloat16, device=dev) for _ in range(3)]
+            for _ in range(sets)]
+    stream = torch.cuda.current_stream()
+
+    def step(i):
+        o = outs[i % sets]
+        sva.sva_qkv_proj_mxfp4(xs[i % sets], cd, sd, bias, w.H, w.d, q=o[0], k=o[1], v=o[2], stream=stream)
+
+    for i in range(warmup):
+        step(i)
+    torch.cuda.synchronize()
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    a.record(stream)
+    for i in range(steps):
+        step(i)
+    b.record(stream)
+    torch.cuda.synchronize()
+    return a.elapsed_time(b) / steps
+
+
+def proj_cpu_leg(w, min_secs: float = 10.0, tokens: int = 1024):
+    """The fp64 projection oracle on the host over the workload's first
+    `tokens` tokens, repeated until `min_secs` have passed."""
+    import numpy as np
+    from threadpoolctl import threadpool_info, threadpool_limits
+    from block_causal_linear_phi_amd import workloads as wl
+    from oracle import proj_oracle
+
+    cores = min(len(os.sched_getaffinity(0)), 16)
+    x = wl.draw((tokens, w.C), wl.seed_for(w.name, "x", 0, 0), 1.0, "bf16")[0][None]
+    codes, scales = wl.mxfp4_weights(w.n_out, w.C, wl.seed_for(w.name, "w", 0, 0))
+    with threadpool_limits(limits=cores):
+        blas = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+        reps, t0 = 0, time.perf_counter()
+        while True:
+            proj_oracle.qkv_project(x, codes, scales, None, w.H, w.d)
+            reps += 1
+            secs = time.perf_counter() - t0
+            if secs >= min_secs:
+                break
+    return {"value": reps * tokens / secs, "unit": "tokens/s", "cores": int(min(cores, blas)), "kind": "oracle",
+            "sample": f"{w.name}: first {tokens} tokens, {reps} passes, {secs:.1f} s, numpy fp64 "
+                      f"(decode per pass; BLAS threads {blas} of {cores} host cores)"}
+
+
 def copy_calibration(mib: int, reps: int = 5):
     """A plain streaming kernel of known size (torch.mul(x, 1.0, out=y) on
     fp32: reads and writes mib MiB each).  Its FETCH_SIZE / WRITE_SIZE
@@ -347,7 +413,8 @@ def cpu_leg(w, reps: int):
 
 def _short_kernel(name: str) -> str:
     for k in ("sva_reduce_kernel", "sva_scan_kernel", "sva_apply_kernel", "sva_prep_kernel",
-              "sva_bwd_out_kernel", "sva_bwd_kv_kernel", "sva_tconv_kernel", "sva_tconv_commit_kernel"):
+              "sva_bwd_out_kernel", "sva_bwd_kv_kernel", "sva_tconv_kernel", "sva_tconv_commit_kernel",
+              "sva_qkv_proj_kernel"):
         if k in name:
             short = k.replace("sva_", "").replace("_kernel", "")
             if k == "sva_tconv_kernel" and "sva_tconv_commit_kernel" in name:
@@ -399,8 +466,9 @@ def summarize_profile(args):
         wk = sum(cs["WRITE_SIZE"]) / len(cs["WRITE_SIZE"])
         traffic[k] = {"fetch_kib": fk, "write_kib": wk, "read_bytes": fk * 1024 * f_scale,
                       "write_bytes": wk * 1024 * w_scale, "bytes": fk * 1024 * f_scale + wk * 1024 * w_scale}
-    name = ("tconv_" if args.tconv else "") + args.workload
-    doc = {"workload": name, "source_sha256": source_sha256(TCONV_SRC if args.tconv else KERNEL_SRC),
+    name = ("tconv_" if args.tconv else "proj_" if args.proj else "") + args.workload
+    src = TCONV_SRC if args.tconv else PROJ_SRC if args.proj else KERNEL_SRC
+    doc = {"workload": name, "source_sha256": source_sha256(src),
            "fetch_scale": f_scale,
            "write_scale": w_scale, "calibration": f"{CALIB_KERNEL} kernel reading and writing "
                                                   f"{calib_bytes} bytes", "per_launch": traffic,
@@ -408,7 +476,8 @@ def summarize_profile(args):
     os.makedirs(PROFILES, exist_ok=True)
     with open(traffic_file(name + args.label), "w") as f:
         json.dump(doc, f, indent=1)
-    what = "causal temporal convolution" if args.tconv else "backward" if args.label == "_bwd" else "forward"
+    what = ("causal temporal convolution" if args.tconv else "QKV projection with MXFP4 weights" if args.proj
+            else "backward" if args.label == "_bwd" else "forward")
     lines = [f"# Kernel times and HBM traffic, {args.workload} workload, {what}", "",
              "Commands (run from the repository root on one MI355X):", ""]
     lines += [f"    {c}" for c in args.commands]
@@ -444,6 +513,8 @@ def main():
                     help="time the backward (sva_lin_attn_bwd) instead of the forward")
     ap.add_argument("--tconv", action="store_true",
                     help="time the causal temporal convolution of the Mix-FFN on the workload's grid instead")
+    ap.add_argument("--proj", action="store_true",
+                    help="time the QKV projection with MXFP4 weights on the workload's tokens instead")
     ap.add_argument("--no-streaming", action="store_true",
                     help="with --tconv: time the one-shot call only (profiling runs)")
     ap.add_argument("--copy-calib", type=int, default=0, metavar="MIB",
@@ -468,6 +539,38 @@ def main():
     from block_causal_linear_phi_amd import workloads as wl
     if args.copy_calib:
         copy_calibration(args.copy_calib)
+    if args.proj:
+        pw = wl.PROJ_WORKLOADS["proj_" + args.workload]
+        ms = proj_leg(pw, args.steps, args.warmup, args.sets)
+        flops = 2.0 * pw.B * pw.N * pw.C * pw.n_out
+        tflops = flops / (ms * 1e-3) / 1e12
+        io = pw.B * pw.N * (pw.C + pw.n_out) * 2 + pw.n_out * pw.C * (0.5 + 1 / 32) + pw.n_out * 4
+        line = {
+            "metric": "tokens/s of the QKV projection with MXFP4 weights (q, k, v for all heads)",
+            "value": pw.B * pw.N / (ms * 1e-3), "unit": "tokens/s", "n_gpus": 1, "steps": args.steps,
+            "warmup": args.warmup, "ms_per_step": ms, "higher_is_better": True, "scaling": "weak",
+            "vs_baseline": None, "dtype": "bf16",
+            "data": "synthetic (seeded N(0,1) activations; uniform E2M1 codes, E8M0 scales 2^-7..2^-3; resident in HBM)",
+            "config": {"workload": f"{pw.name}: B={pw.B} N={pw.N} tokens, C={pw.C} -> 3 x {pw.H} heads x {pw.d}, "
+                                   "MXFP4 weights, bf16 activations and outputs",
+                       "B": pw.B, "tokens": pw.N, "C": pw.C, "H": pw.H, "d": pw.d},
+            # bf16 MFMA after an exact weight decode: priced against the bf16 dense peak
+            "roofline": {"bound": "mfma", "kernel": "qkv_proj", "achieved": tflops, "peak": MFMA_BF16_PEAK_TFLOPS,
+                         "unit": "TFLOP/s", "frac": tflops / MFMA_BF16_PEAK_TFLOPS, "traffic": None,
+                         "flops": flops, "io_bytes": io},
+            "hbm_gbs": io / (ms * 1e-3) / 1e9,
+        }
+        try:
+            with open(traffic_file(pw.name)) as f:
+                prof = json.load(f)
+            if prof.get("source_sha256") == source_sha256(PROJ_SRC) and "qkv_proj" in prof.get("per_launch", {}):
+                line["roofline"]["traffic"] = prof["per_launch"]["qkv_proj"]["bytes"] / 1e9
+        except (OSError, ValueError):
+            pass
+        if not args.no_cpu_baseline:
+            line["cpu_baseline"] = proj_cpu_leg(pw)
+        print(json.dumps(line), flush=True)
+        return
     if args.tconv:
         tw = wl.TCONV_WORKLOADS["tconv_" + args.workload]
         fwd_ms, apply_ms, commit_ms = tconv_leg(tw, args.steps, args.warmup, args.sets, not args.no_streaming)

@@ -6,7 +6,7 @@ import subprocess
 
 PKG = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(PKG)
-SRCS = [os.path.join(PKG, "csrc", n) for n in ("sva.hip", "tconv.hip")]
+SRCS = [os.path.join(PKG, "csrc", n) for n in ("sva.hip", "tconv.hip", "proj.hip")]
 OUT = os.path.join(PKG, "libsva.so")
 
 HIPCC_FLAGS = [

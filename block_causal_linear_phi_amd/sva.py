@@ -39,6 +39,11 @@ class SvaTconvDesc(ctypes.Structure):
     ]
 
 
+class SvaProjDesc(ctypes.Structure):
+    _fields_ = [("B", ctypes.c_int), ("N", ctypes.c_int), ("C", ctypes.c_int), ("H", ctypes.c_int),
+                ("d", ctypes.c_int)]
+
+
 class SvaError(RuntimeError):
     def __init__(self, status: int, where: str):
         self.status = status
@@ -69,6 +74,7 @@ _SIG = {
     "sva_tconv_fwd": (ctypes.c_int, [ctypes.POINTER(SvaTconvDesc)] + [_VP] * 7),
     "sva_tconv_apply": (ctypes.c_int, [ctypes.POINTER(SvaTconvDesc)] + [_VP] * 6),
     "sva_tconv_commit": (ctypes.c_int, [ctypes.POINTER(SvaTconvDesc)] + [_VP] * 3),
+    "sva_qkv_proj_mxfp4": (ctypes.c_int, [ctypes.POINTER(SvaProjDesc)] + [_VP] * 8),
 }
 
 
@@ -312,3 +318,23 @@ def sva_tconv_commit(cache, x, *, stream=None):
     desc = _tconv_desc_from(x, x.shape[1])
     st = lib().sva_tconv_commit(ctypes.byref(desc), _ptr(cache), _ptr(x), _stream(stream))
     _check(st, "sva_tconv_commit")
+
+
+# QKV projection with MXFP4 weights (include/sva_proj.h).
+
+def sva_qkv_proj_mxfp4(x, codes, scales, bias, H: int, d: int, *, q=None, k=None, v=None, stream=None):
+    """x [B, N, C] bf16; codes [3 H d, C / 2] uint8 (two 4-bit codes a byte,
+    low nibble first); scales [3 H d, C / 32] uint8 (E8M0); bias [3 H d]
+    fp32 or None.  Returns (q, k, v), each [B, H, N, d] bf16."""
+    import torch
+    if x.dim() != 3 or x.dtype != torch.bfloat16:
+        raise ValueError("x must be [B, N, C] bf16")
+    B, N, C = x.shape
+    desc = SvaProjDesc(B, N, C, H, d)
+    outs = []
+    for t in (q, k, v):
+        outs.append(torch.empty((B, H, N, d), dtype=torch.bfloat16, device=x.device) if t is None else t)
+    st = lib().sva_qkv_proj_mxfp4(ctypes.byref(desc), _ptr(x), _ptr(codes), _ptr(scales), _ptr(bias),
+                                  _ptr(outs[0]), _ptr(outs[1]), _ptr(outs[2]), _stream(stream))
+    _check(st, "sva_qkv_proj_mxfp4")
+    return tuple(outs)

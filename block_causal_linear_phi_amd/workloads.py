@@ -170,3 +170,44 @@ def tconv_params(w: TconvWorkload):
     taps, _ = draw((w.C, 3), seed_for(w.name, "w", 0, 0), float(np.sqrt(1.0 / 3.0)), "f32")
     bias, _ = draw((w.C,), seed_for(w.name, "bias", 0, 0), 0.1, "f32")
     return taps, bias
+
+
+# QKV projection with MXFP4 weights.  The pages give no model width; the
+# input channels are the attention workloads' H * d = 1024 (as for the
+# temporal convolution), the outputs [q | k | v] for 16 heads of 64.  Codes
+# are uniform over the 16 E2M1 values; block scales are E8M0 bytes 120..124
+# (2^-7 .. 2^-3); activations N(0, 1) bf16, drawn per (workload, b, token
+# block of 4096) slice; bias N(0, 0.01) fp32.
+
+@dataclass(frozen=True)
+class ProjWorkload:
+    name: str
+    B: int
+    N: int
+    C: int
+    H: int
+    d: int
+
+    @property
+    def n_out(self) -> int:
+        return 3 * self.H * self.d
+
+
+PROJ_WORKLOADS = {
+    "proj_720p": ProjWorkload("proj_720p", B=1, N=75600, C=1024, H=16, d=64),
+}
+
+
+def mxfp4_weights(n_out: int, C: int, seed: int):
+    """(codes [n_out, C] uint8 in 0..15, scales [n_out, C // 32] uint8)."""
+    rng = np.random.default_rng(np.random.PCG64(seed))
+    codes = rng.integers(0, 16, (n_out, C), dtype=np.uint8)
+    scales = rng.integers(120, 125, (n_out, C // 32), dtype=np.uint8)
+    return codes, scales
+
+
+def pack_nibbles(codes: np.ndarray) -> np.ndarray:
+    """[rows, C] 4-bit codes -> [rows, C // 2] bytes, channel 2j in the low
+    nibble of byte j and channel 2j + 1 in the high nibble."""
+    c = np.asarray(codes, dtype=np.uint8)
+    return (c[:, 0::2] | (c[:, 1::2] << 4)).astype(np.uint8)

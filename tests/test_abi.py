@@ -264,3 +264,31 @@ def test_tconv_pointer_checks_happen_before_launch():
     assert lib.sva_tconv_commit(ctypes.byref(d), CO, X, None) == inv
     assert lib.sva_tconv_commit(ctypes.byref(one), X + 4096, X, None) == inv  # cache inside x
     assert lib.sva_tconv_commit(ctypes.byref(one), None, X, None) == inv
+
+
+# QKV projection (include/sva_proj.h)
+
+@fake_pointers
+def test_proj_checks_happen_before_launch():
+    lib = sva.lib()
+    inv, uns = sva.SVA_ERR_INVALID_ARG, sva.SVA_ERR_UNSUPPORTED
+    X, C, S, Q, K, V = 1 << 30, 1 << 20, 1 << 21, 1 << 34, 1 << 35, 1 << 36
+
+    def call(**kw):
+        base = dict(B=1, N=75600, C=1024, H=16, d=64)
+        base.update(kw)
+        dsc = sva.SvaProjDesc(base["B"], base["N"], base["C"], base["H"], base["d"])
+        return lambda *p: lib.sva_qkv_proj_mxfp4(ctypes.byref(dsc), *p, None)
+
+    assert call(C=96)(X, C, S, None, Q, K, V) == uns        # C not a multiple of 64
+    assert call(H=3)(X, C, S, None, Q, K, V) == uns         # H d not a multiple of 128
+    assert call(d=36, H=32)(X, C, S, None, Q, K, V) == uns  # d not a multiple of 8
+    assert call(N=0)(X, C, S, None, Q, K, V) == inv
+    ok = call()
+    assert ok(None, C, S, None, Q, K, V) == inv            # null x
+    assert ok(X, C, S, None, Q, None, V) == inv            # null k
+    assert ok(X + 8, C, S, None, Q, K, V) == inv           # misaligned x
+    assert ok(X, C + 4, S, None, Q, K, V) == inv           # misaligned codes
+    assert ok(X, C, S, 8, Q, K, V) == inv                  # misaligned bias
+    assert ok(X, C, S, None, X + 4096, K, V) == inv        # q over x
+    assert ok(X, C, S, None, Q, Q + 4096, V) == inv        # k over q
