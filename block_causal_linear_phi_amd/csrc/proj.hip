@@ -15,10 +15,15 @@
 // (256 x 64 bf16) and weight tile (128 x 64, decoded to bf16 with
 // v_cvt_scalef32_pk_bf16_fp4: two 4-bit codes and their E8M0 block scale per
 // instruction, exact) sit in LDS, double-buffered, with the global loads of
-// the stage after next in registers.  Consecutive workgroup indices go to
-// the eight XCDs in turn, so the tiles are ordered to keep every workgroup
-// that reads one x tile on the same XCD (its L2 then serves the 24 output
-// tiles of a 720p QKV projection).
+// the stage after next in registers.  At this tile the operand reads from LDS
+// (0.5 KB an MFMA, 128 KB a stage per CU) take about as long as the MFMAs
+// (measured: without them the kernel ran twice as fast).  Tried and slower:
+// 128 x 128 per wave (one wave per SIMD, the accumulators in AGPRs, then
+// room for one stage of prefetch only), decoding the weights per wave from
+// staged 4-bit codes, two 4-wave workgroups per CU.  Consecutive workgroup
+// indices go to the eight XCDs in turn, so the tiles are ordered to keep
+// every workgroup that reads one x tile on the same XCD (its L2 then serves
+// the 24 output tiles of a 720p QKV projection).
 
 #include <hip/hip_runtime.h>
 #include <stdint.h>
@@ -51,9 +56,14 @@ struct ProjGeo {
   int stages;     // C / kTileK
 };
 
-// Piece p of row r: XOR-swizzled so that 16 lanes reading one piece of 16
-// rows hit different banks.
-__device__ __forceinline__ int sw(int r, int p) { return r * kPieces + (p ^ (r & 7)); }
+// Piece p of row r, XOR-swizzled with f(r) = (r & 7) ^ ((r >> 1) & 4).  A
+// 16-byte LDS read is served eight lanes at a time, so the eight rows one
+// such group reads must get distinct f: the B operand's groups are eight
+// consecutive rows from a multiple of 8, the A operand's (fo order) rows
+// {0-3, 8-11} or {4-7, 12-15} (+32): both are conflict-free, and so are the
+// tile writes (8 pieces of one row; pieces {0, 2, 4, 6} of two adjacent
+// rows).  r & 7 alone gave the A reads 2-way conflicts.
+__device__ __forceinline__ int sw(int r, int p) { return r * kPieces + (p ^ ((r & 7) ^ ((r >> 1) & 4))); }
 
 // A-operand row permutation: accumulator rt, element i of lane (g, .) holds
 // feature fo(rt, 4g + i) = 32(rt/2) + 8g + 4(rt%2) + i, so accumulators 0, 1
@@ -72,10 +82,11 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t rsrc(const void* base, uint32_
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, 0x00020000);
 }
 
-// E8M0 scale byte -> the fp32 factor 2^(e - 127); 0 is the denormal 2^-127,
-// 255 is NaN.
+// E8M0 scale byte -> the fp32 factor 2^(e - 127) (0 gives the denormal
+// 2^-127), or NaN for 255; selects, no branches.
 __device__ __forceinline__ float e8m0_scale(uint32_t e) {
-  return e == 0 ? __uint_as_float(0x00400000u) : e == 255 ? __uint_as_float(0x7fc00000u) : __uint_as_float(e << 23);
+  const uint32_t bits = e == 0 ? 0x00400000u : e << 23;
+  return __uint_as_float(e == 255 ? 0x7fc00000u : bits);
 }
 
 // Eight bytes of codes (16 channels, low nibble first) -> 16 bf16 weights.
@@ -91,7 +102,7 @@ __device__ __forceinline__ void decode16(uint2 c, float s, uint32_t (&o)[8]) {
 }
 
 // A stage's global data in registers: 4 pieces of x, 8 bytes of codes and
-// one scale byte per thread.
+// the aligned word holding the thread's scale byte.
 struct StageRegs {
   uint4 x[kXLoads];
   uint2 c;
@@ -143,16 +154,22 @@ __global__ __launch_bounds__(kPjThreads, 1) void sva_qkv_proj_kernel(
       r.x[j] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(xr, off, 0, 0));
     }
     r.c = *(const uint2*)(crow + k0 / 2 + 8 * w_q);
-    r.s = srow[(k0 + 16 * w_q) / 32];
+    r.s = *(const uint32_t*)(srow + (((k0 + 16 * w_q) / 32) & ~3));
   };
-  auto store = [&](const StageRegs& r, int buf) {
+  auto store = [&](const StageRegs& r, int s, int buf) {
 #pragma unroll
     for (int j = 0; j < kXLoads; ++j) {
       const int u = tid + j * kPjThreads;
       xs[buf][sw(u / kPieces, u % kPieces)] = r.x[j];
     }
+    // The scale byte passes through an empty asm here: otherwise the
+    // compiler masks it at the end of the previous iteration, right after
+    // its load, and waits there for every load in flight.
+    uint32_t sb = r.s;
+    asm volatile("" : "+v"(sb));
+    const int sbyte = ((s * kTileK + 16 * w_q) / 32) & 3;
     uint32_t o[8];
-    decode16(r.c, e8m0_scale(r.s), o);
+    decode16(r.c, e8m0_scale((sb >> (8 * sbyte)) & 0xffu), o);
     ws[buf][sw(w_row, 2 * w_q)] = make_uint4(o[0], o[1], o[2], o[3]);
     ws[buf][sw(w_row, 2 * w_q + 1)] = make_uint4(o[4], o[5], o[6], o[7]);
   };
@@ -180,16 +197,26 @@ __global__ __launch_bounds__(kPjThreads, 1) void sva_qkv_proj_kernel(
 
   // Pipeline: stage s is computed from LDS buffer s % 2 while stage s + 1
   // waits in registers set (s + 1) % 2 and stage s + 2's loads are in flight.
+  // Every prefetch is issued, with the stage index clamped to the last one
+  // (repeat loads at the tail are in bounds and unused): a conditional load
+  // leaves the compiler unsure how many loads are in flight after it, and it
+  // then waits for all of them.
+  const int last = g.stages - 1;
   StageRegs r0, r1;
   load(r0, 0);
-  if (g.stages > 1) load(r1, 1);
-  store(r0, 0);
-  if (g.stages > 2) load(r0, 2);
+  load(r1, min(1, last));
+  store(r0, 0, 0);
+  load(r0, min(2, last));
   __syncthreads();
+  // The scheduling barriers keep the next stage's decode below the MFMAs:
+  // hoisted above them, its first use of a just-loaded scale byte made the
+  // wave wait for every load in flight (one in-order counter) each stage.
   auto step = [&](int s, StageRegs& nxt) {
     compute(s & 1);
-    if (s + 1 < g.stages) store(nxt, (s + 1) & 1);
-    if (s + 3 < g.stages) load(nxt, s + 3);
+    __builtin_amdgcn_sched_barrier(0);
+    if (s + 1 < g.stages) store(nxt, s + 1, (s + 1) & 1);
+    __builtin_amdgcn_sched_barrier(0);
+    load(nxt, min(s + 3, last));
     __syncthreads();
   };
   int s = 0;
@@ -247,7 +274,8 @@ extern "C" sva_status sva_qkv_proj_mxfp4(const sva_proj_desc* desc, const void* 
   if (!desc) return SVA_ERR_INVALID_ARG;
   const sva_proj_desc& d = *desc;
   if (d.B < 1 || d.N < 1 || d.C < 1 || d.H < 1 || d.d < 1) return SVA_ERR_INVALID_ARG;
-  if (d.C % kTileK != 0 || (d.H * d.d) % kTileN != 0 || d.d % 8 != 0) return SVA_ERR_UNSUPPORTED;
+  // C: whole stages, and word-aligned rows of scale bytes (C / 32 a multiple of 4)
+  if (d.C % 128 != 0 || (d.H * d.d) % kTileN != 0 || d.d % 8 != 0) return SVA_ERR_UNSUPPORTED;
   const long long M = (long long)d.B * d.N;
   const long long Mt = (M + kTileM - 1) / kTileM;
   const long long Nt = 3LL * d.H * d.d / kTileN;
@@ -256,7 +284,7 @@ extern "C" sva_status sva_qkv_proj_mxfp4(const sva_proj_desc* desc, const void* 
     return SVA_ERR_UNSUPPORTED;
   if (!x || !codes || !scales || !q || !k || !v) return SVA_ERR_INVALID_ARG;
   if (!aligned(x, 16) || !aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(codes, 8) ||
-      (bias && !aligned(bias, 16)))
+      !aligned(scales, 4) || (bias && !aligned(bias, 16)))
     return SVA_ERR_INVALID_ARG;
   const size_t xb = (size_t)M * d.C * 2, ob = (size_t)M * d.H * d.d * 2;
   const size_t cb = 3 * (size_t)d.H * d.d * d.C / 2, sb = 3 * (size_t)d.H * d.d * d.C / 32;

@@ -30,12 +30,12 @@
  *   scales  [3*H*d, C/32] bytes (E8M0), one per 32 input channels
  *   bias    [3*H*d] fp32, or NULL
  *   q, k, v [B, H, N, d] bf16, the layout sva_lin_attn_* take
- * Limits: C a multiple of 64; H*d a multiple of 128; d a multiple of 8.
+ * Limits: C a multiple of 128; H*d a multiple of 128; d a multiple of 8.
  *
  * Ownership and errors as in sva.h: caller-owned device pointers (x, q, k,
- * v 16-byte aligned; codes 8-byte aligned), nothing allocated or kept,
- * synchronous validation before any launch (nothing written on error),
- * work queued on `stream`.  No workspace is needed.
+ * v 16-byte aligned; codes 8-byte and scales 4-byte aligned), nothing
+ * allocated or kept, synchronous validation before any launch (nothing
+ * written on error), work queued on `stream`.  No workspace is needed.
  */
 #ifndef SVA_PROJ_H
 #define SVA_PROJ_H

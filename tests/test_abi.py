@@ -280,7 +280,8 @@ def test_proj_checks_happen_before_launch():
         dsc = sva.SvaProjDesc(base["B"], base["N"], base["C"], base["H"], base["d"])
         return lambda *p: lib.sva_qkv_proj_mxfp4(ctypes.byref(dsc), *p, None)
 
-    assert call(C=96)(X, C, S, None, Q, K, V) == uns        # C not a multiple of 64
+    assert call(C=96)(X, C, S, None, Q, K, V) == uns        # C not a multiple of 128
+    assert call(C=192)(X, C, S, None, Q, K, V) == uns
     assert call(H=3)(X, C, S, None, Q, K, V) == uns         # H d not a multiple of 128
     assert call(d=36, H=32)(X, C, S, None, Q, K, V) == uns  # d not a multiple of 8
     assert call(N=0)(X, C, S, None, Q, K, V) == inv
@@ -289,6 +290,7 @@ def test_proj_checks_happen_before_launch():
     assert ok(X, C, S, None, Q, None, V) == inv            # null k
     assert ok(X + 8, C, S, None, Q, K, V) == inv           # misaligned x
     assert ok(X, C + 4, S, None, Q, K, V) == inv           # misaligned codes
+    assert ok(X, C, S + 2, None, Q, K, V) == inv           # misaligned scales
     assert ok(X, C, S, 8, Q, K, V) == inv                  # misaligned bias
     assert ok(X, C, S, None, X + 4096, K, V) == inv        # q over x
     assert ok(X, C, S, None, Q, Q + 4096, V) == inv        # k over q
