@@ -3,7 +3,8 @@ constant-size block KV cache (SANA-Video) on AMD MI355X (gfx950).
 
 The computation lives in libsva.so (hand-written HIP kernels behind the C ABI
 in include/sva.h, include/sva_tconv.h and include/sva_proj.h); `sva` is its thin
-ctypes binding.
+ctypes binding and `autograd` wraps the attention's forward and backward for
+torch training.
 """
 from .sva import (  # noqa: F401
     SVA_BF16, SVA_F32, SvaDesc, SvaError, make_desc, sva_block_cache_apply, sva_block_cache_commit,
@@ -12,3 +13,4 @@ from .sva import (  # noqa: F401
     SvaTconvDesc, make_tconv_desc, sva_tconv_apply, sva_tconv_commit, sva_tconv_fwd,
     SvaProjDesc, sva_qkv_proj_mxfp4,
 )
+from .autograd import BlockCausalLinearAttention, block_causal_linear_attention  # noqa: F401
