@@ -314,6 +314,7 @@ def proj_leg(w, steps: int, warmup: int, sets: int):
     codes, scales = wl.mxfp4_weights(w.n_out, w.C, wl.seed_for(w.name, "w", 0, 0))
     cd = torch.from_numpy(wl.pack_nibbles(codes)).to(dev)
     sd = torch.from_numpy(scales).to(dev)
+    wp = sva.sva_mxfp4_pack_weights(cd, sd, w.H, w.d)  # once, as at weight load
     bias = torch.from_numpy(wl.draw((w.n_out,), wl.seed_for(w.name, "bias", 0, 0), 0.1, "f32")[0]).to(dev)
     xs = [x0] + [x0.clone() for _ in range(sets - 1)]
     outs = [[torch.empty((w.B, w.H, w.N, w.d), dtype=torch.bfloat16, device=dev) for _ in range(3)]
@@ -322,7 +323,7 @@ def proj_leg(w, steps: int, warmup: int, sets: int):
 
     def step(i):
         o = outs[i % sets]
-        sva.sva_qkv_proj_mxfp4(xs[i % sets], cd, sd, bias, w.H, w.d, q=o[0], k=o[1], v=o[2], stream=stream)
+        sva.sva_qkv_proj_mxfp4(xs[i % sets], wp, bias, w.H, w.d, q=o[0], k=o[1], v=o[2], stream=stream)
 
     for i in range(warmup):
         step(i)

@@ -9,21 +9,23 @@
 // v_mfma_f32_16x16x32_bf16: the A operand is a 16-feature slice of the
 // decoded weights, the B operand 16 tokens, so a lane's accumulators hold
 // consecutive output features of one token and the epilogue writes 16-byte
-// pieces of the [B, H, N, d] rows directly.  A workgroup (8 waves) owns 128
-// output features x 256 tokens; a wave 64 features x 64 tokens (4 x 4
-// accumulators).  The input channels advance 64 per stage: a stage's x tile
-// (256 x 64 bf16) and weight tile (128 x 64, decoded to bf16 with
-// v_cvt_scalef32_pk_bf16_fp4: two 4-bit codes and their E8M0 block scale per
-// instruction, exact) sit in LDS, double-buffered, with the global loads of
-// the stage after next in registers.  At this tile the operand reads from LDS
-// (0.5 KB an MFMA, 128 KB a stage per CU) take about as long as the MFMAs
-// (measured: without them the kernel ran twice as fast).  Tried and slower:
-// 128 x 128 per wave (one wave per SIMD, the accumulators in AGPRs, then
-// room for one stage of prefetch only), decoding the weights per wave from
-// staged 4-bit codes, two 4-wave workgroups per CU.  Consecutive workgroup
-// indices go to the eight XCDs in turn, so the tiles are ordered to keep
-// every workgroup that reads one x tile on the same XCD (its L2 then serves
-// the 24 output tiles of a 720p QKV projection).
+// pieces of the [B, H, N, d] rows directly.  A workgroup (8 waves) owns 256
+// output features x 128 tokens; a wave 64 features x 64 tokens (4 x 4
+// accumulators).  The input channels advance 128 per stage.
+//
+// Only x goes through LDS (128 x 128 bf16 a stage, double-buffered, the
+// stage after next in registers).  Each wave loads its own weights straight
+// from global memory into registers, one stage ahead, in the packed layout
+// sva_mxfp4_pack_weights writes (4 KiB of codes and 256 bytes of scales per
+// wave and stage, contiguous), and decodes them per k-step with
+// v_cvt_scalef32_pk_bf16_fp4 (two 4-bit codes and their E8M0 block scale per
+// instruction, exact).  Staging decoded weights in LDS instead (the previous
+// design) made the operand reads from LDS as long as the MFMAs (0.5 KB an
+// MFMA at this tile); the natural [row][channel] code layout, read straight
+// from global memory, stalled the texture path on 16 rows per load.
+// Consecutive workgroup indices go to the eight XCDs in turn, so the tiles
+// are ordered to keep every workgroup that reads one x tile on the same XCD
+// (its L2 then serves the 12 output tiles of a 720p QKV projection).
 
 #include <hip/hip_runtime.h>
 #include <stdint.h>
@@ -39,12 +41,11 @@ typedef __bf16 pj_bf16x8 __attribute__((ext_vector_type(8)));
 typedef __bf16 pj_bf16x2 __attribute__((ext_vector_type(2)));
 
 constexpr int kPjThreads = 512;  // 8 waves
-constexpr int kTileN = 128;      // output features per workgroup
-constexpr int kTileM = 256;      // tokens per workgroup
-constexpr int kTileK = 64;       // input channels per stage
-constexpr int kPieces = kTileK * 2 / 16;        // 16-byte pieces of a row per stage
+constexpr int kTileN = 256;      // output features per workgroup
+constexpr int kTileM = 128;      // tokens per workgroup
+constexpr int kTileK = 128;      // input channels per stage
+constexpr int kPieces = kTileK * 2 / 16;        // 16-byte pieces of an x row per stage
 constexpr int kXU4 = kTileM * kPieces;          // x tile, 16-byte units
-constexpr int kWU4 = kTileN * kPieces;          // weight tile, 16-byte units
 constexpr int kXLoads = kXU4 / kPjThreads;      // x pieces per thread per stage
 
 struct ProjGeo {
@@ -52,18 +53,16 @@ struct ProjGeo {
   int N;          // tokens per sample
   int C;          // input channels
   int H, d;
+  int n_out;      // 3 * H * d
   int Mt, Nt;     // token tiles, feature tiles
   int stages;     // C / kTileK
 };
 
-// Piece p of row r, XOR-swizzled with f(r) = (r & 7) ^ ((r >> 1) & 4).  A
-// 16-byte LDS read is served eight lanes at a time, so the eight rows one
-// such group reads must get distinct f: the B operand's groups are eight
-// consecutive rows from a multiple of 8, the A operand's (fo order) rows
-// {0-3, 8-11} or {4-7, 12-15} (+32): both are conflict-free, and so are the
-// tile writes (8 pieces of one row; pieces {0, 2, 4, 6} of two adjacent
-// rows).  r & 7 alone gave the A reads 2-way conflicts.
-__device__ __forceinline__ int sw(int r, int p) { return r * kPieces + (p ^ ((r & 7) ^ ((r >> 1) & 4))); }
+// Piece p of row r of the x tile, XOR-swizzled by r & 7: the B operand's
+// 16-byte reads (served eight lanes at a time) take one piece of eight
+// consecutive rows, and the tile writes eight consecutive pieces of one row;
+// both land in eight distinct 16-byte bank groups.
+__device__ __forceinline__ int sw(int r, int p) { return r * kPieces + (p ^ (r & 15)); }
 
 // A-operand row permutation: accumulator rt, element i of lane (g, .) holds
 // feature fo(rt, 4g + i) = 32(rt/2) + 8g + 4(rt%2) + i, so accumulators 0, 1
@@ -89,23 +88,20 @@ __device__ __forceinline__ float e8m0_scale(uint32_t e) {
   return __uint_as_float(e == 255 ? 0x7fc00000u : bits);
 }
 
-// Eight bytes of codes (16 channels, low nibble first) -> 16 bf16 weights.
-__device__ __forceinline__ void decode16(uint2 c, float s, uint32_t (&o)[8]) {
-  o[0] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(c.x, s, 0));
-  o[1] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(c.x, s, 1));
-  o[2] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(c.x, s, 2));
-  o[3] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(c.x, s, 3));
-  o[4] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(c.y, s, 0));
-  o[5] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(c.y, s, 1));
-  o[6] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(c.y, s, 2));
-  o[7] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(c.y, s, 3));
+// One word of codes (8 channels, low nibble first) -> the 8 bf16 weights of
+// an A operand.
+__device__ __forceinline__ uint4 decode8(uint32_t c, float s) {
+  return make_uint4(__builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(c, s, 0)),
+                    __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(c, s, 1)),
+                    __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(c, s, 2)),
+                    __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(c, s, 3)));
 }
 
-// A stage's global data in registers: 4 pieces of x, 8 bytes of codes and
-// the aligned word holding the thread's scale byte.
-struct StageRegs {
-  uint4 x[kXLoads];
-  uint2 c;
+// A wave's weights for one stage: per accumulator row tile rt, the lane's 16
+// bytes of codes (one MX block: 32 channels), and one word whose byte rt is
+// that block's scale.
+struct WRegs {
+  uint4 c[4];
   uint32_t s;
 };
 
@@ -115,11 +111,9 @@ __device__ __forceinline__ uint32_t pack2(float a, float b) {
 }
 
 __global__ __launch_bounds__(kPjThreads, 1) void sva_qkv_proj_kernel(
-    const void* __restrict__ xp, const uint8_t* __restrict__ codes, const uint8_t* __restrict__ scales,
-    const float* __restrict__ bias, void* __restrict__ qp, void* __restrict__ kp, void* __restrict__ vp,
-    ProjGeo g) {
+    const void* __restrict__ xp, const uint8_t* __restrict__ wpack, const float* __restrict__ bias,
+    void* __restrict__ qp, void* __restrict__ kp, void* __restrict__ vp, ProjGeo g) {
   __shared__ uint4 xs[2][kXU4];
-  __shared__ uint4 ws[2][kWU4];
 
   // Tile order: workgroup i runs on XCD i % 8; within an XCD, consecutive
   // workgroups take the feature tiles of one token tile.
@@ -134,44 +128,44 @@ __global__ __launch_bounds__(kPjThreads, 1) void sva_qkv_proj_kernel(
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int lane = tid & 63;
   const int lg = lane >> 4, lr = lane & 15;
-  const int wn = wave & 1, wm = wave >> 1;  // 64 features x 64 tokens each
+  const int wn = wave & 3, wm = wave >> 2;  // 64 features x 64 tokens each
 
-  // x rows m0 .. m0 + 255 (rows past M read as zeros)
+  // x rows m0 .. m0 + 127 (rows past M read as zeros)
   const int rows = min(kTileM, g.M - m0);
   const size_t row_bytes = (size_t)g.C * 2;
   const __amdgpu_buffer_rsrc_t xr = rsrc((const char*)xp + (size_t)m0 * row_bytes, (uint32_t)(rows * row_bytes));
-  // weights: thread t decodes 16 channels (half an MX block) of feature t / 4
-  const int w_row = tid >> 2, w_q = tid & 3;
-  const uint8_t* crow = codes + (size_t)(n0 + w_row) * (g.C / 2);
-  const uint8_t* srow = scales + (size_t)(n0 + w_row) * (g.C / 32);
 
-  auto load = [&](StageRegs& r, int s) {
+  // The MFMA contraction slots of a stage are assigned so that lane group lg
+  // takes channels 32 lg + 8 j + e in k-step j: the lane's weights of a stage
+  // are then one MX block per accumulator row tile, 16 bytes of codes and one
+  // scale byte, and its x operands are pieces 4 lg + j of the token row.  The
+  // packed layout puts a wave's codes of one stage in 4 KiB and its scales in
+  // one word per lane, so each load is contiguous across the wave.  A wave
+  // past n_out (a partial last tile) reads the last block and stores nothing.
+  const int blk = min(n0 / 64 + wn, g.n_out / 64 - 1);
+  const uint8_t* cbase = wpack + ((size_t)blk * g.stages * 4) * 1024 + lane * 16;
+  const uint8_t* sbase = wpack + (size_t)g.n_out * (g.C / 2) + ((size_t)blk * g.stages * 64 + lane) * 4;
+
+  auto load_x = [&](uint4 (&r)[kXLoads], int s) {
     const int k0 = s * kTileK;
 #pragma unroll
     for (int j = 0; j < kXLoads; ++j) {
       const int u = tid + j * kPjThreads;
       const uint32_t off = (uint32_t)((u / kPieces) * row_bytes + (size_t)k0 * 2 + 16 * (u % kPieces));
-      r.x[j] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(xr, off, 0, 0));
+      r[j] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(xr, off, 0, 0));
     }
-    r.c = *(const uint2*)(crow + k0 / 2 + 8 * w_q);
-    r.s = *(const uint32_t*)(srow + (((k0 + 16 * w_q) / 32) & ~3));
   };
-  auto store = [&](const StageRegs& r, int s, int buf) {
+  auto store_x = [&](const uint4 (&r)[kXLoads], int buf) {
 #pragma unroll
     for (int j = 0; j < kXLoads; ++j) {
       const int u = tid + j * kPjThreads;
-      xs[buf][sw(u / kPieces, u % kPieces)] = r.x[j];
+      xs[buf][sw(u / kPieces, u % kPieces)] = r[j];
     }
-    // The scale byte passes through an empty asm here: otherwise the
-    // compiler masks it at the end of the previous iteration, right after
-    // its load, and waits there for every load in flight.
-    uint32_t sb = r.s;
-    asm volatile("" : "+v"(sb));
-    const int sbyte = ((s * kTileK + 16 * w_q) / 32) & 3;
-    uint32_t o[8];
-    decode16(r.c, e8m0_scale((sb >> (8 * sbyte)) & 0xffu), o);
-    ws[buf][sw(w_row, 2 * w_q)] = make_uint4(o[0], o[1], o[2], o[3]);
-    ws[buf][sw(w_row, 2 * w_q + 1)] = make_uint4(o[4], o[5], o[6], o[7]);
+  };
+  auto load_w = [&](WRegs& w, int s) {
+#pragma unroll
+    for (int rt = 0; rt < 4; ++rt) w.c[rt] = *(const uint4*)(cbase + ((size_t)s * 4 + rt) * 1024);
+    w.s = *(const uint32_t*)(sbase + (size_t)s * 256);
   };
 
   pj_floatx4 acc[4][4];
@@ -180,14 +174,25 @@ __global__ __launch_bounds__(kPjThreads, 1) void sva_qkv_proj_kernel(
 #pragma unroll
     for (int j = 0; j < 4; ++j) acc[i][j] = pj_floatx4{0.f, 0.f, 0.f, 0.f};
 
-  auto compute = [&](int buf) {
+  auto compute = [&](const WRegs& w, int buf) {
+    // The scale bytes pass through an empty asm here: otherwise the
+    // compiler converts them right after their loads, one stage early, and
+    // waits there for every load in flight (one in-order counter).
+    uint32_t e = w.s;
+    asm volatile("" : "+v"(e));
+    float sc[4];
 #pragma unroll
-    for (int ks = 0; ks < kTileK / 32; ++ks) {
+    for (int rt = 0; rt < 4; ++rt) sc[rt] = e8m0_scale((e >> (8 * rt)) & 0xffu);
+#pragma unroll
+    for (int j = 0; j < kTileK / 32; ++j) {
       uint4 a[4], b[4];
 #pragma unroll
-      for (int rt = 0; rt < 4; ++rt) a[rt] = ws[buf][sw(wn * 64 + fo(rt, lr), 4 * ks + lg)];
+      for (int rt = 0; rt < 4; ++rt) {
+        const uint32_t cw = j == 0 ? w.c[rt].x : j == 1 ? w.c[rt].y : j == 2 ? w.c[rt].z : w.c[rt].w;
+        a[rt] = decode8(cw, sc[rt]);
+      }
 #pragma unroll
-      for (int tt = 0; tt < 4; ++tt) b[tt] = xs[buf][sw(wm * 64 + tt * 16 + lr, 4 * ks + lg)];
+      for (int tt = 0; tt < 4; ++tt) b[tt] = xs[buf][sw(wm * 64 + tt * 16 + lr, 4 * lg + j)];
 #pragma unroll
       for (int rt = 0; rt < 4; ++rt)
 #pragma unroll
@@ -195,36 +200,38 @@ __global__ __launch_bounds__(kPjThreads, 1) void sva_qkv_proj_kernel(
     }
   };
 
-  // Pipeline: stage s is computed from LDS buffer s % 2 while stage s + 1
-  // waits in registers set (s + 1) % 2 and stage s + 2's loads are in flight.
-  // Every prefetch is issued, with the stage index clamped to the last one
-  // (repeat loads at the tail are in bounds and unused): a conditional load
-  // leaves the compiler unsure how many loads are in flight after it, and it
-  // then waits for all of them.
+  // Pipeline: stage s is computed from LDS buffer s % 2 and weight registers
+  // s % 2 while stage s + 1's x waits in registers and stage s + 2's x loads
+  // are in flight; stage s + 1's weights are requested before stage s's
+  // MFMAs.  Every load is issued, with the stage index clamped to the last
+  // one (repeat loads at the tail are in bounds and unused): a conditional
+  // load leaves the compiler unsure how many loads are in flight after it,
+  // and it then waits for all of them.
   const int last = g.stages - 1;
-  StageRegs r0, r1;
-  load(r0, 0);
-  load(r1, min(1, last));
-  store(r0, 0, 0);
-  load(r0, min(2, last));
+  uint4 x0[kXLoads], x1[kXLoads];
+  WRegs w0, w1;
+  load_w(w0, 0);
+  load_x(x0, 0);
+  load_x(x1, min(1, last));
+  store_x(x0, 0);
+  load_x(x0, min(2, last));
   __syncthreads();
-  // The scheduling barriers keep the next stage's decode below the MFMAs:
-  // hoisted above them, its first use of a just-loaded scale byte made the
-  // wave wait for every load in flight (one in-order counter) each stage.
-  auto step = [&](int s, StageRegs& nxt) {
-    compute(s & 1);
+  auto step = [&](int s, const WRegs& wc, WRegs& wn_, uint4 (&xn)[kXLoads]) {
+    load_w(wn_, min(s + 1, last));
     __builtin_amdgcn_sched_barrier(0);
-    if (s + 1 < g.stages) store(nxt, s + 1, (s + 1) & 1);
+    compute(wc, s & 1);
     __builtin_amdgcn_sched_barrier(0);
-    load(nxt, min(s + 3, last));
+    if (s + 1 < g.stages) store_x(xn, (s + 1) & 1);
+    __builtin_amdgcn_sched_barrier(0);
+    load_x(xn, min(s + 3, last));
     __syncthreads();
   };
   int s = 0;
   for (; s + 2 <= g.stages; s += 2) {
-    step(s, r1);
-    step(s + 1, r0);
+    step(s, w0, w1, x1);
+    step(s + 1, w1, w0, x0);
   }
-  if (s < g.stages) step(s, r1);
+  if (s < g.stages) step(s, w0, w1, x1);
 
   // Epilogue: lane (lg, lr) holds, for token tile tt, features
   // fb + 8 lg + 0..7 (accumulators 0, 1) and fb + 32 + 8 lg + 0..7 (2, 3).
@@ -232,6 +239,7 @@ __global__ __launch_bounds__(kPjThreads, 1) void sva_qkv_proj_kernel(
 #pragma unroll
   for (int run = 0; run < 2; ++run) {
     const int f = n0 + wn * 64 + 32 * run + 8 * lg;  // first of 8 features
+    if (f >= g.n_out) continue;
     const int which = f / HD;
     const int h = (f - which * HD) / g.d;
     const int fd = f - which * HD - h * g.d;
@@ -259,6 +267,27 @@ __global__ __launch_bounds__(kPjThreads, 1) void sva_qkv_proj_kernel(
   }
 }
 
+// Repacks natural-layout MXFP4 weights (codes [n_out, C/2], scales
+// [n_out, C/32]) into the projection's layout: thread (blk, s, lane) writes
+// the lane's 16 code bytes of each row tile rt of 64-feature block blk and
+// stage s, and the word of their four scale bytes.
+__global__ void sva_mxfp4_pack_kernel(const uint8_t* __restrict__ codes, const uint8_t* __restrict__ scales,
+                                      uint8_t* __restrict__ wpack, int n_out, int C, int stages, int total) {
+  const int t = blockIdx.x * blockDim.x + threadIdx.x;
+  if (t >= total) return;
+  const int lane = t & 63, lg = lane >> 4, lr = lane & 15;
+  const int s = (t >> 6) % stages, blk = (t >> 6) / stages;
+  uint32_t sw_word = 0;
+#pragma unroll
+  for (int rt = 0; rt < 4; ++rt) {
+    const int n = blk * 64 + fo(rt, lr);
+    const uint4 c = *(const uint4*)(codes + (size_t)n * (C / 2) + 64 * s + 16 * lg);
+    *(uint4*)(wpack + (((size_t)blk * stages + s) * 4 + rt) * 1024 + lane * 16) = c;
+    sw_word |= (uint32_t)scales[(size_t)n * (C / 32) + 4 * s + lg] << (8 * rt);
+  }
+  *(uint32_t*)(wpack + (size_t)n_out * (C / 2) + (((size_t)blk * stages + s) * 64 + lane) * 4) = sw_word;
+}
+
 bool aligned(const void* p, uintptr_t a) { return ((uintptr_t)p & (a - 1)) == 0; }
 
 bool overlap(const void* a, size_t an, const void* b, size_t bn) {
@@ -266,33 +295,70 @@ bool overlap(const void* a, size_t an, const void* b, size_t bn) {
   return x < y + bn && y < x + an;
 }
 
-}  // namespace
-
-extern "C" sva_status sva_qkv_proj_mxfp4(const sva_proj_desc* desc, const void* x, const void* codes,
-                                         const void* scales, const float* bias, void* q, void* k, void* v,
-                                         void* stream) {
+// Shape checks shared by both entry points.
+sva_status check_desc(const sva_proj_desc* desc) {
   if (!desc) return SVA_ERR_INVALID_ARG;
   const sva_proj_desc& d = *desc;
   if (d.B < 1 || d.N < 1 || d.C < 1 || d.H < 1 || d.d < 1) return SVA_ERR_INVALID_ARG;
-  // C: whole stages, and word-aligned rows of scale bytes (C / 32 a multiple of 4)
-  if (d.C % 128 != 0 || (d.H * d.d) % kTileN != 0 || d.d % 8 != 0) return SVA_ERR_UNSUPPORTED;
+  if (d.C % kTileK != 0 || (d.H * (long long)d.d) % 64 != 0 || d.d % 8 != 0) return SVA_ERR_UNSUPPORTED;
   const long long M = (long long)d.B * d.N;
   const long long Mt = (M + kTileM - 1) / kTileM;
-  const long long Nt = 3LL * d.H * d.d / kTileN;
-  const long long grid = (Mt + 7) / 8 * 8 * Nt;
-  if (M >= (1LL << 31) || (long long)kTileM * d.C * 2 >= (1LL << 31) || grid >= (1LL << 31))
+  const long long Nt = (3LL * d.H * d.d + kTileN - 1) / kTileN;
+  if (M >= (1LL << 31) || (long long)kTileM * d.C * 2 >= (1LL << 31) || (Mt + 7) / 8 * 8 * Nt >= (1LL << 31) ||
+      3LL * d.H * d.d * d.C >= (1LL << 31))
     return SVA_ERR_UNSUPPORTED;
-  if (!x || !codes || !scales || !q || !k || !v) return SVA_ERR_INVALID_ARG;
-  if (!aligned(x, 16) || !aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(codes, 8) ||
-      !aligned(scales, 4) || (bias && !aligned(bias, 16)))
+  return SVA_OK;
+}
+
+size_t packed_bytes(const sva_proj_desc& d) {
+  const size_t n_out = 3 * (size_t)d.H * d.d;
+  return n_out * d.C / 2 + n_out * d.C / 32;
+}
+
+}  // namespace
+
+extern "C" sva_status sva_mxfp4_pack_weights(const sva_proj_desc* desc, const void* codes, const void* scales,
+                                             void* wpack, void* stream) {
+  const sva_status st = check_desc(desc);
+  if (st != SVA_OK) return st;
+  const sva_proj_desc& d = *desc;
+  if (!codes || !scales || !wpack) return SVA_ERR_INVALID_ARG;
+  if (!aligned(codes, 16) || !aligned(wpack, 16)) return SVA_ERR_INVALID_ARG;
+  const int n_out = 3 * d.H * d.d;
+  const size_t cb = (size_t)n_out * d.C / 2, sb = (size_t)n_out * d.C / 32, pb = packed_bytes(d);
+  if (overlap(wpack, pb, codes, cb) || overlap(wpack, pb, scales, sb)) return SVA_ERR_INVALID_ARG;
+  const int stages = d.C / kTileK;
+  const int total = n_out / 64 * stages * 64;
+  const uint8_t* cp = (const uint8_t*)codes;
+  const uint8_t* sp = (const uint8_t*)scales;
+  uint8_t* wp = (uint8_t*)wpack;
+  int C = d.C;
+  int n = n_out;
+  void* args[] = {(void*)&cp, (void*)&sp, (void*)&wp, &n, &C, (void*)&stages, (void*)&total};
+  if (hipLaunchKernel((const void*)&sva_mxfp4_pack_kernel, dim3((unsigned)((total + 255) / 256)), dim3(256), args,
+                      0, (hipStream_t)stream) != hipSuccess)
+    return SVA_ERR_HIP;
+  return SVA_OK;
+}
+
+extern "C" sva_status sva_qkv_proj_mxfp4(const sva_proj_desc* desc, const void* x, const void* wpack,
+                                         const float* bias, void* q, void* k, void* v, void* stream) {
+  const sva_status st = check_desc(desc);
+  if (st != SVA_OK) return st;
+  const sva_proj_desc& d = *desc;
+  if (!x || !wpack || !q || !k || !v) return SVA_ERR_INVALID_ARG;
+  if (!aligned(x, 16) || !aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(wpack, 16) ||
+      (bias && !aligned(bias, 16)))
     return SVA_ERR_INVALID_ARG;
-  const size_t xb = (size_t)M * d.C * 2, ob = (size_t)M * d.H * d.d * 2;
-  const size_t cb = 3 * (size_t)d.H * d.d * d.C / 2, sb = 3 * (size_t)d.H * d.d * d.C / 32;
+  const long long M = (long long)d.B * d.N;
+  const long long Mt = (M + kTileM - 1) / kTileM;
+  const long long Nt = (3LL * d.H * d.d + kTileN - 1) / kTileN;
+  const long long grid = (Mt + 7) / 8 * 8 * Nt;
+  const size_t xb = (size_t)M * d.C * 2, ob = (size_t)M * d.H * d.d * 2, pb = packed_bytes(d);
   const size_t bb = 3 * (size_t)d.H * d.d * 4;
   void* outs[3] = {q, k, v};
   for (int i = 0; i < 3; ++i) {
-    if (overlap(outs[i], ob, x, xb) || overlap(outs[i], ob, codes, cb) || overlap(outs[i], ob, scales, sb) ||
-        (bias && overlap(outs[i], ob, bias, bb)))
+    if (overlap(outs[i], ob, x, xb) || overlap(outs[i], ob, wpack, pb) || (bias && overlap(outs[i], ob, bias, bb)))
       return SVA_ERR_INVALID_ARG;
     for (int j = 0; j < i; ++j)
       if (overlap(outs[i], ob, outs[j], ob)) return SVA_ERR_INVALID_ARG;
@@ -303,12 +369,12 @@ extern "C" sva_status sva_qkv_proj_mxfp4(const sva_proj_desc* desc, const void* 
   g.C = d.C;
   g.H = d.H;
   g.d = d.d;
+  g.n_out = 3 * d.H * d.d;
   g.Mt = (int)Mt;
   g.Nt = (int)Nt;
   g.stages = d.C / kTileK;
-  const uint8_t* cp = (const uint8_t*)codes;
-  const uint8_t* sp = (const uint8_t*)scales;
-  void* args[] = {(void*)&x, (void*)&cp, (void*)&sp, (void*)&bias, (void*)&q, (void*)&k, (void*)&v, &g};
+  const uint8_t* wp = (const uint8_t*)wpack;
+  void* args[] = {(void*)&x, (void*)&wp, (void*)&bias, (void*)&q, (void*)&k, (void*)&v, &g};
   if (hipLaunchKernel((const void*)&sva_qkv_proj_kernel, dim3((unsigned)grid), dim3(kPjThreads), args, 0,
                       (hipStream_t)stream) != hipSuccess)
     return SVA_ERR_HIP;

@@ -74,7 +74,8 @@ _SIG = {
     "sva_tconv_fwd": (ctypes.c_int, [ctypes.POINTER(SvaTconvDesc)] + [_VP] * 7),
     "sva_tconv_apply": (ctypes.c_int, [ctypes.POINTER(SvaTconvDesc)] + [_VP] * 6),
     "sva_tconv_commit": (ctypes.c_int, [ctypes.POINTER(SvaTconvDesc)] + [_VP] * 3),
-    "sva_qkv_proj_mxfp4": (ctypes.c_int, [ctypes.POINTER(SvaProjDesc)] + [_VP] * 8),
+    "sva_mxfp4_pack_weights": (ctypes.c_int, [ctypes.POINTER(SvaProjDesc)] + [_VP] * 4),
+    "sva_qkv_proj_mxfp4": (ctypes.c_int, [ctypes.POINTER(SvaProjDesc)] + [_VP] * 7),
 }
 
 
@@ -322,9 +323,28 @@ def sva_tconv_commit(cache, x, *, stream=None):
 
 # QKV projection with MXFP4 weights (include/sva_proj.h).
 
-def sva_qkv_proj_mxfp4(x, codes, scales, bias, H: int, d: int, *, q=None, k=None, v=None, stream=None):
-    """x [B, N, C] bf16; codes [3 H d, C / 2] uint8 (two 4-bit codes a byte,
-    low nibble first); scales [3 H d, C / 32] uint8 (E8M0); bias [3 H d]
+def mxfp4_packed_bytes(n_out: int, C: int) -> int:
+    """Size of the packed weights: that of the codes plus the scales."""
+    return n_out * C // 2 + n_out * C // 32
+
+
+def sva_mxfp4_pack_weights(codes, scales, H: int, d: int, *, out=None, stream=None):
+    """codes [3 H d, C / 2] uint8 (two 4-bit codes a byte, low nibble first),
+    scales [3 H d, C / 32] uint8 (E8M0) -> the packed weights (uint8 tensor)
+    that sva_qkv_proj_mxfp4 takes.  Weights are constant: pack them once."""
+    import torch
+    n_out, half = codes.shape
+    C = 2 * half
+    if out is None:
+        out = torch.empty((mxfp4_packed_bytes(n_out, C),), dtype=torch.uint8, device=codes.device)
+    desc = SvaProjDesc(1, 1, C, H, d)
+    st = lib().sva_mxfp4_pack_weights(ctypes.byref(desc), _ptr(codes), _ptr(scales), _ptr(out), _stream(stream))
+    _check(st, "sva_mxfp4_pack_weights")
+    return out
+
+
+def sva_qkv_proj_mxfp4(x, wpack, bias, H: int, d: int, *, q=None, k=None, v=None, stream=None):
+    """x [B, N, C] bf16; wpack from sva_mxfp4_pack_weights; bias [3 H d]
     fp32 or None.  Returns (q, k, v), each [B, H, N, d] bf16."""
     import torch
     if x.dim() != 3 or x.dtype != torch.bfloat16:
@@ -334,7 +354,7 @@ def sva_qkv_proj_mxfp4(x, codes, scales, bias, H: int, d: int, *, q=None, k=None
     outs = []
     for t in (q, k, v):
         outs.append(torch.empty((B, H, N, d), dtype=torch.bfloat16, device=x.device) if t is None else t)
-    st = lib().sva_qkv_proj_mxfp4(ctypes.byref(desc), _ptr(x), _ptr(codes), _ptr(scales), _ptr(bias),
+    st = lib().sva_qkv_proj_mxfp4(ctypes.byref(desc), _ptr(x), _ptr(wpack), _ptr(bias),
                                   _ptr(outs[0]), _ptr(outs[1]), _ptr(outs[2]), _stream(stream))
     _check(st, "sva_qkv_proj_mxfp4")
     return tuple(outs)

@@ -28,14 +28,23 @@
  *   codes   [3*H*d, C/2] bytes: output row n holds the codes of input
  *           channels 2j (low nibble) and 2j+1 (high nibble) in byte j
  *   scales  [3*H*d, C/32] bytes (E8M0), one per 32 input channels
+ *   wpack   the same codes and scales reordered by sva_mxfp4_pack_weights
+ *           for the projection's loads; 3*H*d*C/2 + 3*H*d*C/32 bytes (the
+ *           size of codes plus scales).  With P = 3*H*d/64 blocks of 64
+ *           output rows and S = C/128 stages of 128 channels:
+ *             codes part, [P][S][4][64] x 16 bytes: entry (p, s, t, l) holds
+ *               channels 128 s + 32 (l / 16) .. + 31 of row 64 p + r(t, l % 16);
+ *             scales part (after it), [P][S][64] words: byte t of word
+ *               (p, s, l) is the scale of the same block;
+ *             r(t, i) = 32 (t / 2) + 8 (i / 4) + 4 (t % 2) + i % 4.
  *   bias    [3*H*d] fp32, or NULL
  *   q, k, v [B, H, N, d] bf16, the layout sva_lin_attn_* take
- * Limits: C a multiple of 128; H*d a multiple of 128; d a multiple of 8.
+ * Limits: C a multiple of 128; H*d a multiple of 64; d a multiple of 8.
  *
  * Ownership and errors as in sva.h: caller-owned device pointers (x, q, k,
- * v 16-byte aligned; codes 8-byte and scales 4-byte aligned), nothing
- * allocated or kept, synchronous validation before any launch (nothing
- * written on error), work queued on `stream`.  No workspace is needed.
+ * v, codes and wpack 16-byte aligned), nothing allocated or kept,
+ * synchronous validation before any launch (nothing written on error), work
+ * queued on `stream`.  No workspace is needed.
  */
 #ifndef SVA_PROJ_H
 #define SVA_PROJ_H
@@ -54,12 +63,18 @@ typedef struct sva_proj_desc {
   int d;  /* head dimension */
 } sva_proj_desc;
 
-/* q, k, v = split(x W + bias) as above.  q, k, v must not overlap each
- * other or any input.  SVA_ERR_UNSUPPORTED for C, H*d or d outside the
- * limits; SVA_ERR_INVALID_ARG for a bad shape, pointer or overlap. */
-sva_status sva_qkv_proj_mxfp4(const sva_proj_desc* desc, const void* x, const void* codes,
-                              const void* scales, const float* bias, void* q, void* k, void* v,
-                              void* stream);
+/* wpack = the packed form of (codes, scales), as above.  Weights are
+ * constant across calls: pack them once.  wpack must not overlap codes or
+ * scales.  SVA_ERR_UNSUPPORTED / SVA_ERR_INVALID_ARG as for the projection. */
+sva_status sva_mxfp4_pack_weights(const sva_proj_desc* desc, const void* codes, const void* scales, void* wpack,
+                                  void* stream);
+
+/* q, k, v = split(x W + bias) as above, W given packed.  q, k, v must not
+ * overlap each other or any input.  SVA_ERR_UNSUPPORTED for C, H*d or d
+ * outside the limits; SVA_ERR_INVALID_ARG for a bad shape, pointer or
+ * overlap. */
+sva_status sva_qkv_proj_mxfp4(const sva_proj_desc* desc, const void* x, const void* wpack, const float* bias,
+                              void* q, void* k, void* v, void* stream);
 
 #ifdef __cplusplus
 }

@@ -272,7 +272,7 @@ def test_tconv_pointer_checks_happen_before_launch():
 def test_proj_checks_happen_before_launch():
     lib = sva.lib()
     inv, uns = sva.SVA_ERR_INVALID_ARG, sva.SVA_ERR_UNSUPPORTED
-    X, C, S, Q, K, V = 1 << 30, 1 << 20, 1 << 21, 1 << 34, 1 << 35, 1 << 36
+    X, W, Q, K, V = 1 << 30, 1 << 20, 1 << 34, 1 << 35, 1 << 36
 
     def call(**kw):
         base = dict(B=1, N=75600, C=1024, H=16, d=64)
@@ -280,17 +280,42 @@ def test_proj_checks_happen_before_launch():
         dsc = sva.SvaProjDesc(base["B"], base["N"], base["C"], base["H"], base["d"])
         return lambda *p: lib.sva_qkv_proj_mxfp4(ctypes.byref(dsc), *p, None)
 
-    assert call(C=96)(X, C, S, None, Q, K, V) == uns        # C not a multiple of 128
-    assert call(C=192)(X, C, S, None, Q, K, V) == uns
-    assert call(H=3)(X, C, S, None, Q, K, V) == uns         # H d not a multiple of 128
-    assert call(d=36, H=32)(X, C, S, None, Q, K, V) == uns  # d not a multiple of 8
-    assert call(N=0)(X, C, S, None, Q, K, V) == inv
+    assert call(C=96)(X, W, None, Q, K, V) == uns        # C not a multiple of 128
+    assert call(C=192)(X, W, None, Q, K, V) == uns
+    assert call(H=1, d=32)(X, W, None, Q, K, V) == uns   # H d not a multiple of 64
+    assert call(d=36, H=32)(X, W, None, Q, K, V) == uns  # d not a multiple of 8
+    assert call(N=0)(X, W, None, Q, K, V) == inv
     ok = call()
-    assert ok(None, C, S, None, Q, K, V) == inv            # null x
-    assert ok(X, C, S, None, Q, None, V) == inv            # null k
-    assert ok(X + 8, C, S, None, Q, K, V) == inv           # misaligned x
-    assert ok(X, C + 4, S, None, Q, K, V) == inv           # misaligned codes
-    assert ok(X, C, S + 2, None, Q, K, V) == inv           # misaligned scales
-    assert ok(X, C, S, 8, Q, K, V) == inv                  # misaligned bias
-    assert ok(X, C, S, None, X + 4096, K, V) == inv        # q over x
-    assert ok(X, C, S, None, Q, Q + 4096, V) == inv        # k over q
+    assert ok(None, W, None, Q, K, V) == inv            # null x
+    assert ok(X, None, None, Q, K, V) == inv            # null weights
+    assert ok(X, W, None, Q, None, V) == inv            # null k
+    assert ok(X + 8, W, None, Q, K, V) == inv           # misaligned x
+    assert ok(X, W + 8, None, Q, K, V) == inv           # misaligned weights
+    assert ok(X, W, 8, Q, K, V) == inv                  # misaligned bias
+    assert ok(X, W, None, X + 4096, K, V) == inv        # q over x
+    assert ok(X, W, None, W + 4096, K, V) == inv        # q over the weights
+    assert ok(X, W, None, Q, Q + 4096, V) == inv        # k over q
+
+
+@fake_pointers
+def test_pack_checks_happen_before_launch():
+    lib = sva.lib()
+    inv, uns = sva.SVA_ERR_INVALID_ARG, sva.SVA_ERR_UNSUPPORTED
+    Cd, S, P = 1 << 30, 1 << 31, 1 << 32
+
+    def call(**kw):
+        base = dict(B=1, N=1, C=1024, H=16, d=64)
+        base.update(kw)
+        dsc = sva.SvaProjDesc(base["B"], base["N"], base["C"], base["H"], base["d"])
+        return lambda *p: lib.sva_mxfp4_pack_weights(ctypes.byref(dsc), *p, None)
+
+    assert call(C=64)(Cd, S, P) == uns                   # C not a multiple of 128
+    assert call(H=1, d=32)(Cd, S, P) == uns              # H d not a multiple of 64
+    ok = call()
+    assert ok(None, S, P) == inv
+    assert ok(Cd, None, P) == inv
+    assert ok(Cd, S, None) == inv
+    assert ok(Cd + 4, S, P) == inv                       # misaligned codes
+    assert ok(Cd, S, P + 8) == inv                       # misaligned output
+    assert ok(Cd, S, Cd + 4096) == inv                   # output over the codes
+    assert ok(Cd, S, S - 4096) == inv                    # output over the scales

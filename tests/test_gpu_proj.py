@@ -3,9 +3,10 @@ against the fp64 oracle (oracle/proj_oracle.py) on identical seeded inputs.
 
 Bar: max|gpu - oracle| / max|oracle| <= 1e-2 per output tensor (bf16
 inputs and outputs; the weights decode exactly and the products accumulate
-in fp32, so the bf16 output rounding dominates).  Small cases cover a ragged
-last token tile, sample boundaries inside a tile, several channel
-stages, d = 32 and 64, no bias, and extreme E8M0 scales (denormal weights,
+in fp32, so the bf16 output rounding dominates).  The weights go through
+sva_mxfp4_pack_weights first.  Small cases cover a ragged last token tile,
+sample boundaries inside a tile, several channel stages, partial feature
+tiles, d = 32 and 64, no bias, and extreme E8M0 scales (denormal weights,
 and weights up to 6 * 2^125); the 720p-sized projection runs in full and is
 compared on sampled tokens.
 """
@@ -32,15 +33,20 @@ def _weights(n_out, C, seed, lo=120, hi=125):
     codes, scales = wl.mxfp4_weights(n_out, C, seed)
     if (lo, hi) != (120, 125):
         scales = np.random.default_rng(seed + 7).integers(lo, hi, scales.shape, dtype=np.uint8)
-    return codes, scales, (torch.from_numpy(wl.pack_nibbles(codes)).to(DEV), torch.from_numpy(scales).to(DEV))
+    cd = torch.from_numpy(wl.pack_nibbles(codes)).to(DEV)
+    sd = torch.from_numpy(scales).to(DEV)
+    return codes, scales, cd, sd
 
 
-# (name, B, N, C, H, d, bias)
+# (name, B, N, C, H, d, bias): ragged token tiles, partial feature tiles
+# (3 H d = 192, 384, 576), sample boundaries inside a tile, 1 to 3 stages.
 CASES = [
     ("ragged_tile", 1, 100, 128, 2, 64, True),
     ("samples_in_tile", 2, 300, 128, 4, 32, True),
-    ("six_stages", 1, 513, 384, 2, 64, False),
+    ("three_stages", 1, 513, 384, 2, 64, False),
     ("several_tiles", 3, 700, 256, 8, 32, True),
+    ("one_block_rows", 2, 130, 256, 1, 64, True),
+    ("three_blocks", 1, 257, 128, 3, 64, True),
 ]
 
 
@@ -50,12 +56,13 @@ def test_proj_small(case):
     _say(f"proj_small {name}")
     xv, xraw = wl.draw((B, N, C), 201, 1.0, "bf16")
     xd = to_device(xraw, "bf16")
-    codes, scales, (cd, sd) = _weights(3 * H * d, C, 202)
+    codes, scales, cd, sd = _weights(3 * H * d, C, 202)
+    wp = sva.sva_mxfp4_pack_weights(cd, sd, H, d)
     bias = bd = None
     if with_bias:
         bias = wl.draw((3 * H * d,), 203, 0.1, "f32")[0]
         bd = torch.from_numpy(bias).to(DEV)
-    q, k, v = sva.sva_qkv_proj_mxfp4(xd, cd, sd, bd, H, d)
+    q, k, v = sva.sva_qkv_proj_mxfp4(xd, wp, bd, H, d)
     torch.cuda.synchronize()
     ref = orc.qkv_project(xv, codes, scales, bias, H, d)
     errs = [relerr(g_, r_) for g_, r_ in zip((q, k, v), ref)]
@@ -72,9 +79,10 @@ def test_proj_extreme_scales(lo, hi, x_scale):
     and sum stays in range, and the weights decode exactly."""
     B, N, C, H, d = 1, 64, 128, 2, 64
     _say(f"proj extreme scales {lo}..{hi - 1}")
-    codes, scales, (cd, sd) = _weights(3 * H * d, C, 211, lo, hi)
+    codes, scales, cd, sd = _weights(3 * H * d, C, 211, lo, hi)
+    wp = sva.sva_mxfp4_pack_weights(cd, sd, H, d)
     xv, xraw = wl.draw((B, N, C), 213, x_scale, "bf16")
-    q, k, v = sva.sva_qkv_proj_mxfp4(to_device(xraw, "bf16"), cd, sd, None, H, d)
+    q, k, v = sva.sva_qkv_proj_mxfp4(to_device(xraw, "bf16"), wp, None, H, d)
     torch.cuda.synchronize()
     ref = orc.qkv_project(xv, codes, scales, None, H, d)
     for g_, r_ in zip((q, k, v), ref):
@@ -97,8 +105,9 @@ def test_proj_720p_sampled_tokens():
     codes, scales = wl.mxfp4_weights(w.n_out, w.C, wl.seed_for(w.name, "w", 0, 0))
     bias = wl.draw((w.n_out,), wl.seed_for(w.name, "bias", 0, 0), 0.1, "f32")[0]
     _say("proj 720p: running")
-    q, k, v = sva.sva_qkv_proj_mxfp4(xd, torch.from_numpy(wl.pack_nibbles(codes)).to(DEV),
-                                     torch.from_numpy(scales).to(DEV), torch.from_numpy(bias).to(DEV), w.H, w.d)
+    wp = sva.sva_mxfp4_pack_weights(torch.from_numpy(wl.pack_nibbles(codes)).to(DEV),
+                                    torch.from_numpy(scales).to(DEV), w.H, w.d)
+    q, k, v = sva.sva_qkv_proj_mxfp4(xd, wp, torch.from_numpy(bias).to(DEV), w.H, w.d)
     torch.cuda.synchronize()
     toks = np.random.default_rng(5).choice(w.N, 96, replace=False)
     toks.sort()
