@@ -9,11 +9,13 @@
 // v_mfma_f32_16x16x32_bf16: the A operand is a 16-feature slice of the
 // decoded weights, the B operand 16 tokens, so a lane's accumulators hold
 // consecutive output features of one token and the epilogue writes 16-byte
-// pieces of the [B, H, N, d] rows directly.  A workgroup (8 waves) owns 256
-// output features x 128 tokens; a wave 64 features x 64 tokens (4 x 4
-// accumulators).  The input channels advance 128 per stage.
+// pieces of the [B, H, N, d] rows directly.  A workgroup (4 waves) owns 256
+// output features x 64 tokens; a wave 64 features x 64 tokens (4 x 4
+// accumulators).  Two workgroups share a CU (198 registers a lane), so one's
+// epilogue overlaps the other's MFMAs (8-wave workgroups of 256 x 128, one
+// per CU, took 7% longer).  The input channels advance 128 per stage.
 //
-// Only x goes through LDS (128 x 128 bf16 a stage, double-buffered, the
+// Only x goes through LDS (64 x 128 bf16 a stage, double-buffered, the
 // stage after next in registers).  Each wave loads its own weights straight
 // from global memory into registers, one stage ahead, in the packed layout
 // sva_mxfp4_pack_weights writes (4 KiB of codes and 256 bytes of scales per
@@ -25,7 +27,12 @@
 // from global memory, stalled the texture path on 16 rows per load.
 // Consecutive workgroup indices go to the eight XCDs in turn, so the tiles
 // are ordered to keep every workgroup that reads one x tile on the same XCD
-// (its L2 then serves the 12 output tiles of a 720p QKV projection).
+// (its L2 then serves the 12 output tiles of a 720p QKV projection; x is
+// fetched from HBM once).  Outputs are stored non-temporally: written
+// through the L2 like the x tiles, they cost 8% more time.  A persistent
+// version (a grid of resident workgroups, the stages of consecutive tiles in
+// one pipeline, outputs leaving through LDS one piece per stage) was no
+// faster.
 
 #include <hip/hip_runtime.h>
 #include <stdint.h>
@@ -40,9 +47,9 @@ typedef uint32_t pj_u32x4 __attribute__((ext_vector_type(4)));
 typedef __bf16 pj_bf16x8 __attribute__((ext_vector_type(8)));
 typedef __bf16 pj_bf16x2 __attribute__((ext_vector_type(2)));
 
-constexpr int kPjThreads = 512;  // 8 waves
+constexpr int kPjThreads = 256;  // 4 waves
 constexpr int kTileN = 256;      // output features per workgroup
-constexpr int kTileM = 128;      // tokens per workgroup
+constexpr int kTileM = 64;       // tokens per workgroup
 constexpr int kTileK = 128;      // input channels per stage
 constexpr int kPieces = kTileK * 2 / 16;        // 16-byte pieces of an x row per stage
 constexpr int kXU4 = kTileM * kPieces;          // x tile, 16-byte units
@@ -110,7 +117,7 @@ __device__ __forceinline__ uint32_t pack2(float a, float b) {
   return __builtin_bit_cast(uint32_t, v);
 }
 
-__global__ __launch_bounds__(kPjThreads, 1) void sva_qkv_proj_kernel(
+__global__ __launch_bounds__(kPjThreads, 2) void sva_qkv_proj_kernel(
     const void* __restrict__ xp, const uint8_t* __restrict__ wpack, const float* __restrict__ bias,
     void* __restrict__ qp, void* __restrict__ kp, void* __restrict__ vp, ProjGeo g) {
   __shared__ uint4 xs[2][kXU4];
@@ -128,9 +135,9 @@ __global__ __launch_bounds__(kPjThreads, 1) void sva_qkv_proj_kernel(
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int lane = tid & 63;
   const int lg = lane >> 4, lr = lane & 15;
-  const int wn = wave & 3, wm = wave >> 2;  // 64 features x 64 tokens each
+  const int wn = wave & 3, wm = wave >> 2;  // 64 features x 64 tokens each (wm = 0)
 
-  // x rows m0 .. m0 + 127 (rows past M read as zeros)
+  // x rows m0 .. m0 + 63 (rows past M read as zeros)
   const int rows = min(kTileM, g.M - m0);
   const size_t row_bytes = (size_t)g.C * 2;
   const __amdgpu_buffer_rsrc_t xr = rsrc((const char*)xp + (size_t)m0 * row_bytes, (uint32_t)(rows * row_bytes));
@@ -261,7 +268,8 @@ __global__ __launch_bounds__(kPjThreads, 1) void sva_qkv_proj_kernel(
         const pj_floatx4 lo = acc[2 * run][tt], hi = acc[2 * run + 1][tt];
         const uint4 v = make_uint4(pack2(lo[0] + bb[0], lo[1] + bb[1]), pack2(lo[2] + bb[2], lo[3] + bb[3]),
                                    pack2(hi[0] + bb[4], hi[1] + bb[5]), pack2(hi[2] + bb[6], hi[3] + bb[7]));
-        *(uint4*)(dst + ((((size_t)b * g.H + h) * g.N + t) * g.d + fd) * 2) = v;
+        __builtin_nontemporal_store(__builtin_bit_cast(pj_u32x4, v),
+                                    (pj_u32x4*)(dst + ((((size_t)b * g.H + h) * g.N + t) * g.d + fd) * 2));
       }
     }
   }
