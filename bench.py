@@ -229,6 +229,52 @@ def cached_leg(w, steps: int, warmup: int):
     return apply_ms, a.elapsed_time(b) / steps
 
 
+def stream_leg(w, reps: int, warmup: int):
+    """Block-by-block generation of the whole workload on one constant-size
+    cache: for each block c in order, sva_block_cache_apply (the block's
+    output against the blocks before it and itself) then
+    sva_block_cache_commit of its k, v.  Returns ms per full pass over all
+    blocks (the two tiny zero fills that reset the cache per pass included)."""
+    import torch
+    from block_causal_linear_phi_amd import sva
+
+    dev = torch.device("cuda:0")
+    fg = (w.F, w.Hs, w.Ws)
+    kw = dict(rope=w.rope, split=w.split, base=w.base)
+    bt = w.block_tokens
+    blocks = []
+    for t in ("q", "k", "v"):
+        full = upload(w, t)
+        blocks.append([full[:, :, c * bt:(c + 1) * bt].contiguous() for c in range(w.nb)])
+        del full
+    S = torch.zeros((w.B, w.H, w.d, w.d), dtype=torch.float32, device=dev)
+    z = torch.zeros((w.B, w.H, w.d), dtype=torch.float32, device=dev)
+    out = torch.empty_like(blocks[0][0])
+    desc = sva.make_desc(w.B, w.H, w.d, fg, w.F, t0=0, eps=w.eps,
+                         dtype=sva.SVA_BF16 if w.dtype == "bf16" else sva.SVA_F32, **kw)
+    ws = torch.zeros(sva.sva_block_cache_workspace(desc), dtype=torch.uint8, device=dev)
+    stream = torch.cuda.current_stream()
+
+    def one_pass():
+        S.zero_()
+        z.zero_()
+        for c in range(w.nb):
+            q, k, v = blocks[0][c], blocks[1][c], blocks[2][c]
+            sva.sva_block_cache_apply(S, z, q, k, v, fg, t0=c * w.F, eps=w.eps, out=out, ws=ws, stream=stream, **kw)
+            sva.sva_block_cache_commit(S, z, k, v, fg, t0=c * w.F, ws=ws, stream=stream, **kw)
+
+    for _ in range(warmup):
+        one_pass()
+    torch.cuda.synchronize()
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    a.record(stream)
+    for _ in range(reps):
+        one_pass()
+    b.record(stream)
+    torch.cuda.synchronize()
+    return a.elapsed_time(b) / reps
+
+
 def tconv_leg(w, steps: int, warmup: int, sets: int, streaming: bool = True):
     """The causal temporal convolution (sva_tconv_fwd) over all blocks of the
     workload's activations, `sets` input/output buffer sets alternating;
@@ -415,7 +461,7 @@ def cpu_leg(w, reps: int):
 def _short_kernel(name: str) -> str:
     for k in ("sva_reduce_kernel", "sva_scan_kernel", "sva_apply_kernel", "sva_prep_kernel",
               "sva_bwd_out_kernel", "sva_bwd_kv_kernel", "sva_tconv_kernel", "sva_tconv_commit_kernel",
-              "sva_qkv_proj_kernel"):
+              "sva_qkv_proj_kernel", "sva_mxfp4_pack_kernel"):
         if k in name:
             short = k.replace("sva_", "").replace("_kernel", "")
             if k == "sva_tconv_kernel" and "sva_tconv_commit_kernel" in name:
@@ -516,6 +562,8 @@ def main():
                     help="time the causal temporal convolution of the Mix-FFN on the workload's grid instead")
     ap.add_argument("--proj", action="store_true",
                     help="time the QKV projection with MXFP4 weights on the workload's tokens instead")
+    ap.add_argument("--stream", action="store_true",
+                    help="block-by-block generation on one cache (apply + commit per block); --steps passes")
     ap.add_argument("--no-streaming", action="store_true",
                     help="with --tconv: time the one-shot call only (profiling runs)")
     ap.add_argument("--copy-calib", type=int, default=0, metavar="MIB",
@@ -624,6 +672,26 @@ def main():
             "hbm_frac_step": 8 * tensor / (ms * 1e-3) / (HBM_PEAK_GBS * 1e9),
             "states": "saved by the forward (sva_lin_attn_fwd_save)",
             "ms_per_step_recomputing_states": ms_recompute,
+        }), flush=True)
+        return
+    if args.stream:
+        ms = stream_leg(w, args.steps, args.warmup)
+        esz = 2 if w.dtype == "bf16" else 4
+        tensor = w.B * w.H * w.N * w.d * esz
+        cache = w.B * w.H * (w.d * w.d + w.d) * 4
+        # apply reads q, k, v and the cache and writes out; commit reads k, v
+        # and updates the cache: 6 tensor passes and 3 cache passes a block
+        alg = 6 * tensor + 3 * cache * w.nb
+        print(json.dumps({
+            "metric": "tokens/s (all heads) of block-by-block generation on one cache (apply + commit per block)",
+            "value": w.B * w.N / (ms * 1e-3), "unit": "tokens/s", "n_gpus": 1, "steps": args.steps,
+            "warmup": args.warmup, "ms_per_step": ms, "higher_is_better": True, "scaling": "weak",
+            "vs_baseline": None, "dtype": "bf16" if w.dtype == "bf16" else "f32", "data": data_note,
+            "config": {"workload": f"{w.name} streamed: B={w.B} H={w.H} d={w.d} grid {w.T}x{w.Hs}x{w.Ws} "
+                                   f"({w.N} tokens) as {w.nb} blocks of {w.F} frames, one {cache}-byte cache",
+                       "B": w.B, "H": w.H, "d": w.d, "tokens": w.N, "blocks": w.nb},
+            "us_per_block": ms * 1e3 / w.nb,
+            "alg_bytes": alg, "hbm_frac_step": alg / (ms * 1e-3) / (HBM_PEAK_GBS * 1e9),
         }), flush=True)
         return
     if w.prior_blocks:
