@@ -82,6 +82,19 @@ def test_streaming_equals_one_shot(dtype):
         assert relerr(o, one[:, :, sl].float().cpu().numpy().astype(np.float64)) <= tol
     assert relerr(S, S_ref.cpu().numpy().astype(np.float64)) <= 1e-5
     assert relerr(z, z_ref.cpu().numpy().astype(np.float64)) <= 1e-5
+    # The last denoising step of a block can output and commit in one call: a
+    # one-block forward with the cache as both S0 and S_out.
+    S2 = torch.zeros_like(S)
+    z2 = torch.zeros_like(z)
+    for c in range(nblk):
+        sl = slice(c * Nb, (c + 1) * Nb)
+        qb, kb, vb = (x[:, :, sl].contiguous() for x in (qd, kd, vd))
+        o = sva.sva_lin_attn_fwd(qb, kb, vb, (F, Hs, Ws), F, t0=c * F, rope=True, split=split, S0=S2, z0=z2,
+                                 S_out=S2, z_out=z2)
+        torch.cuda.synchronize()
+        assert relerr(o, one[:, :, sl].float().cpu().numpy().astype(np.float64)) <= tol
+    assert relerr(S2, S_ref.cpu().numpy().astype(np.float64)) <= 1e-5
+    assert relerr(z2, z_ref.cpu().numpy().astype(np.float64)) <= 1e-5
 
 
 def test_v_ones_gives_one_without_rope():
