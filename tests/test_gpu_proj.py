@@ -117,3 +117,37 @@ def test_proj_720p_sampled_tokens():
     errs = [relerr(g_[:, :, idx], r_) for g_, r_ in zip((q, k, v), ref)]
     _say(f"  errs {errs}")
     assert max(errs) <= TOL["bf16"]
+
+
+def test_pack_layout_matches_header():
+    """sva_mxfp4_pack_weights writes the layout include/sva_proj.h spells
+    out: with P = 3 H d / 64 row blocks and S = C / 128 stages, codes entry
+    (p, s, t, l) = the 16 code bytes of channels 128 s + 32 (l / 16) .. + 31
+    of row 64 p + r(t, l % 16), then scale word (p, s, l) with byte t the
+    scale of that block; r(t, i) = 32 (t / 2) + 8 (i / 4) + 4 (t % 2) + i % 4.
+    The expected bytes are rebuilt here with numpy from that text."""
+    H, d, C = 2, 96, 384
+    n_out = 3 * H * d
+    _say("pack layout")
+    codes, scales, cd, sd = _weights(n_out, C, 221)
+    packed = sva.sva_mxfp4_pack_weights(cd, sd, H, d).cpu().numpy()
+    nib = wl.pack_nibbles(codes)  # [n_out, C / 2]
+    P, S = n_out // 64, C // 128
+    t = np.arange(4)[:, None]
+    i = np.arange(64)[None, :] % 16
+    rows = 32 * (t // 2) + 8 * (i // 4) + 4 * (t % 2) + i % 4  # [4, 64]
+    lg = np.arange(64) // 16
+    exp_c = np.empty((P, S, 4, 64, 16), np.uint8)
+    exp_s = np.empty((P, S, 64, 4), np.uint8)
+    for p in range(P):
+        for s in range(S):
+            for tt in range(4):
+                for l in range(64):
+                    n = 64 * p + rows[tt, l]
+                    ch0 = 128 * s + 32 * lg[l]
+                    exp_c[p, s, tt, l] = nib[n, ch0 // 2: ch0 // 2 + 16]
+                    exp_s[p, s, l, tt] = scales[n, ch0 // 32]
+    nc = n_out * C // 2
+    assert packed.shape == (nc + n_out * C // 32,)
+    assert np.array_equal(packed[:nc], exp_c.reshape(-1))
+    assert np.array_equal(packed[nc:], exp_s.reshape(-1))
