@@ -489,6 +489,58 @@ def _short_kernel(name: str) -> str:
     return name.split("(")[0][-60:]
 
 
+MFMA_COUNTERS = ("SQ_INSTS_MFMA", "SQ_INSTS_VALU_MFMA_MOPS_BF16", "SQ_INSTS_VALU_MFMA_MOPS_F32")
+
+
+def summarize_mfma(args):
+    """MFMA activity per kernel from one rocprofv3 --pmc pass of
+    MFMA_COUNTERS and a --kernel-trace pass of the same command: MFMA
+    instructions and flops per launch (MOPS x 512 flops), the achieved rate
+    over the kernel's average duration, and its fraction of the dense peak."""
+    import csv
+    import glob
+    from collections import defaultdict
+
+    def csvs(d, suffix):
+        return [f for f in glob.glob(os.path.join(d, "**", "*.csv"), recursive=True) if f.endswith(suffix)]
+
+    dur = defaultdict(list)
+    for r in csv.DictReader(open(csvs(args.trace_dir, "kernel_trace.csv")[0])):
+        if "sva_" in r["Kernel_Name"]:
+            dur[_short_kernel(r["Kernel_Name"])].append((int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3)
+    cnt = defaultdict(lambda: defaultdict(list))
+    for r in csv.DictReader(open(csvs(args.pmc_dir, "counter_collection.csv")[0])):
+        if "sva_" in r["Kernel_Name"]:
+            cnt[_short_kernel(r["Kernel_Name"])][r["Counter_Name"]].append(float(r["Counter_Value"]))
+    name = ("proj_" if args.proj else "") + args.workload + args.label
+    lines = [f"# MFMA activity per kernel, {name} workload", "",
+             "Commands (run from the repository root on one MI355X):", ""]
+    lines += [f"    {c}" for c in args.commands]
+    lines += ["", "Per launch (mean over the profiled launches). flops = SQ_INSTS_VALU_MFMA_MOPS_* x 512;",
+              "rate = flops / the kernel's mean duration in the trace pass; peak: 2.5 PFLOP/s bf16,",
+              "157.3 TFLOP/s fp32 (dense).", "",
+              "| kernel | mean us | MFMA instructions | bf16 GFLOP | fp32 GFLOP | TFLOP/s | % of peak |",
+              "|---|---|---|---|---|---|---|"]
+    out = {}
+    for k in sorted(cnt):
+        c = {n: sum(v) / len(v) for n, v in cnt[k].items()}
+        us = sum(dur[k]) / len(dur[k]) if dur.get(k) else float("nan")
+        fb = c.get("SQ_INSTS_VALU_MFMA_MOPS_BF16", 0.0) * 512
+        ff = c.get("SQ_INSTS_VALU_MFMA_MOPS_F32", 0.0) * 512
+        rate = (fb + ff) / (us * 1e-6) / 1e12 if us == us and us > 0 else float("nan")
+        peak = MFMA_BF16_PEAK_TFLOPS if fb >= ff else 157.3
+        out[k] = {"us": us, "mfma_insts": c.get("SQ_INSTS_MFMA"), "bf16_flops": fb, "f32_flops": ff,
+                  "tflops": rate, "frac_of_peak": rate / peak}
+        lines.append(f"| {k} | {us:.2f} | {c.get('SQ_INSTS_MFMA', 0):.4g} | {fb / 1e9:.2f} | {ff / 1e9:.2f} | "
+                     f"{rate:.1f} | {100 * rate / peak:.1f} |")
+    src = PROJ_SRC if args.proj else KERNEL_SRC
+    lines += ["", f"Kernel source sha256: `{source_sha256(src)}`", ""]
+    os.makedirs(PROFILES, exist_ok=True)
+    with open(os.path.join(PROFILES, f"sva_mfma_{name}.md"), "w") as f:
+        f.write("\n".join(lines))
+    print(json.dumps({"summarized_mfma": name, "per_launch": out}))
+
+
 def summarize_profile(args):
     """Turn rocprofv3 CSV output into the committed summaries: a kernel-time
     table and per-launch HBM traffic (FETCH_SIZE / WRITE_SIZE scaled by what
@@ -584,6 +636,9 @@ def main():
                     help="with --tconv: time the one-shot call only (profiling runs)")
     ap.add_argument("--copy-calib", type=int, default=0, metavar="MIB",
                     help="also run a plain fp32 streaming kernel over MIB MiB (counter calibration)")
+    ap.add_argument("--summarize-mfma", action="store_true",
+                    help="write profiles/sva_mfma_<workload>.md from --pmc-dir and --trace-dir")
+    ap.add_argument("--pmc-dir")
     ap.add_argument("--summarize-profile", action="store_true",
                     help="write profiles/ summaries from rocprofv3 output directories, then exit")
     ap.add_argument("--trace-dir")
@@ -595,6 +650,9 @@ def main():
     args = ap.parse_args()
     if args.summarize_profile:
         summarize_profile(args)
+        return
+    if args.summarize_mfma:
+        summarize_mfma(args)
         return
     if args.gpus != 1:
         print("bench.py measures one GPU: this build has no multi-GPU path (heads and samples shard "
