@@ -47,6 +47,8 @@ CASES = [
     ("several_tiles", 3, 700, 256, 8, 32, True),
     ("one_block_rows", 2, 130, 256, 1, 64, True),
     ("three_blocks", 1, 257, 128, 3, 64, True),
+    ("one_token", 1, 1, 128, 1, 64, True),
+    ("whole_tiles", 2, 128, 256, 4, 64, False),
 ]
 
 
