@@ -99,6 +99,10 @@ sva_status sva_lin_attn_fwd_workspace(const sva_desc* desc, size_t* bytes);
  *   S_out, z_out out: final cache (S_{nb-1}, Z_{nb-1}) fp32, or both NULL;
  *            may be the same buffers as S0, z0 (updated in place)
  *   ws, ws_bytes: caller-owned scratch of at least sva_lin_attn_fwd_workspace
+ * With one block (T == frames_per_block, t0 = its first frame) and the cache
+ * as both S0/z0 and S_out/z_out, one call gives the block's output and
+ * commits the block: sva_block_cache_apply then sva_block_cache_commit in a
+ * single pass over q, k, v (a block's last denoising step).
  */
 sva_status sva_lin_attn_fwd(const sva_desc* desc, const void* q, const void* k,
                             const void* v, void* out, const float* S0,
