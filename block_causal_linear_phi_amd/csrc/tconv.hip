@@ -144,7 +144,10 @@ __global__ __launch_bounds__(kTconvThreads) void sva_tconv_kernel(
   const uint4* xs = x + col;
   uint4* ys = y + col;
   const long long cidx = bp * g.CV + cv;
-  uint4 prev = cache_in ? cache_in[cidx] : zero;
+  // (A conditional expression over the two lvalues made the compiler select
+  // between their addresses and keep `zero` in scratch memory.)
+  uint4 prev = make_uint4(0u, 0u, 0u, 0u);
+  if (cache_in) prev = cache_in[cidx];
   uint4 cur = load_nt(xs);
   int in_block = 0;  // frame index inside its block
   // Output t from (prev, cur, next) = frames t-1, t, t+1; next is zero at a
