@@ -63,6 +63,25 @@ def test_fwd_small(case, dtype):
 
 
 @pytest.mark.parametrize("dtype", ["f32", "bf16"])
+@pytest.mark.parametrize("base,eps,t0", [(500.0, 1e-3, 0), (1e6, 1e-6, 0), (10000.0, 1e-6, 5000)],
+                         ids=["base500_eps1e-3", "base1e6", "t0_5000"])
+def test_fwd_other_base_eps_and_positions(base, eps, t0, dtype):
+    """Descriptor values other than the workloads': the RoPE base (angles
+    base^(-2i/d_a)), a larger eps, and large absolute frame positions (the
+    angle's reduction to one turn)."""
+    B, H, d, grid, F, split = 1, 2, 64, (6, 5, 7), 3, (16, 24, 24)
+    _say(f"fwd base={base} eps={eps} t0={t0} {dtype}")
+    N = grid[0] * grid[1] * grid[2]
+    q, qd = rand((B, H, N, d), 11, dtype)
+    k, kd = rand((B, H, N, d), 12, dtype)
+    v, vd = rand((B, H, N, d), 13, dtype)
+    out = sva.sva_lin_attn_fwd(qd, kd, vd, grid, F, t0=t0, rope=True, split=split, base=base, eps=eps)
+    torch.cuda.synchronize()
+    ref, _, _ = orc.lin_attn_fwd(q, k, v, grid, F, t0=t0, rope=True, split=split, base=base, eps=eps)
+    assert relerr(out, ref) <= TOL[dtype]
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
 def test_fwd_with_initial_cache_in_place(dtype):
     """S0/z0 given and S_out/z_out the same buffers: the final cache is
     written in place."""
