@@ -11,6 +11,6 @@ from .sva import (  # noqa: F401
     sva_block_cache_workspace, sva_lin_attn_bwd, sva_lin_attn_bwd_workspace, sva_lin_attn_fwd,
     sva_lin_attn_fwd_save, sva_lin_attn_fwd_workspace, sva_lin_attn_states_bytes, sva_phi_rope_prep,
     SvaTconvDesc, make_tconv_desc, sva_tconv_apply, sva_tconv_commit, sva_tconv_fwd,
-    SvaProjDesc, sva_qkv_proj_mxfp4, sva_mxfp4_pack_weights, mxfp4_packed_bytes,
+    SvaProjDesc, sva_qkv_proj_mxfp4, sva_mxfp4_pack_weights, mxfp4_packed_bytes, sva_proj_lin_attn_fwd,
 )
 from .autograd import BlockCausalLinearAttention, block_causal_linear_attention  # noqa: F401

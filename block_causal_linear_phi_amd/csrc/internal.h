@@ -1,0 +1,33 @@
+// Internal interfaces between the library's source files (not part of the
+// C ABI): the projection file's launchers that the fused projection +
+// attention entry point in sva.hip drives.
+#ifndef SVA_INTERNAL_H
+#define SVA_INTERNAL_H
+
+#include <hip/hip_runtime.h>
+
+#include "sva.h"
+#include "sva_proj.h"
+
+// Geometry of the fused k, v projection + per-block state reduction (head
+// dimension 64; H even; L divides Nb, Nb divides N).
+struct SvaKvReduceArgs {
+  int B, N, C, H;      // samples, tokens per sample, input channels, heads
+  int Nb, nb, L;       // tokens per block, blocks, tokens per range
+  int Hs, Ws, t0;      // latent rows, columns, first frame
+  int rope, dt, dh;    // RoPE on; t and h axis widths
+  float rope_base;
+};
+
+// Partials of every (range, block) piece at slot g + bhc (g: the range's
+// index along the flattened (b, h, token) axis in units of L; bhc: the
+// block's flattened index), each S^T (64 x 64) then z (64), fp32.
+hipError_t sva_internal_kv_proj_reduce(const SvaKvReduceArgs& a, const void* x, const void* wpack,
+                                       const float* bias, float* partials, hipStream_t stream);
+
+// sva_qkv_proj_mxfp4 restricted to output features [0, f_end) (q alone:
+// f_end = H * d); validation as for the full projection.
+sva_status sva_internal_proj_features(const sva_proj_desc* desc, const void* x, const void* wpack,
+                                      const float* bias, int f_end, void* q, void* k, void* v, void* stream);
+
+#endif  // SVA_INTERNAL_H

@@ -37,6 +37,7 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include "internal.h"
 #include "sva.h"
 #include "sva_proj.h"
 
@@ -60,9 +61,24 @@ struct ProjGeo {
   int N;          // tokens per sample
   int C;          // input channels
   int H, d;
-  int n_out;      // 3 * H * d
+  int n_out;      // features computed: [0, n_out) of the packed weights
+  int n_pack;     // rows of the packed weights (3 * H * d)
   int Mt, Nt;     // token tiles, feature tiles
   int stages;     // C / kTileK
+};
+
+struct KvGeo {
+  int N, C, H;      // tokens per sample, input channels, heads (head dimension 64)
+  int n_pack;       // rows of the packed weights (3 * H * 64)
+  int stages;       // C / kTileK
+  int L;            // tokens per range; divides Nb
+  int ranges;       // N / L
+  int Nb, nb;       // tokens per block, blocks per sample
+  int npairs;       // H / 2
+  int nrg;          // B * ranges
+  int Hs, Ws, t0;   // latent grid rows and columns, first frame
+  int rope, dt, dh; // RoPE on, t and h axis widths (w takes the rest)
+  float log2_base;  // log2 of the RoPE base
 };
 
 // Piece p of row r of the x tile, XOR-swizzled by r & 7: the B operand's
@@ -151,7 +167,7 @@ __global__ __launch_bounds__(kPjThreads, 2) void sva_qkv_proj_kernel(
   // past n_out (a partial last tile) reads the last block and stores nothing.
   const int blk = min(n0 / 64 + wn, g.n_out / 64 - 1);
   const uint8_t* cbase = wpack + ((size_t)blk * g.stages * 4) * 1024 + lane * 16;
-  const uint8_t* sbase = wpack + (size_t)g.n_out * (g.C / 2) + ((size_t)blk * g.stages * 64 + lane) * 4;
+  const uint8_t* sbase = wpack + (size_t)g.n_pack * (g.C / 2) + ((size_t)blk * g.stages * 64 + lane) * 4;
 
   auto load_x = [&](uint4 (&r)[kXLoads], int s) {
     const int k0 = s * kTileK;
@@ -275,6 +291,288 @@ __global__ __launch_bounds__(kPjThreads, 2) void sva_qkv_proj_kernel(
   }
 }
 
+// ---------------------------------------------------------------------------
+// k and v projections fused with the per-block state reduction.
+//
+// A workgroup takes a range of L tokens of one sample (L divides the block's
+// token count, so a range lies in one block) and two heads h0, h0 + 1; its
+// waves compute k and v of those heads (64 features each) for 64-token
+// tiles with the projection's GEMM.  Instead of storing k and v, each tile's
+// epilogue rounds them to bf16 (as a stored tensor would be), applies phi
+// and the numerator-only 3D RoPE to k, stages both transposed in LDS and
+// adds the tile's v^T RoPE(phi k) to the head's state on MFMA, and phi k to
+// its normaliser.  At the end of the range each head's state and normaliser
+// go to the partial slot the block scan reads for (range, block): slot g + bhc
+// with g the range's index along the flattened (b, h, token) axis in units
+// of L.  So k and v never reach HBM.
+// ---------------------------------------------------------------------------
+
+constexpr int kKvThreads = 256;  // waves: k(h0), v(h0), k(h0+1), v(h0+1)
+static_assert(kKvThreads == kPjThreads, "the GEMM part assumes the projection's workgroup size");
+
+// A wave's 64 x 64 bf16 tile, transposed: feature row f (128 bytes = 64
+// tokens), 16-byte piece p = token / 8 at p ^ (f & 7).
+__device__ __forceinline__ int kv_piece(int f, int p) { return f * 8 + (p ^ (f & 7)); }
+
+__global__ __launch_bounds__(kKvThreads, 2) void sva_kv_proj_reduce_kernel(
+    const void* __restrict__ xp, const uint8_t* __restrict__ wpack, const float* __restrict__ bias,
+    float* __restrict__ partials, KvGeo g) {
+  // The x stages double as the epilogue's k and v tiles (the GEMM is done
+  // with them by then); the head states accumulate in LDS, lane by lane, so
+  // that nothing beyond the projection's registers lives across the GEMM.
+  __shared__ uint4 xs[2][kXU4];
+  __shared__ pj_floatx4 sacc[kKvThreads / 64][8][64];
+  __shared__ float zs[2][64];
+  static_assert(sizeof(xs) == (kKvThreads / 64) * 64 * 8 * sizeof(uint4), "tiles alias the x stages");
+  uint4* const kvt = &xs[0][0];  // wave w's tile at kvt + w * 512
+
+  // Tile order: workgroup i runs on XCD i % 8; consecutive workgroups of one
+  // XCD take the head pairs of one token range (they read the same x).
+  const int xcd = blockIdx.x & 7;
+  const int local = blockIdx.x >> 3;
+  const int rg = (local / g.npairs) * 8 + xcd;
+  const int pair = local % g.npairs;
+  if (rg >= g.nrg) return;
+  const int b = rg / g.ranges, r = rg - b * g.ranges;
+  const int n_begin = r * g.L, n_end = n_begin + g.L;
+  const int c = n_begin / g.Nb;
+
+  const int tid = threadIdx.x;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int lane = tid & 63;
+  const int lg = lane >> 4, lr = lane & 15;
+  const int kind = wave & 1;                 // 0: k, 1: v
+  const int head = 2 * pair + (wave >> 1);
+  const int blk = (1 + kind) * g.H + head;   // packed 64-row block (d = 64)
+  const uint8_t* cbase = wpack + ((size_t)blk * g.stages * 4) * 1024 + lane * 16;
+  const uint8_t* sbase = wpack + (size_t)g.n_pack * (g.C / 2) + ((size_t)blk * g.stages * 64 + lane) * 4;
+  const size_t row_bytes = (size_t)g.C * 2;
+  const long long M = (long long)(g.nrg / g.ranges) * g.N;  // B * N rows of x
+
+#pragma unroll
+  for (int k = 0; k < 8; ++k) sacc[wave][k][lane] = pj_floatx4{0.f, 0.f, 0.f, 0.f};
+  if (tid < 128) zs[tid >> 6][tid & 63] = 0.f;
+
+  const int ntiles = (g.L + kTileM - 1) / kTileM;
+  for (int it = 0; it < ntiles; ++it) {
+    const int n0 = n_begin + it * kTileM;
+    const long long m0 = (long long)b * g.N + n0;
+    const int rows = (int)min((long long)kTileM, M - m0);
+    const __amdgpu_buffer_rsrc_t xr = rsrc((const char*)xp + m0 * row_bytes, (uint32_t)(rows * row_bytes));
+    auto load_x = [&](uint4 (&rg4)[kXLoads], int s) {
+      const int k0 = s * kTileK;
+#pragma unroll
+      for (int j = 0; j < kXLoads; ++j) {
+        const int u = tid + j * kKvThreads;
+        const uint32_t off = (uint32_t)((u / kPieces) * row_bytes + (size_t)k0 * 2 + 16 * (u % kPieces));
+        rg4[j] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(xr, off, 0, 0));
+      }
+    };
+    auto store_x = [&](const uint4 (&rg4)[kXLoads], int buf) {
+#pragma unroll
+      for (int j = 0; j < kXLoads; ++j) {
+        const int u = tid + j * kKvThreads;
+        xs[buf][sw(u / kPieces, u % kPieces)] = rg4[j];
+      }
+    };
+    auto load_w = [&](WRegs& w, int s) {
+#pragma unroll
+      for (int rt = 0; rt < 4; ++rt) w.c[rt] = *(const uint4*)(cbase + ((size_t)s * 4 + rt) * 1024);
+      w.s = *(const uint32_t*)(sbase + (size_t)s * 256);
+    };
+    pj_floatx4 acc[4][4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) acc[i][j] = pj_floatx4{0.f, 0.f, 0.f, 0.f};
+    auto compute = [&](const WRegs& w, int buf) {
+      uint32_t e = w.s;
+      asm volatile("" : "+v"(e));  // see the projection kernel
+      float sc[4];
+#pragma unroll
+      for (int rt = 0; rt < 4; ++rt) sc[rt] = e8m0_scale((e >> (8 * rt)) & 0xffu);
+#pragma unroll
+      for (int j = 0; j < kTileK / 32; ++j) {
+        uint4 a[4], bo[4];
+#pragma unroll
+        for (int rt = 0; rt < 4; ++rt) {
+          const uint32_t cw = j == 0 ? w.c[rt].x : j == 1 ? w.c[rt].y : j == 2 ? w.c[rt].z : w.c[rt].w;
+          a[rt] = decode8(cw, sc[rt]);
+        }
+#pragma unroll
+        for (int tt = 0; tt < 4; ++tt) bo[tt] = xs[buf][sw(tt * 16 + lr, 4 * lg + j)];
+#pragma unroll
+        for (int rt = 0; rt < 4; ++rt)
+#pragma unroll
+          for (int tt = 0; tt < 4; ++tt) acc[rt][tt] = mfma(a[rt], bo[tt], acc[rt][tt]);
+      }
+    };
+    // The projection's pipeline (see sva_qkv_proj_kernel).  The barrier
+    // first: every wave has read the previous tile's k and v from xs.
+    const int last = g.stages - 1;
+    uint4 x0[kXLoads], x1[kXLoads];
+    WRegs w0, w1;
+    load_w(w0, 0);
+    load_x(x0, 0);
+    load_x(x1, min(1, last));
+    __syncthreads();
+    store_x(x0, 0);
+    load_x(x0, min(2, last));
+    __syncthreads();
+    auto step = [&](int s, const WRegs& wc, WRegs& wn_, uint4 (&xn)[kXLoads]) {
+      load_w(wn_, min(s + 1, last));
+      __builtin_amdgcn_sched_barrier(0);
+      compute(wc, s & 1);
+      __builtin_amdgcn_sched_barrier(0);
+      if (s + 1 < g.stages) store_x(xn, (s + 1) & 1);
+      __builtin_amdgcn_sched_barrier(0);
+      load_x(xn, min(s + 3, last));
+      __syncthreads();
+    };
+    int s = 0;
+    for (; s + 2 <= g.stages; s += 2) {
+      step(s, w0, w1, x1);
+      step(s + 1, w1, w0, x0);
+    }
+    if (s < g.stages) step(s, w0, w1, x1);
+
+    // Epilogue.  Lane (lg, lr) holds features 32 run + 8 lg + 0..7
+    // (accumulators 2 run, 2 run + 1) of token 16 tt + lr.  Values are
+    // rounded to bf16 as the stored tensor would be; k then gets phi (and its
+    // normaliser share) and the rotation of its position, and is rounded to
+    // bf16 again; tokens past the range contribute zeros.
+    // (lg through an empty asm: otherwise the compiler hoists the bias and
+    // the RoPE constants out of the tile loop, and they occupy registers
+    // through the GEMM.)
+    int lgv = lg;
+    asm volatile("" : "+v"(lgv));
+    float bb[2][8];
+#pragma unroll
+    for (int run = 0; run < 2; ++run)
+#pragma unroll
+      for (int i = 0; i < 8; ++i) bb[run][i] = bias ? bias[blk * 64 + 32 * run + 8 * lgv + i] : 0.f;
+    float inv[2][4];  // RoPE: base^(-2i/d_axis) / (2 pi) of the lane's 8 pairs
+    int axis[2][4];
+#pragma unroll
+    for (int run = 0; run < 2; ++run)
+#pragma unroll
+      for (int pp = 0; pp < 4; ++pp) {
+        const int f = 32 * run + 8 * lgv + 2 * pp;
+        const int ax = f < g.dt ? 0 : f < g.dt + g.dh ? 1 : 2;
+        const int start = ax == 0 ? 0 : ax == 1 ? g.dt : g.dt + g.dh;
+        const int width = ax == 0 ? g.dt : ax == 1 ? g.dh : 64 - g.dt - g.dh;
+        axis[run][pp] = ax;
+        inv[run][pp] = exp2f(-(float)(f - start) / (float)width * g.log2_base) * 0.15915494309189535f;
+      }
+    float zt[2][8];
+#pragma unroll
+    for (int run = 0; run < 2; ++run)
+#pragma unroll
+      for (int i = 0; i < 8; ++i) zt[run][i] = 0.f;
+    char* tile = reinterpret_cast<char*>(kvt + wave * 512);
+#pragma unroll
+    for (int tt = 0; tt < 4; ++tt) {
+      const int tok = 16 * tt + lr;
+      const int n = n0 + tok;
+      const bool valid = n < n_end;
+      float val[2][8];
+#pragma unroll
+      for (int run = 0; run < 2; ++run)
+#pragma unroll
+        for (int i = 0; i < 8; ++i)
+          val[run][i] = (float)(__bf16)(acc[2 * run + (i >> 2)][tt][i & 3] + bb[run][i]);
+      if (kind == 0) {
+        const int hw = g.Hs * g.Ws;
+        const int pt = g.t0 + n / hw, ph = (n / g.Ws) % g.Hs, pw = n % g.Ws;
+#pragma unroll
+        for (int run = 0; run < 2; ++run) {
+#pragma unroll
+          for (int i = 0; i < 8; ++i) {
+            val[run][i] = fmaxf(val[run][i], 0.f);
+            zt[run][i] += valid ? val[run][i] : 0.f;
+          }
+          if (g.rope) {
+#pragma unroll
+            for (int pp = 0; pp < 4; ++pp) {
+              const int ax = axis[run][pp];
+              const int ps = ax == 0 ? pt : ax == 1 ? ph : pw;
+              const float turn = __builtin_amdgcn_fractf((float)ps * inv[run][pp]);
+              const float sn = __builtin_amdgcn_sinf(turn), cs = __builtin_amdgcn_cosf(turn);
+              const float x = val[run][2 * pp], y = val[run][2 * pp + 1];
+              val[run][2 * pp] = x * cs - y * sn;
+              val[run][2 * pp + 1] = x * sn + y * cs;
+            }
+          }
+        }
+      }
+#pragma unroll
+      for (int run = 0; run < 2; ++run)
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+          const int f = 32 * run + 8 * lg + i;
+          const __bf16 h = (__bf16)(valid ? val[run][i] : 0.f);
+          *reinterpret_cast<__bf16*>(tile + kv_piece(f, tok >> 3) * 16 + (tok & 7) * 2) = h;
+        }
+    }
+    if (kind == 0) {
+      // the tile's normaliser share, summed over the 16 token lanes
+#pragma unroll
+      for (int run = 0; run < 2; ++run)
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+          float t = zt[run][i];
+          t += __shfl_xor(t, 1);
+          t += __shfl_xor(t, 2);
+          t += __shfl_xor(t, 4);
+          t += __shfl_xor(t, 8);
+          if (lr == 0) zs[wave >> 1][32 * run + 8 * lg + i] += t;
+        }
+    }
+    __syncthreads();
+    // State rows (value features) 32 (1 - kind) .. + 31 of this wave's head:
+    // S^T[fo][fi] += sum over the tile's tokens of v[fo] RoPE(phi k)[fi].
+    const uint4* vt = kvt + ((wave & 2) + 1) * 512;
+    const uint4* kt = kvt + (wave & 2) * 512;
+    pj_floatx4 sa[2][4];
+#pragma unroll
+    for (int ft = 0; ft < 2; ++ft)
+#pragma unroll
+      for (int fc = 0; fc < 4; ++fc) sa[ft][fc] = sacc[wave][4 * ft + fc][lane];
+#pragma unroll
+    for (int ks = 0; ks < 2; ++ks) {
+      uint4 a[2], bo[4];
+#pragma unroll
+      for (int ft = 0; ft < 2; ++ft) a[ft] = vt[kv_piece(16 * (2 * (1 - kind) + ft) + lr, 4 * ks + lg)];
+#pragma unroll
+      for (int fc = 0; fc < 4; ++fc) bo[fc] = kt[kv_piece(16 * fc + lr, 4 * ks + lg)];
+#pragma unroll
+      for (int ft = 0; ft < 2; ++ft)
+#pragma unroll
+        for (int fc = 0; fc < 4; ++fc) sa[ft][fc] = mfma(a[ft], bo[fc], sa[ft][fc]);
+    }
+#pragma unroll
+    for (int ft = 0; ft < 2; ++ft)
+#pragma unroll
+      for (int fc = 0; fc < 4; ++fc) sacc[wave][4 * ft + fc][lane] = sa[ft][fc];
+  }
+
+  // Partial of (range, block): S^T (row fo, column fi), then z.
+  __syncthreads();
+  const long long bh = (long long)b * g.H + head;
+  const long long gv = bh * g.ranges + r;
+  const long long bhc = bh * g.nb + c;
+  float* dst = partials + (gv + bhc) * (64 * 64 + 64);
+#pragma unroll
+  for (int ft = 0; ft < 2; ++ft)
+#pragma unroll
+    for (int fc = 0; fc < 4; ++fc) {
+      const pj_floatx4 v4 = sacc[wave][4 * ft + fc][lane];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) dst[(16 * (2 * (1 - kind) + ft) + 4 * lg + i) * 64 + 16 * fc + lr] = v4[i];
+    }
+  if (kind == 0) dst[64 * 64 + lane] = zs[wave >> 1][lane];
+}
+
 // Repacks natural-layout MXFP4 weights (codes [n_out, C/2], scales
 // [n_out, C/32]) into the projection's layout: thread (blk, s, lane) writes
 // the lane's 16 code bytes of each row tile rt of 64-feature block blk and
@@ -349,8 +647,8 @@ extern "C" sva_status sva_mxfp4_pack_weights(const sva_proj_desc* desc, const vo
   return SVA_OK;
 }
 
-extern "C" sva_status sva_qkv_proj_mxfp4(const sva_proj_desc* desc, const void* x, const void* wpack,
-                                         const float* bias, void* q, void* k, void* v, void* stream) {
+sva_status sva_internal_proj_features(const sva_proj_desc* desc, const void* x, const void* wpack,
+                                      const float* bias, int f_end, void* q, void* k, void* v, void* stream) {
   const sva_status st = check_desc(desc);
   if (st != SVA_OK) return st;
   const sva_proj_desc& d = *desc;
@@ -358,14 +656,18 @@ extern "C" sva_status sva_qkv_proj_mxfp4(const sva_proj_desc* desc, const void* 
   if (!aligned(x, 16) || !aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(wpack, 16) ||
       (bias && !aligned(bias, 16)))
     return SVA_ERR_INVALID_ARG;
+  const int n_pack = 3 * d.H * d.d;
+  if (f_end < 64 || f_end > n_pack || f_end % 64 != 0) return SVA_ERR_INVALID_ARG;
   const long long M = (long long)d.B * d.N;
   const long long Mt = (M + kTileM - 1) / kTileM;
-  const long long Nt = (3LL * d.H * d.d + kTileN - 1) / kTileN;
+  const long long Nt = (f_end + kTileN - 1) / kTileN;
   const long long grid = (Mt + 7) / 8 * 8 * Nt;
   const size_t xb = (size_t)M * d.C * 2, ob = (size_t)M * d.H * d.d * 2, pb = packed_bytes(d);
   const size_t bb = 3 * (size_t)d.H * d.d * 4;
+  // the outputs that features [0, f_end) reach
   void* outs[3] = {q, k, v};
-  for (int i = 0; i < 3; ++i) {
+  const int n_outs = (f_end + d.H * d.d - 1) / (d.H * d.d);
+  for (int i = 0; i < n_outs; ++i) {
     if (overlap(outs[i], ob, x, xb) || overlap(outs[i], ob, wpack, pb) || (bias && overlap(outs[i], ob, bias, bb)))
       return SVA_ERR_INVALID_ARG;
     for (int j = 0; j < i; ++j)
@@ -377,7 +679,8 @@ extern "C" sva_status sva_qkv_proj_mxfp4(const sva_proj_desc* desc, const void* 
   g.C = d.C;
   g.H = d.H;
   g.d = d.d;
-  g.n_out = 3 * d.H * d.d;
+  g.n_out = f_end;
+  g.n_pack = n_pack;
   g.Mt = (int)Mt;
   g.Nt = (int)Nt;
   g.stages = d.C / kTileK;
@@ -387,4 +690,38 @@ extern "C" sva_status sva_qkv_proj_mxfp4(const sva_proj_desc* desc, const void* 
                       (hipStream_t)stream) != hipSuccess)
     return SVA_ERR_HIP;
   return SVA_OK;
+}
+
+hipError_t sva_internal_kv_proj_reduce(const SvaKvReduceArgs& a, const void* x, const void* wpack,
+                                       const float* bias, float* partials, hipStream_t stream) {
+  KvGeo g;
+  g.N = a.N;
+  g.C = a.C;
+  g.H = a.H;
+  g.n_pack = 3 * a.H * 64;
+  g.stages = a.C / kTileK;
+  g.L = a.L;
+  g.ranges = a.N / a.L;
+  g.Nb = a.Nb;
+  g.nb = a.nb;
+  g.npairs = a.H / 2;
+  g.nrg = a.B * g.ranges;
+  g.Hs = a.Hs;
+  g.Ws = a.Ws;
+  g.t0 = a.t0;
+  g.rope = a.rope;
+  g.dt = a.dt;
+  g.dh = a.dh;
+  g.log2_base = log2f(a.rope_base);
+  const long long grid = ((long long)g.nrg + 7) / 8 * 8 * g.npairs;
+  const uint8_t* wp = (const uint8_t*)wpack;
+  void* args[] = {(void*)&x, (void*)&wp, (void*)&bias, (void*)&partials, &g};
+  return hipLaunchKernel((const void*)&sva_kv_proj_reduce_kernel, dim3((unsigned)grid), dim3(kKvThreads), args, 0,
+                         stream);
+}
+
+extern "C" sva_status sva_qkv_proj_mxfp4(const sva_proj_desc* desc, const void* x, const void* wpack,
+                                         const float* bias, void* q, void* k, void* v, void* stream) {
+  if (!desc) return SVA_ERR_INVALID_ARG;
+  return sva_internal_proj_features(desc, x, wpack, bias, 3 * desc->H * desc->d, q, k, v, stream);
 }

@@ -37,7 +37,9 @@
 #include <mutex>
 #include <tuple>
 
+#include "internal.h"
 #include "sva.h"
+#include "sva_proj.h"
 
 namespace {
 
@@ -2243,6 +2245,102 @@ sva_status run_bwd(const sva_desc* desc, const void* q, const void* k, const voi
   return SVA_OK;
 }
 
+// Projection + attention with k and v reduced inside the projection.  The
+// ranges of the fused kernel take the place of the reduction's workgroup
+// ranges: L tokens each, L dividing the block's token count, so that the
+// scan finds piece (g, block) at slot g + block exactly as it does for the
+// reduction.
+struct ProjPlan {
+  Plan p;
+  long long L, G;
+  size_t off_q, off_partials, off_frags, off_zc, bytes;
+};
+
+sva_status plan_proj_fwd(const sva_desc* a, const sva_proj_desc* pd, ProjPlan* pp) {
+  sva_status s = check_common(a, false, &pp->p);
+  if (s != SVA_OK) return s;
+  const Plan& p = pp->p;
+  if (!pd) return SVA_ERR_INVALID_ARG;
+  if (!p.bf16 || p.D != 64) return SVA_ERR_UNSUPPORTED;
+  if (pd->B != a->B || pd->H != a->H || pd->d != a->d || pd->N != p.N) return SVA_ERR_INVALID_ARG;
+  if (a->H % 2 != 0 || pd->C % 128 != 0 || pd->C < 128) return SVA_ERR_UNSUPPORTED;
+  if (p.rope && (a->rope_dt % 2 != 0 || a->rope_dh % 2 != 0)) return SVA_ERR_UNSUPPORTED;
+  long long L = 1;
+  for (long long cand = p.Nb < 2048 ? p.Nb : 2048; cand >= 1; --cand)
+    if (p.Nb % cand == 0) {
+      L = cand;
+      break;
+    }
+  pp->L = L;
+  const long long total = (long long)p.BH * p.N;
+  pp->G = total / L;
+  if (pp->G + (long long)p.BH * p.nb >= (1LL << 31) / (p.D * p.D + p.D)) return SVA_ERR_UNSUPPORTED;
+  const size_t E = (size_t)p.D * p.D + p.D;
+  size_t off = 0;
+  pp->off_q = off;
+  off = align256(off + (size_t)total * p.D * 2);
+  pp->off_partials = off;
+  off = align256(off + (size_t)(pp->G + (long long)p.BH * p.nb) * E * sizeof(float));
+  pp->off_frags = off;
+  off = align256(off + (size_t)p.BH * p.nb * p.D * p.D * 2);
+  pp->off_zc = off;
+  off = align256(off + (size_t)p.BH * p.nb * p.D * sizeof(float));
+  pp->bytes = off;
+  return SVA_OK;
+}
+
+sva_status run_proj_fwd(const sva_desc* a, const sva_proj_desc* pd, const void* x, const void* wpack,
+                        const float* bias, void* out, const float* S0, const float* z0, float* S_out,
+                        float* z_out, void* ws, size_t ws_bytes, void* stream) {
+  ProjPlan pp;
+  sva_status s = plan_proj_fwd(a, pd, &pp);
+  if (s != SVA_OK) return s;
+  Plan& p = pp.p;
+  if (!x || !wpack || !out) return SVA_ERR_INVALID_ARG;
+  if (!is_aligned16(x) || !is_aligned16(wpack) || !is_aligned16(out) || (bias && !is_aligned16(bias)))
+    return SVA_ERR_INVALID_ARG;
+  if ((S0 == nullptr) != (z0 == nullptr) || (S_out == nullptr) != (z_out == nullptr))
+    return SVA_ERR_INVALID_ARG;
+  if ((S0 && (!is_aligned16(S0) || !is_aligned16(z0))) ||
+      (S_out && (!is_aligned16(S_out) || !is_aligned16(z_out))))
+    return SVA_ERR_INVALID_ARG;
+  if (!ws || ws_bytes < pp.bytes || !is_aligned16(ws)) return SVA_ERR_WORKSPACE;
+  const size_t nbytes = qkv_bytes(p);
+  const size_t xbytes = (size_t)pd->B * pd->N * pd->C * 2;
+  if (overlaps(out, nbytes, x, xbytes) || overlaps(out, nbytes, ws, ws_bytes)) return SVA_ERR_INVALID_ARG;
+  char* wsb = (char*)ws;
+  void* q = wsb + pp.off_q;
+  float* partials = (float*)(wsb + pp.off_partials);
+  void* frags = wsb + pp.off_frags;
+  float* zc = (float*)(wsb + pp.off_zc);
+  hipStream_t st = (hipStream_t)stream;
+  // q: the projection's first H*d features, into the workspace
+  s = sva_internal_proj_features(pd, x, wpack, bias, pd->H * pd->d, q, q, q, stream);
+  if (s != SVA_OK) return s;
+  SvaKvReduceArgs ka;
+  ka.B = pd->B;
+  ka.N = pd->N;
+  ka.C = pd->C;
+  ka.H = pd->H;
+  ka.Nb = p.Nb;
+  ka.nb = p.nb;
+  ka.L = (int)pp.L;
+  ka.Hs = a->Hs;
+  ka.Ws = a->Ws;
+  ka.t0 = a->t0;
+  ka.rope = p.rope ? 1 : 0;
+  ka.dt = a->rope_dt;
+  ka.dh = a->rope_dh;
+  ka.rope_base = a->rope_base;
+  if (sva_internal_kv_proj_reduce(ka, x, wpack, bias, partials, st) != hipSuccess) return SVA_ERR_HIP;
+  plan_grids(&p);
+  if (SVA_DISPATCH2(p, launch_scan, p, partials, S0, z0, S_out, z_out, frags, zc, true, st, false, pp.L) !=
+      hipSuccess)
+    return SVA_ERR_HIP;
+  if (SVA_DISPATCH(p, launch_apply, p, q, out, frags, zc, a->eps, st) != hipSuccess) return SVA_ERR_HIP;
+  return SVA_OK;
+}
+
 }  // namespace
 
 // ---------------------------------------------------------------------------
@@ -2277,6 +2375,22 @@ sva_status sva_lin_attn_fwd(const sva_desc* desc, const void* q, const void* k, 
                             void* out, const float* S0, const float* z0, float* S_out,
                             float* z_out, void* ws, size_t ws_bytes, void* stream) {
   return run_fwd(desc, q, k, v, out, S0, z0, S_out, z_out, ws, ws_bytes, stream, nullptr);
+}
+
+sva_status sva_proj_lin_attn_fwd_workspace(const sva_desc* attn, const sva_proj_desc* proj, size_t* bytes) {
+  if (!bytes) return SVA_ERR_INVALID_ARG;
+  ProjPlan pp;
+  sva_status s = plan_proj_fwd(attn, proj, &pp);
+  if (s != SVA_OK) return s;
+  *bytes = pp.bytes;
+  return SVA_OK;
+}
+
+sva_status sva_proj_lin_attn_fwd(const sva_desc* attn, const sva_proj_desc* proj, const void* x,
+                                 const void* wpack, const float* bias, void* out, const float* S0,
+                                 const float* z0, float* S_out, float* z_out, void* ws, size_t ws_bytes,
+                                 void* stream) {
+  return run_proj_fwd(attn, proj, x, wpack, bias, out, S0, z0, S_out, z_out, ws, ws_bytes, stream);
 }
 
 sva_status sva_lin_attn_fwd_traced(const sva_desc* desc, const void* q, const void* k,

@@ -76,6 +76,10 @@ _SIG = {
     "sva_tconv_commit": (ctypes.c_int, [ctypes.POINTER(SvaTconvDesc)] + [_VP] * 3),
     "sva_mxfp4_pack_weights": (ctypes.c_int, [ctypes.POINTER(SvaProjDesc)] + [_VP] * 4),
     "sva_qkv_proj_mxfp4": (ctypes.c_int, [ctypes.POINTER(SvaProjDesc)] + [_VP] * 7),
+    "sva_proj_lin_attn_fwd_workspace": (ctypes.c_int, [ctypes.POINTER(SvaDesc), ctypes.POINTER(SvaProjDesc),
+                                                        ctypes.POINTER(ctypes.c_size_t)]),
+    "sva_proj_lin_attn_fwd": (ctypes.c_int, [ctypes.POINTER(SvaDesc), ctypes.POINTER(SvaProjDesc)] + [_VP] * 9
+                              + [ctypes.c_size_t, _VP]),
 }
 
 
@@ -358,3 +362,27 @@ def sva_qkv_proj_mxfp4(x, wpack, bias, H: int, d: int, *, q=None, k=None, v=None
                                   _ptr(outs[0]), _ptr(outs[1]), _ptr(outs[2]), _stream(stream))
     _check(st, "sva_qkv_proj_mxfp4")
     return tuple(outs)
+
+
+def sva_proj_lin_attn_fwd(x, wpack, bias, H: int, grid: Tuple[int, int, int], frames_per_block: int, *,
+                          t0: int = 0, rope: bool = False, split=None, base: float = 10000.0, eps: float = 1e-6,
+                          S0=None, z0=None, S_out=None, z_out=None, out=None, ws=None, stream=None):
+    """Projection and attention fused (sva_proj_lin_attn_fwd): x [B, N, C]
+    bf16 with N = T * Hs * Ws; wpack from sva_mxfp4_pack_weights for H heads
+    of d = 64; bias [3 H 64] fp32 or None.  Returns out [B, H, N, 64] bf16."""
+    import torch
+    if x.dim() != 3 or x.dtype != torch.bfloat16:
+        raise ValueError("x must be [B, N, C] bf16")
+    B, N, C = x.shape
+    q_like = torch.empty((B, H, N, 64), dtype=torch.bfloat16, device=x.device) if out is None else out
+    desc = _desc_from(q_like, grid, frames_per_block, t0, rope, split, base, eps)
+    pdesc = SvaProjDesc(B, N, C, H, 64)
+    n = ctypes.c_size_t()
+    _check(lib().sva_proj_lin_attn_fwd_workspace(ctypes.byref(desc), ctypes.byref(pdesc), ctypes.byref(n)),
+           "sva_proj_lin_attn_fwd_workspace")
+    ws = _workspace(n.value, x, ws)
+    st = lib().sva_proj_lin_attn_fwd(ctypes.byref(desc), ctypes.byref(pdesc), _ptr(x), _ptr(wpack), _ptr(bias),
+                                     _ptr(q_like), _ptr(S0), _ptr(z0), _ptr(S_out), _ptr(z_out), _ptr(ws),
+                                     ws.numel() * ws.element_size(), _stream(stream))
+    _check(st, "sva_proj_lin_attn_fwd")
+    return q_like

@@ -76,6 +76,26 @@ sva_status sva_mxfp4_pack_weights(const sva_proj_desc* desc, const void* codes, 
 sva_status sva_qkv_proj_mxfp4(const sva_proj_desc* desc, const void* x, const void* wpack, const float* bias,
                               void* q, void* k, void* v, void* stream);
 
+/* Projection and attention in one pass over the tokens' k and v:
+ *   out = sva_lin_attn_fwd(attn, q, k, v, ...) with (q, k, v) =
+ *         sva_qkv_proj_mxfp4(proj, x, wpack, bias) rounded to bf16,
+ * where k and v never reach memory: the k, v projection's epilogue applies
+ * phi and the numerator-only RoPE to k (the [talk] 3D RoPE segment and the
+ * [news] positional-encoding paragraph) and adds each 64-token tile's
+ * RoPE(phi k)^T v and phi k to the block states ([talk] linear-attention and
+ * block KV cache segments).  q goes through the workspace.  The SANA-Video
+ * article's 4-bit quantization paragraph motivates fusing the projection
+ * into the attention.
+ *   attn: bf16, d = 64, H even; proj: the same B, H, d, and N = T*Hs*Ws;
+ *   S0, z0, S_out, z_out, eps and RoPE as in sva_lin_attn_fwd.
+ * SVA_ERR_UNSUPPORTED outside those limits or the projection's; the
+ * workspace is sva_proj_lin_attn_fwd_workspace bytes. */
+sva_status sva_proj_lin_attn_fwd_workspace(const sva_desc* attn, const sva_proj_desc* proj, size_t* bytes);
+sva_status sva_proj_lin_attn_fwd(const sva_desc* attn, const sva_proj_desc* proj, const void* x,
+                                 const void* wpack, const float* bias, void* out, const float* S0,
+                                 const float* z0, float* S_out, float* z_out, void* ws, size_t ws_bytes,
+                                 void* stream);
+
 #ifdef __cplusplus
 }
 #endif
