@@ -399,6 +399,63 @@ def proj_leg(w, steps: int, warmup: int, sets: int):
     return a.elapsed_time(b) / steps
 
 
+def fused_leg(w, aw, steps: int, warmup: int, sets: int):
+    """Projection + attention at the workload's token count, two ways, each
+    timed over `steps` calls with `sets` input/output sets alternating:
+      fused: sva_proj_lin_attn_fwd (k, v reduced inside the projection);
+      two calls: sva_qkv_proj_mxfp4 then sva_lin_attn_fwd on the stored
+      q, k, v.  Returns (fused ms, two-call ms)."""
+    import torch
+    from block_causal_linear_phi_amd import sva
+    from block_causal_linear_phi_amd import workloads as wl
+
+    dev = torch.device("cuda:0")
+    x0 = torch.empty((w.B, w.N, w.C), dtype=torch.bfloat16, device=dev)
+    for j, s0 in enumerate(range(0, w.N, 4096)):
+        n = min(4096, w.N - s0)
+        _, raw = wl.draw((n, w.C), wl.seed_for(w.name, "x", 0, j), 1.0, "bf16")
+        x0[0, s0:s0 + n].copy_(torch.from_numpy(raw.view("int16")).view(torch.bfloat16))
+    codes, scales = wl.mxfp4_weights(w.n_out, w.C, wl.seed_for(w.name, "w", 0, 0))
+    wp = sva.sva_mxfp4_pack_weights(torch.from_numpy(wl.pack_nibbles(codes)).to(dev),
+                                    torch.from_numpy(scales).to(dev), w.H, w.d)
+    bias = torch.from_numpy(wl.draw((w.n_out,), wl.seed_for(w.name, "bias", 0, 0), 0.1, "f32")[0]).to(dev)
+    xs = [x0] + [x0.clone() for _ in range(sets - 1)]
+    outs = [torch.empty((w.B, w.H, w.N, w.d), dtype=torch.bfloat16, device=dev) for _ in range(sets)]
+    qkv = [torch.empty((w.B, w.H, w.N, w.d), dtype=torch.bfloat16, device=dev) for _ in range(3)]
+    grid = (aw.T, aw.Hs, aw.Ws)
+    kw = dict(t0=aw.t0, rope=aw.rope, split=aw.split, base=aw.base, eps=aw.eps)
+    fdesc = sva.make_desc(w.B, w.H, w.d, grid, aw.F, dtype=sva.SVA_BF16, **kw)
+    pdesc = sva.SvaProjDesc(w.B, w.N, w.C, w.H, w.d)
+    n = ctypes.c_size_t()
+    sva._check(sva.lib().sva_proj_lin_attn_fwd_workspace(ctypes.byref(fdesc), ctypes.byref(pdesc), ctypes.byref(n)),
+               "sva_proj_lin_attn_fwd_workspace")
+    fws = torch.empty(n.value, dtype=torch.uint8, device=dev)
+    aws = torch.empty(sva.sva_lin_attn_fwd_workspace(fdesc), dtype=torch.uint8, device=dev)
+    stream = torch.cuda.current_stream()
+
+    def fused(i):
+        sva.sva_proj_lin_attn_fwd(xs[i % sets], wp, bias, w.H, grid, aw.F, out=outs[i % sets], ws=fws,
+                                  stream=stream, **kw)
+
+    def two(i):
+        sva.sva_qkv_proj_mxfp4(xs[i % sets], wp, bias, w.H, w.d, q=qkv[0], k=qkv[1], v=qkv[2], stream=stream)
+        sva.sva_lin_attn_fwd(qkv[0], qkv[1], qkv[2], grid, aw.F, out=outs[i % sets], ws=aws, stream=stream, **kw)
+
+    res = []
+    for fn in (fused, two):
+        for i in range(warmup):
+            fn(i)
+        torch.cuda.synchronize()
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record(stream)
+        for i in range(steps):
+            fn(i)
+        b.record(stream)
+        torch.cuda.synchronize()
+        res.append(a.elapsed_time(b) / steps)
+    return res[0], res[1]
+
+
 def proj_cpu_leg(w, min_secs: float = 10.0, tokens: int = 1024):
     """The fp64 projection oracle on the host over the workload's first
     `tokens` tokens, repeated until `min_secs` have passed."""
@@ -628,6 +685,8 @@ def main():
                     help="time the backward (sva_lin_attn_bwd) instead of the forward")
     ap.add_argument("--tconv", action="store_true",
                     help="time the causal temporal convolution of the Mix-FFN on the workload's grid instead")
+    ap.add_argument("--fused", action="store_true",
+                    help="projection + attention: the fused entry point against the two calls")
     ap.add_argument("--proj", action="store_true",
                     help="time the QKV projection with MXFP4 weights on the workload's tokens instead")
     ap.add_argument("--stream", action="store_true",
@@ -662,6 +721,24 @@ def main():
     from block_causal_linear_phi_amd import workloads as wl
     if args.copy_calib:
         copy_calibration(args.copy_calib)
+    if args.fused:
+        pw = wl.PROJ_WORKLOADS["proj_" + args.workload]
+        aw = wl.WORKLOADS[args.workload]
+        ms, ms_two = fused_leg(pw, aw, args.steps, args.warmup, args.sets)
+        flops = 2.0 * pw.B * pw.N * pw.C * pw.n_out
+        print(json.dumps({
+            "metric": "tokens/s of the QKV projection (MXFP4 weights) and block-causal attention forward, fused",
+            "value": pw.B * pw.N / (ms * 1e-3), "unit": "tokens/s", "n_gpus": 1, "steps": args.steps,
+            "warmup": args.warmup, "ms_per_step": ms, "higher_is_better": True, "scaling": "weak",
+            "vs_baseline": None, "dtype": "bf16",
+            "data": "synthetic (seeded N(0,1) activations; uniform E2M1 codes, E8M0 scales 2^-7..2^-3; resident in HBM)",
+            "config": {"workload": f"{pw.name} + {aw.name}: x [{pw.B}, {pw.N}, {pw.C}] -> q, k, v of {pw.H} heads x "
+                                   f"{pw.d} -> block-causal attention, grid {aw.T}x{aw.Hs}x{aw.Ws}, blocks of {aw.F}",
+                       "B": pw.B, "tokens": pw.N, "C": pw.C, "H": pw.H, "d": pw.d},
+            "ms_per_step_two_calls": ms_two, "speedup_over_two_calls": ms_two / ms,
+            "projection_tflops": flops / (ms * 1e-3) / 1e12,
+        }), flush=True)
+        return
     if args.proj:
         pw = wl.PROJ_WORKLOADS["proj_" + args.workload]
         ms = proj_leg(pw, args.steps, args.warmup, args.sets)

@@ -2265,12 +2265,27 @@ sva_status plan_proj_fwd(const sva_desc* a, const sva_proj_desc* pd, ProjPlan* p
   if (pd->B != a->B || pd->H != a->H || pd->d != a->d || pd->N != p.N) return SVA_ERR_INVALID_ARG;
   if (a->H % 2 != 0 || pd->C % 128 != 0 || pd->C < 128) return SVA_ERR_UNSUPPORTED;
   if (p.rope && (a->rope_dt % 2 != 0 || a->rope_dh % 2 != 0)) return SVA_ERR_UNSUPPORTED;
+  // Range length L: a divisor of the block length (a range never straddles
+  // a block), chosen for the k/v kernel's occupancy.  That kernel runs one
+  // workgroup per (range, head pair), two per CU, each a loop over ceil(L/64)
+  // token tiles; with 256 CUs (512 slots) the estimated time is
+  // ceil(workgroups / 512) rounds of ceil(L/64) tiles, plus the partials'
+  // write and the scan's read of them (about 1e8 bytes per tile's time).
+  // Ties go to the longer range (fewer partials).
   long long L = 1;
-  for (long long cand = p.Nb < 2048 ? p.Nb : 2048; cand >= 1; --cand)
-    if (p.Nb % cand == 0) {
+  double best = 0.0;
+  const long long pairs = a->H / 2;
+  for (long long cand = p.Nb < 2048 ? p.Nb : 2048; cand >= 1; --cand) {
+    if (p.Nb % cand != 0) continue;
+    const long long ranges = (long long)a->B * (p.N / cand);
+    const long long wgs = (ranges + 7) / 8 * 8 * pairs;
+    const double cost = (double)((wgs + 511) / 512) * (double)((cand + 63) / 64) +
+                        (double)ranges * a->H * (p.D * p.D + p.D) * 8.0 / 1e8;
+    if (L == 1 || cost < best) {
       L = cand;
-      break;
+      best = cost;
     }
+  }
   pp->L = L;
   const long long total = (long long)p.BH * p.N;
   pp->G = total / L;
