@@ -6,8 +6,31 @@
 
 #include <hip/hip_runtime.h>
 
+#include <stdint.h>
+
 #include "sva.h"
 #include "sva_proj.h"
+
+// n / d for 0 <= n < 2^31 as (umulhi(n, mul) + n) >> shift, constants from
+// the round-up method (Granlund & Montgomery, "Division by invariant
+// integers using multiplication", 1994).
+struct FastDiv {
+  uint32_t mul, shift, div;
+};
+
+inline FastDiv make_fastdiv(uint32_t d) {
+  FastDiv f;
+  uint32_t s = 0;
+  while ((1ull << s) < d) ++s;
+  f.shift = s;
+  f.mul = (uint32_t)(((1ull << 32) * ((1ull << s) - d)) / d + 1);
+  f.div = d;
+  return f;
+}
+
+__device__ __forceinline__ uint32_t fdiv(uint32_t n, const FastDiv& f) {
+  return (__umulhi(n, f.mul) + n) >> f.shift;
+}
 
 // Geometry of the fused k, v projection + per-block state reduction (head
 // dimension 64; H even; L divides Nb, Nb divides N).

@@ -76,10 +76,20 @@ struct KvGeo {
   int Nb, nb;       // tokens per block, blocks per sample
   int npairs;       // H / 2
   int nrg;          // B * ranges
+  FastDiv fHW, fWs; // division by Hs * Ws and by Ws
   int Hs, Ws, t0;   // latent grid rows and columns, first frame
   int rope, dt, dh; // RoPE on, t and h axis widths (w takes the rest)
   float log2_base;  // log2 of the RoPE base
+  double log2_base_d;
+  int F;            // frames per block
+  int tab_entries;  // F dt/2 + Hs dh/2 + Ws dw/2 (the RoPE table's size)
 };
+
+// LDS RoPE table of the fused k, v kernel: cos/sin of every (axis position,
+// frequency) one workgroup's range can need: [F frames of its block][dt/2],
+// then [Hs][dh/2], then [Ws][dw/2].  Sized so that two workgroups still fit
+// in a CU's 160 KB of LDS; larger grids rotate on the fly.
+constexpr int kRopeTab = 1728;
 
 // Piece p of row r of the x tile, XOR-swizzled by r & 7: the B operand's
 // 16-byte reads (served eight lanes at a time) take one piece of eight
@@ -314,6 +324,7 @@ static_assert(kKvThreads == kPjThreads, "the GEMM part assumes the projection's 
 // tokens), 16-byte piece p = token / 8 at p ^ (f & 7).
 __device__ __forceinline__ int kv_piece(int f, int p) { return f * 8 + (p ^ (f & 7)); }
 
+template <bool kTab>
 __global__ __launch_bounds__(kKvThreads, 2) void sva_kv_proj_reduce_kernel(
     const void* __restrict__ xp, const uint8_t* __restrict__ wpack, const float* __restrict__ bias,
     float* __restrict__ partials, KvGeo g) {
@@ -323,6 +334,8 @@ __global__ __launch_bounds__(kKvThreads, 2) void sva_kv_proj_reduce_kernel(
   __shared__ uint4 xs[2][kXU4];
   __shared__ pj_floatx4 sacc[kKvThreads / 64][8][64];
   __shared__ float zs[2][64];
+  __shared__ float bs[kKvThreads / 64][64];
+  __shared__ float2 rtab[kTab ? kRopeTab : 1];
   static_assert(sizeof(xs) == (kKvThreads / 64) * 64 * 8 * sizeof(uint4), "tiles alias the x stages");
   uint4* const kvt = &xs[0][0];  // wave w's tile at kvt + w * 512
 
@@ -352,33 +365,78 @@ __global__ __launch_bounds__(kKvThreads, 2) void sva_kv_proj_reduce_kernel(
 #pragma unroll
   for (int k = 0; k < 8; ++k) sacc[wave][k][lane] = pj_floatx4{0.f, 0.f, 0.f, 0.f};
   if (tid < 128) zs[tid >> 6][tid & 63] = 0.f;
+  bs[wave][lane] = bias ? bias[blk * 64 + lane] : 0.f;
+  const int ht = g.dt >> 1, hh = g.dh >> 1, hwd = (64 - g.dt - g.dh) >> 1;
+  const int off_h = g.F * ht, off_w = off_h + g.Hs * hh;
+  if constexpr (kTab) {
+    // cos, sin of pos * base^(-2i/width) turns: the angle in fp64, reduced
+    // to [-1/2, 1/2] turn, then the hardware sine and cosine (which take
+    // turns); read by the tile loop after its first barrier.
+    for (int e = tid; e < g.tab_entries; e += kKvThreads) {
+      int pos, i, width;
+      if (e < off_h) {
+        pos = g.t0 + c * g.F + e / ht, i = e % ht, width = g.dt;
+      } else if (e < off_w) {
+        pos = (e - off_h) / hh, i = (e - off_h) % hh, width = g.dh;
+      } else {
+        pos = (e - off_w) / hwd, i = (e - off_w) % hwd, width = 64 - g.dt - g.dh;
+      }
+      double rv = (double)pos * exp2(-(double)(2 * i) / (double)width * g.log2_base_d) * 0.15915494309189535;
+      rv -= rint(rv);
+      rtab[e] = make_float2(__builtin_amdgcn_cosf((float)rv), __builtin_amdgcn_sinf((float)rv));
+    }
+  }
 
+  // x rows of token tile t of the range; past the last tile the descriptor
+  // is empty (its loads return zeros and touch no memory).
   const int ntiles = (g.L + kTileM - 1) / kTileM;
+  auto tile_rsrc = [&](int t) {
+    const long long m0 = (long long)b * g.N + n_begin + (long long)t * kTileM;
+    const int rows = t < ntiles ? (int)min((long long)kTileM, M - m0) : 0;
+    return rsrc((const char*)xp + m0 * row_bytes, (uint32_t)(rows * row_bytes));
+  };
+  auto load_x = [&](uint4 (&rg4)[kXLoads], __amdgpu_buffer_rsrc_t xr, int s) {
+    const int k0 = s * kTileK;
+#pragma unroll
+    for (int j = 0; j < kXLoads; ++j) {
+      const int u = tid + j * kKvThreads;
+      const uint32_t off = (uint32_t)((u / kPieces) * row_bytes + (size_t)k0 * 2 + 16 * (u % kPieces));
+      rg4[j] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(xr, off, 0, 0));
+    }
+  };
+  auto store_x = [&](const uint4 (&rg4)[kXLoads], int buf) {
+#pragma unroll
+    for (int j = 0; j < kXLoads; ++j) {
+      const int u = tid + j * kKvThreads;
+      xs[buf][sw(u / kPieces, u % kPieces)] = rg4[j];
+    }
+  };
+  auto load_w = [&](WRegs& w, int s) {
+#pragma unroll
+    for (int rt = 0; rt < 4; ++rt) w.c[rt] = *(const uint4*)(cbase + ((size_t)s * 4 + rt) * 1024);
+    w.s = *(const uint32_t*)(sbase + (size_t)s * 256);
+  };
+
+  // The GEMM pipeline runs on across tiles: the last steps of a tile load
+  // the next tile's first two x stages and first weight stage, which stay in
+  // registers through the epilogue (the stage count is even, so they land in
+  // x0, x1 and w0, where the prologue expects them).
+  const int last = g.stages - 1;
+  uint4 x0[kXLoads], x1[kXLoads];
+  WRegs w0, w1;
+  load_w(w0, 0);
+  {
+    const __amdgpu_buffer_rsrc_t xr0 = tile_rsrc(0);
+    load_x(x0, xr0, 0);
+    load_x(x1, xr0, 1);
+  }
   for (int it = 0; it < ntiles; ++it) {
     const int n0 = n_begin + it * kTileM;
-    const long long m0 = (long long)b * g.N + n0;
-    const int rows = (int)min((long long)kTileM, M - m0);
-    const __amdgpu_buffer_rsrc_t xr = rsrc((const char*)xp + m0 * row_bytes, (uint32_t)(rows * row_bytes));
-    auto load_x = [&](uint4 (&rg4)[kXLoads], int s) {
-      const int k0 = s * kTileK;
-#pragma unroll
-      for (int j = 0; j < kXLoads; ++j) {
-        const int u = tid + j * kKvThreads;
-        const uint32_t off = (uint32_t)((u / kPieces) * row_bytes + (size_t)k0 * 2 + 16 * (u % kPieces));
-        rg4[j] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(xr, off, 0, 0));
-      }
-    };
-    auto store_x = [&](const uint4 (&rg4)[kXLoads], int buf) {
-#pragma unroll
-      for (int j = 0; j < kXLoads; ++j) {
-        const int u = tid + j * kKvThreads;
-        xs[buf][sw(u / kPieces, u % kPieces)] = rg4[j];
-      }
-    };
-    auto load_w = [&](WRegs& w, int s) {
-#pragma unroll
-      for (int rt = 0; rt < 4; ++rt) w.c[rt] = *(const uint4*)(cbase + ((size_t)s * 4 + rt) * 1024);
-      w.s = *(const uint32_t*)(sbase + (size_t)s * 256);
+    const __amdgpu_buffer_rsrc_t xr = tile_rsrc(it), xr_next = tile_rsrc(it + 1);
+    // x stage vs of this tile, or vs - stages of the next one
+    auto load_v = [&](uint4 (&rg4)[kXLoads], int vs) {
+      const bool nx = vs >= g.stages;
+      load_x(rg4, nx ? xr_next : xr, nx ? vs - g.stages : vs);
     };
     pj_floatx4 acc[4][4];
 #pragma unroll
@@ -407,34 +465,33 @@ __global__ __launch_bounds__(kKvThreads, 2) void sva_kv_proj_reduce_kernel(
           for (int tt = 0; tt < 4; ++tt) acc[rt][tt] = mfma(a[rt], bo[tt], acc[rt][tt]);
       }
     };
-    // The projection's pipeline (see sva_qkv_proj_kernel).  The barrier
-    // first: every wave has read the previous tile's k and v from xs.
-    const int last = g.stages - 1;
-    uint4 x0[kXLoads], x1[kXLoads];
-    WRegs w0, w1;
-    load_w(w0, 0);
-    load_x(x0, 0);
-    load_x(x1, min(1, last));
+    // The barrier first: every wave has read the previous tile's k and v
+    // from xs.
     __syncthreads();
     store_x(x0, 0);
-    load_x(x0, min(2, last));
+    load_v(x0, 2);
     __syncthreads();
     auto step = [&](int s, const WRegs& wc, WRegs& wn_, uint4 (&xn)[kXLoads]) {
-      load_w(wn_, min(s + 1, last));
+      load_w(wn_, s + 1);
       __builtin_amdgcn_sched_barrier(0);
       compute(wc, s & 1);
       __builtin_amdgcn_sched_barrier(0);
-      if (s + 1 < g.stages) store_x(xn, (s + 1) & 1);
+      store_x(xn, (s + 1) & 1);
       __builtin_amdgcn_sched_barrier(0);
-      load_x(xn, min(s + 3, last));
+      load_v(xn, s + 3);
       __syncthreads();
     };
     int s = 0;
-    for (; s + 2 <= g.stages; s += 2) {
+    for (; s + 2 < g.stages; s += 2) {
       step(s, w0, w1, x1);
       step(s + 1, w1, w0, x0);
     }
-    if (s < g.stages) step(s, w0, w1, x1);
+    step(s, w0, w1, x1);
+    // the tile's last stage: weights of stage 0 for the next tile, no x
+    load_w(w0, 0);
+    __builtin_amdgcn_sched_barrier(0);
+    compute(w1, 1);
+    __syncthreads();  // every wave is done with xs, which the epilogue overwrites
 
     // Epilogue.  Lane (lg, lr) holds features 32 run + 8 lg + 0..7
     // (accumulators 2 run, 2 run + 1) of token 16 tt + lr.  Values are
@@ -450,9 +507,11 @@ __global__ __launch_bounds__(kKvThreads, 2) void sva_kv_proj_reduce_kernel(
 #pragma unroll
     for (int run = 0; run < 2; ++run)
 #pragma unroll
-      for (int i = 0; i < 8; ++i) bb[run][i] = bias ? bias[blk * 64 + 32 * run + 8 * lgv + i] : 0.f;
-    float inv[2][4];  // RoPE: base^(-2i/d_axis) / (2 pi) of the lane's 8 pairs
-    int axis[2][4];
+      for (int i = 0; i < 8; ++i) bb[run][i] = bs[wave][32 * run + 8 * lgv + i];
+    // RoPE of the lane's 8 pairs: the axis, and either the table entry of
+    // position 0 and the entries per position step, or base^(-2i/width)/(2 pi)
+    float inv[2][4];
+    int axis[2][4], eoff[2][4], estr[2][4];
 #pragma unroll
     for (int run = 0; run < 2; ++run)
 #pragma unroll
@@ -462,7 +521,12 @@ __global__ __launch_bounds__(kKvThreads, 2) void sva_kv_proj_reduce_kernel(
         const int start = ax == 0 ? 0 : ax == 1 ? g.dt : g.dt + g.dh;
         const int width = ax == 0 ? g.dt : ax == 1 ? g.dh : 64 - g.dt - g.dh;
         axis[run][pp] = ax;
-        inv[run][pp] = exp2f(-(float)(f - start) / (float)width * g.log2_base) * 0.15915494309189535f;
+        if constexpr (kTab) {
+          eoff[run][pp] = (ax == 0 ? 0 : ax == 1 ? off_h : off_w) + ((f - start) >> 1);
+          estr[run][pp] = width >> 1;
+        } else {
+          inv[run][pp] = exp2f(-(float)(f - start) / (float)width * g.log2_base) * 0.15915494309189535f;
+        }
       }
     float zt[2][8];
 #pragma unroll
@@ -482,8 +546,11 @@ __global__ __launch_bounds__(kKvThreads, 2) void sva_kv_proj_reduce_kernel(
         for (int i = 0; i < 8; ++i)
           val[run][i] = (float)(__bf16)(acc[2 * run + (i >> 2)][tt][i & 3] + bb[run][i]);
       if (kind == 0) {
-        const int hw = g.Hs * g.Ws;
-        const int pt = g.t0 + n / hw, ph = (n / g.Ws) % g.Hs, pw = n % g.Ws;
+        const uint32_t np = (uint32_t)(valid ? n : n_end - 1);  // positions past the range: any in it
+        const uint32_t fr = fdiv(np, g.fHW), rem = np - fr * g.fHW.div;
+        const uint32_t row = fdiv(rem, g.fWs);
+        const int pt = kTab ? (int)fr - c * g.F : g.t0 + (int)fr;  // table: the frame within the block
+        const int ph = (int)row, pw = (int)(rem - row * g.fWs.div);
 #pragma unroll
         for (int run = 0; run < 2; ++run) {
 #pragma unroll
@@ -496,8 +563,14 @@ __global__ __launch_bounds__(kKvThreads, 2) void sva_kv_proj_reduce_kernel(
             for (int pp = 0; pp < 4; ++pp) {
               const int ax = axis[run][pp];
               const int ps = ax == 0 ? pt : ax == 1 ? ph : pw;
-              const float turn = __builtin_amdgcn_fractf((float)ps * inv[run][pp]);
-              const float sn = __builtin_amdgcn_sinf(turn), cs = __builtin_amdgcn_cosf(turn);
+              float sn, cs;
+              if constexpr (kTab) {
+                const float2 e = rtab[eoff[run][pp] + ps * estr[run][pp]];
+                cs = e.x, sn = e.y;
+              } else {
+                const float turn = __builtin_amdgcn_fractf((float)ps * inv[run][pp]);
+                sn = __builtin_amdgcn_sinf(turn), cs = __builtin_amdgcn_cosf(turn);
+              }
               const float x = val[run][2 * pp], y = val[run][2 * pp + 1];
               val[run][2 * pp] = x * cs - y * sn;
               val[run][2 * pp + 1] = x * sn + y * cs;
@@ -694,6 +767,10 @@ sva_status sva_internal_proj_features(const sva_proj_desc* desc, const void* x, 
 
 hipError_t sva_internal_kv_proj_reduce(const SvaKvReduceArgs& a, const void* x, const void* wpack,
                                        const float* bias, float* partials, hipStream_t stream) {
+  // The kernel's pipeline carries the next tile's first stages through the
+  // epilogue in fixed registers, which takes an even stage count.
+  if (a.C % (2 * kTileK) != 0 || a.C < 2 * kTileK || a.H % 2 != 0 || a.L <= 0 || a.N % a.L != 0)
+    return hipErrorInvalidValue;
   KvGeo g;
   g.N = a.N;
   g.C = a.C;
@@ -708,15 +785,22 @@ hipError_t sva_internal_kv_proj_reduce(const SvaKvReduceArgs& a, const void* x, 
   g.nrg = a.B * g.ranges;
   g.Hs = a.Hs;
   g.Ws = a.Ws;
+  g.fHW = make_fastdiv((uint32_t)(a.Hs * a.Ws));
+  g.fWs = make_fastdiv((uint32_t)a.Ws);
   g.t0 = a.t0;
   g.rope = a.rope;
   g.dt = a.dt;
   g.dh = a.dh;
   g.log2_base = log2f(a.rope_base);
+  g.log2_base_d = log2((double)a.rope_base);
+  g.F = a.Nb / (a.Hs * a.Ws);
+  g.tab_entries = g.F * (a.dt / 2) + a.Hs * (a.dh / 2) + a.Ws * ((64 - a.dt - a.dh) / 2);
+  const bool tab = a.rope && g.tab_entries <= kRopeTab;
   const long long grid = ((long long)g.nrg + 7) / 8 * 8 * g.npairs;
   const uint8_t* wp = (const uint8_t*)wpack;
   void* args[] = {(void*)&x, (void*)&wp, (void*)&bias, (void*)&partials, &g};
-  return hipLaunchKernel((const void*)&sva_kv_proj_reduce_kernel, dim3((unsigned)grid), dim3(kKvThreads), args, 0,
+  const void* fn = tab ? (const void*)&sva_kv_proj_reduce_kernel<true> : (const void*)&sva_kv_proj_reduce_kernel<false>;
+  return hipLaunchKernel(fn, dim3((unsigned)grid), dim3(kKvThreads), args, 0,
                          stream);
 }
 

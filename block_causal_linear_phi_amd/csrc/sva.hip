@@ -29,6 +29,7 @@
 // video sizes.
 
 #include <hip/hip_runtime.h>
+#include <cstdlib>
 #include <stdint.h>
 #include <string.h>
 
@@ -65,26 +66,7 @@ constexpr int kMaxTableEntries = 4096; // RoPE cos/sin table, 32 KiB of LDS
 // Small integer helpers
 // ---------------------------------------------------------------------------
 
-// n / d for 0 <= n < 2^31 as (umulhi(n, mul) + n) >> shift, constants from
-// the round-up method (Granlund & Montgomery, "Division by invariant
-// integers using multiplication", 1994).
-struct FastDiv {
-  uint32_t mul, shift, div;
-};
-
-FastDiv make_fastdiv(uint32_t d) {
-  FastDiv f;
-  uint32_t s = 0;
-  while ((1ull << s) < d) ++s;
-  f.shift = s;
-  f.mul = (uint32_t)(((1ull << 32) * ((1ull << s) - d)) / d + 1);
-  f.div = d;
-  return f;
-}
-
-__device__ __forceinline__ uint32_t fdiv(uint32_t n, const FastDiv& f) {
-  return (__umulhi(n, f.mul) + n) >> f.shift;
-}
+// FastDiv (n / d by multiply and shift) is in internal.h.
 
 // ---------------------------------------------------------------------------
 // phi + 3D RoPE stage (shared by every kernel)
@@ -2263,7 +2245,7 @@ sva_status plan_proj_fwd(const sva_desc* a, const sva_proj_desc* pd, ProjPlan* p
   if (!pd) return SVA_ERR_INVALID_ARG;
   if (!p.bf16 || p.D != 64) return SVA_ERR_UNSUPPORTED;
   if (pd->B != a->B || pd->H != a->H || pd->d != a->d || pd->N != p.N) return SVA_ERR_INVALID_ARG;
-  if (a->H % 2 != 0 || pd->C % 128 != 0 || pd->C < 128) return SVA_ERR_UNSUPPORTED;
+  if (a->H % 2 != 0 || pd->C % 256 != 0 || pd->C < 256) return SVA_ERR_UNSUPPORTED;
   if (p.rope && (a->rope_dt % 2 != 0 || a->rope_dh % 2 != 0)) return SVA_ERR_UNSUPPORTED;
   // Range length L: a divisor of the block length (a range never straddles
   // a block), chosen for the k/v kernel's occupancy.  That kernel runs one
@@ -2285,6 +2267,11 @@ sva_status plan_proj_fwd(const sva_desc* a, const sva_proj_desc* pd, ProjPlan* p
       L = cand;
       best = cost;
     }
+  }
+  if (const char* e = getenv("SVA_PROJ_RANGE_TOKENS")) {  // explicit range length
+    const long long v = atoll(e);
+    if (v <= 0 || v > p.Nb || p.Nb % v != 0) return SVA_ERR_INVALID_ARG;
+    L = v;
   }
   pp->L = L;
   const long long total = (long long)p.BH * p.N;

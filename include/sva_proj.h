@@ -86,10 +86,16 @@ sva_status sva_qkv_proj_mxfp4(const sva_proj_desc* desc, const void* x, const vo
  * block KV cache segments).  q goes through the workspace.  The SANA-Video
  * article's 4-bit quantization paragraph motivates fusing the projection
  * into the attention.
- *   attn: bf16, d = 64, H even; proj: the same B, H, d, and N = T*Hs*Ws;
+ *   attn: bf16, d = 64, H even; proj: the same B, H, d, N = T*Hs*Ws, and
+ *   C a multiple of 256 (an even number of 128-channel stages);
  *   S0, z0, S_out, z_out, eps and RoPE as in sva_lin_attn_fwd.
  * SVA_ERR_UNSUPPORTED outside those limits or the projection's; the
- * workspace is sva_proj_lin_attn_fwd_workspace bytes. */
+ * workspace is sva_proj_lin_attn_fwd_workspace bytes.
+ * The tokens are reduced in ranges of L tokens that divide the block
+ * length, one workgroup per (range, head pair); L is chosen for occupancy
+ * unless the environment variable SVA_PROJ_RANGE_TOKENS gives it (a divisor
+ * of the block length, else SVA_ERR_INVALID_ARG).  The workspace size
+ * depends on L: query it under the same setting. */
 sva_status sva_proj_lin_attn_fwd_workspace(const sva_desc* attn, const sva_proj_desc* proj, size_t* bytes);
 sva_status sva_proj_lin_attn_fwd(const sva_desc* attn, const sva_proj_desc* proj, const void* x,
                                  const void* wpack, const float* bias, void* out, const float* S0,

@@ -319,3 +319,25 @@ def test_pack_checks_happen_before_launch():
     assert ok(Cd, S, P + 8) == inv                       # misaligned output
     assert ok(Cd, S, Cd + 4096) == inv                   # output over the codes
     assert ok(Cd, S, S - 4096) == inv                    # output over the scales
+
+def test_fused_workspace_checks(monkeypatch):
+    """The fused projection + attention takes an even number of 128-channel
+    stages and an explicit range length only where it divides the block."""
+    lib = sva.lib()
+    grid, F = (21, 45, 80), 3
+    fdesc = sva.make_desc(1, 16, 64, grid, F, dtype=sva.SVA_BF16, rope=True, split=(16, 24, 24))
+
+    def query(C):
+        n = ctypes.c_size_t()
+        pdesc = sva.SvaProjDesc(1, 21 * 45 * 80, C, 16, 64)
+        return lib.sva_proj_lin_attn_fwd_workspace(ctypes.byref(fdesc), ctypes.byref(pdesc), ctypes.byref(n)), n.value
+
+    st, auto_bytes = query(1024)
+    assert st == sva.SVA_OK and auto_bytes > 0
+    assert query(384)[0] == sva.SVA_ERR_UNSUPPORTED   # three stages
+    assert query(128)[0] == sva.SVA_ERR_UNSUPPORTED
+    monkeypatch.setenv("SVA_PROJ_RANGE_TOKENS", "1800")  # divides 3 * 45 * 80
+    st, long_bytes = query(1024)
+    assert st == sva.SVA_OK and long_bytes < auto_bytes  # fewer partials
+    monkeypatch.setenv("SVA_PROJ_RANGE_TOKENS", "1000")
+    assert query(1024)[0] == sva.SVA_ERR_INVALID_ARG

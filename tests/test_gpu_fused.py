@@ -39,18 +39,31 @@ def _weights(n_out, C, seed):
 
 # (name, B, H, grid, F, C, split or None, t0, bias, initial cache)
 CASES = [
-    ("ragged_tiles", 1, 2, (6, 5, 7), 3, 128, (16, 24, 24), 3, True, False),
+    ("ragged_tiles", 1, 2, (6, 5, 7), 3, 256, (16, 24, 24), 3, True, False),
     ("two_samples", 2, 4, (4, 8, 9), 2, 256, (16, 24, 24), 0, False, False),
-    ("no_rope", 1, 2, (3, 10, 10), 1, 128, None, 0, True, False),
-    ("cache_in_place", 1, 2, (4, 6, 7), 2, 384, (8, 28, 28), 6, True, True),
+    ("no_rope", 1, 2, (3, 10, 10), 1, 512, None, 0, True, False),
+    ("cache_in_place", 1, 2, (4, 6, 7), 2, 768, (8, 28, 28), 6, True, True),
+    ("long_ranges", 1, 2, (2, 40, 41), 2, 256, (16, 24, 24), 0, True, False),
+    # RoPE table (F dt/2 + Hs dh/2 + Ws dw/2 entries) past the kernel's LDS
+    # budget: angles on the fly
+    ("wide_rows", 1, 2, (2, 3, 300), 1, 256, (16, 24, 24), 11, True, False),
 ]
 
 
+def _long_range(Nb):
+    """The largest divisor of the block length up to 2048 tokens: ranges of
+    many 64-token tiles, the last one ragged where 64 does not divide it."""
+    return max(L for L in range(1, min(Nb, 2048) + 1) if Nb % L == 0)
+
+
+@pytest.mark.parametrize("ranges", ["auto", "long"])
 @pytest.mark.parametrize("case", CASES, ids=[c[0] for c in CASES])
-def test_fused_small(case):
+def test_fused_small(case, ranges, monkeypatch):
     name, B, H, grid, F, C, split, t0, with_bias, cache = case
-    _say(f"fused {name}")
     N = grid[0] * grid[1] * grid[2]
+    if ranges == "long":
+        monkeypatch.setenv("SVA_PROJ_RANGE_TOKENS", str(_long_range(F * grid[1] * grid[2])))
+    _say(f"fused {name} ranges {ranges}")
     xv, xraw = wl.draw((B, N, C), 301, 1.0, "bf16")
     codes, scales, cd, sd = _weights(3 * H * 64, C, 302)
     wp = sva.sva_mxfp4_pack_weights(cd, sd, H, 64)
