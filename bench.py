@@ -795,7 +795,7 @@ def main():
         try:
             with open(traffic_file(tw.name)) as f:
                 prof = json.load(f)
-            if prof.get("source_sha256") == source_sha256() and "tconv" in prof.get("per_launch", {}):
+            if prof.get("source_sha256") == source_sha256(TCONV_SRC) and "tconv" in prof.get("per_launch", {}):
                 line["roofline"]["traffic"] = prof["per_launch"]["tconv"]["bytes"] / 1e9
         except (OSError, ValueError):
             pass
