@@ -1,6 +1,7 @@
 // Internal interfaces between the library's source files (not part of the
-// C ABI): the projection file's launchers that the fused projection +
-// attention entry point in sva.hip drives.
+// C ABI): division by run-time constants, and the projection file's
+// launchers that the fused projection + attention entry point in sva.hip
+// drives.
 #ifndef SVA_INTERNAL_H
 #define SVA_INTERNAL_H
 

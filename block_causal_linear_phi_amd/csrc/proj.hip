@@ -138,6 +138,13 @@ struct WRegs {
   uint32_t s;
 };
 
+// The fused k, v kernel's: two row tiles of a k block and two of a v block,
+// each block with its own scale word.
+struct KvWRegs {
+  uint4 c[4];
+  uint32_t sk, sv;
+};
+
 __device__ __forceinline__ uint32_t pack2(float a, float b) {
   const pj_bf16x2 v = {(__bf16)a, (__bf16)b};  // round to nearest even
   return __builtin_bit_cast(uint32_t, v);
@@ -315,9 +322,15 @@ __global__ __launch_bounds__(kPjThreads, 2) void sva_qkv_proj_kernel(
 // go to the partial slot the block scan reads for (range, block): slot g + bhc
 // with g the range's index along the flattened (b, h, token) axis in units
 // of L.  So k and v never reach HBM.
+//
+// The GEMM pipeline runs on across the tiles of a range (the next tile's
+// first x and weight stages load during the epilogue), the bias sits in LDS,
+// and RoPE reads cos/sin from a per-workgroup LDS table of the positions the
+// range can hold (kTab), or computes them on the fly for grids whose table
+// would not fit beside two workgroups per CU.
 // ---------------------------------------------------------------------------
 
-constexpr int kKvThreads = 256;  // waves: k(h0), v(h0), k(h0+1), v(h0+1)
+constexpr int kKvThreads = 256;  // waves: (h0, half 0), (h0, half 1), (h0+1, 0), (h0+1, 1)
 static_assert(kKvThreads == kPjThreads, "the GEMM part assumes the projection's workgroup size");
 
 // A wave's 64 x 64 bf16 tile, transposed: feature row f (128 bytes = 64
@@ -354,18 +367,24 @@ __global__ __launch_bounds__(kKvThreads, 2) void sva_kv_proj_reduce_kernel(
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int lane = tid & 63;
   const int lg = lane >> 4, lr = lane & 15;
-  const int kind = wave & 1;                 // 0: k, 1: v
+  // A wave computes features 32 half .. + 31 of both k and v of its head
+  // (row tiles 2 half, 2 half + 1 of each packed 64-row block), so that
+  // every wave takes an equal share of the epilogue's phi and RoPE.
+  const int half = wave & 1;
   const int head = 2 * pair + (wave >> 1);
-  const int blk = (1 + kind) * g.H + head;   // packed 64-row block (d = 64)
-  const uint8_t* cbase = wpack + ((size_t)blk * g.stages * 4) * 1024 + lane * 16;
-  const uint8_t* sbase = wpack + (size_t)g.n_pack * (g.C / 2) + ((size_t)blk * g.stages * 64 + lane) * 4;
+  const int blk_k = g.H + head, blk_v = 2 * g.H + head;
+  // the v block lies H blocks past the k block (offsets uniform over the wave)
+  const uint8_t* cbase = wpack + ((size_t)blk_k * g.stages * 4 + 2 * half) * 1024 + lane * 16;
+  const uint8_t* sbase = wpack + (size_t)g.n_pack * (g.C / 2) + ((size_t)blk_k * g.stages * 64 + lane) * 4;
+  const size_t cvoff = (size_t)g.H * g.stages * 4 * 1024, svoff = (size_t)g.H * g.stages * 256;
+  const int sshift = 16 * half;  // the scale bytes of row tiles 2 half, 2 half + 1
   const size_t row_bytes = (size_t)g.C * 2;
   const long long M = (long long)(g.nrg / g.ranges) * g.N;  // B * N rows of x
 
 #pragma unroll
   for (int k = 0; k < 8; ++k) sacc[wave][k][lane] = pj_floatx4{0.f, 0.f, 0.f, 0.f};
   if (tid < 128) zs[tid >> 6][tid & 63] = 0.f;
-  bs[wave][lane] = bias ? bias[blk * 64 + lane] : 0.f;
+  bs[wave][lane] = bias ? bias[(lane < 32 ? blk_k : blk_v) * 64 + 32 * half + (lane & 31)] : 0.f;
   const int ht = g.dt >> 1, hh = g.dh >> 1, hwd = (64 - g.dt - g.dh) >> 1;
   const int off_h = g.F * ht, off_w = off_h + g.Hs * hh;
   if constexpr (kTab) {
@@ -411,10 +430,13 @@ __global__ __launch_bounds__(kKvThreads, 2) void sva_kv_proj_reduce_kernel(
       xs[buf][sw(u / kPieces, u % kPieces)] = rg4[j];
     }
   };
-  auto load_w = [&](WRegs& w, int s) {
+  // accumulators 0, 1: k row tiles; 2, 3: v row tiles
+  auto load_w = [&](KvWRegs& w, int s) {
 #pragma unroll
-    for (int rt = 0; rt < 4; ++rt) w.c[rt] = *(const uint4*)(cbase + ((size_t)s * 4 + rt) * 1024);
-    w.s = *(const uint32_t*)(sbase + (size_t)s * 256);
+    for (int rt = 0; rt < 4; ++rt)
+      w.c[rt] = *(const uint4*)(cbase + (rt < 2 ? 0 : cvoff) + ((size_t)s * 4 + (rt & 1)) * 1024);
+    w.sk = *(const uint32_t*)(sbase + (size_t)s * 256);
+    w.sv = *(const uint32_t*)(sbase + svoff + (size_t)s * 256);
   };
 
   // The GEMM pipeline runs on across tiles: the last steps of a tile load
@@ -423,7 +445,7 @@ __global__ __launch_bounds__(kKvThreads, 2) void sva_kv_proj_reduce_kernel(
   // x0, x1 and w0, where the prologue expects them).
   const int last = g.stages - 1;
   uint4 x0[kXLoads], x1[kXLoads];
-  WRegs w0, w1;
+  KvWRegs w0, w1;
   load_w(w0, 0);
   {
     const __amdgpu_buffer_rsrc_t xr0 = tile_rsrc(0);
@@ -443,9 +465,11 @@ __global__ __launch_bounds__(kKvThreads, 2) void sva_kv_proj_reduce_kernel(
     for (int i = 0; i < 4; ++i)
 #pragma unroll
       for (int j = 0; j < 4; ++j) acc[i][j] = pj_floatx4{0.f, 0.f, 0.f, 0.f};
-    auto compute = [&](const WRegs& w, int buf) {
-      uint32_t e = w.s;
-      asm volatile("" : "+v"(e));  // see the projection kernel
+    auto compute = [&](const KvWRegs& w, int buf) {
+      uint32_t ek = w.sk, ev = w.sv;
+      asm volatile("" : "+v"(ek));  // see the projection kernel
+      asm volatile("" : "+v"(ev));
+      const uint32_t e = ((ek >> sshift) & 0xffffu) | ((ev >> sshift) << 16);
       float sc[4];
 #pragma unroll
       for (int rt = 0; rt < 4; ++rt) sc[rt] = e8m0_scale((e >> (8 * rt)) & 0xffu);
@@ -471,7 +495,7 @@ __global__ __launch_bounds__(kKvThreads, 2) void sva_kv_proj_reduce_kernel(
     store_x(x0, 0);
     load_v(x0, 2);
     __syncthreads();
-    auto step = [&](int s, const WRegs& wc, WRegs& wn_, uint4 (&xn)[kXLoads]) {
+    auto step = [&](int s, const KvWRegs& wc, KvWRegs& wn_, uint4 (&xn)[kXLoads]) {
       load_w(wn_, s + 1);
       __builtin_amdgcn_sched_barrier(0);
       compute(wc, s & 1);
@@ -508,101 +532,91 @@ __global__ __launch_bounds__(kKvThreads, 2) void sva_kv_proj_reduce_kernel(
     for (int run = 0; run < 2; ++run)
 #pragma unroll
       for (int i = 0; i < 8; ++i) bb[run][i] = bs[wave][32 * run + 8 * lgv + i];
-    // RoPE of the lane's 8 pairs: the axis, and either the table entry of
-    // position 0 and the entries per position step, or base^(-2i/width)/(2 pi)
-    float inv[2][4];
-    int axis[2][4], eoff[2][4], estr[2][4];
+    // RoPE of the lane's 4 k pairs (features 32 half + 8 lg + 0..7 of the
+    // head): the axis, and either the table entry of position 0 and the
+    // entries per position step, or base^(-2i/width)/(2 pi)
+    float inv[4];
+    int axis[4], eoff[4], estr[4];
 #pragma unroll
-    for (int run = 0; run < 2; ++run)
-#pragma unroll
-      for (int pp = 0; pp < 4; ++pp) {
-        const int f = 32 * run + 8 * lgv + 2 * pp;
-        const int ax = f < g.dt ? 0 : f < g.dt + g.dh ? 1 : 2;
-        const int start = ax == 0 ? 0 : ax == 1 ? g.dt : g.dt + g.dh;
-        const int width = ax == 0 ? g.dt : ax == 1 ? g.dh : 64 - g.dt - g.dh;
-        axis[run][pp] = ax;
-        if constexpr (kTab) {
-          eoff[run][pp] = (ax == 0 ? 0 : ax == 1 ? off_h : off_w) + ((f - start) >> 1);
-          estr[run][pp] = width >> 1;
-        } else {
-          inv[run][pp] = exp2f(-(float)(f - start) / (float)width * g.log2_base) * 0.15915494309189535f;
-        }
+    for (int pp = 0; pp < 4; ++pp) {
+      const int f = 32 * half + 8 * lgv + 2 * pp;
+      const int ax = f < g.dt ? 0 : f < g.dt + g.dh ? 1 : 2;
+      const int start = ax == 0 ? 0 : ax == 1 ? g.dt : g.dt + g.dh;
+      const int width = ax == 0 ? g.dt : ax == 1 ? g.dh : 64 - g.dt - g.dh;
+      axis[pp] = ax;
+      if constexpr (kTab) {
+        eoff[pp] = (ax == 0 ? 0 : ax == 1 ? off_h : off_w) + ((f - start) >> 1);
+        estr[pp] = width >> 1;
+      } else {
+        inv[pp] = exp2f(-(float)(f - start) / (float)width * g.log2_base) * 0.15915494309189535f;
       }
-    float zt[2][8];
+    }
+    float zt[8];
 #pragma unroll
-    for (int run = 0; run < 2; ++run)
-#pragma unroll
-      for (int i = 0; i < 8; ++i) zt[run][i] = 0.f;
-    char* tile = reinterpret_cast<char*>(kvt + wave * 512);
+    for (int i = 0; i < 8; ++i) zt[i] = 0.f;
+    // k rows to the head's k tile, v rows to its v tile
+    char* const ktile = reinterpret_cast<char*>(kvt + (wave & 2) * 512);
+    char* const vtile = reinterpret_cast<char*>(kvt + ((wave & 2) + 1) * 512);
 #pragma unroll
     for (int tt = 0; tt < 4; ++tt) {
       const int tok = 16 * tt + lr;
       const int n = n0 + tok;
       const bool valid = n < n_end;
-      float val[2][8];
+      float val[2][8];  // [0]: k, [1]: v
 #pragma unroll
       for (int run = 0; run < 2; ++run)
 #pragma unroll
         for (int i = 0; i < 8; ++i)
           val[run][i] = (float)(__bf16)(acc[2 * run + (i >> 2)][tt][i & 3] + bb[run][i]);
-      if (kind == 0) {
-        const uint32_t np = (uint32_t)(valid ? n : n_end - 1);  // positions past the range: any in it
-        const uint32_t fr = fdiv(np, g.fHW), rem = np - fr * g.fHW.div;
-        const uint32_t row = fdiv(rem, g.fWs);
-        const int pt = kTab ? (int)fr - c * g.F : g.t0 + (int)fr;  // table: the frame within the block
-        const int ph = (int)row, pw = (int)(rem - row * g.fWs.div);
+      const uint32_t np = (uint32_t)(valid ? n : n_end - 1);  // positions past the range: any in it
+      const uint32_t fr = fdiv(np, g.fHW), rem = np - fr * g.fHW.div;
+      const uint32_t row = fdiv(rem, g.fWs);
+      const int pt = kTab ? (int)fr - c * g.F : g.t0 + (int)fr;  // table: the frame within the block
+      const int ph = (int)row, pw = (int)(rem - row * g.fWs.div);
 #pragma unroll
-        for (int run = 0; run < 2; ++run) {
+      for (int i = 0; i < 8; ++i) {
+        val[0][i] = fmaxf(val[0][i], 0.f);
+        zt[i] += valid ? val[0][i] : 0.f;
+      }
+      if (g.rope) {
 #pragma unroll
-          for (int i = 0; i < 8; ++i) {
-            val[run][i] = fmaxf(val[run][i], 0.f);
-            zt[run][i] += valid ? val[run][i] : 0.f;
+        for (int pp = 0; pp < 4; ++pp) {
+          const int ax = axis[pp];
+          const int ps = ax == 0 ? pt : ax == 1 ? ph : pw;
+          float sn, cs;
+          if constexpr (kTab) {
+            const float2 e = rtab[eoff[pp] + ps * estr[pp]];
+            cs = e.x, sn = e.y;
+          } else {
+            const float turn = __builtin_amdgcn_fractf((float)ps * inv[pp]);
+            sn = __builtin_amdgcn_sinf(turn), cs = __builtin_amdgcn_cosf(turn);
           }
-          if (g.rope) {
-#pragma unroll
-            for (int pp = 0; pp < 4; ++pp) {
-              const int ax = axis[run][pp];
-              const int ps = ax == 0 ? pt : ax == 1 ? ph : pw;
-              float sn, cs;
-              if constexpr (kTab) {
-                const float2 e = rtab[eoff[run][pp] + ps * estr[run][pp]];
-                cs = e.x, sn = e.y;
-              } else {
-                const float turn = __builtin_amdgcn_fractf((float)ps * inv[run][pp]);
-                sn = __builtin_amdgcn_sinf(turn), cs = __builtin_amdgcn_cosf(turn);
-              }
-              const float x = val[run][2 * pp], y = val[run][2 * pp + 1];
-              val[run][2 * pp] = x * cs - y * sn;
-              val[run][2 * pp + 1] = x * sn + y * cs;
-            }
-          }
+          const float x = val[0][2 * pp], y = val[0][2 * pp + 1];
+          val[0][2 * pp] = x * cs - y * sn;
+          val[0][2 * pp + 1] = x * sn + y * cs;
         }
       }
 #pragma unroll
       for (int run = 0; run < 2; ++run)
 #pragma unroll
         for (int i = 0; i < 8; ++i) {
-          const int f = 32 * run + 8 * lg + i;
+          const int f = 32 * half + 8 * lg + i;
           const __bf16 h = (__bf16)(valid ? val[run][i] : 0.f);
-          *reinterpret_cast<__bf16*>(tile + kv_piece(f, tok >> 3) * 16 + (tok & 7) * 2) = h;
+          *reinterpret_cast<__bf16*>((run ? vtile : ktile) + kv_piece(f, tok >> 3) * 16 + (tok & 7) * 2) = h;
         }
     }
-    if (kind == 0) {
-      // the tile's normaliser share, summed over the 16 token lanes
+    // the tile's normaliser share, summed over the 16 token lanes
 #pragma unroll
-      for (int run = 0; run < 2; ++run)
-#pragma unroll
-        for (int i = 0; i < 8; ++i) {
-          float t = zt[run][i];
-          t += __shfl_xor(t, 1);
-          t += __shfl_xor(t, 2);
-          t += __shfl_xor(t, 4);
-          t += __shfl_xor(t, 8);
-          if (lr == 0) zs[wave >> 1][32 * run + 8 * lg + i] += t;
-        }
+    for (int i = 0; i < 8; ++i) {
+      float t = zt[i];
+      t += __shfl_xor(t, 1);
+      t += __shfl_xor(t, 2);
+      t += __shfl_xor(t, 4);
+      t += __shfl_xor(t, 8);
+      if (lr == 0) zs[wave >> 1][32 * half + 8 * lg + i] += t;
     }
     __syncthreads();
-    // State rows (value features) 32 (1 - kind) .. + 31 of this wave's head:
+    // State rows (value features) 32 half .. + 31 of this wave's head:
     // S^T[fo][fi] += sum over the tile's tokens of v[fo] RoPE(phi k)[fi].
     const uint4* vt = kvt + ((wave & 2) + 1) * 512;
     const uint4* kt = kvt + (wave & 2) * 512;
@@ -615,7 +629,7 @@ __global__ __launch_bounds__(kKvThreads, 2) void sva_kv_proj_reduce_kernel(
     for (int ks = 0; ks < 2; ++ks) {
       uint4 a[2], bo[4];
 #pragma unroll
-      for (int ft = 0; ft < 2; ++ft) a[ft] = vt[kv_piece(16 * (2 * (1 - kind) + ft) + lr, 4 * ks + lg)];
+      for (int ft = 0; ft < 2; ++ft) a[ft] = vt[kv_piece(16 * (2 * half + ft) + lr, 4 * ks + lg)];
 #pragma unroll
       for (int fc = 0; fc < 4; ++fc) bo[fc] = kt[kv_piece(16 * fc + lr, 4 * ks + lg)];
 #pragma unroll
@@ -641,9 +655,9 @@ __global__ __launch_bounds__(kKvThreads, 2) void sva_kv_proj_reduce_kernel(
     for (int fc = 0; fc < 4; ++fc) {
       const pj_floatx4 v4 = sacc[wave][4 * ft + fc][lane];
 #pragma unroll
-      for (int i = 0; i < 4; ++i) dst[(16 * (2 * (1 - kind) + ft) + 4 * lg + i) * 64 + 16 * fc + lr] = v4[i];
+      for (int i = 0; i < 4; ++i) dst[(16 * (2 * half + ft) + 4 * lg + i) * 64 + 16 * fc + lr] = v4[i];
     }
-  if (kind == 0) dst[64 * 64 + lane] = zs[wave >> 1][lane];
+  if (half == 0) dst[64 * 64 + lane] = zs[wave >> 1][lane];
 }
 
 // Repacks natural-layout MXFP4 weights (codes [n_out, C/2], scales
