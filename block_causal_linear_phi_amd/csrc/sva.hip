@@ -2309,7 +2309,15 @@ sva_status run_proj_fwd(const sva_desc* a, const sva_proj_desc* pd, const void* 
   if (!ws || ws_bytes < pp.bytes || !is_aligned16(ws)) return SVA_ERR_WORKSPACE;
   const size_t nbytes = qkv_bytes(p);
   const size_t xbytes = (size_t)pd->B * pd->N * pd->C * 2;
-  if (overlaps(out, nbytes, x, xbytes) || overlaps(out, nbytes, ws, ws_bytes)) return SVA_ERR_INVALID_ARG;
+  const size_t n_out = (size_t)3 * pd->H * pd->d;
+  const size_t wbytes = n_out * pd->C / 2 + n_out * pd->C / 32;  // codes, then the scale words
+  const size_t s_bytes = (size_t)p.BH * p.D * p.D * sizeof(float), z_bytes = (size_t)p.BH * p.D * sizeof(float);
+  if (overlaps(out, nbytes, x, xbytes) || overlaps(out, nbytes, ws, ws_bytes) ||
+      overlaps(out, nbytes, wpack, wbytes) || overlaps(ws, ws_bytes, x, xbytes) ||
+      overlaps(ws, ws_bytes, wpack, wbytes) || (bias && overlaps(ws, ws_bytes, bias, n_out * sizeof(float))) ||
+      (S_out && (overlaps(S_out, s_bytes, ws, ws_bytes) || overlaps(S_out, s_bytes, out, nbytes) ||
+                 overlaps(z_out, z_bytes, ws, ws_bytes) || overlaps(z_out, z_bytes, out, nbytes))))
+    return SVA_ERR_INVALID_ARG;
   char* wsb = (char*)ws;
   void* q = wsb + pp.off_q;
   float* partials = (float*)(wsb + pp.off_partials);

@@ -341,3 +341,37 @@ def test_fused_workspace_checks(monkeypatch):
     assert st == sva.SVA_OK and long_bytes < auto_bytes  # fewer partials
     monkeypatch.setenv("SVA_PROJ_RANGE_TOKENS", "1000")
     assert query(1024)[0] == sva.SVA_ERR_INVALID_ARG
+
+
+@fake_pointers
+def test_fused_pointer_checks_happen_before_launch():
+    """The fused projection + attention validates every pointer, the
+    workspace and the overlaps before any launch (fake device addresses)."""
+    lib = sva.lib()
+    grid, F, H, C = (21, 45, 80), 3, 16, 1024
+    N = grid[0] * grid[1] * grid[2]
+    fdesc = sva.make_desc(1, H, 64, grid, F, dtype=sva.SVA_BF16, rope=True, split=(16, 24, 24))
+    pdesc = sva.SvaProjDesc(1, N, C, H, 64)
+    n = ctypes.c_size_t()
+    assert lib.sva_proj_lin_attn_fwd_workspace(ctypes.byref(fdesc), ctypes.byref(pdesc), ctypes.byref(n)) == sva.SVA_OK
+    X, W, O, WS = 1 << 36, 1 << 37, 1 << 38, 1 << 39   # x, packed weights, out, workspace
+    inv = sva.SVA_ERR_INVALID_ARG
+
+    def call(x=X, w=W, out=O, ws=WS, ws_bytes=None, bias=None, S=None, z=None):
+        return lib.sva_proj_lin_attn_fwd(ctypes.byref(fdesc), ctypes.byref(pdesc), x, w, bias, out, None, None,
+                                         S, z, ws, n.value if ws_bytes is None else ws_bytes, None)
+
+    assert call(x=None) == inv
+    assert call(w=None) == inv
+    assert call(out=None) == inv
+    assert call(x=X + 8) == inv                              # misaligned
+    assert call(bias=8) == inv
+    assert call(S=1 << 40, z=None) == inv                    # S_out without z_out
+    assert call(ws=None) == sva.SVA_ERR_WORKSPACE
+    assert call(ws_bytes=n.value - 16) == sva.SVA_ERR_WORKSPACE
+    assert call(out=X + 4096) == inv                         # out over x
+    assert call(out=W + 4096) == inv                         # out over the weights
+    assert call(ws=X + 4096) == inv                          # workspace over x
+    assert call(ws=W + 4096) == inv                          # workspace over the weights
+    assert call(ws=O + 4096) == inv                          # workspace over out
+    assert call(S=WS + 4096, z=1 << 41) == inv               # cache over the workspace
