@@ -369,10 +369,11 @@ def proj_leg(w, steps: int, warmup: int, sets: int):
 
     dev = torch.device("cuda:0")
     x0 = torch.empty((w.B, w.N, w.C), dtype=torch.bfloat16, device=dev)
-    for j, s0 in enumerate(range(0, w.N, 4096)):
-        n = min(4096, w.N - s0)
-        _, raw = wl.draw((n, w.C), wl.seed_for(w.name, "x", 0, j), 1.0, "bf16")
-        x0[0, s0:s0 + n].copy_(torch.from_numpy(raw.view("int16")).view(torch.bfloat16))
+    for bi in range(w.B):
+        for j, s0 in enumerate(range(0, w.N, 4096)):
+            n = min(4096, w.N - s0)
+            _, raw = wl.draw((n, w.C), wl.seed_for(w.name, "x", bi, j), 1.0, "bf16")
+            x0[bi, s0:s0 + n].copy_(torch.from_numpy(raw.view("int16")).view(torch.bfloat16))
     codes, scales = wl.mxfp4_weights(w.n_out, w.C, wl.seed_for(w.name, "w", 0, 0))
     cd = torch.from_numpy(wl.pack_nibbles(codes)).to(dev)
     sd = torch.from_numpy(scales).to(dev)
@@ -411,10 +412,11 @@ def fused_leg(w, aw, steps: int, warmup: int, sets: int):
 
     dev = torch.device("cuda:0")
     x0 = torch.empty((w.B, w.N, w.C), dtype=torch.bfloat16, device=dev)
-    for j, s0 in enumerate(range(0, w.N, 4096)):
-        n = min(4096, w.N - s0)
-        _, raw = wl.draw((n, w.C), wl.seed_for(w.name, "x", 0, j), 1.0, "bf16")
-        x0[0, s0:s0 + n].copy_(torch.from_numpy(raw.view("int16")).view(torch.bfloat16))
+    for bi in range(w.B):
+        for j, s0 in enumerate(range(0, w.N, 4096)):
+            n = min(4096, w.N - s0)
+            _, raw = wl.draw((n, w.C), wl.seed_for(w.name, "x", bi, j), 1.0, "bf16")
+            x0[bi, s0:s0 + n].copy_(torch.from_numpy(raw.view("int16")).view(torch.bfloat16))
     codes, scales = wl.mxfp4_weights(w.n_out, w.C, wl.seed_for(w.name, "w", 0, 0))
     wp = sva.sva_mxfp4_pack_weights(torch.from_numpy(wl.pack_nibbles(codes)).to(dev),
                                     torch.from_numpy(scales).to(dev), w.H, w.d)

@@ -195,6 +195,8 @@ class ProjWorkload:
 
 PROJ_WORKLOADS = {
     "proj_720p": ProjWorkload("proj_720p", B=1, N=75600, C=1024, H=16, d=64),
+    "proj_480p": ProjWorkload("proj_480p", B=1, N=32760, C=1024, H=16, d=64),
+    "proj_minute": ProjWorkload("proj_minute", B=2, N=374400, C=1024, H=16, d=64),
 }
 
 
