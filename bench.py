@@ -431,8 +431,8 @@ def fused_leg(w, aw, steps: int, warmup: int, sets: int):
     n = ctypes.c_size_t()
     sva._check(sva.lib().sva_proj_lin_attn_fwd_workspace(ctypes.byref(fdesc), ctypes.byref(pdesc), ctypes.byref(n)),
                "sva_proj_lin_attn_fwd_workspace")
-    fws = torch.empty(n.value, dtype=torch.uint8, device=dev)
-    aws = torch.empty(sva.sva_lin_attn_fwd_workspace(fdesc), dtype=torch.uint8, device=dev)
+    fws = torch.zeros(n.value, dtype=torch.uint8, device=dev)
+    aws = torch.zeros(sva.sva_lin_attn_fwd_workspace(fdesc), dtype=torch.uint8, device=dev)
     stream = torch.cuda.current_stream()
 
     def fused(i):

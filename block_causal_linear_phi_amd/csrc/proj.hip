@@ -79,8 +79,7 @@ struct KvGeo {
   FastDiv fHW, fWs; // division by Hs * Ws and by Ws
   int Hs, Ws, t0;   // latent grid rows and columns, first frame
   int rope, dt, dh; // RoPE on, t and h axis widths (w takes the rest)
-  float log2_base;  // log2 of the RoPE base
-  double log2_base_d;
+  double log2_base_d;  // log2 of the RoPE base
   int F;            // frames per block
   int tab_entries;  // F dt/2 + Hs dh/2 + Ws dw/2 (the RoPE table's size)
 };
@@ -535,7 +534,10 @@ __global__ __launch_bounds__(kKvThreads, 2) void sva_kv_proj_reduce_kernel(
     // RoPE of the lane's 4 k pairs (features 32 half + 8 lg + 0..7 of the
     // head): the axis, and either the table entry of position 0 and the
     // entries per position step, or base^(-2i/width)/(2 pi)
-    float inv[4];
+    // On the fly, the turn of a frame pair is that of the block's first
+    // frame (reduced in fp64, so that large absolute frame indices keep
+    // their precision) plus the local frame times the frequency.
+    float inv[4], tbase[4];
     int axis[4], eoff[4], estr[4];
 #pragma unroll
     for (int pp = 0; pp < 4; ++pp) {
@@ -548,7 +550,11 @@ __global__ __launch_bounds__(kKvThreads, 2) void sva_kv_proj_reduce_kernel(
         eoff[pp] = (ax == 0 ? 0 : ax == 1 ? off_h : off_w) + ((f - start) >> 1);
         estr[pp] = width >> 1;
       } else {
-        inv[pp] = exp2f(-(float)(f - start) / (float)width * g.log2_base) * 0.15915494309189535f;
+        const double inv_d = exp2(-(double)(f - start) / (double)width * g.log2_base_d) * 0.15915494309189535;
+        double tb = ax == 0 ? (double)(g.t0 + c * g.F) * inv_d : 0.0;
+        tb -= rint(tb);
+        inv[pp] = (float)inv_d;
+        tbase[pp] = (float)tb;
       }
     }
     float zt[8];
@@ -571,11 +577,14 @@ __global__ __launch_bounds__(kKvThreads, 2) void sva_kv_proj_reduce_kernel(
       const uint32_t np = (uint32_t)(valid ? n : n_end - 1);  // positions past the range: any in it
       const uint32_t fr = fdiv(np, g.fHW), rem = np - fr * g.fHW.div;
       const uint32_t row = fdiv(rem, g.fWs);
-      const int pt = kTab ? (int)fr - c * g.F : g.t0 + (int)fr;  // table: the frame within the block
+      const int pt = (int)fr - c * g.F;  // the frame within the block
       const int ph = (int)row, pw = (int)(rem - row * g.fWs.div);
 #pragma unroll
       for (int i = 0; i < 8; ++i) {
-        val[0][i] = fmaxf(val[0][i], 0.f);
+        // phi on the bit pattern, as in the attention kernels: every value
+        // with the sign bit set (negative numbers, -0, a negative-signed
+        // NaN) becomes +0, every other value passes unchanged
+        val[0][i] = __int_as_float(max(__float_as_int(val[0][i]), 0));
         zt[i] += valid ? val[0][i] : 0.f;
       }
       if (g.rope) {
@@ -588,7 +597,7 @@ __global__ __launch_bounds__(kKvThreads, 2) void sva_kv_proj_reduce_kernel(
             const float2 e = rtab[eoff[pp] + ps * estr[pp]];
             cs = e.x, sn = e.y;
           } else {
-            const float turn = __builtin_amdgcn_fractf((float)ps * inv[pp]);
+            const float turn = __builtin_amdgcn_fractf(tbase[pp] + (float)ps * inv[pp]);
             sn = __builtin_amdgcn_sinf(turn), cs = __builtin_amdgcn_cosf(turn);
           }
           const float x = val[0][2 * pp], y = val[0][2 * pp + 1];
@@ -805,7 +814,6 @@ hipError_t sva_internal_kv_proj_reduce(const SvaKvReduceArgs& a, const void* x, 
   g.rope = a.rope;
   g.dt = a.dt;
   g.dh = a.dh;
-  g.log2_base = log2f(a.rope_base);
   g.log2_base_d = log2((double)a.rope_base);
   g.F = a.Nb / (a.Hs * a.Ws);
   g.tab_entries = g.F * (a.dt / 2) + a.Hs * (a.dh / 2) + a.Ws * ((64 - a.dt - a.dh) / 2);

@@ -29,7 +29,6 @@
 // video sizes.
 
 #include <hip/hip_runtime.h>
-#include <cstdlib>
 #include <stdint.h>
 #include <string.h>
 
@@ -82,8 +81,31 @@ struct RopeArgs {
   int off_h, off_w, n_entries;
   int t0;               // global frame of the call's first frame
   int F;                // frames per block (rows of the t part)
+  FastDiv fht, fhh, fhw;  // division by dt/2, dh/2, dw/2 (1 for an empty axis)
   double inv_rev[32];   // base^(-2i/d_a) / (2 pi), indexed by global pair p
 };
+
+// The frequencies reach the table build through registers: lane l of every
+// wave holds that of global pair l % 32, picked from the kernel arguments
+// with uniform (scalar) reads at kernel start, and the build takes a pair's
+// value from its lane with ds_bpermute.  An indexed read of the
+// kernel-argument array inside the build would be a vector memory round trip
+// per entry, and since vector loads complete in issue order, each would also
+// wait for every streaming load in flight.
+__device__ __forceinline__ double load_lane_freq(const RopeArgs& ra) {
+  const int p = threadIdx.x & 31;
+  double f = ra.inv_rev[0];
+#pragma unroll
+  for (int i = 1; i < 32; ++i) f = p == i ? ra.inv_rev[i] : f;
+  return f;
+}
+
+__device__ __forceinline__ double freq_of(double lane_freq, int p) {
+  const uint64_t bits = __builtin_bit_cast(uint64_t, lane_freq);
+  const uint32_t lo = (uint32_t)__builtin_amdgcn_ds_bpermute(p << 2, (int)(uint32_t)bits);
+  const uint32_t hi = (uint32_t)__builtin_amdgcn_ds_bpermute(p << 2, (int)(uint32_t)(bits >> 32));
+  return __builtin_bit_cast(double, ((uint64_t)hi << 32) | lo);
+}
 
 // One table entry.  PRECISE (fp32 inputs): fp64 angle reduced to one turn,
 // then an accurate single-precision sincos.  Otherwise (bf16 inputs): the
@@ -103,33 +125,45 @@ __device__ __forceinline__ float2 rope_entry(int pos, double inv_rev) {
   return make_float2(c, s);
 }
 
-// h and w parts of the table (the same for every block).
-template <bool PRECISE>
-__device__ void build_rope_hw(float2* tab, const RopeArgs& ra) {
-  const int ht = ra.dt >> 1, hh = ra.dh >> 1, hw = ra.dw >> 1;
-  for (int e = ra.off_h + threadIdx.x; e < ra.n_entries; e += blockDim.x) {
-    int pos, p;
-    if (e < ra.off_w) {
-      const int x = e - ra.off_h;
-      pos = x / hh;
-      p = ht + (x - pos * hh);
-    } else {
-      const int x = e - ra.off_w;
-      pos = x / hw;
-      p = ht + hh + (x - pos * hw);
-    }
-    tab[e] = rope_entry<PRECISE>(pos, ra.inv_rev[p]);
+// The table entries [e_begin, e_end) of NT threads: entry e goes to thread
+// e % NT.  The loop runs over whole wavefronts (every lane takes part in the
+// cross-lane reads); at(e) gives (position, global pair) of entry e.
+template <bool PRECISE, int NT, typename At>
+__device__ __forceinline__ void build_rope_range(float2* tab, int e_begin, int e_end, double lane_freq, At at) {
+  const int lane = threadIdx.x & 63;
+  const int wave_base = (int)(threadIdx.x & ~63u);
+  for (int e0 = e_begin + wave_base; e0 < e_end; e0 += NT) {
+    const int e = e0 + lane;
+    const int2 pp = at(min(e, e_end - 1));
+    const double inv = freq_of(lane_freq, pp.y);
+    if (e < e_end) tab[e] = rope_entry<PRECISE>(pp.x, inv);
   }
 }
 
+// h and w parts of the table (the same for every block).
+template <bool PRECISE, int NT>
+__device__ void build_rope_hw(float2* tab, const RopeArgs& ra, double lane_freq) {
+  const int ht = ra.dt >> 1, hh = ra.dh >> 1;
+  build_rope_range<PRECISE, NT>(tab, ra.off_h, ra.n_entries, lane_freq, [&](int e) {
+    if (e < ra.off_w) {
+      const uint32_t x = (uint32_t)(e - ra.off_h);
+      const uint32_t pos = fdiv(x, ra.fhh);
+      return make_int2((int)pos, ht + (int)(x - pos * ra.fhh.div));
+    }
+    const uint32_t x = (uint32_t)(e - ra.off_w);
+    const uint32_t pos = fdiv(x, ra.fhw);
+    return make_int2((int)pos, ht + hh + (int)(x - pos * ra.fhw.div));
+  });
+}
+
 // t part of the table for block c: rows are global frames t0 + c*F + row.
-template <bool PRECISE>
-__device__ void build_rope_t(float2* tab, const RopeArgs& ra, int c) {
-  const int ht = ra.dt >> 1;
-  for (int e = threadIdx.x; e < ra.off_h; e += blockDim.x) {
-    const int row = e / ht;
-    tab[e] = rope_entry<PRECISE>(ra.t0 + c * ra.F + row, ra.inv_rev[e - row * ht]);
-  }
+template <bool PRECISE, int NT>
+__device__ void build_rope_t(float2* tab, const RopeArgs& ra, int c, double lane_freq) {
+  const int tbase = ra.t0 + c * ra.F;
+  build_rope_range<PRECISE, NT>(tab, 0, ra.off_h, lane_freq, [&](int e) {
+    const uint32_t row = fdiv((uint32_t)e, ra.fht);
+    return make_int2(tbase + (int)row, e - (int)(row * ra.fht.div));
+  });
 }
 
 // A token's RoPE coordinates packed in one word, ten bits each: frame within
@@ -295,19 +329,21 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, ui
 constexpr int kLoadPolicy = 2;   // nt
 constexpr int kStorePolicy = 0;  // default
 
-template <int NW>
+// POLICY: kLoadPolicy for the streamed inputs; 0 (default caching) for the
+// small per-block operands that many workgroups read.
+template <int NW, int POLICY = kLoadPolicy>
 __device__ __forceinline__ void buf_load(uint32_t* dst, __amdgpu_buffer_rsrc_t r, uint32_t off) {
   if constexpr (NW == 1) {
-    dst[0] = (uint32_t)__builtin_amdgcn_raw_buffer_load_b32(r, off, 0, kLoadPolicy);
+    dst[0] = (uint32_t)__builtin_amdgcn_raw_buffer_load_b32(r, off, 0, POLICY);
   } else if constexpr (NW == 2) {
-    const uint2 t = __builtin_bit_cast(uint2, __builtin_amdgcn_raw_buffer_load_b64(r, off, 0, kLoadPolicy));
+    const uint2 t = __builtin_bit_cast(uint2, __builtin_amdgcn_raw_buffer_load_b64(r, off, 0, POLICY));
     dst[0] = t.x; dst[1] = t.y;
   } else {
     static_assert(NW % 4 == 0, "word count");
 #pragma unroll
     for (int i = 0; i < NW / 4; ++i) {
       const uint4 t =
-          __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(r, off + 16 * i, 0, kLoadPolicy));
+          __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(r, off + 16 * i, 0, POLICY));
       dst[4 * i] = t.x; dst[4 * i + 1] = t.y; dst[4 * i + 2] = t.z; dst[4 * i + 3] = t.w;
     }
   }
@@ -466,6 +502,7 @@ __global__ __launch_bounds__(red_threads<BF16>(), red_min_blocks<BF16>()) void s
   const int cg = lane & 15;
   const int tg = lane >> 4;
 
+  const double lane_freq = ROPE ? load_lane_freq(ra) : 0.0;
   PairLoc pl[NPAIR > 0 ? NPAIR : 1];
   if (ROPE) {
 #pragma unroll
@@ -580,8 +617,8 @@ __global__ __launch_bounds__(red_threads<BF16>(), red_min_blocks<BF16>()) void s
     // the first loads are in flight.  Every wave has passed the previous
     // segment's epilogue barrier, so no wave still reads the old t rows.
     if (ROPE) {
-      if (pos == g0) build_rope_hw<!BF16>(tab, ra);
-      build_rope_t<!BF16>(tab, ra, c);
+      if (pos == g0) build_rope_hw<!BF16, RT>(tab, ra, lane_freq);
+      build_rope_t<!BF16, RT>(tab, ra, c, lane_freq);
     }
     lds_barrier();
     int k = 0;
@@ -881,6 +918,7 @@ __global__ __launch_bounds__(app_threads<BF16>(), app_min_blocks<BF16>()) void s
   // one per run.
   constexpr bool RUNS = BF16 && ROPE == 3;
   constexpr int NLOC = RUNS ? NKS : NPAIR;
+  const double lane_freq = ROPE ? load_lane_freq(ra) : 0.0;
   PairLoc pl[NLOC];
   if (ROPE) {
 #pragma unroll
@@ -918,50 +956,38 @@ __global__ __launch_bounds__(app_threads<BF16>(), app_min_blocks<BF16>()) void s
       for (int i = 0; i < NLD; ++i) buf_load<4>(qw + 4 * i, qrs, off + i * RPI * ROWB);
     };
 
-    // Segment prologue.  The prefix operand of this block is loaded first,
-    // then the segment's first two steps of q: vector memory results return
-    // in issue order, so staging the operand waits for it only and the q
-    // loads stay in flight while the operand (and the RoPE table rows) go to
-    // LDS.
+    // Segment prologue, in three groups so that no wait covers more than it
+    // must (vector loads complete in issue order):
+    //   1. loads of this block's prefix operand S_c^T and of Z_c;
+    //   2. loads of the segment's first two steps of q;
+    //   3. the operand to LDS and the denominator operand to registers (these
+    //      wait for group 1 only, while the q loads stay in flight), then the
+    //      RoPE table rows.
+    // The scheduling barriers keep the groups in this order, and every use
+    // of group 1 sits in the same block as its loads, before any branch, so
+    // the compiler does not sink those loads below the q loads.
     lds_barrier();  // every wave has read the previous segment's fstage and t rows
+    // (Raw buffer loads: the compiler keeps them in program order, whereas
+    // plain loads through const restrict pointers count as invariant and may
+    // be sunk next to their use, behind the q loads.)
     constexpr int FR = (FRAG_U4 + AT - 1) / AT;
-    uint4 fr[FR];
+    uint32_t fr[FR][4];
     {
-      const uint4* src = (const uint4*)frags + bhc * FRAG_U4;
+      const __amdgpu_buffer_rsrc_t frs = make_rsrc((const uint4*)frags + bhc * FRAG_U4, FRAG_U4 * 16);
 #pragma unroll
-      for (int i = 0; i < FR; ++i)
-        if (FRAG_U4 % AT == 0 || tid + i * AT < FRAG_U4) fr[i] = src[tid + i * AT];
+      for (int i = 0; i < FR; ++i)  // pieces past the operand read as zeros and are not stored
+        buf_load<4, 0>(fr[i], frs, (uint32_t)(tid + i * AT) * 16);
     }
-    // Denominator operand.  fp32: the lane's FPLa entries of Z.  bf16: the
-    // A operand of a 16x16x32 MFMA against the unrotated phi(q) tile, row 0
-    // holding Z rounded to bf16 and row 4 the rounding remainder (also in
-    // bf16), other rows zero; Z_hi + Z_lo carries Z to about 2^-17 relative,
-    // and the MFMA forms the bf16 x bf16 products exactly and sums in fp32.
-    float z[BF16 ? 1 : FPLa];
-    u32x4 az[BF16 ? NKS : 1];
+    // Z_c: bf16, the 8-feature runs of the lane's k-steps; fp32, the lane's
+    // FPLa features in runs of 4.
+    constexpr int NZ4 = BF16 ? 2 * NKS : FPLa / 4;
+    uint32_t zr[NZ4][4];
     {
-      const float* zsrc = zc + bhc * D;
-      if constexpr (BF16) {
+      const __amdgpu_buffer_rsrc_t zrs = make_rsrc(zc + bhc * D, D * 4);
 #pragma unroll
-        for (int ks = 0; ks < NKS; ++ks) {
-          const float4 t0 = *(const float4*)(zsrc + apply_feat<BF16>(g, 8 * ks));
-          const float4 t1 = *(const float4*)(zsrc + apply_feat<BF16>(g, 8 * ks + 4));
-          const float zz[8] = {t0.x, t0.y, t0.z, t0.w, t1.x, t1.y, t1.z, t1.w};
-#pragma unroll
-          for (int m = 0; m < 4; ++m) {
-            const bf16x2_t hi = {(__bf16)zz[2 * m], (__bf16)zz[2 * m + 1]};
-            const bf16x2_t lo = {(__bf16)(zz[2 * m] - (float)hi[0]), (__bf16)(zz[2 * m + 1] - (float)hi[1])};
-            az[ks][m] = row == 0 ? __builtin_bit_cast(uint32_t, hi) : row == 4 ? __builtin_bit_cast(uint32_t, lo) : 0u;
-          }
-        }
-      } else {
-#pragma unroll
-        for (int m = 0; m < FPLa; m += 4) {  // runs of 4 consecutive features
-          const float4 t = *(const float4*)(zsrc + apply_feat<BF16>(g, m));
-          z[m] = t.x; z[m + 1] = t.y; z[m + 2] = t.z; z[m + 3] = t.w;
-        }
-      }
+      for (int i = 0; i < NZ4; ++i) buf_load<4, 0>(zr[i], zrs, (uint32_t)apply_feat<BF16>(g, 4 * i) * 4);
     }
+    __builtin_amdgcn_sched_barrier(0);
     constexpr int WSTRIDE = 16 * TPS * (AT / 64);
     const int t_first = js + wave * 16 * TPS;
     const int nsteps = t_first < je ? (je - t_first + WSTRIDE - 1) / WSTRIDE : 0;
@@ -973,14 +999,41 @@ __global__ __launch_bounds__(app_threads<BF16>(), app_min_blocks<BF16>()) void s
     load_stepq(qa, t_first);
     load_stepq(qb, t_first + WSTRIDE);
     __builtin_amdgcn_sched_barrier(0);
-    if (ROPE) {
-      if (pos == g0) build_rope_hw<!BF16>(tab, ra);
-      build_rope_t<!BF16>(tab, ra, c);
-    }
 #pragma unroll
     for (int i = 0; i < FR; ++i) {
       const int u = tid + i * AT;
-      if (FRAG_U4 % AT == 0 || u < FRAG_U4) fstage[frag_at(u / CPR, u % CPR)] = fr[i];
+      if (FRAG_U4 % AT == 0 || u < FRAG_U4)
+        fstage[frag_at(u / CPR, u % CPR)] = make_uint4(fr[i][0], fr[i][1], fr[i][2], fr[i][3]);
+    }
+    // Denominator operand.  fp32: the lane's FPLa entries of Z.  bf16: the
+    // A operand of a 16x16x32 MFMA against the unrotated phi(q) tile, row 0
+    // holding Z rounded to bf16 and row 4 the rounding remainder (also in
+    // bf16), other rows zero; Z_hi + Z_lo carries Z to about 2^-17 relative,
+    // and the MFMA forms the bf16 x bf16 products exactly and sums in fp32.
+    float z[BF16 ? 1 : FPLa];
+    u32x4 az[BF16 ? NKS : 1];
+    if constexpr (BF16) {
+#pragma unroll
+      for (int ks = 0; ks < NKS; ++ks) {
+        float zz[8];
+#pragma unroll
+        for (int i = 0; i < 8; ++i) zz[i] = __uint_as_float(zr[2 * ks + i / 4][i % 4]);
+#pragma unroll
+        for (int m = 0; m < 4; ++m) {
+          const bf16x2_t hi = {(__bf16)zz[2 * m], (__bf16)zz[2 * m + 1]};
+          const bf16x2_t lo = {(__bf16)(zz[2 * m] - (float)hi[0]), (__bf16)(zz[2 * m + 1] - (float)hi[1])};
+          az[ks][m] = row == 0 ? __builtin_bit_cast(uint32_t, hi) : row == 4 ? __builtin_bit_cast(uint32_t, lo) : 0u;
+        }
+      }
+    } else {
+#pragma unroll
+      for (int i = 0; i < NZ4; ++i)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) z[4 * i + j] = __uint_as_float(zr[i][j]);
+    }
+    if (ROPE) {
+      if (pos == g0) build_rope_hw<!BF16, AT>(tab, ra, lane_freq);
+      build_rope_t<!BF16, AT>(tab, ra, c, lane_freq);
     }
     lds_barrier();
 
@@ -1390,6 +1443,7 @@ __global__ __launch_bounds__(kThreads, 1) void sva_bwd_out_kernel(
   uint4* tq = tiles[wave][0];
   uint4* to = tiles[wave][1];
 
+  const double lane_freq = ROPE ? load_lane_freq(ra) : 0.0;
   PairLoc pl[NLOC];
   if (ROPE) {
 #pragma unroll
@@ -1429,8 +1483,8 @@ __global__ __launch_bounds__(kThreads, 1) void sva_bwd_out_kernel(
     load3(xa, t_first);
     __builtin_amdgcn_sched_barrier(0);
     if (ROPE) {
-      if (pos == g0) build_rope_hw<false>(tab, ra);
-      build_rope_t<false>(tab, ra, c);
+      if (pos == g0) build_rope_hw<false, kThreads>(tab, ra, lane_freq);
+      build_rope_t<false, kThreads>(tab, ra, c, lane_freq);
     }
     stage_operand<D, true>(fst, fr, tid);
     if (tid < D) zst[tid] = zmine;
@@ -1660,6 +1714,7 @@ __global__ __launch_bounds__(kThreads, 2) void sva_bwd_kv_kernel(
   uint4* tk = tiles[wave][0];
   uint4* tv = tiles[wave][1];
 
+  const double lane_freq = ROPE ? load_lane_freq(ra) : 0.0;
   PairLoc pl[NLOC];
   if (ROPE) {
 #pragma unroll
@@ -1698,8 +1753,8 @@ __global__ __launch_bounds__(kThreads, 2) void sva_bwd_kv_kernel(
     load2(xa, t_first);
     __builtin_amdgcn_sched_barrier(0);
     if (ROPE) {
-      if (pos == g0) build_rope_hw<false>(tab, ra);
-      build_rope_t<false>(tab, ra, c);
+      if (pos == g0) build_rope_hw<false, kThreads>(tab, ra, lane_freq);
+      build_rope_t<false, kThreads>(tab, ra, c, lane_freq);
     }
     stage_operand<D, false>(fsT, fr, tid);
     stage_operand<D, true>(fsN, fr, tid);
@@ -1792,8 +1847,9 @@ __global__ __launch_bounds__(kThreads) void sva_prep_kernel(
   float2* tab = reinterpret_cast<float2*>(tab_raw);
   const int c = blockIdx.y;
   if (ROPE) {
-    build_rope_hw<!BF16>(tab, ra);
-    build_rope_t<!BF16>(tab, ra, c);
+    const double lane_freq = load_lane_freq(ra);
+    build_rope_hw<!BF16, kThreads>(tab, ra, lane_freq);
+    build_rope_t<!BF16, kThreads>(tab, ra, c, lane_freq);
   }
   __syncthreads();
   const int j = blockIdx.x * kThreads + threadIdx.x;  // block-local token
@@ -1955,6 +2011,9 @@ Plan make_plan(const sva_desc* d) {
     ra.n_entries = ra.off_w + d->Ws * (ra.dw / 2);
     ra.t0 = d->t0;
     ra.F = d->frames_per_block;
+    ra.fht = make_fastdiv((uint32_t)(ra.dt / 2 > 0 ? ra.dt / 2 : 1));
+    ra.fhh = make_fastdiv((uint32_t)(ra.dh / 2 > 0 ? ra.dh / 2 : 1));
+    ra.fhw = make_fastdiv((uint32_t)(ra.dw / 2 > 0 ? ra.dw / 2 : 1));
     const double two_pi = 6.283185307179586476925286766559;
     int p_idx = 0;
     const int widths[3] = {ra.dt, ra.dh, ra.dw};
@@ -2268,8 +2327,8 @@ sva_status plan_proj_fwd(const sva_desc* a, const sva_proj_desc* pd, ProjPlan* p
       best = cost;
     }
   }
-  if (const char* e = getenv("SVA_PROJ_RANGE_TOKENS")) {  // explicit range length
-    const long long v = atoll(e);
+  if (pd->range_tokens != 0) {  // the caller's range length
+    const long long v = pd->range_tokens;
     if (v <= 0 || v > p.Nb || p.Nb % v != 0) return SVA_ERR_INVALID_ARG;
     L = v;
   }

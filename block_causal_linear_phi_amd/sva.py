@@ -40,8 +40,10 @@ class SvaTconvDesc(ctypes.Structure):
 
 
 class SvaProjDesc(ctypes.Structure):
+    # range_tokens: the fused entry point's reduction range length (0 = chosen
+    # by the library); the pack and projection calls ignore it
     _fields_ = [("B", ctypes.c_int), ("N", ctypes.c_int), ("C", ctypes.c_int), ("H", ctypes.c_int),
-                ("d", ctypes.c_int)]
+                ("d", ctypes.c_int), ("range_tokens", ctypes.c_int)]
 
 
 class SvaError(RuntimeError):
@@ -135,6 +137,76 @@ def _check(status: int, where: str):
         raise SvaError(status, where)
 
 
+# Argument checks.  The C ABI sees only pointers, so the binding is where
+# tensor shapes, dtypes, contiguity and devices are checked; every check runs
+# before the library is called and raises ValueError (TypeError for a
+# non-tensor or an unsupported dtype).  Shapes, dtypes and contiguity are
+# checked for every argument first, then the device of every argument.
+
+def _as_tensor(name, t):
+    import torch
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor, got {type(t).__name__}")
+    return t
+
+
+def _check_layout(name, t, shape, dtype):
+    _as_tensor(name, t)
+    if shape is not None and tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} has shape {tuple(t.shape)}, expected {tuple(shape)}")
+    if dtype is not None and t.dtype != dtype:
+        raise ValueError(f"{name} has dtype {t.dtype}, expected {dtype}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+
+
+def _check_devices(ref_name, ref, named):
+    if ref.device.type != "cuda":
+        raise ValueError(f"{ref_name} must be on a GPU (cuda) device, got {ref.device}")
+    for name, t in named:
+        if t is not None and t.device != ref.device:
+            raise ValueError(f"{name} is on {t.device}, expected {ref.device} (the device of {ref_name})")
+
+
+def _check_bytes(name, t):
+    """A byte buffer (workspace, saved states, packed weights): contiguous."""
+    _as_tensor(name, t)
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+
+
+def _check_attn(q, grid, like_q=(), caches=(), buffers=(), qname="q"):
+    """q [B, H, T*Hs*Ws, d] (bf16 or fp32); like_q: (name, tensor) pairs
+    with q's shape and dtype (None skipped); caches: (name, tensor, kind)
+    with kind "S" [B, H, d, d] or "z" [B, H, d], fp32 (None skipped);
+    buffers: (name, byte tensor) pairs (None skipped)."""
+    import torch
+    _as_tensor(qname, q)
+    if q.dim() != 4:
+        raise ValueError(f"{qname} must be [B, H, N, d], got shape {tuple(q.shape)}")
+    _dtype_code(q)
+    B, H, N, d = q.shape
+    T, Hs, Ws = grid
+    if N != T * Hs * Ws:
+        raise ValueError(f"{qname} holds {N} tokens per sequence but the grid {T}x{Hs}x{Ws} has {T * Hs * Ws}")
+    _check_layout(qname, q, None, None)
+    for name, t in like_q:
+        if t is not None:
+            _check_layout(name, t, q.shape, q.dtype)
+    for name, t, kind in caches:
+        if t is not None:
+            _check_layout(name, t, (B, H, d, d) if kind == "S" else (B, H, d), torch.float32)
+    for name, t in buffers:
+        if t is not None:
+            _check_bytes(name, t)
+    _check_devices(qname, q, [(n, t) for n, t in like_q] + [(n, t) for n, t, _ in caches] + list(buffers))
+
+
+def _pair(name_a, a, name_b, b):
+    if (a is None) != (b is None):
+        raise ValueError(f"{name_a} and {name_b} must be given together")
+
+
 def _desc_from(q, grid, F, t0, rope, split, base, eps) -> SvaDesc:
     if q.dim() != 4:
         raise ValueError("q, k, v must be [B, H, N, d]")
@@ -162,10 +234,13 @@ def sva_block_cache_workspace(desc: SvaDesc) -> int:
 
 
 def _workspace(nbytes: int, like, ws):
+    """The caller's workspace, or a new zero-filled one (a workspace must be
+    zero-filled before its first use: its arrival counters start at zero, and
+    every call leaves them zero again)."""
     import torch
     if ws is not None:
         return ws
-    return torch.empty(max(nbytes, 1), dtype=torch.uint8, device=like.device)
+    return torch.zeros(max(nbytes, 1), dtype=torch.uint8, device=like.device)
 
 
 def sva_lin_attn_fwd(q, k, v, grid: Tuple[int, int, int], frames_per_block: int, *, t0: int = 0,
@@ -174,6 +249,11 @@ def sva_lin_attn_fwd(q, k, v, grid: Tuple[int, int, int], frames_per_block: int,
                      events=None):
     """One-shot block-causal forward (sva_lin_attn_fwd).  Returns `out`."""
     import torch
+    _pair("S0", S0, "z0", z0)
+    _pair("S_out", S_out, "z_out", z_out)
+    _check_attn(q, grid, like_q=[("k", k), ("v", v), ("out", out)],
+                caches=[("S0", S0, "S"), ("z0", z0, "z"), ("S_out", S_out, "S"), ("z_out", z_out, "z")],
+                buffers=[("ws", ws)])
     desc = _desc_from(q, grid, frames_per_block, t0, rope, split, base, eps)
     if out is None:
         out = torch.empty_like(q)
@@ -203,6 +283,11 @@ def sva_lin_attn_fwd_save(q, k, v, grid: Tuple[int, int, int], frames_per_block:
     """Forward that keeps its prefix states for the backward
     (sva_lin_attn_fwd_save).  Returns (out, states)."""
     import torch
+    _pair("S0", S0, "z0", z0)
+    _pair("S_out", S_out, "z_out", z_out)
+    _check_attn(q, grid, like_q=[("k", k), ("v", v), ("out", out)],
+                caches=[("S0", S0, "S"), ("z0", z0, "z"), ("S_out", S_out, "S"), ("z_out", z_out, "z")],
+                buffers=[("ws", ws), ("states", states)])
     desc = _desc_from(q, grid, frames_per_block, t0, rope, split, base, eps)
     if out is None:
         out = torch.empty_like(q)
@@ -224,6 +309,15 @@ def sva_lin_attn_bwd(q, k, v, out, dout, grid: Tuple[int, int, int], frames_per_
     dS0/dz0 are filled when given.  `states` from sva_lin_attn_fwd_save
     skips recomputing the forward's prefix states."""
     import torch
+    for na, ta, nb_, tb in (("S0", S0, "z0", z0), ("dS_out", dS_out, "dz_out", dz_out), ("dS0", dS0, "dz0", dz0)):
+        _pair(na, ta, nb_, tb)
+    if out is None or dout is None:
+        raise ValueError("out and dout are required")
+    _check_attn(q, grid, like_q=[("k", k), ("v", v), ("out", out), ("dout", dout), ("dq", dq), ("dk", dk),
+                                 ("dv", dv)],
+                caches=[("S0", S0, "S"), ("z0", z0, "z"), ("dS_out", dS_out, "S"), ("dz_out", dz_out, "z"),
+                        ("dS0", dS0, "S"), ("dz0", dz0, "z")],
+                buffers=[("ws", ws), ("states", states)])
     desc = _desc_from(q, grid, frames_per_block, t0, rope, split, base, eps)
     dq = torch.empty_like(q) if dq is None else dq
     dk = torch.empty_like(k) if dk is None else dk
@@ -243,6 +337,10 @@ def sva_block_cache_apply(S, z, q, k, v, frame_grid: Tuple[int, int, int], *, t0
     """Output of one block against the committed cache (S, z); the cache is
     not modified.  frame_grid = (F, Hs, Ws).  Returns `out`."""
     import torch
+    _check_attn(q, frame_grid, like_q=[("k", k), ("v", v), ("out", out)], caches=[("S", S, "S"), ("z", z, "z")],
+                buffers=[("ws", ws)])
+    if S is None or z is None:
+        raise ValueError("the cache S, z is required")
     desc = _desc_from(q, frame_grid, frame_grid[0], t0, rope, split, base, eps)
     if out is None:
         out = torch.empty_like(q)
@@ -256,6 +354,10 @@ def sva_block_cache_apply(S, z, q, k, v, frame_grid: Tuple[int, int, int], *, t0
 def sva_block_cache_commit(S, z, k, v, frame_grid: Tuple[int, int, int], *, t0: int, rope: bool = False,
                            split=None, base: float = 10000.0, ws=None, stream=None):
     """Adds one block's K, V to the cache (S, z) in place."""
+    _check_attn(k, frame_grid, like_q=[("v", v)], caches=[("S", S, "S"), ("z", z, "z")], buffers=[("ws", ws)],
+                qname="k")
+    if S is None or z is None:
+        raise ValueError("the cache S, z is required")
     desc = _desc_from(k, frame_grid, frame_grid[0], t0, rope, split, base, 0.0)
     ws = _workspace(sva_block_cache_workspace(desc), k, ws)
     st = lib().sva_block_cache_commit(ctypes.byref(desc), _ptr(S), _ptr(z), _ptr(k), _ptr(v), _ptr(ws),
@@ -267,6 +369,7 @@ def sva_phi_rope_prep(x, grid: Tuple[int, int, int], *, t0: int = 0, rope: bool 
                       base: float = 10000.0, want_phi: bool = True, stream=None):
     """The phi + RoPE stage alone: returns (RoPE(phi x), phi x) as fp32."""
     import torch
+    _check_attn(x, grid, qname="x")
     desc = _desc_from(x, grid, grid[0], t0, rope, split, base, 0.0)
     xr = torch.empty(x.shape, dtype=torch.float32, device=x.device)
     xp = torch.empty_like(xr) if want_phi else None
@@ -289,6 +392,33 @@ def _tconv_desc_from(x, F) -> SvaTconvDesc:
     return make_tconv_desc(B, T, Hs, Ws, C, F, _dtype_code(x))
 
 
+def _check_tconv(x, w=None, bias=None, caches=(), y=None):
+    """x [B, T, Hs, Ws, C] (bf16 or fp32), taps w [C, 3] and bias [C] fp32,
+    caches [B, Hs, Ws, C] in x's dtype, y like x (None skipped)."""
+    import torch
+    _as_tensor("x", x)
+    if x.dim() != 5:
+        raise ValueError(f"x must be [B, T, Hs, Ws, C], got shape {tuple(x.shape)}")
+    _dtype_code(x)
+    B, T, Hs, Ws, C = x.shape
+    _check_layout("x", x, None, None)
+    named = []
+    if w is not None:
+        _check_layout("w", w, (C, 3), torch.float32)
+        named.append(("w", w))
+    if bias is not None:
+        _check_layout("bias", bias, (C,), torch.float32)
+        named.append(("bias", bias))
+    for name, t in caches:
+        if t is not None:
+            _check_layout(name, t, (B, Hs, Ws, C), x.dtype)
+            named.append((name, t))
+    if y is not None:
+        _check_layout("y", y, x.shape, x.dtype)
+        named.append(("y", y))
+    _check_devices("x", x, named)
+
+
 def sva_tconv_fwd(x, w, bias, frames_per_block: int, *, cache_in=None, y=None, cache_out=None,
                   stream=None):
     """Block-causal temporal convolution over all blocks of x [B, T, Hs, Ws, C]
@@ -296,6 +426,9 @@ def sva_tconv_fwd(x, w, bias, frames_per_block: int, *, cache_in=None, y=None, c
     frame carried into block 0 (None: zero); cache_out, if given, receives the
     last frame.  Returns y."""
     import torch
+    if w is None:
+        raise ValueError("the taps w are required")
+    _check_tconv(x, w, bias, [("cache_in", cache_in), ("cache_out", cache_out)], y)
     desc = _tconv_desc_from(x, frames_per_block)
     if y is None:
         y = torch.empty_like(x)
@@ -309,6 +442,9 @@ def sva_tconv_apply(cache, x, w, bias, *, y=None, stream=None):
     """Output of one block x [B, F, Hs, Ws, C] against the cache [B, Hs, Ws, C];
     the cache is not modified.  Returns y."""
     import torch
+    if w is None or cache is None:
+        raise ValueError("the taps w and the cache are required")
+    _check_tconv(x, w, bias, [("cache", cache)], y)
     desc = _tconv_desc_from(x, x.shape[1])
     if y is None:
         y = torch.empty_like(x)
@@ -320,6 +456,9 @@ def sva_tconv_apply(cache, x, w, bias, *, y=None, stream=None):
 
 def sva_tconv_commit(cache, x, *, stream=None):
     """cache <- the last frame of one block x [B, F, Hs, Ws, C], in place."""
+    if cache is None:
+        raise ValueError("the cache is required")
+    _check_tconv(x, caches=[("cache", cache)])
     desc = _tconv_desc_from(x, x.shape[1])
     st = lib().sva_tconv_commit(ctypes.byref(desc), _ptr(cache), _ptr(x), _stream(stream))
     _check(st, "sva_tconv_commit")
@@ -337,24 +476,57 @@ def sva_mxfp4_pack_weights(codes, scales, H: int, d: int, *, out=None, stream=No
     scales [3 H d, C / 32] uint8 (E8M0) -> the packed weights (uint8 tensor)
     that sva_qkv_proj_mxfp4 takes.  Weights are constant: pack them once."""
     import torch
+    _as_tensor("codes", codes)
+    if codes.dim() != 2:
+        raise ValueError(f"codes must be [3 H d, C / 2], got shape {tuple(codes.shape)}")
     n_out, half = codes.shape
     C = 2 * half
+    if n_out != 3 * H * d:
+        raise ValueError(f"codes has {n_out} rows, expected 3 H d = {3 * H * d}")
+    if C % 32:
+        raise ValueError(f"C = {C} is not a whole number of 32-channel scale blocks")
+    _check_layout("codes", codes, None, torch.uint8)
+    _check_layout("scales", scales, (n_out, C // 32), torch.uint8)
+    if out is not None:
+        _check_layout("out", out, (mxfp4_packed_bytes(n_out, C),), torch.uint8)
+    _check_devices("codes", codes, [("scales", scales), ("out", out)])
     if out is None:
         out = torch.empty((mxfp4_packed_bytes(n_out, C),), dtype=torch.uint8, device=codes.device)
-    desc = SvaProjDesc(1, 1, C, H, d)
+    desc = SvaProjDesc(1, 1, C, H, d, 0)
     st = lib().sva_mxfp4_pack_weights(ctypes.byref(desc), _ptr(codes), _ptr(scales), _ptr(out), _stream(stream))
     _check(st, "sva_mxfp4_pack_weights")
     return out
+
+
+def _check_proj_inputs(x, wpack, bias, H, d):
+    """x [B, N, C] bf16, wpack the packed weights for 3 H d outputs, bias
+    [3 H d] fp32 or None (layouts only; devices are checked by the caller)."""
+    import torch
+    _as_tensor("x", x)
+    if x.dim() != 3:
+        raise ValueError(f"x must be [B, N, C], got shape {tuple(x.shape)}")
+    _check_layout("x", x, None, torch.bfloat16)
+    C = x.shape[2]
+    n_out = 3 * H * d
+    _check_bytes("wpack", wpack)
+    if wpack.numel() * wpack.element_size() != mxfp4_packed_bytes(n_out, C):
+        raise ValueError(f"wpack holds {wpack.numel() * wpack.element_size()} bytes, expected "
+                         f"{mxfp4_packed_bytes(n_out, C)} for {n_out} outputs of C = {C}")
+    if bias is not None:
+        _check_layout("bias", bias, (n_out,), torch.float32)
 
 
 def sva_qkv_proj_mxfp4(x, wpack, bias, H: int, d: int, *, q=None, k=None, v=None, stream=None):
     """x [B, N, C] bf16; wpack from sva_mxfp4_pack_weights; bias [3 H d]
     fp32 or None.  Returns (q, k, v), each [B, H, N, d] bf16."""
     import torch
-    if x.dim() != 3 or x.dtype != torch.bfloat16:
-        raise ValueError("x must be [B, N, C] bf16")
+    _check_proj_inputs(x, wpack, bias, H, d)
     B, N, C = x.shape
-    desc = SvaProjDesc(B, N, C, H, d)
+    for name, t in (("q", q), ("k", k), ("v", v)):
+        if t is not None:
+            _check_layout(name, t, (B, H, N, d), torch.bfloat16)
+    _check_devices("x", x, [("wpack", wpack), ("bias", bias), ("q", q), ("k", k), ("v", v)])
+    desc = SvaProjDesc(B, N, C, H, d, 0)
     outs = []
     for t in (q, k, v):
         outs.append(torch.empty((B, H, N, d), dtype=torch.bfloat16, device=x.device) if t is None else t)
@@ -366,17 +538,34 @@ def sva_qkv_proj_mxfp4(x, wpack, bias, H: int, d: int, *, q=None, k=None, v=None
 
 def sva_proj_lin_attn_fwd(x, wpack, bias, H: int, grid: Tuple[int, int, int], frames_per_block: int, *,
                           t0: int = 0, rope: bool = False, split=None, base: float = 10000.0, eps: float = 1e-6,
-                          S0=None, z0=None, S_out=None, z_out=None, out=None, ws=None, stream=None):
+                          S0=None, z0=None, S_out=None, z_out=None, out=None, ws=None, stream=None,
+                          range_tokens: int = 0):
     """Projection and attention fused (sva_proj_lin_attn_fwd): x [B, N, C]
     bf16 with N = T * Hs * Ws; wpack from sva_mxfp4_pack_weights for H heads
-    of d = 64; bias [3 H 64] fp32 or None.  Returns out [B, H, N, 64] bf16."""
+    of d = 64; bias [3 H 64] fp32 or None.  range_tokens: tokens per
+    reduction range (0: chosen by the library; else a divisor of the block
+    length).  Returns out [B, H, N, 64] bf16."""
     import torch
-    if x.dim() != 3 or x.dtype != torch.bfloat16:
-        raise ValueError("x must be [B, N, C] bf16")
+    _pair("S0", S0, "z0", z0)
+    _pair("S_out", S_out, "z_out", z_out)
+    _check_proj_inputs(x, wpack, bias, H, 64)
     B, N, C = x.shape
+    T, Hs, Ws = grid
+    if N != T * Hs * Ws:
+        raise ValueError(f"x holds {N} tokens per sample but the grid {T}x{Hs}x{Ws} has {T * Hs * Ws}")
+    if out is not None:
+        _check_layout("out", out, (B, H, N, 64), torch.bfloat16)
+    for name, t, shape in (("S0", S0, (B, H, 64, 64)), ("z0", z0, (B, H, 64)), ("S_out", S_out, (B, H, 64, 64)),
+                           ("z_out", z_out, (B, H, 64))):
+        if t is not None:
+            _check_layout(name, t, shape, torch.float32)
+    if ws is not None:
+        _check_bytes("ws", ws)
+    _check_devices("x", x, [("wpack", wpack), ("bias", bias), ("out", out), ("S0", S0), ("z0", z0),
+                            ("S_out", S_out), ("z_out", z_out), ("ws", ws)])
     q_like = torch.empty((B, H, N, 64), dtype=torch.bfloat16, device=x.device) if out is None else out
     desc = _desc_from(q_like, grid, frames_per_block, t0, rope, split, base, eps)
-    pdesc = SvaProjDesc(B, N, C, H, 64)
+    pdesc = SvaProjDesc(B, N, C, H, 64, int(range_tokens))
     n = ctypes.c_size_t()
     _check(lib().sva_proj_lin_attn_fwd_workspace(ctypes.byref(desc), ctypes.byref(pdesc), ctypes.byref(n)),
            "sva_proj_lin_attn_fwd_workspace")

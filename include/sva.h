@@ -35,15 +35,21 @@
  * pointer and must be 16-byte aligned.
  *
  * Ownership: the caller allocates and frees every buffer, including the
- * workspace.  The library allocates nothing, keeps no pointer after a call
- * returns and holds no global state: calls on disjoint buffers may run
- * concurrently.  `out` must not overlap q, k or v.
+ * workspace.  The library allocates nothing and keeps no pointer after a
+ * call returns.  Its only process-wide state is a per-device memo of the
+ * occupancy queries that size its grids (filled on first use, under a
+ * mutex, and never changed after), so calls on disjoint buffers may run
+ * concurrently from several threads.  `out` must not overlap q, k or v.
  *
  * Errors: validation is synchronous, happens before anything is launched,
  * and on error nothing is written.  Work is queued on `stream` (a
  * hipStream_t; NULL = the default stream) and runs asynchronously; a kernel
  * fault surfaces at the caller's next synchronisation.  A failed launch
- * returns SVA_ERR_HIP.  NaN/Inf inputs are not checked (ReLU maps NaN to 0).
+ * returns SVA_ERR_HIP.  NaN/Inf inputs are not checked.  phi is a max with
+ * zero on the bit pattern: every value with the sign bit set (negative
+ * numbers, -0, -Inf and a NaN with its sign bit set) becomes +0, every
+ * other value (+Inf and a NaN with its sign bit clear included) passes
+ * unchanged and propagates into the sums.
  * Sums are taken in a fixed order: two calls on equal inputs give equal bits.
  */
 #ifndef SVA_H

@@ -61,6 +61,9 @@ typedef struct sva_proj_desc {
   int C;  /* input channels */
   int H;  /* heads */
   int d;  /* head dimension */
+  int range_tokens; /* sva_proj_lin_attn_fwd only: tokens per reduction
+                       range, 0 = chosen by the library (see there);
+                       ignored by the pack and projection calls */
 } sva_proj_desc;
 
 /* wpack = the packed form of (codes, scales), as above.  Weights are
@@ -93,9 +96,10 @@ sva_status sva_qkv_proj_mxfp4(const sva_proj_desc* desc, const void* x, const vo
  * workspace is sva_proj_lin_attn_fwd_workspace bytes.
  * The tokens are reduced in ranges of L tokens that divide the block
  * length, one workgroup per (range, head pair); L is chosen for occupancy
- * unless the environment variable SVA_PROJ_RANGE_TOKENS gives it (a divisor
- * of the block length, else SVA_ERR_INVALID_ARG).  The workspace size
- * depends on L: query it under the same setting. */
+ * when proj->range_tokens is 0, else L = proj->range_tokens (a divisor of
+ * the block length, else SVA_ERR_INVALID_ARG).  L fixes the order of the
+ * fp32 sums, and the workspace size depends on it: query the workspace with
+ * the same descriptor. */
 sva_status sva_proj_lin_attn_fwd_workspace(const sva_desc* attn, const sva_proj_desc* proj, size_t* bytes);
 sva_status sva_proj_lin_attn_fwd(const sva_desc* attn, const sva_proj_desc* proj, const void* x,
                                  const void* wpack, const float* bias, void* out, const float* S0,

@@ -50,3 +50,26 @@ def device_workload(w: wl.Workload, step: int = 0, keep=(), n_tokens=None):
             if (b, h) in keep:
                 host[(t, b, h)] = vals
     return dev, host
+
+
+def host_bits(t: torch.Tensor) -> np.ndarray:
+    """A device tensor's values on the host: fp32 as is, bf16 widened to fp32
+    exactly (one copy of the whole tensor)."""
+    if t.dtype == torch.bfloat16:
+        raw = t.detach().view(torch.int16).cpu().numpy().view(np.uint16)
+        return wl.bf16_bits_to_f32(raw)
+    return t.detach().float().cpu().numpy()
+
+
+def compare_slices(slices, check, workers: int = 8):
+    """Runs check(b, h) -> relative error for every (b, h) in `slices` in a
+    thread pool (numpy releases the GIL; BLAS limited to one thread per
+    worker) and returns the worst error and its slice."""
+    from threadpoolctl import threadpool_limits
+
+    def one(bh):
+        return check(*bh), bh
+
+    with threadpool_limits(limits=1), ThreadPoolExecutor(workers) as ex:
+        results = list(ex.map(one, list(slices)))
+    return max(results)

@@ -34,7 +34,7 @@ def test_two_threads_two_streams_match_sequential():
             q, k, v = jobs[j]
             stream = torch.cuda.Stream(device=DEV)  # default priority
             desc = sva.make_desc(2, 4, 64, grid, F, rope=True, split=split)
-            ws = torch.empty(sva.sva_lin_attn_fwd_workspace(desc), dtype=torch.uint8, device=DEV)
+            ws = torch.zeros(sva.sva_lin_attn_fwd_workspace(desc), dtype=torch.uint8, device=DEV)
             with torch.cuda.stream(stream):
                 for i in range(20):
                     outs[j][i] = sva.sva_lin_attn_fwd(q, k, v, grid, F, rope=True, split=split, ws=ws,

@@ -4,8 +4,8 @@ oracle on identical seeded inputs.
 Bar: max|gpu - oracle| / max|oracle| <= 1e-5 for fp32 inputs and <= 1e-2 for
 bf16 inputs.  Sizes span several 16/32-token tiles, ragged tails, several
 blocks, both head dims and every RoPE axis; the video-shaped workloads run
-at full size in the launch configuration the benchmark times, compared on
-all heads (480p, cached step) or on sampled heads (720p, minute stream).
+at full size in the launch configuration the benchmark times, with every
+(b, h) slice compared element by element.
 """
 import sys
 
@@ -15,7 +15,7 @@ import torch
 
 from block_causal_linear_phi_amd import sva
 from block_causal_linear_phi_amd import workloads as wl
-from gpu_helpers import DEV, TOL, device_workload, rand, relerr
+from gpu_helpers import DEV, TOL, compare_slices, device_workload, host_bits, rand, relerr
 from oracle import sva_oracle as orc
 
 pytestmark = pytest.mark.gpu
@@ -141,38 +141,43 @@ def test_tiny_workload():
     assert relerr(out, ref) <= 1e-5
 
 
-def _full_workload_check(name, heads):
+def _full_workload_check(name):
+    """The workload at full size, in the launch configuration the benchmark
+    times; every (b, h) slice of the output compared element by element with
+    the oracle on the same seeded inputs (regenerated slice by slice)."""
     w = wl.WORKLOADS[name]
     _say(f"{name}: generating")
-    dev, host = device_workload(w, keep=set(heads))
+    dev, _ = device_workload(w)
     _say(f"{name}: running")
     out = sva.sva_lin_attn_fwd(dev["q"], dev["k"], dev["v"], (w.T, w.Hs, w.Ws), w.F, t0=w.t0, rope=w.rope,
                                split=w.split, base=w.base, eps=w.eps)
     torch.cuda.synchronize()
     assert bool(torch.isfinite(out).all())
-    worst = 0.0
-    for (b, h) in heads:
-        _say(f"{name}: oracle head {(b, h)}")
-        q, k, v = (host[(t, b, h)][None, None] for t in ("q", "k", "v"))
+    got = host_bits(out)
+    del dev
+
+    def check(b, h):
+        q, k, v = (wl.slice_qkv(w, t, b, h)[0][None, None] for t in "qkv")
         ref, _, _ = orc.lin_attn_fwd(q, k, v, (w.T, w.Hs, w.Ws), w.F, t0=w.t0, rope=w.rope,
                                      split=w.split, base=w.base, eps=w.eps)
-        worst = max(worst, relerr(out[b, h], ref[0, 0]))
-    _say(f"{name}: worst rel err {worst:.3e}")
+        return relerr(got[b, h].astype(np.float64), ref[0, 0])
+
+    _say(f"{name}: oracle on all {w.B * w.H} (b, h) slices")
+    worst, where = compare_slices([(b, h) for b in range(w.B) for h in range(w.H)], check)
+    _say(f"{name}: worst rel err {worst:.3e} at (b, h) = {where}")
     assert worst <= TOL[w.dtype]
-    return dev, out
 
 
 def test_480p_all_heads():
-    w = wl.WORKLOADS["480p"]
-    _full_workload_check("480p", [(0, h) for h in range(w.H)])
+    _full_workload_check("480p")
 
 
-def test_720p_sampled_heads():
-    _full_workload_check("720p", [(0, 0), (0, 7), (0, 15)])
+def test_720p_all_heads():
+    _full_workload_check("720p")
 
 
-def test_minute_sampled_heads():
-    _full_workload_check("minute", [(0, 0), (1, 15)])
+def test_minute_all_heads():
+    _full_workload_check("minute")
 
 
 def test_cached_step_workload():

@@ -9,7 +9,8 @@ import torch
 
 from block_causal_linear_phi_amd import sva
 from block_causal_linear_phi_amd import workloads as wl
-from gpu_helpers import DEV, device_workload, rand, relerr
+from gpu_helpers import DEV, compare_slices, device_workload, host_bits, rand, relerr
+from oracle import sva_oracle as orc
 
 pytestmark = pytest.mark.gpu
 
@@ -117,7 +118,9 @@ def test_cache_memory_constant_over_80_block_stream():
     """[talk]: constant memory regardless of length.  An 80-block stream of
     the minute-long workload's shape (B=2, H=16, 3 x 30 x 52 blocks) runs
     apply + commit per block on one fixed cache without any growth in device
-    memory; the workspace is one-block sized and reused."""
+    memory; the workspace is one-block sized and reused.  The final cache and
+    the last block's output match the oracle's stream of the same blocks on
+    every (b, h) slice."""
     w = wl.WORKLOADS["minute"]
     fg = (w.F, w.Hs, w.Ws)
     _say("80-block stream")
@@ -125,7 +128,7 @@ def test_cache_memory_constant_over_80_block_stream():
     S = torch.zeros((w.B, w.H, w.d, w.d), dtype=torch.float32, device=DEV)
     z = torch.zeros((w.B, w.H, w.d), dtype=torch.float32, device=DEV)
     desc = sva.make_desc(w.B, w.H, w.d, fg, w.F, t0=0, rope=True, split=w.split)
-    ws = torch.empty(sva.sva_block_cache_workspace(desc), dtype=torch.uint8, device=DEV)
+    ws = torch.zeros(sva.sva_block_cache_workspace(desc), dtype=torch.uint8, device=DEV)
     out = torch.empty_like(blocks[0]["q"])
     torch.cuda.synchronize()
     before = torch.cuda.memory_allocated()
@@ -138,3 +141,24 @@ def test_cache_memory_constant_over_80_block_stream():
     assert torch.cuda.memory_allocated() == before
     assert bool(torch.isfinite(out).all()) and bool(torch.isfinite(S).all())
     assert S.numel() * 4 + z.numel() * 4 == w.B * w.H * (w.d * w.d + w.d) * 4
+    got_out, got_S, got_z = host_bits(out), S.cpu().numpy(), z.cpu().numpy()
+    kw = dict(rope=True, split=w.split, base=w.base)
+
+    def check(b, h):
+        data = [[wl.slice_qkv(w, t, b, h, s, w.block_tokens)[0][None, None] for t in "qkv"] for s in range(2)]
+        Sr, zr = np.zeros((1, 1, w.d, w.d)), np.zeros((1, 1, w.d))
+        for c in range(w.nb):
+            q, k, v = data[c % 2]
+            if c == w.nb - 1:
+                ref_out = orc.block_cache_apply(Sr, zr, q, k, v, fg, t0=c * w.F, eps=w.eps, **kw)
+            Sr, zr = orc.block_cache_commit(Sr, zr, k, v, fg, t0=c * w.F, **kw)
+        eo = relerr(got_out[b, h].astype(np.float64), ref_out[0, 0])
+        eS = relerr(got_S[b, h].astype(np.float64), Sr[0, 0])
+        ez = relerr(got_z[b, h].astype(np.float64), zr[0, 0])
+        assert ez <= 1e-5, (b, h, ez)
+        return max(eo, eS)
+
+    _say("80-block stream: oracle stream on every (b, h) slice")
+    worst, where = compare_slices([(b, h) for b in range(w.B) for h in range(w.H)], check)
+    _say(f"80-block stream: worst rel err (last output, final S) {worst:.3e} at {where}")
+    assert worst <= 1e-2
