@@ -7,10 +7,16 @@ timing; two buffer sets alternate so the 256 MB Infinity Cache cannot hold a
 step's working set.
 
 Prints one JSON line.  `value` = tokens/s over all heads (B*N tokens per
-step / step time) over K uninstrumented steps.  The `roofline` object rates
-the dominant kernel by its algorithmic bytes (its inputs read once + its
-outputs written once) over its average duration, timed live with HIP events
-that the library records on its launch stream during K further steps.
+step / step time) over K uninstrumented steps after W warm-up steps.  The
+`roofline` object rates the dominant kernel by its algorithmic bytes (its
+inputs read once + its outputs written once) over its average duration,
+timed live on the launch stream over K back-to-back launches of that kernel
+alone (sva_lin_attn_fwd_stages), with no event between launches.  The same
+line carries the median and minimum step over further runs, each kernel's
+time and HBM fraction, a plain device copy's bandwidth (the practical
+ceiling), and the other workloads (480p, the minute stream, the tiny fp32
+case, the cached denoising step and its commit), all measured in this
+process before the headline timing.
 """
 from __future__ import annotations
 
@@ -45,48 +51,51 @@ def traffic_file(workload: str) -> str:
     return os.path.join(PROFILES, f"sva_traffic_{workload}.json")
 
 
-class HipEvents:
-    """hipEvent_t handles from the HIP runtime (the library records them on
-    the stream its kernels run on)."""
+def upload(w, tensor: str, step: int = 0, n_tokens=None):
+    """The workload's seeded [B, H, N, d] tensor `tensor` for `step` (the
+    first n_tokens tokens of each sequence, or all), on cuda:0; the (b, h)
+    slices are drawn in a thread pool (numpy's generator releases the GIL)."""
+    from concurrent.futures import ThreadPoolExecutor
 
-    def __init__(self):
-        self.rt = ctypes.CDLL("libamdhip64.so")
-        self.rt.hipEventCreate.argtypes = [ctypes.POINTER(ctypes.c_void_p)]
-        self.rt.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float), ctypes.c_void_p, ctypes.c_void_p]
-        self.rt.hipEventDestroy.argtypes = [ctypes.c_void_p]
-
-    def create(self):
-        ev = ctypes.c_void_p()
-        if self.rt.hipEventCreate(ctypes.byref(ev)) != 0:
-            raise RuntimeError("hipEventCreate failed")
-        return ev.value
-
-    def elapsed_ms(self, a, b) -> float:
-        ms = ctypes.c_float()
-        if self.rt.hipEventElapsedTime(ctypes.byref(ms), a, b) != 0:
-            raise RuntimeError("hipEventElapsedTime failed")
-        return ms.value
-
-    def destroy(self, ev):
-        self.rt.hipEventDestroy(ev)
-
-
-def upload(w, tensor: str, step: int = 0):
-    """The workload's seeded [B, H, N, d] tensor `tensor` for `step`, on cuda:0."""
     import torch
     from block_causal_linear_phi_amd import workloads as wl
 
+    n = w.N if n_tokens is None else n_tokens
     tdt = torch.bfloat16 if w.dtype == "bf16" else torch.float32
-    x = torch.empty((w.B, w.H, w.N, w.d), dtype=tdt, device=torch.device("cuda:0"))
-    for b in range(w.B):
-        for h in range(w.H):
-            _, raw = wl.slice_qkv(w, tensor, b, h, step)
+    x = torch.empty((w.B, w.H, n, w.d), dtype=tdt, device=torch.device("cuda:0"))
+
+    def one(bh):
+        b, h = bh
+        _, raw = wl.slice_qkv(w, tensor, b, h, step, n)
+        return bh, raw
+
+    with ThreadPoolExecutor(16) as ex:
+        for (b, h), raw in ex.map(one, [(b, h) for b in range(w.B) for h in range(w.H)]):
             src = torch.from_numpy(raw.view("int16") if w.dtype == "bf16" else raw)
             x[b, h].copy_(src.view(tdt) if w.dtype == "bf16" else src)
     return x
 
 
-def gpu_leg(w, steps: int, warmup: int, sets: int):
+def _timed(stream, fn, n):
+    """ms per call of fn(i) over n back-to-back calls between two events."""
+    import torch
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    a.record(stream)
+    for i in range(n):
+        fn(i)
+    b.record(stream)
+    torch.cuda.synchronize()
+    return a.elapsed_time(b) / n
+
+
+def gpu_leg(w, steps: int, warmup: int, sets: int, repeats: int = 0, stage_calls: int = 0):
+    """The forward (sva_lin_attn_fwd) of workload w, `sets` input/output
+    buffer sets alternating.  Returns a dict:
+      ms            ms per step over W untimed + K timed uninstrumented steps;
+      repeat_ms     per-step ms of `repeats` further runs of K steps each;
+      stage_us      per-launch us of each kernel, each timed alone over
+                    `stage_calls` back-to-back launches (sva_lin_attn_fwd_stages)
+                    on the same buffers: no event sits between two launches."""
     import torch
     from block_causal_linear_phi_amd import sva
 
@@ -100,44 +109,28 @@ def gpu_leg(w, steps: int, warmup: int, sets: int):
                          base=w.base, eps=w.eps, dtype=sva.SVA_BF16 if w.dtype == "bf16" else sva.SVA_F32)
     ws = torch.zeros(sva.sva_lin_attn_fwd_workspace(desc), dtype=torch.uint8, device=dev)
     stream = torch.cuda.current_stream()
-    hip = HipEvents()
-    evs = [[hip.create() for _ in range(4)] for _ in range(steps)]
 
-    def step(i, events=None):
-        s = i % sets
-        x = bufs[s]
+    def step(i, stages=sva.SVA_STAGE_ALL):
+        s_ = i % sets
+        x = bufs[s_]
         sva.sva_lin_attn_fwd(x["q"], x["k"], x["v"], (w.T, w.Hs, w.Ws), w.F, t0=w.t0, rope=w.rope,
-                             split=w.split, base=w.base, eps=w.eps, out=outs[s], ws=ws, stream=stream,
-                             events=events)
+                             split=w.split, base=w.base, eps=w.eps, out=outs[s_], ws=ws, stream=stream,
+                             stages=stages)
 
     for i in range(warmup):
         step(i)
     torch.cuda.synchronize()
-    # Timed region: K uninstrumented steps between two synchronisations.
-    t_start = torch.cuda.Event(enable_timing=True)
-    t_end = torch.cuda.Event(enable_timing=True)
-    t_start.record(stream)
-    for i in range(steps):
-        step(warmup + i)
-    t_end.record(stream)
-    torch.cuda.synchronize()
-    total_ms = t_start.elapsed_time(t_end)
-    # Kernel timing: the same K steps again, with the library recording HIP
-    # events on its launch stream around each kernel.  A recorded event costs
-    # a few microseconds of GPU time, so these steps are kept out of the
-    # throughput figure above.
-    for i in range(steps):
-        step(warmup + steps + i, evs[i])
-    torch.cuda.synchronize()
-    per = {"reduce": [], "scan": [], "apply": []}
-    for e in evs:
-        per["reduce"].append(hip.elapsed_ms(e[0], e[1]))
-        per["scan"].append(hip.elapsed_ms(e[1], e[2]))
-        per["apply"].append(hip.elapsed_ms(e[2], e[3]))
-    for e in evs:
-        for x in e:
-            hip.destroy(x)
-    return total_ms, per
+    res = {"ms": _timed(stream, lambda i: step(warmup + i), steps)}
+    res["repeat_ms"] = [_timed(stream, step, steps) for _ in range(repeats)]
+    res["stage_us"] = {}
+    if stage_calls:
+        for name, st in (("reduce", sva.SVA_STAGE_REDUCE), ("scan", sva.SVA_STAGE_SCAN),
+                         ("apply", sva.SVA_STAGE_APPLY)):
+            step(0)  # a full call leaves the prefix operands each stage reads
+            torch.cuda.synchronize()
+            res["stage_us"][name] = 1e3 * _timed(stream, lambda i: step(i, st), stage_calls)
+    del bufs, outs, ws
+    return res
 
 
 def bwd_leg(w, steps: int, warmup: int, sets: int):
@@ -508,6 +501,48 @@ def copy_calibration(mib: int, reps: int = 5):
     del x, y
 
 
+def copy_ceiling(mib: int = 512, reps: int = 10):
+    """A plain device copy (torch copy_ of mib MiB, bf16) on this GPU: the
+    practical HBM ceiling that the roofline fractions are read against."""
+    import torch
+    n = mib * (1 << 20) // 2
+    x = torch.ones(n, dtype=torch.bfloat16, device="cuda:0")
+    y = torch.empty_like(x)
+    for _ in range(3):
+        y.copy_(x)
+    torch.cuda.synchronize()
+    ms = _timed(torch.cuda.current_stream(), lambda i: y.copy_(x), reps)
+    gbs = 2 * n * 2 / (ms * 1e-3) / 1e9
+    del x, y
+    return {"kernel": f"torch copy_ of {mib} MiB (read + write)", "us": ms * 1e3, "GB/s": gbs,
+            "frac_of_peak": gbs / HBM_PEAK_GBS}
+
+
+def other_workloads(steps: int, warmup: int, sets: int):
+    """The other configurations, each timed in this process with the
+    forward's buffer rotation: 480p and the minute stream (one-shot forward,
+    with per-kernel times), the tiny fp32 case, and the cached denoising step
+    (us per step and per commit)."""
+    from block_causal_linear_phi_amd import workloads as wl
+
+    out = {}
+    for name, k_steps in (("480p", steps), ("minute", max(2, steps // 4)), ("tiny", steps)):
+        w = wl.WORKLOADS[name]
+        res = gpu_leg(w, k_steps, warmup, sets if name != "tiny" else 1, stage_calls=k_steps if name != "tiny" else 0)
+        esz = 2 if w.dtype == "bf16" else 4
+        step_bytes = 4 * w.B * w.H * w.N * w.d * esz
+        ent = {"us_per_step": res["ms"] * 1e3, "tokens_per_s": w.B * w.N / (res["ms"] * 1e-3),
+               "hbm_frac_step": step_bytes / (res["ms"] * 1e-3) / (HBM_PEAK_GBS * 1e9), "steps": k_steps}
+        if res["stage_us"]:
+            ent["kernels_us"] = {k: round(v, 2) for k, v in res["stage_us"].items()}
+        out[name] = ent
+    w = wl.WORKLOADS["cached_step"]
+    apply_ms, commit_ms = cached_leg(w, steps, warmup)
+    out["cached_step"] = {"us_per_step": apply_ms * 1e3, "commit_us": commit_ms * 1e3,
+                          "tokens_per_s": w.B * w.block_tokens / (apply_ms * 1e-3)}
+    return out
+
+
 def cpu_leg(w, reps: int):
     """The fp64 oracle on the host: all heads of the workload, `reps` times."""
     import numpy as np
@@ -708,6 +743,10 @@ def main():
     ap.add_argument("--calib-mib", type=int, default=256)
     ap.add_argument("--commands", nargs="*", default=[])
     ap.add_argument("--label", default="", help="summary name suffix, e.g. _bwd")
+    ap.add_argument("--repeats", type=int, default=10,
+                    help="further runs of K steps for the median and min step time")
+    ap.add_argument("--no-others", action="store_true",
+                    help="720p: skip the other workloads and the copy ceiling")
     args = ap.parse_args()
     if args.summarize_profile:
         summarize_profile(args)
@@ -866,14 +905,22 @@ def main():
             / (apply_ms * 1e-3) / (HBM_PEAK_GBS * 1e9),
         }), flush=True)
         return
-    total_ms, per = gpu_leg(w, args.steps, args.warmup, args.sets)
-    ms_per_step = total_ms / args.steps
+    # The other workloads and the copy ceiling are measured first, in the same
+    # process (their steps also bring the clocks up); then the W warm-up and
+    # K timed steps of the headline workload.
+    others = {}
+    copy = None
+    if not args.no_others and w.name == "720p":
+        copy = copy_ceiling()
+        others = other_workloads(args.steps, args.warmup, args.sets)
+    res = gpu_leg(w, args.steps, args.warmup, args.sets, repeats=args.repeats, stage_calls=args.steps)
+    ms_per_step = res["ms"]
     esz = 2 if w.dtype == "bf16" else 4
     elems = w.B * w.H * w.N * w.d
-    alg_bytes = {"reduce": 2 * elems * esz, "apply": 2 * elems * esz, "scan": 0}
-    avg = {k: sum(v) / len(v) for k, v in per.items()}
-    dom = "reduce" if avg["reduce"] >= avg["apply"] else "apply"
-    achieved = alg_bytes[dom] / (avg[dom] * 1e-3) / 1e9
+    alg_bytes = {"reduce": 2 * elems * esz, "apply": 2 * elems * esz}
+    stage_us = res["stage_us"]
+    dom = "reduce" if stage_us["reduce"] >= stage_us["apply"] else "apply"
+    achieved = alg_bytes[dom] / (stage_us[dom] * 1e-6) / 1e9
     traffic = None
     try:
         with open(traffic_file(w.name)) as f:
@@ -883,6 +930,7 @@ def main():
     except (OSError, ValueError):
         traffic = None
     step_bytes = 4 * elems * esz
+    reps = sorted(res["repeat_ms"]) or [ms_per_step]
     line = {
         "metric": "tokens/s (all heads) block-causal linear attn fwd; % of HBM peak",
         "value": w.B * w.N / (ms_per_step * 1e-3),
@@ -901,12 +949,23 @@ def main():
                                f"numerator-only 3D RoPE {w.split[0]}/{w.split[1]}/{w.split[2]}",
                    "B": w.B, "H": w.H, "d": w.d, "tokens": w.N, "blocks": w.nb},
         "hbm_frac_step": step_bytes / (ms_per_step * 1e-3) / (HBM_PEAK_GBS * 1e9),
+        # the step over `repeats` further runs of K steps each (GPU time)
+        "step_us": {"mean": ms_per_step * 1e3, "median": reps[len(reps) // 2] * 1e3, "min": reps[0] * 1e3,
+                    "max": reps[-1] * 1e3, "runs": len(res["repeat_ms"])},
+        # dominant kernel: algorithmic bytes per launch / its duration, the
+        # duration from K back-to-back launches of that kernel alone
         "roofline": {"bound": "hbm", "kernel": dom, "achieved": achieved, "peak": HBM_PEAK_GBS,
                      "unit": "GB/s", "frac": achieved / HBM_PEAK_GBS, "traffic": traffic,
                      "traffic_unit": "GB per launch", "alg_bytes": alg_bytes[dom] / 1e9},
-        "kernels_us": {k: round(v * 1e3, 2) for k, v in avg.items()},
-        "kernels_gbs": {k: round(alg_bytes[k] / (avg[k] * 1e-3) / 1e9, 1) for k in ("reduce", "apply")},
+        "kernels_us": {k: round(v, 2) for k, v in stage_us.items()},
+        "kernels_frac": {k: round(alg_bytes[k] / (stage_us[k] * 1e-6) / 1e9 / HBM_PEAK_GBS, 4)
+                         for k in ("reduce", "apply")},
     }
+    if copy is not None:
+        line["copy_ceiling"] = copy
+        line["hbm_frac_of_copy_ceiling"] = step_bytes / (ms_per_step * 1e-3) / 1e9 / copy["GB/s"]
+    if others:
+        line["other_workloads"] = others
     if not args.no_cpu_baseline:
         line["cpu_baseline"] = cpu_leg(w, args.cpu_reps)
     print(json.dumps(line), flush=True)

@@ -67,10 +67,6 @@ constexpr int kMaxTableEntries = 4096; // RoPE cos/sin table, 32 KiB of LDS
 
 // FastDiv (n / d by multiply and shift) is in internal.h.
 
-// ---------------------------------------------------------------------------
-// phi + 3D RoPE stage (shared by every kernel)
-// ---------------------------------------------------------------------------
-
 // RoPE layout for one call.  The cos/sin table lives in LDS as float2
 // entries: [F rows x dt/2] for t (the frames of the block being processed,
 // rebuilt per block), then [Hs rows x dh/2] for h, then [Ws rows x dw/2] for
@@ -349,21 +345,30 @@ __device__ __forceinline__ void buf_load(uint32_t* dst, __amdgpu_buffer_rsrc_t r
   }
 }
 
-template <int NW>
+template <int NW, int POLICY = kStorePolicy>
 __device__ __forceinline__ void buf_store(__amdgpu_buffer_rsrc_t r, uint32_t off, const uint32_t* src) {
   if constexpr (NW == 1) {
-    __builtin_amdgcn_raw_buffer_store_b32(src[0], r, off, 0, kStorePolicy);
+    __builtin_amdgcn_raw_buffer_store_b32(src[0], r, off, 0, POLICY);
   } else if constexpr (NW == 2) {
     __builtin_amdgcn_raw_buffer_store_b64(__builtin_bit_cast(u32x2, make_uint2(src[0], src[1])), r, off, 0,
-                                          kStorePolicy);
+                                          POLICY);
   } else {
     static_assert(NW % 4 == 0, "word count");
 #pragma unroll
     for (int i = 0; i < NW / 4; ++i)
       __builtin_amdgcn_raw_buffer_store_b128(
-          u32x4{src[4 * i], src[4 * i + 1], src[4 * i + 2], src[4 * i + 3]}, r, off + 16 * i, 0, kStorePolicy);
+          u32x4{src[4 * i], src[4 * i + 1], src[4 * i + 2], src[4 * i + 3]}, r, off + 16 * i, 0, POLICY);
   }
 }
+
+// Device-scope coherence for the folded prefix's exchange through memory
+// (the sc1 bit of gfx94x/gfx950 vector memory instructions): a store is
+// acknowledged only once every XCD can see it, and a load does not take a
+// line that another XCD's L2 may hold stale.  These are the bits the
+// compiler itself gives agent-scope atomic loads and stores; using them on
+// the few bytes exchanged avoids the device-scope fences, each of which
+// writes back or invalidates a whole L2.
+constexpr int kDeviceScope = 16;
 
 // Unpack `CNT` elements (bf16 pairs or fp32 words) into floats.
 template <bool BF16, int CNT>
@@ -460,6 +465,153 @@ struct SplitArgs {
   long long L;      // flattened tokens per workgroup
 };
 
+__device__ __forceinline__ void add4(float4& a, const float4& b) {
+  a.x += b.x; a.y += b.y; a.z += b.z; a.w += b.w;
+}
+
+// ---------------------------------------------------------------------------
+// The prefix over blocks, folded into the reduction
+//
+// Every reduction workgroup that writes its last piece of a sequence (b, h)
+// counts its arrival on that sequence's counter: its pieces are stored with
+// device scope, each wave waits until its stores are acknowledged, the
+// workgroup meets at a barrier, and one thread adds 1 with a device-scope
+// vector atomic.  The workgroup that brings the count to the number of
+// workgroups covering the sequence is the last one: with device-scope loads
+// it reads every piece of the sequence, forms the inclusive prefix S_c, Z_c
+// over its blocks in a fixed order and writes the output pass's operands
+// (and the final cache), then puts the counter back to zero for the next
+// call.  No workgroup ever
+// waits for another, so there is nothing to bound; the counters only have to
+// be zero when a workspace is first used.
+// ---------------------------------------------------------------------------
+
+struct FoldArgs {
+  unsigned* counters;  // [B*H] arrival counters, zero before and after a call
+  const float* S0;     // initial cache [B,H,d,d] in the caller's [fi][fo] layout, or null
+  const float* z0;
+  float* S_out;        // final cache, or null; may be S0/z0 (each element is read before it is written)
+  float* z_out;
+  void* frags;         // prefix operands S_c^T [B*H*nb, d, d] in the input dtype, or null
+  float* zc;           // Z_c [B*H*nb, d] fp32 (written together with frags)
+};
+
+// First and last slot of the pieces of flattened block bhc (the piece of
+// workgroup g sits at slot g + bhc, so a block's pieces are contiguous).  The
+// slot between two blocks is unused when a workgroup range ends exactly at
+// the block boundary.
+__device__ __forceinline__ long long block_first_slot(long long bhc, int Nb, long long L) {
+  return (bhc * Nb) / L + bhc;
+}
+__device__ __forceinline__ long long block_last_slot(long long bhc, int Nb, long long L) {
+  return (bhc * Nb + Nb - 1) / L + bhc;
+}
+
+// The prefix of sequence bh, by one workgroup of NT threads: thread t owns
+// the 4-element groups t, t + NT, ... of a partial (S^T, then z).  The
+// sequence's slots are walked in order, CH per round with all their loads
+// issued at once; each block's sum starts from zero, takes the block's
+// slots in slot order, then is added to the running prefix (the scan
+// kernel's order).  The partials were written by other workgroups during
+// this launch, so they are read with device-scope loads.
+template <bool BF16, int D, int NT>
+__device__ __forceinline__ void scan_sequence(const float* partials, int bh, int nb, int Nb, long long L,
+                                              const FoldArgs& fa) {
+  constexpr int E = D * D + D;
+  constexpr int E4 = E / 4;
+  constexpr int NG = (E4 + NT - 1) / NT;
+  constexpr int CH = 8;
+  // The thread index goes through an empty asm so that the addresses below
+  // are computed here, not hoisted to the kernel's start where they would
+  // stay live (and spill) across the streaming loop.
+  int tid = threadIdx.x;
+  asm volatile("" : "+v"(tid));
+  int e[NG];
+  float4 run[NG], acc[NG];
+#pragma unroll
+  for (int i = 0; i < NG; ++i) {
+    e[i] = min(4 * (tid + i * NT), E - 4);  // threads past the end repeat the last group and store nothing
+    run[i] = acc[i] = make_float4(0.f, 0.f, 0.f, 0.f);
+    if (fa.S0) {  // element e of S^T is S[e % D][e / D]
+      if (e[i] < D * D) {
+        const float* s0 = fa.S0 + (long long)bh * D * D + (e[i] % D) * D + e[i] / D;
+        run[i] = make_float4(s0[0], s0[D], s0[2 * D], s0[3 * D]);
+      } else {
+        run[i] = *(const float4*)(fa.z0 + (long long)bh * D + (e[i] - D * D));
+      }
+    }
+  }
+  auto owns = [&](int i) { return NG * NT == E4 || tid + i * NT < E4; };
+  const long long bhc0 = (long long)bh * nb;
+  const long long s_first = block_first_slot(bhc0, Nb, L);
+  const long long s_last = block_last_slot(bhc0 + nb - 1, Nb, L);
+  long long s_beg = s_first;  // slots of the current block c
+  long long s_end = block_last_slot(bhc0, Nb, L);
+  int c = 0;
+  // device-scope loads over the sequence's slots (see kDeviceScope)
+  const __amdgpu_buffer_rsrc_t prs =
+      make_rsrc(partials + s_first * E, (uint32_t)((s_last - s_first + 1) * E * sizeof(float)));
+  for (long long s0 = s_first; s0 <= s_last; s0 += CH) {
+    float4 x[CH][NG];
+#pragma unroll
+    for (int j = 0; j < CH; ++j) {
+      const long long sj = min(s0 + j, s_last);  // slots past the last one repeat it and are not added
+#pragma unroll
+      for (int i = 0; i < NG; ++i) {
+        uint32_t w[4];
+        buf_load<4, kDeviceScope>(w, prs, (uint32_t)((sj - s_first) * E + e[i]) * 4);
+        x[j][i] = make_float4(__uint_as_float(w[0]), __uint_as_float(w[1]), __uint_as_float(w[2]),
+                              __uint_as_float(w[3]));
+      }
+    }
+#pragma unroll
+    for (int j = 0; j < CH; ++j) {
+      const long long sj = s0 + j;
+      if (sj > s_last) break;
+      if (sj >= s_beg) {
+#pragma unroll
+        for (int i = 0; i < NG; ++i) add4(acc[i], x[j][i]);
+      }
+      if (sj == s_end) {  // block c complete: extend the prefix and emit it
+        const long long bhc = bhc0 + c;
+#pragma unroll
+        for (int i = 0; i < NG; ++i) {
+          add4(run[i], acc[i]);
+          acc[i] = make_float4(0.f, 0.f, 0.f, 0.f);
+          if (!fa.frags || !owns(i)) continue;
+          if (e[i] < D * D) {
+            if (BF16) {
+              *(uint2*)((__bf16*)fa.frags + bhc * D * D + e[i]) =
+                  make_uint2(pack_bf16x2(run[i].x, run[i].y), pack_bf16x2(run[i].z, run[i].w));
+            } else {
+              *(float4*)((float*)fa.frags + bhc * D * D + e[i]) = run[i];
+            }
+          } else {
+            *(float4*)(fa.zc + bhc * D + (e[i] - D * D)) = run[i];
+          }
+        }
+        ++c;
+        if (c < nb) {
+          s_beg = block_first_slot(bhc0 + c, Nb, L);
+          s_end = block_last_slot(bhc0 + c, Nb, L);
+        }
+      }
+    }
+  }
+  if (fa.S_out) {
+#pragma unroll
+    for (int i = 0; i < NG; ++i) {
+      if (!owns(i)) continue;
+      if (e[i] < D * D) {
+        float* so = fa.S_out + (long long)bh * D * D + (e[i] % D) * D + e[i] / D;
+        so[0] = run[i].x; so[D] = run[i].y; so[2 * D] = run[i].z; so[3 * D] = run[i].w;
+      } else {
+        *(float4*)(fa.z_out + (long long)bh * D + (e[i] - D * D)) = run[i];
+      }
+    }
+  }
+}
+
 // ---------------------------------------------------------------------------
 // Kernel 1: per-block state reduction
 //
@@ -472,10 +624,10 @@ struct SplitArgs {
 // Accumulator (r, s)[i] of lane l holds S[FPL*(4*(l/16)+i)+r][FPL*(l%16)+s].
 // ---------------------------------------------------------------------------
 
-template <bool BF16, int D, int ROPE>
+template <bool BF16, int D, int ROPE, bool FOLD>
 __global__ __launch_bounds__(red_threads<BF16>(), red_min_blocks<BF16>()) void sva_reduce_kernel(
     const void* __restrict__ kp, const void* __restrict__ vp, float* __restrict__ partials,
-    Geo geo, SplitArgs sp, RopeArgs ra) {
+    Geo geo, SplitArgs sp, RopeArgs ra, FoldArgs fa) {
   constexpr int RT = red_threads<BF16>();
   constexpr int FPL = D / 16;
   constexpr int NPAIR = FPL / 2;
@@ -495,6 +647,7 @@ __global__ __launch_bounds__(red_threads<BF16>(), red_min_blocks<BF16>()) void s
   static_assert(NWV == NT || NWV == 2 * NT, "waves per workgroup");
   __shared__ float red[NT][D * D];
   __shared__ float zred[NWV][D];
+  __shared__ int fold_last;
 
   const int tid = threadIdx.x;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform
@@ -503,18 +656,18 @@ __global__ __launch_bounds__(red_threads<BF16>(), red_min_blocks<BF16>()) void s
   const int tg = lane >> 4;
 
   const double lane_freq = ROPE ? load_lane_freq(ra) : 0.0;
-  PairLoc pl[NPAIR > 0 ? NPAIR : 1];
-  if (ROPE) {
-#pragma unroll
-    for (int pp = 0; pp < NPAIR; ++pp) pl[pp] = pair_loc(NPAIR * cg + pp, ra);
-  }
+  PairLoc pl[NPAIR > 0 ? NPAIR : 1];  // set per segment, once the first loads are out
 
   const long long g0 = (long long)blockIdx.x * sp.L;
   const long long g1 = min(g0 + sp.L, sp.total);
   const char* kb = (const char*)kp;
   const char* vb = (const char*)vp;
 
-  for (long long pos = g0; pos < g1;) {
+  // Every workgroup has at least one token (the grid is ceil(total / L)), so the
+  // loop needs no entry test, which would split the reads of the kernel
+  // arguments into two dependent rounds.
+  long long pos = g0;
+  do {
     const long long bhc = pos / geo.Nb;
     const long long seg_end = min(g1, (bhc + 1) * (long long)geo.Nb);
     const int bh = (int)(bhc / geo.nb);
@@ -613,6 +766,15 @@ __global__ __launch_bounds__(red_threads<BF16>(), red_min_blocks<BF16>()) void s
     load_step(kA, vA, s_first);
     load_step(kB, vB, s_first + WSTRIDE);
     __builtin_amdgcn_sched_barrier(0);
+    // The RoPE layout is read from the kernel arguments only now, so that
+    // the streaming loads above wait for no more than the pointers and the
+    // split.
+    if (ROPE) {
+      int cg_seg = cg;  // opaque per segment: keeps this setup below the loads
+      asm volatile("" : "+v"(cg_seg));
+#pragma unroll
+      for (int pp = 0; pp < NPAIR; ++pp) pl[pp] = pair_loc(NPAIR * cg_seg + pp, ra);
+    }
     // The RoPE table (h, w rows once; t rows for this block) is built while
     // the first loads are in flight.  Every wave has passed the previous
     // segment's epilogue barrier, so no wave still reads the old t rows.
@@ -685,7 +847,10 @@ __global__ __launch_bounds__(red_threads<BF16>(), red_min_blocks<BF16>()) void s
     // along the flattened token axis, so g + bhc strictly increases from one
     // piece to the next and the slots of one block's pieces are contiguous.
     // A partial holds S transposed (row fo, column fi), then z.
-    float* dst = partials + ((long long)blockIdx.x + bhc) * E;
+    // (Stored with device scope when the prefix is folded in: the last
+    // workgroup of the sequence, on any XCD, reads them back.)
+    constexpr int PP = FOLD ? kDeviceScope : 0;
+    const __amdgpu_buffer_rsrc_t prs = make_rsrc(partials + ((long long)blockIdx.x + bhc) * E, E * 4);
     for (int e = tid; e < D * D / 4; e += RT) {
       const int fo = e % D, fi0 = 4 * (e / D);  // consecutive lanes: consecutive fo
       float t[4];
@@ -695,17 +860,45 @@ __global__ __launch_bounds__(red_threads<BF16>(), red_min_blocks<BF16>()) void s
 #pragma unroll
         for (int w = 1; w < NT; ++w) t[j] += red[w][(fi0 + j) * D + fo];
       }
-      *(float4*)(dst + fo * D + fi0) = make_float4(t[0], t[1], t[2], t[3]);
+      const uint32_t w4[4] = {__float_as_uint(t[0]), __float_as_uint(t[1]), __float_as_uint(t[2]),
+                              __float_as_uint(t[3])};
+      buf_store<4, PP>(prs, (uint32_t)(fo * D + fi0) * 4, w4);
     }
     for (int e = tid; e < D; e += RT) {
       float t = zred[0][e];
 #pragma unroll
       for (int w = 1; w < NWV; ++w) t += zred[w][e];
-      dst[D * D + e] = t;
+      const uint32_t w1 = __float_as_uint(t);
+      buf_store<1, PP>(prs, (uint32_t)(D * D + e) * 4, &w1);
+    }
+    if constexpr (FOLD) {
+      // This workgroup's last piece of sequence bh: count the arrival (see
+      // the folded prefix above); the last arrival forms bh's prefix.  The
+      // pieces were stored with device scope: each wave waits until its
+      // stores are acknowledged, the workgroup meets, then one thread counts
+      // with a device-scope atomic.  The empty asm statements keep the
+      // compiler from moving memory accesses across these points.
+      if (seg_end >= g1 || seg_end == (long long)(bh + 1) * geo.N) {
+        asm volatile("" ::: "memory");
+        __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): this wave's stores are visible device-wide
+        __builtin_amdgcn_s_barrier();
+        if (tid == 0) {
+          const long long first = (long long)bh * geo.N / sp.L;
+          const long long last = ((long long)(bh + 1) * geo.N - 1) / sp.L;
+          const unsigned old = __hip_atomic_fetch_add(fa.counters + bh, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+          fold_last = old + 1 == (unsigned)(last - first + 1);
+        }
+        lds_barrier();
+        if (fold_last) {
+          asm volatile("" ::: "memory");
+          scan_sequence<BF16, D, RT>(partials, bh, geo.nb, geo.Nb, sp.L, fa);
+          if (tid == 0) __hip_atomic_store(fa.counters + bh, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        }
+      }
     }
     // `red` is next written after the next segment's barrier.
     pos = seg_end;
-  }
+  } while (pos < g1);
 }
 
 // ---------------------------------------------------------------------------
@@ -731,10 +924,6 @@ struct ScanArgs {
 constexpr int kScanLanes = 8;                      // block-lanes per element
 constexpr int kScanElems = kThreads / kScanLanes;  // 4-element groups per workgroup
 
-// Sum, in slot order, of the partials of flattened block bhc at element e.
-__device__ __forceinline__ void add4(float4& a, const float4& b) {
-  a.x += b.x; a.y += b.y; a.z += b.z; a.w += b.w;
-}
 
 // Sum, in slot order, of the partials of flattened block bhc at elements
 // e .. e+3.
@@ -919,18 +1108,18 @@ __global__ __launch_bounds__(app_threads<BF16>(), app_min_blocks<BF16>()) void s
   constexpr bool RUNS = BF16 && ROPE == 3;
   constexpr int NLOC = RUNS ? NKS : NPAIR;
   const double lane_freq = ROPE ? load_lane_freq(ra) : 0.0;
-  PairLoc pl[NLOC];
-  if (ROPE) {
-#pragma unroll
-    for (int i = 0; i < NLOC; ++i) pl[i] = pair_loc(apply_feat<BF16>(g, RUNS ? 8 * i : 2 * i) >> 1, ra);
-  }
+  PairLoc pl[NLOC];  // set per segment, once the first loads are out
 
   const long long g0 = (long long)blockIdx.x * sp.L;
   const long long g1 = min(g0 + sp.L, sp.total);
   const char* qb = (const char*)qp;
   char* ob = (char*)outp;
 
-  for (long long pos = g0; pos < g1;) {
+  // Every workgroup has at least one token (the grid is ceil(total / L)), so the
+  // loop needs no entry test, which would split the reads of the kernel
+  // arguments into two dependent rounds.
+  long long pos = g0;
+  do {
     const long long bhc = pos / geo.Nb;
     const long long seg_end = min(g1, (bhc + 1) * (long long)geo.Nb);
     const int bh = (int)(bhc / geo.nb);
@@ -999,6 +1188,14 @@ __global__ __launch_bounds__(app_threads<BF16>(), app_min_blocks<BF16>()) void s
     load_stepq(qa, t_first);
     load_stepq(qb, t_first + WSTRIDE);
     __builtin_amdgcn_sched_barrier(0);
+    // the RoPE layout is read from the kernel arguments only now (as in the
+    // reduction)
+    if (ROPE) {
+      int g_seg = g;  // opaque per segment: keeps this setup below the loads
+      asm volatile("" : "+v"(g_seg));
+#pragma unroll
+      for (int i = 0; i < NLOC; ++i) pl[i] = pair_loc(apply_feat<BF16>(g_seg, RUNS ? 8 * i : 2 * i) >> 1, ra);
+    }
 #pragma unroll
     for (int i = 0; i < FR; ++i) {
       const int u = tid + i * AT;
@@ -1214,7 +1411,7 @@ __global__ __launch_bounds__(app_threads<BF16>(), app_min_blocks<BF16>()) void s
     if (k < nsteps) compute_stepq(qa, t_first + k * WSTRIDE);
     if (k + 1 < nsteps) compute_stepq(qb, t_first + (k + 1) * WSTRIDE);
     pos = seg_end;
-  }
+  } while (pos < g1);
 }
 
 // ---------------------------------------------------------------------------
@@ -1452,7 +1649,11 @@ __global__ __launch_bounds__(kThreads, 1) void sva_bwd_out_kernel(
 
   const long long g0 = (long long)blockIdx.x * sp.L;
   const long long g1 = min(g0 + sp.L, sp.total);
-  for (long long pos = g0; pos < g1;) {
+  // Every workgroup has at least one token (the grid is ceil(total / L)), so the
+  // loop needs no entry test, which would split the reads of the kernel
+  // arguments into two dependent rounds.
+  long long pos = g0;
+  do {
     const long long bhc = pos / geo.Nb;
     const long long seg_end = min(g1, (bhc + 1) * (long long)geo.Nb);
     const int bh = (int)(bhc / geo.nb);
@@ -1682,7 +1883,7 @@ __global__ __launch_bounds__(kThreads, 1) void sva_bwd_out_kernel(
       dst[D * D + e] = t1;
     }
     pos = seg_end;
-  }
+  } while (pos < g1);
 }
 
 // State side: k, v -> dk, dv.  gfrag holds G_c^T (bf16) and gc holds g_c per
@@ -1723,7 +1924,11 @@ __global__ __launch_bounds__(kThreads, 2) void sva_bwd_kv_kernel(
 
   const long long g0 = (long long)blockIdx.x * sp.L;
   const long long g1 = min(g0 + sp.L, sp.total);
-  for (long long pos = g0; pos < g1;) {
+  // Every workgroup has at least one token (the grid is ceil(total / L)), so the
+  // loop needs no entry test, which would split the reads of the kernel
+  // arguments into two dependent rounds.
+  long long pos = g0;
+  do {
     const long long bhc = pos / geo.Nb;
     const long long seg_end = min(g1, (bhc + 1) * (long long)geo.Nb);
     const int bh = (int)(bhc / geo.nb);
@@ -1831,7 +2036,7 @@ __global__ __launch_bounds__(kThreads, 2) void sva_bwd_kv_kernel(
     }
     if (k < nsteps) compute(xa, t_first + k * WSTRIDE);
     pos = seg_end;
-  }
+  } while (pos < g1);
 }
 
 // ---------------------------------------------------------------------------
@@ -1890,13 +2095,17 @@ struct Plan {
   SplitArgs bwd, bwd_kv;  // backward output side and state side
   int G_bwd_out, G_bwd_kv;
   size_t tab_bytes;
-  size_t off_partials, off_frags, off_zc, ws_bytes;
+  // The forward's prefix runs inside the reduction (the last workgroup of
+  // each sequence forms it) instead of in a separate scan launch.
+  bool fold;
+  size_t off_counters, off_partials, off_frags, off_zc, ws_bytes;
   size_t states_zc, states_bytes;  // saved prefix states: operands at 0, Z_c at states_zc
 };
 
 constexpr long long kRedWorkgroupsMax = 1024;  // bounds the partials workspace
 constexpr long long kAppWorkgroupsMax = 4096;
 constexpr long long kMinTokensPerWG = 256;
+constexpr int kFoldMinBlocks = 32;  // blocks per sequence from which the prefix is folded
 
 size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 
@@ -1975,6 +2184,25 @@ sva_status validate_desc(const sva_desc* d, bool one_block) {
   return SVA_OK;
 }
 
+// Workspace layout for a reduction grid of at most max_red_wg workgroups:
+// arrival counters, then the partials (a piece of workgroup g and block c
+// sits in slot g + c, so max_red_wg + B*H*nb slots always suffice), then the
+// prefix operands and Z_c; every region 256-byte aligned.
+void layout_workspace(Plan* p, long long max_red_wg) {
+  const size_t E = (size_t)p->D * p->D + p->D;
+  const size_t esz = p->bf16 ? 2 : 4;
+  size_t off = 0;
+  p->off_counters = off;  // B*H arrival counters of the folded prefix: zero between calls
+  off = align256(off + (size_t)p->BH * sizeof(unsigned));
+  p->off_partials = off;
+  off = align256(off + (size_t)(max_red_wg + (long long)p->BH * p->nb) * E * sizeof(float));
+  p->off_frags = off;
+  off = align256(off + (size_t)p->BH * p->nb * p->D * p->D * esz);
+  p->off_zc = off;
+  off = align256(off + (size_t)p->BH * p->nb * p->D * sizeof(float));
+  p->ws_bytes = off;
+}
+
 Plan make_plan(const sva_desc* d) {
   Plan p;
   memset(&p, 0, sizeof(p));
@@ -2022,35 +2250,40 @@ Plan make_plan(const sva_desc* d) {
         ra.inv_rev[p_idx++] = __builtin_pow((double)d->rope_base, -2.0 * i / widths[ax]) / two_pi;
     p.tab_bytes = (size_t)ra.n_entries * sizeof(float2);
   }
+  // The prefix folded into the reduction saves the scan launch but makes
+  // every reduction workgroup wait for its device-scope stores and atomic,
+  // and leaves one workgroup per sequence to read all of that sequence's
+  // pieces.  Measured on MI355X it is slower for short sequences (one block
+  // of 16 heads: 35.7 against 27.8 us per step; 720p: 125.7 against 110.2
+  // us) and slightly faster for long ones (80 blocks: 1214.9 against 1223.6
+  // us), where the scan kernel's own read of the partials is large.
+  p.fold = p.nb >= kFoldMinBlocks;
   const long long total = (long long)p.BH * p.N;
   // Grids are fixed at launch from the device's occupancy (plan_grids); the
   // workspace is sized for the largest reduce grid.  Piece (g, block) of the
   // reduce lives in slot g + block, so G + B*H*nb slots always suffice.
   p.red = make_split(total, kRedWorkgroupsMax, &p.G_red);
   p.app = make_split(total, kAppWorkgroupsMax, &p.G_app);
-  const size_t E = (size_t)p.D * p.D + p.D;
+  layout_workspace(&p, kRedWorkgroupsMax);
   const size_t esz = p.bf16 ? 2 : 4;
-  size_t off = 0;
-  p.off_partials = off;
-  off = align256(off + (size_t)(kRedWorkgroupsMax + (long long)p.BH * p.nb) * E * sizeof(float));
-  p.off_frags = off;
-  off = align256(off + (size_t)p.BH * p.nb * p.D * p.D * esz);
-  p.off_zc = off;
-  off = align256(off + (size_t)p.BH * p.nb * p.D * sizeof(float));
-  p.ws_bytes = off;
   p.states_zc = align256((size_t)p.BH * p.nb * p.D * p.D * esz);
   p.states_bytes = p.states_zc + align256((size_t)p.BH * p.nb * p.D * sizeof(float));
   return p;
 }
 
+// The reduction; with `fold` non-null it also forms the prefix (FoldArgs).
 template <bool BF16, int D, int ROPE>
-hipError_t launch_reduce(const Plan& p, const void* k, const void* v, float* partials, hipStream_t st) {
+hipError_t launch_reduce(const Plan& p, const void* k, const void* v, float* partials, hipStream_t st,
+                         const FoldArgs* fold = nullptr) {
   Geo geo = p.geo;
   SplitArgs sp = p.red;
   RopeArgs ra = p.ra;
-  void* args[] = {(void*)&k, (void*)&v, (void*)&partials, &geo, &sp, &ra};
-  return hipLaunchKernel((const void*)&sva_reduce_kernel<BF16, D, (ROPE == 3 ? 2 : ROPE)>, dim3(p.G_red),
-                         dim3(red_threads<BF16>()), args, ROPE ? p.tab_bytes : 0, st);
+  FoldArgs fa = fold ? *fold : FoldArgs{};
+  void* args[] = {(void*)&k, (void*)&v, (void*)&partials, &geo, &sp, &ra, &fa};
+  constexpr int RM = ROPE == 3 ? 2 : ROPE;
+  const void* fn = fold ? (const void*)&sva_reduce_kernel<BF16, D, RM, true>
+                        : (const void*)&sva_reduce_kernel<BF16, D, RM, false>;
+  return hipLaunchKernel(fn, dim3(p.G_red), dim3(red_threads<BF16>()), args, ROPE ? p.tab_bytes : 0, st);
 }
 
 template <bool BF16, int D>
@@ -2141,7 +2374,9 @@ template <bool BF16, int D, int ROPE>
 int plan_grids_t(Plan* p) {
   const long long total = (long long)p->BH * p->N;
   const size_t lds = ROPE ? p->tab_bytes : 0;
-  const long long r = resident_workgroups((const void*)&sva_reduce_kernel<BF16, D, (ROPE == 3 ? 2 : ROPE)>, red_threads<BF16>(), lds);
+  const void* red_fn = p->fold ? (const void*)&sva_reduce_kernel<BF16, D, (ROPE == 3 ? 2 : ROPE), true>
+                               : (const void*)&sva_reduce_kernel<BF16, D, (ROPE == 3 ? 2 : ROPE), false>;
+  const long long r = resident_workgroups(red_fn, red_threads<BF16>(), lds);
   const long long a = resident_workgroups((const void*)&sva_apply_kernel<BF16, D, (!BF16 && ROPE == 3 ? 2 : ROPE)>, app_threads<BF16>(), lds);
   p->red = make_split(total, r < kRedWorkgroupsMax ? r : kRedWorkgroupsMax, &p->G_red);
   p->app = make_split(total, a < kAppWorkgroupsMax ? a : kAppWorkgroupsMax, &p->G_app);
@@ -2176,12 +2411,9 @@ sva_status check_common(const sva_desc* d, bool one_block, Plan* p) {
   return SVA_OK;
 }
 
-sva_status run_fwd(const sva_desc* desc, const void* q, const void* k, const void* v, void* out,
-                   const float* S0, const float* z0, float* S_out, float* z_out, void* ws,
-                   size_t ws_bytes, void* stream, void* const* events, void* states = nullptr) {
-  Plan p;
-  sva_status s = check_common(desc, false, &p);
-  if (s != SVA_OK) return s;
+// Pointer checks of the forward (before any launch).
+sva_status check_fwd_pointers(const Plan& p, const void* q, const void* k, const void* v, const void* out,
+                              const float* S0, const float* z0, const float* S_out, const float* z_out) {
   if (!q || !k || !v || !out) return SVA_ERR_INVALID_ARG;
   if (!is_aligned16(q) || !is_aligned16(k) || !is_aligned16(v) || !is_aligned16(out))
     return SVA_ERR_INVALID_ARG;
@@ -2194,32 +2426,46 @@ sva_status run_fwd(const sva_desc* desc, const void* q, const void* k, const voi
   if (overlaps(out, nbytes, q, nbytes) || overlaps(out, nbytes, k, nbytes) ||
       overlaps(out, nbytes, v, nbytes))
     return SVA_ERR_INVALID_ARG;
-  if (!ws || ws_bytes < p.ws_bytes || !is_aligned16(ws)) return SVA_ERR_WORKSPACE;
-  if (states && !is_aligned16(states)) return SVA_ERR_INVALID_ARG;
-  if (events) {
-    for (int i = 0; i < 4; ++i)
-      if (!events[i]) return SVA_ERR_INVALID_ARG;
-  }
+  return SVA_OK;
+}
 
-  plan_grids(&p);
-  hipStream_t st = (hipStream_t)stream;
-  char* wsb = (char*)ws;
+// The forward's kernels for plan p (grids set) on the workspace at wsb.
+sva_status launch_fwd(const Plan& p, const void* q, const void* k, const void* v, void* out, const float* S0,
+                      const float* z0, float* S_out, float* z_out, char* wsb, int stages, void* states,
+                      float eps, hipStream_t st) {
   float* partials = (float*)(wsb + p.off_partials);
   // the prefix states go to the caller's buffer when it keeps them
   void* frags = states ? states : (void*)(wsb + p.off_frags);
   float* zc = states ? (float*)((char*)states + p.states_zc) : (float*)(wsb + p.off_zc);
-  hipError_t e = hipSuccess;
-  if (events && (e = hipEventRecord((hipEvent_t)events[0], st)) != hipSuccess) return SVA_ERR_HIP;
-  if ((e = SVA_DISPATCH(p, launch_reduce, p, k, v, partials, st)) != hipSuccess) return SVA_ERR_HIP;
-  if (events && (e = hipEventRecord((hipEvent_t)events[1], st)) != hipSuccess) return SVA_ERR_HIP;
-  if ((e = SVA_DISPATCH2(p, launch_scan, p, partials, S0, z0, S_out, z_out, frags, zc, true, st)) !=
-      hipSuccess)
+  if (p.fold) {
+    const FoldArgs fa{(unsigned*)(wsb + p.off_counters), S0, z0, S_out, z_out, frags, zc};
+    if ((stages & SVA_STAGE_REDUCE) && SVA_DISPATCH(p, launch_reduce, p, k, v, partials, st, &fa) != hipSuccess)
+      return SVA_ERR_HIP;
+  } else {
+    if ((stages & SVA_STAGE_REDUCE) && SVA_DISPATCH(p, launch_reduce, p, k, v, partials, st) != hipSuccess)
+      return SVA_ERR_HIP;
+    if ((stages & SVA_STAGE_SCAN) &&
+        SVA_DISPATCH2(p, launch_scan, p, partials, S0, z0, S_out, z_out, frags, zc, true, st) != hipSuccess)
+      return SVA_ERR_HIP;
+  }
+  if ((stages & SVA_STAGE_APPLY) && SVA_DISPATCH(p, launch_apply, p, q, out, frags, zc, eps, st) != hipSuccess)
     return SVA_ERR_HIP;
-  if (events && (e = hipEventRecord((hipEvent_t)events[2], st)) != hipSuccess) return SVA_ERR_HIP;
-  if ((e = SVA_DISPATCH(p, launch_apply, p, q, out, frags, zc, desc->eps, st)) != hipSuccess)
-    return SVA_ERR_HIP;
-  if (events && (e = hipEventRecord((hipEvent_t)events[3], st)) != hipSuccess) return SVA_ERR_HIP;
   return SVA_OK;
+}
+
+sva_status run_fwd(const sva_desc* desc, const void* q, const void* k, const void* v, void* out,
+                   const float* S0, const float* z0, float* S_out, float* z_out, void* ws,
+                   size_t ws_bytes, void* stream, int stages = SVA_STAGE_ALL, void* states = nullptr) {
+  Plan p;
+  sva_status s = check_common(desc, false, &p);
+  if (s != SVA_OK) return s;
+  if ((s = check_fwd_pointers(p, q, k, v, out, S0, z0, S_out, z_out)) != SVA_OK) return s;
+  if (!ws || ws_bytes < p.ws_bytes || !is_aligned16(ws)) return SVA_ERR_WORKSPACE;
+  if (states && !is_aligned16(states)) return SVA_ERR_INVALID_ARG;
+  if (stages < 1 || stages > SVA_STAGE_ALL) return SVA_ERR_INVALID_ARG;
+  plan_grids(&p);
+  return launch_fwd(p, q, k, v, out, S0, z0, S_out, z_out, (char*)ws, stages, states, desc->eps,
+                    (hipStream_t)stream);
 }
 
 sva_status run_bwd(const sva_desc* desc, const void* q, const void* k, const void* v, const void* out,
@@ -2252,6 +2498,7 @@ sva_status run_bwd(const sva_desc* desc, const void* q, const void* k, const voi
   if (!ws || ws_bytes < p.ws_bytes || !is_aligned16(ws)) return SVA_ERR_WORKSPACE;
   if (states && !is_aligned16(states)) return SVA_ERR_INVALID_ARG;
 
+  p.fold = false;  // the backward recomputes the prefix with the scan kernel
   plan_grids(&p);
   plan_bwd_grids(&p);
   hipStream_t st = (hipStream_t)stream;
@@ -2443,7 +2690,7 @@ sva_status sva_lin_attn_fwd_workspace(const sva_desc* desc, size_t* bytes) {
 sva_status sva_lin_attn_fwd(const sva_desc* desc, const void* q, const void* k, const void* v,
                             void* out, const float* S0, const float* z0, float* S_out,
                             float* z_out, void* ws, size_t ws_bytes, void* stream) {
-  return run_fwd(desc, q, k, v, out, S0, z0, S_out, z_out, ws, ws_bytes, stream, nullptr);
+  return run_fwd(desc, q, k, v, out, S0, z0, S_out, z_out, ws, ws_bytes, stream);
 }
 
 sva_status sva_proj_lin_attn_fwd_workspace(const sva_desc* attn, const sva_proj_desc* proj, size_t* bytes) {
@@ -2462,12 +2709,10 @@ sva_status sva_proj_lin_attn_fwd(const sva_desc* attn, const sva_proj_desc* proj
   return run_proj_fwd(attn, proj, x, wpack, bias, out, S0, z0, S_out, z_out, ws, ws_bytes, stream);
 }
 
-sva_status sva_lin_attn_fwd_traced(const sva_desc* desc, const void* q, const void* k,
-                                   const void* v, void* out, const float* S0, const float* z0,
-                                   float* S_out, float* z_out, void* ws, size_t ws_bytes,
-                                   void* stream, void* const events[4]) {
-  if (!events) return SVA_ERR_INVALID_ARG;
-  return run_fwd(desc, q, k, v, out, S0, z0, S_out, z_out, ws, ws_bytes, stream, events);
+sva_status sva_lin_attn_fwd_stages(const sva_desc* desc, const void* q, const void* k, const void* v,
+                                   void* out, const float* S0, const float* z0, float* S_out,
+                                   float* z_out, void* ws, size_t ws_bytes, void* stream, int stages) {
+  return run_fwd(desc, q, k, v, out, S0, z0, S_out, z_out, ws, ws_bytes, stream, stages);
 }
 
 sva_status sva_lin_attn_bwd_workspace(const sva_desc* desc, size_t* bytes) {
@@ -2503,7 +2748,7 @@ sva_status sva_lin_attn_fwd_save(const sva_desc* desc, const void* q, const void
                                  float* z_out, void* states, void* ws, size_t ws_bytes,
                                  void* stream) {
   if (!states) return SVA_ERR_INVALID_ARG;
-  return run_fwd(desc, q, k, v, out, S0, z0, S_out, z_out, ws, ws_bytes, stream, nullptr, states);
+  return run_fwd(desc, q, k, v, out, S0, z0, S_out, z_out, ws, ws_bytes, stream, SVA_STAGE_ALL, states);
 }
 
 sva_status sva_block_cache_workspace(const sva_desc* desc, size_t* bytes) {
@@ -2522,7 +2767,7 @@ sva_status sva_block_cache_apply(const sva_desc* desc, const float* S, const flo
   sva_status s = check_common(desc, true, &p);
   if (s != SVA_OK) return s;
   if (!S || !z) return SVA_ERR_INVALID_ARG;
-  return run_fwd(desc, q, k, v, out, S, z, nullptr, nullptr, ws, ws_bytes, stream, nullptr);
+  return run_fwd(desc, q, k, v, out, S, z, nullptr, nullptr, ws, ws_bytes, stream);
 }
 
 sva_status sva_block_cache_commit(const sva_desc* desc, float* S, float* z, const void* k,
@@ -2538,10 +2783,14 @@ sva_status sva_block_cache_commit(const sva_desc* desc, float* S, float* z, cons
   hipStream_t st = (hipStream_t)stream;
   char* wsb = (char*)ws;
   float* partials = (float*)(wsb + p.off_partials);
-  if (SVA_DISPATCH(p, launch_reduce, p, k, v, partials, st) != hipSuccess) return SVA_ERR_HIP;
-  if (SVA_DISPATCH2(p, launch_scan, p, partials, S, z, S, z, nullptr, nullptr, false, st) !=
-      hipSuccess)
-    return SVA_ERR_HIP;
+  if (p.fold) {
+    const FoldArgs fa{(unsigned*)(wsb + p.off_counters), S, z, S, z, nullptr, nullptr};
+    if (SVA_DISPATCH(p, launch_reduce, p, k, v, partials, st, &fa) != hipSuccess) return SVA_ERR_HIP;
+  } else {
+    if (SVA_DISPATCH(p, launch_reduce, p, k, v, partials, st) != hipSuccess) return SVA_ERR_HIP;
+    if (SVA_DISPATCH2(p, launch_scan, p, partials, S, z, S, z, nullptr, nullptr, false, st) != hipSuccess)
+      return SVA_ERR_HIP;
+  }
   return SVA_OK;
 }
 

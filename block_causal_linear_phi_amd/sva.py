@@ -13,6 +13,11 @@ from typing import Optional, Sequence, Tuple
 SVA_F32 = 0
 SVA_BF16 = 1
 
+SVA_STAGE_REDUCE = 1
+SVA_STAGE_SCAN = 2
+SVA_STAGE_APPLY = 4
+SVA_STAGE_ALL = 7
+
 SVA_OK = 0
 SVA_ERR_INVALID_ARG = -1
 SVA_ERR_UNSUPPORTED = -2
@@ -61,8 +66,8 @@ _SIG = {
     "sva_lin_attn_fwd_workspace": (ctypes.c_int, [ctypes.POINTER(SvaDesc), ctypes.POINTER(ctypes.c_size_t)]),
     "sva_lin_attn_fwd": (ctypes.c_int, [ctypes.POINTER(SvaDesc), _VP, _VP, _VP, _VP, _VP, _VP, _VP, _VP,
                                         _VP, ctypes.c_size_t, _VP]),
-    "sva_lin_attn_fwd_traced": (ctypes.c_int, [ctypes.POINTER(SvaDesc), _VP, _VP, _VP, _VP, _VP, _VP, _VP,
-                                               _VP, _VP, ctypes.c_size_t, _VP, ctypes.POINTER(_VP)]),
+    "sva_lin_attn_fwd_stages": (ctypes.c_int, [ctypes.POINTER(SvaDesc), _VP, _VP, _VP, _VP, _VP, _VP, _VP,
+                                               _VP, _VP, ctypes.c_size_t, _VP, ctypes.c_int]),
     "sva_lin_attn_bwd_workspace": (ctypes.c_int, [ctypes.POINTER(SvaDesc), ctypes.POINTER(ctypes.c_size_t)]),
     "sva_lin_attn_bwd": (ctypes.c_int, [ctypes.POINTER(SvaDesc)] + [_VP] * 16 + [ctypes.c_size_t, _VP]),
     "sva_lin_attn_states_bytes": (ctypes.c_int, [ctypes.POINTER(SvaDesc), ctypes.POINTER(ctypes.c_size_t)]),
@@ -246,8 +251,10 @@ def _workspace(nbytes: int, like, ws):
 def sva_lin_attn_fwd(q, k, v, grid: Tuple[int, int, int], frames_per_block: int, *, t0: int = 0,
                      rope: bool = False, split=None, base: float = 10000.0, eps: float = 1e-6,
                      S0=None, z0=None, out=None, S_out=None, z_out=None, ws=None, stream=None,
-                     events=None):
-    """One-shot block-causal forward (sva_lin_attn_fwd).  Returns `out`."""
+                     stages: int = 7):
+    """One-shot block-causal forward (sva_lin_attn_fwd).  Returns `out`.
+    stages (a mask of SVA_STAGE_*) restricts the call to some of its kernels
+    (sva_lin_attn_fwd_stages), for timing them one at a time."""
     import torch
     _pair("S0", S0, "z0", z0)
     _pair("S_out", S_out, "z_out", z_out)
@@ -261,11 +268,10 @@ def sva_lin_attn_fwd(q, k, v, grid: Tuple[int, int, int], frames_per_block: int,
     ws = _workspace(nbytes, q, ws)
     args = (ctypes.byref(desc), _ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(S0), _ptr(z0), _ptr(S_out),
             _ptr(z_out), _ptr(ws), ws.numel() * ws.element_size(), _stream(stream))
-    if events is None:
+    if stages == SVA_STAGE_ALL:
         st = lib().sva_lin_attn_fwd(*args)
     else:
-        arr = (_VP * 4)(*[ctypes.c_void_p(e) for e in events])
-        st = lib().sva_lin_attn_fwd_traced(*args, arr)
+        st = lib().sva_lin_attn_fwd_stages(*args, int(stages))
     _check(st, "sva_lin_attn_fwd")
     return out
 

@@ -93,8 +93,14 @@ const char* sva_status_string(int status);
 /* ABI version of this header: 1. */
 int sva_version(void);
 
-/* Workspace bytes sva_lin_attn_fwd needs for this descriptor (per-block
- * partial states and the prefix states; about nb*B*H*d*d*8 bytes). */
+/* Workspace bytes sva_lin_attn_fwd needs for this descriptor (arrival
+ * counters, per-block partial states and the prefix states; about
+ * nb*B*H*d*d*8 bytes).
+ * Every workspace (this one, the backward's and the block cache's) must be
+ * zero-filled once before its first use: it starts with B*H arrival
+ * counters that the reduction's workgroups count on, and every call leaves
+ * them zero again, so a workspace that is reused needs no further clearing.
+ * Calls that share a workspace must not run concurrently. */
 sva_status sva_lin_attn_fwd_workspace(const sva_desc* desc, size_t* bytes);
 
 /* One-shot block-causal forward over all T/F blocks ([talk], block causal
@@ -115,16 +121,26 @@ sva_status sva_lin_attn_fwd(const sva_desc* desc, const void* q, const void* k,
                             const float* z0, float* S_out, float* z_out,
                             void* ws, size_t ws_bytes, void* stream);
 
-/* Same as sva_lin_attn_fwd, and records the four hipEvent_t in `events` on
- * `stream`: before the per-block reduction, after it, after the prefix scan
- * and after the output pass, so a caller can time each kernel. */
-sva_status sva_lin_attn_fwd_traced(const sva_desc* desc, const void* q,
-                                   const void* k, const void* v, void* out,
-                                   const float* S0, const float* z0,
-                                   float* S_out, float* z_out, void* ws,
-                                   size_t ws_bytes, void* stream,
-                                   void* const events[4]);
+/* Kernels of sva_lin_attn_fwd, selectable for profiling one at a time. */
+typedef enum sva_stage {
+  SVA_STAGE_REDUCE = 1, /* per-block state reduction (with the prefix, where it is folded in) */
+  SVA_STAGE_SCAN = 2,   /* separate prefix scan (a no-op where the reduction forms the prefix) */
+  SVA_STAGE_APPLY = 4,  /* output pass */
+  SVA_STAGE_ALL = 7
+} sva_stage;
 
+/* sva_lin_attn_fwd restricted to the kernels in `stages` (a mask of
+ * sva_stage), launched back to back on `stream`, so that a caller can time
+ * each kernel alone.  A stage reads what the earlier stages of a complete
+ * call left in the workspace: the output pass alone repeats the output of
+ * the last full call made with this workspace, descriptor and inputs.
+ * SVA_STAGE_ALL is sva_lin_attn_fwd.  stages outside 1..7:
+ * SVA_ERR_INVALID_ARG. */
+sva_status sva_lin_attn_fwd_stages(const sva_desc* desc, const void* q, const void* k,
+                                   const void* v, void* out, const float* S0,
+                                   const float* z0, float* S_out, float* z_out,
+                                   void* ws, size_t ws_bytes, void* stream,
+                                   int stages);
 /* Workspace bytes sva_lin_attn_bwd needs (the same as the forward's).
  * SVA_ERR_UNSUPPORTED unless desc->dtype == SVA_BF16. */
 sva_status sva_lin_attn_bwd_workspace(const sva_desc* desc, size_t* bytes);

@@ -128,11 +128,21 @@ def test_pointer_checks_happen_before_launch():
 
 
 @fake_pointers
-def test_traced_needs_events():
+@pytest.mark.parametrize("stages", [0, 8, -1])
+def test_stages_mask_is_checked(stages):
     d = _desc()
-    st = sva.lib().sva_lin_attn_fwd_traced(ctypes.byref(d), 1 << 30, 1 << 33, 1 << 34, 1 << 36, None, None,
-                                           None, None, 16, 1 << 40, None, None)
+    st = sva.lib().sva_lin_attn_fwd_stages(ctypes.byref(d), 1 << 30, 1 << 33, 1 << 34, 1 << 36, None, None,
+                                           None, None, 16, 1 << 40, None, stages)
     assert st == sva.SVA_ERR_INVALID_ARG
+
+
+def test_workspace_starts_with_the_counters():
+    """The forward's workspace grows by the B*H arrival counters (one 256-byte
+    aligned region) over its partials and prefix states."""
+    d = _desc()
+    n = sva.sva_lin_attn_fwd_workspace(d)
+    E, nb, BH = 64 * 64 + 64, 7, 16
+    assert n >= 256 + (BH * nb) * E * 4 + BH * nb * (64 * 64 * 2 + 64 * 4)
 
 
 def test_bwd_workspace_and_dtype():

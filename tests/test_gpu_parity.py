@@ -38,6 +38,10 @@ SMALL = [
     # axis widths that are not multiples of 4: the unpaired table-lookup path
     ("odd_split_d64", 1, 2, 64, (4, 5, 6), 2, (6, 26, 32), 3),
     ("odd_split_d32", 2, 1, 32, (3, 4, 9), 3, (10, 10, 12), 0),
+    # 32 or more blocks a sequence: the prefix is formed inside the reduction
+    # (the last workgroup of each sequence), not by a scan launch
+    ("many_blocks_d64", 2, 2, 64, (40, 3, 5), 1, (16, 24, 24), 7),
+    ("many_blocks_d32", 1, 3, 32, (64, 2, 4), 2, (8, 12, 12), 0),
 ]
 
 
@@ -82,11 +86,13 @@ def test_fwd_other_base_eps_and_positions(base, eps, t0, dtype):
 
 
 @pytest.mark.parametrize("dtype", ["f32", "bf16"])
-def test_fwd_with_initial_cache_in_place(dtype):
+@pytest.mark.parametrize("grid,F", [((4, 6, 10), 2), ((36, 2, 3), 1)], ids=["scan", "folded_prefix"])
+def test_fwd_with_initial_cache_in_place(dtype, grid, F):
     """S0/z0 given and S_out/z_out the same buffers: the final cache is
-    written in place."""
-    B, H, d, grid, F, split, t0 = 1, 4, 64, (4, 6, 10), 2, (16, 24, 24), 6
-    _say(f"fwd_initial_cache {dtype}")
+    written in place (by the scan kernel, or by the reduction's last
+    workgroup when a sequence has 32 or more blocks)."""
+    B, H, d, split, t0 = 1, 4, 64, (16, 24, 24), 6
+    _say(f"fwd_initial_cache {dtype} {grid} F={F}")
     N = grid[0] * grid[1] * grid[2]
     q, qd = rand((B, H, N, d), 11, dtype)
     k, kd = rand((B, H, N, d), 12, dtype)
