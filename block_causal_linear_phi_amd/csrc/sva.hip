@@ -2660,6 +2660,46 @@ sva_status run_proj_fwd(const sva_desc* a, const sva_proj_desc* pd, const void* 
 }  // namespace
 
 // ---------------------------------------------------------------------------
+// Scratch of sva_block_cache_apply_noalloc
+//
+// A file-scope device array: every GPU the library runs on holds its own copy
+// until the process ends.  In host code the array's name is only a stand-in
+// for the device symbol, never a device address; the address of each GPU's
+// copy comes from hipGetSymbolAddress, taken once per device with that device
+// current, and only that pointer is handed to kernels.  Every call on a GPU
+// shares that GPU's copy, so calls that overlap on one GPU race.  A one-block
+// call forms its prefix with the scan kernel and writes every region it reads
+// earlier in the same call (the reduction's pieces, then the prefix operands),
+// so nothing in the array has to start at zero.
+// ---------------------------------------------------------------------------
+
+static constexpr size_t kScratchBytes = (size_t)16 << 20;
+static __device__ __align__(256) unsigned char scratch[kScratchBytes];
+
+namespace {
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices];
+
+// The current device's copy of `scratch`.
+sva_status device_scratch(void** out) {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return SVA_ERR_HIP;
+  if (dev < 0 || dev >= kMaxDevices) return SVA_ERR_UNSUPPORTED;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* ptr = nullptr;
+    if (hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch)) != hipSuccess || !ptr) return SVA_ERR_HIP;
+    g_scratch_ptr[dev] = ptr;
+  }
+  *out = g_scratch_ptr[dev];
+  return SVA_OK;
+}
+
+}  // namespace
+
+// ---------------------------------------------------------------------------
 // C ABI
 // ---------------------------------------------------------------------------
 
@@ -2768,6 +2808,23 @@ sva_status sva_block_cache_apply(const sva_desc* desc, const float* S, const flo
   if (s != SVA_OK) return s;
   if (!S || !z) return SVA_ERR_INVALID_ARG;
   return run_fwd(desc, q, k, v, out, S, z, nullptr, nullptr, ws, ws_bytes, stream);
+}
+
+sva_status sva_block_cache_apply_noalloc(const sva_desc* desc, const float* S, const float* z, const void* q,
+                                         const void* k, const void* v, void* out, void* stream) {
+  Plan p;
+  sva_status s = check_common(desc, true, &p);
+  if (s != SVA_OK) return s;
+  if (!S || !z) return SVA_ERR_INVALID_ARG;
+  if ((s = check_fwd_pointers(p, q, k, v, out, S, z, nullptr, nullptr)) != SVA_OK) return s;
+  void* scr = nullptr;
+  if ((s = device_scratch(&scr)) != SVA_OK) return s;
+  plan_grids(&p);
+  if (p.fold) return SVA_ERR_UNSUPPORTED;  // one block: the prefix is always the scan kernel's
+  layout_workspace(&p, p.G_red);           // sized for this launch's reduction grid
+  if (p.ws_bytes > kScratchBytes) return SVA_ERR_WORKSPACE;
+  return launch_fwd(p, q, k, v, out, S, z, nullptr, nullptr, (char*)scr, SVA_STAGE_ALL, nullptr, desc->eps,
+                    (hipStream_t)stream);
 }
 
 sva_status sva_block_cache_commit(const sva_desc* desc, float* S, float* z, const void* k,

@@ -77,6 +77,8 @@ _SIG = {
                                              ctypes.c_size_t, _VP]),
     "sva_block_cache_commit": (ctypes.c_int, [ctypes.POINTER(SvaDesc), _VP, _VP, _VP, _VP, _VP,
                                               ctypes.c_size_t, _VP]),
+    "sva_block_cache_apply_noalloc": (ctypes.c_int, [ctypes.POINTER(SvaDesc), _VP, _VP, _VP, _VP, _VP, _VP,
+                                                     _VP]),
     "sva_phi_rope_prep": (ctypes.c_int, [ctypes.POINTER(SvaDesc), _VP, _VP, _VP, _VP]),
     "sva_tconv_fwd": (ctypes.c_int, [ctypes.POINTER(SvaTconvDesc)] + [_VP] * 7),
     "sva_tconv_apply": (ctypes.c_int, [ctypes.POINTER(SvaTconvDesc)] + [_VP] * 6),
@@ -354,6 +356,22 @@ def sva_block_cache_apply(S, z, q, k, v, frame_grid: Tuple[int, int, int], *, t0
     st = lib().sva_block_cache_apply(ctypes.byref(desc), _ptr(S), _ptr(z), _ptr(q), _ptr(k), _ptr(v),
                                      _ptr(out), _ptr(ws), ws.numel() * ws.element_size(), _stream(stream))
     _check(st, "sva_block_cache_apply")
+    return out
+
+
+def sva_block_cache_apply_noalloc(S, z, q, k, v, frame_grid: Tuple[int, int, int], *, t0: int,
+                                  rope: bool = False, split=None, base: float = 10000.0, eps: float = 1e-6,
+                                  out, stream=None):
+    """sva_block_cache_apply on the library's static scratch: nothing is
+    allocated, `out` included (the caller passes it).  Calls on one GPU
+    share the scratch and must not overlap."""
+    _check_attn(q, frame_grid, like_q=[("k", k), ("v", v), ("out", out)], caches=[("S", S, "S"), ("z", z, "z")])
+    if S is None or z is None or out is None:
+        raise ValueError("the cache S, z and out are required")
+    desc = _desc_from(q, frame_grid, frame_grid[0], t0, rope, split, base, eps)
+    st = lib().sva_block_cache_apply_noalloc(ctypes.byref(desc), _ptr(S), _ptr(z), _ptr(q), _ptr(k), _ptr(v),
+                                             _ptr(out), _stream(stream))
+    _check(st, "sva_block_cache_apply_noalloc")
     return out
 
 

@@ -206,6 +206,24 @@ sva_status sva_block_cache_apply(const sva_desc* desc, const float* S,
                                  const void* v, void* out, void* ws,
                                  size_t ws_bytes, void* stream);
 
+/* sva_block_cache_apply without a caller workspace, for callers that cannot
+ * allocate device memory (code under HIP graph capture, tight serving loops,
+ * harnesses that forbid hipMalloc).  It allocates nothing: its scratch is a
+ * static array of 16 MiB in the library's device code, one copy per GPU,
+ * held until the process ends.  The result equals sva_block_cache_apply's.
+ * The scratch a call needs is (R + B*H) * (d*d + d) * 4 bytes for the
+ * reduction's per-workgroup pieces (R: the device's resident reduction
+ * workgroups, 256 on MI355X) plus B*H*d*d*esize + B*H*d*4 for the prefix
+ * operands, with 256-byte alignment: up to about 480 heads x samples of
+ * d = 64 in bf16; beyond the array's size it returns SVA_ERR_WORKSPACE
+ * before any launch.  Every call on one GPU shares that GPU's copy: calls
+ * that overlap on one GPU (other streams or threads) race and must be
+ * serialised by the caller. */
+sva_status sva_block_cache_apply_noalloc(const sva_desc* desc, const float* S,
+                                         const float* z, const void* q,
+                                         const void* k, const void* v,
+                                         void* out, void* stream);
+
 /* Adds ONE block to the cache in place ([talk], block KV cache segment: the
  * state is updated additively): S += sum RoPE(phi k) v^T, z += sum phi k over
  * the block's tokens at global frames t0 .. t0+F-1.  The caller chooses which
