@@ -88,48 +88,97 @@ def _timed(stream, fn, n):
     return a.elapsed_time(b) / n
 
 
-def gpu_leg(w, steps: int, warmup: int, sets: int, repeats: int = 0, stage_calls: int = 0):
-    """The forward (sva_lin_attn_fwd) of workload w, `sets` input/output
-    buffer sets alternating.  Returns a dict:
-      ms            ms per step over W untimed + K timed uninstrumented steps;
-      repeat_ms     per-step ms of `repeats` further runs of K steps each;
-      stage_us      per-launch us of each kernel, each timed alone over
-                    `stage_calls` back-to-back launches (sva_lin_attn_fwd_stages)
-                    on the same buffers: no event sits between two launches."""
+def graph_timed(fn, n: int, replays: int = 5):
+    """ms per call of fn(i) for n calls captured in one HIP graph (torch's
+    CUDAGraph on its capture stream) and replayed `replays` times: the launch
+    cost of the host is out of the figure, which matters for kernels of a
+    few microseconds.  The library issues only kernel launches, so the graph
+    holds kernel nodes only."""
     import torch
-    from block_causal_linear_phi_amd import sva
-
-    dev = torch.device("cuda:0")
-    tdt = torch.bfloat16 if w.dtype == "bf16" else torch.float32
-    shape = (w.B, w.H, w.N, w.d)
-    base = {t: upload(w, t) for t in ("q", "k", "v")}
-    bufs = [base] + [{t: base[t].clone() for t in base} for _ in range(sets - 1)]
-    outs = [torch.empty(shape, dtype=tdt, device=dev) for _ in range(sets)]
-    desc = sva.make_desc(w.B, w.H, w.d, (w.T, w.Hs, w.Ws), w.F, t0=w.t0, rope=w.rope, split=w.split,
-                         base=w.base, eps=w.eps, dtype=sva.SVA_BF16 if w.dtype == "bf16" else sva.SVA_F32)
-    ws = torch.zeros(sva.sva_lin_attn_fwd_workspace(desc), dtype=torch.uint8, device=dev)
-    stream = torch.cuda.current_stream()
-
-    def step(i, stages=sva.SVA_STAGE_ALL):
-        s_ = i % sets
-        x = bufs[s_]
-        sva.sva_lin_attn_fwd(x["q"], x["k"], x["v"], (w.T, w.Hs, w.Ws), w.F, t0=w.t0, rope=w.rope,
-                             split=w.split, base=w.base, eps=w.eps, out=outs[s_], ws=ws, stream=stream,
-                             stages=stages)
-
-    for i in range(warmup):
-        step(i)
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        for i in range(n):
+            fn(i)
+    g.replay()
     torch.cuda.synchronize()
-    res = {"ms": _timed(stream, lambda i: step(warmup + i), steps)}
-    res["repeat_ms"] = [_timed(stream, step, steps) for _ in range(repeats)]
-    res["stage_us"] = {}
-    if stage_calls:
-        for name, st in (("reduce", sva.SVA_STAGE_REDUCE), ("scan", sva.SVA_STAGE_SCAN),
-                         ("apply", sva.SVA_STAGE_APPLY)):
-            step(0)  # a full call leaves the prefix operands each stage reads
-            torch.cuda.synchronize()
-            res["stage_us"][name] = 1e3 * _timed(stream, lambda i: step(i, st), stage_calls)
-    del bufs, outs, ws
+    stream = torch.cuda.current_stream()
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    a.record(stream)
+    for _ in range(replays):
+        g.replay()
+    b.record(stream)
+    torch.cuda.synchronize()
+    ms = a.elapsed_time(b) / (replays * n)
+    del g
+    return ms
+
+
+class ForwardBench:
+    """The forward (sva_lin_attn_fwd) of workload w on `sets` input/output
+    buffer sets that alternate between steps (uploaded at construction)."""
+
+    def __init__(self, w, sets: int):
+        import torch
+        from block_causal_linear_phi_amd import sva
+
+        self.w, self.sets, self.sva = w, sets, sva
+        dev = torch.device("cuda:0")
+        tdt = torch.bfloat16 if w.dtype == "bf16" else torch.float32
+        base = {t: upload(w, t) for t in ("q", "k", "v")}
+        self.bufs = [base] + [{t: base[t].clone() for t in base} for _ in range(sets - 1)]
+        self.outs = [torch.empty((w.B, w.H, w.N, w.d), dtype=tdt, device=dev) for _ in range(sets)]
+        desc = sva.make_desc(w.B, w.H, w.d, (w.T, w.Hs, w.Ws), w.F, t0=w.t0, rope=w.rope, split=w.split,
+                             base=w.base, eps=w.eps, dtype=sva.SVA_BF16 if w.dtype == "bf16" else sva.SVA_F32)
+        self.ws = torch.zeros(sva.sva_lin_attn_fwd_workspace(desc), dtype=torch.uint8, device=dev)
+        torch.cuda.synchronize()
+
+    def step(self, i, stages=7):
+        w, s_ = self.w, i % self.sets
+        x = self.bufs[s_]
+        self.sva.sva_lin_attn_fwd(x["q"], x["k"], x["v"], (w.T, w.Hs, w.Ws), w.F, t0=w.t0, rope=w.rope,
+                                  split=w.split, base=w.base, eps=w.eps, out=self.outs[s_], ws=self.ws,
+                                  stages=stages)
+
+    def run(self, steps: int, warmup: int, repeats: int = 0, stage_calls: int = 0):
+        """Returns a dict:
+          ms          ms per step over W untimed + K timed uninstrumented steps;
+          repeat_ms   per-step ms of `repeats` further runs of K steps each;
+          stage_us    per-launch us of each kernel, each timed alone over
+                      `stage_calls` back-to-back launches (sva_lin_attn_fwd_stages)
+                      on the same buffers, no event between two launches;
+          stage_graph_us  the same launches captured in a HIP graph and
+                      replayed (no host launch cost)."""
+        import torch
+        stream = torch.cuda.current_stream()
+        for i in range(warmup):
+            self.step(i)
+        torch.cuda.synchronize()
+        res = {"ms": _timed(stream, lambda i: self.step(warmup + i), steps)}
+        res["repeat_ms"] = [_timed(stream, self.step, steps) for _ in range(repeats)]
+        res["stage_us"], res["stage_graph_us"] = {}, {}
+        if stage_calls:
+            sva = self.sva
+            for name, st in (("reduce", sva.SVA_STAGE_REDUCE), ("scan", sva.SVA_STAGE_SCAN),
+                             ("apply", sva.SVA_STAGE_APPLY)):
+                self.step(0)  # a full call leaves the prefix operands each stage reads
+                torch.cuda.synchronize()
+                res["stage_us"][name] = 1e3 * _timed(stream, lambda i: self.step(i, st), stage_calls)
+            for name, st in (("reduce", sva.SVA_STAGE_REDUCE), ("scan", sva.SVA_STAGE_SCAN),
+                             ("apply", sva.SVA_STAGE_APPLY)):
+                self.step(0)
+                torch.cuda.synchronize()
+                res["stage_graph_us"][name] = 1e3 * graph_timed(lambda i: self.step(i, st), stage_calls)
+        return res
+
+    def free(self):
+        del self.bufs, self.outs, self.ws
+
+
+def gpu_leg(w, steps: int, warmup: int, sets: int, repeats: int = 0, stage_calls: int = 0):
+    """ForwardBench(w, sets).run(...), buffers freed afterwards."""
+    fb = ForwardBench(w, sets)
+    res = fb.run(steps, warmup, repeats, stage_calls)
+    fb.free()
     return res
 
 
@@ -178,8 +227,10 @@ def cached_leg(w, steps: int, warmup: int):
     """Streaming generation: a cache committed from the workload's prior
     blocks, then `steps` denoising steps of one block against it
     (sva_block_cache_apply, the cache read only), cycling over the workload's
-    per-step q, k, v; then commits of the last step's k, v.  Returns
-    (ms per apply, ms per commit)."""
+    per-step q, k, v; then commits of the last step's k, v.  Each is timed
+    over back-to-back calls, and again replayed from a HIP graph (no host
+    launch cost), as is the workspace-free apply.  Returns ms per call:
+    apply_ms, commit_ms, apply_graph_ms, commit_graph_ms, noalloc_graph_ms."""
     import torch
     from block_causal_linear_phi_amd import sva
 
@@ -196,30 +247,30 @@ def cached_leg(w, steps: int, warmup: int):
     desc = sva.make_desc(w.B, w.H, w.d, fg, w.F, t0=w.t0, eps=w.eps,
                          dtype=sva.SVA_BF16 if w.dtype == "bf16" else sva.SVA_F32, **kw)
     ws = torch.zeros(sva.sva_block_cache_workspace(desc), dtype=torch.uint8, device=dev)
+    S2, z2 = S.clone(), z.clone()  # a second cache for the commits
     stream = torch.cuda.current_stream()
 
     def apply(i):
         x = data[i % w.steps]
-        sva.sva_block_cache_apply(S, z, x["q"], x["k"], x["v"], fg, t0=w.t0, eps=w.eps, out=out, ws=ws,
-                                  stream=stream, **kw)
+        sva.sva_block_cache_apply(S, z, x["q"], x["k"], x["v"], fg, t0=w.t0, eps=w.eps, out=out, ws=ws, **kw)
+
+    def noalloc(i):
+        x = data[i % w.steps]
+        sva.sva_block_cache_apply_noalloc(S, z, x["q"], x["k"], x["v"], fg, t0=w.t0, eps=w.eps, out=out, **kw)
+
+    last = data[w.steps - 1]
+
+    def commit(i):
+        sva.sva_block_cache_commit(S2, z2, last["k"], last["v"], fg, t0=w.t0, ws=ws, **kw)
 
     for i in range(warmup):
         apply(i)
     torch.cuda.synchronize()
-    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    a.record(stream)
-    for i in range(steps):
-        apply(i)
-    b.record(stream)
-    torch.cuda.synchronize()
-    apply_ms = a.elapsed_time(b) / steps
-    last = data[w.steps - 1]
-    a.record(stream)
-    for i in range(steps):
-        sva.sva_block_cache_commit(S, z, last["k"], last["v"], fg, t0=w.t0, ws=ws, stream=stream, **kw)
-    b.record(stream)
-    torch.cuda.synchronize()
-    return apply_ms, a.elapsed_time(b) / steps
+    res = {"apply_ms": _timed(stream, apply, steps), "commit_ms": _timed(stream, commit, steps)}
+    res["apply_graph_ms"] = graph_timed(apply, steps)
+    res["commit_graph_ms"] = graph_timed(commit, steps)
+    res["noalloc_graph_ms"] = graph_timed(noalloc, steps)
+    return res
 
 
 def stream_leg(w, reps: int, warmup: int):
@@ -534,12 +585,16 @@ def other_workloads(steps: int, warmup: int, sets: int):
         ent = {"us_per_step": res["ms"] * 1e3, "tokens_per_s": w.B * w.N / (res["ms"] * 1e-3),
                "hbm_frac_step": step_bytes / (res["ms"] * 1e-3) / (HBM_PEAK_GBS * 1e9), "steps": k_steps}
         if res["stage_us"]:
-            ent["kernels_us"] = {k: round(v, 2) for k, v in res["stage_us"].items()}
+            ent["kernels_us"] = {k: round(v, 2) for k, v in res["stage_graph_us"].items()}
+            ent["kernels_eager_us"] = {k: round(v, 2) for k, v in res["stage_us"].items()}
         out[name] = ent
     w = wl.WORKLOADS["cached_step"]
-    apply_ms, commit_ms = cached_leg(w, steps, warmup)
-    out["cached_step"] = {"us_per_step": apply_ms * 1e3, "commit_us": commit_ms * 1e3,
-                          "tokens_per_s": w.B * w.block_tokens / (apply_ms * 1e-3)}
+    c = cached_leg(w, steps, warmup)
+    out["cached_step"] = {"us_per_step": c["apply_ms"] * 1e3, "commit_us": c["commit_ms"] * 1e3,
+                          "us_per_step_graph": c["apply_graph_ms"] * 1e3,
+                          "commit_us_graph": c["commit_graph_ms"] * 1e3,
+                          "us_per_step_noalloc_graph": c["noalloc_graph_ms"] * 1e3,
+                          "tokens_per_s": w.B * w.block_tokens / (c["apply_ms"] * 1e-3)}
     return out
 
 
@@ -649,8 +704,28 @@ def summarize_profile(args):
 
     stats = [f for f in one(args.trace_dir) if f.endswith("kernel_stats.csv")][0]
     rows = list(csv.DictReader(open(stats)))
+    # The longest run of consecutive launches of each kernel in the trace:
+    # bench.py times each kernel over such a run (its back-to-back stage
+    # launches), so the run's mean duration is the figure to compare.
+    trace = [f for f in one(args.trace_dir) if f.endswith("kernel_trace.csv")]
+    runs = {}
+    if trace:
+        disp = sorted(((int(r["Start_Timestamp"]), int(r["End_Timestamp"]), _short_kernel(r["Kernel_Name"]))
+                       for r in csv.DictReader(open(trace[0]))), key=lambda t: t[0])
+        i = 0
+        while i < len(disp):
+            j = i
+            while j + 1 < len(disp) and disp[j + 1][2] == disp[i][2]:
+                j += 1
+            n = j - i + 1
+            if n > runs.get(disp[i][2], (0, 0.0, 0.0))[0]:
+                durs = [(e - b) / 1e3 for b, e, _ in disp[i:j + 1]]
+                gaps = [(disp[m + 1][0] - disp[m][1]) / 1e3 for m in range(i, j)]
+                runs[disp[i][2]] = (n, sum(durs) / n, (sum(gaps) / len(gaps)) if gaps else 0.0)
+            i = j + 1
     counters = defaultdict(list)
-    for d, cname in ((args.fetch_dir, "FETCH_SIZE"), (args.write_dir, "WRITE_SIZE")):
+    with_traffic = bool(args.fetch_dir and args.write_dir)
+    for d, cname in ((args.fetch_dir, "FETCH_SIZE"), (args.write_dir, "WRITE_SIZE")) if with_traffic else ():
         f = [x for x in one(d) if x.endswith("counter_collection.csv")][0]
         for r in csv.DictReader(open(f)):
             if r["Counter_Name"] == cname:
@@ -661,8 +736,8 @@ def summarize_profile(args):
         vals = [v for (k, c), vs in counters.items() if substr in k and c == cname for v in vs]
         return sum(vals) / len(vals) if vals else None
 
-    f_scale = calib_bytes / (mean_for(CALIB_KERNEL, "FETCH_SIZE") * 1024)
-    w_scale = calib_bytes / (mean_for(CALIB_KERNEL, "WRITE_SIZE") * 1024)
+    f_scale = calib_bytes / (mean_for(CALIB_KERNEL, "FETCH_SIZE") * 1024) if with_traffic else None
+    w_scale = calib_bytes / (mean_for(CALIB_KERNEL, "WRITE_SIZE") * 1024) if with_traffic else None
     by_short = defaultdict(lambda: defaultdict(list))
     for (kname, cname), vs in counters.items():
         if "sva_" in kname:
@@ -683,10 +758,12 @@ def summarize_profile(args):
                                                   f"{calib_bytes} bytes", "per_launch": traffic,
            "commands": args.commands}
     os.makedirs(PROFILES, exist_ok=True)
-    with open(traffic_file(name + args.label), "w") as f:
-        json.dump(doc, f, indent=1)
+    if with_traffic:
+        with open(traffic_file(name + args.label), "w") as f:
+            json.dump(doc, f, indent=1)
     what = ("causal temporal convolution" if args.tconv else "QKV projection with MXFP4 weights" if args.proj
-            else "backward" if args.label == "_bwd" else "forward")
+            else "backward" if args.label == "_bwd" else "denoising step and commit" if args.workload == "cached_step"
+            else "forward")
     lines = [f"# Kernel times and HBM traffic, {args.workload} workload, {what}", "",
              "Commands (run from the repository root on one MI355X):", ""]
     lines += [f"    {c}" for c in args.commands]
@@ -695,17 +772,37 @@ def summarize_profile(args):
     for r in rows:
         lines.append(f"| {_short_kernel(r['Name'])} | {r['Calls']} | {float(r['AverageNs']) / 1e3:.2f} | "
                      f"{float(r['MinNs']) / 1e3:.2f} | {float(r['MaxNs']) / 1e3:.2f} | {float(r['Percentage']):.1f} |")
-    lines += ["", "## HBM traffic per launch (FETCH_SIZE, WRITE_SIZE)", "",
-              f"Scale factors from the {CALIB_KERNEL} streaming kernel over {calib_bytes} bytes: "
-              f"FETCH_SIZE x {f_scale:.4f}, WRITE_SIZE x {w_scale:.4f}.", "",
-              "| kernel | FETCH_SIZE KiB | WRITE_SIZE KiB | read MB | write MB | total MB |", "|---|---|---|---|---|---|"]
-    for k, t in traffic.items():
-        lines.append(f"| {k} | {t['fetch_kib']:.0f} | {t['write_kib']:.0f} | {t['read_bytes'] / 1e6:.1f} | "
-                     f"{t['write_bytes'] / 1e6:.1f} | {t['bytes'] / 1e6:.1f} |")
+    long_runs = {k: v for k, v in runs.items() if v[0] >= 10}
+    if long_runs:
+        lines += ["", "## Longest run of back-to-back launches of each kernel", "",
+                  "The figure bench.py's roofline uses (it times each kernel over such a run).", "",
+                  "| kernel | launches | mean us | mean gap to the next launch us |", "|---|---|---|---|"]
+        for k, (n, mu, gap) in sorted(long_runs.items(), key=lambda kv: -kv[1][0]):
+            lines.append(f"| {k} | {n} | {mu:.2f} | {gap:.2f} |")
+    if trace:
+        lib = [d for d in disp if d[2] in ("reduce", "scan", "apply")]
+        gaps = defaultdict(list)
+        for a_, b_ in zip(lib, lib[1:]):
+            if b_[0] - a_[1] < 20000:  # within one call sequence (under 20 us apart)
+                gaps[(a_[2], b_[2])].append((b_[0] - a_[1]) / 1e3)
+        if gaps:
+            lines += ["", "## Gaps between consecutive library kernels (under the profiler)", "",
+                      "| from | to | count | mean gap us |", "|---|---|---|---|"]
+            for (x, y), g in sorted(gaps.items()):
+                lines.append(f"| {x} | {y} | {len(g)} | {sum(g) / len(g):.2f} |")
+    if with_traffic:
+        lines += ["", "## HBM traffic per launch (FETCH_SIZE, WRITE_SIZE)", "",
+                  f"Scale factors from the {CALIB_KERNEL} streaming kernel over {calib_bytes} bytes: "
+                  f"FETCH_SIZE x {f_scale:.4f}, WRITE_SIZE x {w_scale:.4f}.", "",
+                  "| kernel | FETCH_SIZE KiB | WRITE_SIZE KiB | read MB | write MB | total MB |",
+                  "|---|---|---|---|---|---|"]
+        for k, t in traffic.items():
+            lines.append(f"| {k} | {t['fetch_kib']:.0f} | {t['write_kib']:.0f} | {t['read_bytes'] / 1e6:.1f} | "
+                         f"{t['write_bytes'] / 1e6:.1f} | {t['bytes'] / 1e6:.1f} |")
     lines += ["", f"Kernel source sha256: `{doc['source_sha256']}`", ""]
     with open(os.path.join(PROFILES, f"sva_kernels_{name}{args.label}.md"), "w") as f:
         f.write("\n".join(lines))
-    print(json.dumps({"summarized": name, "traffic": traffic}))
+    print(json.dumps({"summarized": name, "traffic": traffic, "back_to_back": runs}))
 
 
 def main():
@@ -889,7 +986,8 @@ def main():
         }), flush=True)
         return
     if w.prior_blocks:
-        apply_ms, commit_ms = cached_leg(w, args.steps, args.warmup)
+        c = cached_leg(w, args.steps, args.warmup)
+        apply_ms, commit_ms = c["apply_ms"], c["commit_ms"]
         tok = w.B * w.block_tokens
         print(json.dumps({
             "metric": "tokens/s of one cached denoising step (block apply against the cache)",
@@ -901,6 +999,8 @@ def main():
                                    f"{w.prior_blocks} committed blocks, {w.dtype}",
                        "B": w.B, "H": w.H, "d": w.d, "tokens": w.block_tokens},
             "us_per_step": apply_ms * 1e3, "commit_us": commit_ms * 1e3,
+            "us_per_step_graph": c["apply_graph_ms"] * 1e3, "commit_us_graph": c["commit_graph_ms"] * 1e3,
+            "us_per_step_noalloc_graph": c["noalloc_graph_ms"] * 1e3,
             "hbm_frac_step": 4 * w.B * w.H * w.block_tokens * w.d * (2 if w.dtype == "bf16" else 4)
             / (apply_ms * 1e-3) / (HBM_PEAK_GBS * 1e9),
         }), flush=True)
@@ -908,17 +1008,21 @@ def main():
     # The other workloads and the copy ceiling are measured first, in the same
     # process (their steps also bring the clocks up); then the W warm-up and
     # K timed steps of the headline workload.
+    fb = ForwardBench(w, args.sets)
     others = {}
     copy = None
     if not args.no_others and w.name == "720p":
         copy = copy_ceiling()
         others = other_workloads(args.steps, args.warmup, args.sets)
-    res = gpu_leg(w, args.steps, args.warmup, args.sets, repeats=args.repeats, stage_calls=args.steps)
+    res = fb.run(args.steps, args.warmup, repeats=args.repeats, stage_calls=args.steps)
+    fb.free()
     ms_per_step = res["ms"]
     esz = 2 if w.dtype == "bf16" else 4
     elems = w.B * w.H * w.N * w.d
     alg_bytes = {"reduce": 2 * elems * esz, "apply": 2 * elems * esz}
-    stage_us = res["stage_us"]
+    # kernel durations: back-to-back launches replayed from a HIP graph (the
+    # same figure rocprofv3's trace gives for a run of back-to-back launches)
+    stage_us = res["stage_graph_us"]
     dom = "reduce" if stage_us["reduce"] >= stage_us["apply"] else "apply"
     achieved = alg_bytes[dom] / (stage_us[dom] * 1e-6) / 1e9
     traffic = None
@@ -958,6 +1062,9 @@ def main():
                      "unit": "GB/s", "frac": achieved / HBM_PEAK_GBS, "traffic": traffic,
                      "traffic_unit": "GB per launch", "alg_bytes": alg_bytes[dom] / 1e9},
         "kernels_us": {k: round(v, 2) for k, v in stage_us.items()},
+        # the same launches issued one Python call at a time (the scan's few
+        # microseconds are below the host's cost per call)
+        "kernels_eager_us": {k: round(v, 2) for k, v in res["stage_us"].items()},
         "kernels_frac": {k: round(alg_bytes[k] / (stage_us[k] * 1e-6) / 1e9 / HBM_PEAK_GBS, 4)
                          for k in ("reduce", "apply")},
     }
