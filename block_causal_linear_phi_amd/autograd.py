@@ -22,20 +22,20 @@ class BlockCausalLinearAttention(torch.autograd.Function):
         q, k, v = q.contiguous(), k.contiguous(), v.contiguous()
         out, states = sva.sva_lin_attn_fwd_save(q, k, v, grid, frames_per_block, t0=t0, rope=rope, split=split,
                                                 base=base, eps=eps, S0=S0, z0=z0)
-        ctx.save_for_backward(q, k, v, out, states, S0, z0)
+        ctx.save_for_backward(q, k, v, states, S0, z0)  # the output is formed again in the backward
         ctx.cfg = dict(grid=grid, frames_per_block=frames_per_block, t0=t0, rope=rope, split=split, base=base,
                        eps=eps)
         return out
 
     @staticmethod
     def backward(ctx, dout):
-        q, k, v, out, states, S0, z0 = ctx.saved_tensors
+        q, k, v, states, S0, z0 = ctx.saved_tensors
         c = ctx.cfg
         dS0 = dz0 = None
         if S0 is not None and (ctx.needs_input_grad[10] or ctx.needs_input_grad[11]):
             dS0 = torch.empty_like(S0)
             dz0 = torch.empty_like(z0)
-        dq, dk, dv = sva.sva_lin_attn_bwd(q, k, v, out, dout.contiguous(), c["grid"], c["frames_per_block"],
+        dq, dk, dv = sva.sva_lin_attn_bwd(q, k, v, dout.contiguous(), c["grid"], c["frames_per_block"],
                                           t0=c["t0"], rope=c["rope"], split=c["split"], base=c["base"],
                                           eps=c["eps"], S0=S0, z0=z0, states=states, dS0=dS0, dz0=dz0)
         return dq, dk, dv, None, None, None, None, None, None, None, dS0, dz0

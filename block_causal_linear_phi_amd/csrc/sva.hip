@@ -388,6 +388,13 @@ __device__ __forceinline__ uint32_t relu_bf16x2(uint32_t w) {
   return __builtin_bit_cast(uint32_t, r);
 }
 
+// For a pair already through relu_bf16x2: all ones in each 16-bit half that
+// is not +0 (where the derivative of ReLU is 1), zeros elsewhere.
+__device__ __forceinline__ uint32_t relu_pass_mask(uint32_t relu_w) {
+  const i16x2_t one = __builtin_elementwise_min(__builtin_bit_cast(i16x2_t, relu_w), i16x2_t{1, 1});
+  return __builtin_bit_cast(uint32_t, i16x2_t{0, 0} - one);
+}
+
 // Unpack with phi = ReLU applied on the bits.
 template <bool BF16, int CNT>
 __device__ __forceinline__ void unpack_relu(float* f, const uint32_t* w) {
@@ -957,7 +964,8 @@ __device__ __forceinline__ float4 block_sum(const float* __restrict__ partials, 
 template <bool BF16, int D>
 __global__ __launch_bounds__(kThreads) void sva_scan_kernel(
     const float* __restrict__ partials, const float* S0, const float* z0, float* S_out,
-    float* z_out, void* __restrict__ frags, float* __restrict__ zc, ScanArgs a) {
+    float* z_out, void* __restrict__ frags, float* __restrict__ zc, void* __restrict__ frags_lo,
+    ScanArgs a) {
   constexpr int E = D * D + D;
   static_assert(E % 4 == 0 && (D * D) % 4 == 0, "element groups");
   __shared__ float4 lane_tot[kScanLanes][kScanElems];
@@ -1015,7 +1023,14 @@ __global__ __launch_bounds__(kThreads) void sva_scan_kernel(
     if (a.write_frags) {
       if (in_S) {
         if (BF16) {
-          *(uint2*)((__bf16*)frags + bhc * D * D + e) = make_uint2(pack_bf16x2(run.x, run.y), pack_bf16x2(run.z, run.w));
+          const uint2 hi = make_uint2(pack_bf16x2(run.x, run.y), pack_bf16x2(run.z, run.w));
+          *(uint2*)((__bf16*)frags + bhc * D * D + e) = hi;
+          if (frags_lo) {
+            // the remainder S - hi in bf16: hi + lo carries S to about 16 bits
+            const uint2 lo = make_uint2(pack_bf16x2(run.x - bf16_lo(hi.x), run.y - bf16_hi(hi.x)),
+                                        pack_bf16x2(run.z - bf16_lo(hi.y), run.w - bf16_hi(hi.y)));
+            *(uint2*)((__bf16*)frags_lo + bhc * D * D + e) = lo;
+          }
         } else {
           *(float4*)((float*)frags + bhc * D * D + e) = run;
         }
@@ -1597,20 +1612,23 @@ __device__ __forceinline__ u32x4 tr_operand(const uint4* t0, const uint4* t1, in
   return r;
 }
 
-// Output side: q, dout, out -> dq, with the gradients of the block states
-// fused in: per (workgroup, block) piece it writes dS_c^T = (sum qt dnum^T)^T
-// and dZ_c = sum dden phi(q) into `partials` (the reduction's slot layout).
-// sfrag holds S_c^T (bf16) and zc holds Z_c per (b, h, block).  dS takes
-// qt / den (rounded to bf16 once) and the exact dout as MFMA operands with
-// tokens along k, read back transposed from the wave's LDS tiles.  One
-// workgroup per CU: with the 64 dS accumulators a wave needs more than 256
-// registers, and at one wave per SIMD it gets 512 (accumulation registers
-// included) instead of spilling (measured 23 us faster at 720p than two
-// workgroups per CU with spills).
+// Output side: q, dout -> dq, with the gradients of the block states fused
+// in: per (workgroup, block) piece it writes dS_c^T = (sum qt dnum^T)^T and
+// dZ_c = sum dden phi(q) into `partials` (the reduction's slot layout).
+// sfrag holds S_c^T in bf16 and sfrag_lo the remainder S_c^T - sfrag in
+// bf16, zc holds Z_c, per (b, h, block).  S_c dout runs on both parts (the
+// rounding of S_c to bf16 alone, about 2^-9, is amplified where dout . num
+// cancels).  The output itself is not read: the denominator's term needs
+// dout . num, which is qt . (S_c dout), the product dq takes anyway, so q and
+// dout are the only streams read.  dS takes qt / den (rounded to bf16 once)
+// and the exact dout as MFMA operands with tokens along k, read back
+// transposed from the wave's LDS tiles.  One workgroup per CU: with the 64 dS accumulators a wave needs
+// more than 256 registers, and at one wave per SIMD it gets 512
+// (accumulation registers included) instead of spilling.
 template <int D, int ROPE>
 __global__ __launch_bounds__(kThreads, 1) void sva_bwd_out_kernel(
-    const void* __restrict__ qp, const void* __restrict__ dop, const void* __restrict__ op,
-    void* __restrict__ dqp, float* __restrict__ partials, const void* __restrict__ sfrag,
+    const void* __restrict__ qp, const void* __restrict__ dop, void* __restrict__ dqp,
+    float* __restrict__ partials, const void* __restrict__ sfrag, const void* __restrict__ sfrag_lo,
     const float* __restrict__ zc, Geo geo, SplitArgs sp, RopeArgs ra, float eps) {
   using T = BTile<D>;
   constexpr int FPLa = D / 4;
@@ -1624,12 +1642,13 @@ __global__ __launch_bounds__(kThreads, 1) void sva_bwd_out_kernel(
 
   extern __shared__ float4 tab_raw[];
   float2* tab = reinterpret_cast<float2*>(tab_raw);
-  __shared__ uint4 fst[D * T::CPR];  // S_c, rows = key features
-  __shared__ float zst[D];
-  // Per wave: q in / dq out, out, and for the two steps of a pair the dout
-  // tiles and the qt/den tiles.  After the loop the region is the scratch of
-  // the cross-wave sum (2 d*d tiles and 4 z rows).
-  __shared__ uint4 tiles[NWAVE][6][T::TSZ];
+  __shared__ uint4 fst[D * T::CPR];  // S_c in bf16, rows = key features
+  __shared__ uint4 fsl[D * T::CPR];  // S_c - fst in bf16
+  __shared__ __align__(16) float zst[D];
+  // Per wave: q in / dq out, and for the two steps of a pair the dout tiles
+  // and the qt/den tiles.  After the loop the region is the scratch of the
+  // cross-wave sum (2 d*d tiles and 4 z rows).
+  __shared__ uint4 tiles[NWAVE][5][T::TSZ];
   static_assert(sizeof(tiles) >= (2 * D * D + NWAVE * D) * sizeof(float), "epilogue scratch");
 
   const int tid = threadIdx.x;
@@ -1638,7 +1657,6 @@ __global__ __launch_bounds__(kThreads, 1) void sva_bwd_out_kernel(
   const int g = lane >> 4;
   const int row = lane & 15;
   uint4* tq = tiles[wave][0];
-  uint4* to = tiles[wave][1];
 
   const double lane_freq = ROPE ? load_lane_freq(ra) : 0.0;
   PairLoc pl[NLOC];
@@ -1665,31 +1683,46 @@ __global__ __launch_bounds__(kThreads, 1) void sva_bwd_out_kernel(
     const uint32_t nbytes = (uint32_t)je * T::ROWB;
     const __amdgpu_buffer_rsrc_t qrs = make_rsrc((const char*)qp + blk_off, nbytes);
     const __amdgpu_buffer_rsrc_t drs = make_rsrc((const char*)dop + blk_off, nbytes);
-    const __amdgpu_buffer_rsrc_t ors = make_rsrc((const char*)op + blk_off, nbytes);
     const __amdgpu_buffer_rsrc_t dqrs = make_rsrc((char*)dqp + blk_off, nbytes);
 
-    lds_barrier();  // every wave is done with the previous block's operand, t rows and scratch
-    uint4 fr[FR];
+    lds_barrier();  // every wave is done with the previous block's operands, t rows and scratch
+    uint4 fr[FR], frl[FR];
     load_operand<D>(fr, sfrag, bhc, tid);
+    load_operand<D>(frl, sfrag_lo, bhc, tid);
     const float zmine = tid < D ? zc[bhc * D + tid] : 0.f;
     constexpr int WSTRIDE = 16 * NWAVE;
     const int t_first = js + wave * 16;
     const int nsteps = t_first < je ? (je - t_first + WSTRIDE - 1) / WSTRIDE : 0;
-    uint32_t xa[3][NW], xb[3][NW];
-    auto load3 = [&](uint32_t (&x)[3][NW], int t) {
+    // Four register sets: three steps stay in flight while one is computed
+    // (one wave per SIMD leaves nothing else to cover the memory latency).
+    uint32_t x0[2][NW], x1[2][NW], x2[2][NW], x3[2][NW];
+    auto load2 = [&](uint32_t (&x)[2][NW], int k) {
+      const int t = t_first + k * WSTRIDE;
       btile_load<D>(x[0], qrs, t, lane);
       btile_load<D>(x[1], drs, t, lane);
-      btile_load<D>(x[2], ors, t, lane);
     };
-    load3(xa, t_first);
+    load2(x0, 0);
     __builtin_amdgcn_sched_barrier(0);
     if (ROPE) {
       if (pos == g0) build_rope_hw<false, kThreads>(tab, ra, lane_freq);
       build_rope_t<false, kThreads>(tab, ra, c, lane_freq);
     }
     stage_operand<D, true>(fst, fr, tid);
+    stage_operand<D, true>(fsl, frl, tid);
     if (tid < D) zst[tid] = zmine;
     lds_barrier();
+    // S_c's A-operand fragments stay in registers for the whole segment (read
+    // from LDS per tile they would be the largest LDS stream of the loop)
+    u32x4 sh[NRT][NKS], sl[NRT][NKS];
+#pragma unroll
+    for (int rt = 0; rt < NRT; ++rt)
+#pragma unroll
+      for (int ks = 0; ks < NKS; ++ks) {
+        const uint4 x = fst[T::frag_at(T::fo(rt, row), 4 * ks + g)];
+        const uint4 y = fsl[T::frag_at(T::fo(rt, row), 4 * ks + g)];
+        sh[rt][ks] = u32x4{x.x, x.y, x.z, x.w};
+        sl[rt][ks] = u32x4{y.x, y.y, y.z, y.w};
+      }
 
     // The denominator operand (rows 0 and 4: Z rounded to bf16 and the
     // remainder), as in the output pass.  Z_c itself is read from LDS where
@@ -1716,13 +1749,26 @@ __global__ __launch_bounds__(kThreads, 1) void sva_bwd_out_kernel(
 
     // One 16-token tile; `slot` picks the dout and qt/den tiles kept for the
     // pair's dS product.
-    auto compute = [&](const uint32_t (&x)[3][NW], int t, int slot) {
-      uint4* td = tiles[wave][2 + slot];
-      uint4* ts = tiles[wave][4 + slot];
-      uint32_t qw[NW], dw[NW], ow[NW];
+    auto compute = [&](const uint32_t (&x)[2][NW], int t, int slot) {
+      uint4* td = tiles[wave][1 + slot];
+      uint4* ts = tiles[wave][3 + slot];
+      uint32_t qw[NW], dw[NW];
       btile_to_mfma<D>(tq, x[0], qw, lane);
       btile_to_mfma<D>(td, x[1], dw, lane);  // the dout tile stays for the dS operand
-      btile_to_mfma<D>(to, x[2], ow, lane);
+      u32x4 bd[NKS];
+#pragma unroll
+      for (int i = 0; i < NW; ++i) bd[i >> 2][i & 3] = dw[i];
+      floatx4 acc[NRT];
+#pragma unroll
+      for (int rt = 0; rt < NRT; ++rt) acc[rt] = floatx4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int ks = 0; ks < NKS; ++ks)
+#pragma unroll
+        for (int rt = 0; rt < NRT; ++rt) acc[rt] = mfma_bf16(sh[rt][ks], bd[ks], acc[rt]);  // S_c dout
+#pragma unroll
+      for (int ks = 0; ks < NKS; ++ks)
+#pragma unroll
+        for (int rt = 0; rt < NRT; ++rt) acc[rt] = mfma_bf16(sl[rt][ks], bd[ks], acc[rt]);
       uint32_t rqw[NW];
       u32x4 rq[NKS];
 #pragma unroll
@@ -1733,30 +1779,21 @@ __global__ __launch_bounds__(kThreads, 1) void sva_bwd_out_kernel(
       floatx4 dacc = floatx4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int ks = 0; ks < NKS; ++ks) dacc = mfma_bf16(az[ks], rq[ks], dacc);
-      float dot = 0.f;
-#pragma unroll
-      for (int m = 0; m < FPLa; ++m) dot += bf16_elem(dw, m) * bf16_elem(ow, m);
       const float den = sum_over_rows(dacc[0]) + eps;
-      dot = sum_over_rows(dot);
       // rows past the segment hold zeros; their 1/den is taken as 0 so that
       // they add nothing (also when eps is 0)
-      const float inv = t + row < je ? 1.0f / den : 0.f;
-      const float dd = -dot * inv;  // dden: -(dout . out) / den
+      const float inv = t + row < je ? __builtin_amdgcn_rcpf(den) : 0.f;
       uint32_t co = 0;
       if constexpr (ROPE != 0) co = decode_packed((uint32_t)min(t + row, je - 1), geo.fHW, geo.fWs);
-      {
-        // qt / den, rounded to bf16, into the tile of the dS product (the
-        // unrotated phi(q) first feeds this lane's dZ share)
-        float qf[FPLa];
+      float qf[FPLa];  // qt
 #pragma unroll
-        for (int m = 0; m < FPLa; ++m) {
-          qf[m] = bf16_elem(rqw, m);
-          zacc[m] += dd * qf[m];
-        }
-        if constexpr (ROPE != 0) {
-          if constexpr (RUNS) rope_lane_runs<NKS>(qf, tab, pl, co);
-          else rope_lane<ROPE, NPAIR>(qf, tab, pl, co);
-        }
+      for (int m = 0; m < FPLa; ++m) qf[m] = bf16_elem(rqw, m);
+      if constexpr (ROPE != 0) {
+        if constexpr (RUNS) rope_lane_runs<NKS>(qf, tab, pl, co);
+        else rope_lane<ROPE, NPAIR>(qf, tab, pl, co);
+      }
+      {
+        // qt / den, rounded to bf16, into the tile of the dS product
         uint32_t sw[NW];
 #pragma unroll
         for (int i = 0; i < NW; ++i) sw[i] = pack_bf16x2(qf[2 * i] * inv, qf[2 * i + 1] * inv);
@@ -1764,16 +1801,16 @@ __global__ __launch_bounds__(kThreads, 1) void sva_bwd_out_kernel(
         for (int i = 0; i < NW / 4; ++i)
           ts[T::at(row, 4 * i + g)] = make_uint4(sw[4 * i], sw[4 * i + 1], sw[4 * i + 2], sw[4 * i + 3]);
       }
-      u32x4 bd[NKS];
+      // dout . num = qt . (S_c dout): this lane's key features, then the rows
+      float dot = 0.f;
 #pragma unroll
-      for (int i = 0; i < NW; ++i) bd[i >> 2][i & 3] = dw[i];
-      floatx4 acc[NRT];
+      for (int m = 0; m < FPLa; ++m) dot += qf[m] * acc[m >> 2][m & 3];
+      const float dd = -sum_over_rows(dot) * inv * inv;  // dden: -(dout . num) / den^2
 #pragma unroll
-      for (int rt = 0; rt < NRT; ++rt) acc[rt] = floatx4{0.f, 0.f, 0.f, 0.f};
-      mfma_staged<D>(acc, fst, bd, lane);  // S_c dout, then / den: S_c dnum
+      for (int m = 0; m < FPLa; ++m) zacc[m] += dd * bf16_elem(rqw, m);
       float gq[FPLa];
 #pragma unroll
-      for (int m = 0; m < FPLa; ++m) gq[m] = acc[m >> 2][m & 3] * inv;
+      for (int m = 0; m < FPLa; ++m) gq[m] = acc[m >> 2][m & 3] * inv;  // S_c dnum
       if constexpr (ROPE != 0) {
         if constexpr (RUNS) rope_lane_runs<NKS, true>(gq, tab, pl, co);
         else rope_lane<ROPE, NPAIR, true>(gq, tab, pl, co);
@@ -1781,54 +1818,48 @@ __global__ __launch_bounds__(kThreads, 1) void sva_bwd_out_kernel(
       uint32_t dqw[NW];
 #pragma unroll
       for (int i = 0; i < NW; ++i) {
-        const uint32_t r = rqw[i];
         const float2 zz = *(const float2*)(zst + apply_feat<true>(g, 2 * i));  // runs of 8: pairs stay together
-        const float a = (r & 0xffffu) ? gq[2 * i] + dd * zz.x : 0.f;
-        const float b = (r >> 16) ? gq[2 * i + 1] + dd * zz.y : 0.f;
-        dqw[i] = pack_bf16x2(a, b);
+        // masked after packing, so that no branch guards the Z reads
+        dqw[i] = pack_bf16x2(gq[2 * i] + dd * zz.x, gq[2 * i + 1] + dd * zz.y) & relu_pass_mask(rqw[i]);
       }
       btile_store<D>(tq, dqw, dqrs, t, lane);
     };
     // dS += (qt/den)^T dout over the 32 tokens of a pair of steps.  The
     // transposing reads always run on the whole wavefront: under a partial
     // exec mask ds_read_b64_tr_b16 still writes the destination registers of
-    // the masked-off lanes (measured on gfx950), so an odd last step zeroes
-    // the second pair of tiles instead of masking lanes.
+    // the masked-off lanes (measured on gfx950), so a step past the segment
+    // is computed on zeros instead of masking lanes.
     auto ds_pair = [&]() {
       __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
       u32x4 bo[NRT];
 #pragma unroll
-      for (int st = 0; st < NRT; ++st) bo[st] = tr_operand<D>(tiles[wave][2], tiles[wave][3], 16 * st, lane);
+      for (int st = 0; st < NRT; ++st) bo[st] = tr_operand<D>(tiles[wave][1], tiles[wave][2], 16 * st, lane);
 #pragma unroll
       for (int rt = 0; rt < NRT; ++rt) {
-        const u32x4 ao = tr_operand<D>(tiles[wave][4], tiles[wave][5], 16 * rt, lane);
+        const u32x4 ao = tr_operand<D>(tiles[wave][3], tiles[wave][4], 16 * rt, lane);
 #pragma unroll
         for (int st = 0; st < NRT; ++st) sacc[rt][st] = mfma_bf16(ao, bo[st], sacc[rt][st]);
       }
       __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
     };
 
-    int k = 0;
-    for (; k + 2 <= nsteps; k += 2) {
-      const int t0 = t_first + k * WSTRIDE;
-      load3(xb, t0 + WSTRIDE);
+    // Whole pairs of steps: when only the first step of the last pair is
+    // inside the segment, the second one reads zeros (the loads past the
+    // segment's end return 0), gets 1/den = 0 on every row, adds nothing to
+    // dS and dZ, and its stores are dropped, so no slot needs clearing.
+    auto step = [&](const uint32_t (&x)[2][NW], int k, int slot) {
+      compute(x, t_first + k * WSTRIDE, slot);
+    };
+    for (int k = 0; k < nsteps; k += 2) {
+      load2(x1, k + 1);
       __builtin_amdgcn_sched_barrier(0);
-      compute(xa, t0, 0);
+      step(x0, k, 0);
       __builtin_amdgcn_sched_barrier(0);
-      load3(xa, t0 + 2 * WSTRIDE);
+      load2(x0, k + 2);
       __builtin_amdgcn_sched_barrier(0);
-      compute(xb, t0 + WSTRIDE, 1);
+      step(x1, k + 1, 1);
       ds_pair();
       __builtin_amdgcn_sched_barrier(0);
-    }
-    if (k < nsteps) {
-      compute(xa, t_first + k * WSTRIDE, 0);
-#pragma unroll
-      for (int u = lane; u < T::TSZ; u += 64) {
-        tiles[wave][3][u] = make_uint4(0u, 0u, 0u, 0u);
-        tiles[wave][5][u] = make_uint4(0u, 0u, 0u, 0u);
-      }
-      ds_pair();
     }
 
     // Fixed-order sum over the waves: waves 2, 3 store their tiles, waves 0,
@@ -2098,8 +2129,10 @@ struct Plan {
   // The forward's prefix runs inside the reduction (the last workgroup of
   // each sequence forms it) instead of in a separate scan launch.
   bool fold;
-  size_t off_counters, off_partials, off_frags, off_zc, ws_bytes;
-  size_t states_zc, states_bytes;  // saved prefix states: operands at 0, Z_c at states_zc
+  size_t off_counters, off_partials, off_frags, off_zc, off_frags_lo, ws_bytes;
+  // Saved prefix states: the operands S_c^T at 0, for bf16 their remainders
+  // (S_c^T - operand, in bf16) at states_lo, Z_c at states_zc.
+  size_t states_lo, states_zc, states_bytes;
 };
 
 constexpr long long kRedWorkgroupsMax = 1024;  // bounds the partials workspace
@@ -2200,6 +2233,8 @@ void layout_workspace(Plan* p, long long max_red_wg) {
   off = align256(off + (size_t)p->BH * p->nb * p->D * p->D * esz);
   p->off_zc = off;
   off = align256(off + (size_t)p->BH * p->nb * p->D * sizeof(float));
+  p->off_frags_lo = off;  // the backward's remainders of the operands (bf16)
+  off = align256(off + (p->bf16 ? (size_t)p->BH * p->nb * p->D * p->D * 2 : 0));
   p->ws_bytes = off;
 }
 
@@ -2266,7 +2301,8 @@ Plan make_plan(const sva_desc* d) {
   p.app = make_split(total, kAppWorkgroupsMax, &p.G_app);
   layout_workspace(&p, kRedWorkgroupsMax);
   const size_t esz = p.bf16 ? 2 : 4;
-  p.states_zc = align256((size_t)p.BH * p.nb * p.D * p.D * esz);
+  p.states_lo = align256((size_t)p.BH * p.nb * p.D * p.D * esz);
+  p.states_zc = p.states_lo + (p.bf16 ? align256((size_t)p.BH * p.nb * p.D * p.D * 2) : 0);
   p.states_bytes = p.states_zc + align256((size_t)p.BH * p.nb * p.D * sizeof(float));
   return p;
 }
@@ -2289,7 +2325,7 @@ hipError_t launch_reduce(const Plan& p, const void* k, const void* v, float* par
 template <bool BF16, int D>
 hipError_t launch_scan(const Plan& p, const float* partials, const float* S0, const float* z0,
                        float* S_out, float* z_out, void* frags, float* zc, bool write_frags,
-                       hipStream_t st, bool reverse = false, long long L = 0) {
+                       hipStream_t st, bool reverse = false, long long L = 0, void* frags_lo = nullptr) {
   ScanArgs a;
   a.nb = p.nb;
   a.Nb = p.Nb;
@@ -2300,7 +2336,7 @@ hipError_t launch_scan(const Plan& p, const float* partials, const float* S0, co
   a.write_final = S_out != nullptr;
   a.reverse = reverse;
   void* args[] = {(void*)&partials, (void*)&S0, (void*)&z0, (void*)&S_out, (void*)&z_out,
-                  (void*)&frags, (void*)&zc, &a};
+                  (void*)&frags, (void*)&zc, (void*)&frags_lo, &a};
   constexpr int groups = (D * D + D) / 4;
   return hipLaunchKernel((const void*)&sva_scan_kernel<BF16, D>,
                          dim3((groups + kScanElems - 1) / kScanElems, p.BH), dim3(kThreads), args, 0, st);
@@ -2329,14 +2365,14 @@ hipError_t launch_prep(const Plan& p, const void* x, float* xr, float* xphi, hip
 
 // Backward launchers (bf16 only; BF16 is always true where they are used).
 template <bool BF16, int D, int ROPE>
-hipError_t launch_bwd_out(const Plan& p, const void* q, const void* dout, const void* out, void* dq,
-                          float* partials, const void* frags, const float* zc, float eps, hipStream_t st) {
+hipError_t launch_bwd_out(const Plan& p, const void* q, const void* dout, void* dq, float* partials,
+                          const void* frags, const void* frags_lo, const float* zc, float eps, hipStream_t st) {
   static_assert(BF16, "the backward runs on bf16 inputs");
   Geo geo = p.geo;
   SplitArgs sp = p.bwd;
   RopeArgs ra = p.ra;
-  void* args[] = {(void*)&q, (void*)&dout, (void*)&out, (void*)&dq, (void*)&partials,
-                  (void*)&frags, (void*)&zc, &geo, &sp, &ra, &eps};
+  void* args[] = {(void*)&q, (void*)&dout, (void*)&dq, (void*)&partials, (void*)&frags, (void*)&frags_lo,
+                  (void*)&zc, &geo, &sp, &ra, &eps};
   return hipLaunchKernel((const void*)&sva_bwd_out_kernel<D, ROPE>, dim3(p.G_bwd_out),
                          dim3(kThreads), args, ROPE ? p.tab_bytes : 0, st);
 }
@@ -2437,6 +2473,8 @@ sva_status launch_fwd(const Plan& p, const void* q, const void* k, const void* v
   // the prefix states go to the caller's buffer when it keeps them
   void* frags = states ? states : (void*)(wsb + p.off_frags);
   float* zc = states ? (float*)((char*)states + p.states_zc) : (float*)(wsb + p.off_zc);
+  // the backward takes S_c as two bf16 parts (kept states only)
+  void* frags_lo = states && p.bf16 ? (void*)((char*)states + p.states_lo) : nullptr;
   if (p.fold) {
     const FoldArgs fa{(unsigned*)(wsb + p.off_counters), S0, z0, S_out, z_out, frags, zc};
     if ((stages & SVA_STAGE_REDUCE) && SVA_DISPATCH(p, launch_reduce, p, k, v, partials, st, &fa) != hipSuccess)
@@ -2445,7 +2483,8 @@ sva_status launch_fwd(const Plan& p, const void* q, const void* k, const void* v
     if ((stages & SVA_STAGE_REDUCE) && SVA_DISPATCH(p, launch_reduce, p, k, v, partials, st) != hipSuccess)
       return SVA_ERR_HIP;
     if ((stages & SVA_STAGE_SCAN) &&
-        SVA_DISPATCH2(p, launch_scan, p, partials, S0, z0, S_out, z_out, frags, zc, true, st) != hipSuccess)
+        SVA_DISPATCH2(p, launch_scan, p, partials, S0, z0, S_out, z_out, frags, zc, true, st, false, 0,
+                      frags_lo) != hipSuccess)
       return SVA_ERR_HIP;
   }
   if ((stages & SVA_STAGE_APPLY) && SVA_DISPATCH(p, launch_apply, p, q, out, frags, zc, eps, st) != hipSuccess)
@@ -2463,20 +2502,23 @@ sva_status run_fwd(const sva_desc* desc, const void* q, const void* k, const voi
   if (!ws || ws_bytes < p.ws_bytes || !is_aligned16(ws)) return SVA_ERR_WORKSPACE;
   if (states && !is_aligned16(states)) return SVA_ERR_INVALID_ARG;
   if (stages < 1 || stages > SVA_STAGE_ALL) return SVA_ERR_INVALID_ARG;
+  // kept states carry the operands' bf16 remainders, which the scan kernel
+  // writes (the prefix folded into the reduction forms only the operands)
+  if (states) p.fold = false;
   plan_grids(&p);
   return launch_fwd(p, q, k, v, out, S0, z0, S_out, z_out, (char*)ws, stages, states, desc->eps,
                     (hipStream_t)stream);
 }
 
-sva_status run_bwd(const sva_desc* desc, const void* q, const void* k, const void* v, const void* out,
-                   const void* dout, const float* S0, const float* z0, const float* dS_out,
-                   const float* dz_out, void* dq, void* dk, void* dv, float* dS0, float* dz0,
-                   const void* states, void* ws, size_t ws_bytes, void* stream) {
+sva_status run_bwd(const sva_desc* desc, const void* q, const void* k, const void* v, const void* dout,
+                   const float* S0, const float* z0, const float* dS_out, const float* dz_out, void* dq,
+                   void* dk, void* dv, float* dS0, float* dz0, const void* states, void* ws, size_t ws_bytes,
+                   void* stream) {
   Plan p;
   sva_status s = check_common(desc, false, &p);
   if (s != SVA_OK) return s;
   if (!p.bf16) return SVA_ERR_UNSUPPORTED;
-  const void* in[] = {q, k, v, out, dout};
+  const void* in[] = {q, k, v, dout};
   void* grads[] = {dq, dk, dv};
   for (const void* x : in)
     if (!x || !is_aligned16(x)) return SVA_ERR_INVALID_ARG;
@@ -2510,18 +2552,21 @@ sva_status run_bwd(const sva_desc* desc, const void* q, const void* k, const voi
   // The forward's prefix states: saved by sva_lin_attn_fwd_save, or
   // recomputed here (reduction and scan of the forward) into the workspace.
   const void* sfrags = frags;
+  const void* sfrags_lo = wsb + p.off_frags_lo;
   const float* szc = zc;
   if (states) {
     sfrags = states;
+    sfrags_lo = (const char*)states + p.states_lo;
     szc = (const float*)((const char*)states + p.states_zc);
   } else {
+    void* lo = wsb + p.off_frags_lo;
     if (SVA_BWD(launch_reduce, p, k, v, partials, st) != hipSuccess) return SVA_ERR_HIP;
-    if ((p.D == 64 ? launch_scan<true, 64>(p, partials, S0, z0, nullptr, nullptr, frags, zc, true, st)
-                   : launch_scan<true, 32>(p, partials, S0, z0, nullptr, nullptr, frags, zc, true, st)) !=
-        hipSuccess)
+    if ((p.D == 64 ? launch_scan<true, 64>(p, partials, S0, z0, nullptr, nullptr, frags, zc, true, st, false, 0, lo)
+                   : launch_scan<true, 32>(p, partials, S0, z0, nullptr, nullptr, frags, zc, true, st, false, 0,
+                                           lo)) != hipSuccess)
       return SVA_ERR_HIP;
   }
-  if (SVA_BWD(launch_bwd_out, p, q, dout, out, dq, partials, sfrags, szc, desc->eps, st) != hipSuccess)
+  if (SVA_BWD(launch_bwd_out, p, q, dout, dq, partials, sfrags, sfrags_lo, szc, desc->eps, st) != hipSuccess)
     return SVA_ERR_HIP;
   if ((p.D == 64 ? launch_scan<true, 64>(p, partials, dS_out, dz_out, dS0, dz0, frags, zc, true, st, true,
                                          p.bwd.L)
@@ -2766,11 +2811,11 @@ sva_status sva_lin_attn_bwd_workspace(const sva_desc* desc, size_t* bytes) {
 }
 
 sva_status sva_lin_attn_bwd(const sva_desc* desc, const void* q, const void* k, const void* v,
-                            const void* out, const void* dout, const float* S0, const float* z0,
+                            const void* dout, const float* S0, const float* z0,
                             const float* dS_out, const float* dz_out, const void* states, void* dq,
                             void* dk, void* dv, float* dS0, float* dz0, void* ws, size_t ws_bytes,
                             void* stream) {
-  return run_bwd(desc, q, k, v, out, dout, S0, z0, dS_out, dz_out, dq, dk, dv, dS0, dz0, states, ws,
+  return run_bwd(desc, q, k, v, dout, S0, z0, dS_out, dz_out, dq, dk, dv, dS0, dz0, states, ws,
                  ws_bytes, stream);
 }
 

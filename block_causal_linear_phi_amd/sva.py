@@ -69,7 +69,7 @@ _SIG = {
     "sva_lin_attn_fwd_stages": (ctypes.c_int, [ctypes.POINTER(SvaDesc), _VP, _VP, _VP, _VP, _VP, _VP, _VP,
                                                _VP, _VP, ctypes.c_size_t, _VP, ctypes.c_int]),
     "sva_lin_attn_bwd_workspace": (ctypes.c_int, [ctypes.POINTER(SvaDesc), ctypes.POINTER(ctypes.c_size_t)]),
-    "sva_lin_attn_bwd": (ctypes.c_int, [ctypes.POINTER(SvaDesc)] + [_VP] * 16 + [ctypes.c_size_t, _VP]),
+    "sva_lin_attn_bwd": (ctypes.c_int, [ctypes.POINTER(SvaDesc)] + [_VP] * 15 + [ctypes.c_size_t, _VP]),
     "sva_lin_attn_states_bytes": (ctypes.c_int, [ctypes.POINTER(SvaDesc), ctypes.POINTER(ctypes.c_size_t)]),
     "sva_lin_attn_fwd_save": (ctypes.c_int, [ctypes.POINTER(SvaDesc)] + [_VP] * 10 + [ctypes.c_size_t, _VP]),
     "sva_block_cache_workspace": (ctypes.c_int, [ctypes.POINTER(SvaDesc), ctypes.POINTER(ctypes.c_size_t)]),
@@ -309,20 +309,20 @@ def sva_lin_attn_fwd_save(q, k, v, grid: Tuple[int, int, int], frames_per_block:
     return out, states
 
 
-def sva_lin_attn_bwd(q, k, v, out, dout, grid: Tuple[int, int, int], frames_per_block: int, *, t0: int = 0,
+def sva_lin_attn_bwd(q, k, v, dout, grid: Tuple[int, int, int], frames_per_block: int, *, t0: int = 0,
                      rope: bool = False, split=None, base: float = 10000.0, eps: float = 1e-6,
                      S0=None, z0=None, dS_out=None, dz_out=None, states=None, dq=None, dk=None, dv=None,
                      dS0=None, dz0=None, ws=None, stream=None):
     """Gradients of the forward (sva_lin_attn_bwd), bf16.  Returns (dq, dk, dv);
     dS0/dz0 are filled when given.  `states` from sva_lin_attn_fwd_save
-    skips recomputing the forward's prefix states."""
+    skips recomputing the forward's prefix states.  The forward's output is
+    not needed: the kernels form it again from q and the states."""
     import torch
     for na, ta, nb_, tb in (("S0", S0, "z0", z0), ("dS_out", dS_out, "dz_out", dz_out), ("dS0", dS0, "dz0", dz0)):
         _pair(na, ta, nb_, tb)
-    if out is None or dout is None:
-        raise ValueError("out and dout are required")
-    _check_attn(q, grid, like_q=[("k", k), ("v", v), ("out", out), ("dout", dout), ("dq", dq), ("dk", dk),
-                                 ("dv", dv)],
+    if dout is None:
+        raise ValueError("dout is required")
+    _check_attn(q, grid, like_q=[("k", k), ("v", v), ("dout", dout), ("dq", dq), ("dk", dk), ("dv", dv)],
                 caches=[("S0", S0, "S"), ("z0", z0, "z"), ("dS_out", dS_out, "S"), ("dz_out", dz_out, "z"),
                         ("dS0", dS0, "S"), ("dz0", dz0, "z")],
                 buffers=[("ws", ws), ("states", states)])
@@ -331,7 +331,7 @@ def sva_lin_attn_bwd(q, k, v, out, dout, grid: Tuple[int, int, int], frames_per_
     dk = torch.empty_like(k) if dk is None else dk
     dv = torch.empty_like(v) if dv is None else dv
     ws = _workspace(sva_lin_attn_bwd_workspace(desc), q, ws)
-    st = lib().sva_lin_attn_bwd(ctypes.byref(desc), _ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(dout),
+    st = lib().sva_lin_attn_bwd(ctypes.byref(desc), _ptr(q), _ptr(k), _ptr(v), _ptr(dout),
                                 _ptr(S0), _ptr(z0), _ptr(dS_out), _ptr(dz_out), _ptr(states), _ptr(dq),
                                 _ptr(dk), _ptr(dv),
                                 _ptr(dS0), _ptr(dz0), _ptr(ws), ws.numel() * ws.element_size(), _stream(stream))

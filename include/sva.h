@@ -149,9 +149,10 @@ sva_status sva_lin_attn_bwd_workspace(const sva_desc* desc, size_t* bytes);
  * run ([talk], block causal segment), by the chain rule through the same
  * steps.  For L = <out, dout> + <S_final, dS_out> + <z_final, dz_out>:
  *   q, k, v   in:  the forward's inputs [B, H, N, d] bf16
- *   out       in:  the forward's output for them [B, H, N, d] bf16 (its
- *                  denominator term uses dout . out)
  *   dout      in:  dL/dout [B, H, N, d] bf16
+ * The forward's output is not an input: the denominator's term needs
+ * dout . out, and out is formed again from q and the prefix states (bf16
+ * operands, fp32 sums, not rounded to bf16).
  *   S0, z0    in:  the forward's initial cache fp32, or both NULL (zeros)
  *   dS_out, dz_out in: dL/d(final cache) [B,H,d,d], [B,H,d] fp32, or both
  *                  NULL (zero)
@@ -167,7 +168,7 @@ sva_status sva_lin_attn_bwd_workspace(const sva_desc* desc, size_t* bytes);
  * The derivative of ReLU is taken as 0 at 0.  bf16 only: other dtypes return
  * SVA_ERR_UNSUPPORTED before any work. */
 sva_status sva_lin_attn_bwd(const sva_desc* desc, const void* q, const void* k,
-                            const void* v, const void* out, const void* dout,
+                            const void* v, const void* dout,
                             const float* S0, const float* z0,
                             const float* dS_out, const float* dz_out,
                             const void* states, void* dq, void* dk, void* dv,
@@ -175,14 +176,17 @@ sva_status sva_lin_attn_bwd(const sva_desc* desc, const void* q, const void* k,
                             void* stream);
 
 /* Bytes of the prefix states one forward call can keep for the backward:
- * every block's S_c (in the input dtype) and Z_c (fp32), B*H*nb*(d*d*esize +
- * d*4) plus alignment; about 1.9 MB for 16 heads of d = 64 in 7 blocks. */
+ * every block's S_c (in the input dtype; for bf16 also its remainder S_c -
+ * bf16(S_c) in bf16, which the backward adds back) and Z_c (fp32):
+ * B*H*nb*(d*d*esize*(bf16 ? 2 : 1) + d*4) plus alignment; about 1.9 MB for
+ * 16 heads of d = 64 in 7 blocks. */
 sva_status sva_lin_attn_states_bytes(const sva_desc* desc, size_t* bytes);
 
 /* sva_lin_attn_fwd that also keeps its prefix states in `states`
  * (caller-owned, sva_lin_attn_states_bytes long, 16-byte aligned) for
- * sva_lin_attn_bwd.  The states are written instead of a workspace copy, so
- * keeping them costs nothing extra. */
+ * sva_lin_attn_bwd.  The states are written instead of a workspace copy
+ * (plus, for bf16, the remainders: d*d*2 bytes per block and head), and the
+ * prefix always runs in the scan kernel, which forms the remainders. */
 sva_status sva_lin_attn_fwd_save(const sva_desc* desc, const void* q,
                                  const void* k, const void* v, void* out,
                                  const float* S0, const float* z0,

@@ -159,7 +159,7 @@ def test_bwd_bad_descriptors_are_rejected(kw, code):
     d = _desc(**kw)
     big = 1 << 36  # fake, widely spaced device addresses; nothing is touched
     ptrs = [big * (i + 1) for i in range(8)]
-    st = sva.lib().sva_lin_attn_bwd(ctypes.byref(d), ptrs[0], ptrs[1], ptrs[2], ptrs[3], ptrs[4], None, None,
+    st = sva.lib().sva_lin_attn_bwd(ctypes.byref(d), ptrs[0], ptrs[1], ptrs[2], ptrs[3], None, None,
                                     None, None, None, ptrs[5], ptrs[6], ptrs[7], None, None, 16, 1 << 40, None)
     assert st == code
 
@@ -171,21 +171,21 @@ def test_bwd_pointer_checks_happen_before_launch():
     p = [big * (i + 1) for i in range(8)]
     lib = sva.lib()
     # arguments after `d`, with states (NULL) inserted after dz_out
-    call = lambda *a: lib.sva_lin_attn_bwd(ctypes.byref(d), *a[:9], None, *a[9:])
+    call = lambda *a: lib.sva_lin_attn_bwd(ctypes.byref(d), *a[:8], None, *a[8:])
     # a gradient buffer overlapping an input
-    assert call(p[0], p[1], p[2], p[3], p[4], None, None, None, None, p[0], p[6], p[7], None, None, 16,
+    assert call(p[0], p[1], p[2], p[3], None, None, None, None, p[0], p[6], p[7], None, None, 16,
                 1 << 40, None) == sva.SVA_ERR_INVALID_ARG
     # two gradient buffers overlapping each other
-    assert call(p[0], p[1], p[2], p[3], p[4], None, None, None, None, p[5], p[5] + 64, p[7], None, None, 16,
+    assert call(p[0], p[1], p[2], p[3], None, None, None, None, p[5], p[5] + 64, p[7], None, None, 16,
                 1 << 40, None) == sva.SVA_ERR_INVALID_ARG
     # dS0 without dz0
-    assert call(p[0], p[1], p[2], p[3], p[4], None, None, None, None, p[5], p[6], p[7], 4096, None, 16,
+    assert call(p[0], p[1], p[2], p[3], None, None, None, None, p[5], p[6], p[7], 4096, None, 16,
                 1 << 40, None) == sva.SVA_ERR_INVALID_ARG
     # missing dout
-    assert call(p[0], p[1], p[2], p[3], None, None, None, None, None, p[5], p[6], p[7], None, None, 16,
+    assert call(p[0], p[1], p[2], None, None, None, None, None, p[5], p[6], p[7], None, None, 16,
                 1 << 40, None) == sva.SVA_ERR_INVALID_ARG
     # workspace too small
-    assert call(p[0], p[1], p[2], p[3], p[4], None, None, None, None, p[5], p[6], p[7], None, None, 16,
+    assert call(p[0], p[1], p[2], p[3], None, None, None, None, p[5], p[6], p[7], None, None, 16,
                 16, None) == sva.SVA_ERR_WORKSPACE
 
 
@@ -211,7 +211,9 @@ def test_binding_signatures_match_the_header():
 def test_states_bytes():
     n = sva.sva_lin_attn_states_bytes(_desc())
     d, nb, BH = 64, 7, 16
-    assert BH * nb * (d * d * 2 + d * 4) <= n <= BH * nb * (d * d * 2 + d * 4) + 512
+    # bf16: the operands S_c^T, their bf16 remainders, and Z_c
+    exact = BH * nb * (2 * d * d * 2 + d * 4)
+    assert exact <= n <= exact + 768
 
 
 @fake_pointers

@@ -71,13 +71,13 @@ def test_fwd_save_and_bwd_check_their_extra_arguments():
         sva.sva_lin_attn_fwd_save(q, k, v, GRID, F, states=_t(64, 8, dtype=torch.uint8).t())
     good = _t(1, 2, N, 64)
     with pytest.raises(ValueError, match="shape"):
-        sva.sva_lin_attn_bwd(q, k, v, good, _t(1, 2, N, 32), GRID, F)          # dout
+        sva.sva_lin_attn_bwd(q, k, v, _t(1, 2, N, 32), GRID, F)          # dout
     with pytest.raises(ValueError, match="dtype"):
-        sva.sva_lin_attn_bwd(q, k, v, good, good, GRID, F, dq=_t(1, 2, N, 64, dtype=torch.float32))
+        sva.sva_lin_attn_bwd(q, k, v, good, GRID, F, dq=_t(1, 2, N, 64, dtype=torch.float32))
     with pytest.raises(ValueError, match="together"):
-        sva.sva_lin_attn_bwd(q, k, v, good, good, GRID, F, dS0=_t(1, 2, 64, 64, dtype=torch.float32))
+        sva.sva_lin_attn_bwd(q, k, v, good, GRID, F, dS0=_t(1, 2, 64, 64, dtype=torch.float32))
     with pytest.raises(ValueError, match="GPU"):
-        sva.sva_lin_attn_bwd(q, k, v, good, good, GRID, F)
+        sva.sva_lin_attn_bwd(q, k, v, good, GRID, F)
 
 
 def test_cache_calls_check_the_cache():
