@@ -1519,21 +1519,6 @@ __device__ __forceinline__ void btile_store(uint4* wst, const uint32_t* ow, __am
   __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
 }
 
-// acc[rt] += A[rt] * b over the k-steps, A's rows fo(rt, row) read from an
-// operand matrix staged in LDS (row f, chunk c at frag_at(f, c)).
-template <int D>
-__device__ __forceinline__ void mfma_staged(floatx4* acc, const uint4* fst, const u32x4* b, int lane) {
-  using T = BTile<D>;
-  const int g = lane >> 4, row = lane & 15;
-#pragma unroll
-  for (int ks = 0; ks < T::NKS; ++ks)
-#pragma unroll
-    for (int rt = 0; rt < T::NRT; ++rt) {
-      const uint4 a = fst[T::frag_at(T::fo(rt, row), 4 * ks + g)];
-      acc[rt] = mfma_bf16(u32x4{a.x, a.y, a.z, a.w}, b[ks], acc[rt]);
-    }
-}
-
 // Stage a [D, D] bf16 matrix stored row-major in global memory (M^T of the
 // prefix operands, rows = output features) into LDS: as it is (rows a), or
 // transposed (rows = its columns) for products with the other side.
@@ -1999,6 +1984,18 @@ __global__ __launch_bounds__(kThreads, 2) void sva_bwd_kv_kernel(
     float gz[FPLa];
 #pragma unroll
     for (int m = 0; m < FPLa; ++m) gz[m] = gst[apply_feat<true>(g, m)];
+    // G_c's A-operand fragments, both orientations, in registers for the
+    // segment (not re-read from LDS per tile)
+    u32x4 gT[NRT][NKS], gN[NRT][NKS];
+#pragma unroll
+    for (int rt = 0; rt < NRT; ++rt)
+#pragma unroll
+      for (int ks = 0; ks < NKS; ++ks) {
+        const uint4 x = fsT[T::frag_at(T::fo(rt, row), 4 * ks + g)];
+        const uint4 y = fsN[T::frag_at(T::fo(rt, row), 4 * ks + g)];
+        gT[rt][ks] = u32x4{x.x, x.y, x.z, x.w};
+        gN[rt][ks] = u32x4{y.x, y.y, y.z, y.w};
+      }
 
     auto compute = [&](const uint32_t (&x)[2][NW], int t) {
       uint32_t kw[NW], vw[NW];
@@ -2031,8 +2028,13 @@ __global__ __launch_bounds__(kThreads, 2) void sva_bwd_kv_kernel(
         av[rt] = floatx4{0.f, 0.f, 0.f, 0.f};
         ak[rt] = floatx4{0.f, 0.f, 0.f, 0.f};
       }
-      mfma_staged<D>(av, fsT, kt, lane);  // dv = G_c^T kt
-      mfma_staged<D>(ak, fsN, bv, lane);  // dkt = G_c v
+#pragma unroll
+      for (int ks = 0; ks < NKS; ++ks)
+#pragma unroll
+        for (int rt = 0; rt < NRT; ++rt) {
+          av[rt] = mfma_bf16(gT[rt][ks], kt[ks], av[rt]);  // dv = G_c^T kt
+          ak[rt] = mfma_bf16(gN[rt][ks], bv[ks], ak[rt]);  // dkt = G_c v
+        }
       float gk[FPLa];
 #pragma unroll
       for (int m = 0; m < FPLa; ++m) gk[m] = ak[m >> 2][m & 3];
