@@ -18,11 +18,23 @@ Sources:
           e = 255 is NaN); each element is FP4 E2M1 (1 sign, 2 exponent bits
           with bias 1, 1 mantissa bit; exponent 0 is subnormal: 0 or 0.5).
 
+  OCP MX Specification v1.0, conversion to an MX format (its section 6.3):
+          a block's shared scale is 2^(floor(log2(max |V_i|)) - emax_elem),
+          emax_elem being the largest exponent of the element format (2 for
+          E2M1, whose largest value is 6 = 1.5 * 2^2); each element is
+          V_i / scale rounded to the element format, ties to even, values
+          past the largest normal clamped to it.
+
 Readings taken (each is a choice, not a quote):
   * the 4-bit format is MXFP4 (the block-scaled FP4 that gfx950 implements),
     not NVFP4; the blocks run along the input channels;
-  * activations stay bf16 (4-bit weights, 16-bit activations); weights are
-    decoded exactly and the products accumulate in fp32 on the GPU;
+  * two activation precisions: bf16 activations (W4A16: 4-bit weights,
+    16-bit activations), and MXFP4 activations (W4A4, as SVDQuant's NVFP4
+    deployment quantizes both operands of the projection to 4 bits), each
+    token row quantized per 32 input channels as the MX conversion above
+    states, the shared exponent clamped to E8M0's range [-127, 127] and an
+    all-zero block given scale byte 0; weights are decoded exactly and the
+    products accumulate in fp32 on the GPU;
   * the fused weight's output columns are [q | k | v], each H heads of d
     features: column n = which * H * d + h * d + f;
   * the outputs are q, k, v in the attention's [B, H, N, d] layout, rounded
@@ -33,7 +45,7 @@ from __future__ import annotations
 
 import numpy as np
 
-__all__ = ["e2m1_value", "e8m0_value", "mxfp4_decode", "qkv_project"]
+__all__ = ["e2m1_value", "e8m0_value", "mxfp4_decode", "mxfp4_quantize", "qkv_project", "qkv_project_w4a4"]
 
 
 def e2m1_value(code):
@@ -78,3 +90,46 @@ def qkv_project(x, codes, scales, bias, H, d):
         y = y + np.asarray(bias, dtype=np.float64)[None, None, :]
     y = y.reshape(B, N, 3, H, d).transpose(2, 0, 3, 1, 4)  # [3, B, H, N, d]
     return y[0].copy(), y[1].copy(), y[2].copy()
+
+
+_E2M1_MAGNITUDES = np.array([0.0, 0.5, 1.0, 1.5, 2.0, 3.0, 4.0, 6.0])  # codes 0..7
+
+
+def mxfp4_quantize(x):
+    """x [..., K] (K a multiple of 32) -> (codes [..., K] in 0..15, scales
+    [..., K / 32] bytes), by the MX conversion: per block of 32 consecutive
+    elements, E = floor(log2(max |x_i|)) - 2 clamped to [-127, 127] (an
+    all-zero block takes E = -127), scale byte E + 127, and element i the
+    E2M1 code whose magnitude is nearest to |x_i| / 2^E -- at equal distance
+    the even code -- with the sign of x_i (so -0.0 and negatives that round to
+    zero keep the sign bit).  The largest magnitude, 6, is the nearest value
+    for everything above 5, which is the clamping of the specification."""
+    x = np.asarray(x, dtype=np.float64)
+    K = x.shape[-1]
+    if K % 32 != 0:
+        raise ValueError("the last axis must be a multiple of 32")
+    blocks = x.reshape(x.shape[:-1] + (K // 32, 32))
+    amax = np.abs(blocks).max(axis=-1)
+    _, e = np.frexp(amax)  # amax = m 2^e, m in [0.5, 1): floor(log2 amax) = e - 1
+    E = np.where(amax > 0, e - 1 - 2, -127)
+    E = np.clip(E, -127, 127)
+    v = np.abs(blocks) / np.ldexp(1.0, E)[..., None]
+    dist = np.abs(v[..., None] - _E2M1_MAGNITUDES)  # [..., 32, 8]
+    best = dist.min(axis=-1, keepdims=True)
+    # the nearest magnitudes; among two at equal distance, the even code
+    cand = np.where(dist == best, np.arange(8), 99)
+    even = np.where(cand % 2 == 0, cand, 99).min(axis=-1)
+    code = np.where(even < 99, even, cand.min(axis=-1))
+    code = code + 8 * np.signbit(blocks)
+    return code.reshape(x.shape).astype(np.int64), (E + 127).astype(np.int64)
+
+
+def qkv_project_w4a4(x, codes, scales, bias, H, d):
+    """As qkv_project, with the activations taken through mxfp4_quantize first
+    (per token row, blocks along the input channels): y = X W + bias with
+    X = mxfp4_decode(mxfp4_quantize(x)) and W = mxfp4_decode(codes, scales)^T."""
+    x = np.asarray(x, dtype=np.float64)
+    B, N, C = x.shape
+    xc, xs = mxfp4_quantize(x.reshape(B * N, C))
+    xq = mxfp4_decode(xc, xs).reshape(B, N, C)
+    return qkv_project(xq, codes, scales, bias, H, d)
