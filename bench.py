@@ -34,6 +34,7 @@ if ROOT not in sys.path:
 
 HBM_PEAK_GBS = 8000.0  # MI355X HBM3E, GB/s
 MFMA_BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 matrix peak
+MFMA_FP4_PEAK_TFLOPS = 10100.0  # MI355X dense fp4 (MX) matrix peak
 KERNEL_SRC = os.path.join(ROOT, "block_causal_linear_phi_amd", "csrc", "sva.hip")
 TCONV_SRC = os.path.join(ROOT, "block_causal_linear_phi_amd", "csrc", "tconv.hip")
 PROJ_SRC = os.path.join(ROOT, "block_causal_linear_phi_amd", "csrc", "proj.hip")
@@ -444,6 +445,52 @@ def proj_leg(w, steps: int, warmup: int, sets: int):
     return a.elapsed_time(b) / steps
 
 
+def proj_w4a4_leg(w, steps: int, warmup: int, sets: int):
+    """The W4A4 QKV projection on the workload's tokens: one step = the MX
+    conversion of x (sva_mxfp4_quant_acts) then the 4-bit GEMM
+    (sva_qkv_proj_w4a4), `sets` input/output buffer sets alternating.
+    Returns ms per step, and ms per call of each kernel alone (back to back,
+    no event between launches)."""
+    import torch
+    from block_causal_linear_phi_amd import sva
+    from block_causal_linear_phi_amd import workloads as wl
+
+    dev = torch.device("cuda:0")
+    x0 = torch.empty((w.B, w.N, w.C), dtype=torch.bfloat16, device=dev)
+    for bi in range(w.B):
+        for j, s0 in enumerate(range(0, w.N, 4096)):
+            n = min(4096, w.N - s0)
+            _, raw = wl.draw((n, w.C), wl.seed_for(w.name, "x", bi, j), 1.0, "bf16")
+            x0[bi, s0:s0 + n].copy_(torch.from_numpy(raw.view("int16")).view(torch.bfloat16))
+    codes, scales = wl.mxfp4_weights(w.n_out, w.C, wl.seed_for(w.name, "w", 0, 0))
+    wp = sva.sva_mxfp4_pack_weights(torch.from_numpy(wl.pack_nibbles(codes)).to(dev),
+                                    torch.from_numpy(scales).to(dev), w.H, w.d)  # once, as at weight load
+    bias = torch.from_numpy(wl.draw((w.n_out,), wl.seed_for(w.name, "bias", 0, 0), 0.1, "f32")[0]).to(dev)
+    xs = [x0] + [x0.clone() for _ in range(sets - 1)]
+    xqs = [sva.sva_mxfp4_quant_acts(x) for x in xs]
+    outs = [[torch.empty((w.B, w.H, w.N, w.d), dtype=torch.bfloat16, device=dev) for _ in range(3)]
+            for _ in range(sets)]
+    stream = torch.cuda.current_stream()
+
+    def quant(i):
+        sva.sva_mxfp4_quant_acts(xs[i % sets], out=xqs[i % sets], stream=stream)
+
+    def gemm(i):
+        o = outs[i % sets]
+        sva.sva_qkv_proj_w4a4(xqs[i % sets], wp, bias, w.B, w.N, w.C, w.H, w.d, q=o[0], k=o[1], v=o[2],
+                              stream=stream)
+
+    def step(i):
+        quant(i)
+        gemm(i)
+
+    for i in range(warmup):
+        step(i)
+    torch.cuda.synchronize()
+    ms = _timed(stream, step, steps)
+    return ms, _timed(stream, quant, steps), _timed(stream, gemm, steps)
+
+
 def fused_leg(w, aw, steps: int, warmup: int, sets: int):
     """Projection + attention at the workload's token count, two ways, each
     timed over `steps` calls with `sets` input/output sets alternating:
@@ -815,6 +862,8 @@ def main():
     ap.add_argument("--sets", type=int, default=2, help="input buffer sets that alternate between steps")
     ap.add_argument("--cpu-reps", type=int, default=4)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--proj-w4a4", action="store_true",
+                    help="time the W4A4 QKV projection (activation conversion + 4-bit GEMM)")
     ap.add_argument("--backward", action="store_true",
                     help="time the backward (sva_lin_attn_bwd) instead of the forward")
     ap.add_argument("--tconv", action="store_true",
@@ -876,6 +925,36 @@ def main():
             "ms_per_step_two_calls": ms_two, "speedup_over_two_calls": ms_two / ms,
             "projection_tflops": flops / (ms * 1e-3) / 1e12,
         }), flush=True)
+        return
+    if args.proj_w4a4:
+        pw = wl.PROJ_WORKLOADS["proj_" + args.workload]
+        ms, q_ms, g_ms = proj_w4a4_leg(pw, args.steps, args.warmup, args.sets)
+        M = pw.B * pw.N
+        flops = 2.0 * M * pw.C * pw.n_out
+        x_bytes = M * pw.C * 2
+        xq_bytes = M * pw.C // 2 + M * pw.C // 32
+        w_bytes = pw.n_out * pw.C * (0.5 + 1 / 32)
+        out_bytes = M * pw.n_out * 2
+        gemm_io = xq_bytes + w_bytes + out_bytes + pw.n_out * 4
+        quant_io = x_bytes + xq_bytes
+        gemm_gbs = gemm_io / (g_ms * 1e-3) / 1e9
+        line = {
+            "metric": "tokens/s of the QKV projection, W4A4 (MXFP4 activations and weights; q, k, v for all heads)",
+            "value": M / (ms * 1e-3), "unit": "tokens/s", "n_gpus": 1, "steps": args.steps,
+            "warmup": args.warmup, "ms_per_step": ms, "higher_is_better": True, "scaling": "weak",
+            "vs_baseline": None, "dtype": "fp4",
+            "data": "synthetic (seeded N(0,1) activations; uniform E2M1 codes, E8M0 scales 2^-7..2^-3; resident in HBM)",
+            "config": {"workload": f"{pw.name}: B={pw.B} N={pw.N} tokens, C={pw.C} -> 3 x {pw.H} heads x {pw.d}, "
+                                   "MXFP4 activations (converted in the step) and weights, bf16 outputs",
+                       "B": pw.B, "tokens": pw.N, "C": pw.C, "H": pw.H, "d": pw.d},
+            # the GEMM writes 2 bytes per output for 2 C / 4 bits of operands: bound by its output stream
+            "roofline": {"bound": "hbm", "kernel": "qkv_proj_w4a4", "achieved": gemm_gbs, "peak": HBM_PEAK_GBS,
+                         "unit": "GB/s", "frac": gemm_gbs / HBM_PEAK_GBS, "traffic": None, "io_bytes": gemm_io},
+            "kernels_us": {"quant_acts": q_ms * 1e3, "qkv_proj_w4a4": g_ms * 1e3},
+            "quant_hbm_frac": quant_io / (q_ms * 1e-3) / 1e9 / HBM_PEAK_GBS,
+            "gemm_fp4_mfma_frac": flops / (g_ms * 1e-3) / 1e12 / MFMA_FP4_PEAK_TFLOPS,
+        }
+        print(json.dumps(line), flush=True)
         return
     if args.proj:
         pw = wl.PROJ_WORKLOADS["proj_" + args.workload]

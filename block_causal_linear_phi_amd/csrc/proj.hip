@@ -149,6 +149,47 @@ __device__ __forceinline__ uint32_t pack2(float a, float b) {
   return __builtin_bit_cast(uint32_t, v);
 }
 
+// Epilogue of a wave's 64 x 64 tile: lane (lg, lr) holds, for token tile
+// tt, features f0 + 8 lg + 0..7 (accumulators 0, 1) and f0 + 32 + 8 lg +
+// 0..7 (2, 3) of token t0 + 16 tt + lr.  Adds the bias, rounds to bf16 and
+// stores 16-byte pieces straight into the [B, H, N, d] rows (non-temporal).
+__device__ __forceinline__ void store_qkv(const pj_floatx4 (&acc)[4][4], const ProjGeo& g,
+                                          const float* __restrict__ bias, void* __restrict__ qp,
+                                          void* __restrict__ kp, void* __restrict__ vp, int f0, int t0, int lg,
+                                          int lr) {
+  const int HD = g.H * g.d;
+#pragma unroll
+  for (int run = 0; run < 2; ++run) {
+    const int f = f0 + 32 * run + 8 * lg;  // first of 8 features
+    if (f >= g.n_out) continue;
+    const int which = f / HD;
+    const int h = (f - which * HD) / g.d;
+    const int fd = f - which * HD - h * g.d;
+    char* dst = (char*)(which == 0 ? qp : which == 1 ? kp : vp);
+    float bb[8];
+    if (bias) {
+      const float4 b0 = *(const float4*)(bias + f), b1 = *(const float4*)(bias + f + 4);
+      bb[0] = b0.x; bb[1] = b0.y; bb[2] = b0.z; bb[3] = b0.w;
+      bb[4] = b1.x; bb[5] = b1.y; bb[6] = b1.z; bb[7] = b1.w;
+    } else {
+#pragma unroll
+      for (int i = 0; i < 8; ++i) bb[i] = 0.f;
+    }
+#pragma unroll
+    for (int tt = 0; tt < 4; ++tt) {
+      const int m = t0 + tt * 16 + lr;
+      if (m < g.M) {
+        const int b = m / g.N, t = m - b * g.N;
+        const pj_floatx4 lo = acc[2 * run][tt], hi = acc[2 * run + 1][tt];
+        const uint4 v = make_uint4(pack2(lo[0] + bb[0], lo[1] + bb[1]), pack2(lo[2] + bb[2], lo[3] + bb[3]),
+                                   pack2(hi[0] + bb[4], hi[1] + bb[5]), pack2(hi[2] + bb[6], hi[3] + bb[7]));
+        __builtin_nontemporal_store(__builtin_bit_cast(pj_u32x4, v),
+                                    (pj_u32x4*)(dst + ((((size_t)b * g.H + h) * g.N + t) * g.d + fd) * 2));
+      }
+    }
+  }
+}
+
 __global__ __launch_bounds__(kPjThreads, 2) void sva_qkv_proj_kernel(
     const void* __restrict__ xp, const uint8_t* __restrict__ wpack, const float* __restrict__ bias,
     void* __restrict__ qp, void* __restrict__ kp, void* __restrict__ vp, ProjGeo g) {
@@ -272,39 +313,202 @@ __global__ __launch_bounds__(kPjThreads, 2) void sva_qkv_proj_kernel(
   }
   if (s < g.stages) step(s, w0, w1, x1);
 
-  // Epilogue: lane (lg, lr) holds, for token tile tt, features
-  // fb + 8 lg + 0..7 (accumulators 0, 1) and fb + 32 + 8 lg + 0..7 (2, 3).
-  const int HD = g.H * g.d;
+  store_qkv(acc, g, bias, qp, kp, vp, n0 + wn * 64, m0 + wm * 64, lg, lr);
+}
+
+// ---------------------------------------------------------------------------
+// W4A4: the activations in MXFP4 as well.
+//
+// The pages deploy the 4-bit projections through SVDQuant in NVFP4, which
+// puts both operands of the projection in 4 bits; gfx950's counterpart is
+// MXFP4 on the scaled MFMA (v_mfma_scale_f32_16x16x128_f8f6f4), four times
+// the bf16 rate.  sva_mxfp4_quant_kernel converts the activations once
+// (OCP MX conversion, per token row and 32 input channels); the GEMM then
+// reads 4-bit x straight from global memory in the MFMA's B layout (lane
+// (lg, lr): token lr, channels 32 lg .. 32 lg + 31 of the stage, 16 bytes)
+// with its E8M0 scale, and the packed weights exactly as the bf16 kernel
+// does: the packed layout is already the A layout of the scaled MFMA (lane
+// (lg, lr): row lr, channels 32 lg .. + 31), and the word of four scale
+// bytes per lane is its scale operand, the row tile picking the byte.  No
+// decode instructions and no LDS.
+// ---------------------------------------------------------------------------
+
+constexpr int kQuantThreads = 256;
+
+// One thread per 32-channel block of a token row.  The shared exponent
+// comes from the exponent field of the block's largest magnitude (bf16
+// magnitudes order as their bit patterns): floor(log2 amax) - 2, at least
+// -127 (scale byte 0, also for an all-zero block).  The elements go through
+// v_cvt_scalef32_pk_fp4_f32, which rounds x / scale to E2M1 (nearest, ties
+// to even, clamped at 6, the sign kept); measured on gfx950 to equal that
+// rule for every finite bf16 input at power-of-two scales.  Below scale
+// byte 64 both x and the scale are multiplied by 2^64 (exact), so that the
+// scale is a normal fp32 number.  Non-finite inputs are outside the
+// contract.
+__global__ __launch_bounds__(kQuantThreads) void sva_mxfp4_quant_kernel(const uint32_t* __restrict__ x,
+                                                                       uint8_t* __restrict__ codes,
+                                                                       uint8_t* __restrict__ scales,
+                                                                       long long nblk) {
+  const long long i = (long long)blockIdx.x * kQuantThreads + threadIdx.x;
+  if (i >= nblk) return;
+  const uint4* src = (const uint4*)(x + i * 16);  // 32 bf16, two a word, low half first
+  uint32_t w[16];
 #pragma unroll
-  for (int run = 0; run < 2; ++run) {
-    const int f = n0 + wn * 64 + 32 * run + 8 * lg;  // first of 8 features
-    if (f >= g.n_out) continue;
-    const int which = f / HD;
-    const int h = (f - which * HD) / g.d;
-    const int fd = f - which * HD - h * g.d;
-    char* dst = (char*)(which == 0 ? qp : which == 1 ? kp : vp);
-    float bb[8];
-    if (bias) {
-      const float4 b0 = *(const float4*)(bias + f), b1 = *(const float4*)(bias + f + 4);
-      bb[0] = b0.x; bb[1] = b0.y; bb[2] = b0.z; bb[3] = b0.w;
-      bb[4] = b1.x; bb[5] = b1.y; bb[6] = b1.z; bb[7] = b1.w;
-    } else {
+  for (int j = 0; j < 4; ++j) {
+    const uint4 v = src[j];
+    w[4 * j] = v.x; w[4 * j + 1] = v.y; w[4 * j + 2] = v.z; w[4 * j + 3] = v.w;
+  }
+  uint32_t amax = 0;
 #pragma unroll
-      for (int i = 0; i < 8; ++i) bb[i] = 0.f;
-    }
+  for (int j = 0; j < 16; ++j) amax = max(amax, max(w[j] & 0x7fffu, (w[j] >> 16) & 0x7fffu));
+  const uint32_t e = amax >> 7;  // the bf16 (and fp32) exponent field
+  const uint32_t code = e > 2 ? e - 2 : 0;
+  const bool pre = code < 64;
+  const float mul = pre ? 0x1p64f : 1.0f;
+  const float scale = __uint_as_float((code + (pre ? 64u : 0u)) << 23);
+  // channels 2j, 2j + 1 of input word j -> byte j % 4 of output word j / 4
+  auto lo = [&](int j) { return __uint_as_float(w[j] << 16) * mul; };
+  auto hi = [&](int j) { return __uint_as_float(w[j] & 0xffff0000u) * mul; };
+  uint32_t out[4];
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    uint32_t r = 0;
+    r = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(r, lo(4 * q), hi(4 * q), scale, 0);
+    r = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(r, lo(4 * q + 1), hi(4 * q + 1), scale, 1);
+    r = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(r, lo(4 * q + 2), hi(4 * q + 2), scale, 2);
+    r = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(r, lo(4 * q + 3), hi(4 * q + 3), scale, 3);
+    out[q] = r;
+  }
+  *(uint4*)(codes + i * 16) = make_uint4(out[0], out[1], out[2], out[3]);
+  scales[i] = (uint8_t)code;
+}
+
+typedef int pj_v8i __attribute__((ext_vector_type(8)));
+
+// acc += (A * 2^(sa byte RT)) (B * 2^(sb)) with A, B 16 x 128 and 128 x 16
+// fp4 (E2M1) tiles; RT picks the A scale's byte.
+template <int RT>
+__device__ __forceinline__ pj_floatx4 mfma_fp4(const uint4& a, uint32_t sa, const uint4& b, uint32_t sb,
+                                               pj_floatx4 c) {
+  const pj_v8i av = {(int)a.x, (int)a.y, (int)a.z, (int)a.w, 0, 0, 0, 0};
+  const pj_v8i bv = {(int)b.x, (int)b.y, (int)b.z, (int)b.w, 0, 0, 0, 0};
+  return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(av, bv, c, 4, 4, RT, (int)sa, 0, (int)sb);
+}
+
+// The workgroup's 64 x-rows of up to kXChunk channels live in LDS: codes at
+// a pitch of 32 16-byte pieces a row, piece p of row r at p ^ (r & 31) (the
+// B reads of one instruction -- 16 rows, 4 pieces each -- fall in distinct
+// bank groups), and one word of four scale bytes per row and stage.
+constexpr int kXChunk = 1024;                 // channels per LDS chunk
+constexpr int kXChunkStages = kXChunk / kTileK;
+constexpr int kXPitch = kXChunk / 32;         // 16-byte pieces per row
+
+__global__ __launch_bounds__(kPjThreads, 2) void sva_qkv_proj_w4a4_kernel(
+    const uint8_t* __restrict__ xq, const uint8_t* __restrict__ xsc, const uint8_t* __restrict__ wpack,
+    const float* __restrict__ bias, void* __restrict__ qp, void* __restrict__ kp, void* __restrict__ vp,
+    ProjGeo g) {
+  __shared__ uint4 xcs[kTileM * kXPitch];
+  __shared__ uint32_t xss[kTileM * kXChunkStages];
+
+  // Tile order as in the bf16 kernel: the feature tiles of one token tile on
+  // one XCD, whose L2 then serves its x.
+  const int xcd = blockIdx.x & 7;
+  const int local = blockIdx.x >> 3;
+  const int mt = (local / g.Nt) * 8 + xcd;
+  const int nt = local % g.Nt;
+  if (mt >= g.Mt) return;
+  const int m0 = mt * kTileM, n0 = nt * kTileN;
+
+  const int tid = threadIdx.x;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int lane = tid & 63;
+  const int lg = lane >> 4, lr = lane & 15;
+  const int wn = wave & 3;
+
+  // x rows m0 .. m0 + 63 (rows past M read as zero codes and zero scales)
+  const int rows = min(kTileM, g.M - m0);
+  const uint32_t crow = (uint32_t)g.C / 2, srow = (uint32_t)g.C / 32;
+  const __amdgpu_buffer_rsrc_t xr = rsrc(xq + (size_t)m0 * crow, (uint32_t)rows * crow);
+  const __amdgpu_buffer_rsrc_t sr = rsrc(xsc + (size_t)m0 * srow, (uint32_t)rows * srow);
+
+  const int blk = min(n0 / 64 + wn, g.n_out / 64 - 1);
+  const uint8_t* cbase = wpack + ((size_t)blk * g.stages * 4) * 1024 + lane * 16;
+  const uint8_t* sbase = wpack + (size_t)g.n_pack * (g.C / 2) + ((size_t)blk * g.stages * 64 + lane) * 4;
+
+  auto load_w = [&](WRegs& w, int s) {
+#pragma unroll
+    for (int rt = 0; rt < 4; ++rt) w.c[rt] = *(const uint4*)(cbase + ((size_t)s * 4 + rt) * 1024);
+    w.s = *(const uint32_t*)(sbase + (size_t)s * 256);
+  };
+
+  pj_floatx4 acc[4][4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) acc[i][j] = pj_floatx4{0.f, 0.f, 0.f, 0.f};
+
+  // One stage (128 channels) from chunk-local stage sl: B operands and
+  // scales from LDS, the weights from registers.
+  auto compute = [&](const WRegs& w, int sl) {
 #pragma unroll
     for (int tt = 0; tt < 4; ++tt) {
-      const int m = m0 + wm * 64 + tt * 16 + lr;
-      if (m < g.M) {
-        const int b = m / g.N, t = m - b * g.N;
-        const pj_floatx4 lo = acc[2 * run][tt], hi = acc[2 * run + 1][tt];
-        const uint4 v = make_uint4(pack2(lo[0] + bb[0], lo[1] + bb[1]), pack2(lo[2] + bb[2], lo[3] + bb[3]),
-                                   pack2(hi[0] + bb[4], hi[1] + bb[5]), pack2(hi[2] + bb[6], hi[3] + bb[7]));
-        __builtin_nontemporal_store(__builtin_bit_cast(pj_u32x4, v),
-                                    (pj_u32x4*)(dst + ((((size_t)b * g.H + h) * g.N + t) * g.d + fd) * 2));
-      }
+      const int r = tt * 16 + lr;
+      const uint4 b = xcs[r * kXPitch + ((4 * sl + lg) ^ (r & 31))];
+      const uint32_t sb = (xss[r * kXChunkStages + sl] >> (8 * lg)) & 0xffu;
+      acc[0][tt] = mfma_fp4<0>(w.c[0], w.s, b, sb, acc[0][tt]);
+      acc[1][tt] = mfma_fp4<1>(w.c[1], w.s, b, sb, acc[1][tt]);
+      acc[2][tt] = mfma_fp4<2>(w.c[2], w.s, b, sb, acc[2][tt]);
+      acc[3][tt] = mfma_fp4<3>(w.c[3], w.s, b, sb, acc[3][tt]);
+    }
+  };
+
+  // Weights: two register sets, stage s + 1 loading while stage s computes;
+  // every load is issued, the stage clamped to the last (repeat loads at the
+  // tail are in bounds and unused), so the count of loads in flight is exact.
+  const int last = g.stages - 1;
+  WRegs w0, w1;
+  load_w(w0, 0);
+  for (int s0 = 0; s0 < g.stages; s0 += kXChunkStages) {
+    const int ns = min(kXChunkStages, g.stages - s0);
+    // this chunk's x rows into LDS (every wave is past the previous chunk)
+    __syncthreads();
+    const uint32_t pieces = (uint32_t)ns * 4;  // 16-byte pieces a row in this chunk (4 a stage)
+#pragma unroll
+    for (int j = 0; j < kTileM * kXPitch / kPjThreads; ++j) {
+      const int u = tid + j * kPjThreads;
+      const int r = u / kXPitch, pc = u % kXPitch;
+      if ((uint32_t)pc < pieces)
+        xcs[r * kXPitch + (pc ^ (r & 31))] = __builtin_bit_cast(
+            uint4, __builtin_amdgcn_raw_buffer_load_b128(xr, (uint32_t)r * crow + 64 * s0 + 16 * pc, 0, 0));
+    }
+#pragma unroll
+    for (int j = 0; j < kTileM * kXChunkStages / kPjThreads; ++j) {
+      const int u = tid + j * kPjThreads;
+      const int r = u / kXChunkStages, sl = u % kXChunkStages;
+      if (sl < ns) xss[u] = __builtin_amdgcn_raw_buffer_load_b32(sr, (uint32_t)r * srow + 4 * (s0 + sl), 0, 0);
+    }
+    __syncthreads();
+    int sl = 0;
+    for (; sl + 2 <= ns; sl += 2) {
+      load_w(w1, min(s0 + sl + 1, last));
+      __builtin_amdgcn_sched_barrier(0);
+      compute(w0, sl);
+      __builtin_amdgcn_sched_barrier(0);
+      load_w(w0, min(s0 + sl + 2, last));
+      __builtin_amdgcn_sched_barrier(0);
+      compute(w1, sl + 1);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    if (sl < ns) {
+      load_w(w1, min(s0 + sl + 1, last));
+      __builtin_amdgcn_sched_barrier(0);
+      compute(w0, sl);
+      __builtin_amdgcn_sched_barrier(0);
+      w0 = w1;
     }
   }
+
+  store_qkv(acc, g, bias, qp, kp, vp, n0 + wn * 64, m0, lg, lr);
 }
 
 // ---------------------------------------------------------------------------
@@ -717,6 +921,12 @@ size_t packed_bytes(const sva_proj_desc& d) {
   return n_out * d.C / 2 + n_out * d.C / 32;
 }
 
+// 4-bit activations: codes [B N, C / 2] then scales [B N, C / 32].
+size_t acts_bytes(const sva_proj_desc& d) {
+  const size_t M = (size_t)d.B * d.N;
+  return M * d.C / 2 + M * d.C / 32;
+}
+
 }  // namespace
 
 extern "C" sva_status sva_mxfp4_pack_weights(const sva_proj_desc* desc, const void* codes, const void* scales,
@@ -830,4 +1040,74 @@ extern "C" sva_status sva_qkv_proj_mxfp4(const sva_proj_desc* desc, const void* 
                                          const float* bias, void* q, void* k, void* v, void* stream) {
   if (!desc) return SVA_ERR_INVALID_ARG;
   return sva_internal_proj_features(desc, x, wpack, bias, 3 * desc->H * desc->d, q, k, v, stream);
+}
+
+extern "C" sva_status sva_mxfp4_acts_bytes(const sva_proj_desc* desc, size_t* bytes) {
+  if (!bytes) return SVA_ERR_INVALID_ARG;
+  const sva_status st = check_desc(desc);
+  if (st != SVA_OK) return st;
+  *bytes = acts_bytes(*desc);
+  return SVA_OK;
+}
+
+extern "C" sva_status sva_mxfp4_quant_acts(const sva_proj_desc* desc, const void* x, void* xq, void* stream) {
+  const sva_status st = check_desc(desc);
+  if (st != SVA_OK) return st;
+  const sva_proj_desc& d = *desc;
+  if (!x || !xq || !aligned(x, 16) || !aligned(xq, 16)) return SVA_ERR_INVALID_ARG;
+  const long long M = (long long)d.B * d.N;
+  if (overlap(xq, acts_bytes(d), x, (size_t)M * d.C * 2)) return SVA_ERR_INVALID_ARG;
+  long long nblk = M * (d.C / 32);
+  const long long grid = (nblk + kQuantThreads - 1) / kQuantThreads;
+  if (grid >= (1LL << 31)) return SVA_ERR_UNSUPPORTED;
+  const uint32_t* xp = (const uint32_t*)x;
+  uint8_t* codes = (uint8_t*)xq;
+  uint8_t* scales = codes + (size_t)M * d.C / 2;
+  void* args[] = {(void*)&xp, (void*)&codes, (void*)&scales, (void*)&nblk};
+  if (hipLaunchKernel((const void*)&sva_mxfp4_quant_kernel, dim3((unsigned)grid), dim3(kQuantThreads), args, 0,
+                      (hipStream_t)stream) != hipSuccess)
+    return SVA_ERR_HIP;
+  return SVA_OK;
+}
+
+extern "C" sva_status sva_qkv_proj_w4a4(const sva_proj_desc* desc, const void* xq, const void* wpack,
+                                        const float* bias, void* q, void* k, void* v, void* stream) {
+  const sva_status st = check_desc(desc);
+  if (st != SVA_OK) return st;
+  const sva_proj_desc& d = *desc;
+  if (!xq || !wpack || !q || !k || !v) return SVA_ERR_INVALID_ARG;
+  if (!aligned(xq, 16) || !aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(wpack, 16) ||
+      (bias && !aligned(bias, 16)))
+    return SVA_ERR_INVALID_ARG;
+  const int n_pack = 3 * d.H * d.d;
+  const long long M = (long long)d.B * d.N;
+  const size_t ab = acts_bytes(d), ob = (size_t)M * d.H * d.d * 2, pb = packed_bytes(d);
+  const size_t bb = (size_t)n_pack * 4;
+  void* outs[3] = {q, k, v};
+  for (int i = 0; i < 3; ++i) {
+    if (overlap(outs[i], ob, xq, ab) || overlap(outs[i], ob, wpack, pb) || (bias && overlap(outs[i], ob, bias, bb)))
+      return SVA_ERR_INVALID_ARG;
+    for (int j = 0; j < i; ++j)
+      if (overlap(outs[i], ob, outs[j], ob)) return SVA_ERR_INVALID_ARG;
+  }
+  ProjGeo g;
+  g.M = (int)M;
+  g.N = d.N;
+  g.C = d.C;
+  g.H = d.H;
+  g.d = d.d;
+  g.n_out = n_pack;
+  g.n_pack = n_pack;
+  g.Mt = (int)((M + kTileM - 1) / kTileM);
+  g.Nt = (n_pack + kTileN - 1) / kTileN;
+  g.stages = d.C / kTileK;
+  const long long grid = ((long long)g.Mt + 7) / 8 * 8 * g.Nt;
+  const uint8_t* codes = (const uint8_t*)xq;
+  const uint8_t* scales = codes + (size_t)M * d.C / 2;
+  const uint8_t* wp = (const uint8_t*)wpack;
+  void* args[] = {(void*)&codes, (void*)&scales, (void*)&wp, (void*)&bias, (void*)&q, (void*)&k, (void*)&v, &g};
+  if (hipLaunchKernel((const void*)&sva_qkv_proj_w4a4_kernel, dim3((unsigned)grid), dim3(kPjThreads), args, 0,
+                      (hipStream_t)stream) != hipSuccess)
+    return SVA_ERR_HIP;
+  return SVA_OK;
 }

@@ -85,6 +85,9 @@ _SIG = {
     "sva_tconv_commit": (ctypes.c_int, [ctypes.POINTER(SvaTconvDesc)] + [_VP] * 3),
     "sva_mxfp4_pack_weights": (ctypes.c_int, [ctypes.POINTER(SvaProjDesc)] + [_VP] * 4),
     "sva_qkv_proj_mxfp4": (ctypes.c_int, [ctypes.POINTER(SvaProjDesc)] + [_VP] * 7),
+    "sva_mxfp4_acts_bytes": (ctypes.c_int, [ctypes.POINTER(SvaProjDesc), ctypes.POINTER(ctypes.c_size_t)]),
+    "sva_mxfp4_quant_acts": (ctypes.c_int, [ctypes.POINTER(SvaProjDesc)] + [_VP] * 3),
+    "sva_qkv_proj_w4a4": (ctypes.c_int, [ctypes.POINTER(SvaProjDesc)] + [_VP] * 7),
     "sva_proj_lin_attn_fwd_workspace": (ctypes.c_int, [ctypes.POINTER(SvaDesc), ctypes.POINTER(SvaProjDesc),
                                                         ctypes.POINTER(ctypes.c_size_t)]),
     "sva_proj_lin_attn_fwd": (ctypes.c_int, [ctypes.POINTER(SvaDesc), ctypes.POINTER(SvaProjDesc)] + [_VP] * 9
@@ -557,6 +560,66 @@ def sva_qkv_proj_mxfp4(x, wpack, bias, H: int, d: int, *, q=None, k=None, v=None
     st = lib().sva_qkv_proj_mxfp4(ctypes.byref(desc), _ptr(x), _ptr(wpack), _ptr(bias),
                                   _ptr(outs[0]), _ptr(outs[1]), _ptr(outs[2]), _stream(stream))
     _check(st, "sva_qkv_proj_mxfp4")
+    return tuple(outs)
+
+
+def mxfp4_acts_bytes(M: int, C: int) -> int:
+    """Bytes of M token rows of C channels in MXFP4: codes then scales."""
+    return M * C // 2 + M * C // 32
+
+
+def sva_mxfp4_quant_acts(x, *, out=None, stream=None):
+    """x [B, N, C] bf16 -> the MXFP4 activations (uint8 tensor of
+    mxfp4_acts_bytes(B N, C) bytes: codes [B N, C / 2], then scales
+    [B N, C / 32]) that sva_qkv_proj_w4a4 takes."""
+    import torch
+    _as_tensor("x", x)
+    if x.dim() != 3:
+        raise ValueError(f"x must be [B, N, C], got shape {tuple(x.shape)}")
+    _check_layout("x", x, None, torch.bfloat16)
+    B, N, C = x.shape
+    nbytes = mxfp4_acts_bytes(B * N, C)
+    if out is None:
+        out = torch.empty(nbytes, dtype=torch.uint8, device=x.device)
+    else:
+        _check_bytes("out", out)
+        if out.numel() * out.element_size() != nbytes:
+            raise ValueError(f"out holds {out.numel() * out.element_size()} bytes, expected {nbytes}")
+    _check_devices("x", x, [("out", out)])
+    desc = SvaProjDesc(B, N, C, 1, 64, 0)  # H, d do not enter the conversion
+    st = lib().sva_mxfp4_quant_acts(ctypes.byref(desc), _ptr(x), _ptr(out), _stream(stream))
+    _check(st, "sva_mxfp4_quant_acts")
+    return out
+
+
+def sva_qkv_proj_w4a4(xq, wpack, bias, B: int, N: int, C: int, H: int, d: int, *, q=None, k=None, v=None,
+                      stream=None):
+    """xq from sva_mxfp4_quant_acts of an x [B, N, C]; wpack from
+    sva_mxfp4_pack_weights; bias [3 H d] fp32 or None.  Returns (q, k, v),
+    each [B, H, N, d] bf16."""
+    import torch
+    _check_bytes("xq", xq)
+    if xq.numel() * xq.element_size() != mxfp4_acts_bytes(B * N, C):
+        raise ValueError(f"xq holds {xq.numel() * xq.element_size()} bytes, expected "
+                         f"{mxfp4_acts_bytes(B * N, C)} for {B * N} rows of C = {C}")
+    n_out = 3 * H * d
+    _check_bytes("wpack", wpack)
+    if wpack.numel() * wpack.element_size() != mxfp4_packed_bytes(n_out, C):
+        raise ValueError(f"wpack holds {wpack.numel() * wpack.element_size()} bytes, expected "
+                         f"{mxfp4_packed_bytes(n_out, C)} for {n_out} outputs of C = {C}")
+    if bias is not None:
+        _check_layout("bias", bias, (n_out,), torch.float32)
+    for name, t in (("q", q), ("k", k), ("v", v)):
+        if t is not None:
+            _check_layout(name, t, (B, H, N, d), torch.bfloat16)
+    _check_devices("xq", xq, [("wpack", wpack), ("bias", bias), ("q", q), ("k", k), ("v", v)])
+    desc = SvaProjDesc(B, N, C, H, d, 0)
+    outs = []
+    for t in (q, k, v):
+        outs.append(torch.empty((B, H, N, d), dtype=torch.bfloat16, device=xq.device) if t is None else t)
+    st = lib().sva_qkv_proj_w4a4(ctypes.byref(desc), _ptr(xq), _ptr(wpack), _ptr(bias),
+                                 _ptr(outs[0]), _ptr(outs[1]), _ptr(outs[2]), _stream(stream))
+    _check(st, "sva_qkv_proj_w4a4")
     return tuple(outs)
 
 

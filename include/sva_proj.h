@@ -10,8 +10,9 @@
  *   OCP Microscaling Formats (MX) Specification v1.0: the MXFP4 format used
  *          here (gfx950 implements the MX formats; NVFP4 is NVIDIA's).
  *
- * What is computed (readings: MXFP4 weights, bf16 activations, fp32
- * accumulation; output columns ordered [q | k | v] x H heads x d features):
+ * What is computed (readings: MXFP4 weights, bf16 activations -- or MXFP4
+ * activations, see sva_qkv_proj_w4a4 -- fp32 accumulation; output columns
+ * ordered [q | k | v] x H heads x d features):
  *   W[c][n]  = e2m1(code[n][c]) * 2^(scale[n][c / 32] - 127)
  *   y[m][n]  = sum_c x[m][c] W[c][n] + bias[n]        (m = b * N + token)
  *   q[b][h][t][f] = y[b*N + t][0*H*d + h*d + f], k: 1*H*d + ..., v: 2*H*d + ...
@@ -78,6 +79,39 @@ sva_status sva_mxfp4_pack_weights(const sva_proj_desc* desc, const void* codes, 
  * overlap. */
 sva_status sva_qkv_proj_mxfp4(const sva_proj_desc* desc, const void* x, const void* wpack, const float* bias,
                               void* q, void* k, void* v, void* stream);
+
+/* W4A4: the activations in MXFP4 as well.  SVDQuant's NVFP4 deployment
+ * ([news], 4-bit quantization and performance paragraphs) quantizes both
+ * operands of the projection to 4 bits; here the activations go through
+ * the OCP MX conversion (specification section 6.3), per token row and 32
+ * input channels:
+ *   E      = floor(log2(max |x_i|)) - 2, clamped to >= -127 (an all-zero
+ *            block: -127); scale byte E + 127
+ *   code_i = the E2M1 code nearest to x_i / 2^E, ties to the even code,
+ *            magnitudes above 6 clamped to 6, sign bit = x_i's (so values
+ *            that round to zero keep it)
+ * and the projection multiplies the 4-bit x by the 4-bit weights on the
+ * scaled MFMA (exact products, fp32 sums), then adds the bias and rounds to
+ * bf16 as sva_qkv_proj_mxfp4 does:
+ *   y[m][n] = sum_c X[m][c] W[c][n] + bias[n],  X = decode(codes_x, scales_x).
+ * x must be finite (a block holding an infinity or NaN gets unspecified
+ * codes); weight scale byte 255 (NaN) is outside the contract here.
+ *
+ * Quantized activations (xq): codes [B*N, C/2] (channels 2j low nibble,
+ * 2j+1 high nibble of byte j), then scales [B*N, C/32] (E8M0 bytes):
+ * sva_mxfp4_acts_bytes bytes, 16-byte aligned, caller-owned. */
+sva_status sva_mxfp4_acts_bytes(const sva_proj_desc* desc, size_t* bytes);
+
+/* xq = the MX conversion of x [B, N, C] bf16, as above.  xq must not overlap
+ * x.  Errors as for the projection. */
+sva_status sva_mxfp4_quant_acts(const sva_proj_desc* desc, const void* x, void* xq, void* stream);
+
+/* q, k, v = split(X W + bias) with X the 4-bit activations in xq (from
+ * sva_mxfp4_quant_acts with the same descriptor) and W packed by
+ * sva_mxfp4_pack_weights; layouts, limits and errors as for
+ * sva_qkv_proj_mxfp4. */
+sva_status sva_qkv_proj_w4a4(const sva_proj_desc* desc, const void* xq, const void* wpack, const float* bias,
+                             void* q, void* k, void* v, void* stream);
 
 /* Projection and attention in one pass over the tokens' k and v:
  *   out = sva_lin_attn_fwd(attn, q, k, v, ...) with (q, k, v) =
