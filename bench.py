@@ -673,7 +673,8 @@ def cpu_leg(w, reps: int):
 def _short_kernel(name: str) -> str:
     for k in ("sva_reduce_kernel", "sva_scan_kernel", "sva_apply_kernel", "sva_prep_kernel",
               "sva_bwd_out_kernel", "sva_bwd_kv_kernel", "sva_tconv_kernel", "sva_tconv_commit_kernel",
-              "sva_qkv_proj_kernel", "sva_mxfp4_pack_kernel"):
+              "sva_qkv_proj_kernel", "sva_mxfp4_pack_kernel", "sva_mxfp4_quant_kernel", "sva_qkv_proj_w4a4_kernel",
+              "sva_kv_proj_reduce_kernel"):
         if k in name:
             short = k.replace("sva_", "").replace("_kernel", "")
             if k == "sva_tconv_kernel" and "sva_tconv_commit_kernel" in name:
@@ -790,13 +791,26 @@ def summarize_profile(args):
         if "sva_" in kname:
             by_short[_short_kernel(kname)][cname] += vs
     traffic = {}
+
+    def add_traffic(key, fs, ws):
+        fk, wk = sum(fs) / len(fs), sum(ws) / len(ws)
+        traffic[key] = {"fetch_kib": fk, "write_kib": wk, "read_bytes": fk * 1024 * f_scale,
+                        "write_bytes": wk * 1024 * w_scale, "bytes": fk * 1024 * f_scale + wk * 1024 * w_scale}
+
     for k, cs in by_short.items():
         if not cs["FETCH_SIZE"] or not cs["WRITE_SIZE"]:
             continue
-        fk = sum(cs["FETCH_SIZE"]) / len(cs["FETCH_SIZE"])
-        wk = sum(cs["WRITE_SIZE"]) / len(cs["WRITE_SIZE"])
-        traffic[k] = {"fetch_kib": fk, "write_kib": wk, "read_bytes": fk * 1024 * f_scale,
-                      "write_bytes": wk * 1024 * w_scale, "bytes": fk * 1024 * f_scale + wk * 1024 * w_scale}
+        ws = cs["WRITE_SIZE"]
+        if len(ws) == len(cs["FETCH_SIZE"]) and max(ws) > 2 * min(ws) > 0:
+            # one kernel launched on two sizes (the fused leg's q-only and
+            # q, k, v projections): a row for each, split at the geometric mean
+            cut = (max(ws) * min(ws)) ** 0.5
+            lo = [i for i, w in enumerate(ws) if w < cut]
+            hi = [i for i, w in enumerate(ws) if w >= cut]
+            add_traffic(k + " (smaller launches)", [cs["FETCH_SIZE"][i] for i in lo], [ws[i] for i in lo])
+            add_traffic(k + " (larger launches)", [cs["FETCH_SIZE"][i] for i in hi], [ws[i] for i in hi])
+        else:
+            add_traffic(k, cs["FETCH_SIZE"], ws)
     name = ("tconv_" if args.tconv else "proj_" if args.proj else "") + args.workload
     src = TCONV_SRC if args.tconv else PROJ_SRC if args.proj else KERNEL_SRC
     doc = {"workload": name, "source_sha256": source_sha256(src),
@@ -808,8 +822,13 @@ def summarize_profile(args):
     if with_traffic:
         with open(traffic_file(name + args.label), "w") as f:
             json.dump(doc, f, indent=1)
-    what = ("causal temporal convolution" if args.tconv else "QKV projection with MXFP4 weights" if args.proj
-            else "backward" if args.label == "_bwd" else "denoising step and commit" if args.workload == "cached_step"
+    what = ("causal temporal convolution" if args.tconv
+            else "W4A4 QKV projection (MXFP4 activations and weights)" if args.proj and args.label == "_w4a4"
+            else "QKV projection with MXFP4 weights" if args.proj
+            else "backward" if args.label == "_bwd"
+            else "fused QKV projection (MXFP4 weights) + attention forward, and the two-call path"
+            if args.label == "_fused"
+            else "denoising step and commit" if args.workload == "cached_step"
             else "forward")
     lines = [f"# Kernel times and HBM traffic, {args.workload} workload, {what}", "",
              "Commands (run from the repository root on one MI355X):", ""]
@@ -847,6 +866,8 @@ def summarize_profile(args):
             lines.append(f"| {k} | {t['fetch_kib']:.0f} | {t['write_kib']:.0f} | {t['read_bytes'] / 1e6:.1f} | "
                          f"{t['write_bytes'] / 1e6:.1f} | {t['bytes'] / 1e6:.1f} |")
     lines += ["", f"Kernel source sha256: `{doc['source_sha256']}`", ""]
+    if args.label == "_fused":  # the fused path runs kernels of both sources
+        lines[-1:-1] = [f"Projection source sha256: `{source_sha256(PROJ_SRC)}`"]
     with open(os.path.join(PROFILES, f"sva_kernels_{name}{args.label}.md"), "w") as f:
         f.write("\n".join(lines))
     print(json.dumps({"summarized": name, "traffic": traffic, "back_to_back": runs}))
@@ -951,9 +972,17 @@ def main():
             "roofline": {"bound": "hbm", "kernel": "qkv_proj_w4a4", "achieved": gemm_gbs, "peak": HBM_PEAK_GBS,
                          "unit": "GB/s", "frac": gemm_gbs / HBM_PEAK_GBS, "traffic": None, "io_bytes": gemm_io},
             "kernels_us": {"quant_acts": q_ms * 1e3, "qkv_proj_w4a4": g_ms * 1e3},
+            "hbm_gbs_step": (quant_io + gemm_io) / (ms * 1e-3) / 1e9,
             "quant_hbm_frac": quant_io / (q_ms * 1e-3) / 1e9 / HBM_PEAK_GBS,
             "gemm_fp4_mfma_frac": flops / (g_ms * 1e-3) / 1e12 / MFMA_FP4_PEAK_TFLOPS,
         }
+        try:
+            with open(traffic_file(pw.name + "_w4a4")) as f:
+                prof = json.load(f)
+            if prof.get("source_sha256") == source_sha256(PROJ_SRC) and "qkv_proj_w4a4" in prof.get("per_launch", {}):
+                line["roofline"]["traffic"] = prof["per_launch"]["qkv_proj_w4a4"]["bytes"] / 1e9
+        except (OSError, ValueError):
+            pass
         print(json.dumps(line), flush=True)
         return
     if args.proj:
