@@ -65,6 +65,7 @@ struct ProjGeo {
   int n_pack;     // rows of the packed weights (3 * H * d)
   int Mt, Nt;     // token tiles, feature tiles
   int stages;     // C / kTileK
+  FastDiv fN, fHD, fd;  // division by N, H * d and d (the epilogue's indices)
 };
 
 struct KvGeo {
@@ -162,8 +163,8 @@ __device__ __forceinline__ void store_qkv(const pj_floatx4 (&acc)[4][4], const P
   for (int run = 0; run < 2; ++run) {
     const int f = f0 + 32 * run + 8 * lg;  // first of 8 features
     if (f >= g.n_out) continue;
-    const int which = f / HD;
-    const int h = (f - which * HD) / g.d;
+    const int which = (int)fdiv((uint32_t)f, g.fHD);
+    const int h = (int)fdiv((uint32_t)(f - which * HD), g.fd);
     const int fd = f - which * HD - h * g.d;
     char* dst = (char*)(which == 0 ? qp : which == 1 ? kp : vp);
     float bb[8];
@@ -179,7 +180,7 @@ __device__ __forceinline__ void store_qkv(const pj_floatx4 (&acc)[4][4], const P
     for (int tt = 0; tt < 4; ++tt) {
       const int m = t0 + tt * 16 + lr;
       if (m < g.M) {
-        const int b = m / g.N, t = m - b * g.N;
+        const int b = (int)fdiv((uint32_t)m, g.fN), t = m - b * g.N;
         const pj_floatx4 lo = acc[2 * run][tt], hi = acc[2 * run + 1][tt];
         const uint4 v = make_uint4(pack2(lo[0] + bb[0], lo[1] + bb[1]), pack2(lo[2] + bb[2], lo[3] + bb[3]),
                                    pack2(hi[0] + bb[4], hi[1] + bb[5]), pack2(hi[2] + bb[6], hi[3] + bb[7]));
@@ -990,6 +991,9 @@ sva_status sva_internal_proj_features(const sva_proj_desc* desc, const void* x, 
   g.Mt = (int)Mt;
   g.Nt = (int)Nt;
   g.stages = d.C / kTileK;
+  g.fN = make_fastdiv((uint32_t)d.N);
+  g.fHD = make_fastdiv((uint32_t)(d.H * d.d));
+  g.fd = make_fastdiv((uint32_t)d.d);
   const uint8_t* wp = (const uint8_t*)wpack;
   void* args[] = {(void*)&x, (void*)&wp, (void*)&bias, (void*)&q, (void*)&k, (void*)&v, &g};
   if (hipLaunchKernel((const void*)&sva_qkv_proj_kernel, dim3((unsigned)grid), dim3(kPjThreads), args, 0,
@@ -1101,6 +1105,9 @@ extern "C" sva_status sva_qkv_proj_w4a4(const sva_proj_desc* desc, const void* x
   g.Mt = (int)((M + kTileM - 1) / kTileM);
   g.Nt = (n_pack + kTileN - 1) / kTileN;
   g.stages = d.C / kTileK;
+  g.fN = make_fastdiv((uint32_t)d.N);
+  g.fHD = make_fastdiv((uint32_t)(d.H * d.d));
+  g.fd = make_fastdiv((uint32_t)d.d);
   const long long grid = ((long long)g.Mt + 7) / 8 * 8 * g.Nt;
   const uint8_t* codes = (const uint8_t*)xq;
   const uint8_t* scales = codes + (size_t)M * d.C / 2;
