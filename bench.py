@@ -491,12 +491,13 @@ def proj_w4a4_leg(w, steps: int, warmup: int, sets: int):
     return ms, _timed(stream, quant, steps), _timed(stream, gemm, steps)
 
 
-def fused_leg(w, aw, steps: int, warmup: int, sets: int):
+def fused_leg(w, aw, steps: int, warmup: int, sets: int, rounds: int = 5):
     """Projection + attention at the workload's token count, two ways, each
     timed over `steps` calls with `sets` input/output sets alternating:
       fused: sva_proj_lin_attn_fwd (k, v reduced inside the projection);
       two calls: sva_qkv_proj_mxfp4 then sva_lin_attn_fwd on the stored
-      q, k, v.  Returns (fused ms, two-call ms)."""
+      q, k, v.  Returns (fused ms, two-call ms), medians over `rounds`
+      alternating rounds."""
     import torch
     from block_causal_linear_phi_amd import sva
     from block_causal_linear_phi_amd import workloads as wl
@@ -534,19 +535,20 @@ def fused_leg(w, aw, steps: int, warmup: int, sets: int):
         sva.sva_qkv_proj_mxfp4(xs[i % sets], wp, bias, w.H, w.d, q=qkv[0], k=qkv[1], v=qkv[2], stream=stream)
         sva.sva_lin_attn_fwd(qkv[0], qkv[1], qkv[2], grid, aw.F, out=outs[i % sets], ws=aws, stream=stream, **kw)
 
-    res = []
+    # The two ways alternate over `rounds` rounds of `steps` calls each, and
+    # each reports its median round: the MFMA-heavy projection's speed drifts
+    # with the clocks over a run, and a fixed order would hand that drift to
+    # one of the two.
     for fn in (fused, two):
         for i in range(warmup):
             fn(i)
-        torch.cuda.synchronize()
-        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        a.record(stream)
-        for i in range(steps):
-            fn(i)
-        b.record(stream)
-        torch.cuda.synchronize()
-        res.append(a.elapsed_time(b) / steps)
-    return res[0], res[1]
+    torch.cuda.synchronize()
+    times = {fused: [], two: []}
+    for r in range(rounds):
+        for fn in ((fused, two) if r % 2 == 0 else (two, fused)):
+            times[fn].append(_timed(stream, fn, steps))
+    med = {fn: sorted(t)[len(t) // 2] for fn, t in times.items()}
+    return med[fused], med[two]
 
 
 def proj_cpu_leg(w, min_secs: float = 10.0, tokens: int = 1024):
@@ -642,6 +644,50 @@ def other_workloads(steps: int, warmup: int, sets: int):
                           "commit_us_graph": c["commit_graph_ms"] * 1e3,
                           "us_per_step_noalloc_graph": c["noalloc_graph_ms"] * 1e3,
                           "tokens_per_s": w.B * w.block_tokens / (c["apply_ms"] * 1e-3)}
+    return out
+
+
+def extension_rows(steps: int, warmup: int, sets: int):
+    """The rows beyond the forward, each timed in this process at the 720p
+    size (after the headline): the backward from saved states, the temporal
+    convolution, the QKV projection with bf16 and with MXFP4 activations,
+    projection + attention fused against two calls (720p and 480p), and
+    block-by-block generation.  Fewer steps than the headline: each row is a
+    mean over `steps` back-to-back calls after `warmup`."""
+    import torch
+    from block_causal_linear_phi_amd import workloads as wl
+
+    w720 = wl.WORKLOADS["720p"]
+    out = {}
+    ms, ms_re = bwd_leg(w720, steps, warmup, sets)
+    out["backward_720p"] = {"us_per_step": ms * 1e3, "tokens_per_s": w720.B * w720.N / (ms * 1e-3),
+                            "us_per_step_recomputing_states": ms_re * 1e3,
+                            "alg_bytes": 7 * w720.B * w720.H * w720.N * w720.d * 2}
+    torch.cuda.empty_cache()
+    tw = wl.TCONV_WORKLOADS["tconv_720p"]
+    t_ms, t_apply, t_commit = tconv_leg(tw, steps, warmup, sets, True)
+    tbytes = 2 * tw.B * tw.T * tw.Hs * tw.Ws * tw.C * (2 if tw.dtype == "bf16" else 4)
+    out["tconv_720p"] = {"us_per_step": t_ms * 1e3, "hbm_frac_step": tbytes / (t_ms * 1e-3) / (HBM_PEAK_GBS * 1e9),
+                         "block_apply_us": t_apply * 1e3, "block_commit_us": t_commit * 1e3}
+    torch.cuda.empty_cache()
+    pw = wl.PROJ_WORKLOADS["proj_720p"]
+    flops = 2.0 * pw.B * pw.N * pw.C * pw.n_out
+    p_ms = proj_leg(pw, steps, warmup, sets)
+    out["proj_w4a16_720p"] = {"us_per_step": p_ms * 1e3, "tflops": flops / (p_ms * 1e-3) / 1e12,
+                              "frac_of_bf16_peak": flops / (p_ms * 1e-3) / 1e12 / MFMA_BF16_PEAK_TFLOPS}
+    torch.cuda.empty_cache()
+    s_ms, q_ms, g_ms = proj_w4a4_leg(pw, steps, warmup, sets)
+    out["proj_w4a4_720p"] = {"us_per_step": s_ms * 1e3, "quant_acts_us": q_ms * 1e3, "gemm_us": g_ms * 1e3,
+                             "gemm_frac_of_fp4_peak": flops / (g_ms * 1e-3) / 1e12 / MFMA_FP4_PEAK_TFLOPS}
+    torch.cuda.empty_cache()
+    for name in ("720p", "480p"):
+        f_ms, two_ms = fused_leg(wl.PROJ_WORKLOADS["proj_" + name], wl.WORKLOADS[name], steps, warmup, sets)
+        out["fused_" + name] = {"us_per_step": f_ms * 1e3, "two_calls_us_per_step": two_ms * 1e3,
+                                "speedup_over_two_calls": two_ms / f_ms}
+        torch.cuda.empty_cache()
+    st_ms, sp_ms = stream_leg(w720, steps, warmup)
+    out["stream_720p"] = {"us_per_block": st_ms * 1e3 / w720.nb, "us_per_block_apply_then_commit": sp_ms * 1e3 / w720.nb}
+    torch.cuda.empty_cache()
     return out
 
 
@@ -1121,10 +1167,12 @@ def main():
     res = fb.run(args.steps, args.warmup, repeats=args.repeats, stage_calls=args.steps)
     fb.free()
     others = {}
+    ext = {}
     copy = None
     if not args.no_others and w.name == "720p":
         copy = copy_ceiling()
         others = other_workloads(args.steps, args.warmup, args.sets)
+        ext = extension_rows(min(args.steps, 20), min(args.warmup, 10), args.sets)
     ms_per_step = res["ms"]
     esz = 2 if w.dtype == "bf16" else 4
     elems = w.B * w.H * w.N * w.d
@@ -1182,6 +1230,9 @@ def main():
         line["hbm_frac_of_copy_ceiling"] = step_bytes / (ms_per_step * 1e-3) / 1e9 / copy["GB/s"]
     if others:
         line["other_workloads"] = others
+    if ext:
+        line["extension_rows"] = {k: {kk: (round(vv, 4) if isinstance(vv, float) else vv) for kk, vv in v.items()}
+                                  for k, v in ext.items()}
     if not args.no_cpu_baseline:
         line["cpu_baseline"] = cpu_leg(w, args.cpu_reps)
     print(json.dumps(line), flush=True)
