@@ -491,13 +491,15 @@ def proj_w4a4_leg(w, steps: int, warmup: int, sets: int):
     return ms, _timed(stream, quant, steps), _timed(stream, gemm, steps)
 
 
-def fused_leg(w, aw, steps: int, warmup: int, sets: int, rounds: int = 5):
+def fused_leg(w, aw, steps: int, warmup: int, sets: int, rounds: int = 5, w4a4: bool = False):
     """Projection + attention at the workload's token count, two ways, each
     timed over `steps` calls with `sets` input/output sets alternating:
       fused: sva_proj_lin_attn_fwd (k, v reduced inside the projection);
       two calls: sva_qkv_proj_mxfp4 then sva_lin_attn_fwd on the stored
-      q, k, v.  Returns (fused ms, two-call ms), medians over `rounds`
-      alternating rounds."""
+      q, k, v.  With w4a4 both ways take the activations through
+      sva_mxfp4_quant_acts first and use the 4-bit-activation calls
+      (sva_proj_lin_attn_fwd_w4a4; sva_qkv_proj_w4a4).  Returns (fused ms,
+      two-call ms), medians over `rounds` alternating rounds."""
     import torch
     from block_causal_linear_phi_amd import sva
     from block_causal_linear_phi_amd import workloads as wl
@@ -527,12 +529,23 @@ def fused_leg(w, aw, steps: int, warmup: int, sets: int, rounds: int = 5):
     aws = torch.zeros(sva.sva_lin_attn_fwd_workspace(fdesc), dtype=torch.uint8, device=dev)
     stream = torch.cuda.current_stream()
 
+    xq = torch.empty(sva.mxfp4_acts_bytes(w.B * w.N, w.C), dtype=torch.uint8, device=dev) if w4a4 else None
+
     def fused(i):
-        sva.sva_proj_lin_attn_fwd(xs[i % sets], wp, bias, w.H, grid, aw.F, out=outs[i % sets], ws=fws,
-                                  stream=stream, **kw)
+        if w4a4:
+            sva.sva_mxfp4_quant_acts(xs[i % sets], out=xq, stream=stream)
+            sva.sva_proj_lin_attn_fwd_w4a4(xq, wp, bias, w.B, w.C, w.H, grid, aw.F, out=outs[i % sets], ws=fws,
+                                           stream=stream, **kw)
+        else:
+            sva.sva_proj_lin_attn_fwd(xs[i % sets], wp, bias, w.H, grid, aw.F, out=outs[i % sets], ws=fws,
+                                      stream=stream, **kw)
 
     def two(i):
-        sva.sva_qkv_proj_mxfp4(xs[i % sets], wp, bias, w.H, w.d, q=qkv[0], k=qkv[1], v=qkv[2], stream=stream)
+        if w4a4:
+            sva.sva_mxfp4_quant_acts(xs[i % sets], out=xq, stream=stream)
+            sva.sva_qkv_proj_w4a4(xq, wp, bias, w.B, w.N, w.C, w.H, w.d, q=qkv[0], k=qkv[1], v=qkv[2], stream=stream)
+        else:
+            sva.sva_qkv_proj_mxfp4(xs[i % sets], wp, bias, w.H, w.d, q=qkv[0], k=qkv[1], v=qkv[2], stream=stream)
         sva.sva_lin_attn_fwd(qkv[0], qkv[1], qkv[2], grid, aw.F, out=outs[i % sets], ws=aws, stream=stream, **kw)
 
     # The two ways alternate over `rounds` rounds of `steps` calls each, and
@@ -651,7 +664,8 @@ def extension_rows(steps: int, warmup: int, sets: int):
     """The rows beyond the forward, each timed in this process at the 720p
     size (after the headline): the backward from saved states, the temporal
     convolution, the QKV projection with bf16 and with MXFP4 activations,
-    projection + attention fused against two calls (720p and 480p), and
+    projection + attention fused against two calls (720p and 480p; bf16
+    and MXFP4 activations), and
     block-by-block generation.  Fewer steps than the headline: each row is a
     mean over `steps` back-to-back calls after `warmup`."""
     import torch
@@ -680,11 +694,14 @@ def extension_rows(steps: int, warmup: int, sets: int):
     out["proj_w4a4_720p"] = {"us_per_step": s_ms * 1e3, "quant_acts_us": q_ms * 1e3, "gemm_us": g_ms * 1e3,
                              "gemm_frac_of_fp4_peak": flops / (g_ms * 1e-3) / 1e12 / MFMA_FP4_PEAK_TFLOPS}
     torch.cuda.empty_cache()
-    for name in ("720p", "480p"):
-        f_ms, two_ms = fused_leg(wl.PROJ_WORKLOADS["proj_" + name], wl.WORKLOADS[name], steps, warmup, sets)
-        out["fused_" + name] = {"us_per_step": f_ms * 1e3, "two_calls_us_per_step": two_ms * 1e3,
-                                "speedup_over_two_calls": two_ms / f_ms}
-        torch.cuda.empty_cache()
+    for w4a4 in (False, True):
+        for name in ("720p", "480p"):
+            f_ms, two_ms = fused_leg(wl.PROJ_WORKLOADS["proj_" + name], wl.WORKLOADS[name], steps, warmup, sets,
+                                     w4a4=w4a4)
+            out[("fused_w4a4_" if w4a4 else "fused_") + name] = {
+                "us_per_step": f_ms * 1e3, "two_calls_us_per_step": two_ms * 1e3,
+                "speedup_over_two_calls": two_ms / f_ms}
+            torch.cuda.empty_cache()
     st_ms, sp_ms = stream_leg(w720, steps, warmup)
     out["stream_720p"] = {"us_per_block": st_ms * 1e3 / w720.nb, "us_per_block_apply_then_commit": sp_ms * 1e3 / w720.nb}
     torch.cuda.empty_cache()
@@ -720,7 +737,7 @@ def _short_kernel(name: str) -> str:
     for k in ("sva_reduce_kernel", "sva_scan_kernel", "sva_apply_kernel", "sva_prep_kernel",
               "sva_bwd_out_kernel", "sva_bwd_kv_kernel", "sva_tconv_kernel", "sva_tconv_commit_kernel",
               "sva_qkv_proj_kernel", "sva_mxfp4_pack_kernel", "sva_mxfp4_quant_kernel", "sva_qkv_proj_w4a4_kernel",
-              "sva_kv_proj_reduce_kernel"):
+              "sva_kv_proj_reduce_kernel", "sva_kv_proj_reduce_w4a4_kernel"):
         if k in name:
             short = k.replace("sva_", "").replace("_kernel", "")
             if k == "sva_tconv_kernel" and "sva_tconv_commit_kernel" in name:
@@ -874,6 +891,8 @@ def summarize_profile(args):
             else "backward" if args.label == "_bwd"
             else "fused QKV projection (MXFP4 weights) + attention forward, and the two-call path"
             if args.label == "_fused"
+            else "fused QKV projection (MXFP4 weights and activations) + attention forward, and the two-call path"
+            if args.label == "_fused_w4a4"
             else "denoising step and commit" if args.workload == "cached_step"
             else "forward")
     lines = [f"# Kernel times and HBM traffic, {args.workload} workload, {what}", "",
@@ -912,7 +931,7 @@ def summarize_profile(args):
             lines.append(f"| {k} | {t['fetch_kib']:.0f} | {t['write_kib']:.0f} | {t['read_bytes'] / 1e6:.1f} | "
                          f"{t['write_bytes'] / 1e6:.1f} | {t['bytes'] / 1e6:.1f} |")
     lines += ["", f"Kernel source sha256: `{doc['source_sha256']}`", ""]
-    if args.label == "_fused":  # the fused path runs kernels of both sources
+    if args.label in ("_fused", "_fused_w4a4"):  # the fused path runs kernels of both sources
         lines[-1:-1] = [f"Projection source sha256: `{source_sha256(PROJ_SRC)}`"]
     with open(os.path.join(PROFILES, f"sva_kernels_{name}{args.label}.md"), "w") as f:
         f.write("\n".join(lines))
@@ -937,6 +956,8 @@ def main():
                     help="time the causal temporal convolution of the Mix-FFN on the workload's grid instead")
     ap.add_argument("--fused", action="store_true",
                     help="projection + attention: the fused entry point against the two calls")
+    ap.add_argument("--w4a4", action="store_true",
+                    help="with --fused: MXFP4 activations (conversion + the W4A4 calls) in both ways")
     ap.add_argument("--proj", action="store_true",
                     help="time the QKV projection with MXFP4 weights on the workload's tokens instead")
     ap.add_argument("--stream", action="store_true",
@@ -978,10 +999,11 @@ def main():
     if args.fused:
         pw = wl.PROJ_WORKLOADS["proj_" + args.workload]
         aw = wl.WORKLOADS[args.workload]
-        ms, ms_two = fused_leg(pw, aw, args.steps, args.warmup, args.sets)
+        ms, ms_two = fused_leg(pw, aw, args.steps, args.warmup, args.sets, w4a4=args.w4a4)
         flops = 2.0 * pw.B * pw.N * pw.C * pw.n_out
+        acts = "MXFP4 weights and activations, conversion included" if args.w4a4 else "MXFP4 weights"
         print(json.dumps({
-            "metric": "tokens/s of the QKV projection (MXFP4 weights) and block-causal attention forward, fused",
+            "metric": f"tokens/s of the QKV projection ({acts}) and block-causal attention forward, fused",
             "value": pw.B * pw.N / (ms * 1e-3), "unit": "tokens/s", "n_gpus": 1, "steps": args.steps,
             "warmup": args.warmup, "ms_per_step": ms, "higher_is_better": True, "scaling": "weak",
             "vs_baseline": None, "dtype": "bf16",

@@ -12,6 +12,6 @@ from .sva import (  # noqa: F401
     sva_lin_attn_fwd_save, sva_lin_attn_fwd_workspace, sva_lin_attn_states_bytes, sva_phi_rope_prep,
     SvaTconvDesc, make_tconv_desc, sva_tconv_apply, sva_tconv_commit, sva_tconv_fwd,
     SvaProjDesc, sva_qkv_proj_mxfp4, sva_mxfp4_pack_weights, mxfp4_packed_bytes, sva_proj_lin_attn_fwd,
-    mxfp4_acts_bytes, sva_mxfp4_quant_acts, sva_qkv_proj_w4a4,
+    mxfp4_acts_bytes, sva_mxfp4_quant_acts, sva_qkv_proj_w4a4, sva_proj_lin_attn_fwd_w4a4,
 )
 from .autograd import BlockCausalLinearAttention, block_causal_linear_attention  # noqa: F401

@@ -49,9 +49,17 @@ struct SvaKvReduceArgs {
 hipError_t sva_internal_kv_proj_reduce(const SvaKvReduceArgs& a, const void* x, const void* wpack,
                                        const float* bias, float* partials, hipStream_t stream);
 
+// The same from the 4-bit activations xq (sva_mxfp4_quant_acts' layout).
+hipError_t sva_internal_kv_proj_reduce_w4a4(const SvaKvReduceArgs& a, const void* xq, const void* wpack,
+                                            const float* bias, float* partials, hipStream_t stream);
+
 // sva_qkv_proj_mxfp4 restricted to output features [0, f_end) (q alone:
 // f_end = H * d); validation as for the full projection.
 sva_status sva_internal_proj_features(const sva_proj_desc* desc, const void* x, const void* wpack,
                                       const float* bias, int f_end, void* q, void* k, void* v, void* stream);
+
+// sva_qkv_proj_w4a4 restricted to output features [0, f_end).
+sva_status sva_internal_proj_w4a4_features(const sva_proj_desc* desc, const void* xq, const void* wpack,
+                                           const float* bias, int f_end, void* q, void* k, void* v, void* stream);
 
 #endif  // SVA_INTERNAL_H

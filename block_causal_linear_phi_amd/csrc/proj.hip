@@ -145,6 +145,14 @@ struct KvWRegs {
   uint32_t sk, sv;
 };
 
+// Workgroup barrier for LDS only: waits for this wave's LDS accesses
+// (lgkmcnt(0); 0xC07F leaves vmcnt and expcnt at their maxima), so global
+// loads in flight stay in flight across it.
+__device__ __forceinline__ void lds_sync() {
+  __builtin_amdgcn_s_waitcnt(0xC07F);
+  __builtin_amdgcn_s_barrier();
+}
+
 __device__ __forceinline__ uint32_t pack2(float a, float b) {
   const pj_bf16x2 v = {(__bf16)a, (__bf16)b};  // round to nearest even
   return __builtin_bit_cast(uint32_t, v);
@@ -520,28 +528,238 @@ __global__ __launch_bounds__(kPjThreads, 2) void sva_qkv_proj_w4a4_kernel(
 // waves compute k and v of those heads (64 features each) for 64-token
 // tiles with the projection's GEMM.  Instead of storing k and v, each tile's
 // epilogue rounds them to bf16 (as a stored tensor would be), applies phi
-// and the numerator-only 3D RoPE to k, stages both transposed in LDS and
-// adds the tile's v^T RoPE(phi k) to the head's state on MFMA, and phi k to
-// its normaliser.  At the end of the range each head's state and normaliser
-// go to the partial slot the block scan reads for (range, block): slot g + bhc
-// with g the range's index along the flattened (b, h, token) axis in units
-// of L.  So k and v never reach HBM.
+// and the numerator-only 3D RoPE to k, stages both in LDS and adds the
+// tile's v^T RoPE(phi k) to the head's state on MFMA (operands read with
+// LDS transpose reads), and phi k to its normaliser.  At the end of the
+// range each head's state and normaliser go to the partial slot the block
+// scan reads for (range, block): slot g + bhc with g the range's index along
+// the flattened (b, h, token) axis in units of L.  So k and v never reach
+// HBM.
 //
 // The GEMM pipeline runs on across the tiles of a range (the next tile's
-// first x and weight stages load during the epilogue), the bias sits in LDS,
-// and RoPE reads cos/sin from a per-workgroup LDS table of the positions the
-// range can hold (kTab), or computes them on the fly for grids whose table
-// would not fit beside two workgroups per CU.
+// first x and weight stages load during the epilogue), the accumulators
+// start from the bias, and RoPE reads cos/sin from a per-workgroup LDS
+// table of the positions the range can hold, or computes them on the fly
+// for grids whose table would not fit beside two workgroups per CU.
 // ---------------------------------------------------------------------------
 
 constexpr int kKvThreads = 256;  // waves: (h0, half 0), (h0, half 1), (h0+1, 0), (h0+1, 1)
 static_assert(kKvThreads == kPjThreads, "the GEMM part assumes the projection's workgroup size");
 
-// A wave's 64 x 64 bf16 tile, transposed: feature row f (128 bytes = 64
-// tokens), 16-byte piece p = token / 8 at p ^ (f & 7).
-__device__ __forceinline__ int kv_piece(int f, int p) { return f * 8 + (p ^ (f & 7)); }
+// Pieces shared by the fused k, v kernels (bf16 and 4-bit activations):
+// both GEMMs leave a wave's 64 features x 64 tokens in the same accumulator
+// layout, so the epilogue, the state update and the partial are common.
 
-template <bool kTab>
+// The LDS RoPE table of block c (see kRopeTab): cos, sin of pos *
+// base^(-2i/width) turns, the angle in fp64 reduced to [-1/2, 1/2] turn,
+// then the hardware sine and cosine (which take turns).
+__device__ __forceinline__ void kv_build_rope_table(float2* rtab, const KvGeo& g, int c, int tid) {
+  const int ht = g.dt >> 1, hh = g.dh >> 1, hwd = (64 - g.dt - g.dh) >> 1;
+  const int off_h = g.F * ht, off_w = off_h + g.Hs * hh;
+  for (int e = tid; e < g.tab_entries; e += kKvThreads) {
+    int pos, i, width;
+    if (e < off_h) {
+      pos = g.t0 + c * g.F + e / ht, i = e % ht, width = g.dt;
+    } else if (e < off_w) {
+      pos = (e - off_h) / hh, i = (e - off_h) % hh, width = g.dh;
+    } else {
+      pos = (e - off_w) / hwd, i = (e - off_w) % hwd, width = 64 - g.dt - g.dh;
+    }
+    double rv = (double)pos * exp2(-(double)(2 * i) / (double)width * g.log2_base_d) * 0.15915494309189535;
+    rv -= rint(rv);
+    rtab[e] = make_float2(__builtin_amdgcn_cosf((float)rv), __builtin_amdgcn_sinf((float)rv));
+  }
+}
+
+// Epilogue of one 64-token tile (tokens n0 ..) of the range [.., n_end) of
+// block c.  Lane (lg, lr) holds features 32 half + 8 lg + 0..7 of the head's
+// k (accumulators 0, 1) and v (2, 3) for token 16 tt + lr, bias included
+// (the accumulators start from it).  Values are rounded to bf16 as the
+// stored tensors would be; k then gets phi (its normaliser share goes to the
+// lane's zt, which kv_z_reduce sums at the end) and the rotation of its
+// position, and is rounded to bf16 again.  Only v is zeroed past the range
+// (its zero rows keep those tokens out of S; the normaliser masks k
+// itself), and only in a ragged tile (kFull false).
+// The head's k and v tiles go to LDS row-major, for kv_state_mfma_tr after
+// a barrier: row = token, 128 bytes of 64 bf16 features, 16-byte piece p of
+// row t at p ^ (t & 7); a lane's 8 features of one token are one piece, so
+// a token tile takes two 16-byte writes a lane.  lgv is lg, through an
+// empty asm where registers are short: the compiler would otherwise hoist
+// the RoPE constants out of the tile loop, and they would occupy registers
+// through the GEMM.  RoPE: kRope 0 takes the cos/sin table with the lane's
+// 4 pairs on one axis (every axis width a multiple of 8: the pairs' entries
+// are consecutive), 1 the table pair by pair, 2 computes the angles.
+__device__ __forceinline__ int kv_rm_off(int t, int p) { return t * 128 + ((p ^ (t & 7)) << 4); }
+
+template <int kRope, bool kFull>
+__device__ __forceinline__ void kv_tile_epilogue_rm(const pj_floatx4 (&acc)[4][4], const KvGeo& g,
+                                                    const float2* rtab, uint4* kvt, float (&zt)[8], int wave,
+                                                    int half, int lg, int lgv, int lr, int n0, int n_end, int c) {
+  const int off_h = g.F * (g.dt >> 1), off_w = off_h + g.Hs * (g.dh >> 1);
+  float inv[4], tbase[4];
+  int axis[4], eoff[4], estr[4];
+#pragma unroll
+  for (int pp = 0; pp < 4; ++pp) {
+    const int f = 32 * half + 8 * lgv + 2 * pp;
+    const int ax = f < g.dt ? 0 : f < g.dt + g.dh ? 1 : 2;
+    const int start = ax == 0 ? 0 : ax == 1 ? g.dt : g.dt + g.dh;
+    const int width = ax == 0 ? g.dt : ax == 1 ? g.dh : 64 - g.dt - g.dh;
+    axis[pp] = ax;
+    if constexpr (kRope < 2) {
+      eoff[pp] = (ax == 0 ? 0 : ax == 1 ? off_h : off_w) + ((f - start) >> 1);
+      estr[pp] = width >> 1;
+    } else {
+      const double inv_d = exp2(-(double)(f - start) / (double)width * g.log2_base_d) * 0.15915494309189535;
+      double tb = ax == 0 ? (double)(g.t0 + c * g.F) * inv_d : 0.0;
+      tb -= rint(tb);
+      inv[pp] = (float)inv_d;
+      tbase[pp] = (float)tb;
+    }
+  }
+  char* const ktile = reinterpret_cast<char*>(kvt + (wave & 2) * 512);
+  char* const vtile = reinterpret_cast<char*>(kvt + ((wave & 2) + 1) * 512);
+  const int piece = 4 * half + lg;
+#pragma unroll
+  for (int tt = 0; tt < 4; ++tt) {
+    const int tok = 16 * tt + lr;
+    const int n = n0 + tok;
+    const bool valid = kFull || n < n_end;
+    // element i of the lane's 8 features: accumulator 2 run + i / 4, entry i % 4
+    uint4 vw = make_uint4(pack2(acc[2][tt][0], acc[2][tt][1]), pack2(acc[2][tt][2], acc[2][tt][3]),
+                          pack2(acc[3][tt][0], acc[3][tt][1]), pack2(acc[3][tt][2], acc[3][tt][3]));
+    if (!kFull && !valid) vw = make_uint4(0u, 0u, 0u, 0u);
+    float kv8[8];
+#pragma unroll
+    for (int m = 0; m < 4; ++m) {
+      const uint32_t w = pack2(acc[m >> 1][tt][2 * (m & 1)], acc[m >> 1][tt][2 * (m & 1) + 1]);
+      // phi on the bit pattern, as in the attention kernels: every value
+      // with the sign bit set (negative numbers, -0, a negative-signed NaN)
+      // becomes +0, every other value passes unchanged
+      kv8[2 * m] = __int_as_float(max((int)(w << 16), 0));
+      kv8[2 * m + 1] = __int_as_float(max((int)(w & 0xffff0000u), 0));
+    }
+#pragma unroll
+    for (int i = 0; i < 8; ++i) zt[i] += valid ? kv8[i] : 0.f;
+    if (g.rope) {
+      const uint32_t np = (uint32_t)(valid ? n : n_end - 1);  // positions past the range: any in it
+      const uint32_t fr = fdiv(np, g.fHW), rem = np - fr * g.fHW.div;
+      const uint32_t row = fdiv(rem, g.fWs);
+      const int pt = (int)fr - c * g.F;  // the frame within the block
+      const int ph = (int)row, pw = (int)(rem - row * g.fWs.div);
+      const int ps0 = axis[0] == 0 ? pt : axis[0] == 1 ? ph : pw;
+      const int e0 = eoff[0] + ps0 * estr[0];
+#pragma unroll
+      for (int pp = 0; pp < 4; ++pp) {
+        float sn, cs;
+        if constexpr (kRope == 0) {
+          const float2 e = rtab[e0 + pp];
+          cs = e.x, sn = e.y;
+        } else if constexpr (kRope == 1) {
+          const int ax = axis[pp];
+          const int ps = ax == 0 ? pt : ax == 1 ? ph : pw;
+          const float2 e = rtab[eoff[pp] + ps * estr[pp]];
+          cs = e.x, sn = e.y;
+        } else {
+          const int ax = axis[pp];
+          const int ps = ax == 0 ? pt : ax == 1 ? ph : pw;
+          const float turn = __builtin_amdgcn_fractf(tbase[pp] + (float)ps * inv[pp]);
+          sn = __builtin_amdgcn_sinf(turn), cs = __builtin_amdgcn_cosf(turn);
+        }
+        const float x = kv8[2 * pp], y = kv8[2 * pp + 1];
+        kv8[2 * pp] = x * cs - y * sn;
+        kv8[2 * pp + 1] = x * sn + y * cs;
+      }
+    }
+    const uint4 kw = make_uint4(pack2(kv8[0], kv8[1]), pack2(kv8[2], kv8[3]), pack2(kv8[4], kv8[5]),
+                                pack2(kv8[6], kv8[7]));
+    *reinterpret_cast<uint4*>(ktile + kv_rm_off(tok, piece)) = kw;
+    *reinterpret_cast<uint4*>(vtile + kv_rm_off(tok, piece)) = vw;
+  }
+}
+
+// The lanes' normaliser shares summed over the 16 token lanes: features
+// 32 half + 8 lg + i of the head, into zhead (one wave per half writes).
+__device__ __forceinline__ void kv_z_reduce(const float (&zt)[8], float* zhead, int half, int lg, int lr) {
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    float t = zt[i];
+    t += __shfl_xor(t, 1);
+    t += __shfl_xor(t, 2);
+    t += __shfl_xor(t, 4);
+    t += __shfl_xor(t, 8);
+    if (lr == 0) zhead[32 * half + 8 * lg + i] = t;
+  }
+}
+
+typedef short pj_i16x4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) pj_i16x4* lds_i16x4_ptr;
+
+// State rows (value features) 32 half .. + 31 of the wave's head, from the
+// tiles kv_tile_epilogue_rm wrote: S^T[fo][fi] += sum over the tile's tokens
+// of v[fo] RoPE(phi k)[fi]; sa[ft][fc] element i of lane (lg, lr) is row
+// 16 (2 half + ft) + 4 lg + i, column 16 fc + lr.  The operands come with
+// LDS transpose reads (ds_read_b64_tr_b16): within each 16-lane group,
+// output lane i's element m
+// is element i % 4 of the 8 bytes input lane 4 m + i / 4 points at.  So
+// input lane j pointing at row tb + j / 4, features f0 + 4 (j % 4) .. + 3
+// hands output lane i feature f0 + i of rows tb .. tb + 3: the 4 token
+// slots of an MFMA operand, for the feature the lane's operand row needs.
+__device__ __forceinline__ void kv_state_mfma_tr(pj_floatx4 (&sa)[2][4], const uint4* kvt, int wave, int half,
+                                                 int lane) {
+  const char* const vt = reinterpret_cast<const char*>(kvt + ((wave & 2) + 1) * 512);
+  const char* const kt = reinterpret_cast<const char*>(kvt + (wave & 2) * 512);
+  const int grp = lane >> 4, j = lane & 15;
+  auto rd = [&](const char* tile, int tb, int f0) {
+    const int row = tb + (j >> 2);
+    const int f = f0 + 4 * (j & 3);
+    const int off = row * 128 + (((f >> 3) ^ (row & 7)) << 4) + (f & 7) * 2;
+    return __builtin_bit_cast(uint2, __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4_ptr)(tile + off)));
+  };
+#pragma unroll
+  for (int ks = 0; ks < 2; ++ks) {
+    const int tb = 32 * ks + 8 * grp;  // the lane group's 8 tokens of this k-step
+    uint4 a[2], bo[4];
+#pragma unroll
+    for (int ft = 0; ft < 2; ++ft) {
+      const uint2 lo = rd(vt, tb, 32 * half + 16 * ft), hi = rd(vt, tb + 4, 32 * half + 16 * ft);
+      a[ft] = make_uint4(lo.x, lo.y, hi.x, hi.y);
+    }
+#pragma unroll
+    for (int fc = 0; fc < 4; ++fc) {
+      const uint2 lo = rd(kt, tb, 16 * fc), hi = rd(kt, tb + 4, 16 * fc);
+      bo[fc] = make_uint4(lo.x, lo.y, hi.x, hi.y);
+    }
+#pragma unroll
+    for (int ft = 0; ft < 2; ++ft)
+#pragma unroll
+      for (int fc = 0; fc < 4; ++fc) sa[ft][fc] = mfma(a[ft], bo[fc], sa[ft][fc]);
+  }
+}
+
+// The wave's share of the partial of (range r of sample b, block c) for
+// head `head`: S^T rows 32 half .. + 31 (row fo, column fi), and from the
+// waves of half 0 the head's z.  The partial sits at slot gv + bhc, with gv
+// the range's index along the flattened (b, h, token) axis in units of L.
+__device__ __forceinline__ void kv_store_partial(const pj_floatx4 (&sa)[2][4], const float* zhead,
+                                                 float* __restrict__ partials, const KvGeo& g, int b, int head,
+                                                 int r, int c, int half, int lg, int lr, int lane) {
+  const long long bh = (long long)b * g.H + head;
+  const long long gv = bh * g.ranges + r;
+  const long long bhc = bh * g.nb + c;
+  float* dst = partials + (gv + bhc) * (64 * 64 + 64);
+#pragma unroll
+  for (int ft = 0; ft < 2; ++ft)
+#pragma unroll
+    for (int fc = 0; fc < 4; ++fc) {
+      const pj_floatx4 v4 = sa[ft][fc];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) dst[(16 * (2 * half + ft) + 4 * lg + i) * 64 + 16 * fc + lr] = v4[i];
+    }
+  if (half == 0) dst[64 * 64 + lane] = zhead[lane];
+}
+
+// kRope: as for kv_tile_epilogue_rm (0, 1: the LDS table; 2: on the fly).
+template <int kRope>
 __global__ __launch_bounds__(kKvThreads, 2) void sva_kv_proj_reduce_kernel(
     const void* __restrict__ xp, const uint8_t* __restrict__ wpack, const float* __restrict__ bias,
     float* __restrict__ partials, KvGeo g) {
@@ -552,7 +770,7 @@ __global__ __launch_bounds__(kKvThreads, 2) void sva_kv_proj_reduce_kernel(
   __shared__ pj_floatx4 sacc[kKvThreads / 64][8][64];
   __shared__ float zs[2][64];
   __shared__ float bs[kKvThreads / 64][64];
-  __shared__ float2 rtab[kTab ? kRopeTab : 1];
+  __shared__ float2 rtab[kRope < 2 ? kRopeTab : 1];
   static_assert(sizeof(xs) == (kKvThreads / 64) * 64 * 8 * sizeof(uint4), "tiles alias the x stages");
   uint4* const kvt = &xs[0][0];  // wave w's tile at kvt + w * 512
 
@@ -587,28 +805,11 @@ __global__ __launch_bounds__(kKvThreads, 2) void sva_kv_proj_reduce_kernel(
 
 #pragma unroll
   for (int k = 0; k < 8; ++k) sacc[wave][k][lane] = pj_floatx4{0.f, 0.f, 0.f, 0.f};
-  if (tid < 128) zs[tid >> 6][tid & 63] = 0.f;
+  float zt[8];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) zt[i] = 0.f;
   bs[wave][lane] = bias ? bias[(lane < 32 ? blk_k : blk_v) * 64 + 32 * half + (lane & 31)] : 0.f;
-  const int ht = g.dt >> 1, hh = g.dh >> 1, hwd = (64 - g.dt - g.dh) >> 1;
-  const int off_h = g.F * ht, off_w = off_h + g.Hs * hh;
-  if constexpr (kTab) {
-    // cos, sin of pos * base^(-2i/width) turns: the angle in fp64, reduced
-    // to [-1/2, 1/2] turn, then the hardware sine and cosine (which take
-    // turns); read by the tile loop after its first barrier.
-    for (int e = tid; e < g.tab_entries; e += kKvThreads) {
-      int pos, i, width;
-      if (e < off_h) {
-        pos = g.t0 + c * g.F + e / ht, i = e % ht, width = g.dt;
-      } else if (e < off_w) {
-        pos = (e - off_h) / hh, i = (e - off_h) % hh, width = g.dh;
-      } else {
-        pos = (e - off_w) / hwd, i = (e - off_w) % hwd, width = 64 - g.dt - g.dh;
-      }
-      double rv = (double)pos * exp2(-(double)(2 * i) / (double)width * g.log2_base_d) * 0.15915494309189535;
-      rv -= rint(rv);
-      rtab[e] = make_float2(__builtin_amdgcn_cosf((float)rv), __builtin_amdgcn_sinf((float)rv));
-    }
-  }
+  if constexpr (kRope < 2) kv_build_rope_table(rtab, g, c, tid);
 
   // x rows of token tile t of the range; past the last tile the descriptor
   // is empty (its loads return zeros and touch no memory).
@@ -664,11 +865,15 @@ __global__ __launch_bounds__(kKvThreads, 2) void sva_kv_proj_reduce_kernel(
       const bool nx = vs >= g.stages;
       load_x(rg4, nx ? xr_next : xr, nx ? vs - g.stages : vs);
     };
+    // The accumulators start from the bias (row tile rt, entry i of lane
+    // (lg, .): feature 8 lg + 4 (rt % 2) + i of the wave's k or v features).
     pj_floatx4 acc[4][4];
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
+    for (int i = 0; i < 4; ++i) {
+      const float4 b4 = *reinterpret_cast<const float4*>(&bs[wave][32 * (i >> 1) + 8 * lg + 4 * (i & 1)]);
 #pragma unroll
-      for (int j = 0; j < 4; ++j) acc[i][j] = pj_floatx4{0.f, 0.f, 0.f, 0.f};
+      for (int j = 0; j < 4; ++j) acc[i][j] = pj_floatx4{b4.x, b4.y, b4.z, b4.w};
+    }
     auto compute = [&](const KvWRegs& w, int buf) {
       uint32_t ek = w.sk, ev = w.sv;
       asm volatile("" : "+v"(ek));  // see the projection kernel
@@ -721,157 +926,256 @@ __global__ __launch_bounds__(kKvThreads, 2) void sva_kv_proj_reduce_kernel(
     compute(w1, 1);
     __syncthreads();  // every wave is done with xs, which the epilogue overwrites
 
-    // Epilogue.  Lane (lg, lr) holds features 32 run + 8 lg + 0..7
-    // (accumulators 2 run, 2 run + 1) of token 16 tt + lr.  Values are
-    // rounded to bf16 as the stored tensor would be; k then gets phi (and its
-    // normaliser share) and the rotation of its position, and is rounded to
-    // bf16 again; tokens past the range contribute zeros.
-    // (lg through an empty asm: otherwise the compiler hoists the bias and
-    // the RoPE constants out of the tile loop, and they occupy registers
-    // through the GEMM.)
     int lgv = lg;
     asm volatile("" : "+v"(lgv));
-    float bb[2][8];
-#pragma unroll
-    for (int run = 0; run < 2; ++run)
-#pragma unroll
-      for (int i = 0; i < 8; ++i) bb[run][i] = bs[wave][32 * run + 8 * lgv + i];
-    // RoPE of the lane's 4 k pairs (features 32 half + 8 lg + 0..7 of the
-    // head): the axis, and either the table entry of position 0 and the
-    // entries per position step, or base^(-2i/width)/(2 pi)
-    // On the fly, the turn of a frame pair is that of the block's first
-    // frame (reduced in fp64, so that large absolute frame indices keep
-    // their precision) plus the local frame times the frequency.
-    float inv[4], tbase[4];
-    int axis[4], eoff[4], estr[4];
-#pragma unroll
-    for (int pp = 0; pp < 4; ++pp) {
-      const int f = 32 * half + 8 * lgv + 2 * pp;
-      const int ax = f < g.dt ? 0 : f < g.dt + g.dh ? 1 : 2;
-      const int start = ax == 0 ? 0 : ax == 1 ? g.dt : g.dt + g.dh;
-      const int width = ax == 0 ? g.dt : ax == 1 ? g.dh : 64 - g.dt - g.dh;
-      axis[pp] = ax;
-      if constexpr (kTab) {
-        eoff[pp] = (ax == 0 ? 0 : ax == 1 ? off_h : off_w) + ((f - start) >> 1);
-        estr[pp] = width >> 1;
-      } else {
-        const double inv_d = exp2(-(double)(f - start) / (double)width * g.log2_base_d) * 0.15915494309189535;
-        double tb = ax == 0 ? (double)(g.t0 + c * g.F) * inv_d : 0.0;
-        tb -= rint(tb);
-        inv[pp] = (float)inv_d;
-        tbase[pp] = (float)tb;
-      }
-    }
-    float zt[8];
-#pragma unroll
-    for (int i = 0; i < 8; ++i) zt[i] = 0.f;
-    // k rows to the head's k tile, v rows to its v tile
-    char* const ktile = reinterpret_cast<char*>(kvt + (wave & 2) * 512);
-    char* const vtile = reinterpret_cast<char*>(kvt + ((wave & 2) + 1) * 512);
-#pragma unroll
-    for (int tt = 0; tt < 4; ++tt) {
-      const int tok = 16 * tt + lr;
-      const int n = n0 + tok;
-      const bool valid = n < n_end;
-      float val[2][8];  // [0]: k, [1]: v
-#pragma unroll
-      for (int run = 0; run < 2; ++run)
-#pragma unroll
-        for (int i = 0; i < 8; ++i)
-          val[run][i] = (float)(__bf16)(acc[2 * run + (i >> 2)][tt][i & 3] + bb[run][i]);
-      const uint32_t np = (uint32_t)(valid ? n : n_end - 1);  // positions past the range: any in it
-      const uint32_t fr = fdiv(np, g.fHW), rem = np - fr * g.fHW.div;
-      const uint32_t row = fdiv(rem, g.fWs);
-      const int pt = (int)fr - c * g.F;  // the frame within the block
-      const int ph = (int)row, pw = (int)(rem - row * g.fWs.div);
-#pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        // phi on the bit pattern, as in the attention kernels: every value
-        // with the sign bit set (negative numbers, -0, a negative-signed
-        // NaN) becomes +0, every other value passes unchanged
-        val[0][i] = __int_as_float(max(__float_as_int(val[0][i]), 0));
-        zt[i] += valid ? val[0][i] : 0.f;
-      }
-      if (g.rope) {
-#pragma unroll
-        for (int pp = 0; pp < 4; ++pp) {
-          const int ax = axis[pp];
-          const int ps = ax == 0 ? pt : ax == 1 ? ph : pw;
-          float sn, cs;
-          if constexpr (kTab) {
-            const float2 e = rtab[eoff[pp] + ps * estr[pp]];
-            cs = e.x, sn = e.y;
-          } else {
-            const float turn = __builtin_amdgcn_fractf(tbase[pp] + (float)ps * inv[pp]);
-            sn = __builtin_amdgcn_sinf(turn), cs = __builtin_amdgcn_cosf(turn);
-          }
-          const float x = val[0][2 * pp], y = val[0][2 * pp + 1];
-          val[0][2 * pp] = x * cs - y * sn;
-          val[0][2 * pp + 1] = x * sn + y * cs;
-        }
-      }
-#pragma unroll
-      for (int run = 0; run < 2; ++run)
-#pragma unroll
-        for (int i = 0; i < 8; ++i) {
-          const int f = 32 * half + 8 * lg + i;
-          const __bf16 h = (__bf16)(valid ? val[run][i] : 0.f);
-          *reinterpret_cast<__bf16*>((run ? vtile : ktile) + kv_piece(f, tok >> 3) * 16 + (tok & 7) * 2) = h;
-        }
-    }
-    // the tile's normaliser share, summed over the 16 token lanes
-#pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      float t = zt[i];
-      t += __shfl_xor(t, 1);
-      t += __shfl_xor(t, 2);
-      t += __shfl_xor(t, 4);
-      t += __shfl_xor(t, 8);
-      if (lr == 0) zs[wave >> 1][32 * half + 8 * lg + i] += t;
-    }
+    if (n0 + kTileM <= n_end)
+      kv_tile_epilogue_rm<kRope, true>(acc, g, rtab, kvt, zt, wave, half, lg, lgv, lr, n0, n_end, c);
+    else
+      kv_tile_epilogue_rm<kRope, false>(acc, g, rtab, kvt, zt, wave, half, lg, lgv, lr, n0, n_end, c);
     __syncthreads();
-    // State rows (value features) 32 half .. + 31 of this wave's head:
-    // S^T[fo][fi] += sum over the tile's tokens of v[fo] RoPE(phi k)[fi].
-    const uint4* vt = kvt + ((wave & 2) + 1) * 512;
-    const uint4* kt = kvt + (wave & 2) * 512;
     pj_floatx4 sa[2][4];
 #pragma unroll
     for (int ft = 0; ft < 2; ++ft)
 #pragma unroll
       for (int fc = 0; fc < 4; ++fc) sa[ft][fc] = sacc[wave][4 * ft + fc][lane];
-#pragma unroll
-    for (int ks = 0; ks < 2; ++ks) {
-      uint4 a[2], bo[4];
-#pragma unroll
-      for (int ft = 0; ft < 2; ++ft) a[ft] = vt[kv_piece(16 * (2 * half + ft) + lr, 4 * ks + lg)];
-#pragma unroll
-      for (int fc = 0; fc < 4; ++fc) bo[fc] = kt[kv_piece(16 * fc + lr, 4 * ks + lg)];
-#pragma unroll
-      for (int ft = 0; ft < 2; ++ft)
-#pragma unroll
-        for (int fc = 0; fc < 4; ++fc) sa[ft][fc] = mfma(a[ft], bo[fc], sa[ft][fc]);
-    }
+    kv_state_mfma_tr(sa, kvt, wave, half, lane);
 #pragma unroll
     for (int ft = 0; ft < 2; ++ft)
 #pragma unroll
       for (int fc = 0; fc < 4; ++fc) sacc[wave][4 * ft + fc][lane] = sa[ft][fc];
   }
 
-  // Partial of (range, block): S^T (row fo, column fi), then z.
+  kv_z_reduce(zt, zs[wave >> 1], half, lg, lr);
   __syncthreads();
-  const long long bh = (long long)b * g.H + head;
-  const long long gv = bh * g.ranges + r;
-  const long long bhc = bh * g.nb + c;
-  float* dst = partials + (gv + bhc) * (64 * 64 + 64);
+  pj_floatx4 sa[2][4];
 #pragma unroll
   for (int ft = 0; ft < 2; ++ft)
 #pragma unroll
-    for (int fc = 0; fc < 4; ++fc) {
-      const pj_floatx4 v4 = sacc[wave][4 * ft + fc][lane];
+    for (int fc = 0; fc < 4; ++fc) sa[ft][fc] = sacc[wave][4 * ft + fc][lane];
+  kv_store_partial(sa, zs[wave >> 1], partials, g, b, head, r, c, half, lg, lr, lane);
+}
+
+// The fused k, v kernel on 4-bit activations: the work split, the tile order
+// and the epilogue of sva_kv_proj_reduce_kernel, with the GEMM of
+// sva_qkv_proj_w4a4_kernel (the scaled fp4 MFMA on the 4-bit x tile from
+// LDS, the packed weights one stage ahead in registers).  A token tile's x
+// codes (64 rows of up to 1024 channels a chunk, rows XOR-swizzled) and
+// scale words go straight from global memory to LDS (buffer loads with the
+// lds bit, which take no registers): the next tile's are issued once every
+// wave is done with the current ones, after the tile's last weight loads
+// (vector loads complete in issue order, so no weight wait also waits for
+// them), and land while the epilogue runs on its own LDS tiles.  Grids
+// with more than 1024 channels reload the x buffer per chunk, in turn.  The
+// head states stay in registers.
+constexpr int kRopeTabW4 = 1536;  // this kernel's RoPE table: two workgroups a CU with both x and k, v tiles
+
+typedef __attribute__((address_space(3))) void* lds_void_ptr;
+
+// kRope: as for kv_tile_epilogue_rm (0, 1: the LDS table; 2: on the fly).
+template <int kRope>
+__global__ __launch_bounds__(kKvThreads, 2) void sva_kv_proj_reduce_w4a4_kernel(
+    const uint8_t* __restrict__ xq, const uint8_t* __restrict__ xsc, const uint8_t* __restrict__ wpack,
+    const float* __restrict__ bias, float* __restrict__ partials, KvGeo g) {
+  __shared__ uint4 xcs[kTileM * kXPitch];
+  __shared__ uint32_t xss[kTileM * kXChunkStages];
+  __shared__ uint4 kvt[(kKvThreads / 64) * 512];  // wave w's k or v tile at kvt + w * 512
+  __shared__ float zs[2][64];
+  __shared__ float bs[kKvThreads / 64][64];
+  __shared__ float2 rtab[kRope < 2 ? kRopeTabW4 : 1];
+  static_assert(kTileM * kXPitch == 32 * 64 && kTileM * kXChunkStages == 8 * 64,
+                "x unit: 32 code and 8 scale loads of 64 lanes, 8 and 2 a wave");
+
+  // Tile order as in the bf16 kernel: the head pairs of one range on one XCD.
+  const int xcd = blockIdx.x & 7;
+  const int local = blockIdx.x >> 3;
+  const int rg = (local / g.npairs) * 8 + xcd;
+  const int pair = local % g.npairs;
+  if (rg >= g.nrg) return;
+  const int b = rg / g.ranges, r = rg - b * g.ranges;
+  const int n_begin = r * g.L, n_end = n_begin + g.L;
+  const int c = n_begin / g.Nb;
+
+  const int tid = threadIdx.x;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int lane = tid & 63;
+  const int lg = lane >> 4, lr = lane & 15;
+  const int half = wave & 1;
+  const int head = 2 * pair + (wave >> 1);
+  const int blk_k = g.H + head, blk_v = 2 * g.H + head;
+  const uint8_t* cbase = wpack + ((size_t)blk_k * g.stages * 4 + 2 * half) * 1024 + lane * 16;
+  const uint8_t* sbase = wpack + (size_t)g.n_pack * (g.C / 2) + ((size_t)blk_k * g.stages * 64 + lane) * 4;
+  const size_t cvoff = (size_t)g.H * g.stages * 4 * 1024, svoff = (size_t)g.H * g.stages * 256;
+  const int sshift = 16 * half;
+  const uint32_t crow = (uint32_t)g.C / 2, srow = (uint32_t)g.C / 32;
+  const long long M = (long long)(g.nrg / g.ranges) * g.N;
+  const int nch = (g.stages + kXChunkStages - 1) / kXChunkStages;
+
+  bs[wave][lane] = bias ? bias[(lane < 32 ? blk_k : blk_v) * 64 + 32 * half + (lane & 31)] : 0.f;
+  if constexpr (kRope < 2) kv_build_rope_table(rtab, g, c, tid);
+
+  // x unit (tile t, chunk j) into LDS.  Load i of wave w fills code slots
+  // 64 (8 w + i) + lane, i.e. rows 2 (8 w + i) + lane / 32 at swizzled
+  // position lane % 32, so the lane fetches piece (lane % 32) ^ (row & 31);
+  // scale load i fills words 64 (2 w + i) + lane = (row, stage) (u / 8,
+  // u % 8).  Pieces and stages past the chunk, rows past the tokens, and
+  // every load past the last tile get an offset past the descriptor's
+  // range: they write zeros and touch no memory.
+  const int ntiles = (g.L + kTileM - 1) / kTileM;
+  constexpr uint32_t kPast = 0x80000000u;
+  auto load_unit = [&](int t, int j) {
+    const long long m0 = (long long)b * g.N + n_begin + (long long)t * kTileM;
+    const int rows = t < ntiles ? (int)min((long long)kTileM, M - m0) : 0;
+    const __amdgpu_buffer_rsrc_t cr = rsrc(xq + m0 * crow, (uint32_t)rows * crow);
+    const __amdgpu_buffer_rsrc_t sr = rsrc(xsc + m0 * srow, (uint32_t)rows * srow);
+    const int s0 = j * kXChunkStages;
+    const int ns = min(kXChunkStages, g.stages - s0);
+    // Where registers are short (the per-pair RoPE modes) the lane index
+    // goes through an empty asm: the offsets are then recomputed per call
+    // rather than kept live (and spilled) across the tile loop.
+    int ln = lane;
+    if constexpr (kRope != 0) asm volatile("" : "+v"(ln));
 #pragma unroll
-      for (int i = 0; i < 4; ++i) dst[(16 * (2 * half + ft) + 4 * lg + i) * 64 + 16 * fc + lr] = v4[i];
+    for (int i = 0; i < 8; ++i) {
+      const int row = 2 * (8 * wave + i) + (ln >> 5);
+      const int piece = (ln & 31) ^ (row & 31);
+      const uint32_t off = piece < 4 * ns ? (uint32_t)row * crow + 64 * s0 + 16 * piece : kPast;
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(cr, (lds_void_ptr)(xcs + 64 * (8 * wave + i)), 16, off, 0, 0, 0);
     }
-  if (half == 0) dst[64 * 64 + lane] = zs[wave >> 1][lane];
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+      const int u = 64 * (2 * wave + i) + ln;
+      const int sl = u % kXChunkStages;
+      const uint32_t off = sl < ns ? (uint32_t)(u / kXChunkStages) * srow + 4 * (s0 + sl) : kPast;
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(sr, (lds_void_ptr)(xss + 64 * (2 * wave + i)), 4, off, 0, 0, 0);
+    }
+  };
+  // Every wave's loads of the unit have landed in LDS: each wave waits for
+  // its own (vmcnt(0)), then the workgroup meets.  The empty asm statements
+  // keep the compiler from moving LDS accesses across.
+  auto unit_ready = [&]() {
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
+    __syncthreads();
+    asm volatile("" ::: "memory");
+  };
+  // accumulators 0, 1: k row tiles; 2, 3: v row tiles
+  auto load_w = [&](KvWRegs& w, int s) {
+#pragma unroll
+    for (int rt = 0; rt < 4; ++rt)
+      w.c[rt] = *(const uint4*)(cbase + (rt < 2 ? 0 : cvoff) + ((size_t)s * 4 + (rt & 1)) * 1024);
+    w.sk = *(const uint32_t*)(sbase + (size_t)s * 256);
+    w.sv = *(const uint32_t*)(sbase + svoff + (size_t)s * 256);
+  };
+
+  pj_floatx4 sa[2][4];
+#pragma unroll
+  for (int ft = 0; ft < 2; ++ft)
+#pragma unroll
+    for (int fc = 0; fc < 4; ++fc) sa[ft][fc] = pj_floatx4{0.f, 0.f, 0.f, 0.f};
+  float zt[8];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) zt[i] = 0.f;
+
+  // The weights go by pairs of stages (C is a multiple of 256) in a ring of
+  // two register pairs: pair q + 1 loads while pair q computes, so every
+  // load is issued two stages before its use (one stage ahead left each
+  // stage waiting for L2).  The weights do not depend on the token tile: the
+  // pair after a tile's last is its pair 0, for the next tile, and it loads
+  // during the tile's last pair.
+  const int np = g.stages / 2;
+  auto load_pair = [&](KvWRegs (&w)[2], int q) {
+    load_w(w[0], 2 * q);
+    load_w(w[1], 2 * q + 1);
+  };
+  KvWRegs P0[2], P1[2];
+  load_pair(P0, 0);
+  load_unit(0, 0);
+  for (int it = 0; it < ntiles; ++it) {
+    const int n0 = n_begin + it * kTileM;
+    // The accumulators start from the bias: row tile rt, entry i of lane
+    // (lg, .) is feature 8 lg + 4 (rt % 2) + i of the wave's k (rt < 2) or
+    // v features.
+    pj_floatx4 acc[4][4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const float4 b4 = *reinterpret_cast<const float4*>(&bs[wave][32 * (i >> 1) + 8 * lg + 4 * (i & 1)]);
+#pragma unroll
+      for (int j = 0; j < 4; ++j) acc[i][j] = pj_floatx4{b4.x, b4.y, b4.z, b4.w};
+    }
+    // one stage from chunk-local stage sl: B operands and scales from LDS,
+    // the weights' scale bytes of this wave's row tiles gathered into one
+    // word (k tiles in bytes 0, 1; v tiles in 2, 3) for op_sel
+    auto compute = [&](const KvWRegs& w, int sl) {
+      uint32_t ek = w.sk, ev = w.sv;
+      asm volatile("" : "+v"(ek));
+      asm volatile("" : "+v"(ev));
+      const uint32_t e = ((ek >> sshift) & 0xffffu) | ((ev >> sshift) << 16);
+#pragma unroll
+      for (int tt = 0; tt < 4; ++tt) {
+        const int row = tt * 16 + lr;
+        const uint4 bo = xcs[row * kXPitch + ((4 * sl + lg) ^ (row & 31))];
+        const uint32_t sb = (xss[row * kXChunkStages + sl] >> (8 * lg)) & 0xffu;
+        acc[0][tt] = mfma_fp4<0>(w.c[0], e, bo, sb, acc[0][tt]);
+        acc[1][tt] = mfma_fp4<1>(w.c[1], e, bo, sb, acc[1][tt]);
+        acc[2][tt] = mfma_fp4<2>(w.c[2], e, bo, sb, acc[2][tt]);
+        acc[3][tt] = mfma_fp4<3>(w.c[3], e, bo, sb, acc[3][tt]);
+      }
+    };
+    for (int j = 0; j < nch; ++j) {
+      if (j > 0) {  // past 1024 channels: the next chunk, once every wave is done with this one
+        __syncthreads();
+        load_unit(it, j);
+      }
+      unit_ready();
+      const int q0 = j * (kXChunkStages / 2);                   // the chunk's first pair
+      const int nq = min(kXChunkStages, g.stages - 2 * q0) / 2;  // its pairs
+      int ql = 0;
+      for (; ql + 2 <= nq; ql += 2) {
+        const int q = q0 + ql;
+        load_pair(P1, (q + 1) % np);
+        __builtin_amdgcn_sched_barrier(0);
+        compute(P0[0], 2 * ql);
+        compute(P0[1], 2 * ql + 1);
+        __builtin_amdgcn_sched_barrier(0);
+        load_pair(P0, (q + 2) % np);
+        __builtin_amdgcn_sched_barrier(0);
+        compute(P1[0], 2 * ql + 2);
+        compute(P1[1], 2 * ql + 3);
+        __builtin_amdgcn_sched_barrier(0);
+      }
+      if (ql < nq) {  // an odd pair count: the last pair, then the ring shifts
+        load_pair(P1, (q0 + ql + 1) % np);
+        __builtin_amdgcn_sched_barrier(0);
+        compute(P0[0], 2 * ql);
+        compute(P0[1], 2 * ql + 1);
+        __builtin_amdgcn_sched_barrier(0);
+        P0[0] = P1[0];
+        P0[1] = P1[1];
+      }
+    }
+    // Every wave is done with the x buffer: the next tile's first chunk
+    // loads into it during the epilogue.  (Barriers on LDS alone from here
+    // on: the weight and x loads in flight stay in flight.)
+    asm volatile("" ::: "memory");
+    lds_sync();
+    asm volatile("" ::: "memory");
+    load_unit(it + 1, 0);
+    // (in the per-pair modes, lg through an empty asm: their RoPE constants
+    // are then set per tile instead of occupying registers through the GEMM)
+    int lgv = lg;
+    if constexpr (kRope != 0) asm volatile("" : "+v"(lgv));
+    if (n0 + kTileM <= n_end)
+      kv_tile_epilogue_rm<kRope, true>(acc, g, rtab, kvt, zt, wave, half, lg, lgv, lr, n0, n_end, c);
+    else
+      kv_tile_epilogue_rm<kRope, false>(acc, g, rtab, kvt, zt, wave, half, lg, lgv, lr, n0, n_end, c);
+    asm volatile("" ::: "memory");
+    lds_sync();
+    asm volatile("" ::: "memory");
+    kv_state_mfma_tr(sa, kvt, wave, half, lane);
+  }
+  kv_z_reduce(zt, zs[wave >> 1], half, lg, lr);
+  __syncthreads();  // zs complete
+  kv_store_partial(sa, zs[wave >> 1], partials, g, b, head, r, c, half, lg, lr, lane);
 }
 
 // Repacks natural-layout MXFP4 weights (codes [n_out, C/2], scales
@@ -1002,13 +1306,14 @@ sva_status sva_internal_proj_features(const sva_proj_desc* desc, const void* x, 
   return SVA_OK;
 }
 
-hipError_t sva_internal_kv_proj_reduce(const SvaKvReduceArgs& a, const void* x, const void* wpack,
-                                       const float* bias, float* partials, hipStream_t stream) {
-  // The kernel's pipeline carries the next tile's first stages through the
-  // epilogue in fixed registers, which takes an even stage count.
-  if (a.C % (2 * kTileK) != 0 || a.C < 2 * kTileK || a.H % 2 != 0 || a.L <= 0 || a.N % a.L != 0)
-    return hipErrorInvalidValue;
-  KvGeo g;
+namespace {
+
+// The fused k, v kernels' geometry; false where the kernels' pipeline does
+// not apply (it carries the next tile's first weight stage through the
+// epilogue in fixed registers, which takes an even stage count).
+bool make_kv_geo(const SvaKvReduceArgs& a, KvGeo* out) {
+  if (a.C % (2 * kTileK) != 0 || a.C < 2 * kTileK || a.H % 2 != 0 || a.L <= 0 || a.N % a.L != 0) return false;
+  KvGeo& g = *out;
   g.N = a.N;
   g.C = a.C;
   g.H = a.H;
@@ -1031,13 +1336,43 @@ hipError_t sva_internal_kv_proj_reduce(const SvaKvReduceArgs& a, const void* x, 
   g.log2_base_d = log2((double)a.rope_base);
   g.F = a.Nb / (a.Hs * a.Ws);
   g.tab_entries = g.F * (a.dt / 2) + a.Hs * (a.dh / 2) + a.Ws * ((64 - a.dt - a.dh) / 2);
-  const bool tab = a.rope && g.tab_entries <= kRopeTab;
+  return true;
+}
+
+}  // namespace
+
+hipError_t sva_internal_kv_proj_reduce(const SvaKvReduceArgs& a, const void* x, const void* wpack,
+                                       const float* bias, float* partials, hipStream_t stream) {
+  KvGeo g;
+  if (!make_kv_geo(a, &g)) return hipErrorInvalidValue;
+  const int mode = !a.rope ? 0 : g.tab_entries > kRopeTab ? 2 : (a.dt % 8 == 0 && a.dh % 8 == 0) ? 0 : 1;
   const long long grid = ((long long)g.nrg + 7) / 8 * 8 * g.npairs;
   const uint8_t* wp = (const uint8_t*)wpack;
   void* args[] = {(void*)&x, (void*)&wp, (void*)&bias, (void*)&partials, &g};
-  const void* fn = tab ? (const void*)&sva_kv_proj_reduce_kernel<true> : (const void*)&sva_kv_proj_reduce_kernel<false>;
-  return hipLaunchKernel(fn, dim3((unsigned)grid), dim3(kKvThreads), args, 0,
-                         stream);
+  const void* fn = mode == 0   ? (const void*)&sva_kv_proj_reduce_kernel<0>
+                   : mode == 1 ? (const void*)&sva_kv_proj_reduce_kernel<1>
+                               : (const void*)&sva_kv_proj_reduce_kernel<2>;
+  return hipLaunchKernel(fn, dim3((unsigned)grid), dim3(kKvThreads), args, 0, stream);
+}
+
+hipError_t sva_internal_kv_proj_reduce_w4a4(const SvaKvReduceArgs& a, const void* xq, const void* wpack,
+                                            const float* bias, float* partials, hipStream_t stream) {
+  KvGeo g;
+  if (!make_kv_geo(a, &g)) return hipErrorInvalidValue;
+  // RoPE: the LDS table where it fits, the lane's 4 pairs on one axis
+  // where every axis width is a multiple of 8; without RoPE the mode does
+  // not matter (the epilogue skips the rotation)
+  const int mode = !a.rope ? 0 : g.tab_entries > kRopeTabW4 ? 2 : (a.dt % 8 == 0 && a.dh % 8 == 0) ? 0 : 1;
+  const long long grid = ((long long)g.nrg + 7) / 8 * 8 * g.npairs;
+  const long long M = (long long)a.B * a.N;
+  const uint8_t* codes = (const uint8_t*)xq;
+  const uint8_t* scales = codes + (size_t)M * a.C / 2;
+  const uint8_t* wp = (const uint8_t*)wpack;
+  void* args[] = {(void*)&codes, (void*)&scales, (void*)&wp, (void*)&bias, (void*)&partials, &g};
+  const void* fn = mode == 0   ? (const void*)&sva_kv_proj_reduce_w4a4_kernel<0>
+                   : mode == 1 ? (const void*)&sva_kv_proj_reduce_w4a4_kernel<1>
+                               : (const void*)&sva_kv_proj_reduce_w4a4_kernel<2>;
+  return hipLaunchKernel(fn, dim3((unsigned)grid), dim3(kKvThreads), args, 0, stream);
 }
 
 extern "C" sva_status sva_qkv_proj_mxfp4(const sva_proj_desc* desc, const void* x, const void* wpack,
@@ -1074,8 +1409,8 @@ extern "C" sva_status sva_mxfp4_quant_acts(const sva_proj_desc* desc, const void
   return SVA_OK;
 }
 
-extern "C" sva_status sva_qkv_proj_w4a4(const sva_proj_desc* desc, const void* xq, const void* wpack,
-                                        const float* bias, void* q, void* k, void* v, void* stream) {
+sva_status sva_internal_proj_w4a4_features(const sva_proj_desc* desc, const void* xq, const void* wpack,
+                                           const float* bias, int f_end, void* q, void* k, void* v, void* stream) {
   const sva_status st = check_desc(desc);
   if (st != SVA_OK) return st;
   const sva_proj_desc& d = *desc;
@@ -1084,11 +1419,14 @@ extern "C" sva_status sva_qkv_proj_w4a4(const sva_proj_desc* desc, const void* x
       (bias && !aligned(bias, 16)))
     return SVA_ERR_INVALID_ARG;
   const int n_pack = 3 * d.H * d.d;
+  if (f_end < 64 || f_end > n_pack || f_end % 64 != 0) return SVA_ERR_INVALID_ARG;
   const long long M = (long long)d.B * d.N;
   const size_t ab = acts_bytes(d), ob = (size_t)M * d.H * d.d * 2, pb = packed_bytes(d);
   const size_t bb = (size_t)n_pack * 4;
+  // the outputs that features [0, f_end) reach
   void* outs[3] = {q, k, v};
-  for (int i = 0; i < 3; ++i) {
+  const int n_outs = (f_end + d.H * d.d - 1) / (d.H * d.d);
+  for (int i = 0; i < n_outs; ++i) {
     if (overlap(outs[i], ob, xq, ab) || overlap(outs[i], ob, wpack, pb) || (bias && overlap(outs[i], ob, bias, bb)))
       return SVA_ERR_INVALID_ARG;
     for (int j = 0; j < i; ++j)
@@ -1100,10 +1438,10 @@ extern "C" sva_status sva_qkv_proj_w4a4(const sva_proj_desc* desc, const void* x
   g.C = d.C;
   g.H = d.H;
   g.d = d.d;
-  g.n_out = n_pack;
+  g.n_out = f_end;
   g.n_pack = n_pack;
   g.Mt = (int)((M + kTileM - 1) / kTileM);
-  g.Nt = (n_pack + kTileN - 1) / kTileN;
+  g.Nt = (f_end + kTileN - 1) / kTileN;
   g.stages = d.C / kTileK;
   g.fN = make_fastdiv((uint32_t)d.N);
   g.fHD = make_fastdiv((uint32_t)(d.H * d.d));
@@ -1117,4 +1455,10 @@ extern "C" sva_status sva_qkv_proj_w4a4(const sva_proj_desc* desc, const void* x
                       (hipStream_t)stream) != hipSuccess)
     return SVA_ERR_HIP;
   return SVA_OK;
+}
+
+extern "C" sva_status sva_qkv_proj_w4a4(const sva_proj_desc* desc, const void* xq, const void* wpack,
+                                        const float* bias, void* q, void* k, void* v, void* stream) {
+  if (!desc) return SVA_ERR_INVALID_ARG;
+  return sva_internal_proj_w4a4_features(desc, xq, wpack, bias, 3 * desc->H * desc->d, q, k, v, stream);
 }

@@ -2644,9 +2644,11 @@ sva_status plan_proj_fwd(const sva_desc* a, const sva_proj_desc* pd, ProjPlan* p
   return SVA_OK;
 }
 
+// x: bf16 activations [B, N, C], or with w4a4 their MXFP4 form (codes, then
+// scales, as sva_mxfp4_quant_acts writes them).
 sva_status run_proj_fwd(const sva_desc* a, const sva_proj_desc* pd, const void* x, const void* wpack,
                         const float* bias, void* out, const float* S0, const float* z0, float* S_out,
-                        float* z_out, void* ws, size_t ws_bytes, void* stream) {
+                        float* z_out, void* ws, size_t ws_bytes, void* stream, bool w4a4) {
   ProjPlan pp;
   sva_status s = plan_proj_fwd(a, pd, &pp);
   if (s != SVA_OK) return s;
@@ -2661,7 +2663,8 @@ sva_status run_proj_fwd(const sva_desc* a, const sva_proj_desc* pd, const void* 
     return SVA_ERR_INVALID_ARG;
   if (!ws || ws_bytes < pp.bytes || !is_aligned16(ws)) return SVA_ERR_WORKSPACE;
   const size_t nbytes = qkv_bytes(p);
-  const size_t xbytes = (size_t)pd->B * pd->N * pd->C * 2;
+  const size_t M = (size_t)pd->B * pd->N;
+  const size_t xbytes = w4a4 ? M * pd->C / 2 + M * pd->C / 32 : M * pd->C * 2;
   const size_t n_out = (size_t)3 * pd->H * pd->d;
   const size_t wbytes = n_out * pd->C / 2 + n_out * pd->C / 32;  // codes, then the scale words
   const size_t s_bytes = (size_t)p.BH * p.D * p.D * sizeof(float), z_bytes = (size_t)p.BH * p.D * sizeof(float);
@@ -2678,7 +2681,8 @@ sva_status run_proj_fwd(const sva_desc* a, const sva_proj_desc* pd, const void* 
   float* zc = (float*)(wsb + pp.off_zc);
   hipStream_t st = (hipStream_t)stream;
   // q: the projection's first H*d features, into the workspace
-  s = sva_internal_proj_features(pd, x, wpack, bias, pd->H * pd->d, q, q, q, stream);
+  s = w4a4 ? sva_internal_proj_w4a4_features(pd, x, wpack, bias, pd->H * pd->d, q, q, q, stream)
+           : sva_internal_proj_features(pd, x, wpack, bias, pd->H * pd->d, q, q, q, stream);
   if (s != SVA_OK) return s;
   SvaKvReduceArgs ka;
   ka.B = pd->B;
@@ -2695,7 +2699,9 @@ sva_status run_proj_fwd(const sva_desc* a, const sva_proj_desc* pd, const void* 
   ka.dt = a->rope_dt;
   ka.dh = a->rope_dh;
   ka.rope_base = a->rope_base;
-  if (sva_internal_kv_proj_reduce(ka, x, wpack, bias, partials, st) != hipSuccess) return SVA_ERR_HIP;
+  if ((w4a4 ? sva_internal_kv_proj_reduce_w4a4(ka, x, wpack, bias, partials, st)
+            : sva_internal_kv_proj_reduce(ka, x, wpack, bias, partials, st)) != hipSuccess)
+    return SVA_ERR_HIP;
   plan_grids(&p);
   if (SVA_DISPATCH2(p, launch_scan, p, partials, S0, z0, S_out, z_out, frags, zc, true, st, false, pp.L) !=
       hipSuccess)
@@ -2793,7 +2799,14 @@ sva_status sva_proj_lin_attn_fwd(const sva_desc* attn, const sva_proj_desc* proj
                                  const void* wpack, const float* bias, void* out, const float* S0,
                                  const float* z0, float* S_out, float* z_out, void* ws, size_t ws_bytes,
                                  void* stream) {
-  return run_proj_fwd(attn, proj, x, wpack, bias, out, S0, z0, S_out, z_out, ws, ws_bytes, stream);
+  return run_proj_fwd(attn, proj, x, wpack, bias, out, S0, z0, S_out, z_out, ws, ws_bytes, stream, false);
+}
+
+sva_status sva_proj_lin_attn_fwd_w4a4(const sva_desc* attn, const sva_proj_desc* proj, const void* xq,
+                                      const void* wpack, const float* bias, void* out, const float* S0,
+                                      const float* z0, float* S_out, float* z_out, void* ws, size_t ws_bytes,
+                                      void* stream) {
+  return run_proj_fwd(attn, proj, xq, wpack, bias, out, S0, z0, S_out, z_out, ws, ws_bytes, stream, true);
 }
 
 sva_status sva_lin_attn_fwd_stages(const sva_desc* desc, const void* q, const void* k, const void* v,

@@ -92,6 +92,8 @@ _SIG = {
                                                         ctypes.POINTER(ctypes.c_size_t)]),
     "sva_proj_lin_attn_fwd": (ctypes.c_int, [ctypes.POINTER(SvaDesc), ctypes.POINTER(SvaProjDesc)] + [_VP] * 9
                               + [ctypes.c_size_t, _VP]),
+    "sva_proj_lin_attn_fwd_w4a4": (ctypes.c_int, [ctypes.POINTER(SvaDesc), ctypes.POINTER(SvaProjDesc)] + [_VP] * 9
+                                   + [ctypes.c_size_t, _VP]),
 }
 
 
@@ -598,17 +600,7 @@ def sva_qkv_proj_w4a4(xq, wpack, bias, B: int, N: int, C: int, H: int, d: int, *
     sva_mxfp4_pack_weights; bias [3 H d] fp32 or None.  Returns (q, k, v),
     each [B, H, N, d] bf16."""
     import torch
-    _check_bytes("xq", xq)
-    if xq.numel() * xq.element_size() != mxfp4_acts_bytes(B * N, C):
-        raise ValueError(f"xq holds {xq.numel() * xq.element_size()} bytes, expected "
-                         f"{mxfp4_acts_bytes(B * N, C)} for {B * N} rows of C = {C}")
-    n_out = 3 * H * d
-    _check_bytes("wpack", wpack)
-    if wpack.numel() * wpack.element_size() != mxfp4_packed_bytes(n_out, C):
-        raise ValueError(f"wpack holds {wpack.numel() * wpack.element_size()} bytes, expected "
-                         f"{mxfp4_packed_bytes(n_out, C)} for {n_out} outputs of C = {C}")
-    if bias is not None:
-        _check_layout("bias", bias, (n_out,), torch.float32)
+    _check_w4a4_inputs(xq, wpack, bias, B, N, C, H, d)
     for name, t in (("q", q), ("k", k), ("v", v)):
         if t is not None:
             _check_layout(name, t, (B, H, N, d), torch.bfloat16)
@@ -623,6 +615,57 @@ def sva_qkv_proj_w4a4(xq, wpack, bias, B: int, N: int, C: int, H: int, d: int, *
     return tuple(outs)
 
 
+def _check_w4a4_inputs(xq, wpack, bias, B, N, C, H, d):
+    """xq the MXFP4 activations of an x [B, N, C], wpack the packed weights
+    for 3 H d outputs, bias [3 H d] fp32 or None (layouts only)."""
+    import torch
+    _check_bytes("xq", xq)
+    if xq.numel() * xq.element_size() != mxfp4_acts_bytes(B * N, C):
+        raise ValueError(f"xq holds {xq.numel() * xq.element_size()} bytes, expected "
+                         f"{mxfp4_acts_bytes(B * N, C)} for {B * N} rows of C = {C}")
+    n_out = 3 * H * d
+    _check_bytes("wpack", wpack)
+    if wpack.numel() * wpack.element_size() != mxfp4_packed_bytes(n_out, C):
+        raise ValueError(f"wpack holds {wpack.numel() * wpack.element_size()} bytes, expected "
+                         f"{mxfp4_packed_bytes(n_out, C)} for {n_out} outputs of C = {C}")
+    if bias is not None:
+        _check_layout("bias", bias, (n_out,), torch.float32)
+
+
+def _proj_lin_attn(fn_name, xin, xname, wpack, bias, B, N, C, H, grid, frames_per_block, t0, rope, split, base,
+                   eps, S0, z0, S_out, z_out, out, ws, stream, range_tokens):
+    """The fused projection + attention calls' common part: the output and
+    cache checks, the descriptors, the workspace and the call."""
+    import torch
+    _pair("S0", S0, "z0", z0)
+    _pair("S_out", S_out, "z_out", z_out)
+    T, Hs, Ws = grid
+    if N != T * Hs * Ws:
+        raise ValueError(f"{xname} holds {N} tokens per sample but the grid {T}x{Hs}x{Ws} has {T * Hs * Ws}")
+    if out is not None:
+        _check_layout("out", out, (B, H, N, 64), torch.bfloat16)
+    for name, t, shape in (("S0", S0, (B, H, 64, 64)), ("z0", z0, (B, H, 64)), ("S_out", S_out, (B, H, 64, 64)),
+                           ("z_out", z_out, (B, H, 64))):
+        if t is not None:
+            _check_layout(name, t, shape, torch.float32)
+    if ws is not None:
+        _check_bytes("ws", ws)
+    _check_devices(xname, xin, [("wpack", wpack), ("bias", bias), ("out", out), ("S0", S0), ("z0", z0),
+                                ("S_out", S_out), ("z_out", z_out), ("ws", ws)])
+    q_like = torch.empty((B, H, N, 64), dtype=torch.bfloat16, device=xin.device) if out is None else out
+    desc = _desc_from(q_like, grid, frames_per_block, t0, rope, split, base, eps)
+    pdesc = SvaProjDesc(B, N, C, H, 64, int(range_tokens))
+    n = ctypes.c_size_t()
+    _check(lib().sva_proj_lin_attn_fwd_workspace(ctypes.byref(desc), ctypes.byref(pdesc), ctypes.byref(n)),
+           "sva_proj_lin_attn_fwd_workspace")
+    ws = _workspace(n.value, xin, ws)
+    st = getattr(lib(), fn_name)(ctypes.byref(desc), ctypes.byref(pdesc), _ptr(xin), _ptr(wpack), _ptr(bias),
+                                 _ptr(q_like), _ptr(S0), _ptr(z0), _ptr(S_out), _ptr(z_out), _ptr(ws),
+                                 ws.numel() * ws.element_size(), _stream(stream))
+    _check(st, fn_name)
+    return q_like
+
+
 def sva_proj_lin_attn_fwd(x, wpack, bias, H: int, grid: Tuple[int, int, int], frames_per_block: int, *,
                           t0: int = 0, rope: bool = False, split=None, base: float = 10000.0, eps: float = 1e-6,
                           S0=None, z0=None, S_out=None, z_out=None, out=None, ws=None, stream=None,
@@ -632,33 +675,21 @@ def sva_proj_lin_attn_fwd(x, wpack, bias, H: int, grid: Tuple[int, int, int], fr
     of d = 64; bias [3 H 64] fp32 or None.  range_tokens: tokens per
     reduction range (0: chosen by the library; else a divisor of the block
     length).  Returns out [B, H, N, 64] bf16."""
-    import torch
-    _pair("S0", S0, "z0", z0)
-    _pair("S_out", S_out, "z_out", z_out)
     _check_proj_inputs(x, wpack, bias, H, 64)
     B, N, C = x.shape
+    return _proj_lin_attn("sva_proj_lin_attn_fwd", x, "x", wpack, bias, B, N, C, H, grid, frames_per_block, t0,
+                          rope, split, base, eps, S0, z0, S_out, z_out, out, ws, stream, range_tokens)
+
+
+def sva_proj_lin_attn_fwd_w4a4(xq, wpack, bias, B: int, C: int, H: int, grid: Tuple[int, int, int],
+                               frames_per_block: int, *, t0: int = 0, rope: bool = False, split=None,
+                               base: float = 10000.0, eps: float = 1e-6, S0=None, z0=None, S_out=None, z_out=None,
+                               out=None, ws=None, stream=None, range_tokens: int = 0):
+    """The same on 4-bit activations (sva_proj_lin_attn_fwd_w4a4): xq from
+    sva_mxfp4_quant_acts of an x [B, N, C] with N = T * Hs * Ws; the rest as
+    for sva_proj_lin_attn_fwd.  Returns out [B, H, N, 64] bf16."""
     T, Hs, Ws = grid
-    if N != T * Hs * Ws:
-        raise ValueError(f"x holds {N} tokens per sample but the grid {T}x{Hs}x{Ws} has {T * Hs * Ws}")
-    if out is not None:
-        _check_layout("out", out, (B, H, N, 64), torch.bfloat16)
-    for name, t, shape in (("S0", S0, (B, H, 64, 64)), ("z0", z0, (B, H, 64)), ("S_out", S_out, (B, H, 64, 64)),
-                           ("z_out", z_out, (B, H, 64))):
-        if t is not None:
-            _check_layout(name, t, shape, torch.float32)
-    if ws is not None:
-        _check_bytes("ws", ws)
-    _check_devices("x", x, [("wpack", wpack), ("bias", bias), ("out", out), ("S0", S0), ("z0", z0),
-                            ("S_out", S_out), ("z_out", z_out), ("ws", ws)])
-    q_like = torch.empty((B, H, N, 64), dtype=torch.bfloat16, device=x.device) if out is None else out
-    desc = _desc_from(q_like, grid, frames_per_block, t0, rope, split, base, eps)
-    pdesc = SvaProjDesc(B, N, C, H, 64, int(range_tokens))
-    n = ctypes.c_size_t()
-    _check(lib().sva_proj_lin_attn_fwd_workspace(ctypes.byref(desc), ctypes.byref(pdesc), ctypes.byref(n)),
-           "sva_proj_lin_attn_fwd_workspace")
-    ws = _workspace(n.value, x, ws)
-    st = lib().sva_proj_lin_attn_fwd(ctypes.byref(desc), ctypes.byref(pdesc), _ptr(x), _ptr(wpack), _ptr(bias),
-                                     _ptr(q_like), _ptr(S0), _ptr(z0), _ptr(S_out), _ptr(z_out), _ptr(ws),
-                                     ws.numel() * ws.element_size(), _stream(stream))
-    _check(st, "sva_proj_lin_attn_fwd")
-    return q_like
+    N = T * Hs * Ws
+    _check_w4a4_inputs(xq, wpack, bias, B, N, C, H, 64)
+    return _proj_lin_attn("sva_proj_lin_attn_fwd_w4a4", xq, "xq", wpack, bias, B, N, C, H, grid, frames_per_block,
+                          t0, rope, split, base, eps, S0, z0, S_out, z_out, out, ws, stream, range_tokens)

@@ -140,6 +140,20 @@ sva_status sva_proj_lin_attn_fwd(const sva_desc* attn, const sva_proj_desc* proj
                                  const float* z0, float* S_out, float* z_out, void* ws, size_t ws_bytes,
                                  void* stream);
 
+/* The same pass on 4-bit activations (W4A4, as SVDQuant deploys it: [news],
+ * 4-bit quantization paragraph):
+ *   out = sva_lin_attn_fwd(attn, q, k, v, ...) with (q, k, v) =
+ *         sva_qkv_proj_w4a4(proj, xq, wpack, bias) rounded to bf16,
+ * xq being sva_mxfp4_quant_acts' output for the same proj descriptor
+ * (sva_mxfp4_acts_bytes bytes; xq must not overlap out or the workspace).
+ * k and v never reach memory, as above; limits, range length, workspace
+ * (sva_proj_lin_attn_fwd_workspace with the same descriptors) and errors as
+ * for sva_proj_lin_attn_fwd. */
+sva_status sva_proj_lin_attn_fwd_w4a4(const sva_desc* attn, const sva_proj_desc* proj, const void* xq,
+                                      const void* wpack, const float* bias, void* out, const float* S0,
+                                      const float* z0, float* S_out, float* z_out, void* ws, size_t ws_bytes,
+                                      void* stream);
+
 #ifdef __cplusplus
 }
 #endif

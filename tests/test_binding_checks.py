@@ -144,3 +144,22 @@ def test_projection_checks():
                                   z0=_t(1, H, 63, dtype=torch.float32))
     with pytest.raises(ValueError, match="GPU"):
         sva.sva_proj_lin_attn_fwd(x, wp, None, H, GRID, F)
+
+
+def test_w4a4_checks():
+    H, d, C = 2, 64, 256
+    xq = _t(sva.mxfp4_acts_bytes(N, C), dtype=torch.uint8)
+    wp = _t(sva.mxfp4_packed_bytes(3 * H * d, C), dtype=torch.uint8)
+    with pytest.raises(ValueError, match="bytes"):
+        sva.sva_qkv_proj_w4a4(xq[:-1], wp, None, 1, N, C, H, d)
+    with pytest.raises(ValueError, match="bytes"):
+        sva.sva_qkv_proj_w4a4(xq, wp[:-16], None, 1, N, C, H, d)
+    with pytest.raises(ValueError, match="bytes"):
+        # the grid holds more tokens than xq's rows
+        sva.sva_proj_lin_attn_fwd_w4a4(xq, wp, None, 1, C, H, (GRID[0] + 2, GRID[1], GRID[2]), F)
+    with pytest.raises(ValueError, match="shape"):
+        sva.sva_proj_lin_attn_fwd_w4a4(xq, wp, _t(3 * H * d - 1, dtype=torch.float32), 1, C, H, GRID, F)
+    with pytest.raises(ValueError, match="shape"):
+        sva.sva_proj_lin_attn_fwd_w4a4(xq, wp, None, 1, C, H, GRID, F, out=_t(1, H, N, 32))
+    with pytest.raises(ValueError, match="GPU"):
+        sva.sva_proj_lin_attn_fwd_w4a4(xq, wp, None, 1, C, H, GRID, F)
