@@ -85,6 +85,25 @@ struct KvGeo {
   int tab_entries;  // F dt/2 + Hs dh/2 + Ws dw/2 (the RoPE table's size)
 };
 
+struct QaGeo {
+  int N, C, H;      // tokens per sample, input channels, heads (head dimension 64)
+  int n_pack;       // rows of the packed weights (3 * H * 64)
+  int stages;       // C / kTileK
+  int Nb, nb;       // tokens per block, blocks per sample
+  int tiles_blk;    // 64-token tiles per block (the last one ragged)
+  int tpw;          // tiles per workgroup
+  int groups;       // workgroups per block and head quad: ceil(tiles_blk / tpw)
+  int ngrp;         // B * nb * groups
+  int nquads;       // ceil(H / 4)
+  FastDiv fHW, fWs; // division by Hs * Ws and by Ws
+  int Hs, Ws, t0;   // latent grid rows and columns, first frame
+  int rope, dt, dh; // RoPE on, t and h axis widths (w takes the rest)
+  double log2_base_d;  // log2 of the RoPE base
+  int F;            // frames per block
+  int tab_entries;  // F dt/2 + Hs dh/2 + Ws dw/2
+  float eps;
+};
+
 // LDS RoPE table of the fused k, v kernel: cos/sin of every (axis position,
 // frequency) one workgroup's range can need: [F frames of its block][dt/2],
 // then [Hs][dh/2], then [Ws][dw/2].  Sized so that two workgroups still fit
@@ -550,10 +569,12 @@ static_assert(kKvThreads == kPjThreads, "the GEMM part assumes the projection's 
 // both GEMMs leave a wave's 64 features x 64 tokens in the same accumulator
 // layout, so the epilogue, the state update and the partial are common.
 
-// The LDS RoPE table of block c (see kRopeTab): cos, sin of pos *
+// The LDS RoPE table of block c (see kRopeTab; any geometry with KvGeo's
+// RoPE fields): cos, sin of pos *
 // base^(-2i/width) turns, the angle in fp64 reduced to [-1/2, 1/2] turn,
 // then the hardware sine and cosine (which take turns).
-__device__ __forceinline__ void kv_build_rope_table(float2* rtab, const KvGeo& g, int c, int tid) {
+template <typename Geo>
+__device__ __forceinline__ void kv_build_rope_table(float2* rtab, const Geo& g, int c, int tid) {
   const int ht = g.dt >> 1, hh = g.dh >> 1, hwd = (64 - g.dt - g.dh) >> 1;
   const int off_h = g.F * ht, off_w = off_h + g.Hs * hh;
   for (int e = tid; e < g.tab_entries; e += kKvThreads) {
@@ -1178,6 +1199,319 @@ __global__ __launch_bounds__(kKvThreads, 2) void sva_kv_proj_reduce_w4a4_kernel(
   kv_store_partial(sa, zs[wave >> 1], partials, g, b, head, r, c, half, lg, lr, lane);
 }
 
+// ---------------------------------------------------------------------------
+// The q projection fused with the output pass, on 4-bit activations.
+//
+// A workgroup takes `tpw` consecutive 64-token tiles of one block of one
+// sample and four heads (a quad): wave w computes q of head 4 quad + w (all 64
+// features) with the 4-bit GEMM of the k, v kernel (the x tile in LDS by
+// buffer loads with the lds bit, the weights two stages ahead), and applies
+// the output pass in its epilogue: q (bias included: the accumulators start
+// from it) is rounded to bf16 as a stored tensor would be; phi gives phi q
+// for the RoPE-free denominator and the rotation of its position q~ for the
+// numerator; out = (q~ S_c) / (phi q . Z_c + eps) with the block's prefix
+// state S_c, Z_c from the scan.  The numerator runs on MFMA, transposed
+// (out^T = S_c^T q~^T): the GEMM leaves lane (lg, lr) features 8 lg + 0..7
+// and 32 + 8 lg + 0..7 of token lr -- exactly the B operand of the two
+// k-steps over the 64 q features -- and A holds rows of S_c^T (the scan's
+// bf16 operands, in registers for the whole workgroup), its rows permuted
+// like the projection's so that the lane's outputs are again two runs of 8
+// consecutive features, stored as 16-byte pieces.  The denominator is an
+// fp32 dot on the VALU.  q never reaches HBM; out past the block's last
+// token falls outside the store descriptor and is dropped.
+// ---------------------------------------------------------------------------
+
+// kRope: as for kv_tile_epilogue_rm (0, 1: the LDS table; 2: on the fly).
+template <int kRope>
+__global__ __launch_bounds__(kKvThreads, 2) void sva_q_proj_apply_w4a4_kernel(
+    const uint8_t* __restrict__ xq, const uint8_t* __restrict__ xsc, const uint8_t* __restrict__ wpack,
+    const float* __restrict__ bias, const uint16_t* __restrict__ frags, const float* __restrict__ zc,
+    uint16_t* __restrict__ out, QaGeo g) {
+  __shared__ uint4 xcs[kTileM * kXPitch];
+  __shared__ uint32_t xss[kTileM * kXChunkStages];
+  __shared__ float2 rtab[kRope < 2 ? kRopeTabW4 : 1];
+  __shared__ float bz[kKvThreads / 64][2][64];  // per wave: the head's q bias, then Z_c
+
+  // Tile order: the four head quads of one tile group on one XCD (they read
+  // the same x).
+  const int xcd = blockIdx.x & 7;
+  const int local = blockIdx.x >> 3;
+  const int tg = (local / g.nquads) * 8 + xcd;
+  const int quad = local % g.nquads;
+  if (tg >= g.ngrp) return;
+  const int b = tg / (g.nb * g.groups);
+  const int rem = tg - b * g.nb * g.groups;
+  const int c = rem / g.groups, grp = rem - c * g.groups;
+  const int t_begin = grp * g.tpw, t_end = min(t_begin + g.tpw, g.tiles_blk);
+  const int blk0 = c * g.Nb;               // the block's first token
+  const int n_end = blk0 + g.Nb;
+
+  const int tid = threadIdx.x;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int lane = tid & 63;
+  const int lg = lane >> 4, lr = lane & 15;
+  // With H not a multiple of 4 the last quad's waves past the heads compute
+  // head H - 1 again (every load stays in bounds) and store nothing.
+  const bool live = 4 * quad + wave < g.H;
+  const int head = min(4 * quad + wave, g.H - 1);
+  const uint8_t* cbase = wpack + ((size_t)head * g.stages * 4) * 1024 + lane * 16;
+  const uint8_t* sbase = wpack + (size_t)g.n_pack * (g.C / 2) + ((size_t)head * g.stages * 64 + lane) * 4;
+  const uint32_t crow = (uint32_t)g.C / 2, srow = (uint32_t)g.C / 32;
+  const long long M = (long long)(g.ngrp / (g.nb * g.groups)) * g.N;
+  const int nch = (g.stages + kXChunkStages - 1) / kXChunkStages;
+  const long long bh = (long long)b * g.H + head;
+  const long long bhc = bh * g.nb + c;
+
+  if constexpr (kRope < 2) kv_build_rope_table(rtab, g, c, tid);
+
+  // The block's prefix state for this head: A operands of S_c^T rows
+  // fo(ot, lr) (the projection's row permutation), k-steps of 32 q features;
+  // Z_c at the lane's 16 features.
+  uint4 sA[4][2];
+#pragma unroll
+  for (int ot = 0; ot < 4; ++ot) {
+    const int fo_row = 32 * (ot >> 1) + 8 * (lr >> 2) + 4 * (ot & 1) + (lr & 3);
+#pragma unroll
+    for (int ks = 0; ks < 2; ++ks)
+      sA[ot][ks] = *reinterpret_cast<const uint4*>(frags + (bhc * 64 + fo_row) * 64 + 32 * ks + 8 * lg);
+  }
+  // the head's q bias and Z_c, read per tile from LDS (read first after
+  // the first barrier)
+  bz[wave][0][lane] = bias ? bias[head * 64 + lane] : 0.f;
+  bz[wave][1][lane] = zc[bhc * 64 + lane];
+
+  // The output rows of this head: a store past the block's last token is
+  // outside the descriptor and dropped.
+  const __amdgpu_buffer_rsrc_t orr =
+      rsrc(out + (bh * g.N + blk0) * 64, (uint32_t)g.Nb * 128u);
+
+  // x unit (tile t of the block, chunk j): as in the k, v kernel.
+  constexpr uint32_t kPast = 0x80000000u;
+  auto load_unit = [&](int t, int j) {
+    const long long m0 = (long long)b * g.N + blk0 + (long long)t * kTileM;
+    const int rows = t < t_end ? (int)min((long long)kTileM, M - m0) : 0;
+    const __amdgpu_buffer_rsrc_t cr = rsrc(xq + m0 * crow, (uint32_t)rows * crow);
+    const __amdgpu_buffer_rsrc_t sr = rsrc(xsc + m0 * srow, (uint32_t)rows * srow);
+    const int s0 = j * kXChunkStages;
+    const int ns = min(kXChunkStages, g.stages - s0);
+    int ln = lane;
+    if constexpr (kRope != 0) asm volatile("" : "+v"(ln));
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const int row = 2 * (8 * wave + i) + (ln >> 5);
+      const int piece = (ln & 31) ^ (row & 31);
+      const uint32_t off = piece < 4 * ns ? (uint32_t)row * crow + 64 * s0 + 16 * piece : kPast;
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(cr, (lds_void_ptr)(xcs + 64 * (8 * wave + i)), 16, off, 0, 0, 0);
+    }
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+      const int u = 64 * (2 * wave + i) + ln;
+      const int sl = u % kXChunkStages;
+      const uint32_t off = sl < ns ? (uint32_t)(u / kXChunkStages) * srow + 4 * (s0 + sl) : kPast;
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(sr, (lds_void_ptr)(xss + 64 * (2 * wave + i)), 4, off, 0, 0, 0);
+    }
+  };
+  auto unit_ready = [&]() {
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
+    __syncthreads();
+    asm volatile("" ::: "memory");
+  };
+  auto load_w = [&](WRegs& w, int s) {
+#pragma unroll
+    for (int rt = 0; rt < 4; ++rt) w.c[rt] = *(const uint4*)(cbase + ((size_t)s * 4 + rt) * 1024);
+    w.s = *(const uint32_t*)(sbase + (size_t)s * 256);
+  };
+  const int np = g.stages / 2;
+  auto load_pair = [&](WRegs (&w)[2], int q) {
+    load_w(w[0], 2 * q);
+    load_w(w[1], 2 * q + 1);
+  };
+
+  // RoPE of the lane's 8 pairs: features 8 lg + 2 pp (group 0) and
+  // 32 + 8 lg + 2 pp (group 1), pp = 0..3
+  const int off_h = g.F * (g.dt >> 1), off_w = off_h + g.Hs * (g.dh >> 1);
+  int lgv = lg;
+  if constexpr (kRope != 0) asm volatile("" : "+v"(lgv));
+
+  WRegs P0[2], P1[2];
+  load_pair(P0, 0);
+  load_unit(t_begin, 0);
+  for (int t = t_begin; t < t_end; ++t) {
+    const int n0 = blk0 + t * kTileM;
+    // the accumulators start from the bias: row tile rt, entry i of lane
+    // (lg, .) is feature 32 (rt / 2) + 8 lg + 4 (rt % 2) + i
+    pj_floatx4 acc[4][4];
+#pragma unroll
+    for (int rt = 0; rt < 4; ++rt) {
+      const float4 b4 = *reinterpret_cast<const float4*>(&bz[wave][0][32 * (rt >> 1) + 8 * lg + 4 * (rt & 1)]);
+#pragma unroll
+      for (int tt = 0; tt < 4; ++tt) acc[rt][tt] = pj_floatx4{b4.x, b4.y, b4.z, b4.w};
+    }
+    auto compute = [&](const WRegs& w, int sl) {
+#pragma unroll
+      for (int tt = 0; tt < 4; ++tt) {
+        const int row = tt * 16 + lr;
+        const uint4 bo = xcs[row * kXPitch + ((4 * sl + lg) ^ (row & 31))];
+        const uint32_t sb = (xss[row * kXChunkStages + sl] >> (8 * lg)) & 0xffu;
+        acc[0][tt] = mfma_fp4<0>(w.c[0], w.s, bo, sb, acc[0][tt]);
+        acc[1][tt] = mfma_fp4<1>(w.c[1], w.s, bo, sb, acc[1][tt]);
+        acc[2][tt] = mfma_fp4<2>(w.c[2], w.s, bo, sb, acc[2][tt]);
+        acc[3][tt] = mfma_fp4<3>(w.c[3], w.s, bo, sb, acc[3][tt]);
+      }
+    };
+    for (int j = 0; j < nch; ++j) {
+      if (j > 0) {  // past 1024 channels: the next chunk, once every wave is done with this one
+        __syncthreads();
+        load_unit(t, j);
+      }
+      unit_ready();
+      const int q0 = j * (kXChunkStages / 2);
+      const int nq = min(kXChunkStages, g.stages - 2 * q0) / 2;
+      int ql = 0;
+      for (; ql + 2 <= nq; ql += 2) {
+        const int q = q0 + ql;
+        load_pair(P1, (q + 1) % np);
+        __builtin_amdgcn_sched_barrier(0);
+        compute(P0[0], 2 * ql);
+        compute(P0[1], 2 * ql + 1);
+        __builtin_amdgcn_sched_barrier(0);
+        load_pair(P0, (q + 2) % np);
+        __builtin_amdgcn_sched_barrier(0);
+        compute(P1[0], 2 * ql + 2);
+        compute(P1[1], 2 * ql + 3);
+        __builtin_amdgcn_sched_barrier(0);
+      }
+      if (ql < nq) {
+        load_pair(P1, (q0 + ql + 1) % np);
+        __builtin_amdgcn_sched_barrier(0);
+        compute(P0[0], 2 * ql);
+        compute(P0[1], 2 * ql + 1);
+        __builtin_amdgcn_sched_barrier(0);
+        P0[0] = P1[0];
+        P0[1] = P1[1];
+      }
+    }
+    // Every wave is done with the x buffer: the next tile loads into it
+    // while this one's output pass runs (registers and global memory only,
+    // apart from the RoPE table).
+    asm volatile("" ::: "memory");
+    lds_sync();
+    asm volatile("" ::: "memory");
+    load_unit(t + 1, 0);
+
+    // RoPE constants of the lane's two 8-feature groups
+    float inv[2][4], tbase[2][4];
+    int axis[2][4], eoff[2][4], estr[2][4];
+#pragma unroll
+    for (int gq = 0; gq < 2; ++gq)
+#pragma unroll
+      for (int pp = 0; pp < 4; ++pp) {
+        const int f = 32 * gq + 8 * lgv + 2 * pp;
+        const int ax = f < g.dt ? 0 : f < g.dt + g.dh ? 1 : 2;
+        const int start = ax == 0 ? 0 : ax == 1 ? g.dt : g.dt + g.dh;
+        const int width = ax == 0 ? g.dt : ax == 1 ? g.dh : 64 - g.dt - g.dh;
+        axis[gq][pp] = ax;
+        if constexpr (kRope < 2) {
+          eoff[gq][pp] = (ax == 0 ? 0 : ax == 1 ? off_h : off_w) + ((f - start) >> 1);
+          estr[gq][pp] = width >> 1;
+        } else {
+          const double inv_d = exp2(-(double)(f - start) / (double)width * g.log2_base_d) * 0.15915494309189535;
+          double tb = ax == 0 ? (double)(g.t0 + c * g.F) * inv_d : 0.0;
+          tb -= rint(tb);
+          inv[gq][pp] = (float)inv_d;
+          tbase[gq][pp] = (float)tb;
+        }
+      }
+#pragma unroll
+    for (int tt = 0; tt < 4; ++tt) {
+      const int tok = 16 * tt + lr;
+      const int n = n0 + tok;
+      // q rounded to bf16, then phi on the bit pattern (every value with the
+      // sign bit set becomes +0): features 32 gq + 8 lg + i, i = 0..7, from
+      // accumulators 2 gq + i / 4, entry i % 4
+      float ph[2][8];
+#pragma unroll
+      for (int gq = 0; gq < 2; ++gq)
+#pragma unroll
+        for (int m = 0; m < 4; ++m) {
+          const int rt = 2 * gq + (m >> 1);
+          const uint32_t w = pack2(acc[rt][tt][2 * (m & 1)], acc[rt][tt][2 * (m & 1) + 1]);
+          ph[gq][2 * m] = __int_as_float(max((int)(w << 16), 0));
+          ph[gq][2 * m + 1] = __int_as_float(max((int)(w & 0xffff0000u), 0));
+        }
+      // denominator: phi q . Z_c over the 64 features (16 a lane, then the
+      // four lane groups), fp32
+      float den = 0.f;
+#pragma unroll
+      for (int gq = 0; gq < 2; ++gq) {
+        const float4 z0 = *reinterpret_cast<const float4*>(&bz[wave][1][32 * gq + 8 * lg]);
+        const float4 z1 = *reinterpret_cast<const float4*>(&bz[wave][1][32 * gq + 8 * lg + 4]);
+        const float zz[8] = {z0.x, z0.y, z0.z, z0.w, z1.x, z1.y, z1.z, z1.w};
+#pragma unroll
+        for (int i = 0; i < 8; ++i) den = fmaf(ph[gq][i], zz[i], den);
+      }
+      den += __shfl_xor(den, 16);
+      den += __shfl_xor(den, 32);
+      if (g.rope) {
+        const uint32_t np_ = (uint32_t)min(n, n_end - 1);  // positions past the block: any in it
+        const uint32_t fr = fdiv(np_, g.fHW), rm = np_ - fr * g.fHW.div;
+        const uint32_t row = fdiv(rm, g.fWs);
+        const int pt = (int)fr - c * g.F;
+        const int phh = (int)row, pw = (int)(rm - row * g.fWs.div);
+#pragma unroll
+        for (int gq = 0; gq < 2; ++gq) {
+          const int ps0 = axis[gq][0] == 0 ? pt : axis[gq][0] == 1 ? phh : pw;
+          const int e0 = eoff[gq][0] + ps0 * estr[gq][0];
+#pragma unroll
+          for (int pp = 0; pp < 4; ++pp) {
+            float sn, cs;
+            if constexpr (kRope == 0) {
+              const float2 e = rtab[e0 + pp];
+              cs = e.x, sn = e.y;
+            } else if constexpr (kRope == 1) {
+              const int ax = axis[gq][pp];
+              const int ps = ax == 0 ? pt : ax == 1 ? phh : pw;
+              const float2 e = rtab[eoff[gq][pp] + ps * estr[gq][pp]];
+              cs = e.x, sn = e.y;
+            } else {
+              const int ax = axis[gq][pp];
+              const int ps = ax == 0 ? pt : ax == 1 ? phh : pw;
+              const float turn = __builtin_amdgcn_fractf(tbase[gq][pp] + (float)ps * inv[gq][pp]);
+              sn = __builtin_amdgcn_sinf(turn), cs = __builtin_amdgcn_cosf(turn);
+            }
+            const float x = ph[gq][2 * pp], y = ph[gq][2 * pp + 1];
+            ph[gq][2 * pp] = x * cs - y * sn;
+            ph[gq][2 * pp + 1] = x * sn + y * cs;
+          }
+        }
+      }
+      // numerator: out^T rows fo(ot, .) = sum over the 64 q features
+      const uint4 B0 = make_uint4(pack2(ph[0][0], ph[0][1]), pack2(ph[0][2], ph[0][3]), pack2(ph[0][4], ph[0][5]),
+                                  pack2(ph[0][6], ph[0][7]));
+      const uint4 B1 = make_uint4(pack2(ph[1][0], ph[1][1]), pack2(ph[1][2], ph[1][3]), pack2(ph[1][4], ph[1][5]),
+                                  pack2(ph[1][6], ph[1][7]));
+      pj_floatx4 o[4];
+#pragma unroll
+      for (int ot = 0; ot < 4; ++ot) {
+        o[ot] = mfma(sA[ot][0], B0, pj_floatx4{0.f, 0.f, 0.f, 0.f});
+        o[ot] = mfma(sA[ot][1], B1, o[ot]);
+      }
+      const float r = __builtin_amdgcn_rcpf(den + g.eps);
+      // lane (lg, lr): output features 8 lg + 0..7 (accumulators 0, 1) and
+      // 32 + 8 lg + 0..7 (2, 3) of token lr
+#pragma unroll
+      for (int gq = 0; gq < 2 && live; ++gq) {
+        const pj_floatx4 a0 = o[2 * gq], a1 = o[2 * gq + 1];
+        const uint32_t w4[4] = {pack2(a0[0] * r, a0[1] * r), pack2(a0[2] * r, a0[3] * r),
+                                pack2(a1[0] * r, a1[1] * r), pack2(a1[2] * r, a1[3] * r)};
+        __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(pj_u32x4, make_uint4(w4[0], w4[1], w4[2], w4[3])),
+                                               orr, (uint32_t)(n - blk0) * 128u + 64 * gq + 16 * lg, 0, 0);
+      }
+    }
+  }
+}
+
 // Repacks natural-layout MXFP4 weights (codes [n_out, C/2], scales
 // [n_out, C/32]) into the projection's layout: thread (blk, s, lane) writes
 // the lane's 16 code bytes of each row tile rt of 64-feature block blk and
@@ -1372,6 +1706,67 @@ hipError_t sva_internal_kv_proj_reduce_w4a4(const SvaKvReduceArgs& a, const void
   const void* fn = mode == 0   ? (const void*)&sva_kv_proj_reduce_w4a4_kernel<0>
                    : mode == 1 ? (const void*)&sva_kv_proj_reduce_w4a4_kernel<1>
                                : (const void*)&sva_kv_proj_reduce_w4a4_kernel<2>;
+  return hipLaunchKernel(fn, dim3((unsigned)grid), dim3(kKvThreads), args, 0, stream);
+}
+
+hipError_t sva_internal_q_proj_apply_w4a4(const SvaKvReduceArgs& a, float eps, const void* xq, const void* wpack,
+                                          const float* bias, const void* frags, const float* zc, void* out,
+                                          hipStream_t stream) {
+  if (a.C % (2 * kTileK) != 0 || a.C < 2 * kTileK || a.H < 1 || a.Nb <= 0 || a.N % a.Nb != 0)
+    return hipErrorInvalidValue;
+  QaGeo g;
+  g.N = a.N;
+  g.C = a.C;
+  g.H = a.H;
+  g.n_pack = 3 * a.H * 64;
+  g.stages = a.C / kTileK;
+  g.Nb = a.Nb;
+  g.nb = a.nb;
+  g.tiles_blk = (a.Nb + kTileM - 1) / kTileM;
+  g.nquads = (a.H + 3) / 4;
+  g.fHW = make_fastdiv((uint32_t)(a.Hs * a.Ws));
+  g.fWs = make_fastdiv((uint32_t)a.Ws);
+  g.Hs = a.Hs;
+  g.Ws = a.Ws;
+  g.t0 = a.t0;
+  g.rope = a.rope;
+  g.dt = a.dt;
+  g.dh = a.dh;
+  g.log2_base_d = log2((double)a.rope_base);
+  g.F = a.Nb / (a.Hs * a.Ws);
+  g.tab_entries = g.F * (a.dt / 2) + a.Hs * (a.dh / 2) + a.Ws * ((64 - a.dt - a.dh) / 2);
+  g.eps = eps;
+  const int mode = !a.rope ? 0 : g.tab_entries > kRopeTabW4 ? 2 : (a.dt % 8 == 0 && a.dh % 8 == 0) ? 0 : 1;
+  const void* fn = mode == 0   ? (const void*)&sva_q_proj_apply_w4a4_kernel<0>
+                   : mode == 1 ? (const void*)&sva_q_proj_apply_w4a4_kernel<1>
+                               : (const void*)&sva_q_proj_apply_w4a4_kernel<2>;
+  // Tiles per workgroup: each workgroup pays about one tile's time for its
+  // set-up (the RoPE table, the state operands, the first x tile), and the
+  // workgroups run in rounds of the resident count, so take the tpw with
+  // the fewest rounds x (tpw + 1) tile times.
+  const long long slots = sva_internal_resident_workgroups(fn, kKvThreads, 0);
+  long long best = -1;
+  g.tpw = 1;
+  for (int tpw = 1; tpw <= 32 && tpw <= g.tiles_blk; ++tpw) {
+    const long long groups = (g.tiles_blk + tpw - 1) / tpw;
+    const long long wgs = ((long long)a.B * a.nb * groups + 7) / 8 * 8 * g.nquads;
+    const long long cost = (wgs + slots - 1) / slots * (tpw + 1);
+    if (best < 0 || cost < best) {
+      best = cost;
+      g.tpw = tpw;
+    }
+  }
+  g.groups = (g.tiles_blk + g.tpw - 1) / g.tpw;
+  g.ngrp = a.B * a.nb * g.groups;
+  const long long grid = ((long long)g.ngrp + 7) / 8 * 8 * g.nquads;
+  if (grid >= (1LL << 31)) return hipErrorInvalidValue;
+  const long long M = (long long)a.B * a.N;
+  const uint8_t* codes = (const uint8_t*)xq;
+  const uint8_t* scales = codes + (size_t)M * a.C / 2;
+  const uint8_t* wp = (const uint8_t*)wpack;
+  const uint16_t* fr = (const uint16_t*)frags;
+  uint16_t* op = (uint16_t*)out;
+  void* args[] = {(void*)&codes, (void*)&scales, (void*)&wp, (void*)&bias, (void*)&fr, (void*)&zc, (void*)&op, &g};
   return hipLaunchKernel(fn, dim3((unsigned)grid), dim3(kKvThreads), args, 0, stream);
 }
 

@@ -2680,10 +2680,12 @@ sva_status run_proj_fwd(const sva_desc* a, const sva_proj_desc* pd, const void* 
   void* frags = wsb + pp.off_frags;
   float* zc = (float*)(wsb + pp.off_zc);
   hipStream_t st = (hipStream_t)stream;
-  // q: the projection's first H*d features, into the workspace
-  s = w4a4 ? sva_internal_proj_w4a4_features(pd, x, wpack, bias, pd->H * pd->d, q, q, q, stream)
-           : sva_internal_proj_features(pd, x, wpack, bias, pd->H * pd->d, q, q, q, stream);
-  if (s != SVA_OK) return s;
+  // bf16 activations: q, the projection's first H*d features, into the
+  // workspace (4-bit activations project q inside the output pass below)
+  if (!w4a4) {
+    s = sva_internal_proj_features(pd, x, wpack, bias, pd->H * pd->d, q, q, q, stream);
+    if (s != SVA_OK) return s;
+  }
   SvaKvReduceArgs ka;
   ka.B = pd->B;
   ka.N = pd->N;
@@ -2706,11 +2708,20 @@ sva_status run_proj_fwd(const sva_desc* a, const sva_proj_desc* pd, const void* 
   if (SVA_DISPATCH2(p, launch_scan, p, partials, S0, z0, S_out, z_out, frags, zc, true, st, false, pp.L) !=
       hipSuccess)
     return SVA_ERR_HIP;
-  if (SVA_DISPATCH(p, launch_apply, p, q, out, frags, zc, a->eps, st) != hipSuccess) return SVA_ERR_HIP;
+  if (w4a4) {
+    if (sva_internal_q_proj_apply_w4a4(ka, a->eps, x, wpack, bias, frags, zc, out, st) != hipSuccess)
+      return SVA_ERR_HIP;
+  } else if (SVA_DISPATCH(p, launch_apply, p, q, out, frags, zc, a->eps, st) != hipSuccess) {
+    return SVA_ERR_HIP;
+  }
   return SVA_OK;
 }
 
 }  // namespace
+
+int sva_internal_resident_workgroups(const void* fn, int threads, size_t lds) {
+  return resident_workgroups(fn, threads, lds);
+}
 
 // ---------------------------------------------------------------------------
 // Scratch of sva_block_cache_apply_noalloc

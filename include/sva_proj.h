@@ -146,9 +146,11 @@ sva_status sva_proj_lin_attn_fwd(const sva_desc* attn, const sva_proj_desc* proj
  *         sva_qkv_proj_w4a4(proj, xq, wpack, bias) rounded to bf16,
  * xq being sva_mxfp4_quant_acts' output for the same proj descriptor
  * (sva_mxfp4_acts_bytes bytes; xq must not overlap out or the workspace).
- * k and v never reach memory, as above; limits, range length, workspace
- * (sva_proj_lin_attn_fwd_workspace with the same descriptors) and errors as
- * for sva_proj_lin_attn_fwd. */
+ * k and v never reach memory, as above, and neither does q: it is projected
+ * inside the output pass, per 64-token tile and head, after the block
+ * prefix is known.  Limits, range length and errors as for
+ * sva_proj_lin_attn_fwd; the workspace is sva_proj_lin_attn_fwd_workspace
+ * bytes for the same descriptors (this call leaves its q region unused). */
 sva_status sva_proj_lin_attn_fwd_w4a4(const sva_desc* attn, const sva_proj_desc* proj, const void* xq,
                                       const void* wpack, const float* bias, void* out, const float* S0,
                                       const float* z0, float* S_out, float* z_out, void* ws, size_t ws_bytes,
