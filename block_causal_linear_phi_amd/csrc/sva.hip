@@ -59,7 +59,7 @@ template <bool BF16> constexpr int red_threads() { return BF16 ? 512 : 256; }
 template <bool BF16> constexpr int app_threads() { return 256; }
 template <bool BF16> constexpr int red_min_blocks() { return BF16 ? (512 / red_threads<BF16>() > 0 ? 512 / red_threads<BF16>() : 1) : 1; }
 template <bool BF16> constexpr int app_min_blocks() { return BF16 ? (768 / app_threads<BF16>() > 0 ? 768 / app_threads<BF16>() : 1) : 1; }
-constexpr int kMaxTableEntries = 4096; // RoPE cos/sin table, 32 KiB of LDS
+constexpr int kMaxTableEntries = 3584; // RoPE cos/sin table, 28 KiB of LDS (beside the reduction's 130 KiB)
 
 // ---------------------------------------------------------------------------
 // Small integer helpers
@@ -647,12 +647,10 @@ __global__ __launch_bounds__(red_threads<BF16>(), red_min_blocks<BF16>()) void s
 
   extern __shared__ float4 tab_raw[];  // 16-byte aligned
   float2* tab = reinterpret_cast<float2*>(tab_raw);
-  // Accumulator tiles for the cross-wave sum: one per wave up to four; with
-  // eight waves, waves 4..7 hand theirs to waves 0..3 first.
+  // Accumulator tiles for the cross-wave sum, one per wave (bf16, d = 64:
+  // 128 KiB; the workgroup has the CU to itself).
   constexpr int NWV = RT / 64;
-  constexpr int NT = NWV > 4 ? 4 : NWV;
-  static_assert(NWV == NT || NWV == 2 * NT, "waves per workgroup");
-  __shared__ float red[NT][D * D];
+  __shared__ float red[NWV][D * D];
   __shared__ float zred[NWV][D];
   __shared__ int fold_last;
 
@@ -811,10 +809,10 @@ __global__ __launch_bounds__(red_threads<BF16>(), red_min_blocks<BF16>()) void s
     if (k + 1 < nsteps) compute_step(kB, vB, s_first + (k + 1) * WSTRIDE);
 
     // Fixed-order reduction over the four lane groups (lane swaps), then over
-    // the waves: with eight waves, waves 4..7 store their tiles and waves
-    // 0..3 add them to their own; the (up to) four tiles are stored, one
-    // barrier, and each thread sums them for 4 contiguous elements in wave
-    // order.
+    // the waves: every wave stores its tile, one barrier, and each thread
+    // sums the tiles for 4 contiguous elements in wave order.  (A two-round
+    // tree over half as much LDS -- waves 4..7 handing their tiles to waves
+    // 0..3 -- cost one more barrier and round of LDS traffic.)
 #pragma unroll
     for (int r = 0; r < FPL; ++r) zacc[r] = sum_over_rows(zacc[r]);
     auto tile_elem = [&](int slot, int r, int i) { return red[slot] + (FPL * (4 * tg + i) + r) * D + FPL * cg; };
@@ -828,23 +826,7 @@ __global__ __launch_bounds__(red_threads<BF16>(), red_min_blocks<BF16>()) void s
           for (int s = 0; s < FPL; ++s) dst[s] = acc[r][s][i];
         }
     };
-    if constexpr (NWV > NT) {
-      if (wave >= NT) store_tile(wave - NT);
-      lds_barrier();
-      if (wave < NT) {
-#pragma unroll
-        for (int r = 0; r < FPL; ++r)
-#pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            const float* src = tile_elem(wave, r, i);
-#pragma unroll
-            for (int s = 0; s < FPL; ++s) acc[r][s][i] += src[s];
-          }
-        store_tile(wave);  // each lane rewrites only the elements it read
-      }
-    } else {
-      store_tile(wave);
-    }
+    store_tile(wave);
     if (tg == 0) {
 #pragma unroll
       for (int r = 0; r < FPL; ++r) zred[wave][FPL * cg + r] = zacc[r];
@@ -865,7 +847,7 @@ __global__ __launch_bounds__(red_threads<BF16>(), red_min_blocks<BF16>()) void s
       for (int j = 0; j < 4; ++j) {
         t[j] = red[0][(fi0 + j) * D + fo];
 #pragma unroll
-        for (int w = 1; w < NT; ++w) t[j] += red[w][(fi0 + j) * D + fo];
+        for (int w = 1; w < NWV; ++w) t[j] += red[w][(fi0 + j) * D + fo];
       }
       const uint32_t w4[4] = {__float_as_uint(t[0]), __float_as_uint(t[1]), __float_as_uint(t[2]),
                               __float_as_uint(t[3])};

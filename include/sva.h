@@ -67,7 +67,7 @@ typedef enum sva_status {
   SVA_OK = 0,
   SVA_ERR_INVALID_ARG = -1,  /* null/misaligned pointer, bad shape, overlap */
   SVA_ERR_UNSUPPORTED = -2,  /* d not 32/64, bad RoPE split, grid too large
-                                (with RoPE: F, Hs, Ws <= 1024 and at most 4096
+                                (with RoPE: F, Hs, Ws <= 1024 and at most 3584
                                 cos/sin table entries, F*dt/2 + Hs*dh/2 +
                                 Ws*dw/2) */
   SVA_ERR_WORKSPACE = -3,    /* workspace missing or smaller than required */
