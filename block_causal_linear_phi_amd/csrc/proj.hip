@@ -47,6 +47,7 @@ typedef float pj_floatx4 __attribute__((ext_vector_type(4)));
 typedef uint32_t pj_u32x4 __attribute__((ext_vector_type(4)));
 typedef __bf16 pj_bf16x8 __attribute__((ext_vector_type(8)));
 typedef __bf16 pj_bf16x2 __attribute__((ext_vector_type(2)));
+typedef __attribute__((address_space(3))) void* lds_void_ptr;  // LDS destination of direct loads
 
 constexpr int kPjThreads = 256;  // 4 waves
 constexpr int kTileN = 256;      // output features per workgroup
@@ -426,7 +427,9 @@ __device__ __forceinline__ pj_floatx4 mfma_fp4(const uint4& a, uint32_t sa, cons
 // The workgroup's 64 x-rows of up to kXChunk channels live in LDS: codes at
 // a pitch of 32 16-byte pieces a row, piece p of row r at p ^ (r & 31) (the
 // B reads of one instruction -- 16 rows, 4 pieces each -- fall in distinct
-// bank groups), and one word of four scale bytes per row and stage.
+// bank groups), and one word of four scale bytes per row and stage.  They
+// come straight from global memory (buffer loads with the lds bit), which
+// leaves the registers to the accumulators and weights.
 constexpr int kXChunk = 1024;                 // channels per LDS chunk
 constexpr int kXChunkStages = kXChunk / kTileK;
 constexpr int kXPitch = kXChunk / 32;         // 16-byte pieces per row
@@ -468,6 +471,29 @@ __global__ __launch_bounds__(kPjThreads, 2) void sva_qkv_proj_w4a4_kernel(
     for (int rt = 0; rt < 4; ++rt) w.c[rt] = *(const uint4*)(cbase + ((size_t)s * 4 + rt) * 1024);
     w.s = *(const uint32_t*)(sbase + (size_t)s * 256);
   };
+  // The chunk of x at stage s0 straight into LDS (buffer loads with the lds
+  // bit, as in the fused k, v kernel): load i of wave w fills code slots
+  // 64 (8 w + i) + lane, rows 2 (8 w + i) + lane / 32 at swizzled position
+  // lane % 32; scale load i fills words 64 (2 w + i) + lane.  Pieces and
+  // stages past the chunk get an offset past the descriptor: zeros.
+  constexpr uint32_t kPast = 0x80000000u;
+  auto load_chunk = [&](int s0) {
+    const int ns = min(kXChunkStages, g.stages - s0);
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const int row = 2 * (8 * wave + i) + (lane >> 5);
+      const int piece = (lane & 31) ^ (row & 31);
+      const uint32_t off = piece < 4 * ns ? (uint32_t)row * crow + 64 * s0 + 16 * piece : kPast;
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(xr, (lds_void_ptr)(xcs + 64 * (8 * wave + i)), 16, off, 0, 0, 0);
+    }
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+      const int u = 64 * (2 * wave + i) + lane;
+      const int sl = u % kXChunkStages;
+      const uint32_t off = sl < ns ? (uint32_t)(u / kXChunkStages) * srow + 4 * (s0 + sl) : kPast;
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(sr, (lds_void_ptr)(xss + 64 * (2 * wave + i)), 4, off, 0, 0, 0);
+    }
+  };
 
   pj_floatx4 acc[4][4];
 #pragma unroll
@@ -475,8 +501,8 @@ __global__ __launch_bounds__(kPjThreads, 2) void sva_qkv_proj_w4a4_kernel(
 #pragma unroll
     for (int j = 0; j < 4; ++j) acc[i][j] = pj_floatx4{0.f, 0.f, 0.f, 0.f};
 
-  // One stage (128 channels) from chunk-local stage sl: B operands and
-  // scales from LDS, the weights from registers.
+  // One stage from chunk-local stage sl: B operands and scales from LDS,
+  // the weights from registers.
   auto compute = [&](const WRegs& w, int sl) {
 #pragma unroll
     for (int tt = 0; tt < 4; ++tt) {
@@ -490,32 +516,27 @@ __global__ __launch_bounds__(kPjThreads, 2) void sva_qkv_proj_w4a4_kernel(
     }
   };
 
-  // Weights: two register sets, stage s + 1 loading while stage s computes;
-  // every load is issued, the stage clamped to the last (repeat loads at the
-  // tail are in bounds and unused), so the count of loads in flight is exact.
-  const int last = g.stages - 1;
+  // Weights one stage ahead, two register sets: every load is issued, the
+  // stage clamped to the last (repeat loads at the tail are in bounds and
+  // unused).  (Two stages ahead in a ring of register pairs raised the
+  // registers past three workgroups a CU, and was no faster.)
   WRegs w0, w1;
   load_w(w0, 0);
-  for (int s0 = 0; s0 < g.stages; s0 += kXChunkStages) {
+  load_chunk(0);
+  const int nch = (g.stages + kXChunkStages - 1) / kXChunkStages;
+  const int last = g.stages - 1;
+  for (int j = 0; j < nch; ++j) {
+    if (j > 0) {  // past 1024 channels: the next chunk, once every wave is done with this one
+      __syncthreads();
+      load_chunk(j * kXChunkStages);
+    }
+    // every wave's loads of the chunk have landed: vmcnt(0), then the workgroup meets
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_s_waitcnt(0x0F70);
+    __syncthreads();
+    asm volatile("" ::: "memory");
+    const int s0 = j * kXChunkStages;
     const int ns = min(kXChunkStages, g.stages - s0);
-    // this chunk's x rows into LDS (every wave is past the previous chunk)
-    __syncthreads();
-    const uint32_t pieces = (uint32_t)ns * 4;  // 16-byte pieces a row in this chunk (4 a stage)
-#pragma unroll
-    for (int j = 0; j < kTileM * kXPitch / kPjThreads; ++j) {
-      const int u = tid + j * kPjThreads;
-      const int r = u / kXPitch, pc = u % kXPitch;
-      if ((uint32_t)pc < pieces)
-        xcs[r * kXPitch + (pc ^ (r & 31))] = __builtin_bit_cast(
-            uint4, __builtin_amdgcn_raw_buffer_load_b128(xr, (uint32_t)r * crow + 64 * s0 + 16 * pc, 0, 0));
-    }
-#pragma unroll
-    for (int j = 0; j < kTileM * kXChunkStages / kPjThreads; ++j) {
-      const int u = tid + j * kPjThreads;
-      const int r = u / kXChunkStages, sl = u % kXChunkStages;
-      if (sl < ns) xss[u] = __builtin_amdgcn_raw_buffer_load_b32(sr, (uint32_t)r * srow + 4 * (s0 + sl), 0, 0);
-    }
-    __syncthreads();
     int sl = 0;
     for (; sl + 2 <= ns; sl += 2) {
       load_w(w1, min(s0 + sl + 1, last));
@@ -527,7 +548,7 @@ __global__ __launch_bounds__(kPjThreads, 2) void sva_qkv_proj_w4a4_kernel(
       compute(w1, sl + 1);
       __builtin_amdgcn_sched_barrier(0);
     }
-    if (sl < ns) {
+    if (sl < ns) {  // an odd stage count (C an odd multiple of 128): the last stage
       load_w(w1, min(s0 + sl + 1, last));
       __builtin_amdgcn_sched_barrier(0);
       compute(w0, sl);
@@ -989,8 +1010,6 @@ __global__ __launch_bounds__(kKvThreads, 2) void sva_kv_proj_reduce_kernel(
 // with more than 1024 channels reload the x buffer per chunk, in turn.  The
 // head states stay in registers.
 constexpr int kRopeTabW4 = 1536;  // this kernel's RoPE table: two workgroups a CU with both x and k, v tiles
-
-typedef __attribute__((address_space(3))) void* lds_void_ptr;
 
 // kRope: as for kv_tile_epilogue_rm (0, 1: the LDS table; 2: on the fly).
 template <int kRope>

@@ -46,10 +46,10 @@ CASES = [
     ("long_ranges", 1, 2, (2, 40, 41), 2, 256, (16, 24, 24), 0, True, False),
     # RoPE table (F dt/2 + Hs dh/2 + Ws dw/2 entries) past the kernel's LDS
     # budget: angles on the fly
-    ("wide_rows", 1, 2, (2, 3, 300), 1, 256, (16, 24, 24), 11, True, False),
+    ("wide_rows", 1, 2, (2, 3, 280), 1, 256, (16, 24, 24), 11, True, False),
     # the same on-the-fly angles at a frame index in the hundred thousands
     # (the block's first-frame turn is reduced in fp64)
-    ("wide_rows_far_frames", 1, 2, (2, 3, 300), 1, 256, (16, 24, 24), 123457, True, False),
+    ("wide_rows_far_frames", 1, 2, (2, 3, 280), 1, 256, (16, 24, 24), 123457, True, False),
 ]
 
 

@@ -63,8 +63,8 @@ CASES = [
     ("cache_in_place", 1, 2, (4, 6, 7), 2, 768, (8, 28, 28), 6, True, True),
     ("long_ranges", 1, 2, (2, 40, 41), 2, 256, (16, 24, 24), 0, True, False),
     # RoPE table past the kernel's LDS budget: angles on the fly, near and far frames
-    ("wide_rows", 1, 2, (2, 3, 300), 1, 256, (16, 24, 24), 11, True, False),
-    ("wide_rows_far_frames", 1, 2, (2, 3, 300), 1, 256, (16, 24, 24), 123457, True, False),
+    ("wide_rows", 1, 2, (2, 3, 280), 1, 256, (16, 24, 24), 11, True, False),
+    ("wide_rows_far_frames", 1, 2, (2, 3, 280), 1, 256, (16, 24, 24), 123457, True, False),
     # 1280 channels: a full 1024-channel chunk and a 256-channel one per tile
     ("two_chunks", 1, 2, (3, 6, 11), 3, 1280, (16, 24, 24), 0, True, False),
 ]
