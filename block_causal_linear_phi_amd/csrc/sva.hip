@@ -2037,19 +2037,28 @@ __global__ __launch_bounds__(kThreads, 2) void sva_bwd_kv_kernel(
       btile_store<D>(tv, dvw, dvrs, t, lane);
     };
 
+    // Three register sets in a ring: steps k + 1 and k + 2 in flight while
+    // step k computes.  Loads past the segment read zeros and are not used.
+    uint32_t xc[2][NW];
+    load2(xb, t_first + WSTRIDE);
     int k = 0;
-    for (; k + 2 <= nsteps; k += 2) {
+    for (; k + 3 <= nsteps; k += 3) {
       const int t0 = t_first + k * WSTRIDE;
-      load2(xb, t0 + WSTRIDE);
+      load2(xc, t0 + 2 * WSTRIDE);
       __builtin_amdgcn_sched_barrier(0);
       compute(xa, t0);
       __builtin_amdgcn_sched_barrier(0);
-      load2(xa, t0 + 2 * WSTRIDE);
+      load2(xa, t0 + 3 * WSTRIDE);
       __builtin_amdgcn_sched_barrier(0);
       compute(xb, t0 + WSTRIDE);
       __builtin_amdgcn_sched_barrier(0);
+      load2(xb, t0 + 4 * WSTRIDE);
+      __builtin_amdgcn_sched_barrier(0);
+      compute(xc, t0 + 2 * WSTRIDE);
+      __builtin_amdgcn_sched_barrier(0);
     }
     if (k < nsteps) compute(xa, t_first + k * WSTRIDE);
+    if (k + 1 < nsteps) compute(xb, t_first + (k + 1) * WSTRIDE);
     pos = seg_end;
   } while (pos < g1);
 }
