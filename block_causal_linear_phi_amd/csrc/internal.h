@@ -58,13 +58,14 @@ hipError_t sva_internal_kv_proj_reduce_w4a4(const SvaKvReduceArgs& a, const void
 sva_status sva_internal_proj_features(const sva_proj_desc* desc, const void* x, const void* wpack,
                                       const float* bias, int f_end, void* q, void* k, void* v, void* stream);
 
-// q projected from the 4-bit activations xq and applied in the same pass:
-// out [B, H, N, 64] bf16 = (RoPE(phi q) S_c) / (phi q . Z_c + eps) with the
-// block prefix operands the scan writes (frags: S_c^T [B H nb][64][64] bf16;
-// zc: Z_c [B H nb][64] fp32).  a.L is not used.
-hipError_t sva_internal_q_proj_apply_w4a4(const SvaKvReduceArgs& a, float eps, const void* xq, const void* wpack,
-                                          const float* bias, const void* frags, const float* zc, void* out,
-                                          hipStream_t stream);
+// q projected from the activations (w4a4: the 4-bit xq; else x [B, N, C]
+// bf16) and applied in the same pass: out [B, H, N, 64] bf16 =
+// (RoPE(phi q) S_c) / (phi q . Z_c + eps) with the block prefix operands the
+// scan writes (frags: S_c^T [B H nb][64][64] bf16; zc: Z_c [B H nb][64]
+// fp32).  a.L is not used.
+hipError_t sva_internal_q_proj_apply(const SvaKvReduceArgs& a, float eps, bool w4a4, const void* x,
+                                    const void* wpack, const float* bias, const void* frags, const float* zc,
+                                    void* out, hipStream_t stream);
 
 // Workgroups of kernel fn the current device holds at once (CUs times
 // workgroups per CU), memoised per (device, kernel, dynamic LDS).

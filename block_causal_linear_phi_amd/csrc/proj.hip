@@ -1241,15 +1241,25 @@ __global__ __launch_bounds__(kKvThreads, 2) void sva_kv_proj_reduce_w4a4_kernel(
 // ---------------------------------------------------------------------------
 
 // kRope: as for kv_tile_epilogue_rm (0, 1: the LDS table; 2: on the fly).
-template <int kRope>
-__global__ __launch_bounds__(kKvThreads, 2) void sva_q_proj_apply_w4a4_kernel(
-    const uint8_t* __restrict__ xq, const uint8_t* __restrict__ xsc, const uint8_t* __restrict__ wpack,
+// kW4: 4-bit activations (xin: the codes, xsc: the scales), else bf16
+// activations (xin: x [B, N, C]; xsc unused).
+template <int kRope, bool kW4>
+__global__ __launch_bounds__(kKvThreads, 2) void sva_q_proj_apply_kernel(
+    const void* __restrict__ xin, const uint8_t* __restrict__ xsc, const uint8_t* __restrict__ wpack,
     const float* __restrict__ bias, const uint16_t* __restrict__ frags, const float* __restrict__ zc,
     uint16_t* __restrict__ out, QaGeo g) {
+  // x: a 4-bit tile's codes (one chunk) and scale words, or two 128-channel
+  // bf16 stages of the tile (the same 32 KiB)
   __shared__ uint4 xcs[kTileM * kXPitch];
-  __shared__ uint32_t xss[kTileM * kXChunkStages];
+  __shared__ uint32_t xss[kW4 ? kTileM * kXChunkStages : 1];
+  static_assert(kTileM * kXPitch == 2 * kXU4, "two bf16 stages fill the 4-bit chunk's buffer");
   __shared__ float2 rtab[kRope < 2 ? kRopeTabW4 : 1];
   __shared__ float bz[kKvThreads / 64][2][64];  // per wave: the head's q bias, then Z_c
+  // The S_c^T operands stay in registers for the 4-bit GEMM; the bf16 GEMM
+  // needs those registers, so there they wait in LDS (one uint4 a lane per
+  // output row tile and k-step) and are read per tile.
+  constexpr bool kSaLds = !kW4;
+  __shared__ uint4 sal[kSaLds ? (kKvThreads / 64) * 8 * 64 : 1];
 
   // Tile order: the four head quads of one tile group on one XCD (they read
   // the same x).
@@ -1275,9 +1285,7 @@ __global__ __launch_bounds__(kKvThreads, 2) void sva_q_proj_apply_w4a4_kernel(
   const int head = min(4 * quad + wave, g.H - 1);
   const uint8_t* cbase = wpack + ((size_t)head * g.stages * 4) * 1024 + lane * 16;
   const uint8_t* sbase = wpack + (size_t)g.n_pack * (g.C / 2) + ((size_t)head * g.stages * 64 + lane) * 4;
-  const uint32_t crow = (uint32_t)g.C / 2, srow = (uint32_t)g.C / 32;
   const long long M = (long long)(g.ngrp / (g.nb * g.groups)) * g.N;
-  const int nch = (g.stages + kXChunkStages - 1) / kXChunkStages;
   const long long bh = (long long)b * g.H + head;
   const long long bhc = bh * g.nb + c;
 
@@ -1286,13 +1294,16 @@ __global__ __launch_bounds__(kKvThreads, 2) void sva_q_proj_apply_w4a4_kernel(
   // The block's prefix state for this head: A operands of S_c^T rows
   // fo(ot, lr) (the projection's row permutation), k-steps of 32 q features;
   // Z_c at the lane's 16 features.
-  uint4 sA[4][2];
+  uint4 sA[kSaLds ? 1 : 4][2];
 #pragma unroll
   for (int ot = 0; ot < 4; ++ot) {
     const int fo_row = 32 * (ot >> 1) + 8 * (lr >> 2) + 4 * (ot & 1) + (lr & 3);
 #pragma unroll
-    for (int ks = 0; ks < 2; ++ks)
-      sA[ot][ks] = *reinterpret_cast<const uint4*>(frags + (bhc * 64 + fo_row) * 64 + 32 * ks + 8 * lg);
+    for (int ks = 0; ks < 2; ++ks) {
+      const uint4 v = *reinterpret_cast<const uint4*>(frags + (bhc * 64 + fo_row) * 64 + 32 * ks + 8 * lg);
+      if constexpr (kSaLds) sal[(wave * 8 + 2 * ot + ks) * 64 + lane] = v;
+      else sA[ot][ks] = v;
+    }
   }
   // the head's q bias and Z_c, read per tile from LDS (read first after
   // the first barrier)
@@ -1304,229 +1315,334 @@ __global__ __launch_bounds__(kKvThreads, 2) void sva_q_proj_apply_w4a4_kernel(
   const __amdgpu_buffer_rsrc_t orr =
       rsrc(out + (bh * g.N + blk0) * 64, (uint32_t)g.Nb * 128u);
 
-  // x unit (tile t of the block, chunk j): as in the k, v kernel.
-  constexpr uint32_t kPast = 0x80000000u;
-  auto load_unit = [&](int t, int j) {
-    const long long m0 = (long long)b * g.N + blk0 + (long long)t * kTileM;
-    const int rows = t < t_end ? (int)min((long long)kTileM, M - m0) : 0;
-    const __amdgpu_buffer_rsrc_t cr = rsrc(xq + m0 * crow, (uint32_t)rows * crow);
-    const __amdgpu_buffer_rsrc_t sr = rsrc(xsc + m0 * srow, (uint32_t)rows * srow);
-    const int s0 = j * kXChunkStages;
-    const int ns = min(kXChunkStages, g.stages - s0);
-    int ln = lane;
-    if constexpr (kRope != 0) asm volatile("" : "+v"(ln));
-#pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      const int row = 2 * (8 * wave + i) + (ln >> 5);
-      const int piece = (ln & 31) ^ (row & 31);
-      const uint32_t off = piece < 4 * ns ? (uint32_t)row * crow + 64 * s0 + 16 * piece : kPast;
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(cr, (lds_void_ptr)(xcs + 64 * (8 * wave + i)), 16, off, 0, 0, 0);
-    }
-#pragma unroll
-    for (int i = 0; i < 2; ++i) {
-      const int u = 64 * (2 * wave + i) + ln;
-      const int sl = u % kXChunkStages;
-      const uint32_t off = sl < ns ? (uint32_t)(u / kXChunkStages) * srow + 4 * (s0 + sl) : kPast;
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(sr, (lds_void_ptr)(xss + 64 * (2 * wave + i)), 4, off, 0, 0, 0);
-    }
-  };
-  auto unit_ready = [&]() {
-    asm volatile("" ::: "memory");
-    __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
-    __syncthreads();
-    asm volatile("" ::: "memory");
-  };
-  auto load_w = [&](WRegs& w, int s) {
-#pragma unroll
-    for (int rt = 0; rt < 4; ++rt) w.c[rt] = *(const uint4*)(cbase + ((size_t)s * 4 + rt) * 1024);
-    w.s = *(const uint32_t*)(sbase + (size_t)s * 256);
-  };
-  const int np = g.stages / 2;
-  auto load_pair = [&](WRegs (&w)[2], int q) {
-    load_w(w[0], 2 * q);
-    load_w(w[1], 2 * q + 1);
-  };
-
   // RoPE of the lane's 8 pairs: features 8 lg + 2 pp (group 0) and
   // 32 + 8 lg + 2 pp (group 1), pp = 0..3
   const int off_h = g.F * (g.dt >> 1), off_w = off_h + g.Hs * (g.dh >> 1);
   int lgv = lg;
   if constexpr (kRope != 0) asm volatile("" : "+v"(lgv));
 
-  WRegs P0[2], P1[2];
-  load_pair(P0, 0);
-  load_unit(t_begin, 0);
-  for (int t = t_begin; t < t_end; ++t) {
-    const int n0 = blk0 + t * kTileM;
-    // the accumulators start from the bias: row tile rt, entry i of lane
-    // (lg, .) is feature 32 (rt / 2) + 8 lg + 4 (rt % 2) + i
-    pj_floatx4 acc[4][4];
+  auto load_w = [&](WRegs& w, int s) {
 #pragma unroll
-    for (int rt = 0; rt < 4; ++rt) {
-      const float4 b4 = *reinterpret_cast<const float4*>(&bz[wave][0][32 * (rt >> 1) + 8 * lg + 4 * (rt & 1)]);
-#pragma unroll
-      for (int tt = 0; tt < 4; ++tt) acc[rt][tt] = pj_floatx4{b4.x, b4.y, b4.z, b4.w};
-    }
-    auto compute = [&](const WRegs& w, int sl) {
-#pragma unroll
-      for (int tt = 0; tt < 4; ++tt) {
-        const int row = tt * 16 + lr;
-        const uint4 bo = xcs[row * kXPitch + ((4 * sl + lg) ^ (row & 31))];
-        const uint32_t sb = (xss[row * kXChunkStages + sl] >> (8 * lg)) & 0xffu;
-        acc[0][tt] = mfma_fp4<0>(w.c[0], w.s, bo, sb, acc[0][tt]);
-        acc[1][tt] = mfma_fp4<1>(w.c[1], w.s, bo, sb, acc[1][tt]);
-        acc[2][tt] = mfma_fp4<2>(w.c[2], w.s, bo, sb, acc[2][tt]);
-        acc[3][tt] = mfma_fp4<3>(w.c[3], w.s, bo, sb, acc[3][tt]);
-      }
-    };
-    for (int j = 0; j < nch; ++j) {
-      if (j > 0) {  // past 1024 channels: the next chunk, once every wave is done with this one
-        __syncthreads();
-        load_unit(t, j);
-      }
-      unit_ready();
-      const int q0 = j * (kXChunkStages / 2);
-      const int nq = min(kXChunkStages, g.stages - 2 * q0) / 2;
-      int ql = 0;
-      for (; ql + 2 <= nq; ql += 2) {
-        const int q = q0 + ql;
-        load_pair(P1, (q + 1) % np);
-        __builtin_amdgcn_sched_barrier(0);
-        compute(P0[0], 2 * ql);
-        compute(P0[1], 2 * ql + 1);
-        __builtin_amdgcn_sched_barrier(0);
-        load_pair(P0, (q + 2) % np);
-        __builtin_amdgcn_sched_barrier(0);
-        compute(P1[0], 2 * ql + 2);
-        compute(P1[1], 2 * ql + 3);
-        __builtin_amdgcn_sched_barrier(0);
-      }
-      if (ql < nq) {
-        load_pair(P1, (q0 + ql + 1) % np);
-        __builtin_amdgcn_sched_barrier(0);
-        compute(P0[0], 2 * ql);
-        compute(P0[1], 2 * ql + 1);
-        __builtin_amdgcn_sched_barrier(0);
-        P0[0] = P1[0];
-        P0[1] = P1[1];
-      }
-    }
-    // Every wave is done with the x buffer: the next tile loads into it
-    // while this one's output pass runs (registers and global memory only,
-    // apart from the RoPE table).
-    asm volatile("" ::: "memory");
-    lds_sync();
-    asm volatile("" ::: "memory");
-    load_unit(t + 1, 0);
-
-    // RoPE constants of the lane's two 8-feature groups
-    float inv[2][4], tbase[2][4];
-    int axis[2][4], eoff[2][4], estr[2][4];
-#pragma unroll
-    for (int gq = 0; gq < 2; ++gq)
-#pragma unroll
-      for (int pp = 0; pp < 4; ++pp) {
-        const int f = 32 * gq + 8 * lgv + 2 * pp;
-        const int ax = f < g.dt ? 0 : f < g.dt + g.dh ? 1 : 2;
-        const int start = ax == 0 ? 0 : ax == 1 ? g.dt : g.dt + g.dh;
-        const int width = ax == 0 ? g.dt : ax == 1 ? g.dh : 64 - g.dt - g.dh;
-        axis[gq][pp] = ax;
-        if constexpr (kRope < 2) {
-          eoff[gq][pp] = (ax == 0 ? 0 : ax == 1 ? off_h : off_w) + ((f - start) >> 1);
-          estr[gq][pp] = width >> 1;
-        } else {
-          const double inv_d = exp2(-(double)(f - start) / (double)width * g.log2_base_d) * 0.15915494309189535;
-          double tb = ax == 0 ? (double)(g.t0 + c * g.F) * inv_d : 0.0;
-          tb -= rint(tb);
-          inv[gq][pp] = (float)inv_d;
-          tbase[gq][pp] = (float)tb;
-        }
-      }
-#pragma unroll
-    for (int tt = 0; tt < 4; ++tt) {
-      const int tok = 16 * tt + lr;
-      const int n = n0 + tok;
-      // q rounded to bf16, then phi on the bit pattern (every value with the
-      // sign bit set becomes +0): features 32 gq + 8 lg + i, i = 0..7, from
-      // accumulators 2 gq + i / 4, entry i % 4
-      float ph[2][8];
-#pragma unroll
+    for (int rt = 0; rt < 4; ++rt) w.c[rt] = *(const uint4*)(cbase + ((size_t)s * 4 + rt) * 1024);
+    w.s = *(const uint32_t*)(sbase + (size_t)s * 256);
+  };
+  // The output pass of tile n0 .. n0 + 63 from the GEMM's accumulators.
+  auto output_pass = [&](const pj_floatx4 (&acc)[4][4], int n0) {
+      // RoPE constants of the lane's two 8-feature groups
+      float inv[2][4], tbase[2][4];
+      int axis[2][4], eoff[2][4], estr[2][4];
+  #pragma unroll
       for (int gq = 0; gq < 2; ++gq)
-#pragma unroll
-        for (int m = 0; m < 4; ++m) {
-          const int rt = 2 * gq + (m >> 1);
-          const uint32_t w = pack2(acc[rt][tt][2 * (m & 1)], acc[rt][tt][2 * (m & 1) + 1]);
-          ph[gq][2 * m] = __int_as_float(max((int)(w << 16), 0));
-          ph[gq][2 * m + 1] = __int_as_float(max((int)(w & 0xffff0000u), 0));
-        }
-      // denominator: phi q . Z_c over the 64 features (16 a lane, then the
-      // four lane groups), fp32
-      float den = 0.f;
-#pragma unroll
-      for (int gq = 0; gq < 2; ++gq) {
-        const float4 z0 = *reinterpret_cast<const float4*>(&bz[wave][1][32 * gq + 8 * lg]);
-        const float4 z1 = *reinterpret_cast<const float4*>(&bz[wave][1][32 * gq + 8 * lg + 4]);
-        const float zz[8] = {z0.x, z0.y, z0.z, z0.w, z1.x, z1.y, z1.z, z1.w};
-#pragma unroll
-        for (int i = 0; i < 8; ++i) den = fmaf(ph[gq][i], zz[i], den);
-      }
-      den += __shfl_xor(den, 16);
-      den += __shfl_xor(den, 32);
-      if (g.rope) {
-        const uint32_t np_ = (uint32_t)min(n, n_end - 1);  // positions past the block: any in it
-        const uint32_t fr = fdiv(np_, g.fHW), rm = np_ - fr * g.fHW.div;
-        const uint32_t row = fdiv(rm, g.fWs);
-        const int pt = (int)fr - c * g.F;
-        const int phh = (int)row, pw = (int)(rm - row * g.fWs.div);
-#pragma unroll
-        for (int gq = 0; gq < 2; ++gq) {
-          const int ps0 = axis[gq][0] == 0 ? pt : axis[gq][0] == 1 ? phh : pw;
-          const int e0 = eoff[gq][0] + ps0 * estr[gq][0];
-#pragma unroll
-          for (int pp = 0; pp < 4; ++pp) {
-            float sn, cs;
-            if constexpr (kRope == 0) {
-              const float2 e = rtab[e0 + pp];
-              cs = e.x, sn = e.y;
-            } else if constexpr (kRope == 1) {
-              const int ax = axis[gq][pp];
-              const int ps = ax == 0 ? pt : ax == 1 ? phh : pw;
-              const float2 e = rtab[eoff[gq][pp] + ps * estr[gq][pp]];
-              cs = e.x, sn = e.y;
-            } else {
-              const int ax = axis[gq][pp];
-              const int ps = ax == 0 ? pt : ax == 1 ? phh : pw;
-              const float turn = __builtin_amdgcn_fractf(tbase[gq][pp] + (float)ps * inv[gq][pp]);
-              sn = __builtin_amdgcn_sinf(turn), cs = __builtin_amdgcn_cosf(turn);
-            }
-            const float x = ph[gq][2 * pp], y = ph[gq][2 * pp + 1];
-            ph[gq][2 * pp] = x * cs - y * sn;
-            ph[gq][2 * pp + 1] = x * sn + y * cs;
+  #pragma unroll
+        for (int pp = 0; pp < 4; ++pp) {
+          const int f = 32 * gq + 8 * lgv + 2 * pp;
+          const int ax = f < g.dt ? 0 : f < g.dt + g.dh ? 1 : 2;
+          const int start = ax == 0 ? 0 : ax == 1 ? g.dt : g.dt + g.dh;
+          const int width = ax == 0 ? g.dt : ax == 1 ? g.dh : 64 - g.dt - g.dh;
+          axis[gq][pp] = ax;
+          if constexpr (kRope < 2) {
+            eoff[gq][pp] = (ax == 0 ? 0 : ax == 1 ? off_h : off_w) + ((f - start) >> 1);
+            estr[gq][pp] = width >> 1;
+          } else {
+            const double inv_d = exp2(-(double)(f - start) / (double)width * g.log2_base_d) * 0.15915494309189535;
+            double tb = ax == 0 ? (double)(g.t0 + c * g.F) * inv_d : 0.0;
+            tb -= rint(tb);
+            inv[gq][pp] = (float)inv_d;
+            tbase[gq][pp] = (float)tb;
           }
         }
+  #pragma unroll
+      for (int tt = 0; tt < 4; ++tt) {
+        const int tok = 16 * tt + lr;
+        const int n = n0 + tok;
+        // q rounded to bf16, then phi on the bit pattern (every value with the
+        // sign bit set becomes +0): features 32 gq + 8 lg + i, i = 0..7, from
+        // accumulators 2 gq + i / 4, entry i % 4
+        float ph[2][8];
+  #pragma unroll
+        for (int gq = 0; gq < 2; ++gq)
+  #pragma unroll
+          for (int m = 0; m < 4; ++m) {
+            const int rt = 2 * gq + (m >> 1);
+            const uint32_t w = pack2(acc[rt][tt][2 * (m & 1)], acc[rt][tt][2 * (m & 1) + 1]);
+            ph[gq][2 * m] = __int_as_float(max((int)(w << 16), 0));
+            ph[gq][2 * m + 1] = __int_as_float(max((int)(w & 0xffff0000u), 0));
+          }
+        // denominator: phi q . Z_c over the 64 features (16 a lane, then the
+        // four lane groups), fp32
+        float den = 0.f;
+  #pragma unroll
+        for (int gq = 0; gq < 2; ++gq) {
+          const float4 z0 = *reinterpret_cast<const float4*>(&bz[wave][1][32 * gq + 8 * lg]);
+          const float4 z1 = *reinterpret_cast<const float4*>(&bz[wave][1][32 * gq + 8 * lg + 4]);
+          const float zz[8] = {z0.x, z0.y, z0.z, z0.w, z1.x, z1.y, z1.z, z1.w};
+  #pragma unroll
+          for (int i = 0; i < 8; ++i) den = fmaf(ph[gq][i], zz[i], den);
+        }
+        den += __shfl_xor(den, 16);
+        den += __shfl_xor(den, 32);
+        if (g.rope) {
+          const uint32_t np_ = (uint32_t)min(n, n_end - 1);  // positions past the block: any in it
+          const uint32_t fr = fdiv(np_, g.fHW), rm = np_ - fr * g.fHW.div;
+          const uint32_t row = fdiv(rm, g.fWs);
+          const int pt = (int)fr - c * g.F;
+          const int phh = (int)row, pw = (int)(rm - row * g.fWs.div);
+  #pragma unroll
+          for (int gq = 0; gq < 2; ++gq) {
+            const int ps0 = axis[gq][0] == 0 ? pt : axis[gq][0] == 1 ? phh : pw;
+            const int e0 = eoff[gq][0] + ps0 * estr[gq][0];
+  #pragma unroll
+            for (int pp = 0; pp < 4; ++pp) {
+              float sn, cs;
+              if constexpr (kRope == 0) {
+                const float2 e = rtab[e0 + pp];
+                cs = e.x, sn = e.y;
+              } else if constexpr (kRope == 1) {
+                const int ax = axis[gq][pp];
+                const int ps = ax == 0 ? pt : ax == 1 ? phh : pw;
+                const float2 e = rtab[eoff[gq][pp] + ps * estr[gq][pp]];
+                cs = e.x, sn = e.y;
+              } else {
+                const int ax = axis[gq][pp];
+                const int ps = ax == 0 ? pt : ax == 1 ? phh : pw;
+                const float turn = __builtin_amdgcn_fractf(tbase[gq][pp] + (float)ps * inv[gq][pp]);
+                sn = __builtin_amdgcn_sinf(turn), cs = __builtin_amdgcn_cosf(turn);
+              }
+              const float x = ph[gq][2 * pp], y = ph[gq][2 * pp + 1];
+              ph[gq][2 * pp] = x * cs - y * sn;
+              ph[gq][2 * pp + 1] = x * sn + y * cs;
+            }
+          }
+        }
+        // numerator: out^T rows fo(ot, .) = sum over the 64 q features
+        const uint4 B0 = make_uint4(pack2(ph[0][0], ph[0][1]), pack2(ph[0][2], ph[0][3]), pack2(ph[0][4], ph[0][5]),
+                                    pack2(ph[0][6], ph[0][7]));
+        const uint4 B1 = make_uint4(pack2(ph[1][0], ph[1][1]), pack2(ph[1][2], ph[1][3]), pack2(ph[1][4], ph[1][5]),
+                                    pack2(ph[1][6], ph[1][7]));
+        pj_floatx4 o[4];
+  #pragma unroll
+        for (int ot = 0; ot < 4; ++ot) {
+          uint4 a0, a1;
+          if constexpr (kSaLds) {
+            a0 = sal[(wave * 8 + 2 * ot) * 64 + lane];
+            a1 = sal[(wave * 8 + 2 * ot + 1) * 64 + lane];
+          } else {
+            a0 = sA[ot][0];
+            a1 = sA[ot][1];
+          }
+          o[ot] = mfma(a0, B0, pj_floatx4{0.f, 0.f, 0.f, 0.f});
+          o[ot] = mfma(a1, B1, o[ot]);
+        }
+        const float r = __builtin_amdgcn_rcpf(den + g.eps);
+        // lane (lg, lr): output features 8 lg + 0..7 (accumulators 0, 1) and
+        // 32 + 8 lg + 0..7 (2, 3) of token lr
+  #pragma unroll
+        for (int gq = 0; gq < 2 && live; ++gq) {
+          const pj_floatx4 a0 = o[2 * gq], a1 = o[2 * gq + 1];
+          const uint32_t w4[4] = {pack2(a0[0] * r, a0[1] * r), pack2(a0[2] * r, a0[3] * r),
+                                  pack2(a1[0] * r, a1[1] * r), pack2(a1[2] * r, a1[3] * r)};
+          __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(pj_u32x4, make_uint4(w4[0], w4[1], w4[2], w4[3])),
+                                                 orr, (uint32_t)(n - blk0) * 128u + 64 * gq + 16 * lg, 0, 0);
+        }
       }
-      // numerator: out^T rows fo(ot, .) = sum over the 64 q features
-      const uint4 B0 = make_uint4(pack2(ph[0][0], ph[0][1]), pack2(ph[0][2], ph[0][3]), pack2(ph[0][4], ph[0][5]),
-                                  pack2(ph[0][6], ph[0][7]));
-      const uint4 B1 = make_uint4(pack2(ph[1][0], ph[1][1]), pack2(ph[1][2], ph[1][3]), pack2(ph[1][4], ph[1][5]),
-                                  pack2(ph[1][6], ph[1][7]));
-      pj_floatx4 o[4];
-#pragma unroll
-      for (int ot = 0; ot < 4; ++ot) {
-        o[ot] = mfma(sA[ot][0], B0, pj_floatx4{0.f, 0.f, 0.f, 0.f});
-        o[ot] = mfma(sA[ot][1], B1, o[ot]);
+  };
+
+  if constexpr (kW4) {
+    // x unit (tile t of the block, chunk j): as in the k, v kernel.
+    const uint8_t* const xq = (const uint8_t*)xin;
+    const uint32_t crow = (uint32_t)g.C / 2, srow = (uint32_t)g.C / 32;
+    const int nch = (g.stages + kXChunkStages - 1) / kXChunkStages;
+    constexpr uint32_t kPast = 0x80000000u;
+    auto load_unit = [&](int t, int j) {
+      const long long m0 = (long long)b * g.N + blk0 + (long long)t * kTileM;
+      const int rows = t < t_end ? (int)min((long long)kTileM, M - m0) : 0;
+      const __amdgpu_buffer_rsrc_t cr = rsrc(xq + m0 * crow, (uint32_t)rows * crow);
+      const __amdgpu_buffer_rsrc_t sr = rsrc(xsc + m0 * srow, (uint32_t)rows * srow);
+      const int s0 = j * kXChunkStages;
+      const int ns = min(kXChunkStages, g.stages - s0);
+      int ln = lane;
+      if constexpr (kRope != 0) asm volatile("" : "+v"(ln));
+  #pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        const int row = 2 * (8 * wave + i) + (ln >> 5);
+        const int piece = (ln & 31) ^ (row & 31);
+        const uint32_t off = piece < 4 * ns ? (uint32_t)row * crow + 64 * s0 + 16 * piece : kPast;
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(cr, (lds_void_ptr)(xcs + 64 * (8 * wave + i)), 16, off, 0, 0, 0);
       }
-      const float r = __builtin_amdgcn_rcpf(den + g.eps);
-      // lane (lg, lr): output features 8 lg + 0..7 (accumulators 0, 1) and
-      // 32 + 8 lg + 0..7 (2, 3) of token lr
-#pragma unroll
-      for (int gq = 0; gq < 2 && live; ++gq) {
-        const pj_floatx4 a0 = o[2 * gq], a1 = o[2 * gq + 1];
-        const uint32_t w4[4] = {pack2(a0[0] * r, a0[1] * r), pack2(a0[2] * r, a0[3] * r),
-                                pack2(a1[0] * r, a1[1] * r), pack2(a1[2] * r, a1[3] * r)};
-        __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(pj_u32x4, make_uint4(w4[0], w4[1], w4[2], w4[3])),
-                                               orr, (uint32_t)(n - blk0) * 128u + 64 * gq + 16 * lg, 0, 0);
+  #pragma unroll
+      for (int i = 0; i < 2; ++i) {
+        const int u = 64 * (2 * wave + i) + ln;
+        const int sl = u % kXChunkStages;
+        const uint32_t off = sl < ns ? (uint32_t)(u / kXChunkStages) * srow + 4 * (s0 + sl) : kPast;
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(sr, (lds_void_ptr)(xss + 64 * (2 * wave + i)), 4, off, 0, 0, 0);
       }
+    };
+    auto unit_ready = [&]() {
+      asm volatile("" ::: "memory");
+      __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
+      __syncthreads();
+      asm volatile("" ::: "memory");
+    };
+    const int np = g.stages / 2;
+    auto load_pair = [&](WRegs (&w)[2], int q) {
+      load_w(w[0], 2 * q);
+      load_w(w[1], 2 * q + 1);
+    };
+
+    WRegs P0[2], P1[2];
+    load_pair(P0, 0);
+    load_unit(t_begin, 0);
+    for (int t = t_begin; t < t_end; ++t) {
+      const int n0 = blk0 + t * kTileM;
+      // the accumulators start from the bias: row tile rt, entry i of lane
+      // (lg, .) is feature 32 (rt / 2) + 8 lg + 4 (rt % 2) + i
+      pj_floatx4 acc[4][4];
+  #pragma unroll
+      for (int rt = 0; rt < 4; ++rt) {
+        const float4 b4 = *reinterpret_cast<const float4*>(&bz[wave][0][32 * (rt >> 1) + 8 * lg + 4 * (rt & 1)]);
+  #pragma unroll
+        for (int tt = 0; tt < 4; ++tt) acc[rt][tt] = pj_floatx4{b4.x, b4.y, b4.z, b4.w};
+      }
+      auto compute = [&](const WRegs& w, int sl) {
+  #pragma unroll
+        for (int tt = 0; tt < 4; ++tt) {
+          const int row = tt * 16 + lr;
+          const uint4 bo = xcs[row * kXPitch + ((4 * sl + lg) ^ (row & 31))];
+          const uint32_t sb = (xss[row * kXChunkStages + sl] >> (8 * lg)) & 0xffu;
+          acc[0][tt] = mfma_fp4<0>(w.c[0], w.s, bo, sb, acc[0][tt]);
+          acc[1][tt] = mfma_fp4<1>(w.c[1], w.s, bo, sb, acc[1][tt]);
+          acc[2][tt] = mfma_fp4<2>(w.c[2], w.s, bo, sb, acc[2][tt]);
+          acc[3][tt] = mfma_fp4<3>(w.c[3], w.s, bo, sb, acc[3][tt]);
+        }
+      };
+      for (int j = 0; j < nch; ++j) {
+        if (j > 0) {  // past 1024 channels: the next chunk, once every wave is done with this one
+          __syncthreads();
+          load_unit(t, j);
+        }
+        unit_ready();
+        const int q0 = j * (kXChunkStages / 2);
+        const int nq = min(kXChunkStages, g.stages - 2 * q0) / 2;
+        int ql = 0;
+        for (; ql + 2 <= nq; ql += 2) {
+          const int q = q0 + ql;
+          load_pair(P1, (q + 1) % np);
+          __builtin_amdgcn_sched_barrier(0);
+          compute(P0[0], 2 * ql);
+          compute(P0[1], 2 * ql + 1);
+          __builtin_amdgcn_sched_barrier(0);
+          load_pair(P0, (q + 2) % np);
+          __builtin_amdgcn_sched_barrier(0);
+          compute(P1[0], 2 * ql + 2);
+          compute(P1[1], 2 * ql + 3);
+          __builtin_amdgcn_sched_barrier(0);
+        }
+        if (ql < nq) {
+          load_pair(P1, (q0 + ql + 1) % np);
+          __builtin_amdgcn_sched_barrier(0);
+          compute(P0[0], 2 * ql);
+          compute(P0[1], 2 * ql + 1);
+          __builtin_amdgcn_sched_barrier(0);
+          P0[0] = P1[0];
+          P0[1] = P1[1];
+        }
+      }
+      // Every wave is done with the x buffer: the next tile loads into it
+      // while this one's output pass runs (registers and global memory only,
+      // apart from the RoPE table).
+      asm volatile("" ::: "memory");
+      lds_sync();
+      asm volatile("" ::: "memory");
+      load_unit(t + 1, 0);
+
+      output_pass(acc, n0);
+    }
+  } else {
+    // bf16 activations: the W4A16 projection's GEMM per tile (x stages
+    // through registers into the two LDS buffers, the weights decoded per
+    // k-step one stage ahead), its pipeline restarted per tile.
+    const size_t row_bytes = (size_t)g.C * 2;
+    const int last = g.stages - 1;
+    for (int t = t_begin; t < t_end; ++t) {
+      const int n0 = blk0 + t * kTileM;
+      const long long m0 = (long long)b * g.N + n0;
+      const int rows = (int)min((long long)kTileM, M - m0);
+      const __amdgpu_buffer_rsrc_t xr = rsrc((const char*)xin + m0 * row_bytes, (uint32_t)(rows * row_bytes));
+      auto load_x = [&](uint4 (&r)[kXLoads], int s) {
+        const int k0 = s * kTileK;
+  #pragma unroll
+        for (int j = 0; j < kXLoads; ++j) {
+          const int u = tid + j * kKvThreads;
+          const uint32_t off = (uint32_t)((u / kPieces) * row_bytes + (size_t)k0 * 2 + 16 * (u % kPieces));
+          r[j] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(xr, off, 0, 0));
+        }
+      };
+      auto store_x = [&](const uint4 (&r)[kXLoads], int buf) {
+  #pragma unroll
+        for (int j = 0; j < kXLoads; ++j) {
+          const int u = tid + j * kKvThreads;
+          xcs[buf * kXU4 + sw(u / kPieces, u % kPieces)] = r[j];
+        }
+      };
+      // the accumulators start from the bias: row tile rt, entry i of lane
+      // (lg, .) is feature 32 (rt / 2) + 8 lg + 4 (rt % 2) + i
+      pj_floatx4 acc[4][4];
+  #pragma unroll
+      for (int rt = 0; rt < 4; ++rt) {
+        const float4 b4 = *reinterpret_cast<const float4*>(&bz[wave][0][32 * (rt >> 1) + 8 * lg + 4 * (rt & 1)]);
+  #pragma unroll
+        for (int tt = 0; tt < 4; ++tt) acc[rt][tt] = pj_floatx4{b4.x, b4.y, b4.z, b4.w};
+      }
+      auto compute = [&](const WRegs& w, int buf) {
+        uint32_t e = w.s;
+        asm volatile("" : "+v"(e));  // see the projection kernel
+        float sc[4];
+  #pragma unroll
+        for (int rt = 0; rt < 4; ++rt) sc[rt] = e8m0_scale((e >> (8 * rt)) & 0xffu);
+  #pragma unroll
+        for (int j = 0; j < kTileK / 32; ++j) {
+          uint4 a[4], bo[4];
+  #pragma unroll
+          for (int rt = 0; rt < 4; ++rt) {
+            const uint32_t cw = j == 0 ? w.c[rt].x : j == 1 ? w.c[rt].y : j == 2 ? w.c[rt].z : w.c[rt].w;
+            a[rt] = decode8(cw, sc[rt]);
+          }
+  #pragma unroll
+          for (int tt = 0; tt < 4; ++tt) bo[tt] = xcs[buf * kXU4 + sw(tt * 16 + lr, 4 * lg + j)];
+  #pragma unroll
+          for (int rt = 0; rt < 4; ++rt)
+  #pragma unroll
+            for (int tt = 0; tt < 4; ++tt) acc[rt][tt] = mfma(a[rt], bo[tt], acc[rt][tt]);
+        }
+      };
+      // the projection kernel's pipeline: stage s from LDS buffer s % 2, stage
+      // s + 1's x in registers, stage s + 2's x in flight, stage s + 1's
+      // weights requested before stage s's MFMAs
+      uint4 x0[kXLoads], x1[kXLoads];
+      WRegs w0, w1;
+      load_w(w0, 0);
+      load_x(x0, 0);
+      load_x(x1, min(1, last));
+      store_x(x0, 0);
+      load_x(x0, min(2, last));
+      __syncthreads();
+      auto step = [&](int st, const WRegs& wc, WRegs& wn_, uint4 (&xn)[kXLoads]) {
+        load_w(wn_, min(st + 1, last));
+        __builtin_amdgcn_sched_barrier(0);
+        compute(wc, st & 1);
+        __builtin_amdgcn_sched_barrier(0);
+        if (st + 1 < g.stages) store_x(xn, (st + 1) & 1);
+        __builtin_amdgcn_sched_barrier(0);
+        load_x(xn, min(st + 3, last));
+        __syncthreads();
+      };
+      int st = 0;
+      for (; st + 2 <= g.stages; st += 2) {
+        step(st, w0, w1, x1);
+        step(st + 1, w1, w0, x0);
+      }
+      if (st < g.stages) step(st, w0, w1, x1);
+      output_pass(acc, n0);
     }
   }
 }
@@ -1728,9 +1844,9 @@ hipError_t sva_internal_kv_proj_reduce_w4a4(const SvaKvReduceArgs& a, const void
   return hipLaunchKernel(fn, dim3((unsigned)grid), dim3(kKvThreads), args, 0, stream);
 }
 
-hipError_t sva_internal_q_proj_apply_w4a4(const SvaKvReduceArgs& a, float eps, const void* xq, const void* wpack,
-                                          const float* bias, const void* frags, const float* zc, void* out,
-                                          hipStream_t stream) {
+hipError_t sva_internal_q_proj_apply(const SvaKvReduceArgs& a, float eps, bool w4a4, const void* x,
+                                    const void* wpack, const float* bias, const void* frags, const float* zc,
+                                    void* out, hipStream_t stream) {
   if (a.C % (2 * kTileK) != 0 || a.C < 2 * kTileK || a.H < 1 || a.Nb <= 0 || a.N % a.Nb != 0)
     return hipErrorInvalidValue;
   QaGeo g;
@@ -1756,9 +1872,12 @@ hipError_t sva_internal_q_proj_apply_w4a4(const SvaKvReduceArgs& a, float eps, c
   g.tab_entries = g.F * (a.dt / 2) + a.Hs * (a.dh / 2) + a.Ws * ((64 - a.dt - a.dh) / 2);
   g.eps = eps;
   const int mode = !a.rope ? 0 : g.tab_entries > kRopeTabW4 ? 2 : (a.dt % 8 == 0 && a.dh % 8 == 0) ? 0 : 1;
-  const void* fn = mode == 0   ? (const void*)&sva_q_proj_apply_w4a4_kernel<0>
-                   : mode == 1 ? (const void*)&sva_q_proj_apply_w4a4_kernel<1>
-                               : (const void*)&sva_q_proj_apply_w4a4_kernel<2>;
+  const void* fn = w4a4 ? (mode == 0   ? (const void*)&sva_q_proj_apply_kernel<0, true>
+                           : mode == 1 ? (const void*)&sva_q_proj_apply_kernel<1, true>
+                                       : (const void*)&sva_q_proj_apply_kernel<2, true>)
+                        : (mode == 0   ? (const void*)&sva_q_proj_apply_kernel<0, false>
+                           : mode == 1 ? (const void*)&sva_q_proj_apply_kernel<1, false>
+                                       : (const void*)&sva_q_proj_apply_kernel<2, false>);
   // Tiles per workgroup: each workgroup pays about one tile's time for its
   // set-up (the RoPE table, the state operands, the first x tile), and the
   // workgroups run in rounds of the resident count, so take the tpw with
@@ -1780,12 +1899,11 @@ hipError_t sva_internal_q_proj_apply_w4a4(const SvaKvReduceArgs& a, float eps, c
   const long long grid = ((long long)g.ngrp + 7) / 8 * 8 * g.nquads;
   if (grid >= (1LL << 31)) return hipErrorInvalidValue;
   const long long M = (long long)a.B * a.N;
-  const uint8_t* codes = (const uint8_t*)xq;
-  const uint8_t* scales = codes + (size_t)M * a.C / 2;
+  const uint8_t* scales = w4a4 ? (const uint8_t*)x + (size_t)M * a.C / 2 : nullptr;
   const uint8_t* wp = (const uint8_t*)wpack;
   const uint16_t* fr = (const uint16_t*)frags;
   uint16_t* op = (uint16_t*)out;
-  void* args[] = {(void*)&codes, (void*)&scales, (void*)&wp, (void*)&bias, (void*)&fr, (void*)&zc, (void*)&op, &g};
+  void* args[] = {(void*)&x, (void*)&scales, (void*)&wp, (void*)&bias, (void*)&fr, (void*)&zc, (void*)&op, &g};
   return hipLaunchKernel(fn, dim3((unsigned)grid), dim3(kKvThreads), args, 0, stream);
 }
 

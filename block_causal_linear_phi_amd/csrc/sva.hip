@@ -2579,7 +2579,7 @@ sva_status run_bwd(const sva_desc* desc, const void* q, const void* k, const voi
 struct ProjPlan {
   Plan p;
   long long L, G;
-  size_t off_q, off_partials, off_frags, off_zc, bytes;
+  size_t off_partials, off_frags, off_zc, bytes;
 };
 
 sva_status plan_proj_fwd(const sva_desc* a, const sva_proj_desc* pd, ProjPlan* pp) {
@@ -2623,8 +2623,6 @@ sva_status plan_proj_fwd(const sva_desc* a, const sva_proj_desc* pd, ProjPlan* p
   if (pp->G + (long long)p.BH * p.nb >= (1LL << 31) / (p.D * p.D + p.D)) return SVA_ERR_UNSUPPORTED;
   const size_t E = (size_t)p.D * p.D + p.D;
   size_t off = 0;
-  pp->off_q = off;
-  off = align256(off + (size_t)total * p.D * 2);
   pp->off_partials = off;
   off = align256(off + (size_t)(pp->G + (long long)p.BH * p.nb) * E * sizeof(float));
   pp->off_frags = off;
@@ -2666,17 +2664,11 @@ sva_status run_proj_fwd(const sva_desc* a, const sva_proj_desc* pd, const void* 
                  overlaps(z_out, z_bytes, ws, ws_bytes) || overlaps(z_out, z_bytes, out, nbytes))))
     return SVA_ERR_INVALID_ARG;
   char* wsb = (char*)ws;
-  void* q = wsb + pp.off_q;
   float* partials = (float*)(wsb + pp.off_partials);
   void* frags = wsb + pp.off_frags;
   float* zc = (float*)(wsb + pp.off_zc);
   hipStream_t st = (hipStream_t)stream;
-  // bf16 activations: q, the projection's first H*d features, into the
-  // workspace (4-bit activations project q inside the output pass below)
-  if (!w4a4) {
-    s = sva_internal_proj_features(pd, x, wpack, bias, pd->H * pd->d, q, q, q, stream);
-    if (s != SVA_OK) return s;
-  }
+
   SvaKvReduceArgs ka;
   ka.B = pd->B;
   ka.N = pd->N;
@@ -2699,12 +2691,9 @@ sva_status run_proj_fwd(const sva_desc* a, const sva_proj_desc* pd, const void* 
   if (SVA_DISPATCH2(p, launch_scan, p, partials, S0, z0, S_out, z_out, frags, zc, true, st, false, pp.L) !=
       hipSuccess)
     return SVA_ERR_HIP;
-  if (w4a4) {
-    if (sva_internal_q_proj_apply_w4a4(ka, a->eps, x, wpack, bias, frags, zc, out, st) != hipSuccess)
-      return SVA_ERR_HIP;
-  } else if (SVA_DISPATCH(p, launch_apply, p, q, out, frags, zc, a->eps, st) != hipSuccess) {
+  // q is projected inside the output pass, once the prefix exists
+  if (sva_internal_q_proj_apply(ka, a->eps, w4a4, x, wpack, bias, frags, zc, out, st) != hipSuccess)
     return SVA_ERR_HIP;
-  }
   return SVA_OK;
 }
 

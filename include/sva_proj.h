@@ -113,16 +113,17 @@ sva_status sva_mxfp4_quant_acts(const sva_proj_desc* desc, const void* x, void* 
 sva_status sva_qkv_proj_w4a4(const sva_proj_desc* desc, const void* xq, const void* wpack, const float* bias,
                              void* q, void* k, void* v, void* stream);
 
-/* Projection and attention in one pass over the tokens' k and v:
+/* Projection and attention without q, k or v in memory:
  *   out = sva_lin_attn_fwd(attn, q, k, v, ...) with (q, k, v) =
- *         sva_qkv_proj_mxfp4(proj, x, wpack, bias) rounded to bf16,
- * where k and v never reach memory: the k, v projection's epilogue applies
- * phi and the numerator-only RoPE to k (the [talk] 3D RoPE segment and the
- * [news] positional-encoding paragraph) and adds each 64-token tile's
- * RoPE(phi k)^T v and phi k to the block states ([talk] linear-attention and
- * block KV cache segments).  q goes through the workspace.  The SANA-Video
- * article's 4-bit quantization paragraph motivates fusing the projection
- * into the attention.
+ *         sva_qkv_proj_mxfp4(proj, x, wpack, bias) rounded to bf16.
+ * The k, v projection's epilogue applies phi and the numerator-only RoPE to
+ * k (the [talk] 3D RoPE segment and the [news] positional-encoding
+ * paragraph) and adds each 64-token tile's RoPE(phi k)^T v and phi k to the
+ * block states ([talk] linear-attention and block KV cache segments); once
+ * the block prefix is formed, q is projected a second pass over x inside
+ * the output pass, per 64-token tile and head.  The SANA-Video article's
+ * 4-bit quantization paragraph motivates fusing the projection into the
+ * attention.
  *   attn: bf16, d = 64, H even; proj: the same B, H, d, N = T*Hs*Ws, and
  *   C a multiple of 256 (an even number of 128-channel stages);
  *   S0, z0, S_out, z_out, eps and RoPE as in sva_lin_attn_fwd.
@@ -146,11 +147,9 @@ sva_status sva_proj_lin_attn_fwd(const sva_desc* attn, const sva_proj_desc* proj
  *         sva_qkv_proj_w4a4(proj, xq, wpack, bias) rounded to bf16,
  * xq being sva_mxfp4_quant_acts' output for the same proj descriptor
  * (sva_mxfp4_acts_bytes bytes; xq must not overlap out or the workspace).
- * k and v never reach memory, as above, and neither does q: it is projected
- * inside the output pass, per 64-token tile and head, after the block
- * prefix is known.  Limits, range length and errors as for
- * sva_proj_lin_attn_fwd; the workspace is sva_proj_lin_attn_fwd_workspace
- * bytes for the same descriptors (this call leaves its q region unused). */
+ * q, k and v never reach memory, as above.  Limits, range length, workspace
+ * (sva_proj_lin_attn_fwd_workspace with the same descriptors: the block
+ * partials and prefix operands) and errors as for sva_proj_lin_attn_fwd. */
 sva_status sva_proj_lin_attn_fwd_w4a4(const sva_desc* attn, const sva_proj_desc* proj, const void* xq,
                                       const void* wpack, const float* bias, void* out, const float* S0,
                                       const float* z0, float* S_out, float* z_out, void* ws, size_t ws_bytes,
