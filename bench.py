@@ -737,7 +737,7 @@ def _short_kernel(name: str) -> str:
     for k in ("sva_reduce_kernel", "sva_scan_kernel", "sva_apply_kernel", "sva_prep_kernel",
               "sva_bwd_out_kernel", "sva_bwd_kv_kernel", "sva_tconv_kernel", "sva_tconv_commit_kernel",
               "sva_qkv_proj_kernel", "sva_mxfp4_pack_kernel", "sva_mxfp4_quant_kernel", "sva_qkv_proj_w4a4_kernel",
-              "sva_kv_proj_reduce_kernel", "sva_kv_proj_reduce_w4a4_kernel"):
+              "sva_kv_proj_reduce_kernel", "sva_kv_proj_reduce_w4a4_kernel", "sva_q_proj_apply_kernel"):
         if k in name:
             short = k.replace("sva_", "").replace("_kernel", "")
             if k == "sva_tconv_kernel" and "sva_tconv_commit_kernel" in name:
