@@ -468,8 +468,10 @@ struct Geo {
 };
 
 struct SplitArgs {
-  long long total;  // BH * N flattened tokens
+  long long total;  // flattened tokens: BH * nb * Nbp
   long long L;      // flattened tokens per workgroup
+  int Nbp;          // a block's length on the flattened axis: Nb, or Nb padded up to a multiple of L
+                    // (positions Nb .. Nbp-1 of a block hold no token)
 };
 
 __device__ __forceinline__ void add4(float4& a, const float4& b) {
@@ -673,12 +675,12 @@ __global__ __launch_bounds__(red_threads<BF16>(), red_min_blocks<BF16>()) void s
   // arguments into two dependent rounds.
   long long pos = g0;
   do {
-    const long long bhc = pos / geo.Nb;
-    const long long seg_end = min(g1, (bhc + 1) * (long long)geo.Nb);
+    const long long bhc = pos / sp.Nbp;
+    const long long seg_end = min(g1, (bhc + 1) * (long long)sp.Nbp);
     const int bh = (int)(bhc / geo.nb);
     const int c = (int)(bhc - (long long)bh * geo.nb);
-    const int js = (int)(pos - bhc * geo.Nb);        // block-local token range
-    const int je = (int)(seg_end - bhc * geo.Nb);
+    const int js = (int)(pos - bhc * sp.Nbp);        // block-local token range
+    const int je = min((int)(seg_end - bhc * sp.Nbp), geo.Nb);
     // Buffer resources over the block's rows [0, je): rows past the segment
     // end read as zeros, so a ragged last step needs no masking (zero k
     // contributes nothing to S or z).
@@ -867,20 +869,21 @@ __global__ __launch_bounds__(red_threads<BF16>(), red_min_blocks<BF16>()) void s
       // stores are acknowledged, the workgroup meets, then one thread counts
       // with a device-scope atomic.  The empty asm statements keep the
       // compiler from moving memory accesses across these points.
-      if (seg_end >= g1 || seg_end == (long long)(bh + 1) * geo.N) {
+      const long long seq_end = (long long)(bh + 1) * geo.nb * sp.Nbp;  // on the flattened axis
+      if (seg_end >= g1 || seg_end == seq_end) {
         asm volatile("" ::: "memory");
         __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): this wave's stores are visible device-wide
         __builtin_amdgcn_s_barrier();
         if (tid == 0) {
-          const long long first = (long long)bh * geo.N / sp.L;
-          const long long last = ((long long)(bh + 1) * geo.N - 1) / sp.L;
+          const long long first = (seq_end - (long long)geo.nb * sp.Nbp) / sp.L;
+          const long long last = (seq_end - 1) / sp.L;
           const unsigned old = __hip_atomic_fetch_add(fa.counters + bh, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
           fold_last = old + 1 == (unsigned)(last - first + 1);
         }
         lds_barrier();
         if (fold_last) {
           asm volatile("" ::: "memory");
-          scan_sequence<BF16, D, RT>(partials, bh, geo.nb, geo.Nb, sp.L, fa);
+          scan_sequence<BF16, D, RT>(partials, bh, geo.nb, sp.Nbp, sp.L, fa);
           if (tid == 0) __hip_atomic_store(fa.counters + bh, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         }
       }
@@ -901,7 +904,7 @@ __global__ __launch_bounds__(red_threads<BF16>(), red_min_blocks<BF16>()) void s
 // ---------------------------------------------------------------------------
 
 struct ScanArgs {
-  int nb, Nb;
+  int nb, Nb;       // blocks; a block's length on the partials' flattened axis (SplitArgs::Nbp)
   long long L;      // flattened tokens per reduce workgroup
   int cpl;          // blocks per block-lane
   int has_init;     // S0/z0 given
@@ -1117,12 +1120,12 @@ __global__ __launch_bounds__(app_threads<BF16>(), app_min_blocks<BF16>()) void s
   // arguments into two dependent rounds.
   long long pos = g0;
   do {
-    const long long bhc = pos / geo.Nb;
-    const long long seg_end = min(g1, (bhc + 1) * (long long)geo.Nb);
+    const long long bhc = pos / sp.Nbp;
+    const long long seg_end = min(g1, (bhc + 1) * (long long)sp.Nbp);
     const int bh = (int)(bhc / geo.nb);
     const int c = (int)(bhc - (long long)bh * geo.nb);
-    const int js = (int)(pos - bhc * geo.Nb);
-    const int je = (int)(seg_end - bhc * geo.Nb);
+    const int js = (int)(pos - bhc * sp.Nbp);
+    const int je = min((int)(seg_end - bhc * sp.Nbp), geo.Nb);
     const long long row0 = (long long)bh * geo.N + (long long)c * geo.Nb;
 
     // Buffer resources over the block's rows [0, je): loads past the segment
@@ -2142,7 +2145,7 @@ bool overlaps(const void* a, size_t an, const void* b, size_t bn) {
   return x < y + bn && y < x + an;
 }
 
-SplitArgs make_split(long long total, long long target_wg, int* G_out) {
+SplitArgs make_split(long long total, long long target_wg, int* G_out, int Nb) {
   long long G = target_wg;
   const long long g_min_tokens = (total + kMinTokensPerWG - 1) / kMinTokensPerWG;
   if (G > g_min_tokens) G = g_min_tokens;
@@ -2150,9 +2153,28 @@ SplitArgs make_split(long long total, long long target_wg, int* G_out) {
   SplitArgs s;
   s.total = total;
   s.L = (total + G - 1) / G;
+  s.Nbp = Nb;
   G = (total + s.L - 1) / s.L;
   *G_out = (int)G;
   return s;
+}
+
+// The split of make_split with every range inside one block, when that takes
+// at most max_wg workgroups: each of the `blocks` blocks is cut into J equal
+// ranges of Lb <= L tokens (its length padded to J * Lb on the flattened
+// axis).  A range that crosses a block boundary costs its workgroup a second
+// setup (the new block's operands, RoPE rows) and epilogue; on a grid of one
+// round that workgroup finishes last.  Splits of several blocks per range,
+// and those that would need more workgroups than fit, stay as they are.
+void align_split(SplitArgs* s, int* G_out, long long blocks, int Nb, long long max_wg) {
+  if (s->L >= Nb) return;
+  const long long J = (Nb + s->L - 1) / s->L;
+  if (blocks * J > max_wg) return;
+  const long long Lb = (Nb + J - 1) / J;
+  s->L = Lb;
+  s->Nbp = (int)(J * Lb);
+  s->total = blocks * s->Nbp;
+  *G_out = (int)(blocks * J);
 }
 
 // How many workgroups of `fn` the current device holds at once (CUs times
@@ -2290,8 +2312,8 @@ Plan make_plan(const sva_desc* d) {
   // Grids are fixed at launch from the device's occupancy (plan_grids); the
   // workspace is sized for the largest reduce grid.  Piece (g, block) of the
   // reduce lives in slot g + block, so G + B*H*nb slots always suffice.
-  p.red = make_split(total, kRedWorkgroupsMax, &p.G_red);
-  p.app = make_split(total, kAppWorkgroupsMax, &p.G_app);
+  p.red = make_split(total, kRedWorkgroupsMax, &p.G_red, p.Nb);
+  p.app = make_split(total, kAppWorkgroupsMax, &p.G_app, p.Nb);
   layout_workspace(&p, kRedWorkgroupsMax);
   const size_t esz = p.bf16 ? 2 : 4;
   p.states_lo = align256((size_t)p.BH * p.nb * p.D * p.D * esz);
@@ -2321,8 +2343,10 @@ hipError_t launch_scan(const Plan& p, const float* partials, const float* S0, co
                        hipStream_t st, bool reverse = false, long long L = 0, void* frags_lo = nullptr) {
   ScanArgs a;
   a.nb = p.nb;
-  a.Nb = p.Nb;
-  a.L = L ? L : p.red.L;  // tokens per workgroup of the kernel that wrote the partials
+  // the split of the kernel that wrote the partials: the reduction's, or
+  // (L given) a flat split of L tokens per workgroup
+  a.Nb = L ? p.Nb : p.red.Nbp;
+  a.L = L ? L : p.red.L;
   a.cpl = (p.nb + kScanLanes - 1) / kScanLanes;
   a.has_init = S0 != nullptr;
   a.write_frags = write_frags;
@@ -2407,8 +2431,13 @@ int plan_grids_t(Plan* p) {
                                : (const void*)&sva_reduce_kernel<BF16, D, (ROPE == 3 ? 2 : ROPE), false>;
   const long long r = resident_workgroups(red_fn, red_threads<BF16>(), lds);
   const long long a = resident_workgroups((const void*)&sva_apply_kernel<BF16, D, (!BF16 && ROPE == 3 ? 2 : ROPE)>, app_threads<BF16>(), lds);
-  p->red = make_split(total, r < kRedWorkgroupsMax ? r : kRedWorkgroupsMax, &p->G_red);
-  p->app = make_split(total, a < kAppWorkgroupsMax ? a : kAppWorkgroupsMax, &p->G_app);
+  const long long r_max = r < kRedWorkgroupsMax ? r : kRedWorkgroupsMax;
+  const long long a_max = a < kAppWorkgroupsMax ? a : kAppWorkgroupsMax;
+  p->red = make_split(total, r_max, &p->G_red, p->Nb);
+  p->app = make_split(total, a_max, &p->G_app, p->Nb);
+  const long long blocks = (long long)p->BH * p->nb;
+  align_split(&p->red, &p->G_red, blocks, p->Nb, r_max);
+  align_split(&p->app, &p->G_app, blocks, p->Nb, a_max);
   return 0;
 }
 
@@ -2421,8 +2450,8 @@ int plan_bwd_grids_t(Plan* p) {
   const long long a = resident_workgroups((const void*)&sva_bwd_out_kernel<D, ROPE>, kThreads, lds);
   const long long b = resident_workgroups((const void*)&sva_bwd_kv_kernel<D, ROPE>, kThreads, lds);
   // its partials use the reduction's slots: at most kRedWorkgroupsMax pieces
-  p->bwd = make_split(total, a < kRedWorkgroupsMax ? a : kRedWorkgroupsMax, &p->G_bwd_out);
-  p->bwd_kv = make_split(total, b < kAppWorkgroupsMax ? b : kAppWorkgroupsMax, &p->G_bwd_kv);
+  p->bwd = make_split(total, a < kRedWorkgroupsMax ? a : kRedWorkgroupsMax, &p->G_bwd_out, p->Nb);
+  p->bwd_kv = make_split(total, b < kAppWorkgroupsMax ? b : kAppWorkgroupsMax, &p->G_bwd_kv, p->Nb);
   return 0;
 }
 
