@@ -670,44 +670,64 @@ __global__ __launch_bounds__(red_threads<BF16>(), red_min_blocks<BF16>()) void s
   const char* kb = (const char*)kp;
   const char* vb = (const char*)vp;
 
-  // Every workgroup has at least one token (the grid is ceil(total / L)), so the
-  // loop needs no entry test, which would split the reads of the kernel
+  // Segment parameters: the block (sequence bh, block c) holding the tokens
+  // at position p, this workgroup's block-local token range [js, je) in it,
+  // buffer resources over the block's rows [0, je) (rows past the segment
+  // end read as zeros, so a ragged last step needs no masking: zero k
+  // contributes nothing to S or z), and this wave's steps.
+  long long bhc, seg_end;
+  int bh, c, je, s_first, nsteps;
+  __amdgpu_buffer_rsrc_t krs, vrs;
+  const uint32_t lane_col = FPL * cg * ESZ;
+  auto enter_segment = [&](long long p) {
+    bhc = p / sp.Nbp;
+    seg_end = min(g1, (bhc + 1) * (long long)sp.Nbp);
+    bh = (int)(bhc / geo.nb);
+    c = (int)(bhc - (long long)bh * geo.nb);
+    const int js = (int)(p - bhc * sp.Nbp);
+    je = min((int)(seg_end - bhc * sp.Nbp), geo.Nb);
+    const long long blk_off = ((long long)bh * geo.N + (long long)c * geo.Nb) * ROWB;
+    krs = make_rsrc(kb + blk_off, (uint32_t)je * ROWB);
+    vrs = make_rsrc(vb + blk_off, (uint32_t)je * ROWB);
+    s_first = js + wave * STEP;
+    nsteps = s_first < je ? (je - s_first + WSTRIDE - 1) / WSTRIDE : 0;
+  };
+
+  floatx4 acc[FPL][FPL];
+  float zacc[FPL];
+
+  // A step is 32 consecutive tokens; lane (cg, tg) takes tokens 4e + tg,
+  // each load reading 4 consecutive token rows (offsets are immediates).
+  auto load_step = [&](uint32_t (&kw)[8][NW], uint32_t (&vw)[8][NW], int s0) {
+    const uint32_t off = (uint32_t)(s0 + tg) * ROWB + lane_col;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      buf_load<NW>(kw[e], krs, off + 4 * e * ROWB);
+      buf_load<NW>(vw[e], vrs, off + 4 * e * ROWB);
+    }
+  };
+
+  // Software pipeline over the wave's steps, three register sets in a ring:
+  // while step k computes, steps k+1 and k+2 are in flight (16 KiB per wave
+  // at bf16, d = 64).  sched_barrier keeps the compiler from sinking a
+  // prefetch below the compute it should overlap.  The first two steps of a
+  // segment are issued before the previous segment's epilogue.
+  uint32_t kA[8][NW], vA[8][NW], kB[8][NW], vB[8][NW], kC[8][NW], vC[8][NW];
+  // Every workgroup has at least one token (the grid is ceil(total / L)), so
+  // the loop needs no entry test, which would split the reads of the kernel
   // arguments into two dependent rounds.
   long long pos = g0;
+  enter_segment(pos);
+  load_step(kA, vA, s_first);
+  load_step(kB, vB, s_first + WSTRIDE);
   do {
-    const long long bhc = pos / sp.Nbp;
-    const long long seg_end = min(g1, (bhc + 1) * (long long)sp.Nbp);
-    const int bh = (int)(bhc / geo.nb);
-    const int c = (int)(bhc - (long long)bh * geo.nb);
-    const int js = (int)(pos - bhc * sp.Nbp);        // block-local token range
-    const int je = min((int)(seg_end - bhc * sp.Nbp), geo.Nb);
-    // Buffer resources over the block's rows [0, je): rows past the segment
-    // end read as zeros, so a ragged last step needs no masking (zero k
-    // contributes nothing to S or z).
-    const long long blk_off = ((long long)bh * geo.N + (long long)c * geo.Nb) * ROWB;
-    const __amdgpu_buffer_rsrc_t krs = make_rsrc(kb + blk_off, (uint32_t)je * ROWB);
-    const __amdgpu_buffer_rsrc_t vrs = make_rsrc(vb + blk_off, (uint32_t)je * ROWB);
-    const uint32_t lane_col = FPL * cg * ESZ;
-
-    floatx4 acc[FPL][FPL];
 #pragma unroll
     for (int r = 0; r < FPL; ++r)
 #pragma unroll
       for (int s = 0; s < FPL; ++s) acc[r][s] = floatx4{0.f, 0.f, 0.f, 0.f};
-    float zacc[FPL];
 #pragma unroll
     for (int r = 0; r < FPL; ++r) zacc[r] = 0.f;
 
-    // A step is 32 consecutive tokens; lane (cg, tg) takes tokens 4e + tg,
-    // each load reading 4 consecutive token rows (offsets are immediates).
-    auto load_step = [&](uint32_t (&kw)[8][NW], uint32_t (&vw)[8][NW], int s0) {
-      const uint32_t off = (uint32_t)(s0 + tg) * ROWB + lane_col;
-#pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        buf_load<NW>(kw[e], krs, off + 4 * e * ROWB);
-        buf_load<NW>(vw[e], vrs, off + 4 * e * ROWB);
-      }
-    };
     auto compute_step = [&](const uint32_t (&kw)[8][NW], const uint32_t (&vw)[8][NW], int s0) {
       // Coordinates: lanes 0..31 decode the step's 32 tokens (clamped to the
       // segment so table indices stay in range), every lane fetches those of
@@ -763,15 +783,6 @@ __global__ __launch_bounds__(red_threads<BF16>(), red_min_blocks<BF16>()) void s
       }
     };
 
-    // Software pipeline over the wave's steps, three register sets in a
-    // ring: while step k computes, steps k+1 and k+2 are in flight (16 KiB
-    // per wave at bf16, d = 64).  sched_barrier keeps the compiler from
-    // sinking a prefetch below the compute it should overlap.
-    const int s_first = js + wave * STEP;
-    const int nsteps = s_first < je ? (je - s_first + WSTRIDE - 1) / WSTRIDE : 0;
-    uint32_t kA[8][NW], vA[8][NW], kB[8][NW], vB[8][NW], kC[8][NW], vC[8][NW];
-    load_step(kA, vA, s_first);
-    load_step(kB, vB, s_first + WSTRIDE);
     __builtin_amdgcn_sched_barrier(0);
     // The RoPE layout is read from the kernel arguments only now, so that
     // the streaming loads above wait for no more than the pointers and the
@@ -810,6 +821,22 @@ __global__ __launch_bounds__(red_threads<BF16>(), red_min_blocks<BF16>()) void s
     if (k < nsteps) compute_step(kA, vA, s_first + k * WSTRIDE);
     if (k + 1 < nsteps) compute_step(kB, vB, s_first + (k + 1) * WSTRIDE);
 
+    // The next segment's first two steps go out now, in flight across this
+    // segment's epilogue (a workgroup whose range crosses a block boundary
+    // otherwise waits a full memory round trip after it).  The epilogue
+    // below needs only this segment's block and sequence.  In the folded
+    // form the epilogue waits for every memory access of the wave, so the
+    // next loads follow it instead.
+    const long long bhc_done = bhc, seg_end_done = seg_end;
+    const int bh_done = bh;
+    const bool more = seg_end < g1;
+    if (!FOLD && more) {
+      enter_segment(seg_end_done);
+      load_step(kA, vA, s_first);
+      load_step(kB, vB, s_first + WSTRIDE);
+    }
+    __builtin_amdgcn_sched_barrier(0);
+
     // Fixed-order reduction over the four lane groups (lane swaps), then over
     // the waves: every wave stores its tile, one barrier, and each thread
     // sums the tiles for 4 contiguous elements in wave order.  (A two-round
@@ -841,7 +868,7 @@ __global__ __launch_bounds__(red_threads<BF16>(), red_min_blocks<BF16>()) void s
     // (Stored with device scope when the prefix is folded in: the last
     // workgroup of the sequence, on any XCD, reads them back.)
     constexpr int PP = FOLD ? kDeviceScope : 0;
-    const __amdgpu_buffer_rsrc_t prs = make_rsrc(partials + ((long long)blockIdx.x + bhc) * E, E * 4);
+    const __amdgpu_buffer_rsrc_t prs = make_rsrc(partials + ((long long)blockIdx.x + bhc_done) * E, E * 4);
     for (int e = tid; e < D * D / 4; e += RT) {
       const int fo = e % D, fi0 = 4 * (e / D);  // consecutive lanes: consecutive fo
       float t[4];
@@ -869,27 +896,32 @@ __global__ __launch_bounds__(red_threads<BF16>(), red_min_blocks<BF16>()) void s
       // stores are acknowledged, the workgroup meets, then one thread counts
       // with a device-scope atomic.  The empty asm statements keep the
       // compiler from moving memory accesses across these points.
-      const long long seq_end = (long long)(bh + 1) * geo.nb * sp.Nbp;  // on the flattened axis
-      if (seg_end >= g1 || seg_end == seq_end) {
+      const long long seq_end = (long long)(bh_done + 1) * geo.nb * sp.Nbp;  // on the flattened axis
+      if (seg_end_done >= g1 || seg_end_done == seq_end) {
         asm volatile("" ::: "memory");
         __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): this wave's stores are visible device-wide
         __builtin_amdgcn_s_barrier();
         if (tid == 0) {
           const long long first = (seq_end - (long long)geo.nb * sp.Nbp) / sp.L;
           const long long last = (seq_end - 1) / sp.L;
-          const unsigned old = __hip_atomic_fetch_add(fa.counters + bh, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+          const unsigned old = __hip_atomic_fetch_add(fa.counters + bh_done, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
           fold_last = old + 1 == (unsigned)(last - first + 1);
         }
         lds_barrier();
         if (fold_last) {
           asm volatile("" ::: "memory");
-          scan_sequence<BF16, D, RT>(partials, bh, geo.nb, sp.Nbp, sp.L, fa);
-          if (tid == 0) __hip_atomic_store(fa.counters + bh, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+          scan_sequence<BF16, D, RT>(partials, bh_done, geo.nb, sp.Nbp, sp.L, fa);
+          if (tid == 0) __hip_atomic_store(fa.counters + bh_done, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         }
+      }
+      if (more) {
+        enter_segment(seg_end_done);
+        load_step(kA, vA, s_first);
+        load_step(kB, vB, s_first + WSTRIDE);
       }
     }
     // `red` is next written after the next segment's barrier.
-    pos = seg_end;
+    pos = seg_end_done;
   } while (pos < g1);
 }
 
