@@ -2231,6 +2231,22 @@ int resident_workgroups(const void* fn, int threads, size_t lds) {
   return n;
 }
 
+// Compute units of the current device (queried once per device).
+int device_cus() {
+  static std::mutex mu;
+  static std::map<int, int> cache;
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return 256;
+  std::lock_guard<std::mutex> lock(mu);
+  auto it = cache.find(dev);
+  if (it != cache.end()) return it->second;
+  int cus = 0;
+  if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus < 1)
+    cus = 256;
+  cache[dev] = cus;
+  return cus;
+}
+
 sva_status validate_desc(const sva_desc* d, bool one_block) {
   if (!d) return SVA_ERR_INVALID_ARG;
   if (d->B < 1 || d->H < 1 || d->T < 1 || d->Hs < 1 || d->Ws < 1 || d->frames_per_block < 1 ||
@@ -2465,8 +2481,16 @@ int plan_grids_t(Plan* p) {
   const long long a = resident_workgroups((const void*)&sva_apply_kernel<BF16, D, (!BF16 && ROPE == 3 ? 2 : ROPE)>, app_threads<BF16>(), lds);
   const long long r_max = r < kRedWorkgroupsMax ? r : kRedWorkgroupsMax;
   const long long a_max = a < kAppWorkgroupsMax ? a : kAppWorkgroupsMax;
+  // When the output pass's minimum of tokens per workgroup, not occupancy,
+  // bounds its grid (one block of a few thousand tokens per sequence), a
+  // multiple of the CU count gives every CU the same number of workgroups
+  // (304 workgroups on 256 CUs left 48 CUs with twice the work of the rest).
+  long long a_target = a_max;
+  const long long a_tok = total / kMinTokensPerWG;
+  const long long cus = device_cus();
+  if (a_tok < a_target) a_target = a_tok >= cus ? a_tok / cus * cus : a_tok;
   p->red = make_split(total, r_max, &p->G_red, p->Nb);
-  p->app = make_split(total, a_max, &p->G_app, p->Nb);
+  p->app = make_split(total, a_target > 0 ? a_target : 1, &p->G_app, p->Nb);
   const long long blocks = (long long)p->BH * p->nb;
   align_split(&p->red, &p->G_red, blocks, p->Nb, r_max);
   align_split(&p->app, &p->G_app, blocks, p->Nb, a_max);

@@ -37,8 +37,8 @@
  * Ownership: the caller allocates and frees every buffer, including the
  * workspace.  The library allocates nothing and keeps no pointer after a
  * call returns.  Its only process-wide state is a per-device memo of the
- * occupancy queries that size its grids (filled on first use, under a
- * mutex, and never changed after), so calls on disjoint buffers may run
+ * occupancy and compute-unit queries that size its grids (filled on first
+ * use, under a mutex, and never changed after), so calls on disjoint buffers may run
  * concurrently from several threads.  `out` must not overlap q, k or v.
  *
  * Errors: validation is synchronous, happens before anything is launched,
