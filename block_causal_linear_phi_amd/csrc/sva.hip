@@ -1008,23 +1008,50 @@ __global__ __launch_bounds__(kThreads) void sva_scan_kernel(
   }
   // Pass 1: block sums of this lane's blocks.  Up to kKeep of them stay in
   // registers for pass 2; lanes with more blocks re-read theirs (L2 hits).
+  // With one block per sequence (the cached step, block-by-block streaming)
+  // the block-lanes split that block's pieces instead: lane ty takes slots
+  // ty, ty + 8, ... (all of its loads issued at once), and lane 0 adds the
+  // eight lane sums in lane order.
   constexpr int kKeep = 4;
   float4 keep[kKeep];
   float4 tot = make_float4(0.f, 0.f, 0.f, 0.f);
+  const bool one = a.nb == 1;
   if (active) {
-    for (int c = c_begin; c < c_end; ++c) {
-      const int cb = a.reverse ? a.nb - 1 - c : c;  // the block, in scan order
-      const float4 bs = block_sum<E>(partials, (long long)bh * a.nb + cb, a.L, a.Nb, e);
+    if (one) {
+      const long long start = (long long)bh * a.Nb;
+      const long long gf = start / a.L;
+      const int n = (int)((start + a.Nb - 1) / a.L - gf + 1);
+      const float* pp = partials + (gf + bh) * E + e;
+      for (int i0 = ty; i0 < n; i0 += 4 * kScanLanes) {
+        float4 x[4];
 #pragma unroll
-      for (int i = 0; i < kKeep; ++i)
-        if (c - c_begin == i) keep[i] = bs;
-      add4(tot, bs);
+        for (int j = 0; j < 4; ++j)  // slots past the last repeat it and are not added
+          x[j] = *(const float4*)(pp + (long long)min(i0 + j * kScanLanes, n - 1) * E);
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+          if (i0 + j * kScanLanes < n) add4(tot, x[j]);
+      }
+    } else {
+      for (int c = c_begin; c < c_end; ++c) {
+        const int cb = a.reverse ? a.nb - 1 - c : c;  // the block, in scan order
+        const float4 bs = block_sum<E>(partials, (long long)bh * a.nb + cb, a.L, a.Nb, e);
+#pragma unroll
+        for (int i = 0; i < kKeep; ++i)
+          if (c - c_begin == i) keep[i] = bs;
+        add4(tot, bs);
+      }
     }
   }
   lane_tot[ty][tx] = tot;
   __syncthreads();
   if (!active) return;
-  for (int l = 0; l < ty; ++l) add4(run, lane_tot[l][tx]);
+  if (one) {
+    if (ty != 0) return;  // lane 0 owns the block (c_begin = 0, c_end = 1)
+    keep[0] = lane_tot[0][tx];
+    for (int l = 1; l < kScanLanes; ++l) add4(keep[0], lane_tot[l][tx]);
+  } else {
+    for (int l = 0; l < ty; ++l) add4(run, lane_tot[l][tx]);
+  }
 
   for (int c = c_begin; c < c_end; ++c) {
     const long long bhc = (long long)bh * a.nb + (a.reverse ? a.nb - 1 - c : c);
