@@ -1722,9 +1722,10 @@ __global__ __launch_bounds__(kThreads, 1) void sva_bwd_out_kernel(
     constexpr int WSTRIDE = 16 * NWAVE;
     const int t_first = js + wave * 16;
     const int nsteps = t_first < je ? (je - t_first + WSTRIDE - 1) / WSTRIDE : 0;
-    // Four register sets: three steps stay in flight while one is computed
-    // (one wave per SIMD leaves nothing else to cover the memory latency).
-    uint32_t x0[2][NW], x1[2][NW], x2[2][NW], x3[2][NW];
+    // Two register sets: the next step is in flight while one is computed.
+    // (A ring of four, three steps in flight, measured the same: 258.3
+    // against 258.1 us per 720p backward.)
+    uint32_t x0[2][NW], x1[2][NW];
     auto load2 = [&](uint32_t (&x)[2][NW], int k) {
       const int t = t_first + k * WSTRIDE;
       btile_load<D>(x[0], qrs, t, lane);
