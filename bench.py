@@ -660,6 +660,10 @@ def other_workloads(steps: int, warmup: int, sets: int):
     return out
 
 
+SECONDARY_WARMUP = 50  # warm-up calls of each leg after the headline
+SECONDARY_STEPS = 100  # timed steps of each other workload, at least
+
+
 def extension_rows(steps: int, warmup: int, sets: int):
     """The rows beyond the forward, each timed in this process at the 720p
     size (after the headline): the backward from saved states, the temporal
@@ -1193,8 +1197,15 @@ def main():
     copy = None
     if not args.no_others and w.name == "720p":
         copy = copy_ceiling()
-        others = other_workloads(args.steps, args.warmup, args.sets)
-        ext = extension_rows(min(args.steps, 20), min(args.warmup, 10), args.sets)
+        # The other workloads and the extension rows are steady-state figures
+        # whatever K and W the headline takes: a leg's first calls after it
+        # sets up its buffers run slower (720p backward over 20 calls: 255 us
+        # after 5 warm-up calls, 240.7 us after 50), and over a few calls the
+        # host's first launches weigh in (480p: 63.1 us over 20 steps, 57.3
+        # over 200), so each leg warms up at least SECONDARY_WARMUP calls and
+        # the other workloads time at least SECONDARY_STEPS.
+        others = other_workloads(max(args.steps, SECONDARY_STEPS), max(args.warmup, SECONDARY_WARMUP), args.sets)
+        ext = extension_rows(min(args.steps, 20), SECONDARY_WARMUP, args.sets)
     ms_per_step = res["ms"]
     esz = 2 if w.dtype == "bf16" else 4
     elems = w.B * w.H * w.N * w.d
