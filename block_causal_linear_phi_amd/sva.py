@@ -130,9 +130,17 @@ def _ptr(t) -> Optional[int]:
 
 
 def _stream(stream) -> Optional[int]:
+    """The HIP stream handle of `stream`, else of the current device's current
+    stream (torch's raw getter: 0.1 us against 2.7 us for
+    torch.cuda.current_stream(), which a tiny call would otherwise spend)."""
     import torch
-    s = torch.cuda.current_stream() if stream is None else stream
-    return s.cuda_stream
+    if stream is not None:
+        return stream.cuda_stream
+    raw = getattr(torch._C, "_cuda_getCurrentRawStream", None)
+    dev = getattr(torch._C, "_cuda_getDevice", None)
+    if raw is None or dev is None:
+        return torch.cuda.current_stream().cuda_stream
+    return raw(dev())
 
 
 def _dtype_code(t) -> int:
