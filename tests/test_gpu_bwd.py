@@ -37,6 +37,12 @@ CASES = [
     ("general_d64", 1, 2, 64, (4, 5, 6), 2, (6, 26, 32), 3, True, False),
     ("one_block_d64", 1, 1, 64, (3, 9, 9), 3, (16, 24, 24), 7, True, True),
     ("lt16_tokens", 1, 1, 64, (3, 1, 1), 1, (16, 24, 24), 2, False, False),
+    # one 20,000-token block per sequence: the suffix scan's block-lanes share
+    # the pieces of that block (more than 32 of them)
+    ("one_long_block", 1, 4, 64, (2, 100, 100), 2, (16, 24, 24), 5, True, True),
+    # 100 blocks of 700 tokens: the recomputed forward takes one reduction
+    # range fewer per block
+    ("fewer_ranges_per_block", 1, 4, 64, (25, 20, 35), 1, (16, 24, 24), 0, True, True),
 ]
 
 

@@ -42,6 +42,13 @@ SMALL = [
     # (the last workgroup of each sequence), not by a scan launch
     ("many_blocks_d64", 2, 2, 64, (40, 3, 5), 1, (16, 24, 24), 7),
     ("many_blocks_d32", 1, 3, 32, (64, 2, 4), 2, (8, 12, 12), 0),
+    # one 20,000-token block per sequence: every block cut into equal ranges
+    # (its length padded on the split axis), and the scan's block-lanes share
+    # more than 32 pieces of one block
+    ("one_long_block", 1, 4, 64, (2, 100, 100), 2, (16, 24, 24), 5),
+    # 100 blocks of 700 tokens: ceil(700 / L) ranges a block would not fit in
+    # one round, so the reduction takes one range fewer per block
+    ("fewer_ranges_per_block", 1, 4, 64, (25, 20, 35), 1, (16, 24, 24), 0),
 ]
 
 
