@@ -49,6 +49,9 @@ SMALL = [
     # 100 blocks of 700 tokens: ceil(700 / L) ranges a block would not fit in
     # one round, so the reduction takes one range fewer per block
     ("fewer_ranges_per_block", 1, 4, 64, (25, 20, 35), 1, (16, 24, 24), 0),
+    # 32 blocks of 2,001 tokens in one sequence: the prefix formed inside the
+    # reduction, on equal ranges of a padded block length
+    ("folded_padded_ranges", 1, 1, 64, (32, 23, 87), 1, (16, 24, 24), 3),
 ]
 
 
