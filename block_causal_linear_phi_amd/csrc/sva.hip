@@ -38,6 +38,7 @@
 #include <tuple>
 
 #include "internal.h"
+#include "split.h"
 #include "sva.h"
 #include "sva_proj.h"
 
@@ -467,13 +468,6 @@ struct Geo {
   FastDiv fHW, fWs;
 };
 
-struct SplitArgs {
-  long long total;  // flattened tokens: BH * nb * Nbp
-  long long L;      // flattened tokens per workgroup
-  int Nbp;          // a block's length on the flattened axis: Nb, or Nb padded up to a multiple of L
-                    // (positions Nb .. Nbp-1 of a block hold no token)
-};
-
 __device__ __forceinline__ void add4(float4& a, const float4& b) {
   a.x += b.x; a.y += b.y; a.z += b.z; a.w += b.w;
 }
@@ -504,17 +498,6 @@ struct FoldArgs {
   void* frags;         // prefix operands S_c^T [B*H*nb, d, d] in the input dtype, or null
   float* zc;           // Z_c [B*H*nb, d] fp32 (written together with frags)
 };
-
-// First and last slot of the pieces of flattened block bhc (the piece of
-// workgroup g sits at slot g + bhc, so a block's pieces are contiguous).  The
-// slot between two blocks is unused when a workgroup range ends exactly at
-// the block boundary.
-__device__ __forceinline__ long long block_first_slot(long long bhc, int Nb, long long L) {
-  return (bhc * Nb) / L + bhc;
-}
-__device__ __forceinline__ long long block_last_slot(long long bhc, int Nb, long long L) {
-  return (bhc * Nb + Nb - 1) / L + bhc;
-}
 
 // The prefix of sequence bh, by one workgroup of NT threads: thread t owns
 // the 4-element groups t, t + NT, ... of a partial (S^T, then z).  The
@@ -680,12 +663,13 @@ __global__ __launch_bounds__(red_threads<BF16>(), red_min_blocks<BF16>()) void s
   __amdgpu_buffer_rsrc_t krs, vrs;
   const uint32_t lane_col = FPL * cg * ESZ;
   auto enter_segment = [&](long long p) {
-    bhc = p / sp.Nbp;
-    seg_end = min(g1, (bhc + 1) * (long long)sp.Nbp);
+    const Segment sg = segment_at(p, g1, sp, geo.Nb);
+    bhc = sg.bhc;
+    seg_end = sg.end;
     bh = (int)(bhc / geo.nb);
     c = (int)(bhc - (long long)bh * geo.nb);
-    const int js = (int)(p - bhc * sp.Nbp);
-    je = min((int)(seg_end - bhc * sp.Nbp), geo.Nb);
+    const int js = sg.js;
+    je = sg.je;
     const long long blk_off = ((long long)bh * geo.N + (long long)c * geo.Nb) * ROWB;
     krs = make_rsrc(kb + blk_off, (uint32_t)je * ROWB);
     vrs = make_rsrc(vb + blk_off, (uint32_t)je * ROWB);
@@ -896,14 +880,13 @@ __global__ __launch_bounds__(red_threads<BF16>(), red_min_blocks<BF16>()) void s
       // stores are acknowledged, the workgroup meets, then one thread counts
       // with a device-scope atomic.  The empty asm statements keep the
       // compiler from moving memory accesses across these points.
-      const long long seq_end = (long long)(bh_done + 1) * geo.nb * sp.Nbp;  // on the flattened axis
-      if (seg_end_done >= g1 || seg_end_done == seq_end) {
+      if (arrives(seg_end_done, g1, bh_done, geo.nb, sp.Nbp)) {
         asm volatile("" ::: "memory");
         __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): this wave's stores are visible device-wide
         __builtin_amdgcn_s_barrier();
         if (tid == 0) {
-          const long long first = (seq_end - (long long)geo.nb * sp.Nbp) / sp.L;
-          const long long last = (seq_end - 1) / sp.L;
+          const long long first = seq_first_wg(bh_done, geo.nb, sp.Nbp, sp.L);
+          const long long last = seq_last_wg(bh_done, geo.nb, sp.Nbp, sp.L);
           const unsigned old = __hip_atomic_fetch_add(fa.counters + bh_done, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
           fold_last = old + 1 == (unsigned)(last - first + 1);
         }
@@ -954,10 +937,9 @@ constexpr int kScanElems = kThreads / kScanLanes;  // 4-element groups per workg
 template <int E>
 __device__ __forceinline__ float4 block_sum(const float* __restrict__ partials, long long bhc,
                                             long long L, int Nb, int e) {
-  const long long start = bhc * Nb;
-  const long long gf = start / L, gl = (start + Nb - 1) / L;
-  const float* p = partials + (gf + bhc) * E + e;
-  const int n = (int)(gl - gf + 1);
+  const long long first = block_first_slot(bhc, Nb, L);
+  const float* p = partials + first * E + e;
+  const int n = (int)(block_last_slot(bhc, Nb, L) - first + 1);
   float4 s = make_float4(0.f, 0.f, 0.f, 0.f);
   int i = 0;
   for (; i + 4 <= n; i += 4) {
@@ -1018,10 +1000,9 @@ __global__ __launch_bounds__(kThreads) void sva_scan_kernel(
   const bool one = a.nb == 1;
   if (active) {
     if (one) {
-      const long long start = (long long)bh * a.Nb;
-      const long long gf = start / a.L;
-      const int n = (int)((start + a.Nb - 1) / a.L - gf + 1);
-      const float* pp = partials + (gf + bh) * E + e;
+      const long long first = block_first_slot(bh, a.Nb, a.L);
+      const int n = (int)(block_last_slot(bh, a.Nb, a.L) - first + 1);
+      const float* pp = partials + first * E + e;
       for (int i0 = ty; i0 < n; i0 += 4 * kScanLanes) {
         float4 x[4];
 #pragma unroll
@@ -1179,12 +1160,13 @@ __global__ __launch_bounds__(app_threads<BF16>(), app_min_blocks<BF16>()) void s
   // arguments into two dependent rounds.
   long long pos = g0;
   do {
-    const long long bhc = pos / sp.Nbp;
-    const long long seg_end = min(g1, (bhc + 1) * (long long)sp.Nbp);
+    const Segment sg = segment_at(pos, g1, sp, geo.Nb);
+    const long long bhc = sg.bhc;
+    const long long seg_end = sg.end;
     const int bh = (int)(bhc / geo.nb);
     const int c = (int)(bhc - (long long)bh * geo.nb);
-    const int js = (int)(pos - bhc * sp.Nbp);
-    const int je = min((int)(seg_end - bhc * sp.Nbp), geo.Nb);
+    const int js = sg.js;
+    const int je = sg.je;
     const long long row0 = (long long)bh * geo.N + (long long)c * geo.Nb;
 
     // Buffer resources over the block's rows [0, je): loads past the segment
@@ -2193,7 +2175,6 @@ struct Plan {
 
 constexpr long long kRedWorkgroupsMax = 1024;  // bounds the partials workspace
 constexpr long long kAppWorkgroupsMax = 4096;
-constexpr long long kMinTokensPerWG = 256;
 constexpr int kFoldMinBlocks = 32;  // blocks per sequence from which the prefix is folded
 
 size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
@@ -2205,50 +2186,10 @@ bool overlaps(const void* a, size_t an, const void* b, size_t bn) {
   return x < y + bn && y < x + an;
 }
 
-SplitArgs make_split(long long total, long long target_wg, int* G_out, int Nb) {
-  long long G = target_wg;
-  const long long g_min_tokens = (total + kMinTokensPerWG - 1) / kMinTokensPerWG;
-  if (G > g_min_tokens) G = g_min_tokens;
-  if (G < 1) G = 1;
-  SplitArgs s;
-  s.total = total;
-  s.L = (total + G - 1) / G;
-  s.Nbp = Nb;
-  G = (total + s.L - 1) / s.L;
-  *G_out = (int)G;
-  return s;
-}
-
-// The split of make_split with every range inside one block, when that takes
-// at most max_wg workgroups: each of the `blocks` blocks is cut into J equal
-// ranges of Lb <= L tokens (its length padded to J * Lb on the flattened
-// axis).  A range that crosses a block boundary costs its workgroup a second
-// setup (the new block's operands, RoPE rows) and epilogue; on a grid of one
-// round that workgroup finishes last.  With `fewer`, when that J needs more
-// workgroups than fit, one range fewer per block is taken if it lengthens a
-// range by at most kAlignSlack tokens: fewer workgroups, none crossing (480p
-// reduction: 224 workgroups of 2,340 tokens instead of 256 of 2,048, 111 of
-// which crossed; 27.8 -> 26.4 us).  Splits of several blocks per range stay
-// as they are.
-constexpr long long kAlignSlack = 512;
-void align_split(SplitArgs* s, int* G_out, long long blocks, int Nb, long long max_wg, bool fewer = false) {
-  if (s->L >= Nb) return;
-  long long J = (Nb + s->L - 1) / s->L;
-  if (blocks * J > max_wg) {
-    if (!fewer) return;
-    J = Nb / s->L;
-    if (J < 1 || blocks * J > max_wg || (Nb + J - 1) / J > s->L + kAlignSlack) return;
-  }
-  const long long Lb = (Nb + J - 1) / J;
-  s->L = Lb;
-  s->Nbp = (int)(J * Lb);
-  s->total = blocks * s->Nbp;
-  *G_out = (int)(blocks * J);
-}
-
 // How many workgroups of `fn` the current device holds at once (CUs times
-// workgroups per CU for its registers and LDS).  Launching exactly that many,
-// each with an equal token range, keeps every CU streaming until the end.
+// workgroups per CU for its registers and LDS): the streaming kernels' grids
+// are at most that many equal token ranges, so that no workgroup waits for a
+// slot (make_split, then align_split).
 int resident_workgroups(const void* fn, int threads, size_t lds) {
   static std::mutex mu;
   static std::map<std::tuple<int, const void*, size_t>, int> cache;
@@ -2518,19 +2459,8 @@ int plan_grids_t(Plan* p) {
   const long long a = resident_workgroups((const void*)&sva_apply_kernel<BF16, D, (!BF16 && ROPE == 3 ? 2 : ROPE)>, app_threads<BF16>(), lds);
   const long long r_max = r < kRedWorkgroupsMax ? r : kRedWorkgroupsMax;
   const long long a_max = a < kAppWorkgroupsMax ? a : kAppWorkgroupsMax;
-  // When the output pass's minimum of tokens per workgroup, not occupancy,
-  // bounds its grid (one block of a few thousand tokens per sequence), a
-  // multiple of the CU count gives every CU the same number of workgroups
-  // (304 workgroups on 256 CUs left 48 CUs with twice the work of the rest).
-  long long a_target = a_max;
-  const long long a_tok = total / kMinTokensPerWG;
-  const long long cus = device_cus();
-  if (a_tok < a_target) a_target = a_tok >= cus ? a_tok / cus * cus : a_tok;
-  p->red = make_split(total, r_max, &p->G_red, p->Nb);
-  p->app = make_split(total, a_target > 0 ? a_target : 1, &p->G_app, p->Nb);
-  const long long blocks = (long long)p->BH * p->nb;
-  align_split(&p->red, &p->G_red, blocks, p->Nb, r_max, true);
-  align_split(&p->app, &p->G_app, blocks, p->Nb, a_max);
+  plan_forward_splits(total, (long long)p->BH * p->nb, p->Nb, r_max, a_max, device_cus(), &p->red, &p->G_red,
+                      &p->app, &p->G_app);
   return 0;
 }
 
