@@ -89,6 +89,31 @@ def _timed(stream, fn, n):
     return a.elapsed_time(b) / n
 
 
+def warm_for(fn, calls: int, min_ms: float = 0.0):
+    """Runs fn(i) for `calls` calls, then, when min_ms is set, more calls
+    until about min_ms of GPU time has run (estimated from the first calls):
+    after the host has set up a workload the GPU has been idle, and its
+    clocks come back over a few milliseconds of work.  Returns the number of
+    calls made."""
+    import torch
+    stream = torch.cuda.current_stream()
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    a.record(stream)
+    for i in range(calls):
+        fn(i)
+    b.record(stream)
+    torch.cuda.synchronize()
+    n = calls
+    if min_ms > 0 and calls > 0:
+        per = max(a.elapsed_time(b) / calls, 1e-3)
+        extra = int(max(0.0, min_ms - a.elapsed_time(b)) / per) + 1
+        for i in range(extra):
+            fn(calls + i)
+        torch.cuda.synchronize()
+        n += extra
+    return n
+
+
 def graph_timed(fn, n: int, replays: int = 5):
     """ms per call of fn(i) for n calls captured in one HIP graph (torch's
     CUDAGraph on its capture stream) and replayed `replays` times: the launch
@@ -140,7 +165,7 @@ class ForwardBench:
                                   split=w.split, base=w.base, eps=w.eps, out=self.outs[s_], ws=self.ws,
                                   stages=stages)
 
-    def run(self, steps: int, warmup: int, repeats: int = 0, stage_calls: int = 0):
+    def run(self, steps: int, warmup: int, repeats: int = 0, stage_calls: int = 0, min_warm_ms: float = 0.0):
         """Returns a dict:
           ms          ms per step over W untimed + K timed uninstrumented steps;
           repeat_ms   per-step ms of `repeats` further runs of K steps each;
@@ -148,12 +173,11 @@ class ForwardBench:
                       `stage_calls` back-to-back launches (sva_lin_attn_fwd_stages)
                       on the same buffers, no event between two launches;
           stage_graph_us  the same launches captured in a HIP graph and
-                      replayed (no host launch cost)."""
+                      replayed (no host launch cost).
+        The headline passes min_warm_ms = 0: exactly `warmup` untimed steps."""
         import torch
         stream = torch.cuda.current_stream()
-        for i in range(warmup):
-            self.step(i)
-        torch.cuda.synchronize()
+        warmup = warm_for(self.step, warmup, min_warm_ms)
         res = {"ms": _timed(stream, lambda i: self.step(warmup + i), steps)}
         res["repeat_ms"] = [_timed(stream, self.step, steps) for _ in range(repeats)]
         res["stage_us"], res["stage_graph_us"] = {}, {}
@@ -175,10 +199,11 @@ class ForwardBench:
         del self.bufs, self.outs, self.ws
 
 
-def gpu_leg(w, steps: int, warmup: int, sets: int, repeats: int = 0, stage_calls: int = 0):
+def gpu_leg(w, steps: int, warmup: int, sets: int, repeats: int = 0, stage_calls: int = 0,
+            min_warm_ms: float = 0.0):
     """ForwardBench(w, sets).run(...), buffers freed afterwards."""
     fb = ForwardBench(w, sets)
-    res = fb.run(steps, warmup, repeats, stage_calls)
+    res = fb.run(steps, warmup, repeats, stage_calls, min_warm_ms)
     fb.free()
     return res
 
@@ -224,7 +249,7 @@ def bwd_leg(w, steps: int, warmup: int, sets: int):
     return res[0], res[1]
 
 
-def cached_leg(w, steps: int, warmup: int):
+def cached_leg(w, steps: int, warmup: int, min_warm_ms: float = 0.0):
     """Streaming generation: a cache committed from the workload's prior
     blocks, then `steps` denoising steps of one block against it
     (sva_block_cache_apply, the cache read only), cycling over the workload's
@@ -264,9 +289,7 @@ def cached_leg(w, steps: int, warmup: int):
     def commit(i):
         sva.sva_block_cache_commit(S2, z2, last["k"], last["v"], fg, t0=w.t0, ws=ws, **kw)
 
-    for i in range(warmup):
-        apply(i)
-    torch.cuda.synchronize()
+    warm_for(apply, warmup, min_warm_ms)
     res = {"apply_ms": _timed(stream, apply, steps), "commit_ms": _timed(stream, commit, steps)}
     res["apply_graph_ms"] = graph_timed(apply, steps)
     res["commit_graph_ms"] = graph_timed(commit, steps)
@@ -641,7 +664,8 @@ def other_workloads(steps: int, warmup: int, sets: int):
     out = {}
     for name, k_steps in (("480p", steps), ("minute", max(2, steps // 4)), ("tiny", steps)):
         w = wl.WORKLOADS[name]
-        res = gpu_leg(w, k_steps, warmup, sets if name != "tiny" else 1, stage_calls=k_steps if name != "tiny" else 0)
+        res = gpu_leg(w, k_steps, warmup, sets if name != "tiny" else 1, stage_calls=k_steps if name != "tiny" else 0,
+                      min_warm_ms=SECONDARY_WARM_MS)
         esz = 2 if w.dtype == "bf16" else 4
         step_bytes = 4 * w.B * w.H * w.N * w.d * esz
         ent = {"us_per_step": res["ms"] * 1e3, "tokens_per_s": w.B * w.N / (res["ms"] * 1e-3),
@@ -651,7 +675,7 @@ def other_workloads(steps: int, warmup: int, sets: int):
             ent["kernels_eager_us"] = {k: round(v, 2) for k, v in res["stage_us"].items()}
         out[name] = ent
     w = wl.WORKLOADS["cached_step"]
-    c = cached_leg(w, steps, warmup)
+    c = cached_leg(w, steps, warmup, SECONDARY_WARM_MS)
     out["cached_step"] = {"us_per_step": c["apply_ms"] * 1e3, "commit_us": c["commit_ms"] * 1e3,
                           "us_per_step_graph": c["apply_graph_ms"] * 1e3,
                           "commit_us_graph": c["commit_graph_ms"] * 1e3,
@@ -661,6 +685,7 @@ def other_workloads(steps: int, warmup: int, sets: int):
 
 
 SECONDARY_WARMUP = 50  # warm-up calls of each leg after the headline
+SECONDARY_WARM_MS = 30.0  # and at least this much GPU time of warm-up calls (the other workloads)
 SECONDARY_STEPS = 100  # timed steps of each other workload, at least
 
 
