@@ -156,10 +156,19 @@ class ForwardBench:
         desc = sva.make_desc(w.B, w.H, w.d, (w.T, w.Hs, w.Ws), w.F, t0=w.t0, rope=w.rope, split=w.split,
                              base=w.base, eps=w.eps, dtype=sva.SVA_BF16 if w.dtype == "bf16" else sva.SVA_F32)
         self.ws = torch.zeros(sva.sva_lin_attn_fwd_workspace(desc), dtype=torch.uint8, device=dev)
+        # a whole step is one prepared call per buffer set (the binding's
+        # checks done here, once)
+        self.calls = [sva.prepare_lin_attn_fwd(x["q"], x["k"], x["v"], (w.T, w.Hs, w.Ws), w.F, t0=w.t0,
+                                               rope=w.rope, split=w.split, base=w.base, eps=w.eps,
+                                               out=self.outs[s_], ws=self.ws)
+                      for s_, x in enumerate(self.bufs)]
         torch.cuda.synchronize()
 
     def step(self, i, stages=7):
         w, s_ = self.w, i % self.sets
+        if stages == 7:
+            self.calls[s_]()
+            return
         x = self.bufs[s_]
         self.sva.sva_lin_attn_fwd(x["q"], x["k"], x["v"], (w.T, w.Hs, w.Ws), w.F, t0=w.t0, rope=w.rope,
                                   split=w.split, base=w.base, eps=w.eps, out=self.outs[s_], ws=self.ws,
@@ -196,7 +205,7 @@ class ForwardBench:
         return res
 
     def free(self):
-        del self.bufs, self.outs, self.ws
+        del self.calls, self.bufs, self.outs, self.ws
 
 
 def gpu_leg(w, steps: int, warmup: int, sets: int, repeats: int = 0, stage_calls: int = 0,

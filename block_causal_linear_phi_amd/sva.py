@@ -291,6 +291,58 @@ def sva_lin_attn_fwd(q, k, v, grid: Tuple[int, int, int], frames_per_block: int,
     return out
 
 
+class PreparedCall:
+    """One library call whose arguments were checked and marshalled once:
+    calling it issues the C call alone (about a microsecond of host time,
+    against tens for a call through the checking wrappers), for loops that
+    repeat a call on the same buffers.  It keeps references to its tensors;
+    their storage must not be resized or freed, and their contents may
+    change between calls.  The stream is the one given at preparation, else
+    the current stream at each call (so a call made under graph capture is
+    captured).  Raises SvaError on a nonzero status."""
+
+    __slots__ = ("_fn", "_args", "_stream", "_keep", "_where", "out")
+
+    def __init__(self, fn_name, args, stream, keep, where, out=None):
+        self._fn = getattr(lib(), fn_name)
+        self._args = tuple(args)
+        self._stream = None if stream is None else stream.cuda_stream
+        self._keep = keep
+        self._where = where
+        self.out = out
+
+    def __call__(self):
+        st = self._fn(*self._args, self._stream if self._stream is not None else _stream(None))
+        if st != SVA_OK:
+            raise SvaError(st, self._where)
+        return self.out
+
+
+def prepare_lin_attn_fwd(q, k, v, grid: Tuple[int, int, int], frames_per_block: int, *, t0: int = 0,
+                         rope: bool = False, split=None, base: float = 10000.0, eps: float = 1e-6,
+                         S0=None, z0=None, out=None, S_out=None, z_out=None, ws=None, stream=None) -> PreparedCall:
+    """sva_lin_attn_fwd with its checks done now: returns a PreparedCall
+    whose calls run the forward on these buffers (out and the workspace
+    are allocated here when not given, and kept)."""
+    import torch
+    _pair("S0", S0, "z0", z0)
+    _pair("S_out", S_out, "z_out", z_out)
+    _check_attn(q, grid, like_q=[("k", k), ("v", v), ("out", out)],
+                caches=[("S0", S0, "S"), ("z0", z0, "z"), ("S_out", S_out, "S"), ("z_out", z_out, "z")],
+                buffers=[("ws", ws)])
+    desc = _desc_from(q, grid, frames_per_block, t0, rope, split, base, eps)
+    if out is None:
+        out = torch.empty_like(q)
+    nbytes = sva_lin_attn_fwd_workspace(desc)
+    if ws is not None and ws.numel() * ws.element_size() < nbytes:
+        raise ValueError(f"ws holds {ws.numel() * ws.element_size()} bytes, the call needs {nbytes}")
+    ws = _workspace(nbytes, q, ws)
+    ptrs = [ctypes.c_void_p(_ptr(t)) for t in (q, k, v, out, S0, z0, S_out, z_out, ws)]
+    args = [ctypes.byref(desc)] + ptrs[:9] + [ctypes.c_size_t(ws.numel() * ws.element_size())]
+    return PreparedCall("sva_lin_attn_fwd", args, stream,
+                        (desc, q, k, v, out, S0, z0, S_out, z_out, ws), "sva_lin_attn_fwd", out)
+
+
 def sva_lin_attn_states_bytes(desc: SvaDesc) -> int:
     n = ctypes.c_size_t()
     _check(lib().sva_lin_attn_states_bytes(ctypes.byref(desc), ctypes.byref(n)), "sva_lin_attn_states_bytes")

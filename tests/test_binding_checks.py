@@ -27,7 +27,10 @@ def _qkv(B=1, H=2, d=64, dtype=torch.bfloat16):
     return _t(B, H, N, d, dtype=dtype), _t(B, H, N, d, dtype=dtype), _t(B, H, N, d, dtype=dtype)
 
 
-def test_fwd_rejects_each_bad_argument():
+@pytest.mark.parametrize("entry", ["call", "prepare"])
+def test_fwd_rejects_each_bad_argument(entry):
+    """The forward, and its prepared form (checked once, at preparation)."""
+    fwd = sva.sva_lin_attn_fwd if entry == "call" else sva.prepare_lin_attn_fwd
     q, k, v = _qkv()
     cases = [
         (dict(k=_t(1, 2, N + 1, 64)), "shape"),                       # k longer than q
@@ -46,7 +49,7 @@ def test_fwd_rejects_each_bad_argument():
         args = dict(q=q, k=k, v=v)
         args.update(kw)
         with pytest.raises(ValueError, match=msg):
-            sva.sva_lin_attn_fwd(args.pop("q"), args.pop("k"), args.pop("v"), GRID, F, **args)
+            fwd(args.pop("q"), args.pop("k"), args.pop("v"), GRID, F, **args)
 
 
 def test_fwd_rejects_unsupported_dtype_and_non_tensors():
