@@ -616,11 +616,11 @@ __device__ __forceinline__ void scan_sequence(const float* partials, int bh, int
 // Accumulator (r, s)[i] of lane l holds S[FPL*(4*(l/16)+i)+r][FPL*(l%16)+s].
 // ---------------------------------------------------------------------------
 
-template <bool BF16, int D, int ROPE, bool FOLD>
-__global__ __launch_bounds__(red_threads<BF16>(), red_min_blocks<BF16>()) void sva_reduce_kernel(
+template <bool BF16, int D, int ROPE, bool FOLD, int RTT = red_threads<BF16>()>
+__global__ __launch_bounds__(RTT, red_min_blocks<BF16>()) void sva_reduce_kernel(
     const void* __restrict__ kp, const void* __restrict__ vp, float* __restrict__ partials,
     Geo geo, SplitArgs sp, RopeArgs ra, FoldArgs fa) {
-  constexpr int RT = red_threads<BF16>();
+  constexpr int RT = RTT;
   constexpr int FPL = D / 16;
   constexpr int NPAIR = FPL / 2;
   constexpr int E = D * D + D;
@@ -2358,9 +2358,15 @@ hipError_t launch_reduce(const Plan& p, const void* k, const void* v, float* par
   FoldArgs fa = fold ? *fold : FoldArgs{};
   void* args[] = {(void*)&k, (void*)&v, (void*)&partials, &geo, &sp, &ra, &fa};
   constexpr int RM = ROPE == 3 ? 2 : ROPE;
+  // One block per sequence (the denoising step, its commit, block-by-block
+  // calls): a range of a few hundred tokens gives an 8-wave workgroup about
+  // one step per wave, so 4 waves (still one workgroup per CU) take two
+  // steps each and their cross-wave sum adds 4 tiles instead of 8.
+  const bool small = BF16 && p.nb == 1 && !fold;
   const void* fn = fold ? (const void*)&sva_reduce_kernel<BF16, D, RM, true>
+                 : small ? (const void*)&sva_reduce_kernel<BF16, D, RM, false, 256>
                         : (const void*)&sva_reduce_kernel<BF16, D, RM, false>;
-  return hipLaunchKernel(fn, dim3(p.G_red), dim3(red_threads<BF16>()), args, ROPE ? p.tab_bytes : 0, st);
+  return hipLaunchKernel(fn, dim3(p.G_red), dim3(small ? 256 : red_threads<BF16>()), args, ROPE ? p.tab_bytes : 0, st);
 }
 
 template <bool BF16, int D>
