@@ -2358,11 +2358,13 @@ hipError_t launch_reduce(const Plan& p, const void* k, const void* v, float* par
   FoldArgs fa = fold ? *fold : FoldArgs{};
   void* args[] = {(void*)&k, (void*)&v, (void*)&partials, &geo, &sp, &ra, &fa};
   constexpr int RM = ROPE == 3 ? 2 : ROPE;
-  // One block per sequence (the denoising step, its commit, block-by-block
-  // calls): a range of a few hundred tokens gives an 8-wave workgroup about
-  // one step per wave, so 4 waves (still one workgroup per CU) take two
-  // steps each and their cross-wave sum adds 4 tiles instead of 8.
-  const bool small = BF16 && p.nb == 1 && !fold;
+  // bf16 without the folded prefix: 4-wave workgroups, two per CU on
+  // block-aligned ranges (448 of them at 480p and 720p, against 224 or 256
+  // of 8 waves: the reduction 25.7 -> 24.9 us at 480p, 54.7 -> 54.2 us at
+  // 720p), and one per CU for one-block calls, where a range of a few
+  // hundred tokens would give 8 waves about one step each (plan_grids_t).
+  // Their cross-wave sum adds 4 tiles instead of 8.
+  const bool small = BF16 && !fold;
   const void* fn = fold ? (const void*)&sva_reduce_kernel<BF16, D, RM, true>
                  : small ? (const void*)&sva_reduce_kernel<BF16, D, RM, false, 256>
                         : (const void*)&sva_reduce_kernel<BF16, D, RM, false>;
@@ -2459,9 +2461,12 @@ template <bool BF16, int D, int ROPE>
 int plan_grids_t(Plan* p) {
   const long long total = (long long)p->BH * p->N;
   const size_t lds = ROPE ? p->tab_bytes : 0;
+  const bool small = BF16 && !p->fold;
   const void* red_fn = p->fold ? (const void*)&sva_reduce_kernel<BF16, D, (ROPE == 3 ? 2 : ROPE), true>
+                     : small ? (const void*)&sva_reduce_kernel<BF16, D, (ROPE == 3 ? 2 : ROPE), false, 256>
                                : (const void*)&sva_reduce_kernel<BF16, D, (ROPE == 3 ? 2 : ROPE), false>;
-  const long long r = resident_workgroups(red_fn, red_threads<BF16>(), lds);
+  long long r = resident_workgroups(red_fn, small ? 256 : red_threads<BF16>(), lds);
+  if (small && p->nb == 1) r = device_cus();  // one block: one 4-wave workgroup per CU (as measured)
   const long long a = resident_workgroups((const void*)&sva_apply_kernel<BF16, D, (!BF16 && ROPE == 3 ? 2 : ROPE)>, app_threads<BF16>(), lds);
   const long long r_max = r < kRedWorkgroupsMax ? r : kRedWorkgroupsMax;
   const long long a_max = a < kAppWorkgroupsMax ? a : kAppWorkgroupsMax;
